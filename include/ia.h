@@ -1,0 +1,153 @@
+/*
+ * ia.h — C ABI of the Interdomain Attention (IA) token-mixer library, libia.so (gfx950).
+ *
+ * Sources for what is computed.  Two web pages describe the method:
+ *   [summary]  "Interdomain Attention: Beyond Token-Level Key-Value Memory", paper summary
+ *              page (paperlayer.ai), organised by the paper's sections;
+ *   [podcast]  "Interdomain Attention: Beyond Token-Level Key-Value Memory", AI Radio episode
+ *              page (montaan.com), whose "Key Components and Derivation" and "Implementation
+ *              Details" paragraphs carry the derivation and the matrix form of the readout.
+ *
+ * The operation, per batch row b and head h (all quantities of one (b,h) slice):
+ *   feature map        phi(x) = elu(x) + 1, applied elementwise to q_t and k_t   [podcast, derivation]
+ *   state recurrence   U_t[m,:]   = lambda_m U_{t-1}[m,:]   + beta_m phi(k_t)     [summary §3.2]
+ *                      Gam_t[m,:] = lambda_m Gam_{t-1}[m,:] + beta_m v_t          [podcast, derivation]
+ *                      eta_t[m]   = lambda_m eta_{t-1}[m]   + beta_m              (a value channel of ones)
+ *   readout            a_t[m] = sum_r phi(q_t)[r] U_t[m,r]   (plain transpose, no conjugate)
+ *                      o_t    = Re(sum_m a_t[m] Gam_t[m,:]) / max(Re(sum_m a_t[m] eta_t[m]), clamp)
+ *   This is the matrix form O = Fq U^T Gamma / Fq U^T eta with element-wise division
+ *   [podcast, derivation], the states U, Gamma, eta of fixed size [summary §3.1], with M
+ *   complex-diagonal modes lambda_m (S4D) [summary §3.2].  The readout at step t includes
+ *   token t.  The clamp (default 1e-6) is one-sided: a negative real part is raised to it.
+ *
+ * Layouts (all row-major, innermost index last, no padding):
+ *   q, k        [B][N][H][F]   in_dtype (IA_F32 or IA_BF16)
+ *   v           [B][N][H][Dv]  in_dtype
+ *   o           [B][N][H][Dv]  out_dtype
+ *   lambda,beta [H][M]         complex64: interleaved (re, im) float pairs
+ *   state U     [B][H][M][F]   complex64 interleaved
+ *   state Gamma [B][H][M][Dv]  complex64 interleaved
+ *   state eta   [B][H][M]      complex64 interleaved
+ *   decode q_t,k_t [B][H][F], v_t and o_t [B][H][Dv]
+ * The state holds 2(F+Dv)M + 2M reals per (b,h): the 2(d_feat + d_h)M of [summary §D.2] plus
+ * the normaliser eta.
+ *
+ * Conventions for every call:
+ *   - All pointers except `desc`, `st` (the struct) are DEVICE pointers, 16-byte aligned.
+ *   - The caller owns every buffer.  The library allocates nothing and keeps no global state.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the null stream);
+ *     the call returns without synchronising.  Results are visible after the stream syncs.
+ *   - Validation happens on the host before anything is enqueued.  On any error nothing is
+ *     enqueued and no output is touched.  A launch failure returns IA_ERR_LAUNCH.  A device
+ *     fault surfaces at the caller's next synchronisation, as in HIP.
+ *   - No call prints, aborts or throws.
+ *   - Results are bitwise reproducible run to run (no floating-point atomics).
+ */
+#ifndef IA_H
+#define IA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  IA_OK = 0,
+  IA_ERR_NULL = 1,         /* a required pointer is NULL */
+  IA_ERR_SHAPE = 2,        /* a size is out of range (B,H,N,F,Dv,M <= 0, or too large) */
+  IA_ERR_DTYPE = 3,        /* unknown dtype code */
+  IA_ERR_ALIGN = 4,        /* a device pointer is not 16-byte aligned */
+  IA_ERR_ALIAS = 5,        /* an output overlaps an input or another output */
+  IA_ERR_DOMAIN = 6,       /* lambda outside the supported domain (see ia_prefill_fwd) */
+  IA_ERR_UNSUPPORTED = 7,  /* a combination this build does not implement */
+  IA_ERR_LAUNCH = 8,       /* the HIP runtime refused a launch */
+  IA_ERR_WORKSPACE = 9     /* workspace NULL or smaller than the *_workspace_bytes query */
+} ia_status;
+
+typedef enum { IA_F32 = 0, IA_BF16 = 1 } ia_dtype;
+
+/* Bidirectional layer: o = IA(x) + flip_t(IA(flip_t x)), each direction from a zero state and
+ * normalised separately, same lambda, beta, q, k, v (the Caduceus-style genomic models of
+ * [summary §5.2, §A.1] run the token mixer over the sequence and its reversal). */
+#define IA_FLAG_BIDIR 1u
+
+typedef struct ia_desc {
+  int B;             /* batch rows */
+  int H;             /* heads */
+  int N;             /* tokens (prefill); ignored by ia_decode_step */
+  int F;             /* feature dim of q and k (R = d_h on the pages); multiple of 16, <= 256 */
+  int Dv;            /* value dim; multiple of 16, <= 256 */
+  int M;             /* complex modes; multiple of 16, <= 128 */
+  int in_dtype;      /* ia_dtype of q, k, v */
+  int out_dtype;     /* ia_dtype of o */
+  float den_clamp;   /* lower clamp of Re(den); must be > 0 (the method uses 1e-6) */
+  unsigned flags;    /* IA_FLAG_BIDIR or 0 */
+  int chunk;         /* chunk length of the chunked prefill; 0 = 64 [summary §A.2] */
+} ia_desc;
+
+/* Recurrent state of all (b,h) slices; three device pointers, layouts above. */
+typedef struct ia_state {
+  void* U;
+  void* Gamma;
+  void* eta;
+} ia_state;
+
+/* Zero the state (the recurrence starts from U = Gamma = eta = 0).  Enqueues a fill kernel
+ * (no memset node), so it may be captured in a graph.  Errors: IA_ERR_NULL, IA_ERR_SHAPE,
+ * IA_ERR_ALIGN, IA_ERR_LAUNCH. */
+ia_status ia_state_init(const ia_desc* desc, ia_state* st, void* stream);
+
+/* Bytes of device workspace ia_prefill_fwd needs for `desc`; 0 if the desc is invalid.
+ * The workspace holds per-segment state summaries of the chunked scan and, for
+ * IA_FLAG_BIDIR, nothing more; its contents need no initialisation and are scratch. */
+size_t ia_prefill_workspace_bytes(const ia_desc* desc);
+
+/* Causal (or, with IA_FLAG_BIDIR, bidirectional) forward of one IA layer over N tokens.
+ *
+ * Runs the chunkwise form of the recurrence: work inside each chunk of `chunk` tokens is done
+ * as dense contractions, the state is passed across chunk boundaries, and a second pass
+ * recomputes each segment from its corrected initial state [summary §3.2, §A.2].  Results
+ * equal the token-by-token recurrence up to rounding and do not depend on `chunk`.
+ *
+ *   q, k, v    inputs, layouts above, read only.
+ *   lambda     [H][M] complex64, 0 < |lambda| <= 1.  With bf16 inputs the chunked path needs
+ *              |lambda|^(-chunk) representable with margin: it returns IA_ERR_DOMAIN when
+ *              any |lambda_m| < 2^(-15/chunk) (0.85 at chunk 64); choose a smaller chunk then.
+ *   beta       [H][M] complex64 input vector of the S4D recurrence (B on the pages).
+ *   st         NULL: start from zero and do not return a state.  Otherwise st->U/Gamma/eta
+ *              hold the initial state on entry and the state after token N-1 on return
+ *              (resume point for a later prefill or decode).  Must be NULL with BIDIR.
+ *   o          [B][N][H][Dv] out_dtype, or NULL: state-only prefill that builds the decoding
+ *              state and writes no outputs [summary §F.2].  o == NULL with st == NULL is an
+ *              error (nothing to compute).
+ *   workspace  device scratch of at least ia_prefill_workspace_bytes(desc) bytes.
+ * Errors: IA_ERR_NULL, IA_ERR_SHAPE, IA_ERR_DTYPE, IA_ERR_ALIGN, IA_ERR_ALIAS (o overlapping
+ * q/k/v/state, or state buffers overlapping inputs), IA_ERR_DOMAIN, IA_ERR_UNSUPPORTED
+ * (BIDIR with st != NULL), IA_ERR_WORKSPACE, IA_ERR_LAUNCH. */
+ia_status ia_prefill_fwd(const ia_desc* desc,
+                         const void* q, const void* k, const void* v,
+                         const void* lambda, const void* beta,
+                         ia_state* st, void* o,
+                         void* workspace, size_t ws_bytes, void* stream);
+
+/* One autoregressive step for every (b,h): updates the state in place with token t and
+ * writes o_t (the recurrence and readout above with N = 1).  The per-step work and the
+ * state are independent of how many tokens came before [summary §3.2, §F.3].
+ *   q_t, k_t  [B][H][F] in_dtype;  v_t [B][H][Dv] in_dtype;  o_t [B][H][Dv] out_dtype.
+ *   st        required; updated in place.
+ * desc->N, desc->chunk and IA_FLAG_BIDIR are ignored (BIDIR has no causal decode: error
+ * IA_ERR_UNSUPPORTED if set).  No workspace.  Errors as ia_prefill_fwd. */
+ia_status ia_decode_step(const ia_desc* desc,
+                         const void* q_t, const void* k_t, const void* v_t,
+                         const void* lambda, const void* beta,
+                         ia_state* st, void* o_t, void* stream);
+
+/* Static string naming a status code. */
+const char* ia_status_string(ia_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IA_H */

@@ -1,0 +1,159 @@
+"""CPU oracle for the Interdomain Attention (IA) layer -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import this package.  The product (``ssm_sequence_mixer_amd``) never does, and this package
+never imports the product.  It shares no code with the HIP library.
+
+Two independent implementations live here:
+
+* ``ia_oracle.c`` (loaded through ctypes): the token-by-token fp64 complex recurrence and
+  readout, serial, one (b,h) slice per call.  ``prefill``/``decode_step``/``bidir`` below only
+  loop over slices and marshal arrays.
+* ``brute.py``: the explicit double sum over s <= t and modes m, in numpy, for tiny inputs.
+
+The method both follow is stated in the header of ``ia_oracle.c``; the sources are the two
+pages titled "Interdomain Attention: Beyond Token-Level Key-Value Memory" (the paper summary
+page, sections 3.1-3.2, and the AI Radio episode page, "Key Components and Derivation").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ia_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libia_oracle.so")
+_lib = None
+
+GCC_CMD = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c99", "-fPIC",
+           "-shared", "-o", _LIB_PATH, _SRC, "-lm"]
+
+
+def build() -> None:
+    """Compile ia_oracle.c into libia_oracle.so beside it."""
+    subprocess.check_call(GCC_CMD)
+
+
+def load_library(path):
+    """ctypes handle of a built ia_oracle.c with its signature declared."""
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.ia_oracle_scan.restype = ctypes.c_int
+    lib.ia_oracle_scan.argtypes = [ctypes.c_int] * 4 + [dp] * 5 + [dp] * 3 + [dp] * 3 + [
+        ctypes.c_double]
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if (not os.path.exists(_LIB_PATH)
+                or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+            build()
+        _lib = load_library(_LIB_PATH)
+    return _lib
+
+
+def _ptr(a):
+    if a is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    assert a.dtype == np.float64 and a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _c2r(z: np.ndarray) -> np.ndarray:
+    """complex array -> float64 array with a trailing (re, im) axis."""
+    z = np.asarray(z, dtype=np.complex128)
+    return np.ascontiguousarray(np.stack([z.real, z.imag], axis=-1))
+
+
+def _r2c(a: np.ndarray) -> np.ndarray:
+    return a[..., 0] + 1j * a[..., 1]
+
+
+def scan(q, k, v, lam, beta, state=None, clamp=1e-6, lib=None):
+    """Recurrence over one (b,h) slice.
+
+    q, k: [N, F]; v: [N, D]; lam, beta: [M] complex; state: (U [M,F], G [M,D], e [M]) complex
+    or None for zeros.  Returns (o [N,D], num [N,D], den [N], (U, G, e)).  ``lib``: another
+    build of ia_oracle.c to call instead (the tests use it for deliberately broken copies).
+    """
+    lib = _load() if lib is None else lib
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    N, F = q.shape
+    D = v.shape[1]
+    M = len(lam)
+    if state is None:
+        U = np.zeros((M, F, 2))
+        G = np.zeros((M, D, 2))
+        e = np.zeros((M, 2))
+    else:
+        U, G, e = (_c2r(x) for x in state)
+    o = np.empty((N, D))
+    num = np.empty((N, D))
+    den = np.empty((N,))
+    lib.ia_oracle_scan(N, F, D, M, _ptr(q), _ptr(k), _ptr(v), _ptr(_c2r(lam)),
+                       _ptr(_c2r(beta)), _ptr(U), _ptr(G), _ptr(e), _ptr(o), _ptr(num),
+                       _ptr(den), float(clamp))
+    return o, num, den, (_r2c(U), _r2c(G), _r2c(e))
+
+
+def prefill(q, k, v, lam, beta, state=None, clamp=1e-6, slices=None, threads=1):
+    """Causal IA layer forward over a batch.
+
+    q, k: [B, N, H, F]; v: [B, N, H, D]; lam, beta: [H, M] complex; state: (U [B,H,M,F],
+    G [B,H,M,D], e [B,H,M]) complex or None.  ``slices``: optional list of (b, h) to compute
+    (others are left NaN).  Returns (o [B,N,H,D], num, den [B,N,H], state).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, N, H, F = q.shape
+    D = v.shape[3]
+    M = lam.shape[1]
+    o = np.full((B, N, H, D), np.nan)
+    num = np.full((B, N, H, D), np.nan)
+    den = np.full((B, N, H), np.nan)
+    U = np.full((B, H, M, F), np.nan, dtype=np.complex128)
+    G = np.full((B, H, M, D), np.nan, dtype=np.complex128)
+    e = np.full((B, H, M), np.nan, dtype=np.complex128)
+    todo = slices if slices is not None else [(b, h) for b in range(B) for h in range(H)]
+
+    def one(bh):
+        b, h = bh
+        st = None if state is None else (state[0][b, h], state[1][b, h], state[2][b, h])
+        r = scan(q[b, :, h], k[b, :, h], v[b, :, h], lam[h], beta[h], st, clamp)
+        return bh, r
+
+    if threads > 1:
+        with ThreadPoolExecutor(threads) as ex:
+            results = list(ex.map(one, todo))
+    else:
+        results = [one(bh) for bh in todo]
+    for (b, h), (ob, nb, db, (Ub, Gb, eb)) in results:
+        o[b, :, h] = ob
+        num[b, :, h] = nb
+        den[b, :, h] = db
+        U[b, h], G[b, h], e[b, h] = Ub, Gb, eb
+    return o, num, den, (U, G, e)
+
+
+def decode_step(q_t, k_t, v_t, lam, beta, state, clamp=1e-6):
+    """One step for every (b,h): q_t, k_t [B,H,F], v_t [B,H,D]; returns (o_t, state)."""
+    o, _, _, st = prefill(np.asarray(q_t)[:, None], np.asarray(k_t)[:, None],
+                          np.asarray(v_t)[:, None], lam, beta, state, clamp)
+    return o[:, 0], st
+
+
+def bidir(q, k, v, lam, beta, clamp=1e-6, slices=None, threads=1):
+    """Bidirectional layer: IA(x) + flip_t(IA(flip_t x)), both from zero state."""
+    fwd = prefill(q, k, v, lam, beta, None, clamp, slices, threads)[0]
+    fl = lambda a: np.ascontiguousarray(np.asarray(a)[:, ::-1])
+    rev = prefill(fl(q), fl(k), fl(v), lam, beta, None, clamp, slices, threads)[0]
+    return fwd + rev[:, ::-1]

@@ -1,0 +1,256 @@
+"""Pins of the CPU oracle to facts other than itself (no GPU).
+
+Each pin is a property fixed by the pages' definition of the layer or by mathematics, not a
+retyping of the oracle's formula:
+  hand    values worked by hand (tests/golden/hand_cases.json)
+  P1      the recurrence equals the unrolled double sum over s <= t and modes (oracle/brute.py)
+  P3      a scan equals the same tokens fed one decode step at a time, from any split point
+  P4      eta_t has the closed form beta (1 - lambda^(t+1)) / (1 - lambda)  (beta (t+1) at 1)
+  P5      with lambda_m the M-th roots of unity, beta = 1 and 2t < M, o_t = v_t exactly
+          (the mode sum is a DFT that keeps only s = s' = t); a conjugated readout would
+          give causal linear attention instead
+  P6      one real mode: o_t is the exponential moving average of v, independent of q and k
+  P7      o is linear in v; invariant under a common real scaling of beta
+  P8      the bidirectional layer commutes with reversing the sequence
+  P9      forced clamp: beta = i with real lambda makes Re(den) < 0, so o = num / clamp
+  P10     the state holds 2(F+Dv)M + 2M reals per (b,h)  (summary page §D.2 plus eta)
+The mutant test at the end builds deliberately broken copies of ia_oracle.c and checks that
+each one fails at least one pin.
+"""
+import json
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import brute
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
+
+
+def _rand_case(rng, N, F, D, M, complex_beta=True, rmin=0.6):
+    q = rng.standard_normal((N, F))
+    k = rng.standard_normal((N, F))
+    v = rng.standard_normal((N, D))
+    r = rng.uniform(rmin, 1.0, M)
+    th = rng.uniform(-np.pi, np.pi, M)
+    lam = r * np.exp(1j * th)
+    beta = (rng.standard_normal(M) + 1j * rng.standard_normal(M)) if complex_beta else np.ones(M)
+    return q, k, v, lam, beta
+
+
+def _rel(a, b):
+    a, b = np.asarray(a), np.asarray(b)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# ---------------------------------------------------------------- pin functions
+# Each takes a scan callable (the oracle, or a broken copy) and returns the error it sees.
+
+def pin_hand(scan):
+    worst = 0.0
+    for c in json.load(open(GOLD))["cases"]:
+        lam = np.array([complex(*x) for x in c["lam"]])
+        beta = np.array([complex(*x) for x in c["beta"]])
+        o, num, den, (U, G, e) = scan(np.array(c["q"]), np.array(c["k"]), np.array(c["v"]),
+                                      lam, beta, None, c["clamp"])
+        cpl = lambda a: np.array(a)[..., 0] + 1j * np.array(a)[..., 1]
+        for got, want in ((o, c["o"]), (num, c["num"]), (den, c["den"]), (U, cpl(c["U_final"])),
+                          (G, cpl(c["G_final"])), (e, cpl(c["e_final"]))):
+            worst = max(worst, _rel(got, want))
+    return worst
+
+
+def pin_brute(scan, seed=0):
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for (N, F, D, M) in ((23, 3, 5, 4), (9, 1, 2, 3), (31, 4, 4, 2)):
+        q, k, v, lam, beta = _rand_case(rng, N, F, D, M)
+        o, num, den, _ = scan(q, k, v, lam, beta, None, 1e-6)
+        ob, nb, db = brute.layer(q, k, v, lam, beta, 1e-6)
+        worst = max(worst, _rel(num, nb), _rel(den, db), _rel(o, ob))
+    return worst
+
+
+def pin_eta_closed_form(scan, seed=1):
+    rng = np.random.default_rng(seed)
+    N, F, D, M = 40, 2, 2, 6
+    q, k, v, lam, beta = _rand_case(rng, N, F, D, M)
+    lam[0] = 1.0  # the lambda = 1 branch
+    _, _, _, (_, _, e) = scan(q, k, v, lam, beta, None, 1e-6)
+    want = np.where(np.abs(lam - 1) > 0, beta * (1 - lam ** N) / np.where(lam == 1, 1, 1 - lam),
+                    beta * N)
+    return _rel(e, want)
+
+
+def pin_dft_roots(scan, seed=2):
+    rng = np.random.default_rng(seed)
+    M, N, F, D = 64, 32, 5, 7   # 2t <= 62 < M
+    q, k, v, _, _ = _rand_case(rng, N, F, D, M)
+    lam = np.exp(2j * np.pi * np.arange(M) / M)
+    o, _, _, _ = scan(q, k, v, lam, np.ones(M), None, 1e-6)
+    return _rel(o, v)
+
+
+def pin_ema(scan, seed=3):
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for lam0 in (0.9, 1.0):
+        q, k, v, _, _ = _rand_case(rng, 50, 3, 4, 1)
+        o, _, _, _ = scan(q, k, v, np.array([lam0]), np.ones(1), None, 1e-6)
+        w = np.array([[lam0 ** (t - s) if s <= t else 0.0 for s in range(50)] for t in range(50)])
+        want = (w @ v) / w.sum(1, keepdims=True)
+        worst = max(worst, _rel(o, want))
+    return worst
+
+
+def pin_clamp(scan, seed=4):
+    rng = np.random.default_rng(seed)
+    N, F, D, M = 12, 3, 3, 4
+    q, k, v, _, _ = _rand_case(rng, N, F, D, M)
+    lam = rng.uniform(0.5, 0.99, M).astype(complex)
+    beta = 1j * np.ones(M)
+    o, num, den, _ = scan(q, k, v, lam, beta, None, 1e-6)
+    if not np.all(den < 0):
+        return np.inf
+    return _rel(o, num / 1e-6)
+
+
+PINS = {"hand": pin_hand, "brute": pin_brute, "eta": pin_eta_closed_form,
+        "dft": pin_dft_roots, "ema": pin_ema, "clamp": pin_clamp}
+TOL = 1e-9
+
+
+# ---------------------------------------------------------------- the pins on the oracle
+
+@pytest.mark.parametrize("name", sorted(PINS))
+def test_pin(name):
+    err = PINS[name](oracle.scan)
+    assert err < TOL, f"{name}: {err}"
+
+
+def test_brute_dft_conjugate_reading_is_linear_attention():
+    # The conjugate-transpose reading of Fq U^T would turn the DFT case into causal linear
+    # attention; check that brute force (independent of the oracle) tells the two apart.
+    rng = np.random.default_rng(5)
+    M, N, F, D = 64, 20, 4, 3
+    q, k, v, _, _ = _rand_case(rng, N, F, D, M)
+    lam = np.exp(2j * np.pi * np.arange(M) / M)
+    o, _, _ = brute.layer(q, k, v, lam, np.ones(M))
+    assert _rel(o, v) < 1e-12
+    S = brute.feature(q) @ brute.feature(k).T
+    S = np.tril(S)
+    lin = (S @ v) / S.sum(1, keepdims=True)
+    assert _rel(o, lin) > 1e-2
+
+
+def test_scan_equals_decode_steps_and_resume():
+    rng = np.random.default_rng(6)
+    B, N, H, F, D, M = 2, 17, 3, 4, 5, 6
+    q = rng.standard_normal((B, N, H, F))
+    k = rng.standard_normal((B, N, H, F))
+    v = rng.standard_normal((B, N, H, D))
+    lam = rng.uniform(0.7, 1, (H, M)) * np.exp(1j * rng.uniform(-3, 3, (H, M)))
+    beta = rng.standard_normal((H, M)) + 1j * rng.standard_normal((H, M))
+    o_full, _, _, st_full = oracle.prefill(q, k, v, lam, beta)
+    for split in (0, 1, 9, 16):
+        o_a, _, _, st = oracle.prefill(q[:, :split], k[:, :split], v[:, :split], lam, beta) \
+            if split else (np.zeros((B, 0, H, D)), None, None, None)
+        outs = [o_a]
+        for t in range(split, N):
+            if st is None:
+                st = tuple(np.zeros(s, np.complex128) for s in ((B, H, M, F), (B, H, M, D), (B, H, M)))
+            ot, st = oracle.decode_step(q[:, t], k[:, t], v[:, t], lam, beta, st)
+            outs.append(ot[:, None])
+        o = np.concatenate(outs, axis=1)
+        assert _rel(o, o_full) < 1e-12
+        for a, b in zip(st, st_full):
+            assert _rel(a, b) < 1e-12
+
+
+def test_linear_in_v_and_beta_scale_invariance():
+    rng = np.random.default_rng(7)
+    N, F, D, M = 30, 4, 3, 5
+    q, k, v1, _, beta = _rand_case(rng, N, F, D, M, complex_beta=False)
+    # S4D-Lin-shaped modes keep Re(den) well above the clamp, where the invariance is exact
+    lam = np.exp(0.05 * (-0.5 + 1j * np.pi * np.arange(M)))
+    v2 = rng.standard_normal((N, D))
+    o1, _, den1, _ = oracle.scan(q, k, v1, lam, beta)
+    assert np.all(den1 > 1e-3)
+    o2 = oracle.scan(q, k, v2, lam, beta)[0]
+    o12 = oracle.scan(q, k, 2.5 * v1 - 0.75 * v2, lam, beta)[0]
+    assert _rel(o12, 2.5 * o1 - 0.75 * o2) < 1e-11
+    o_scaled = oracle.scan(q, k, v1, lam, 3.0 * beta)[0]
+    assert _rel(o_scaled, o1) < 1e-12
+
+
+def test_bidir_flip_symmetry():
+    rng = np.random.default_rng(8)
+    B, N, H, F, D, M = 1, 21, 2, 3, 4, 5
+    q = rng.standard_normal((B, N, H, F))
+    k = rng.standard_normal((B, N, H, F))
+    v = rng.standard_normal((B, N, H, D))
+    lam = rng.uniform(0.7, 1, (H, M)) * np.exp(1j * rng.uniform(-3, 3, (H, M)))
+    beta = np.ones((H, M), complex)
+    fl = lambda a: np.ascontiguousarray(a[:, ::-1])
+    o = oracle.bidir(q, k, v, lam, beta)
+    o_fl = oracle.bidir(fl(q), fl(k), fl(v), lam, beta)
+    assert _rel(o_fl, o[:, ::-1]) < 1e-12
+    # and it is the sum of the two causal passes, each normalised on its own
+    fwd = brute.layer_batched(q, k, v, lam, beta)
+    rev = brute.layer_batched(fl(q), fl(k), fl(v), lam, beta)[:, ::-1]
+    assert _rel(o, fwd + rev) < 1e-10
+
+
+def test_state_size():
+    B, N, H, F, D, M = 1, 3, 1, 6, 10, 4
+    _, _, _, (U, G, e) = oracle.prefill(np.zeros((B, N, H, F)), np.zeros((B, N, H, F)),
+                                        np.zeros((B, N, H, D)), np.ones((H, M), complex),
+                                        np.ones((H, M), complex))
+    reals = 2 * (U[0, 0].size + G[0, 0].size + e[0, 0].size)
+    assert reals == 2 * (F + D) * M + 2 * M
+
+
+def test_nan_propagates():
+    q = np.zeros((3, 2)); k = np.zeros((3, 2)); v = np.ones((3, 2))
+    k[1, 0] = np.nan
+    o = oracle.scan(q, k, v, np.array([0.5, 0.9]), np.ones(2))[0]
+    assert np.all(np.isfinite(o[0])) and np.all(np.isnan(o[1:]))
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+MUTANTS = {
+    "conjugate_readout": ("a += feature(qt[r]) * uc;", "a += feature(qt[r]) * conj(uc);"),
+    "exclusive_readout": ("a += feature(qt[r]) * uc;",
+                          "a += feature(qt[r]) * (uc - bm * feature(kt[r]));"),
+    "keys_from_queries": ("bm * feature(kt[r]);", "bm * feature(qt[r]);"),
+    "value_beta_dropped": ("gc = l * gc + bm * vt[j];", "gc = l * gc + vt[j];"),
+    "lambda_conjugated": ("double complex l = lam[2 * m] + I * lam[2 * m + 1];",
+                          "double complex l = lam[2 * m] - I * lam[2 * m + 1];"),
+    "den_modulus": ("double d = creal(denc);", "double d = cabs(denc);"),
+    "no_clamp": ("double dc = d < clamp ? clamp : d;", "double dc = d;"),
+    "elu_without_one": ("return x > 0.0 ? x + 1.0 : exp(x);", "return x > 0.0 ? x : exp(x);"),
+    "eta_not_decayed": ("ec = l * ec + bm;", "ec = ec + bm;"),
+    "numerator_conj_a": ("numc[j] += a * gc;", "numc[j] += conj(a) * gc;"),
+    "feature_index_shift": ("a += feature(qt[r]) * uc;",
+                            "a += feature(qt[(r + 1) % F]) * uc;"),
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_planted_mistake_fails_a_pin(mutant, tmp_path):
+    src = open(oracle._SRC).read()
+    old, new = MUTANTS[mutant]
+    assert src.count(old) == 1, f"mutation anchor for {mutant} not found once"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new))
+    so = tmp_path / "mutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", str(so),
+                           str(path), "-lm"])
+    lib = oracle.load_library(str(so))
+    scan = lambda *a: oracle.scan(*a, lib=lib)
+    errs = {name: fn(scan) for name, fn in PINS.items()}
+    assert any(not (e < TOL) for e in errs.values()), f"{mutant} passed every pin: {errs}"
