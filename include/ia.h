@@ -79,11 +79,15 @@ typedef struct ia_desc {
   int F;             /* feature dim of q and k (R = d_h on the pages); multiple of 16, <= 256 */
   int Dv;            /* value dim; multiple of 16, <= 256 */
   int M;             /* complex modes; multiple of 16, <= 128 */
+  /* B, H, N, F, Dv, M <= 0: IA_ERR_SHAPE.  F, Dv or M not a multiple of 16 or above the
+   * maximum: IA_ERR_UNSUPPORTED. */
   int in_dtype;      /* ia_dtype of q, k, v */
   int out_dtype;     /* ia_dtype of o */
-  float den_clamp;   /* lower clamp of Re(den); must be > 0 (the method uses 1e-6) */
-  unsigned flags;    /* IA_FLAG_BIDIR or 0 */
-  int chunk;         /* chunk length of the chunked prefill; 0 = 64 [summary §A.2] */
+  float den_clamp;   /* lower clamp of Re(den); finite and > 0 (the method uses 1e-6), else
+                        IA_ERR_DOMAIN */
+  unsigned flags;    /* IA_FLAG_BIDIR or 0; other bits: IA_ERR_UNSUPPORTED */
+  int chunk;         /* chunk length of the chunked prefill: 0 (= 64 [summary §A.2]), 32 or
+                        64; other values: IA_ERR_UNSUPPORTED */
 } ia_desc;
 
 /* Recurrent state of all (b,h) slices; three device pointers, layouts above. */
@@ -98,10 +102,20 @@ typedef struct ia_state {
  * IA_ERR_ALIGN, IA_ERR_LAUNCH. */
 ia_status ia_state_init(const ia_desc* desc, ia_state* st, void* stream);
 
-/* Bytes of device workspace ia_prefill_fwd needs for `desc`; 0 if the desc is invalid.
- * The workspace holds per-segment state summaries of the chunked scan and, for
- * IA_FLAG_BIDIR, nothing more; its contents need no initialisation and are scratch. */
+/* Bytes of device workspace ia_prefill_fwd needs for `desc` (may be 0); 0 also if the desc
+ * is invalid.  The workspace holds per-segment state summaries of the chunked scan, a state
+ * for state-less fp32 calls, and the first direction's fp32 output for IA_FLAG_BIDIR on the
+ * fp32 path.  Its contents need no initialisation and are scratch between calls. */
 size_t ia_prefill_workspace_bytes(const ia_desc* desc);
+
+/* Host-side check of the mode domain for `desc` (lambda_host: [H][M] complex64 in HOST
+ * memory).  lambda lives in device memory in the other calls, which therefore cannot check
+ * it without a synchronisation and do not; callers that build lambda call this once.
+ * IA_ERR_DOMAIN unless every 0 < |lambda| <= 1 + 1e-6 and, for bf16 inputs (the chunked MFMA
+ * path, whose per-chunk decay factorises lambda^(i-j) = lambda^i lambda^(-j)),
+ * |lambda|^(chunk-1) >= 2^-8 (|lambda| >= 0.916 at chunk 64, 0.836 at chunk 32).  Outside
+ * that domain the chunked path stays finite but may miss the bf16 tolerance. */
+ia_status ia_check_lambda(const ia_desc* desc, const void* lambda_host);
 
 /* Causal (or, with IA_FLAG_BIDIR, bidirectional) forward of one IA layer over N tokens.
  *
@@ -111,9 +125,7 @@ size_t ia_prefill_workspace_bytes(const ia_desc* desc);
  * equal the token-by-token recurrence up to rounding and do not depend on `chunk`.
  *
  *   q, k, v    inputs, layouts above, read only.
- *   lambda     [H][M] complex64, 0 < |lambda| <= 1.  With bf16 inputs the chunked path needs
- *              |lambda|^(-chunk) representable with margin: it returns IA_ERR_DOMAIN when
- *              any |lambda_m| < 2^(-15/chunk) (0.85 at chunk 64); choose a smaller chunk then.
+ *   lambda     [H][M] complex64 in the domain of ia_check_lambda (not checked here).
  *   beta       [H][M] complex64 input vector of the S4D recurrence (B on the pages).
  *   st         NULL: start from zero and do not return a state.  Otherwise st->U/Gamma/eta
  *              hold the initial state on entry and the state after token N-1 on return
@@ -123,8 +135,9 @@ size_t ia_prefill_workspace_bytes(const ia_desc* desc);
  *              error (nothing to compute).
  *   workspace  device scratch of at least ia_prefill_workspace_bytes(desc) bytes.
  * Errors: IA_ERR_NULL, IA_ERR_SHAPE, IA_ERR_DTYPE, IA_ERR_ALIGN, IA_ERR_ALIAS (o overlapping
- * q/k/v/state, or state buffers overlapping inputs), IA_ERR_DOMAIN, IA_ERR_UNSUPPORTED
- * (BIDIR with st != NULL), IA_ERR_WORKSPACE, IA_ERR_LAUNCH. */
+ * an input, lambda/beta or the state, or state buffers overlapping inputs or each other),
+ * IA_ERR_DOMAIN (den_clamp), IA_ERR_UNSUPPORTED (BIDIR with st != NULL, sizes, chunk),
+ * IA_ERR_WORKSPACE, IA_ERR_LAUNCH. */
 ia_status ia_prefill_fwd(const ia_desc* desc,
                          const void* q, const void* k, const void* v,
                          const void* lambda, const void* beta,
@@ -145,6 +158,11 @@ ia_status ia_decode_step(const ia_desc* desc,
 
 /* Static string naming a status code. */
 const char* ia_status_string(ia_status s);
+
+/* Static string: the HIP runtime's text for the error behind the calling thread's most recent
+ * IA_ERR_LAUNCH ("no launch error" if there was none).  The one piece of per-thread state
+ * the library keeps. */
+const char* ia_last_launch_error(void);
 
 #ifdef __cplusplus
 }

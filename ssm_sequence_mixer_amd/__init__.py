@@ -1,0 +1,207 @@
+"""MI355X (gfx950) Interdomain Attention token mixer: Python binding of libia.so.
+
+The binding marshals arguments only: every step of the layer runs in the HIP kernels behind
+the C ABI declared in ``include/ia.h``.  Functions carry the C names:
+
+    ia_state_init(desc, state, stream=None)
+    ia_prefill_workspace_bytes(desc)
+    ia_check_lambda(desc, lam_host)
+    ia_prefill_fwd(desc, q, k, v, lam, beta, state, o, workspace, stream=None)
+    ia_decode_step(desc, q_t, k_t, v_t, lam, beta, state, o_t, stream=None)
+
+Tensors are torch tensors on the GPU (PyTorch provides device memory and streams):
+q, k [B,N,H,F], v and o [B,N,H,Dv] in float32 or bfloat16; lam, beta [H,M] complex64; a
+state is a tuple (U [B,H,M,F], Gamma [B,H,M,Dv], eta [B,H,M]) of complex64 tensors.
+``prefill``, ``decode`` and ``new_state`` are conveniences that allocate the outputs with
+torch and then call the same entry points.
+
+Importing fails loudly when libia.so has not been built (``python
+ssm_sequence_mixer_amd/build.py``): there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libia.so")
+
+IA_F32, IA_BF16 = 0, 1
+IA_FLAG_BIDIR = 1
+STATUS = ["IA_OK", "IA_ERR_NULL", "IA_ERR_SHAPE", "IA_ERR_DTYPE", "IA_ERR_ALIGN",
+          "IA_ERR_ALIAS", "IA_ERR_DOMAIN", "IA_ERR_UNSUPPORTED", "IA_ERR_LAUNCH",
+          "IA_ERR_WORKSPACE"]
+
+
+class IADesc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("N", ctypes.c_int),
+                ("F", ctypes.c_int), ("Dv", ctypes.c_int), ("M", ctypes.c_int),
+                ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("den_clamp", ctypes.c_float), ("flags", ctypes.c_uint),
+                ("chunk", ctypes.c_int)]
+
+
+class IAState(ctypes.Structure):
+    _fields_ = [("U", ctypes.c_void_p), ("Gamma", ctypes.c_void_p), ("eta", ctypes.c_void_p)]
+
+
+class IAError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        name = STATUS[status] if 0 <= status < len(STATUS) else str(status)
+        super().__init__(f"{where}: {name}" + (f" ({detail})" if detail else ""))
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python ssm_sequence_mixer_amd/build.py`")
+
+# One HIP runtime per process: torch ships its own libamdhip64.so.7, so torch is loaded first
+# and libia.so's dependency on that soname then binds to the copy already in the process.
+# (Loading the system copy as well gives a second runtime that sees no device.)
+import torch  # noqa: E402,F401
+
+lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_D = ctypes.POINTER(IADesc)
+_S = ctypes.POINTER(IAState)
+lib.ia_state_init.argtypes = [_D, _S, _P]
+lib.ia_state_init.restype = ctypes.c_int
+lib.ia_prefill_workspace_bytes.argtypes = [_D]
+lib.ia_prefill_workspace_bytes.restype = ctypes.c_size_t
+lib.ia_check_lambda.argtypes = [_D, _P]
+lib.ia_check_lambda.restype = ctypes.c_int
+lib.ia_prefill_fwd.argtypes = [_D, _P, _P, _P, _P, _P, _S, _P, _P, ctypes.c_size_t, _P]
+lib.ia_prefill_fwd.restype = ctypes.c_int
+lib.ia_decode_step.argtypes = [_D, _P, _P, _P, _P, _P, _S, _P, _P]
+lib.ia_decode_step.restype = ctypes.c_int
+lib.ia_status_string.argtypes = [ctypes.c_int]
+lib.ia_status_string.restype = ctypes.c_char_p
+lib.ia_last_launch_error.argtypes = []
+lib.ia_last_launch_error.restype = ctypes.c_char_p
+
+EXPORTS = ("ia_state_init", "ia_prefill_workspace_bytes", "ia_check_lambda", "ia_prefill_fwd",
+           "ia_decode_step", "ia_status_string", "ia_last_launch_error")
+
+
+def make_desc(B, H, N, F, Dv, M, in_dtype=IA_BF16, out_dtype=IA_F32, den_clamp=1e-6,
+              bidir=False, chunk=0) -> IADesc:
+    return IADesc(B, H, N, F, Dv, M, in_dtype, out_dtype, den_clamp,
+                  IA_FLAG_BIDIR if bidir else 0, chunk)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else stream)
+
+
+def _state(state):
+    if state is None:
+        return None
+    for t in state:
+        if not t.is_contiguous():
+            raise ValueError("state tensors must be contiguous")
+    return ctypes.pointer(IAState(*(t.data_ptr() for t in state)))
+
+
+def _dense(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors passed to libia must be contiguous")
+
+
+def _check(status, where):
+    if status != 0:
+        detail = lib.ia_last_launch_error().decode() if status == 8 else ""
+        raise IAError(status, where, detail)
+
+
+def dtype_code(dtype) -> int:
+    import torch
+    if dtype == torch.float32:
+        return IA_F32
+    if dtype == torch.bfloat16:
+        return IA_BF16
+    raise ValueError(f"unsupported dtype {dtype}")
+
+
+# ---------------------------------------------------------------- the C entry points
+
+def ia_state_init(desc: IADesc, state, stream=None) -> None:
+    _check(lib.ia_state_init(ctypes.byref(desc), _state(state), _stream(stream)),
+           "ia_state_init")
+
+
+def ia_prefill_workspace_bytes(desc: IADesc) -> int:
+    return int(lib.ia_prefill_workspace_bytes(ctypes.byref(desc)))
+
+
+def ia_check_lambda(desc: IADesc, lam_host) -> None:
+    """lam_host: numpy complex64 [H, M] in host memory."""
+    import numpy as np
+    arr = np.ascontiguousarray(lam_host, dtype=np.complex64)
+    _check(lib.ia_check_lambda(ctypes.byref(desc), arr.ctypes.data_as(ctypes.c_void_p)),
+           "ia_check_lambda")
+
+
+def ia_prefill_fwd(desc: IADesc, q, k, v, lam, beta, state, o, workspace, stream=None):
+    _dense(q, k, v, lam, beta, o, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.ia_prefill_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(lam),
+                              _ptr(beta), _state(state), _ptr(o), _ptr(workspace), ws_bytes,
+                              _stream(stream)), "ia_prefill_fwd")
+
+
+def ia_decode_step(desc: IADesc, q_t, k_t, v_t, lam, beta, state, o_t, stream=None):
+    _dense(q_t, k_t, v_t, lam, beta, o_t)
+    _check(lib.ia_decode_step(ctypes.byref(desc), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(lam),
+                              _ptr(beta), _state(state), _ptr(o_t), _stream(stream)),
+           "ia_decode_step")
+
+
+# ---------------------------------------------------------------- conveniences (torch alloc)
+
+def new_state(B, H, M, F, Dv, device="cuda", stream=None, zero=True):
+    import torch
+    st = (torch.empty((B, H, M, F), dtype=torch.complex64, device=device),
+          torch.empty((B, H, M, Dv), dtype=torch.complex64, device=device),
+          torch.empty((B, H, M), dtype=torch.complex64, device=device))
+    if zero:
+        ia_state_init(make_desc(B, H, 1, F, Dv, M), st, stream)
+    return st
+
+
+def prefill(q, k, v, lam, beta, state=None, out_dtype=None, bidir=False, chunk=0,
+            den_clamp=1e-6, want_output=True, stream=None, workspace=None):
+    """Allocate o (and the workspace) with torch and run ia_prefill_fwd; returns o."""
+    import torch
+    B, N, H, F = q.shape
+    Dv, M = v.shape[3], lam.shape[1]
+    out_dtype = q.dtype if out_dtype is None else out_dtype
+    desc = make_desc(B, H, N, F, Dv, M, dtype_code(q.dtype), dtype_code(out_dtype), den_clamp,
+                     bidir, chunk)
+    o = torch.empty((B, N, H, Dv), dtype=out_dtype, device=q.device) if want_output else None
+    if workspace is None:
+        nb = ia_prefill_workspace_bytes(desc)
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device) if nb else None
+    ia_prefill_fwd(desc, q, k, v, lam, beta, state, o, workspace, stream)
+    return o
+
+
+def decode(q_t, k_t, v_t, lam, beta, state, out_dtype=None,
+           den_clamp=1e-6, stream=None, o_t=None):
+    """One decode step for every (b,h); allocates o_t unless given; returns o_t."""
+    import torch
+    B, H, F = q_t.shape
+    Dv, M = v_t.shape[2], lam.shape[1]
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    desc = make_desc(B, H, 1, F, Dv, M, dtype_code(q_t.dtype), dtype_code(out_dtype), den_clamp)
+    if o_t is None:
+        o_t = torch.empty((B, H, Dv), dtype=out_dtype, device=q_t.device)
+    ia_decode_step(desc, q_t, k_t, v_t, lam, beta, state, o_t, stream)
+    return o_t

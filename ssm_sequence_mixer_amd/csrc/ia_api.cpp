@@ -1,0 +1,265 @@
+// ia_api.cpp — the C ABI of libia.so: host-side validation, workspace layout and dispatch.
+// Every check runs before anything is enqueued; no call synchronises, allocates or prints.
+#include "ia.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "ia_kernels.hpp"
+
+namespace {
+
+size_t esize(int dt) { return dt == IA_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range rng(const void* p, size_t bytes) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return {a, a + bytes};
+}
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+// Checks shared by every call on the descriptor's sizes and codes.
+ia_status check_desc(const ia_desc* d, bool need_n) {
+  if (!d) return IA_ERR_NULL;
+  if (d->B <= 0 || d->H <= 0 || d->F <= 0 || d->Dv <= 0 || d->M <= 0) return IA_ERR_SHAPE;
+  if (need_n && d->N <= 0) return IA_ERR_SHAPE;
+  if (d->F % 16 || d->Dv % 16 || d->M % 16) return IA_ERR_UNSUPPORTED;
+  if (d->F > ia::kMaxDim || d->Dv > ia::kMaxDim || d->M > ia::kMaxModes)
+    return IA_ERR_UNSUPPORTED;
+  if ((d->in_dtype != IA_F32 && d->in_dtype != IA_BF16) ||
+      (d->out_dtype != IA_F32 && d->out_dtype != IA_BF16))
+    return IA_ERR_DTYPE;
+  if (!(std::isfinite(d->den_clamp) && d->den_clamp > 0.f)) return IA_ERR_DOMAIN;
+  if (d->flags & ~IA_FLAG_BIDIR) return IA_ERR_UNSUPPORTED;
+  if (d->chunk != 0 && d->chunk != 32 && d->chunk != 64) return IA_ERR_UNSUPPORTED;
+  // Index arithmetic in the kernels is 64-bit for element offsets; keep grid sizes sane.
+  const double slices = double(d->B) * d->H;
+  if (slices > 1e7 || (need_n && double(d->N) * slices * (d->F + d->Dv) > 9e18))
+    return IA_ERR_SHAPE;
+  return IA_OK;
+}
+
+size_t state_u_bytes(const ia_desc* d) { return size_t(d->B) * d->H * d->M * d->F * 8; }
+size_t state_g_bytes(const ia_desc* d) { return size_t(d->B) * d->H * d->M * d->Dv * 8; }
+size_t state_e_bytes(const ia_desc* d) { return size_t(d->B) * d->H * d->M * 8; }
+size_t state_bytes(const ia_desc* d) {
+  return state_u_bytes(d) + state_g_bytes(d) + state_e_bytes(d);
+}
+
+size_t round_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+ia_status check_state(const ia_desc* d, const ia_state* st) {
+  if (!st || !st->U || !st->Gamma || !st->eta) return IA_ERR_NULL;
+  if (!aligned16(st->U) || !aligned16(st->Gamma) || !aligned16(st->eta)) return IA_ERR_ALIGN;
+  Range u = rng(st->U, state_u_bytes(d)), g = rng(st->Gamma, state_g_bytes(d)),
+        e = rng(st->eta, state_e_bytes(d));
+  if (overlap(u, g) || overlap(u, e) || overlap(g, e)) return IA_ERR_ALIAS;
+  return IA_OK;
+}
+
+// Workspace of the fp32 (token-sequential) prefill path.
+struct ScanWorkspace {
+  size_t state_off, acc_off, bytes;
+};
+
+ScanWorkspace scan_workspace(const ia_desc* d, bool have_state) {
+  ScanWorkspace w{0, 0, 0};
+  const bool bidir = d->flags & IA_FLAG_BIDIR;
+  if (!have_state || bidir) {
+    w.state_off = 0;
+    w.bytes = round_up(state_bytes(d));
+  }
+  if (bidir) {
+    w.acc_off = w.bytes;
+    w.bytes += round_up(size_t(d->B) * d->N * d->H * d->Dv * 4);
+  }
+  return w;
+}
+
+// Text of the HIP error behind the calling thread's most recent IA_ERR_LAUNCH.
+thread_local const char* t_launch_error = "no launch error";
+
+ia_status launch_status(hipError_t e) {
+  if (e == hipSuccess) return IA_OK;
+  t_launch_error = hipGetErrorString(e);
+  return IA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ia_status_string(ia_status s) {
+  switch (s) {
+    case IA_OK: return "IA_OK";
+    case IA_ERR_NULL: return "IA_ERR_NULL: a required pointer is NULL";
+    case IA_ERR_SHAPE: return "IA_ERR_SHAPE: a size is out of range";
+    case IA_ERR_DTYPE: return "IA_ERR_DTYPE: unknown dtype code";
+    case IA_ERR_ALIGN: return "IA_ERR_ALIGN: a device pointer is not 16-byte aligned";
+    case IA_ERR_ALIAS: return "IA_ERR_ALIAS: an output overlaps an input or another output";
+    case IA_ERR_DOMAIN: return "IA_ERR_DOMAIN: a parameter is outside its domain";
+    case IA_ERR_UNSUPPORTED: return "IA_ERR_UNSUPPORTED: combination not implemented";
+    case IA_ERR_LAUNCH: return "IA_ERR_LAUNCH: the HIP runtime refused a launch";
+    case IA_ERR_WORKSPACE: return "IA_ERR_WORKSPACE: workspace missing or too small";
+  }
+  return "unknown ia_status";
+}
+
+const char* ia_last_launch_error(void) { return t_launch_error; }
+
+ia_status ia_check_lambda(const ia_desc* d, const void* lambda_host) {
+  ia_status s = check_desc(d, false);
+  if (s != IA_OK) return s;
+  if (!lambda_host) return IA_ERR_NULL;
+  const float* l = static_cast<const float*>(lambda_host);
+  const int chunk = d->chunk ? d->chunk : 64;
+  for (long i = 0; i < long(d->H) * d->M; ++i) {
+    const double mag = std::hypot(double(l[2 * i]), double(l[2 * i + 1]));
+    if (!(mag > 0.0 && mag <= 1.0 + 1e-6)) return IA_ERR_DOMAIN;
+    if (d->in_dtype == IA_BF16 && std::pow(mag, chunk - 1) < std::ldexp(1.0, -8))
+      return IA_ERR_DOMAIN;
+  }
+  return IA_OK;
+}
+
+ia_status ia_state_init(const ia_desc* d, ia_state* st, void* stream) {
+  ia_status s = check_desc(d, false);
+  if (s != IA_OK) return s;
+  if ((s = check_state(d, st)) != IA_OK) return s;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = ia::launch_fill_zero(st->U, state_u_bytes(d), hs);
+  if (e == hipSuccess) e = ia::launch_fill_zero(st->Gamma, state_g_bytes(d), hs);
+  if (e == hipSuccess) e = ia::launch_fill_zero(st->eta, state_e_bytes(d), hs);
+  return launch_status(e);
+}
+
+size_t ia_prefill_workspace_bytes(const ia_desc* d) {
+  if (check_desc(d, true) != IA_OK) return 0;
+  // The state-less case needs the larger workspace; callers size for it.
+  return scan_workspace(d, false).bytes;
+}
+
+ia_status ia_prefill_fwd(const ia_desc* d, const void* q, const void* k, const void* v,
+                         const void* lambda, const void* beta, ia_state* st, void* o,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  ia_status s = check_desc(d, true);
+  if (s != IA_OK) return s;
+  const bool bidir = d->flags & IA_FLAG_BIDIR;
+  if (!q || !k || !v || !lambda || !beta) return IA_ERR_NULL;
+  if (!o && !st) return IA_ERR_NULL;
+  if (bidir && st) return IA_ERR_UNSUPPORTED;
+  if (bidir && !o) return IA_ERR_NULL;
+  for (const void* p : {q, k, v, lambda, beta})
+    if (!aligned16(p)) return IA_ERR_ALIGN;
+  if (o && !aligned16(o)) return IA_ERR_ALIGN;
+  if (st && (s = check_state(d, st)) != IA_OK) return s;
+
+  const size_t tok = size_t(d->B) * d->N * d->H;
+  const Range rq = rng(q, tok * d->F * esize(d->in_dtype));
+  const Range rk = rng(k, tok * d->F * esize(d->in_dtype));
+  const Range rv = rng(v, tok * d->Dv * esize(d->in_dtype));
+  const Range rl = rng(lambda, size_t(d->H) * d->M * 8);
+  const Range rb = rng(beta, size_t(d->H) * d->M * 8);
+  const Range ins[] = {rq, rk, rv, rl, rb};
+  if (o) {
+    const Range ro = rng(o, tok * d->Dv * esize(d->out_dtype));
+    for (const Range& r : ins)
+      if (overlap(ro, r)) return IA_ERR_ALIAS;
+    if (st && (overlap(ro, rng(st->U, state_u_bytes(d))) ||
+               overlap(ro, rng(st->Gamma, state_g_bytes(d))) ||
+               overlap(ro, rng(st->eta, state_e_bytes(d)))))
+      return IA_ERR_ALIAS;
+  }
+  if (st) {
+    const Range sr[] = {rng(st->U, state_u_bytes(d)), rng(st->Gamma, state_g_bytes(d)),
+                        rng(st->eta, state_e_bytes(d))};
+    for (const Range& a : sr)
+      for (const Range& r : ins)
+        if (overlap(a, r)) return IA_ERR_ALIAS;
+  }
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+
+  // fp32 path: token-sequential recurrence.
+  const ScanWorkspace w = scan_workspace(d, st != nullptr);
+  if (w.bytes) {
+    if (!workspace || ws_bytes < w.bytes) return IA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return IA_ERR_ALIGN;
+    const Range rw = rng(workspace, w.bytes);
+    for (const Range& r : ins)
+      if (overlap(rw, r)) return IA_ERR_ALIAS;
+    if (o && overlap(rw, rng(o, tok * d->Dv * esize(d->out_dtype)))) return IA_ERR_ALIAS;
+  }
+  char* ws = static_cast<char*>(workspace);
+  float2 *U, *G, *E;
+  if (st && !bidir) {
+    U = static_cast<float2*>(st->U);
+    G = static_cast<float2*>(st->Gamma);
+    E = static_cast<float2*>(st->eta);
+  } else {
+    U = reinterpret_cast<float2*>(ws + w.state_off);
+    G = reinterpret_cast<float2*>(ws + w.state_off + state_u_bytes(d));
+    E = reinterpret_cast<float2*>(ws + w.state_off + state_u_bytes(d) + state_g_bytes(d));
+    hipError_t e = ia::launch_fill_zero(ws + w.state_off, state_bytes(d), hs);
+    if (e != hipSuccess) return launch_status(e);
+  }
+  ia::ScanArgs a{q, k, v, static_cast<const float2*>(lambda), static_cast<const float2*>(beta),
+                 U, G, E, o, nullptr, d->B, d->H, d->N, d->F, d->Dv, d->M,
+                 d->in_dtype == IA_BF16, d->out_dtype == IA_BF16, d->den_clamp, 0};
+  if (!bidir) return launch_status(ia::launch_scan_prefill(a, hs));
+
+  float* acc = reinterpret_cast<float*>(ws + w.acc_off);
+  a.o = acc;
+  a.out_bf16 = 0;
+  hipError_t e = ia::launch_scan_prefill(a, hs);
+  if (e == hipSuccess) e = ia::launch_fill_zero(ws + w.state_off, state_bytes(d), hs);
+  if (e == hipSuccess) {
+    a.o = o;
+    a.out_bf16 = d->out_dtype == IA_BF16;
+    a.acc_in = acc;
+    a.reverse = 1;
+    e = ia::launch_scan_prefill(a, hs);
+  }
+  return launch_status(e);
+}
+
+ia_status ia_decode_step(const ia_desc* d, const void* q_t, const void* k_t, const void* v_t,
+                         const void* lambda, const void* beta, ia_state* st, void* o_t,
+                         void* stream) {
+  ia_status s = check_desc(d, false);
+  if (s != IA_OK) return s;
+  if (d->flags & IA_FLAG_BIDIR) return IA_ERR_UNSUPPORTED;
+  if (!q_t || !k_t || !v_t || !lambda || !beta || !o_t) return IA_ERR_NULL;
+  if ((s = check_state(d, st)) != IA_OK) return s;
+  for (const void* p : {q_t, k_t, v_t, lambda, beta, static_cast<const void*>(o_t)})
+    if (!aligned16(p)) return IA_ERR_ALIGN;
+  const size_t bh = size_t(d->B) * d->H;
+  const Range ins[] = {rng(q_t, bh * d->F * esize(d->in_dtype)),
+                       rng(k_t, bh * d->F * esize(d->in_dtype)),
+                       rng(v_t, bh * d->Dv * esize(d->in_dtype)),
+                       rng(lambda, size_t(d->H) * d->M * 8), rng(beta, size_t(d->H) * d->M * 8)};
+  const Range outs[] = {rng(o_t, bh * d->Dv * esize(d->out_dtype)),
+                        rng(st->U, state_u_bytes(d)), rng(st->Gamma, state_g_bytes(d)),
+                        rng(st->eta, state_e_bytes(d))};
+  for (const Range& a : outs)
+    for (const Range& r : ins)
+      if (overlap(a, r)) return IA_ERR_ALIAS;
+  for (int i = 1; i < 4; ++i)
+    if (overlap(outs[0], outs[i])) return IA_ERR_ALIAS;
+  ia::DecodeArgs a{q_t, k_t, v_t, static_cast<const float2*>(lambda),
+                   static_cast<const float2*>(beta), static_cast<float2*>(st->U),
+                   static_cast<float2*>(st->Gamma), static_cast<float2*>(st->eta), o_t,
+                   d->B, d->H, d->F, d->Dv, d->M, d->in_dtype == IA_BF16,
+                   d->out_dtype == IA_BF16, d->den_clamp};
+  return launch_status(ia::launch_decode_step(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

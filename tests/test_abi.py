@@ -1,0 +1,159 @@
+"""C ABI of libia.so, host side only (no GPU): exports and every validation path.
+
+Each call here fails validation, which the library finishes before it enqueues anything,
+so the fake device addresses below are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import ssm_sequence_mixer_amd as ia
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "ia.h")
+P = ctypes.c_void_p
+BASE = 1 << 32            # fake, 16-byte aligned device addresses, far apart
+GAP = 1 << 28
+
+
+def addr(i, off=0):
+    return P(BASE + i * GAP + off)
+
+
+def desc(**kw):
+    d = dict(B=2, H=3, N=70, F=32, Dv=16, M=16, in_dtype=ia.IA_BF16, out_dtype=ia.IA_F32,
+             den_clamp=1e-6, bidir=False, chunk=0)
+    d.update(kw)
+    return ia.make_desc(**d)
+
+
+def state(i=10):
+    return ctypes.pointer(ia.IAState(addr(i).value, addr(i + 1).value, addr(i + 2).value))
+
+
+def prefill(d, q=None, k=None, v=None, lam=None, beta=None, st="default", o=None, ws=None,
+            ws_bytes=1 << 40):
+    q = addr(0) if q is None else q
+    k = addr(1) if k is None else k
+    v = addr(2) if v is None else v
+    lam = addr(3) if lam is None else lam
+    beta = addr(4) if beta is None else beta
+    st = state() if isinstance(st, str) else st
+    o = addr(5) if o is None else o
+    ws = addr(6) if ws is None else ws
+    return ia.lib.ia_prefill_fwd(ctypes.byref(d) if d is not None else None, q, k, v, lam, beta,
+                                 st, o, ws, ws_bytes, None)
+
+
+def test_every_declared_symbol_is_exported():
+    decl = set(re.findall(r"^\s*(?:ia_status|size_t|const char\*)\s+(ia_\w+)\s*\(",
+                          open(HEADER).read(), flags=re.M))
+    assert decl == set(ia.EXPORTS)
+    for name in decl:
+        assert hasattr(ia.lib, name), name
+
+
+def test_status_strings():
+    for code, name in enumerate(ia.STATUS):
+        assert ia.lib.ia_status_string(code).decode().startswith(name)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("B", 0, 2), ("H", -1, 2), ("N", 0, 2), ("F", 0, 2), ("Dv", 0, 2), ("M", 0, 2),
+    ("F", 24, 7), ("Dv", 8, 7), ("M", 20, 7), ("F", 272, 7), ("Dv", 512, 7), ("M", 144, 7),
+    ("in_dtype", 2, 3), ("out_dtype", -1, 3),
+    ("den_clamp", 0.0, 6), ("den_clamp", -1e-6, 6), ("den_clamp", float("nan"), 6),
+    ("den_clamp", float("inf"), 6), ("chunk", 48, 7), ("chunk", 16, 7)])
+def test_desc_validation(field, value, status):
+    d = desc()
+    setattr(d, field, value)
+    assert prefill(d) == status
+    if field not in ("N",):
+        assert ia.lib.ia_decode_step(ctypes.byref(d), addr(0), addr(1), addr(2), addr(3),
+                                     addr(4), state(), addr(5), None) == status
+        assert ia.lib.ia_state_init(ctypes.byref(d), state(), None) == status
+    assert ia.lib.ia_prefill_workspace_bytes(ctypes.byref(d)) == 0
+
+
+def test_unknown_flag_bits():
+    d = desc()
+    d.flags = 2
+    assert prefill(d) == 7
+
+
+def test_null_pointers():
+    assert prefill(None) == 1
+    for kw in ("q", "k", "v", "lam", "beta"):
+        assert prefill(desc(), **{kw: P(0)}) == 1, kw
+    # o and state both absent: nothing to compute
+    assert prefill(desc(), st=None, o=P(0)) == 1
+    assert prefill(desc(), st=ctypes.pointer(ia.IAState(addr(10).value, 0, addr(12).value))) == 1
+    assert ia.lib.ia_state_init(ctypes.byref(desc()), None, None) == 1
+    assert ia.lib.ia_decode_step(ctypes.byref(desc()), addr(0), addr(1), addr(2), addr(3),
+                                 addr(4), None, addr(5), None) == 1
+    assert ia.lib.ia_decode_step(ctypes.byref(desc()), addr(0), addr(1), addr(2), addr(3),
+                                 addr(4), state(), P(0), None) == 1
+
+
+def test_alignment():
+    for kw in ("q", "k", "v", "lam", "beta", "o"):
+        assert prefill(desc(), **{kw: addr({"q": 0, "k": 1, "v": 2, "lam": 3, "beta": 4,
+                                            "o": 5}[kw], 8)}) == 4, kw
+    bad = ctypes.pointer(ia.IAState(addr(10, 4).value, addr(11).value, addr(12).value))
+    assert prefill(desc(), st=bad) == 4
+    assert ia.lib.ia_state_init(ctypes.byref(desc()), bad, None) == 4
+
+
+def test_aliasing():
+    d = desc()
+    # o overlapping each input, and the state
+    for i in range(5):
+        assert prefill(d, o=addr(i, 16)) == 5, i
+    assert prefill(d, o=addr(10, 32)) == 5
+    # state overlapping an input
+    st = ctypes.pointer(ia.IAState(addr(0, 64).value, addr(11).value, addr(12).value))
+    assert prefill(d, st=st) == 5
+    # state buffers overlapping each other
+    st = ctypes.pointer(ia.IAState(addr(10).value, addr(10, 256).value, addr(12).value))
+    assert prefill(d, st=st) == 5
+    # decode: o_t overlapping the state
+    assert ia.lib.ia_decode_step(ctypes.byref(d), addr(0), addr(1), addr(2), addr(3), addr(4),
+                                 state(), addr(11, 16), None) == 5
+
+
+def test_bidir_rules():
+    d = desc(bidir=True)
+    assert prefill(d) == 7                    # a state with BIDIR
+    assert prefill(d, st=None, o=P(0)) == 1   # BIDIR needs an output
+    assert ia.lib.ia_decode_step(ctypes.byref(d), addr(0), addr(1), addr(2), addr(3), addr(4),
+                                 state(), addr(5), None) == 7
+
+
+def test_workspace_checks():
+    for in_dtype in (ia.IA_F32, ia.IA_BF16):
+        d = desc(in_dtype=in_dtype)
+        need = ia.lib.ia_prefill_workspace_bytes(ctypes.byref(d))
+        assert need > 0
+        assert prefill(d, st=None, ws=P(0)) == 9
+        assert prefill(d, st=None, ws_bytes=need - 1) == 9
+        # workspace overlapping an input
+        assert prefill(d, st=None, ws=addr(1, 32)) in (5,)
+
+
+def test_check_lambda_host():
+    d = desc(H=1, M=16)
+    ok = np.exp(0.05 * (-0.5 + 1j * np.pi * np.arange(16))).astype(np.complex64)[None]
+    ia.ia_check_lambda(d, ok)
+    for bad in (np.zeros(16), 1.1 * np.ones(16), 0.5 * np.ones(16)):
+        with pytest.raises(ia.IAError) as e:
+            ia.ia_check_lambda(d, bad.astype(np.complex64)[None])
+        assert e.value.status == 6
+    # fast modes are fine on the fp32 path, which does not factorise the decay
+    ia.ia_check_lambda(desc(H=1, M=16, in_dtype=ia.IA_F32), (0.5 * np.ones(16, np.complex64))[None])
+    # chunk 32 widens the bf16 domain
+    mid = (0.9 * np.ones(16, np.complex64))[None]
+    with pytest.raises(ia.IAError):
+        ia.ia_check_lambda(desc(H=1, M=16), mid)
+    ia.ia_check_lambda(desc(H=1, M=16, chunk=32), mid)

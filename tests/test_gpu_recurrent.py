@@ -1,0 +1,156 @@
+"""GPU parity of the token-by-token kernels (decode step, fp32 prefill) against the oracle.
+
+All inputs are seeded (ia_workloads); the oracle receives the very values the GPU receives.
+"""
+import numpy as np
+import pytest
+
+import ia_workloads as W
+import oracle
+from helpers import TOL_BF16, TOL_F32, dev, host, rowrel, state_rel, tag
+
+pytestmark = pytest.mark.gpu
+
+
+def _lib():
+    import ssm_sequence_mixer_amd as ia
+    return ia
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _oracle_state(B, H, F, D, M, lam, beta, seed):
+    """A non-trivial state: the oracle's state after 9 random tokens."""
+    inp = W.make_inputs(B, H, 9, F, D, M, dtype="f32", seed=seed, std=0.5)
+    _, _, _, st = oracle.prefill(inp["q"], inp["k"], inp["v"], lam, beta)
+    return st
+
+
+@pytest.mark.parametrize("in_dtype,out_dtype", [("f32", "f32"), ("bf16", "f32"), ("bf16", "bf16")])
+def test_decode_steps_match_oracle(in_dtype, out_dtype):
+    torch = _torch()
+    ia = _lib()
+    B, H, F, D, M, steps = 2, 3, 32, 48, 16, 5
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    inp = W.make_inputs(B, H, steps, F, D, M, dtype=in_dtype, seed=11)
+    lam, beta = inp["lam"], inp["beta"] * np.complex64(0.7 - 0.2j)
+    st_ref = _oracle_state(B, H, F, D, M, lam, beta, seed=12)
+    st = tuple(dev(s) for s in st_ref)
+    st_ref = tuple(host(s) for s in st)  # both sides continue from the complex64 state
+    for t in range(steps):
+        tag(f"decode step {t} {in_dtype}->{out_dtype}")
+        o = ia.decode(dev(inp["q"][:, t], tdt[in_dtype]), dev(inp["k"][:, t], tdt[in_dtype]),
+                      dev(inp["v"][:, t], tdt[in_dtype]), dev(lam), dev(beta), st,
+                      out_dtype=tdt[out_dtype])
+        o_ref, st_ref = oracle.decode_step(inp["q"][:, t], inp["k"][:, t], inp["v"][:, t], lam,
+                                           beta, st_ref)
+        torch.cuda.synchronize()
+        tol = TOL_F32 if out_dtype == "f32" else TOL_BF16
+        assert rowrel(host(o), o_ref) < tol
+        assert state_rel(tuple(host(s) for s in st), st_ref) < TOL_F32
+
+
+def test_fp32_prefill_tiny_workload():
+    """The tiny fp32 workload: B=H=1, N=256, F=Dv=M=16, dt=0.01, beta=1; outputs and state."""
+    torch = _torch()
+    ia = _lib()
+    inp = W.tiny()
+    tag("fp32 prefill tiny")
+    st = ia.new_state(1, 1, 16, 16, 16)
+    o = ia.prefill(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["lam"]),
+                   dev(inp["beta"]), state=st, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, _, den_ref, st_ref = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["lam"],
+                                               inp["beta"])
+    assert np.all(den_ref > 10 * 1e-6)
+    assert rowrel(host(o), o_ref) < TOL_F32
+    assert state_rel(tuple(host(s) for s in st), st_ref) < TOL_F32
+
+
+@pytest.mark.parametrize("N", [1, 63, 130])
+def test_fp32_prefill_ragged_and_resume(N):
+    torch = _torch()
+    ia = _lib()
+    B, H, F, D, M = 2, 2, 32, 16, 32
+    inp = W.make_inputs(B, H, N, F, D, M, dtype="f32", seed=20 + N)
+    q, k, v = (dev(inp[n]) for n in "qkv")
+    lam, beta = dev(inp["lam"]), dev(inp["beta"])
+    tag(f"fp32 prefill N={N}")
+    st = ia.new_state(B, H, M, F, D)
+    o = ia.prefill(q, k, v, lam, beta, state=st, out_dtype=torch.float32)
+    o_ref, _, _, st_ref = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"])
+    torch.cuda.synchronize()
+    assert rowrel(host(o), o_ref) < TOL_F32
+    assert state_rel(tuple(host(s) for s in st), st_ref) < TOL_F32
+    # state-only prefill of a prefix, then the rest from that state, equals the whole
+    if N > 1:
+        s = N // 2
+        st2 = ia.new_state(B, H, M, F, D)
+        ia.prefill(q[:, :s].contiguous(), k[:, :s].contiguous(), v[:, :s].contiguous(), lam,
+                   beta, state=st2, want_output=False)
+        o2 = ia.prefill(q[:, s:].contiguous(), k[:, s:].contiguous(), v[:, s:].contiguous(),
+                        lam, beta, state=st2, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert rowrel(host(o2), o_ref[:, s:]) < TOL_F32
+        assert state_rel(tuple(host(x) for x in st2), st_ref) < TOL_F32
+
+
+def test_fp32_bidirectional():
+    torch = _torch()
+    ia = _lib()
+    B, H, N, F, D, M = 1, 2, 45, 16, 32, 16
+    inp = W.make_inputs(B, H, N, F, D, M, dtype="f32", seed=31)
+    tag("fp32 bidir")
+    o = ia.prefill(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["lam"]),
+                   dev(inp["beta"]), bidir=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref = oracle.bidir(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"])
+    assert rowrel(host(o), o_ref) < TOL_F32
+
+
+def test_decode_forced_clamp():
+    """beta = i with real lambda drives Re(den) below zero: o_t = num / clamp."""
+    torch = _torch()
+    ia = _lib()
+    B, H, F, D, M = 1, 1, 16, 16, 16
+    lam = np.full((H, M), 0.9, np.complex64)
+    beta = np.full((H, M), 1j, np.complex64)
+    inp = W.make_inputs(B, H, 3, F, D, M, dtype="f32", seed=41)
+    st = ia.new_state(B, H, M, F, D)
+    st_ref = tuple(np.zeros(s, np.complex128) for s in ((B, H, M, F), (B, H, M, D), (B, H, M)))
+    for t in range(3):
+        tag(f"decode clamp step {t}")
+        o = ia.decode(dev(inp["q"][:, t]), dev(inp["k"][:, t]), dev(inp["v"][:, t]), dev(lam),
+                      dev(beta), st)
+        o_ref, st_ref = oracle.decode_step(inp["q"][:, t], inp["k"][:, t], inp["v"][:, t], lam,
+                                           beta, st_ref)
+        torch.cuda.synchronize()
+        assert np.all(np.abs(o_ref) > 1e3)  # the clamp was hit
+        assert rowrel(host(o), o_ref) < TOL_F32
+
+
+def test_decode_1p3b_shape_batch16():
+    """Decode at the 1.3B-shaped layer (H=16, F=Dv=128, M=64), batch 16, from a prefilled state."""
+    torch = _torch()
+    ia = _lib()
+    wl = W.decode(16, steps=4, prefix=32)
+    pre, stp = wl["prefix"], wl["steps"]
+    lam, beta = wl["lam"], wl["beta"]
+    tag("decode 1.3b B=16 prefix")
+    st = ia.new_state(16, 16, 64, 128, 128)
+    ia.prefill(dev(pre["q"], torch.bfloat16), dev(pre["k"], torch.bfloat16),
+               dev(pre["v"], torch.bfloat16), dev(lam), dev(beta), state=st, want_output=False)
+    _, _, _, st_ref = oracle.prefill(pre["q"], pre["k"], pre["v"], lam, beta, threads=8)
+    torch.cuda.synchronize()
+    assert state_rel(tuple(host(s) for s in st), st_ref) < TOL_F32
+    for t in range(4):
+        tag(f"decode 1.3b B=16 step {t}")
+        o = ia.decode(dev(stp["q"][t], torch.bfloat16), dev(stp["k"][t], torch.bfloat16),
+                      dev(stp["v"][t], torch.bfloat16), dev(lam), dev(beta), st)
+        o_ref, st_ref = oracle.decode_step(stp["q"][t], stp["k"][t], stp["v"][t], lam, beta,
+                                           st_ref)
+        torch.cuda.synchronize()
+        assert rowrel(host(o), o_ref) < TOL_F32
