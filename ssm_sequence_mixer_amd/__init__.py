@@ -74,13 +74,21 @@ lib.ia_prefill_fwd.argtypes = [_D, _P, _P, _P, _P, _P, _S, _P, _P, ctypes.c_size
 lib.ia_prefill_fwd.restype = ctypes.c_int
 lib.ia_decode_step.argtypes = [_D, _P, _P, _P, _P, _P, _S, _P, _P]
 lib.ia_decode_step.restype = ctypes.c_int
+lib.ia_prefill_fwd_profiled.argtypes = [_D, _P, _P, _P, _P, _P, _S, _P, _P, ctypes.c_size_t,
+                                        _P, ctypes.POINTER(ctypes.c_void_p),
+                                        ctypes.POINTER(ctypes.c_int), ctypes.c_int,
+                                        ctypes.POINTER(ctypes.c_int)]
+lib.ia_prefill_fwd_profiled.restype = ctypes.c_int
 lib.ia_status_string.argtypes = [ctypes.c_int]
 lib.ia_status_string.restype = ctypes.c_char_p
 lib.ia_last_launch_error.argtypes = []
 lib.ia_last_launch_error.restype = ctypes.c_char_p
 
 EXPORTS = ("ia_state_init", "ia_prefill_workspace_bytes", "ia_check_lambda", "ia_prefill_fwd",
-           "ia_decode_step", "ia_status_string", "ia_last_launch_error")
+           "ia_prefill_fwd_profiled", "ia_decode_step", "ia_status_string",
+           "ia_last_launch_error")
+KIND_NAMES = {0: "fill", 1: "scan", 2: "tables", 3: "summary", 4: "carry", 5: "chunk",
+              6: "decode"}
 
 
 def make_desc(B, H, N, F, Dv, M, in_dtype=IA_BF16, out_dtype=IA_F32, den_clamp=1e-6,
@@ -155,6 +163,23 @@ def ia_prefill_fwd(desc: IADesc, q, k, v, lam, beta, state, o, workspace, stream
     _check(lib.ia_prefill_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(lam),
                               _ptr(beta), _state(state), _ptr(o), _ptr(workspace), ws_bytes,
                               _stream(stream)), "ia_prefill_fwd")
+
+
+def ia_prefill_fwd_profiled(desc: IADesc, q, k, v, lam, beta, state, o, workspace, events,
+                            stream=None):
+    """As ia_prefill_fwd; `events` is a list of 2*n raw hipEvent_t handles.  Returns the kind
+    codes of the launches recorded (events[2i], events[2i+1] bracket launch i)."""
+    _dense(q, k, v, lam, beta, o, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    n = len(events) // 2
+    ev = (ctypes.c_void_p * (2 * n))(*events)
+    kinds = (ctypes.c_int * max(n, 1))()
+    used = ctypes.c_int(0)
+    _check(lib.ia_prefill_fwd_profiled(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(lam),
+                                       _ptr(beta), _state(state), _ptr(o), _ptr(workspace),
+                                       ws_bytes, _stream(stream), ev, kinds, n,
+                                       ctypes.byref(used)), "ia_prefill_fwd_profiled")
+    return [kinds[i] for i in range(used.value)]
 
 
 def ia_decode_step(desc: IADesc, q_t, k_t, v_t, lam, beta, state, o_t, stream=None):

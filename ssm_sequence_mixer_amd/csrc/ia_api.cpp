@@ -84,6 +84,38 @@ ScanWorkspace scan_workspace(const ia_desc* d, bool have_state) {
   return w;
 }
 
+// Workspace and segmentation of the chunked (bf16, MFMA) path.  Segments cut each sequence so
+// that B*H*segments workgroups cover the 256 compute units about once.
+constexpr int kTargetWorkgroups = 256;
+
+struct ChunkPlan {
+  int C, G, seg_chunks;
+  size_t tables_off, slots_off, acc_off, bytes;
+};
+
+bool use_chunk_path(const ia_desc* d) {
+  return d->in_dtype == IA_BF16 && ia::chunk_supported(d->F, d->Dv, d->M);
+}
+
+ChunkPlan chunk_plan(const ia_desc* d) {
+  ChunkPlan p{};
+  p.C = d->chunk ? d->chunk : 64;
+  const int n_chunks = (d->N + p.C - 1) / p.C;
+  const long seqs = long(d->B) * d->H;
+  long G = (kTargetWorkgroups + seqs - 1) / seqs;
+  if (G > n_chunks) G = n_chunks;
+  if (G < 1) G = 1;
+  p.seg_chunks = int((n_chunks + G - 1) / G);
+  p.G = (n_chunks + p.seg_chunks - 1) / p.seg_chunks;
+  p.tables_off = 0;
+  p.bytes = round_up(size_t(d->H) * ia::chunk_table_bytes(p.C, d->M));
+  p.slots_off = p.bytes;
+  if (p.G > 1) p.bytes += round_up(size_t(seqs) * p.G * d->M * (d->F + d->Dv + 1) * 8);
+  p.acc_off = p.bytes;
+  if (d->flags & IA_FLAG_BIDIR) p.bytes += round_up(size_t(d->B) * d->N * d->H * d->Dv * 4);
+  return p;
+}
+
 // Text of the HIP error behind the calling thread's most recent IA_ERR_LAUNCH.
 thread_local const char* t_launch_error = "no launch error";
 
@@ -94,6 +126,10 @@ ia_status launch_status(hipError_t e) {
 }
 
 }  // namespace
+
+namespace ia {
+thread_local ProfileSink* g_profile = nullptr;
+}
 
 extern "C" {
 
@@ -143,6 +179,7 @@ ia_status ia_state_init(const ia_desc* d, ia_state* st, void* stream) {
 
 size_t ia_prefill_workspace_bytes(const ia_desc* d) {
   if (check_desc(d, true) != IA_OK) return 0;
+  if (use_chunk_path(d)) return chunk_plan(d).bytes;
   // The state-less case needs the larger workspace; callers size for it.
   return scan_workspace(d, false).bytes;
 }
@@ -188,7 +225,55 @@ ia_status ia_prefill_fwd(const ia_desc* d, const void* q, const void* k, const v
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
 
-  // fp32 path: token-sequential recurrence.
+  if (use_chunk_path(d)) {
+    const ChunkPlan pl = chunk_plan(d);
+    if (!workspace || ws_bytes < pl.bytes) return IA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return IA_ERR_ALIGN;
+    const Range rw = rng(workspace, pl.bytes);
+    for (const Range& r : ins)
+      if (overlap(rw, r)) return IA_ERR_ALIAS;
+    if (o && overlap(rw, rng(o, tok * d->Dv * esize(d->out_dtype)))) return IA_ERR_ALIAS;
+    if (st && (overlap(rw, rng(st->U, state_u_bytes(d))) ||
+               overlap(rw, rng(st->Gamma, state_g_bytes(d))) ||
+               overlap(rw, rng(st->eta, state_e_bytes(d)))))
+      return IA_ERR_ALIAS;
+    char* ws = static_cast<char*>(workspace);
+    ia::ChunkPrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.lam = static_cast<const float2*>(lambda);
+    a.beta = static_cast<const float2*>(beta);
+    a.o = o;
+    if (st) {
+      a.U0 = a.U1 = static_cast<float2*>(st->U);
+      a.G0 = a.G1 = static_cast<float2*>(st->Gamma);
+      a.E0 = a.E1 = static_cast<float2*>(st->eta);
+    }
+    a.slots = reinterpret_cast<float2*>(ws + pl.slots_off);
+    a.tables = reinterpret_cast<unsigned char*>(ws + pl.tables_off);
+    a.B = d->B; a.H = d->H; a.N = d->N; a.F = d->F; a.D = d->Dv; a.M = d->M;
+    a.chunk = pl.C;
+    a.segments = pl.G;
+    a.seg_chunks = pl.seg_chunks;
+    a.out_bf16 = d->out_dtype == IA_BF16;
+    a.clamp = d->den_clamp;
+    if (!bidir) return launch_status(ia::launch_chunk_prefill(a, hs));
+    float* acc = reinterpret_cast<float*>(ws + pl.acc_off);
+    a.o = acc;
+    a.out_bf16 = 0;
+    hipError_t e = ia::launch_chunk_prefill(a, hs);
+    if (e == hipSuccess) {
+      a.o = o;
+      a.out_bf16 = d->out_dtype == IA_BF16;
+      a.acc_in = acc;
+      a.reverse = 1;
+      e = ia::launch_chunk_prefill(a, hs);
+    }
+    return launch_status(e);
+  }
+
+  // fp32 path (and bf16 shapes without a chunked instantiation): token-sequential recurrence.
   const ScanWorkspace w = scan_workspace(d, st != nullptr);
   if (w.bytes) {
     if (!workspace || ws_bytes < w.bytes) return IA_ERR_WORKSPACE;
@@ -260,6 +345,23 @@ ia_status ia_decode_step(const ia_desc* d, const void* q_t, const void* k_t, con
                    d->B, d->H, d->F, d->Dv, d->M, d->in_dtype == IA_BF16,
                    d->out_dtype == IA_BF16, d->den_clamp};
   return launch_status(ia::launch_decode_step(a, static_cast<hipStream_t>(stream)));
+}
+
+ia_status ia_prefill_fwd_profiled(const ia_desc* d, const void* q, const void* k,
+                                  const void* v, const void* lambda, const void* beta,
+                                  ia_state* st, void* o, void* workspace, size_t ws_bytes,
+                                  void* stream, void** events, int* kinds, int max_launches,
+                                  int* n_launches) {
+  if (!events || !kinds || !n_launches || max_launches < 0) return IA_ERR_NULL;
+  for (int i = 0; i < 2 * max_launches; ++i)
+    if (!events[i]) return IA_ERR_NULL;
+  ia::ProfileSink sink{events, kinds, max_launches, 0};
+  ia::g_profile = &sink;
+  const ia_status s = ia_prefill_fwd(d, q, k, v, lambda, beta, st, o, workspace, ws_bytes,
+                                     stream);
+  ia::g_profile = nullptr;
+  *n_launches = sink.used;
+  return s;
 }
 
 }  // extern "C"

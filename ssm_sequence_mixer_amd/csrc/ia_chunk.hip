@@ -1,0 +1,253 @@
+// ia_chunk.hip — chunked IA prefill: per-head tables, the segment carry scan, and the
+// host-side dispatch over the kernel instantiations (which live in ia_chunk_f*.hip).
+#include "ia_chunk.hpp"
+
+namespace ia {
+
+#define IA_EXTERN(C, FF, MM)                                                              \
+  extern template hipError_t launch_chunk_t<C, FF, FF, MM>(const ChunkArgs&, int, hipStream_t, \
+                                                           int);
+#define IA_EXTERN_C(C)                                                                    \
+  IA_EXTERN(C, 32, 16) IA_EXTERN(C, 32, 32) IA_EXTERN(C, 32, 64)                          \
+  IA_EXTERN(C, 64, 16) IA_EXTERN(C, 64, 32) IA_EXTERN(C, 64, 64)                          \
+  IA_EXTERN(C, 128, 16) IA_EXTERN(C, 128, 32) IA_EXTERN(C, 128, 64)
+IA_EXTERN_C(32)
+IA_EXTERN_C(64)
+#undef IA_EXTERN_C
+#undef IA_EXTERN
+
+// ---------------------------------------------------------------- per-head tables
+// Once per call, one block per head, one thread per (mode, run of 16 exponents):
+// beta lam^-j in bf16 ([Re;Im] rows) and in scaled fp16 (row j), lam^(2i); per mode
+// lam^(C-1), sum_{j<C} beta lam^-j, the same two for the last chunk's length Lt, and
+// lam^Ls for the segment length Ls.  Each run starts from exp/log and continues by products.
+template <int C, int M>
+__global__ void chunk_tables_kernel(const float2* __restrict__ lam,
+                                    const float2* __restrict__ beta, unsigned char* tables,
+                                    long table_bytes, int Lt, int Ls) {
+  using TL = TableLayout<C, M>;
+  constexpr int RC = TL::RC, RM = TL::RM;
+  constexpr int RUNS = C / 16;
+  const int h = blockIdx.x;
+  unsigned char* tab = tables + (size_t)h * table_bytes;
+  uint16_t* WT = reinterpret_cast<uint16_t*>(tab + TL::oW);
+  uint16_t* Wb = WT + 2 * M * RC;
+  float2* L2 = reinterpret_cast<float2*>(tab + TL::oL2);
+  const int m = threadIdx.x % M, run = threadIdx.x / M;
+  const float2 l = lam[(size_t)h * M + m];
+  const float2 bt = beta[(size_t)h * M + m];
+  __shared__ float s_wmax[M * RUNS];
+
+  // fp16 table exponent: max_j |beta lam^-j| = |beta| |lam|^-(C-1) (|lam| <= 1).
+  const float2 pc1 = cpow_f(l, (float)(C - 1));
+  s_wmax[threadIdx.x] = hypotf(bt.x, bt.y) / hypotf(pc1.x, pc1.y);
+  __syncthreads();
+  float wmax = 0.f;
+  for (int i = 0; i < M * RUNS; ++i) wmax = fmaxf(wmax, s_wmax[i]);
+  const float wscale = pow2_scale(wmax);
+  if (threadIdx.x == 0) *reinterpret_cast<float*>(tab + TL::oSc) = 1.f / wscale;
+
+  const float2 inv = cpow_f(l, -1.f);
+  float2 p = cpow_f(l, -16.f * run);
+  for (int j = 16 * run; j < 16 * run + 16; ++j) {
+    const float re = bt.x * p.x - bt.y * p.y, im = bt.x * p.y + bt.y * p.x;
+    WT[m * RC + j] = f32_to_bf16(re);
+    WT[(M + m) * RC + j] = f32_to_bf16(im);
+    Wb[j * RM + m] = f16_bits(re * wscale);
+    Wb[j * RM + M + m] = f16_bits(im * wscale);
+    p = cmul(p, inv);
+  }
+  const float2 l2 = cmul(l, l);
+  float2 qq = cpow_f(l, 32.f * run);
+  for (int i = 16 * run; i < 16 * run + 16; ++i) {
+    L2[i * M + m] = qq;
+    qq = cmul(qq, l2);
+  }
+  if (run == 0) {
+    float2 pj = make_float2(1.f, 0.f), geo = make_float2(0.f, 0.f), geot = geo;
+    for (int j = 0; j < C; ++j) {
+      if (j == Lt) geot = geo;
+      geo = cfma(bt, pj, geo);
+      pj = cmul(pj, inv);
+    }
+    if (Lt >= C) geot = geo;
+    reinterpret_cast<float2*>(tab + TL::oPow)[m] = pc1;
+    reinterpret_cast<float2*>(tab + TL::oGeo)[m] = geo;
+    reinterpret_cast<float2*>(tab + TL::oPowT)[m] = cpow_f(l, (float)(Lt - 1));
+    reinterpret_cast<float2*>(tab + TL::oGeoT)[m] = geot;
+    reinterpret_cast<float2*>(tab + TL::oPowS)[m] = cpow_f(l, (float)Ls);
+  }
+}
+
+// ---------------------------------------------------------------- segment carry scan
+// Slots of a sequence: 0 = initial state, g = 1..G-1 = end state of segment g-1 computed
+// from zero.  In place: slot g <- lam^Ls slot(g-1) + slot g, so slot g becomes the state
+// entering segment g.  One thread per (sequence, state element); segments in order.
+__global__ void carry_scan_kernel(const float2* __restrict__ U0, const float2* __restrict__ G0,
+                                  const float2* __restrict__ E0, float2* __restrict__ slots,
+                                  const unsigned char* __restrict__ tables, long table_bytes,
+                                  long pows_off, int H, int F, int D, int M, int G, long slot) {
+  const int seq = blockIdx.y;
+  const int h = seq % H;
+  const long n = (long)M * (F + D + 1);
+  const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= n) return;
+  int m;
+  float2 c = make_float2(0.f, 0.f);
+  if (e < (long)M * F) {
+    m = int(e / F);
+    if (U0) c = U0[(size_t)seq * M * F + e];
+  } else if (e < (long)M * (F + D)) {
+    m = int((e - (long)M * F) / D);
+    if (G0) c = G0[(size_t)seq * M * D + (e - (long)M * F)];
+  } else {
+    m = int(e - (long)M * (F + D));
+    if (E0) c = E0[(size_t)seq * M + m];
+  }
+  const float2 pw =
+      reinterpret_cast<const float2*>(tables + (size_t)h * table_bytes + pows_off)[m];
+  float2* s = slots + (size_t)seq * G * slot + e;
+  s[0] = c;
+  for (int gi = 1; gi < G; ++gi) {
+    c = cfma(pw, c, s[(size_t)gi * slot]);
+    s[(size_t)gi * slot] = c;
+  }
+}
+
+// ---------------------------------------------------------------- launch
+
+template <int C>
+static hipError_t dispatch_fdm(const ChunkArgs& a, int F, int D, int M, int n_wg,
+                               hipStream_t st, int kind) {
+#define IA_CASE(FF, MM)                                   \
+  if (F == FF && D == FF && M == MM) return launch_chunk_t<C, FF, FF, MM>(a, n_wg, st, kind);
+  IA_CASE(32, 16) IA_CASE(32, 32) IA_CASE(32, 64)
+  IA_CASE(64, 16) IA_CASE(64, 32) IA_CASE(64, 64)
+  IA_CASE(128, 16) IA_CASE(128, 32) IA_CASE(128, 64)
+#undef IA_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int C, int M>
+static hipError_t launch_tables_cm(const ChunkPrefillArgs& p, long tb, hipStream_t st) {
+  const int Lt = p.N % C == 0 ? C : p.N % C;
+  (void)hipGetLastError();
+  prof_begin(st);
+  hipLaunchKernelGGL((chunk_tables_kernel<C, M>), dim3(p.H), dim3(M * (C / 16)), 0, st, p.lam,
+                     p.beta, p.tables, tb, Lt, p.seg_chunks * C);
+  prof_end(st, kKindTables);
+  return hipGetLastError();
+}
+
+template <int C>
+static hipError_t launch_tables_c(const ChunkPrefillArgs& p, long tb, hipStream_t st) {
+  switch (p.M) {
+    case 16: return launch_tables_cm<C, 16>(p, tb, st);
+    case 32: return launch_tables_cm<C, 32>(p, tb, st);
+    case 64: return launch_tables_cm<C, 64>(p, tb, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool chunk_supported(int F, int D, int M) {
+  return F == D && (F == 32 || F == 64 || F == 128) && (M == 16 || M == 32 || M == 64);
+}
+
+long chunk_table_bytes(int chunk, int M) {
+  switch (chunk * 1000 + M) {
+    case 32016: return TableLayout<32, 16>::bytes;
+    case 32032: return TableLayout<32, 32>::bytes;
+    case 32064: return TableLayout<32, 64>::bytes;
+    case 64016: return TableLayout<64, 16>::bytes;
+    case 64032: return TableLayout<64, 32>::bytes;
+    case 64064: return TableLayout<64, 64>::bytes;
+  }
+  return 0;
+}
+
+static long pows_offset(int chunk, int M) {
+  switch (chunk * 1000 + M) {
+    case 32016: return TableLayout<32, 16>::oPowS;
+    case 32032: return TableLayout<32, 32>::oPowS;
+    case 32064: return TableLayout<32, 64>::oPowS;
+    case 64016: return TableLayout<64, 16>::oPowS;
+    case 64032: return TableLayout<64, 32>::oPowS;
+    case 64064: return TableLayout<64, 64>::oPowS;
+  }
+  return 0;
+}
+
+// Full chunked prefill for one direction: tables, segment end states, carry scan, outputs.
+hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
+  const int C = p.chunk;
+  const int n_chunks = (p.N + C - 1) / C;
+  const int seqs = p.B * p.H;
+  const long slot = (long)p.M * (p.F + p.D + 1);
+  const int G = p.segments;
+  const int seg_chunks = p.seg_chunks;
+  const long tb = chunk_table_bytes(C, p.M);
+  if (G < 1 || (G - 1) * seg_chunks >= n_chunks || G * seg_chunks < n_chunks)
+    return hipErrorInvalidValue;
+
+  hipError_t e = C == 64 ? launch_tables_c<64>(p, tb, st) : launch_tables_c<32>(p, tb, st);
+  if (e != hipSuccess) return e;
+
+  ChunkArgs a{};
+  a.q = static_cast<const uint16_t*>(p.q);
+  a.k = static_cast<const uint16_t*>(p.k);
+  a.v = static_cast<const uint16_t*>(p.v);
+  a.lam = p.lam;
+  a.beta = p.beta;
+  a.N = p.N;
+  a.H = p.H;
+  a.seg_chunks = seg_chunks;
+  a.dir = p.reverse;
+  a.out_bf16 = p.out_bf16;
+  a.clamp = p.clamp;
+  a.slot = slot;
+  a.slots_per_seq = G;
+  a.tables = p.tables;
+  a.table_bytes = tb;
+
+  auto go = [&](const ChunkArgs& x, int n_wg, int kind) -> hipError_t {
+    return C == 64 ? dispatch_fdm<64>(x, p.F, p.D, p.M, n_wg, st, kind)
+                   : dispatch_fdm<32>(x, p.F, p.D, p.M, n_wg, st, kind);
+  };
+
+  ChunkArgs o = a;
+  if (G > 1) {
+    // Pass 1: end state of segments 0..G-2 from a zero state, into slots 1..G-1.
+    ChunkArgs s = a;
+    s.seg_first = 0;
+    s.n_seg = G - 1;
+    s.fin_seg = p.slots;
+    e = go(s, seqs * (G - 1), kKindSummary);
+    if (e != hipSuccess) return e;
+    // Carries: slot g <- state entering segment g (slot 0 <- the initial state).
+    (void)hipGetLastError();
+    prof_begin(st);
+    hipLaunchKernelGGL(carry_scan_kernel, dim3((unsigned)((slot + 255) / 256), seqs), dim3(256),
+                       0, st, p.U0, p.G0, p.E0, p.slots, p.tables, tb, pows_offset(C, p.M), p.H,
+                       p.F, p.D, p.M, G, slot);
+    prof_end(st, kKindCarry);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    o.initc = p.slots;
+  } else {
+    o.init0_U = p.U0;
+    o.init0_G = p.G0;
+    o.init0_E = p.E0;
+  }
+  // Pass 2: every segment from its corrected initial state, with outputs; the last segment
+  // returns the final state.  State-only calls run just the last segment.
+  o.o = p.o;
+  o.acc_in = p.acc_in;
+  o.fin_U = p.U1;
+  o.fin_G = p.G1;
+  o.fin_E = p.E1;
+  o.seg_first = p.o ? 0 : G - 1;
+  o.n_seg = p.o ? G : 1;
+  return go(o, seqs * o.n_seg, kKindChunk);
+}
+
+}  // namespace ia

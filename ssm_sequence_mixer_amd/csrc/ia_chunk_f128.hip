@@ -1,0 +1,13 @@
+// ia_chunk_f128.hip — instantiations of the chunked prefill kernel for F = Dv = 128.
+#include "ia_chunk.hpp"
+
+namespace ia {
+
+template hipError_t launch_chunk_t<32, 128, 128, 16>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_chunk_t<32, 128, 128, 32>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_chunk_t<32, 128, 128, 64>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_chunk_t<64, 128, 128, 16>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_chunk_t<64, 128, 128, 32>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_chunk_t<64, 128, 128, 64>(const ChunkArgs&, int, hipStream_t, int);
+
+}  // namespace ia

@@ -1,0 +1,13 @@
+// ia_chunk_f32.hip — instantiations of the chunked prefill kernel for F = Dv = 32.
+#include "ia_chunk.hpp"
+
+namespace ia {
+
+template hipError_t launch_chunk_t<32, 32, 32, 16>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_chunk_t<32, 32, 32, 32>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_chunk_t<32, 32, 32, 64>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_chunk_t<64, 32, 32, 16>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_chunk_t<64, 32, 32, 32>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_chunk_t<64, 32, 32, 64>(const ChunkArgs&, int, hipStream_t, int);
+
+}  // namespace ia

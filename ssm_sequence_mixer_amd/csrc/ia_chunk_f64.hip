@@ -1,0 +1,13 @@
+// ia_chunk_f64.hip — instantiations of the chunked prefill kernel for F = Dv = 64.
+#include "ia_chunk.hpp"
+
+namespace ia {
+
+template hipError_t launch_chunk_t<32, 64, 64, 16>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_chunk_t<32, 64, 64, 32>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_chunk_t<32, 64, 64, 64>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_chunk_t<64, 64, 64, 16>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_chunk_t<64, 64, 64, 32>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_chunk_t<64, 64, 64, 64>(const ChunkArgs&, int, hipStream_t, int);
+
+}  // namespace ia

@@ -6,6 +6,39 @@
 
 namespace ia {
 
+// Kernel kinds reported by the profiling entry point, in launch order.
+enum LaunchKind {
+  kKindFill = 0,       // state / workspace zero fill
+  kKindScan = 1,       // token-sequential prefill
+  kKindTables = 2,     // per-head decay tables of the chunked prefill
+  kKindSummary = 3,    // chunked prefill, segment end states (no outputs)
+  kKindCarry = 4,      // segment carry scan
+  kKindChunk = 5,      // chunked prefill with outputs (or the last segment's state)
+  kKindDecode = 6,
+};
+
+// While set (only inside ia_prefill_fwd_profiled), every launch records events[2i] before
+// and events[2i+1] after its i-th kernel on the launch stream, and notes its kind.
+struct ProfileSink {
+  void** events;
+  int* kinds;
+  int max_launches;
+  int used;
+};
+extern thread_local ProfileSink* g_profile;
+
+inline void prof_begin(hipStream_t st) {
+  if (g_profile && g_profile->used < g_profile->max_launches)
+    (void)hipEventRecord(static_cast<hipEvent_t>(g_profile->events[2 * g_profile->used]), st);
+}
+inline void prof_end(hipStream_t st, int kind) {
+  if (g_profile && g_profile->used < g_profile->max_launches) {
+    (void)hipEventRecord(static_cast<hipEvent_t>(g_profile->events[2 * g_profile->used + 1]),
+                         st);
+    g_profile->kinds[g_profile->used++] = kind;
+  }
+}
+
 constexpr int kMaxDim = 256;    // largest F and Dv
 constexpr int kMaxModes = 128;  // largest M
 
@@ -30,6 +63,30 @@ struct ScanArgs {
   float clamp;
   int reverse;
 };
+
+// Chunked MFMA prefill of one direction (bf16 inputs).  The sequence is cut into `segments`
+// runs of `seg_chunks` chunks; with more than one, segment end states go through `slots`
+// (B*H*segments states of M*(F+D+1) complex values) and a carry scan.  `tables` holds
+// H * chunk_table_bytes(chunk, M) bytes.  U0/G0/E0: initial state or NULL (zeros);
+// U1/G1/E1: final state or NULL.  o NULL: state only.  acc_in: fp32 added to o, or NULL.
+struct ChunkPrefillArgs {
+  const void *q, *k, *v;
+  const float2 *lam, *beta;
+  void* o;
+  const float* acc_in;
+  const float2 *U0, *G0, *E0;
+  float2 *U1, *G1, *E1;
+  float2* slots;
+  unsigned char* tables;
+  int B, H, N, F, D, M;
+  int chunk, segments, seg_chunks;
+  int reverse, out_bf16;
+  float clamp;
+};
+
+bool chunk_supported(int F, int D, int M);
+long chunk_table_bytes(int chunk, int M);
+hipError_t launch_chunk_prefill(const ChunkPrefillArgs& a, hipStream_t st);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t st);

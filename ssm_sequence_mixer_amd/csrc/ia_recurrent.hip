@@ -201,24 +201,30 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
   if (n4 == 0) return hipSuccess;
   unsigned grid = static_cast<unsigned>(n4 / 256 + 1 < 4096 ? n4 / 256 + 1 : 4096);
   (void)hipGetLastError();
+  prof_begin(st);
   hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, st,
                      static_cast<float4*>(p), n4);
+  prof_end(st, kKindFill);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t st) {
   (void)hipGetLastError();
+  prof_begin(st);
   hipLaunchKernelGGL(decode_step_kernel, dim3(a.B * a.H), dim3(kStepThreads), 0, st, a.q, a.k,
                      a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H, a.F, a.D, a.M, a.in_bf16,
                      a.out_bf16, a.clamp);
+  prof_end(st, kKindDecode);
   return hipGetLastError();
 }
 
 hipError_t launch_scan_prefill(const ScanArgs& a, hipStream_t st) {
   (void)hipGetLastError();
+  prof_begin(st);
   hipLaunchKernelGGL(scan_prefill_kernel, dim3(a.B * a.H), dim3(kStepThreads), 0, st, a.q,
                      a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.acc_in, a.N, a.H, a.F, a.D,
                      a.M, a.in_bf16, a.out_bf16, a.clamp, a.reverse);
+  prof_end(st, kKindScan);
   return hipGetLastError();
 }
 

@@ -55,3 +55,8 @@ def state_rel(st, ref):
 def tag(msg):
     """Print a line naming the case, flushed, before a GPU step."""
     print(f"[case] {msg}", flush=True)
+
+
+def report(name, err):
+    """Print a measured error (visible with pytest -s, and in the log on failure)."""
+    print(f"[err] {name}: {err:.3e}", flush=True)

@@ -1,0 +1,178 @@
+"""GPU parity of the chunked MFMA prefill (bf16 inputs) against the oracle.
+
+Small cases compare every (b,h) slice; the full workload sizes run in the launch
+configuration the benchmark times and compare sampled (b,h) slices, which the oracle
+computes one by one.  Tolerance: row-wise relative error 2e-2 (bf16 inputs).
+"""
+import numpy as np
+import pytest
+
+import ia_workloads as W
+import oracle
+from helpers import TOL_BF16, dev, host, report, rowrel, state_rel, tag
+
+pytestmark = pytest.mark.gpu
+
+
+def _ia():
+    import ssm_sequence_mixer_amd as ia
+    return ia
+
+
+def _run(inp, state=None, chunk=0, out="f32", bidir=False, want_output=True):
+    import torch
+    ia = _ia()
+    q, k, v = (dev(inp[n], torch.bfloat16) for n in "qkv")
+    od = torch.float32 if out == "f32" else torch.bfloat16
+    o = ia.prefill(q, k, v, dev(inp["lam"]), dev(inp["beta"]), state=state, out_dtype=od,
+                   chunk=chunk, bidir=bidir, want_output=want_output)
+    torch.cuda.synchronize()
+    return o
+
+
+@pytest.mark.parametrize("shape", [
+    (2, 2, 200, 32, 16), (1, 3, 130, 64, 32), (1, 2, 257, 128, 64), (2, 1, 64, 32, 64),
+    (1, 2, 1, 64, 16), (1, 1, 33, 128, 32)])
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_chunk_matches_oracle(shape, chunk):
+    B, H, N, F, M = shape
+    inp = W.make_inputs(B, H, N, F, F, M, dtype="bf16", seed=100 + N + F + M + chunk)
+    tag(f"chunk prefill B={B} H={H} N={N} F={F} M={M} C={chunk}")
+    o = _run(inp, chunk=chunk)
+    o_ref = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"])[0]
+    err = rowrel(host(o), o_ref)
+    report(f"chunk {shape} C={chunk}", err)
+    assert err < TOL_BF16
+
+
+@pytest.mark.parametrize("chunk", [32, 64])
+def test_chunk_many_segments_with_state(chunk):
+    """One sequence, 2048 tokens: the plan cuts it into many segments (carry scan), from a
+    non-zero initial state; outputs and the final state against the oracle."""
+    ia = _ia()
+    B, H, N, F, M = 1, 1, 2048, 64, 32
+    inp = W.make_inputs(B, H, N, F, F, M, dtype="bf16", seed=7 + chunk)
+    pre = W.make_inputs(B, H, 20, F, F, M, dtype="bf16", seed=8)
+    st_ref = oracle.prefill(pre["q"], pre["k"], pre["v"], inp["lam"], inp["beta"])[3]
+    st = tuple(dev(s) for s in st_ref)
+    st_ref = tuple(host(s) for s in st)
+    tag(f"chunk prefill many segments C={chunk}")
+    o = _run(inp, state=st, chunk=chunk)
+    o_ref, _, _, st_out = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["lam"],
+                                         inp["beta"], state=st_ref)
+    e_o, e_s = rowrel(host(o), o_ref), state_rel(tuple(host(s) for s in st), st_out)
+    report(f"many segments C={chunk} output", e_o)
+    report(f"many segments C={chunk} state", e_s)
+    assert e_o < TOL_BF16 and e_s < TOL_BF16
+
+
+def test_chunk_size_invariance():
+    B, H, N, F, M = 2, 2, 300, 64, 64
+    inp = W.make_inputs(B, H, N, F, F, M, dtype="bf16", seed=55)
+    tag("chunk size invariance")
+    o32 = host(_run(inp, chunk=32))
+    o64 = host(_run(inp, chunk=64))
+    o_ref = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"])[0]
+    e32, e64, e_x = rowrel(o32, o_ref), rowrel(o64, o_ref), rowrel(o32, o64)
+    report("chunk 32 vs oracle", e32)
+    report("chunk 64 vs oracle", e64)
+    report("chunk 32 vs chunk 64", e_x)
+    assert e32 < TOL_BF16 and e64 < TOL_BF16 and e_x < 2 * TOL_BF16
+
+
+def test_state_only_prefill_then_decode():
+    """State-only prefill (no outputs) then decode steps equal the full prefill's tail."""
+    import torch
+    ia = _ia()
+    B, H, N, F, M = 2, 2, 150, 128, 64
+    inp = W.make_inputs(B, H, N + 4, F, F, M, dtype="bf16", seed=77)
+    head = {n: inp[n][:, :N] for n in "qkv"}
+    head.update(lam=inp["lam"], beta=inp["beta"])
+    st = ia.new_state(B, H, M, F, F)
+    tag("state-only prefill")
+    _run(head, state=st, want_output=False)
+    outs = []
+    for t in range(N, N + 4):
+        outs.append(host(ia.decode(dev(inp["q"][:, t], torch.bfloat16),
+                                   dev(inp["k"][:, t], torch.bfloat16),
+                                   dev(inp["v"][:, t], torch.bfloat16), dev(inp["lam"]),
+                                   dev(inp["beta"]), st)))
+    torch.cuda.synchronize()
+    o_ref = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"])[0]
+    err = rowrel(np.stack(outs, axis=1), o_ref[:, N:])
+    report("state-only prefill then decode", err)
+    assert err < TOL_BF16
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_chunk_bidirectional(out):
+    B, H, N, F, M = 1, 2, 333, 32, 32
+    inp = W.make_inputs(B, H, N, F, F, M, dtype="bf16", seed=91)
+    tag(f"chunk bidir out={out}")
+    o = _run(inp, bidir=True, out=out)
+    o_ref = oracle.bidir(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"])
+    err = rowrel(host(o), o_ref)
+    report(f"chunk bidir out={out}", err)
+    assert err < TOL_BF16
+
+
+def test_chunk_forced_clamp():
+    """beta = i with real lambda: Re(den) < 0 everywhere, o = num / clamp."""
+    B, H, N, F, M = 1, 1, 100, 32, 16
+    inp = W.make_inputs(B, H, N, F, F, M, dtype="bf16", seed=13, dt=0.02,
+                        beta=np.full((1, M), 1j))
+    inp["lam"] = np.full((1, M), np.float32(0.95), np.complex64)
+    tag("chunk forced clamp")
+    o = _run(inp)
+    o_ref, _, den, _ = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"])
+    assert np.all(den < 0)
+    err = rowrel(host(o), o_ref)
+    report("chunk forced clamp", err)
+    assert err < TOL_BF16
+
+
+# ---------------------------------------------------------------- full workload sizes
+
+def _sampled(inp, slices, bidir=False, out="f32", threads=8):
+    o = host(_run(inp, bidir=bidir, out=out))
+    if bidir:
+        ref = oracle.bidir(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"],
+                           slices=slices, threads=threads)
+    else:
+        ref = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"],
+                             slices=slices, threads=threads)[0]
+    worst = 0.0
+    for (b, h) in slices:
+        worst = max(worst, rowrel(o[b, :, h], ref[b, :, h]))
+    return worst
+
+
+def _check_workload(name, err):
+    report(name, err)
+    assert err < TOL_BF16
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_workload_125m_sampled(out):
+    inp = W.l125m()
+    tag(f"125m workload out={out}")
+    _check_workload(f"125m out={out}", _sampled(inp, [(0, 0), (3, 5), (7, 11), (5, 2)], out=out))
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_workload_1p3b_sampled(out):
+    inp = W.l1p3b()
+    tag(f"1.3b workload out={out}")
+    _check_workload(f"1.3b out={out}", _sampled(inp, [(0, 0), (1, 7), (2, 13), (3, 15)], out=out))
+
+
+def test_workload_1p3b_long_sampled():
+    inp = W.l1p3b(N=7168)
+    tag("1.3b x3.5 length workload")
+    _check_workload("1.3b x3.5 length", _sampled(inp, [(0, 3), (3, 12)]))
+
+
+def test_workload_caduceus_sampled():
+    inp = W.caduceus()
+    tag("caduceus bidirectional workload")
+    _check_workload("caduceus bidir", _sampled(inp, [(0, 1), (1, 6)], bidir=True))

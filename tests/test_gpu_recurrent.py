@@ -7,7 +7,7 @@ import pytest
 
 import ia_workloads as W
 import oracle
-from helpers import TOL_BF16, TOL_F32, dev, host, rowrel, state_rel, tag
+from helpers import TOL_BF16, TOL_F32, dev, host, report, rowrel, state_rel, tag
 
 pytestmark = pytest.mark.gpu
 
@@ -145,7 +145,10 @@ def test_decode_1p3b_shape_batch16():
                dev(pre["v"], torch.bfloat16), dev(lam), dev(beta), state=st, want_output=False)
     _, _, _, st_ref = oracle.prefill(pre["q"], pre["k"], pre["v"], lam, beta, threads=8)
     torch.cuda.synchronize()
-    assert state_rel(tuple(host(s) for s in st), st_ref) < TOL_F32
+    # the prefix state comes from bf16 inputs through the chunked MFMA path: bf16 tolerance
+    err = state_rel(tuple(host(s) for s in st), st_ref)
+    report("decode 1.3b B=16 prefix state", err)
+    assert err < TOL_BF16
     for t in range(4):
         tag(f"decode 1.3b B=16 step {t}")
         o = ia.decode(dev(stp["q"][t], torch.bfloat16), dev(stp["k"][t], torch.bfloat16),
@@ -153,4 +156,6 @@ def test_decode_1p3b_shape_batch16():
         o_ref, st_ref = oracle.decode_step(stp["q"][t], stp["k"][t], stp["v"][t], lam, beta,
                                            st_ref)
         torch.cuda.synchronize()
-        assert rowrel(host(o), o_ref) < TOL_F32
+        err = rowrel(host(o), o_ref)
+        report(f"decode 1.3b B=16 step {t}", err)
+        assert err < TOL_BF16
