@@ -17,22 +17,26 @@ IA_EXTERN_C(64)
 #undef IA_EXTERN
 
 // ---------------------------------------------------------------- per-head tables
-// Once per call, one block per head, one thread per (mode, run of 16 exponents):
-// beta lam^-j in bf16 ([Re;Im] rows) and in scaled fp16 (row j), lam^(2i); per mode
-// lam^(C-1), sum_{j<C} beta lam^-j, the same two for the last chunk's length Lt, and
-// lam^Ls for the segment length Ls.  Each run starts from exp/log and continues by products.
+// Once per call, one block per head, one thread per (mode, run of 16 exponents).  Written in
+// the LDS form the prefill kernel copies verbatim: beta lam^-j in bf16 ([Re;Im] rows, j in
+// K-slot order) and in scaled fp16 (row j, modes in K-slot order), both swizzled; the
+// factors lam^(2i), i < 16, and lam^(32r); per mode lam^C, sum_{j<C} beta lam^-j, the same
+// two for the last chunk's length Lt, lam^Ls for the segment length Ls, and 1/lam.  Each run
+// starts from exp/log and continues by products.
 template <int C, int M>
 __global__ void chunk_tables_kernel(const float2* __restrict__ lam,
                                     const float2* __restrict__ beta, unsigned char* tables,
                                     long table_bytes, int Lt, int Ls) {
   using TL = TableLayout<C, M>;
-  constexpr int RC = TL::RC, RM = TL::RM;
+  constexpr int M2 = 2 * M;
   constexpr int RUNS = C / 16;
+  constexpr int L2S = M + 2;
   const int h = blockIdx.x;
   unsigned char* tab = tables + (size_t)h * table_bytes;
   uint16_t* WT = reinterpret_cast<uint16_t*>(tab + TL::oW);
-  uint16_t* Wb = WT + 2 * M * RC;
-  float2* L2 = reinterpret_cast<float2*>(tab + TL::oL2);
+  uint16_t* Wb = WT + M2 * C;
+  float2* L2lo = reinterpret_cast<float2*>(tab + TL::oL2);
+  float2* L2hi = L2lo + 16 * L2S;
   const int m = threadIdx.x % M, run = threadIdx.x / M;
   const float2 l = lam[(size_t)h * M + m];
   const float2 bt = beta[(size_t)h * M + m];
@@ -42,28 +46,32 @@ __global__ void chunk_tables_kernel(const float2* __restrict__ lam,
   const float2 pc1 = cpow_f(l, (float)(C - 1));
   s_wmax[threadIdx.x] = hypotf(bt.x, bt.y) / hypotf(pc1.x, pc1.y);
   __syncthreads();
-  float wmax = 0.f;
-  for (int i = 0; i < M * RUNS; ++i) wmax = fmaxf(wmax, s_wmax[i]);
-  const float wscale = pow2_scale(wmax);
+  for (int st = (M * RUNS) / 2; st > 0; st >>= 1) {
+    if (threadIdx.x < st)
+      s_wmax[threadIdx.x] = fmaxf(s_wmax[threadIdx.x], s_wmax[threadIdx.x + st]);
+    __syncthreads();
+  }
+  const float wscale = pow2_scale(s_wmax[0]);
   if (threadIdx.x == 0) *reinterpret_cast<float*>(tab + TL::oSc) = 1.f / wscale;
 
   const float2 inv = cpow_f(l, -1.f);
   float2 p = cpow_f(l, -16.f * run);
   for (int j = 16 * run; j < 16 * run + 16; ++j) {
-    const float re = bt.x * p.x - bt.y * p.y, im = bt.x * p.y + bt.y * p.x;
-    WT[m * RC + j] = f32_to_bf16(re);
-    WT[(M + m) * RC + j] = f32_to_bf16(im);
-    Wb[j * RM + m] = f16_bits(re * wscale);
-    Wb[j * RM + M + m] = f16_bits(im * wscale);
+    const float2 w = cmul(bt, p);
+    WT[soff<C>(m, kpos(j))] = __builtin_bit_cast(uint16_t, (__bf16)w.x);
+    WT[soff<C>(M + m, kpos(j))] = __builtin_bit_cast(uint16_t, (__bf16)w.y);
+    Wb[soff<M2>(j, kpos(m))] = __builtin_bit_cast(uint16_t, (_Float16)(w.x * wscale));
+    Wb[soff<M2>(j, kpos(M + m))] = __builtin_bit_cast(uint16_t, (_Float16)(w.y * wscale));
     p = cmul(p, inv);
   }
-  const float2 l2 = cmul(l, l);
-  float2 qq = cpow_f(l, 32.f * run);
-  for (int i = 16 * run; i < 16 * run + 16; ++i) {
-    L2[i * M + m] = qq;
-    qq = cmul(qq, l2);
-  }
   if (run == 0) {
+    const float2 l2 = cmul(l, l);
+    float2 qq = make_float2(1.f, 0.f);
+    for (int i = 0; i < 16; ++i) {
+      L2lo[i * L2S + m] = qq;
+      qq = cmul(qq, l2);
+    }
+    for (int r = 0; r < RUNS; ++r) L2hi[r * M + m] = cpow_f(l, 32.f * r);
     float2 pj = make_float2(1.f, 0.f), geo = make_float2(0.f, 0.f), geot = geo;
     for (int j = 0; j < C; ++j) {
       if (j == Lt) geot = geo;
@@ -71,11 +79,12 @@ __global__ void chunk_tables_kernel(const float2* __restrict__ lam,
       pj = cmul(pj, inv);
     }
     if (Lt >= C) geot = geo;
-    reinterpret_cast<float2*>(tab + TL::oPow)[m] = pc1;
+    reinterpret_cast<float2*>(tab + TL::oPow)[m] = cpow_f(l, (float)C);
     reinterpret_cast<float2*>(tab + TL::oGeo)[m] = geo;
-    reinterpret_cast<float2*>(tab + TL::oPowT)[m] = cpow_f(l, (float)(Lt - 1));
+    reinterpret_cast<float2*>(tab + TL::oPowT)[m] = cpow_f(l, (float)Lt);
     reinterpret_cast<float2*>(tab + TL::oGeoT)[m] = geot;
     reinterpret_cast<float2*>(tab + TL::oPowS)[m] = cpow_f(l, (float)Ls);
+    reinterpret_cast<float2*>(tab + TL::oInv)[m] = inv;
   }
 }
 

@@ -12,22 +12,25 @@
 //   P[i,j]   = Re sum_m A[i,m] beta_m lam_m^(i-j)   = Re (lam^i A)(beta lam^-j)^T, j <= i
 //   num[i,:] = P V + Re (lam^i A)(lam G_c)          den[i] = sum_j P[i,j] + Re (lam^i A)(lam eta_c)
 //   o[i,:]   = num[i,:] / max(den[i], clamp)
-//   U_{c+1}  = lam^(L-1) (lam U_c + sum_j beta lam^-j phi(k_j)), same for G with v, eta with 1.
+//   lam U_{c+1} = lam^L (lam U_c + sum_j beta lam^-j phi(k_j)), same for G with v, eta with 1.
 // Complex matrices enter real MFMAs as [Re | Im] blocks of 2M real columns.
 //
 // Workgroup = one (b, h, segment, direction); 64*(C/16 + 4) threads:
 //   readout waves r < C/16 own the 16 queries [16r, 16r+16) of each chunk and chain
 //     S^T -> A'^T -> P^T -> num^T through MFMA accumulators (an accumulator tile of X is the
-//     operand of X^T, with the K index permuted identically on both operands).  They also
-//     fetch the next chunk's q, k, v into registers while the current chunk computes;
-//   state waves own columns of the fp32 state, kept in MFMA accumulators for the whole
-//     segment, update it with two MFMA contractions per chunk, and publish operand copies of
-//     the new state (bf16 lam U, fp16 lam G scaled per column) to LDS.
+//     operand of X^T, with the K index permuted identically on both operands);
+//   state waves own columns of the fp32 state (held as lam U, lam G), kept in MFMA
+//     accumulators for the whole segment, update it with two MFMA contractions per chunk,
+//     publish operand copies of the new state (bf16 lam U, fp16 lam G scaled per column), and
+//     fetch the next chunk's q, k, v into registers while the current chunk computes.
 // Operand precision: features, S, the decay table, U, P and v in bf16; A, beta lam^-j and G
 // in fp16 after exact power-of-two scaling (per query row for A; per value column for G; per
 // head for the table), which keeps the readout's cancelling sums within the bf16 tolerance.
-// Every LDS matrix row is padded by 16 bytes so that the 16 rows an MFMA operand read
-// touches fall in distinct banks.
+// LDS operands are read as one 16-byte access per lane, or as two transposing 8-byte reads
+// (ds_read_b64_tr_b16) for phi(k) and v, which are stored once, row-major: the transposing
+// read returns 4 consecutive rows of one column per lane, exactly the K-slot order of an
+// accumulator-sourced partner.  Tables paired with such a partner store their K axis in that
+// slot order, and 16-byte blocks are XOR-swizzled by row so one read hits distinct banks.
 #pragma once
 
 #include <utility>
@@ -60,15 +63,6 @@ __device__ __forceinline__ Frag lds8(const uint16_t* p) {
   f.u = *reinterpret_cast<const uint4*>(p);
   return f;
 }
-// 4 + 4 values from two places (the permuted K order of an accumulator-sourced partner).
-__device__ __forceinline__ Frag lds44(const uint16_t* p0, const uint16_t* p1) {
-  Frag f;
-  const uint2 a = *reinterpret_cast<const uint2*>(p0);
-  const uint2 b = *reinterpret_cast<const uint2*>(p1);
-  f.u = make_uint4(a.x, a.y, b.x, b.y);
-  return f;
-}
-
 __device__ __forceinline__ bf16x8 pack_bf16(f32x4 a, f32x4 b) {
   bf16x8 r;
   r[0] = (__bf16)a[0]; r[1] = (__bf16)a[1]; r[2] = (__bf16)a[2]; r[3] = (__bf16)a[3];
@@ -76,19 +70,97 @@ __device__ __forceinline__ bf16x8 pack_bf16(f32x4 a, f32x4 b) {
   return r;
 }
 
+// Two floats -> packed bf16 / fp16 pair (hardware round-to-nearest-even conversions).
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  typedef __bf16 v2 __attribute__((ext_vector_type(2)));
+  const v2 r = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint32_t pk_f16(float a, float b) {
+  typedef _Float16 v2 __attribute__((ext_vector_type(2)));
+  const v2 r = {(_Float16)a, (_Float16)b};
+  return __builtin_bit_cast(uint32_t, r);
+}
 __device__ __forceinline__ uint2 pack4_bf16(float a, float b, float c, float d) {
-  return make_uint2(uint32_t(f32_to_bf16(a)) | (uint32_t(f32_to_bf16(b)) << 16),
-                    uint32_t(f32_to_bf16(c)) | (uint32_t(f32_to_bf16(d)) << 16));
+  return make_uint2(pk_bf16(a, b), pk_bf16(c, d));
 }
-
-__device__ __forceinline__ uint16_t f16_bits(float x) {
-  _Float16 h = (_Float16)x;
-  return __builtin_bit_cast(uint16_t, h);
-}
-
 __device__ __forceinline__ uint2 pack4_f16(float a, float b, float c, float d) {
-  return make_uint2(uint32_t(f16_bits(a)) | (uint32_t(f16_bits(b)) << 16),
-                    uint32_t(f16_bits(c)) | (uint32_t(f16_bits(d)) << 16));
+  return make_uint2(pk_f16(a, b), pk_f16(c, d));
+}
+
+// K-slot order of an operand built from two 16x16 accumulator tiles: slot 8g+e of a 32-wide K
+// block holds index 4g+e (e < 4, first tile) or 16+4g+e-4 (second tile).  kpos maps an index
+// to its slot; four consecutive indices starting at a multiple of 4 stay consecutive.
+__host__ __device__ constexpr int kpos(int l) {
+  return (l & ~31) | (8 * ((l & 15) >> 2) + 4 * ((l >> 4) & 1) + (l & 3));
+}
+
+// XOR swizzle of the 16-byte blocks of a row of RL 16-bit elements: rows 0..15 of one
+// operand read (same logical block) land in 16 distinct 16-byte bank groups.
+template <int RL>
+__host__ __device__ constexpr int swz(int row) {
+  constexpr int nb = RL / 8;
+  static_assert(nb == 4 || nb == 8 || nb == 16, "row of 32, 64 or 128 elements");
+  if constexpr (nb == 16) return row & 15;
+  else if constexpr (nb == 8) return (row >> 1) & 7;
+  else return (row >> 2) & 3;
+}
+// Element offset of (row, col) in a swizzled [rows][RL] matrix (col already in slot order).
+template <int RL>
+__host__ __device__ constexpr int soff(int row, int col) {
+  return row * RL + ((((col >> 3) ^ swz<RL>(row)) << 3) | (col & 7));
+}
+
+// Scheduling fence: keeps the loads of later unrolled steps from being hoisted above it, so
+// register use stays per step (latency is covered by the other waves on the SIMD instead).
+#define IA_STEP_FENCE() __builtin_amdgcn_sched_barrier(0)
+
+// Offset of row `row` (0..15), 8-element block `blk` in a swizzled [..][RL] matrix.  Rows
+// 16t + row for any t have the same swizzle, so tile t of a 16-row operand is this offset
+// plus the compile-time constant 16 t RL: per-lane address registers stay few (one per
+// K step), the tile offsets become instruction immediates.
+template <int RL>
+__device__ __forceinline__ int lane_off(int row, int blk) {
+  return row * RL + ((blk ^ swz<RL>(row)) << 3);
+}
+
+// Keeps a per-lane LDS offset out of constant folding.  Several matrices start past 64 KiB,
+// beyond the 16-bit immediate of ds_read/ds_write; folded with a tile offset into one constant
+// the sum no longer fits the immediate and costs a register per tile.  With the matrix base
+// inside the opaque value, tile offsets (< 64 KiB) stay immediates.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
+
+// Operand of a contraction over the rows of a row-major swizzled [K][RL] matrix, in the K-slot
+// order of an accumulator-sourced partner: lane (il, g) gets column 16ct + il at rows
+// 32kb + 4g + {0..3} (slots 0..3) and 32kb + 16 + 4g + {0..3} (slots 4..7).  Each
+// ds_read_b64_tr_b16 of a 16-lane group reads a 4-row x 16-column block (lane l: row l/4,
+// columns 4(l%4)..+3) and hands lane l column l of it.  tr_off gives the per-lane part for
+// column tile ct; row blocks kb add 32 kb RL (the swizzle of row r depends on r mod 16 only).
+template <int RL>
+__device__ __forceinline__ int tr_off(int ct, int lane) {
+  const int g = lane >> 4, lam = lane & 15;
+  const int row = 4 * g + (lam >> 2);
+  const int col = 16 * ct + 4 * (lam & 3);
+  return row * RL + ((((col >> 3) ^ swz<RL>(row)) << 3) | (col & 7));
+}
+template <int RL>
+__device__ __forceinline__ Frag ldtr(const uint16_t* base, int off, int kb) {
+  const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4s_ptr)(base + off + 32 * kb * RL));
+  const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4s_ptr)(base + off + (32 * kb + 16) * RL));
+  Frag f;
+  f.u = make_uint4(uint32_t(uint16_t(a[0])) | (uint32_t(uint16_t(a[1])) << 16),
+                   uint32_t(uint16_t(a[2])) | (uint32_t(uint16_t(a[3])) << 16),
+                   uint32_t(uint16_t(b[0])) | (uint32_t(uint16_t(b[1])) << 16),
+                   uint32_t(uint16_t(b[2])) | (uint32_t(uint16_t(b[3])) << 16));
+  return f;
 }
 
 // Power of two s with s * mx in [2^14, 2^15): maps the largest magnitude of a row or column
@@ -120,29 +192,40 @@ __device__ __forceinline__ float2 cpow_f(float2 lam, float n) {
   return make_float2(mag * cs, mag * sn);
 }
 
+// ---------------------------------------------------------------- wave roles
+// C/16 readout waves and NS state waves.  The widest shapes use 8 state waves (12 waves per
+// workgroup, 3 per SIMD) so that each state wave's share of the fp32 state plus its share of
+// the next chunk's inputs fits its registers; the others use 4.
+template <int F, int D, int M>
+struct StateWaves {
+  static constexpr int NS = (F + D >= 256 && M >= 64) ? 8 : 4;
+};
+
 // ---------------------------------------------------------------- LDS layout
 
-template <int C, int F, int D, int M>
+template <int C, int F, int D, int M, int NR>
 struct Layout {
   static constexpr int M2 = 2 * M;
-  // padded row lengths, in 16-bit elements
-  static constexpr int RF = F + 8, RC = C + 8, RM = M2 + 8;
-  // 16-bit element offsets (all multiples of 8 -> 16-byte aligned)
-  static constexpr int oFk = 0;                    // [C][RF]   bf16 phi(k), row j
-  static constexpr int oFkT = oFk + C * RF;        // [F][RC]   bf16 phi(k)^T
-  static constexpr int oVT = oFkT + F * RC;        // [D][RC]   bf16 v^T
-  static constexpr int oWT = oVT + D * RC;         // [2M][RC]  bf16 beta lam^-j, [Re;Im] rows
-  static constexpr int oWb = oWT + M2 * RC;        // [C][RM]   fp16 scaled beta lam^-j, row j
-  static constexpr int oLU = oWb + C * RM;         // [2M][RF]  bf16 lam U_c, [Re;Im] rows
-  static constexpr int oGT = oLU + M2 * RF;        // [D][RM]   fp16 c_d lam G_c, row d
-  static constexpr int n16 = oGT + D * RM;
-  // fp32 arrays after the 16-bit block (byte offsets)
+  // 16-bit element offsets; every matrix is swizzled by row (see soff).
+  static constexpr int oFk = 0;                    // [C][F]   bf16 phi(k)           (f order)
+  static constexpr int oFq = oFk + C * F;          // [C][F]   bf16 phi(q)           (f order)
+  static constexpr int oV = oFq + C * F;           // [C][D]   bf16 v                (d order)
+  static constexpr int oWT = oV + C * D;           // [2M][C]  bf16 beta lam^-j      (j slots)
+  static constexpr int oWb = oWT + M2 * C;         // [C][2M]  fp16 scaled beta lam^-j (k slots)
+  static constexpr int oLU = oWb + C * M2;         // [2M][F]  bf16 lam U_c          (f order)
+  static constexpr int oGT = oLU + M2 * F;         // [D][2M]  fp16 c_d lam G_c      (k slots)
+  static constexpr int n16 = oGT + D * M2;
+  // 32-bit arrays (byte offsets)
   static constexpr int bC = n16 * 2;               // [D]  float  c_d
-  static constexpr int bLE = bC + D * 4;           // [M]  float2 lam eta_c
+  static constexpr int bCi = bC + D * 4;           // [D]  float  1 / c_d
+  static constexpr int bLE = bCi + D * 4;          // [M]  float2 lam eta_c
   static constexpr int bLam = bLE + M * 8;         // [M]  float2 lam
-  static constexpr int bPowL = bLam + M * 8;       // [M]  float2 lam^(L-1) of the current chunk
+  static constexpr int bPowL = bLam + M * 8;       // [M]  float2 lam^L of the current chunk
   static constexpr int bGeo = bPowL + M * 8;       // [M]  float2 sum_{j<L} beta lam^-j
-  static constexpr int bytes = bGeo + M * 8;
+  static constexpr int L2S = M + 2;                // row stride of the lam^(2i) factor table
+  static constexpr int bL2lo = bGeo + M * 8;       // [16][L2S] float2 lam^(2i), i = 0..15
+  static constexpr int bL2hi = bL2lo + 16 * L2S * 8;  // [NR][M] float2 lam^(32r)
+  static constexpr int bytes = bL2hi + NR * M * 8;
 };
 
 struct ChunkArgs {
@@ -172,28 +255,30 @@ struct ChunkArgs {
 };
 
 // Per-head tables, computed once per call by chunk_tables_kernel (byte offsets).  The two
-// decay tables are stored with the padded LDS row lengths, adjacent, as in LDS.
+// decay tables and the two lam^(2i) factor tables are stored exactly as in LDS.
 template <int C, int M>
 struct TableLayout {
-  static constexpr int RC = C + 8, RM = 2 * M + 8;
-  static constexpr long oW = 0;                       // bf16 [2M][RC] then fp16 [C][RM]
-  static constexpr long nW = 2L * (2L * M * RC + (long)C * RM);
-  static constexpr long oL2 = oW + nW;                // float2 [C][M]: lam^(2i)
-  static constexpr long oPow = oL2 + 8L * C * M;      // float2 [M]: lam^(C-1)
+  static constexpr int NR = C / 16;
+  static constexpr long oW = 0;                       // bf16 [2M][C] then fp16 [C][2M]
+  static constexpr long nW = 2L * (2L * M * C + (long)C * 2 * M);
+  static constexpr long oL2 = oW + nW;                // [16][M+2] then [NR][M] float2
+  static constexpr long nL2 = 8L * (16L * (M + 2) + (long)NR * M);
+  static constexpr long oPow = oL2 + nL2;             // float2 [M]: lam^C
   static constexpr long oGeo = oPow + 8L * M;         // float2 [M]: sum_{j<C} beta lam^-j
-  static constexpr long oPowT = oGeo + 8L * M;        // float2 [M]: lam^(Lt-1), last chunk
+  static constexpr long oPowT = oGeo + 8L * M;        // float2 [M]: lam^Lt, last chunk
   static constexpr long oGeoT = oPowT + 8L * M;       // float2 [M]: sum_{j<Lt} beta lam^-j
   static constexpr long oPowS = oGeoT + 8L * M;       // float2 [M]: lam^(segment length)
-  static constexpr long oSc = oPowS + 8L * M;         // float: 1 / fp16 table scale
+  static constexpr long oInv = oPowS + 8L * M;        // float2 [M]: 1 / lam
+  static constexpr long oSc = oInv + 8L * M;          // float: 1 / fp16 table scale
   static constexpr long bytes = (oSc + 16 + 255) / 256 * 256;
 };
 
 // Per-workgroup context shared by the two wave roles.
 template <int C, int F, int D, int M>
 struct Ctx {
-  uint16_t *sFk, *sFkT, *sVT, *sWT, *sWb, *sLU, *sGT;
-  float* sC;
-  float2 *sLE, *sLam, *sPowL, *sGeo;
+  uint16_t *s16, *sFk, *sFq, *sV, *sWT, *sWb, *sLU, *sGT;
+  float *sC, *sCi;
+  float2 *sLE, *sLam, *sPowL, *sGeo, *sL2lo, *sL2hi;
   const unsigned char* tab;
   int lane, il, g, wave;
   int seq, seg, b, h, c_begin, c_end;
@@ -206,119 +291,57 @@ struct Ctx {
 };
 
 // ---------------------------------------------------------------- readout waves
-// Wave r owns queries [16r, 16r+16) of every chunk.  It also loads tokens [16r, 16r+16) of
-// k and v for everyone (phi(k) rows, phi(k)^T and v^T in LDS), one chunk ahead.
+// Wave R owns queries [16R, 16R+16) of every chunk.
 template <int C, int F, int D, int M, int R>
 __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F, D, M>& x) {
-  using Lay = Layout<C, F, D, M>;
-  using TL = TableLayout<C, M>;
+  using Lay = Layout<C, F, D, M, C / 16>;
   constexpr int NR = C / 16;
+  constexpr int M2 = 2 * M;
   constexpr int MH = M / 16;
-  constexpr int TM = 2 * M / 16;
+  constexpr int TM = M2 / 16;
   constexpr int KF = F / 32;
-  constexpr int KM = 2 * M / 32;
+  constexpr int KM = M2 / 32;
   constexpr int KC = C / 32;
   constexpr int TD = D / 16;
-  constexpr int RF = Lay::RF, RC = Lay::RC, RM = Lay::RM;
-  constexpr int NK = 4 * (F / 8);   // load items of k: 4 token quads x F/8 column octets
-  constexpr int NV = 4 * (D / 8);
-  static_assert(NK <= 64 && NV <= 64, "one load item per lane");
   constexpr int r = R;   // compile-time: causal trip counts below are constants
   const int lane = x.lane, il = x.il, g = x.g;
-
-  float2 lam2i[MH][4];   // lam_m^(2i), i = 16r + il, modes 16mt + 4g + q
-  {
-    const float2* l2 = reinterpret_cast<const float2*>(x.tab + TL::oL2) + (16 * r + il) * M;
+  // Per-lane LDS offsets, one per K step (row il, block 4 step + g); tiles add constants.
+  // Offsets from the LDS base (matrix start included, see opaque): phi(k) / phi(q) (one set,
+  // phi(q) is at a constant distance below 64 KiB), lam U, the two decay tables, lam G, v.
+  int oF[KF], oLU[KF], oWT[KC], oWb[KM], oGT[KM], oV[TD];
 #pragma unroll
-    for (int mt = 0; mt < MH; ++mt)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) lam2i[mt][q] = l2[16 * mt + 4 * g + q];
+  for (int s = 0; s < KF; ++s) {
+    oF[s] = opaque(Lay::oFk + lane_off<F>(il, 4 * s + g));
+    oLU[s] = opaque(Lay::oLU + lane_off<F>(il, 4 * s + g));
   }
-
-  // Raw bf16 inputs of the next chunk (issued before the current chunk's compute).
-  uint4 rk[4], rv[4], rq[KF];
-  const int iq4 = lane & 3, io = lane >> 2;   // this lane's load item: token quad, octet
-  auto prefetch = [&](int c) {
-    const int t0 = c * C + 16 * r + 4 * iq4;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      const int t = t0 + tt;
-      const bool ok = t < a.N;
-      const size_t ti = ok ? x.tok_index(a, x.pos_of(a, t)) : 0;
-      rk[tt] = make_uint4(0, 0, 0, 0);
-      rv[tt] = make_uint4(0, 0, 0, 0);
-      if (ok && lane < NK) rk[tt] = *reinterpret_cast<const uint4*>(a.k + ti * F + 8 * io);
-      if (ok && lane < NV) rv[tt] = *reinterpret_cast<const uint4*>(a.v + ti * D + 8 * io);
-    }
-    if (x.want_out) {
-      const int t = c * C + 16 * r + il;
-      const bool ok = t < a.N;
-      const size_t qoff = ok ? x.tok_index(a, x.pos_of(a, t)) * F : 0;
+  for (int kb = 0; kb < KC; ++kb) oWT[kb] = opaque(Lay::oWT + lane_off<C>(il, 4 * kb + g));
 #pragma unroll
-      for (int s = 0; s < KF; ++s)
-        rq[s] = ok ? *reinterpret_cast<const uint4*>(a.q + qoff + 32 * s + 8 * g)
-                   : make_uint4(0, 0, 0, 0);
-    }
-  };
-  bf16x8 fq[KF];
-  // phi(k) rows and columns, v columns, and this wave's phi(q) operands from the raw data.
-  // Tokens past N have zero features and values (zeros, not phi(0)).
-  auto write_lds = [&](int c) {
-    const int j0 = 16 * r + 4 * iq4;
-    const int L = min(C, a.N - c * C);
-    if (lane < NK) {
-      float f[4][8];
+  for (int kb = 0; kb < KM; ++kb) {
+    oWb[kb] = opaque(Lay::oWb + lane_off<M2>(il, 4 * kb + g));
+    oGT[kb] = opaque(Lay::oGT + lane_off<M2>(il, 4 * kb + g));
+  }
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&rk[tt]);
-        const bool ok = j0 + tt < L;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[tt][e] = ok ? feature(bf16_to_f32(e16[e])) : 0.f;
-        if (x.want_out)
-          *reinterpret_cast<uint4*>(x.sFk + (j0 + tt) * RF + 8 * io) = make_uint4(
-              f32_to_bf16(f[tt][0]) | (uint32_t(f32_to_bf16(f[tt][1])) << 16),
-              f32_to_bf16(f[tt][2]) | (uint32_t(f32_to_bf16(f[tt][3])) << 16),
-              f32_to_bf16(f[tt][4]) | (uint32_t(f32_to_bf16(f[tt][5])) << 16),
-              f32_to_bf16(f[tt][6]) | (uint32_t(f32_to_bf16(f[tt][7])) << 16));
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint2*>(x.sFkT + (8 * io + e) * RC + j0) =
-            pack4_bf16(f[0][e], f[1][e], f[2][e], f[3][e]);
-    }
-    if (lane < NV) {
-      const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&rv[0]);
-      const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&rv[1]);
-      const uint16_t* e2 = reinterpret_cast<const uint16_t*>(&rv[2]);
-      const uint16_t* e3 = reinterpret_cast<const uint16_t*>(&rv[3]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<uint2*>(x.sVT + (8 * io + e) * RC + j0) =
-            make_uint2(uint32_t(e0[e]) | (uint32_t(e1[e]) << 16),
-                       uint32_t(e2[e]) | (uint32_t(e3[e]) << 16));
-    }
-    if (x.want_out) {
-#pragma unroll
-      for (int s = 0; s < KF; ++s) {
-        const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&rq[s]);
-        bf16x8 v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (__bf16)feature(bf16_to_f32(e16[e]));
-        fq[s] = v;
-      }
-    }
-  };
+  for (int dt = 0; dt < TD; ++dt) oV[dt] = opaque(Lay::oV + tr_off<D>(dt, lane));
+  const uint16_t* s16 = x.s16;
+  static_assert(Lay::oFq - Lay::oFk + C * F < 32768, "phi(q) within the immediate range");
+  // fp32 tables past 64 KiB likewise: lam^(2i) rows (il), then lam^(32r), lam eta and 1/c_d
+  // (lane group g).
+  const unsigned char* sb = reinterpret_cast<const unsigned char*>(x.s16);
+  const int oLo = opaque(Lay::bL2lo + 8 * (il * Lay::L2S + 4 * g));
+  const int oG = opaque(Lay::bLE + 32 * g);
+  const int oCi = opaque(Lay::bCi + 16 * g);
+  static_assert(Lay::bL2hi + 8 * (NR * M) - Lay::bLE < 65536, "tables within the immediate range");
 
   __syncthreads();  // tables visible
-  if (x.c_begin < x.c_end) {
-    prefetch(x.c_begin);
-    write_lds(x.c_begin);
-  }
-  __syncthreads();
+  __syncthreads();  // first chunk in LDS
 
   for (int c = x.c_begin; c < x.c_end; ++c) {
-    if (c + 1 < x.c_end) prefetch(c + 1);
     if (x.want_out) {
+      // phi(q) of this wave's queries as B operands (K = f)
+      bf16x8 fq[KF];
+#pragma unroll
+      for (int s = 0; s < KF; ++s) fq[s] = lds8(s16 + oF[s] + (Lay::oFq - Lay::oFk) + 16 * r * F).b;
       // ---- S^T tiles (rows j, columns i), causal: tiles jt <= r
       f32x4 accS[NR];
 #pragma unroll
@@ -327,7 +350,7 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
         if (jt <= r) {
 #pragma unroll
           for (int s = 0; s < KF; ++s)
-            acc = mma_bf16(lds8(x.sFk + (16 * jt + il) * RF + 32 * s + 8 * g).b, fq[s], acc);
+            acc = mma_bf16(lds8(s16 + oF[s] + 16 * jt * F).b, fq[s], acc);
           if (jt == r) {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -335,6 +358,7 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
           }
         }
         accS[jt] = acc;
+        IA_STEP_FENCE();
       }
       bf16x8 Sf[KC];
 #pragma unroll
@@ -343,35 +367,45 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
       // ---- A'^T tiles (rows k, columns i)
       f32x4 accA[TM];
 #pragma unroll
-      for (int kt = 0; kt < TM; ++kt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const uint16_t* wrow = x.sWT + (16 * kt + il) * RC;
+      for (int kt = 0; kt < TM; ++kt) accA[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < KC; ++kb)
-          if (32 * kb <= 16 * r + 15)
-            acc = mma_bf16(lds44(wrow + 32 * kb + 4 * g, wrow + 32 * kb + 16 + 4 * g).b,
-                           Sf[kb], acc);
-        const uint16_t* urow = x.sLU + (16 * kt + il) * RF;
+      for (int kb = 0; kb < KC; ++kb)
+        if (32 * kb <= 16 * r + 15) {
 #pragma unroll
-        for (int s = 0; s < KF; ++s) acc = mma_bf16(lds8(urow + 32 * s + 8 * g).b, fq[s], acc);
-        accA[kt] = acc;
+          for (int kt = 0; kt < TM; ++kt)
+            accA[kt] = mma_bf16(lds8(s16 + oWT[kb] + 16 * kt * C).b, Sf[kb], accA[kt]);
+          IA_STEP_FENCE();
+        }
+#pragma unroll
+      for (int s = 0; s < KF; ++s) {
+#pragma unroll
+        for (int kt = 0; kt < TM; ++kt)
+          accA[kt] = mma_bf16(lds8(s16 + oLU[s] + 16 * kt * F).b, fq[s], accA[kt]);
+        IA_STEP_FENCE();
       }
 
       // ---- lam^(2i) A' (fp32), den_inter, per-query scale, fp16 operands [Re | -Im]
       float den_inter = 0.f, amax = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < MH; ++mt)
+      for (int mt = 0; mt < MH; ++mt) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
+          // m = 16 mt + 4 g + q
+          const int mo = 8 * (16 * mt + q);
+          const float2 lo = *reinterpret_cast<const float2*>(sb + oLo + mo);
+          const float2 hi =
+              *reinterpret_cast<const float2*>(sb + oG + (Lay::bL2hi - Lay::bLE) + 8 * r * M + mo);
+          const float2 le = *reinterpret_cast<const float2*>(sb + oG + mo);
+          const float2 L2 = cmul(lo, hi);
           const float xr = accA[mt][q], yi = accA[mt + MH][q];
-          const float2 L2 = lam2i[mt][q];
           const float ar = xr * L2.x - yi * L2.y, ai = xr * L2.y + yi * L2.x;
           accA[mt][q] = ar;
           accA[mt + MH][q] = -ai;
-          const float2 le = x.sLE[16 * mt + 4 * g + q];
           den_inter += ar * le.x - ai * le.y;
           amax = fmaxf(amax, fmaxf(fabsf(ar), fabsf(ai)));
         }
+        IA_STEP_FENCE();
+      }
       den_inter = xor_sum16_32(den_inter);
       amax = xor_max16_32(amax);
       const float si = pow2_scale(amax);
@@ -391,11 +425,9 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
       for (int jt = 0; jt < NR; ++jt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         if (jt <= r) {
-          const uint16_t* wrow = x.sWb + (16 * jt + il) * RM;
 #pragma unroll
           for (int kb = 0; kb < KM; ++kb)
-            acc = mma_f16(lds44(wrow + 32 * kb + 4 * g, wrow + 32 * kb + 16 + 4 * g).h, Af[kb],
-                          acc);
+            acc = mma_f16(lds8(s16 + oWb[kb] + 16 * jt * M2).h, Af[kb], acc);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             acc[q] *= x.wb_unscale;
@@ -404,10 +436,11 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
           }
         }
         accP[jt] = acc;
+        IA_STEP_FENCE();
       }
       den_intra = xor_sum16_32(den_intra);
       const float den = den_intra + si * den_inter;   // in units of si
-      const float dcl = clamp_den(den, si * a.clamp);
+      const float rd = 1.f / clamp_den(den, si * a.clamp);
       bf16x8 Pf[KC];
 #pragma unroll
       for (int kb = 0; kb < KC; ++kb) Pf[kb] = pack_bf16(accP[2 * kb], accP[2 * kb + 1]);
@@ -419,22 +452,17 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
 #pragma unroll
       for (int dt = 0; dt < TD; ++dt) {
         f32x4 accI = {0.f, 0.f, 0.f, 0.f}, accX = {0.f, 0.f, 0.f, 0.f};
-        const uint16_t* vrow = x.sVT + (16 * dt + il) * RC;
 #pragma unroll
         for (int kb = 0; kb < KC; ++kb)
           if (32 * kb <= 16 * r + 15)
-            accI = mma_bf16(lds44(vrow + 32 * kb + 4 * g, vrow + 32 * kb + 16 + 4 * g).b,
-                            Pf[kb], accI);
-        const uint16_t* grow = x.sGT + (16 * dt + il) * RM;
+            accI = mma_bf16(ldtr<D>(s16, oV[dt], kb).b, Pf[kb], accI);
 #pragma unroll
         for (int kb = 0; kb < KM; ++kb)
-          accX = mma_f16(lds44(grow + 32 * kb + 4 * g, grow + 32 * kb + 16 + 4 * g).h, Af[kb],
-                         accX);
+          accX = mma_f16(lds8(s16 + oGT[kb] + 16 * dt * M2).h, Af[kb], accX);
         if (ok) {
-          const float4 cd = *reinterpret_cast<const float4*>(x.sC + 16 * dt + 4 * g);
-          const float rd = 1.f / dcl;
-          float val[4] = {(accI[0] + accX[0] / cd.x) * rd, (accI[1] + accX[1] / cd.y) * rd,
-                          (accI[2] + accX[2] / cd.z) * rd, (accI[3] + accX[3] / cd.w) * rd};
+          const float4 ci = *reinterpret_cast<const float4*>(sb + oCi + 64 * dt);
+          float val[4] = {(accI[0] + accX[0] * ci.x) * rd, (accI[1] + accX[1] * ci.y) * rd,
+                          (accI[2] + accX[2] * ci.z) * rd, (accI[3] + accX[3] * ci.w) * rd};
           const size_t oi = obase + 16 * dt + 4 * g;
           if (a.acc_in) {
             const float4 prev = *reinterpret_cast<const float4*>(a.acc_in + oi);
@@ -447,34 +475,66 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
             *reinterpret_cast<float4*>(static_cast<float*>(a.o) + oi) =
                 make_float4(val[0], val[1], val[2], val[3]);
         }
+        IA_STEP_FENCE();
       }
     }
     __syncthreads();
-    if (c + 1 < x.c_end) write_lds(c + 1);
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------- state waves
-// State wave u owns feature tiles ft = u, u+4, ... of U^T and value tiles dt = u, u+4, ...
-// of G, in fp32 MFMA accumulators for the whole segment; wave 0 also owns eta.
+// State wave U owns feature tiles ft = U, U+NS, ... of (lam U)^T and value tiles dt = U,
+// U+NS, ... of lam G, in fp32 MFMA accumulators for the whole segment; wave 0 also owns
+// lam eta.
 template <int C, int F, int D, int M, int U>
 __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D, M>& x) {
-  using Lay = Layout<C, F, D, M>;
   using TL = TableLayout<C, M>;
+  using Lay = Layout<C, F, D, M, C / 16>;
+  constexpr int M2 = 2 * M;
   constexpr int MH = M / 16;
-  constexpr int TM = 2 * M / 16;
+  constexpr int TM = M2 / 16;
   constexpr int KC = C / 32;
   constexpr int TD = D / 16;
-  constexpr int NFT = (F / 16 + 3) / 4;
-  constexpr int NDT = (D / 16 + 3) / 4;
-  constexpr int RF = Lay::RF, RC = Lay::RC, RM = Lay::RM;
+  constexpr int NS = StateWaves<F, D, M>::NS;
+  constexpr int NFT = (F / 16 + NS - 1) / NS;
+  constexpr int NDT = (D / 16 + NS - 1) / NS;
   constexpr int u = U;   // compile-time: owned tiles below are constants
   const int lane = x.lane, il = x.il, g = x.g;
+  // Loader share of this wave: 16-byte vectors n = 64u + lane + 64 NS t of the row-major
+  // chunk matrices q, k ([C][F]) and v ([C][D]).
+  constexpr int VF = F / 8, VD = D / 8;
+  constexpr int NL = 64 * NS;
+  constexpr int NLF = (C * VF + NL - 1) / NL, NLD = (C * VD + NL - 1) / NL;
+  // Per-lane LDS offsets (tiles add compile-time constants).
+  // Offsets from the LDS base, matrix start included (see opaque).
+  int offC[KC], trF[NFT], trD[NDT], pubU[NFT], pubG[TM / 2];
+#pragma unroll
+  for (int kb = 0; kb < KC; ++kb) offC[kb] = opaque(Lay::oWT + lane_off<C>(il, 4 * kb + g));
+#pragma unroll
+  for (int fi = 0; fi < NFT; ++fi) {
+    trF[fi] = opaque(Lay::oFk + tr_off<F>(u + NS * fi, lane));
+    // lam U row m = 16mt + il (Re) or M + 16mt + il (Im), columns 16ft + 4g .. +3
+    pubU[fi] = opaque(Lay::oLU + lane_off<F>(il, 2 * (u + NS * fi) + (g >> 1)) + 4 * (g & 1));
+  }
+#pragma unroll
+  for (int di = 0; di < NDT; ++di) trD[di] = opaque(Lay::oV + tr_off<D>(u + NS * di, lane));
+  // c_d lam G row d = 16dt + il, columns kpos(16kt + 4g) = 32 (kt/2) + 8g + 4 (kt%2) .. +3
+#pragma unroll
+  for (int k2 = 0; k2 < TM / 2; ++k2) pubG[k2] = opaque(Lay::oGT + lane_off<M2>(il, 4 * k2 + g));
+  uint16_t* const s16 = x.s16;
+  // fp32 tables past 64 KiB: lam^L by mode row il / group g, c_d by value row il, per-lane
+  // vectors (lam eta, lam^L, the geometric sums) by lane.
+  unsigned char* const sb = reinterpret_cast<unsigned char*>(x.s16);
+  const int oPl = opaque(Lay::bPowL + 8 * il);
+  const int oPg = opaque(Lay::bPowL + 32 * g);
+  const int oCd = opaque(Lay::bC + 4 * il);
+  const int oLn = opaque(Lay::bLE + 8 * lane);
+  auto f2 = [&](int off) -> float2& { return *reinterpret_cast<float2*>(sb + off); };
 
-  f32x4 accU[NFT][TM];   // U^T tiles: rows f = 16ft + 4g + q, columns k = 16kt + il
-  f32x4 accG[NDT][TM];   // G tiles:   rows k = 16kt + 4g + q, columns d = 16dt + il
-  float2 eta = make_float2(0.f, 0.f);  // wave 0, lane m < M
+  f32x4 accU[NFT][TM];   // (lam U)^T tiles: rows f = 16ft + 4g + q, columns k = 16kt + il
+  f32x4 accG[NDT][TM];   // lam G tiles:     rows k = 16kt + 4g + q, columns d = 16dt + il
+  float2 eta = make_float2(0.f, 0.f);  // lam eta; wave 0, lane m < M
 #pragma unroll
   for (int fi = 0; fi < NFT; ++fi)
 #pragma unroll
@@ -484,7 +544,7 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
 #pragma unroll
     for (int kt = 0; kt < TM; ++kt) accG[di][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Initial state.
+  // Initial state (times lam).
   const float2 *iU = nullptr, *iG = nullptr, *iE = nullptr;
   if (a.initc) {
     const float2* base = a.initc + ((size_t)x.seq * a.slots_per_seq + x.seg) * a.slot;
@@ -496,17 +556,19 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
     iG = a.init0_G + (size_t)x.seq * M * D;
     iE = a.init0_E + (size_t)x.seq * M;
   }
+  const float2* lamh = a.lam + (size_t)x.h * M;
   if (iU) {
 #pragma unroll
     for (int fi = 0; fi < NFT; ++fi) {
-      const int ft = u + 4 * fi;
+      const int ft = u + NS * fi;
       if (ft < F / 16) {
 #pragma unroll
         for (int mt = 0; mt < MH; ++mt) {
           const int m = 16 * mt + il;
+          const float2 l = lamh[m];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float2 v = iU[(size_t)m * F + 16 * ft + 4 * g + q];
+            const float2 v = cmul(l, iU[(size_t)m * F + 16 * ft + 4 * g + q]);
             accU[fi][mt][q] = v.x;
             accU[fi][mt + MH][q] = v.y;
           }
@@ -515,19 +577,20 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
     }
 #pragma unroll
     for (int di = 0; di < NDT; ++di) {
-      const int dt = u + 4 * di;
+      const int dt = u + NS * di;
       if (dt < TD) {
 #pragma unroll
         for (int mt = 0; mt < MH; ++mt)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float2 v = iG[(size_t)(16 * mt + 4 * g + q) * D + 16 * dt + il];
+            const int m = 16 * mt + 4 * g + q;
+            const float2 v = cmul(lamh[m], iG[(size_t)m * D + 16 * dt + il]);
             accG[di][mt][q] = v.x;
             accG[di][mt + MH][q] = v.y;
           }
       }
     }
-    if (u == 0 && lane < M) eta = iE[lane];
+    if (u == 0 && lane < M) eta = cmul(lamh[lane], iE[lane]);
   }
 
   // Operand copies of the state for the readout of chunk c: lam U (bf16), c_d lam G (fp16,
@@ -536,134 +599,157 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
   auto publish = [&](int c) {
 #pragma unroll
     for (int fi = 0; fi < NFT; ++fi) {
-      const int ft = u + 4 * fi;
+      const int ft = u + NS * fi;
       if (ft < F / 16) {
 #pragma unroll
         for (int mt = 0; mt < MH; ++mt) {
           const int m = 16 * mt + il;
-          const float2 l = x.sLam[m];
-          float re[4], im[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float xr = accU[fi][mt][q], yi = accU[fi][mt + MH][q];
-            re[q] = l.x * xr - l.y * yi;
-            im[q] = l.x * yi + l.y * xr;
-          }
-          *reinterpret_cast<uint2*>(x.sLU + m * RF + 16 * ft + 4 * g) =
-              pack4_bf16(re[0], re[1], re[2], re[3]);
-          *reinterpret_cast<uint2*>(x.sLU + (M + m) * RF + 16 * ft + 4 * g) =
-              pack4_bf16(im[0], im[1], im[2], im[3]);
+          *reinterpret_cast<uint2*>(s16 + pubU[fi] + 16 * mt * F) = pack4_bf16(
+              accU[fi][mt][0], accU[fi][mt][1], accU[fi][mt][2], accU[fi][mt][3]);
+          *reinterpret_cast<uint2*>(s16 + pubU[fi] + (M + 16 * mt) * F) =
+              pack4_bf16(accU[fi][mt + MH][0], accU[fi][mt + MH][1], accU[fi][mt + MH][2],
+                         accU[fi][mt + MH][3]);
         }
       }
     }
 #pragma unroll
     for (int di = 0; di < NDT; ++di) {
-      const int dt = u + 4 * di;
+      const int dt = u + NS * di;
       if (dt < TD) {
         const int d = 16 * dt + il;
-        // Column max of |lam G| first, then the scaled copy (lam G recomputed, not held).
         float mx = 0.f;
 #pragma unroll
-        for (int mt = 0; mt < MH; ++mt)
+        for (int kt = 0; kt < TM; ++kt)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float2 l = x.sLam[16 * mt + 4 * g + q];
-            const float xr = accG[di][mt][q], yi = accG[di][mt + MH][q];
-            mx = fmaxf(mx, fmaxf(fabsf(l.x * xr - l.y * yi), fabsf(l.x * yi + l.y * xr)));
-          }
+          for (int q = 0; q < 4; ++q) mx = fmaxf(mx, fabsf(accG[di][kt][q]));
         mx = xor_max16_32(mx);
         const float cd = pow2_scale(mx);
-        if (g == 0) x.sC[d] = cd;
-#pragma unroll
-        for (int mt = 0; mt < MH; ++mt) {
-          float re[4], im[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float2 l = x.sLam[16 * mt + 4 * g + q];
-            const float xr = accG[di][mt][q], yi = accG[di][mt + MH][q];
-            re[q] = cd * (l.x * xr - l.y * yi);
-            im[q] = cd * (l.x * yi + l.y * xr);
-          }
-          *reinterpret_cast<uint2*>(x.sGT + d * RM + 16 * mt + 4 * g) =
-              pack4_f16(re[0], re[1], re[2], re[3]);
-          *reinterpret_cast<uint2*>(x.sGT + d * RM + M + 16 * mt + 4 * g) =
-              pack4_f16(im[0], im[1], im[2], im[3]);
+        if (g == 0) {
+          *reinterpret_cast<float*>(sb + oCd + 64 * dt) = cd;
+          *reinterpret_cast<float*>(sb + oCd + (Lay::bCi - Lay::bC) + 64 * dt) = 1.f / cd;
         }
+#pragma unroll
+        for (int kt = 0; kt < TM; ++kt)
+          *reinterpret_cast<uint2*>(s16 + pubG[kt >> 1] + 4 * (kt & 1) + 16 * dt * M2) =
+              pack4_f16(cd * accG[di][kt][0], cd * accG[di][kt][1], cd * accG[di][kt][2],
+                        cd * accG[di][kt][3]);
       }
     }
     if (u == 0 && lane < M) {
-      const float2 l = x.sLam[lane];
-      x.sLE[lane] = make_float2(l.x * eta.x - l.y * eta.y, l.x * eta.y + l.y * eta.x);
+      f2(oLn) = eta;
       if (a.N - c * C < C) {
-        x.sPowL[lane] = reinterpret_cast<const float2*>(x.tab + TL::oPowT)[lane];
-        x.sGeo[lane] = reinterpret_cast<const float2*>(x.tab + TL::oGeoT)[lane];
+        f2(oLn + (Lay::bPowL - Lay::bLE)) = reinterpret_cast<const float2*>(x.tab + TL::oPowT)[lane];
+        f2(oLn + (Lay::bGeo - Lay::bLE)) = reinterpret_cast<const float2*>(x.tab + TL::oGeoT)[lane];
+      }
+    }
+  };
+
+  // Raw bf16 q, k, v of the next chunk, fetched while the current chunk computes.
+  uint4 rq[NLF], rk[NLF], rv[NLD];
+  auto fetch = [&](int c) {
+    const int t0 = c * C;
+#pragma unroll
+    for (int t = 0; t < NLF; ++t) {
+      const int n = 64 * u + lane + NL * t;
+      const int row = n / VF, c8 = n % VF;
+      const bool ok = n < C * VF && t0 + row < a.N;
+      const size_t off = ok ? x.tok_index(a, x.pos_of(a, t0 + row)) * F + 8 * c8 : 0;
+      rk[t] = ok ? *reinterpret_cast<const uint4*>(a.k + off) : make_uint4(0, 0, 0, 0);
+      rq[t] = ok && x.want_out ? *reinterpret_cast<const uint4*>(a.q + off)
+                               : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < NLD; ++t) {
+      const int n = 64 * u + lane + NL * t;
+      const int row = n / VD, c8 = n % VD;
+      const bool ok = n < C * VD && t0 + row < a.N;
+      rv[t] = ok ? *reinterpret_cast<const uint4*>(
+                       a.v + x.tok_index(a, x.pos_of(a, t0 + row)) * D + 8 * c8)
+                 : make_uint4(0, 0, 0, 0);
+    }
+  };
+  // phi(k), phi(q) and v rows into LDS.  Tokens past N have zero features and values (zeros,
+  // not phi(0)).
+  // Vector n0 + NL t lands at row row0 + t NL/VF: NL/VF is a multiple of 16, so all rows of
+  // one lane share the swizzle and differ by a constant offset.
+  static_assert((NL / VF) % 16 == 0 && (NL / VD) % 16 == 0, "loader rows keep the swizzle");
+  const int stF = opaque(Lay::oFk + soff<F>((64 * u + lane) / VF, 8 * ((64 * u + lane) % VF)));
+  const int stD = opaque(Lay::oV + soff<D>((64 * u + lane) / VD, 8 * ((64 * u + lane) % VD)));
+  auto store = [&](int c) {
+    const int L = min(C, a.N - c * C);
+#pragma unroll
+    for (int t = 0; t < NLF; ++t) {
+      const int n = 64 * u + lane + NL * t;
+      if (n < C * VF) {
+        const int row = n / VF;
+        const int so = stF + t * (NL / VF) * F;
+        const bool ok = row < L;
+        const uint16_t* ek = reinterpret_cast<const uint16_t*>(&rk[t]);
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = ok ? feature(bf16_to_f32(ek[e])) : 0.f;
+        *reinterpret_cast<uint4*>(s16 + so) =
+            make_uint4(pk_bf16(f[0], f[1]), pk_bf16(f[2], f[3]), pk_bf16(f[4], f[5]),
+                       pk_bf16(f[6], f[7]));
+        if (x.want_out) {
+          const uint16_t* eq = reinterpret_cast<const uint16_t*>(&rq[t]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = feature(bf16_to_f32(eq[e]));
+          *reinterpret_cast<uint4*>(s16 + so + (Lay::oFq - Lay::oFk)) =
+              make_uint4(pk_bf16(f[0], f[1]), pk_bf16(f[2], f[3]), pk_bf16(f[4], f[5]),
+                         pk_bf16(f[6], f[7]));
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NLD; ++t) {
+      const int n = 64 * u + lane + NL * t;
+      if (n < C * VD) {
+        const int row = n / VD;
+        *reinterpret_cast<uint4*>(s16 + stD + t * (NL / VD) * D) =
+            row < L ? rv[t] : make_uint4(0, 0, 0, 0);
       }
     }
   };
 
   __syncthreads();  // tables visible
-  if (x.c_begin < x.c_end) publish(x.c_begin);
+  if (x.c_begin < x.c_end) {
+    publish(x.c_begin);
+    fetch(x.c_begin);
+    store(x.c_begin);
+  }
   __syncthreads();
 
   for (int c = x.c_begin; c < x.c_end; ++c) {
-    // U^T <- lam^(L-1) (lam U^T + phi(K)^T (beta lam^-j)),  G <- lam^(L-1) (lam G + W^T V)
-    bf16x8 afk[NFT][KC], bv[NDT][KC];
+    if (c + 1 < x.c_end) fetch(c + 1);
+    // lam U^T <- lam^L (lam U^T + phi(K)^T (beta lam^-j)),  lam G <- lam^L (lam G + W^T V)
 #pragma unroll
-    for (int fi = 0; fi < NFT; ++fi) {
-      const int ft = u + 4 * fi;
-      if (ft < F / 16) {
+    for (int kb = 0; kb < KC; ++kb) {
+      bf16x8 afk[NFT], bv[NDT];
 #pragma unroll
-        for (int kb = 0; kb < KC; ++kb)
-          afk[fi][kb] = lds8(x.sFkT + (16 * ft + il) * RC + 32 * kb + 8 * g).b;
+      for (int fi = 0; fi < NFT; ++fi)
+        if (u + NS * fi < F / 16) afk[fi] = ldtr<F>(s16, trF[fi], kb).b;
 #pragma unroll
-        for (int mt = 0; mt < MH; ++mt) {
-          const float2 l = x.sLam[16 * mt + il];
+      for (int di = 0; di < NDT; ++di)
+        if (u + NS * di < TD) bv[di] = ldtr<D>(s16, trD[di], kb).b;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float xr = accU[fi][mt][q], yi = accU[fi][mt + MH][q];
-            accU[fi][mt][q] = l.x * xr - l.y * yi;
-            accU[fi][mt + MH][q] = l.x * yi + l.y * xr;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int di = 0; di < NDT; ++di) {
-      const int dt = u + 4 * di;
-      if (dt < TD) {
-#pragma unroll
-        for (int kb = 0; kb < KC; ++kb)
-          bv[di][kb] = lds8(x.sVT + (16 * dt + il) * RC + 32 * kb + 8 * g).b;
-#pragma unroll
-        for (int mt = 0; mt < MH; ++mt)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float2 l = x.sLam[16 * mt + 4 * g + q];
-            const float xr = accG[di][mt][q], yi = accG[di][mt + MH][q];
-            accG[di][mt][q] = l.x * xr - l.y * yi;
-            accG[di][mt + MH][q] = l.x * yi + l.y * xr;
-          }
-      }
-    }
-#pragma unroll
-    for (int kt = 0; kt < TM; ++kt) {
-#pragma unroll
-      for (int kb = 0; kb < KC; ++kb) {
-        const bf16x8 w = lds8(x.sWT + (16 * kt + il) * RC + 32 * kb + 8 * g).b;
+      for (int kt = 0; kt < TM; ++kt) {
+        const bf16x8 w = lds8(s16 + offC[kb] + 16 * kt * C).b;
 #pragma unroll
         for (int fi = 0; fi < NFT; ++fi)
-          if (u + 4 * fi < F / 16) accU[fi][kt] = mma_bf16(afk[fi][kb], w, accU[fi][kt]);
+          if (u + NS * fi < F / 16) accU[fi][kt] = mma_bf16(afk[fi], w, accU[fi][kt]);
 #pragma unroll
         for (int di = 0; di < NDT; ++di)
-          if (u + 4 * di < TD) accG[di][kt] = mma_bf16(w, bv[di][kb], accG[di][kt]);
+          if (u + NS * di < TD) accG[di][kt] = mma_bf16(w, bv[di], accG[di][kt]);
+        IA_STEP_FENCE();
       }
     }
 #pragma unroll
     for (int fi = 0; fi < NFT; ++fi)
-      if (u + 4 * fi < F / 16) {
+      if (u + NS * fi < F / 16) {
 #pragma unroll
         for (int mt = 0; mt < MH; ++mt) {
-          const float2 p = x.sPowL[16 * mt + il];
+          const float2 p = f2(oPl + 128 * mt);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float xr = accU[fi][mt][q], yi = accU[fi][mt + MH][q];
@@ -674,29 +760,30 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
       }
 #pragma unroll
     for (int di = 0; di < NDT; ++di)
-      if (u + 4 * di < TD) {
+      if (u + NS * di < TD) {
 #pragma unroll
         for (int mt = 0; mt < MH; ++mt)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float2 p = x.sPowL[16 * mt + 4 * g + q];
+            const float2 p = f2(oPg + 8 * (16 * mt + q));
             const float xr = accG[di][mt][q], yi = accG[di][mt + MH][q];
             accG[di][mt][q] = p.x * xr - p.y * yi;
             accG[di][mt + MH][q] = p.x * yi + p.y * xr;
           }
       }
     if (u == 0 && lane < M) {
-      const float2 l = x.sLam[lane], p = x.sPowL[lane], ge = x.sGeo[lane];
-      const float2 t = make_float2(l.x * eta.x - l.y * eta.y + ge.x,
-                                   l.x * eta.y + l.y * eta.x + ge.y);
-      eta = make_float2(p.x * t.x - p.y * t.y, p.x * t.y + p.y * t.x);
+      const float2 ge = f2(oLn + (Lay::bGeo - Lay::bLE));
+      eta = cmul(f2(oLn + (Lay::bPowL - Lay::bLE)), make_float2(eta.x + ge.x, eta.y + ge.y));
     }
     __syncthreads();
-    if (c + 1 < x.c_end) publish(c + 1);
+    if (c + 1 < x.c_end) {
+      store(c + 1);   // first: frees the fetch registers before publish needs temporaries
+      publish(c + 1);
+    }
     __syncthreads();
   }
 
-  // Final state.
+  // Final state (divided by lam).
   float2 *fU = nullptr, *fG = nullptr, *fE = nullptr;
   if (a.fin_seg) {
     float2* base = a.fin_seg + ((size_t)x.seq * a.slots_per_seq + x.seg + 1) * a.slot;
@@ -709,33 +796,37 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
     fE = a.fin_E + (size_t)x.seq * M;
   }
   if (fU) {
+    const float2* inv = reinterpret_cast<const float2*>(x.tab + TL::oInv);
 #pragma unroll
     for (int fi = 0; fi < NFT; ++fi) {
-      const int ft = u + 4 * fi;
+      const int ft = u + NS * fi;
       if (ft < F / 16) {
 #pragma unroll
         for (int mt = 0; mt < MH; ++mt) {
           const int m = 16 * mt + il;
+          const float2 li = inv[m];
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             fU[(size_t)m * F + 16 * ft + 4 * g + q] =
-                make_float2(accU[fi][mt][q], accU[fi][mt + MH][q]);
+                cmul(li, make_float2(accU[fi][mt][q], accU[fi][mt + MH][q]));
         }
       }
     }
 #pragma unroll
     for (int di = 0; di < NDT; ++di) {
-      const int dt = u + 4 * di;
+      const int dt = u + NS * di;
       if (dt < TD) {
 #pragma unroll
         for (int mt = 0; mt < MH; ++mt)
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            fG[(size_t)(16 * mt + 4 * g + q) * D + 16 * dt + il] =
-                make_float2(accG[di][mt][q], accG[di][mt + MH][q]);
+          for (int q = 0; q < 4; ++q) {
+            const int m = 16 * mt + 4 * g + q;
+            fG[(size_t)m * D + 16 * dt + il] =
+                cmul(inv[m], make_float2(accG[di][mt][q], accG[di][mt + MH][q]));
+          }
       }
     }
-    if (u == 0 && lane < M) fE[lane] = eta;
+    if (u == 0 && lane < M) fE[lane] = cmul(inv[lane], eta);
   }
 }
 
@@ -754,26 +845,30 @@ __device__ __forceinline__ void dispatch_role(const ChunkArgs& a, const Ctx<C, F
 }
 
 template <int C, int F, int D, int M>
-__global__ void __launch_bounds__(64 * (C / 16 + 4))
+__global__ void __launch_bounds__(64 * (C / 16 + StateWaves<F, D, M>::NS))
 chunk_prefill_kernel(const ChunkArgs a) {
-  using Lay = Layout<C, F, D, M>;
+  using Lay = Layout<C, F, D, M, C / 16>;
   using TL = TableLayout<C, M>;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   uint16_t* s16 = reinterpret_cast<uint16_t*>(smem_raw);
 
   Ctx<C, F, D, M> x;
+  x.s16 = s16;
   x.sFk = s16 + Lay::oFk;
-  x.sFkT = s16 + Lay::oFkT;
-  x.sVT = s16 + Lay::oVT;
+  x.sFq = s16 + Lay::oFq;
+  x.sV = s16 + Lay::oV;
   x.sWT = s16 + Lay::oWT;
   x.sWb = s16 + Lay::oWb;
   x.sLU = s16 + Lay::oLU;
   x.sGT = s16 + Lay::oGT;
   x.sC = reinterpret_cast<float*>(smem_raw + Lay::bC);
+  x.sCi = reinterpret_cast<float*>(smem_raw + Lay::bCi);
   x.sLE = reinterpret_cast<float2*>(smem_raw + Lay::bLE);
   x.sLam = reinterpret_cast<float2*>(smem_raw + Lay::bLam);
   x.sPowL = reinterpret_cast<float2*>(smem_raw + Lay::bPowL);
   x.sGeo = reinterpret_cast<float2*>(smem_raw + Lay::bGeo);
+  x.sL2lo = reinterpret_cast<float2*>(smem_raw + Lay::bL2lo);
+  x.sL2hi = reinterpret_cast<float2*>(smem_raw + Lay::bL2hi);
   const int tid = threadIdx.x;
   x.lane = tid & 63;
   x.wave = tid >> 6;
@@ -790,12 +885,19 @@ chunk_prefill_kernel(const ChunkArgs a) {
   x.want_out = a.o != nullptr;
   x.tab = a.tables + (size_t)x.h * a.table_bytes;
 
-  // Per-head tables -> LDS (sWT and sWb are adjacent, padded alike, in LDS and the table).
-  static_assert(Lay::oWb == Lay::oWT + 2 * M * Lay::RC, "tables adjacent");
+  // Per-head tables -> LDS: the decay tables (adjacent in LDS and in the table) and the two
+  // lam^(2i) factor tables (likewise adjacent).
+  static_assert(Lay::oWb == Lay::oWT + 2 * M * C, "decay tables adjacent");
+  static_assert(Lay::bL2hi == Lay::bL2lo + 16 * Lay::L2S * 8, "factor tables adjacent");
+  static_assert(TL::nW == 2L * (Lay::oLU - Lay::oWT), "decay table size");
+  static_assert(TL::nL2 == Lay::bytes - Lay::bL2lo, "factor table size");
   {
     const uint4* src = reinterpret_cast<const uint4*>(x.tab + TL::oW);
     uint4* dst = reinterpret_cast<uint4*>(x.sWT);
     for (int e = tid; e < (int)(TL::nW / 16); e += blockDim.x) dst[e] = src[e];
+    const uint4* src2 = reinterpret_cast<const uint4*>(x.tab + TL::oL2);
+    uint4* dst2 = reinterpret_cast<uint4*>(x.sL2lo);
+    for (int e = tid; e < (int)(TL::nL2 / 16); e += blockDim.x) dst2[e] = src2[e];
   }
   x.wb_unscale = *reinterpret_cast<const float*>(x.tab + TL::oSc);
   const float2* lamh = a.lam + (size_t)x.h * M;
@@ -806,13 +908,14 @@ chunk_prefill_kernel(const ChunkArgs a) {
   }
   // Both roles run the same sequence of block barriers.  Each wave runs code specialised
   // for its index, so trip counts and owned tiles are compile-time constants.
-  dispatch_role<C, F, D, M>(a, x, x.wave, std::make_integer_sequence<int, C / 16 + 4>{});
+  dispatch_role<C, F, D, M>(
+      a, x, x.wave, std::make_integer_sequence<int, C / 16 + StateWaves<F, D, M>::NS>{});
 }
 
 template <int C, int F, int D, int M>
 hipError_t launch_chunk_t(const ChunkArgs& a, int n_wg, hipStream_t st, int kind) {
-  constexpr int threads = 64 * (C / 16 + 4);
-  constexpr int bytes = Layout<C, F, D, M>::bytes;
+  constexpr int threads = 64 * (C / 16 + StateWaves<F, D, M>::NS);
+  constexpr int bytes = Layout<C, F, D, M, C / 16>::bytes;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   static bool attr_set = false;
   if (!attr_set) {
