@@ -225,6 +225,17 @@ def cpu_baseline(inp, bidir, budget_s=12.0):
                       f"{wall:.1f} s wall; one slice alone {one:.2f} s"}
 
 
+def calib_copy(torch, mib=256):
+    """A plain elementwise kernel (negation, fp32) that reads and writes `mib` MiB once each:
+    the reference point for FETCH_SIZE / WRITE_SIZE."""
+    src = torch.ones(mib * 2 ** 18, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,6 +244,9 @@ def main():
     ap.add_argument("--workload", default="1.3b", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first run a plain streaming kernel over 256 MiB (read 256 MiB, write "
+                         "256 MiB) whose counter readings scale the hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -245,11 +259,13 @@ def main():
     import ssm_sequence_mixer_amd as ia
 
     torch.cuda.init()
+    if args.calib_copy:
+        calib_copy(torch)
     pf = bench_prefill(args, torch, ia, W)
     dec = None if args.no_decode else bench_decode(torch, ia, W)
     cpu = None if args.no_cpu else cpu_baseline(pf["inp"], pf["cfg"]["bidirectional"])
     line = {
-        "metric": "IA layer fwd tokens/s (prefill)",
+        "metric": "IA layer fwd tokens/s (prefill) + decode step latency; % of MFMA/HBM roofline",
         "value": pf["tokens"] / (pf["ms"] * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,

@@ -110,7 +110,8 @@ ChunkPlan chunk_plan(const ia_desc* d) {
   p.tables_off = 0;
   p.bytes = round_up(size_t(d->H) * ia::chunk_table_bytes(p.C, d->M));
   p.slots_off = p.bytes;
-  if (p.G > 1) p.bytes += round_up(size_t(seqs) * p.G * d->M * (d->F + d->Dv + 1) * 8);
+  if (p.G > 1)
+    p.bytes += round_up(size_t(seqs) * (p.G - 1) * ia::chunk_slot_floats(d->F, d->Dv, d->M) * 4);
   p.acc_off = p.bytes;
   if (d->flags & IA_FLAG_BIDIR) p.bytes += round_up(size_t(d->B) * d->N * d->H * d->Dv * 4);
   return p;
@@ -250,7 +251,7 @@ ia_status ia_prefill_fwd(const ia_desc* d, const void* q, const void* k, const v
       a.G0 = a.G1 = static_cast<float2*>(st->Gamma);
       a.E0 = a.E1 = static_cast<float2*>(st->eta);
     }
-    a.slots = reinterpret_cast<float2*>(ws + pl.slots_off);
+    a.slots = reinterpret_cast<float*>(ws + pl.slots_off);
     a.tables = reinterpret_cast<unsigned char*>(ws + pl.tables_off);
     a.B = d->B; a.H = d->H; a.N = d->N; a.F = d->F; a.D = d->Dv; a.M = d->M;
     a.chunk = pl.C;

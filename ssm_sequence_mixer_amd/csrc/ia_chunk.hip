@@ -1,5 +1,5 @@
-// ia_chunk.hip — chunked IA prefill: per-head tables, the segment carry scan, and the
-// host-side dispatch over the kernel instantiations (which live in ia_chunk_f*.hip).
+// ia_chunk.hip — chunked IA prefill: per-head tables and the host-side dispatch over the
+// kernel instantiations (which live in ia_chunk_f*.hip).
 #include "ia_chunk.hpp"
 
 namespace ia {
@@ -17,109 +17,81 @@ IA_EXTERN_C(64)
 #undef IA_EXTERN
 
 // ---------------------------------------------------------------- per-head tables
-// Once per call, one block per head, one thread per (mode, run of 16 exponents).  Written in
-// the LDS form the prefill kernel copies verbatim: beta lam^-j in bf16 ([Re;Im] rows, j in
-// K-slot order) and in scaled fp16 (row j, modes in K-slot order), both swizzled; the
-// factors lam^(2i), i < 16, and lam^(32r); per mode lam^C, sum_{j<C} beta lam^-j, the same
-// two for the last chunk's length Lt, lam^Ls for the segment length Ls, and 1/lam.  Each run
-// starts from exp/log and continues by products.
+// Once per call.  Block (h, run) holds one thread per (mode m, exponent j) with j in
+// [16 run, 16 run + 16); each entry is a direct complex power exp(n log lam).  Written in the
+// LDS form the prefill kernel copies verbatim: beta lam^-j in bf16 ([Re;Im] rows, j in K-slot
+// order) and in scaled fp16 (row j, modes in K-slot order), both swizzled.  Block run 0 also
+// writes the factors lam^(2i), i < 16, and lam^(32r); per mode lam^C, sum_{j<C} beta lam^-j,
+// the same two for the last chunk's length Lt, lam^Ls for the segment length Ls, and 1/lam.
 template <int C, int M>
-__global__ void chunk_tables_kernel(const float2* __restrict__ lam,
+__global__ void __launch_bounds__(16 * M) chunk_tables_kernel(const float2* __restrict__ lam,
                                     const float2* __restrict__ beta, unsigned char* tables,
                                     long table_bytes, int Lt, int Ls) {
   using TL = TableLayout<C, M>;
   constexpr int M2 = 2 * M;
   constexpr int RUNS = C / 16;
   constexpr int L2S = M + 2;
-  const int h = blockIdx.x;
+  const int h = blockIdx.x, run = blockIdx.y;
   unsigned char* tab = tables + (size_t)h * table_bytes;
   uint16_t* WT = reinterpret_cast<uint16_t*>(tab + TL::oW);
   uint16_t* Wb = WT + M2 * C;
   float2* L2lo = reinterpret_cast<float2*>(tab + TL::oL2);
   float2* L2hi = L2lo + 16 * L2S;
-  const int m = threadIdx.x % M, run = threadIdx.x / M;
+  const int m = threadIdx.x % M, jj = threadIdx.x / M;
+  const int j = 16 * run + jj;
   const float2 l = lam[(size_t)h * M + m];
   const float2 bt = beta[(size_t)h * M + m];
-  __shared__ float s_wmax[M * RUNS];
+  __shared__ float s_max[16 * M];
+  __shared__ float2 s_geo[16 * M], s_geot[16 * M];
 
-  // fp16 table exponent: max_j |beta lam^-j| = |beta| |lam|^-(C-1) (|lam| <= 1).
+  // fp16 table exponent: max_j |beta lam^-j| = |beta| |lam|^-(C-1) (|lam| <= 1); every block
+  // of the head reduces the same values, so all agree on the scale.
   const float2 pc1 = cpow_f(l, (float)(C - 1));
-  s_wmax[threadIdx.x] = hypotf(bt.x, bt.y) / hypotf(pc1.x, pc1.y);
+  s_max[threadIdx.x] = hypotf(bt.x, bt.y) / hypotf(pc1.x, pc1.y);
   __syncthreads();
-  for (int st = (M * RUNS) / 2; st > 0; st >>= 1) {
-    if (threadIdx.x < st)
-      s_wmax[threadIdx.x] = fmaxf(s_wmax[threadIdx.x], s_wmax[threadIdx.x + st]);
+  for (int st = 8 * M; st > 0; st >>= 1) {
+    if (threadIdx.x < st) s_max[threadIdx.x] = fmaxf(s_max[threadIdx.x], s_max[threadIdx.x + st]);
     __syncthreads();
   }
-  const float wscale = pow2_scale(s_wmax[0]);
-  if (threadIdx.x == 0) *reinterpret_cast<float*>(tab + TL::oSc) = 1.f / wscale;
+  const float wscale = pow2_scale(s_max[0]);
 
-  const float2 inv = cpow_f(l, -1.f);
-  float2 p = cpow_f(l, -16.f * run);
-  for (int j = 16 * run; j < 16 * run + 16; ++j) {
-    const float2 w = cmul(bt, p);
-    WT[soff<C>(m, kpos(j))] = __builtin_bit_cast(uint16_t, (__bf16)w.x);
-    WT[soff<C>(M + m, kpos(j))] = __builtin_bit_cast(uint16_t, (__bf16)w.y);
-    Wb[soff<M2>(j, kpos(m))] = __builtin_bit_cast(uint16_t, (_Float16)(w.x * wscale));
-    Wb[soff<M2>(j, kpos(M + m))] = __builtin_bit_cast(uint16_t, (_Float16)(w.y * wscale));
-    p = cmul(p, inv);
+  const float2 w = cmul(bt, cpow_f(l, -(float)j));
+  WT[soff<C>(m, kpos(j))] = __builtin_bit_cast(uint16_t, (__bf16)w.x);
+  WT[soff<C>(M + m, kpos(j))] = __builtin_bit_cast(uint16_t, (__bf16)w.y);
+  Wb[soff<M2>(j, kpos(m))] = __builtin_bit_cast(uint16_t, (_Float16)(w.x * wscale));
+  Wb[soff<M2>(j, kpos(M + m))] = __builtin_bit_cast(uint16_t, (_Float16)(w.y * wscale));
+  if (run != 0) return;
+
+  if (threadIdx.x == 0) *reinterpret_cast<float*>(tab + TL::oSc) = 1.f / wscale;
+  L2lo[jj * L2S + m] = cpow_f(l, 2.f * jj);
+  if (jj < RUNS) L2hi[jj * M + m] = cpow_f(l, 32.f * jj);
+  // Geometric sums over j < C and j < Lt: thread jj takes j = jj, jj + 16, ...
+  float2 geo = make_float2(0.f, 0.f), geot = geo;
+  for (int jx = jj; jx < C; jx += 16) {
+    const float2 t = cmul(bt, cpow_f(l, -(float)jx));
+    geo.x += t.x;
+    geo.y += t.y;
+    if (jx < Lt) {
+      geot.x += t.x;
+      geot.y += t.y;
+    }
   }
-  if (run == 0) {
-    const float2 l2 = cmul(l, l);
-    float2 qq = make_float2(1.f, 0.f);
-    for (int i = 0; i < 16; ++i) {
-      L2lo[i * L2S + m] = qq;
-      qq = cmul(qq, l2);
+  s_geo[threadIdx.x] = geo;
+  s_geot[threadIdx.x] = geot;
+  __syncthreads();
+  if (jj == 0) {
+    for (int k = 1; k < 16; ++k) {
+      geo.x += s_geo[k * M + m].x;
+      geo.y += s_geo[k * M + m].y;
+      geot.x += s_geot[k * M + m].x;
+      geot.y += s_geot[k * M + m].y;
     }
-    for (int r = 0; r < RUNS; ++r) L2hi[r * M + m] = cpow_f(l, 32.f * r);
-    float2 pj = make_float2(1.f, 0.f), geo = make_float2(0.f, 0.f), geot = geo;
-    for (int j = 0; j < C; ++j) {
-      if (j == Lt) geot = geo;
-      geo = cfma(bt, pj, geo);
-      pj = cmul(pj, inv);
-    }
-    if (Lt >= C) geot = geo;
     reinterpret_cast<float2*>(tab + TL::oPow)[m] = cpow_f(l, (float)C);
     reinterpret_cast<float2*>(tab + TL::oGeo)[m] = geo;
     reinterpret_cast<float2*>(tab + TL::oPowT)[m] = cpow_f(l, (float)Lt);
     reinterpret_cast<float2*>(tab + TL::oGeoT)[m] = geot;
     reinterpret_cast<float2*>(tab + TL::oPowS)[m] = cpow_f(l, (float)Ls);
-    reinterpret_cast<float2*>(tab + TL::oInv)[m] = inv;
-  }
-}
-
-// ---------------------------------------------------------------- segment carry scan
-// Slots of a sequence: 0 = initial state, g = 1..G-1 = end state of segment g-1 computed
-// from zero.  In place: slot g <- lam^Ls slot(g-1) + slot g, so slot g becomes the state
-// entering segment g.  One thread per (sequence, state element); segments in order.
-__global__ void carry_scan_kernel(const float2* __restrict__ U0, const float2* __restrict__ G0,
-                                  const float2* __restrict__ E0, float2* __restrict__ slots,
-                                  const unsigned char* __restrict__ tables, long table_bytes,
-                                  long pows_off, int H, int F, int D, int M, int G, long slot) {
-  const int seq = blockIdx.y;
-  const int h = seq % H;
-  const long n = (long)M * (F + D + 1);
-  const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= n) return;
-  int m;
-  float2 c = make_float2(0.f, 0.f);
-  if (e < (long)M * F) {
-    m = int(e / F);
-    if (U0) c = U0[(size_t)seq * M * F + e];
-  } else if (e < (long)M * (F + D)) {
-    m = int((e - (long)M * F) / D);
-    if (G0) c = G0[(size_t)seq * M * D + (e - (long)M * F)];
-  } else {
-    m = int(e - (long)M * (F + D));
-    if (E0) c = E0[(size_t)seq * M + m];
-  }
-  const float2 pw =
-      reinterpret_cast<const float2*>(tables + (size_t)h * table_bytes + pows_off)[m];
-  float2* s = slots + (size_t)seq * G * slot + e;
-  s[0] = c;
-  for (int gi = 1; gi < G; ++gi) {
-    c = cfma(pw, c, s[(size_t)gi * slot]);
-    s[(size_t)gi * slot] = c;
+    reinterpret_cast<float2*>(tab + TL::oInv)[m] = cpow_f(l, -1.f);
   }
 }
 
@@ -142,8 +114,8 @@ static hipError_t launch_tables_cm(const ChunkPrefillArgs& p, long tb, hipStream
   const int Lt = p.N % C == 0 ? C : p.N % C;
   (void)hipGetLastError();
   prof_begin(st);
-  hipLaunchKernelGGL((chunk_tables_kernel<C, M>), dim3(p.H), dim3(M * (C / 16)), 0, st, p.lam,
-                     p.beta, p.tables, tb, Lt, p.seg_chunks * C);
+  hipLaunchKernelGGL((chunk_tables_kernel<C, M>), dim3(p.H, C / 16), dim3(16 * M), 0, st,
+                     p.lam, p.beta, p.tables, tb, Lt, p.seg_chunks * C);
   prof_end(st, kKindTables);
   return hipGetLastError();
 }
@@ -174,24 +146,23 @@ long chunk_table_bytes(int chunk, int M) {
   return 0;
 }
 
-static long pows_offset(int chunk, int M) {
-  switch (chunk * 1000 + M) {
-    case 32016: return TableLayout<32, 16>::oPowS;
-    case 32032: return TableLayout<32, 32>::oPowS;
-    case 32064: return TableLayout<32, 64>::oPowS;
-    case 64016: return TableLayout<64, 16>::oPowS;
-    case 64032: return TableLayout<64, 32>::oPowS;
-    case 64064: return TableLayout<64, 64>::oPowS;
-  }
+long chunk_slot_floats(int F, int D, int M) {
+#define IA_SLOT(FF, MM) \
+  if (F == FF && D == FF && M == MM) return SlotLayout<FF, FF, MM>::floats;
+  IA_SLOT(32, 16) IA_SLOT(32, 32) IA_SLOT(32, 64)
+  IA_SLOT(64, 16) IA_SLOT(64, 32) IA_SLOT(64, 64)
+  IA_SLOT(128, 16) IA_SLOT(128, 32) IA_SLOT(128, 64)
+#undef IA_SLOT
   return 0;
 }
 
-// Full chunked prefill for one direction: tables, segment end states, carry scan, outputs.
+// Full chunked prefill for one direction: tables; the end states of segments 0..G-2 from a
+// zero state; every segment (or, state only, the last) from its initial state, which each
+// workgroup assembles from the caller's state and the earlier segments' end states.
 hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
   const int C = p.chunk;
   const int n_chunks = (p.N + C - 1) / C;
   const int seqs = p.B * p.H;
-  const long slot = (long)p.M * (p.F + p.D + 1);
   const int G = p.segments;
   const int seg_chunks = p.seg_chunks;
   const long tb = chunk_table_bytes(C, p.M);
@@ -213,8 +184,8 @@ hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
   a.dir = p.reverse;
   a.out_bf16 = p.out_bf16;
   a.clamp = p.clamp;
-  a.slot = slot;
-  a.slots_per_seq = G;
+  a.slot_floats = chunk_slot_floats(p.F, p.D, p.M);
+  a.slots_per_seq = G - 1;
   a.tables = p.tables;
   a.table_bytes = tb;
 
@@ -223,32 +194,22 @@ hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
                    : dispatch_fdm<32>(x, p.F, p.D, p.M, n_wg, st, kind);
   };
 
-  ChunkArgs o = a;
   if (G > 1) {
-    // Pass 1: end state of segments 0..G-2 from a zero state, into slots 1..G-1.
+    // Pass 1: end state of segments 0..G-2 from a zero state.
     ChunkArgs s = a;
     s.seg_first = 0;
     s.n_seg = G - 1;
-    s.fin_seg = p.slots;
+    s.seg_end = p.slots;
     e = go(s, seqs * (G - 1), kKindSummary);
     if (e != hipSuccess) return e;
-    // Carries: slot g <- state entering segment g (slot 0 <- the initial state).
-    (void)hipGetLastError();
-    prof_begin(st);
-    hipLaunchKernelGGL(carry_scan_kernel, dim3((unsigned)((slot + 255) / 256), seqs), dim3(256),
-                       0, st, p.U0, p.G0, p.E0, p.slots, p.tables, tb, pows_offset(C, p.M), p.H,
-                       p.F, p.D, p.M, G, slot);
-    prof_end(st, kKindCarry);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    o.initc = p.slots;
-  } else {
-    o.init0_U = p.U0;
-    o.init0_G = p.G0;
-    o.init0_E = p.E0;
   }
-  // Pass 2: every segment from its corrected initial state, with outputs; the last segment
-  // returns the final state.  State-only calls run just the last segment.
+  // Pass 2: every segment from its initial state, with outputs; the last segment returns the
+  // final state.  State-only calls run just the last segment.
+  ChunkArgs o = a;
+  o.seg_prev = G > 1 ? p.slots : nullptr;
+  o.init0_U = p.U0;
+  o.init0_G = p.G0;
+  o.init0_E = p.E0;
   o.o = p.o;
   o.acc_in = p.acc_in;
   o.fin_U = p.U1;

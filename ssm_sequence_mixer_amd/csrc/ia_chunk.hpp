@@ -201,6 +201,19 @@ struct StateWaves {
   static constexpr int NS = (F + D >= 256 && M >= 64) ? 8 : 4;
 };
 
+// Workspace slot of one segment's end state, in the state waves' accumulator layout: wave u,
+// tile t (f tiles then d tiles), lane l, 4 floats at ((u * NT + t) * 64 + l) * 4; lam eta
+// (complex, per mode) after the NS wave blocks.  Each lane moves 16 contiguous bytes per tile.
+template <int F, int D, int M>
+struct SlotLayout {
+  static constexpr int NS = StateWaves<F, D, M>::NS;
+  static constexpr int NFT = (F / 16 + NS - 1) / NS, NDT = (D / 16 + NS - 1) / NS;
+  static constexpr int TM = 2 * M / 16;
+  static constexpr int NT = (NFT + NDT) * TM;       // tiles per wave
+  static constexpr long eta = (long)NS * NT * 256;  // float offset of lam eta
+  static constexpr long floats = eta + 2L * M;
+};
+
 // ---------------------------------------------------------------- LDS layout
 
 template <int C, int F, int D, int M, int NR>
@@ -240,15 +253,17 @@ struct ChunkArgs {
   int dir;                     // 1: the walk runs from position N-1 down to 0
   int out_bf16;
   float clamp;
-  // Initial state: workspace slot `seg` of the sequence when `initc` is set, else (one
-  // segment) the caller's state `init0` or zeros.  Final state: with `fin_seg` set, segment
-  // g writes slot g+1; otherwise the segment holding the last token writes the caller's
-  // `fin` (if set).  Slot components: U at 0, G at M*F, eta at M*(F+D) (complex elements).
+  // Initial state of segment g: the caller's state init0 (or zeros) carried across segments
+  // 0..g-1, whose end states (each computed from a zero state) are the workspace slots
+  // seg_prev[seq][0..g-1]: state <- lam^Ls state + slot, Ls the segment length.  Final state:
+  // with seg_end set, segment g writes slot seg_end[seq][g]; otherwise the segment holding
+  // the last token writes the caller's fin (if set).  Slots hold lam U, lam G and lam eta in
+  // the state waves' accumulator layout (SlotLayout).
   const float2 *init0_U, *init0_G, *init0_E;   // caller layout: [seq][M][F] etc.
-  const float2* initc;
   float2 *fin_U, *fin_G, *fin_E;               // caller layout
-  float2* fin_seg;
-  long slot;                                   // complex elements per slot
+  const float* seg_prev;
+  float* seg_end;
+  long slot_floats;                            // floats per slot
   int slots_per_seq;
   const unsigned char* tables;                 // per-head tables (chunk_tables_kernel)
   long table_bytes;                            // bytes per head
@@ -333,7 +348,33 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
   const int oCi = opaque(Lay::bCi + 16 * g);
   static_assert(Lay::bL2hi + 8 * (NR * M) - Lay::bLE < 65536, "tables within the immediate range");
 
+  // ---- v loader: this wave moves rows 16r + il of the chunk's v, 16-byte blocks g + 4t, from
+  // HBM to LDS (raw bf16).  Token rows are H*D elements apart, backwards in reverse.
+  constexpr int VD = D / 8, NV = VD / 4;
+  int stV[NV];
+#pragma unroll
+  for (int t = 0; t < NV; ++t) stV[t] = opaque(Lay::oV + soff<D>(16 * r + il, 8 * (g + 4 * t)));
+  const int lofV = (a.dir ? -1 : 1) * (16 * r + il) * (a.H * D) + 8 * g;
+  uint4 rv[NV];
+  auto fetch_v = [&](int c) {
+    const int t0 = c * C;
+    const uint16_t* vb = a.v + x.tok_index(a, x.pos_of(a, t0)) * D + lofV;
+    const bool ok = t0 + 16 * r + il < a.N;
+#pragma unroll
+    for (int t = 0; t < NV; ++t)
+      rv[t] = ok ? *reinterpret_cast<const uint4*>(vb + 32 * t) : make_uint4(0, 0, 0, 0);
+  };
+  auto write_v = [&]() {
+#pragma unroll
+    for (int t = 0; t < NV; ++t) *reinterpret_cast<uint4*>(x.s16 + stV[t]) = rv[t];
+  };
+
   __syncthreads();  // tables visible
+  if (x.c_begin < x.c_end) {
+    fetch_v(x.c_begin);
+    write_v();
+    if (x.c_begin + 1 < x.c_end) fetch_v(x.c_begin + 1);
+  }
   __syncthreads();  // first chunk in LDS
 
   for (int c = x.c_begin; c < x.c_end; ++c) {
@@ -478,7 +519,11 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
         IA_STEP_FENCE();
       }
     }
-    __syncthreads();
+    __syncthreads();   // chunk c read by every wave
+    if (c + 1 < x.c_end) {
+      write_v();
+      if (c + 2 < x.c_end) fetch_v(c + 2);
+    }
     __syncthreads();
   }
 }
@@ -503,9 +548,9 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
   const int lane = x.lane, il = x.il, g = x.g;
   // Loader share of this wave: 16-byte vectors n = 64u + lane + 64 NS t of the row-major
   // chunk matrices q, k ([C][F]) and v ([C][D]).
-  constexpr int VF = F / 8, VD = D / 8;
+  constexpr int VF = F / 8;
   constexpr int NL = 64 * NS;
-  constexpr int NLF = (C * VF + NL - 1) / NL, NLD = (C * VD + NL - 1) / NL;
+  constexpr int NLF = (C * VF + NL - 1) / NL;
   // Per-lane LDS offsets (tiles add compile-time constants).
   // Offsets from the LDS base, matrix start included (see opaque).
   int offC[KC], trF[NFT], trD[NDT], pubU[NFT], pubG[TM / 2];
@@ -544,14 +589,11 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
 #pragma unroll
     for (int kt = 0; kt < TM; ++kt) accG[di][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Initial state (times lam).
+  // Initial state (times lam): the caller's state, then the end states of the earlier
+  // segments of this sequence.
+  using SL = SlotLayout<F, D, M>;
   const float2 *iU = nullptr, *iG = nullptr, *iE = nullptr;
-  if (a.initc) {
-    const float2* base = a.initc + ((size_t)x.seq * a.slots_per_seq + x.seg) * a.slot;
-    iU = base;
-    iG = base + (size_t)M * F;
-    iE = base + (size_t)M * (F + D);
-  } else if (x.seg == 0 && a.init0_U) {
+  if (a.init0_U) {
     iU = a.init0_U + (size_t)x.seq * M * F;
     iG = a.init0_G + (size_t)x.seq * M * D;
     iE = a.init0_E + (size_t)x.seq * M;
@@ -592,31 +634,68 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
     }
     if (u == 0 && lane < M) eta = cmul(lamh[lane], iE[lane]);
   }
-
-  // Operand copies of the state for the readout of chunk c: lam U (bf16), c_d lam G (fp16,
-  // c_d a power of two per value column), lam eta; and chunk c's decay factors if it is the
-  // last, partial chunk.
-  auto publish = [&](int c) {
+  if (a.seg_prev && x.seg > 0) {
+    const float2* pows = reinterpret_cast<const float2*>(x.tab + TL::oPowS);
+    for (int sp = 0; sp < x.seg; ++sp) {
+      const float* sl = a.seg_prev + ((size_t)x.seq * a.slots_per_seq + sp) * a.slot_floats;
 #pragma unroll
-    for (int fi = 0; fi < NFT; ++fi) {
-      const int ft = u + NS * fi;
-      if (ft < F / 16) {
+      for (int fi = 0; fi < NFT; ++fi)
+        if (u + NS * fi < F / 16) {
 #pragma unroll
-        for (int mt = 0; mt < MH; ++mt) {
-          const int m = 16 * mt + il;
-          *reinterpret_cast<uint2*>(s16 + pubU[fi] + 16 * mt * F) = pack4_bf16(
-              accU[fi][mt][0], accU[fi][mt][1], accU[fi][mt][2], accU[fi][mt][3]);
-          *reinterpret_cast<uint2*>(s16 + pubU[fi] + (M + 16 * mt) * F) =
-              pack4_bf16(accU[fi][mt + MH][0], accU[fi][mt + MH][1], accU[fi][mt + MH][2],
-                         accU[fi][mt + MH][3]);
+          for (int mt = 0; mt < MH; ++mt) {
+            const float2 p = pows[16 * mt + il];
+            const float4 e0 = *reinterpret_cast<const float4*>(
+                sl + ((u * SL::NT + fi * TM + mt) * 64 + lane) * 4);
+            const float4 e1 = *reinterpret_cast<const float4*>(
+                sl + ((u * SL::NT + fi * TM + mt + MH) * 64 + lane) * 4);
+            const float er[4] = {e0.x, e0.y, e0.z, e0.w}, ei[4] = {e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float xr = accU[fi][mt][q], yi = accU[fi][mt + MH][q];
+              accU[fi][mt][q] = p.x * xr - p.y * yi + er[q];
+              accU[fi][mt + MH][q] = p.x * yi + p.y * xr + ei[q];
+            }
+          }
         }
+#pragma unroll
+      for (int di = 0; di < NDT; ++di)
+        if (u + NS * di < TD) {
+#pragma unroll
+          for (int mt = 0; mt < MH; ++mt) {
+            const float4 e0 = *reinterpret_cast<const float4*>(
+                sl + ((u * SL::NT + (NFT + di) * TM + mt) * 64 + lane) * 4);
+            const float4 e1 = *reinterpret_cast<const float4*>(
+                sl + ((u * SL::NT + (NFT + di) * TM + mt + MH) * 64 + lane) * 4);
+            const float er[4] = {e0.x, e0.y, e0.z, e0.w}, ei[4] = {e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float2 p = pows[16 * mt + 4 * g + q];
+              const float xr = accG[di][mt][q], yi = accG[di][mt + MH][q];
+              accG[di][mt][q] = p.x * xr - p.y * yi + er[q];
+              accG[di][mt + MH][q] = p.x * yi + p.y * xr + ei[q];
+            }
+          }
+        }
+      if (u == 0 && lane < M) {
+        const float2 e = reinterpret_cast<const float2*>(sl + SL::eta)[lane];
+        eta = cmul(pows[lane], eta);
+        eta.x += e.x;
+        eta.y += e.y;
       }
     }
+  }
+
+  // ---- operand copies of the state for the readout of the next chunk, written to LDS between
+  // the two barriers: lam U (bf16), c_d lam G (fp16, c_d a power of two per value column; the
+  // scale and the packing are done while the current chunk's readout runs), lam eta.
+  // (lam U is converted while it is written: 16 conversions, not worth 16 registers held
+  // across the barrier.)
+  uint2 pG[NDT][TM];       // c_d lam G, 4 fp16 each
+  float pC[NDT];
+  auto pack_state = [&]() {
 #pragma unroll
-    for (int di = 0; di < NDT; ++di) {
-      const int dt = u + NS * di;
-      if (dt < TD) {
-        const int d = 16 * dt + il;
+    for (int di = 0; di < NDT; ++di)
+      if (u + NS * di < TD) {
         float mx = 0.f;
 #pragma unroll
         for (int kt = 0; kt < TM; ++kt)
@@ -624,104 +703,124 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
           for (int q = 0; q < 4; ++q) mx = fmaxf(mx, fabsf(accG[di][kt][q]));
         mx = xor_max16_32(mx);
         const float cd = pow2_scale(mx);
+        pC[di] = cd;
+#pragma unroll
+        for (int kt = 0; kt < TM; ++kt)
+          pG[di][kt] = pack4_f16(cd * accG[di][kt][0], cd * accG[di][kt][1],
+                                 cd * accG[di][kt][2], cd * accG[di][kt][3]);
+      }
+  };
+  auto write_state = [&]() {
+#pragma unroll
+    for (int fi = 0; fi < NFT; ++fi)
+      if (u + NS * fi < F / 16) {
+#pragma unroll
+        for (int mt = 0; mt < MH; ++mt) {
+          *reinterpret_cast<uint2*>(s16 + pubU[fi] + 16 * mt * F) = pack4_bf16(
+              accU[fi][mt][0], accU[fi][mt][1], accU[fi][mt][2], accU[fi][mt][3]);
+          *reinterpret_cast<uint2*>(s16 + pubU[fi] + (M + 16 * mt) * F) =
+              pack4_bf16(accU[fi][mt + MH][0], accU[fi][mt + MH][1], accU[fi][mt + MH][2],
+                         accU[fi][mt + MH][3]);
+        }
+      }
+#pragma unroll
+    for (int di = 0; di < NDT; ++di) {
+      const int dt = u + NS * di;
+      if (dt < TD) {
         if (g == 0) {
-          *reinterpret_cast<float*>(sb + oCd + 64 * dt) = cd;
-          *reinterpret_cast<float*>(sb + oCd + (Lay::bCi - Lay::bC) + 64 * dt) = 1.f / cd;
+          *reinterpret_cast<float*>(sb + oCd + 64 * dt) = pC[di];
+          *reinterpret_cast<float*>(sb + oCd + (Lay::bCi - Lay::bC) + 64 * dt) = 1.f / pC[di];
         }
 #pragma unroll
         for (int kt = 0; kt < TM; ++kt)
           *reinterpret_cast<uint2*>(s16 + pubG[kt >> 1] + 4 * (kt & 1) + 16 * dt * M2) =
-              pack4_f16(cd * accG[di][kt][0], cd * accG[di][kt][1], cd * accG[di][kt][2],
-                        cd * accG[di][kt][3]);
+              pG[di][kt];
       }
     }
-    if (u == 0 && lane < M) {
-      f2(oLn) = eta;
-      if (a.N - c * C < C) {
-        f2(oLn + (Lay::bPowL - Lay::bLE)) = reinterpret_cast<const float2*>(x.tab + TL::oPowT)[lane];
-        f2(oLn + (Lay::bGeo - Lay::bLE)) = reinterpret_cast<const float2*>(x.tab + TL::oGeoT)[lane];
-      }
+    if (u == 0 && lane < M) f2(oLn) = eta;
+  };
+  // Decay factors of chunk c when it is the last, partial one (read by the state update).
+  auto write_tail = [&](int c) {
+    if (u == 0 && lane < M && a.N - c * C < C) {
+      f2(oLn + (Lay::bPowL - Lay::bLE)) = reinterpret_cast<const float2*>(x.tab + TL::oPowT)[lane];
+      f2(oLn + (Lay::bGeo - Lay::bLE)) = reinterpret_cast<const float2*>(x.tab + TL::oGeoT)[lane];
     }
   };
 
-  // Raw bf16 q, k, v of the next chunk, fetched while the current chunk computes.
-  uint4 rq[NLF], rk[NLF], rv[NLD];
+  // ---- chunk inputs q, k: this wave loads 16-byte vectors n = 64u + lane + NL t of the
+  // row-major chunk matrices ([C][F]); vector n0 + NL t is row row0 + t NL/VF.  Token rows are
+  // H*F elements apart in memory, walking backwards for the reverse direction; per chunk the
+  // wave-uniform base moves, the per-lane offsets stay.  (The readout waves load v.)
+  const int n0 = 64 * u + lane;
+  const int rowF0 = n0 / VF;
+  const int sgn = a.dir ? -1 : 1;
+  int lofF[NLF];
+#pragma unroll
+  for (int t = 0; t < NLF; ++t)
+    lofF[t] = sgn * (rowF0 + t * (NL / VF)) * (a.H * F) + 8 * (n0 % VF);
+  // LDS rows row0 + t NL/VF share the swizzle of row0 (NL/VF is a multiple of 16).
+  static_assert((NL / VF) % 16 == 0, "loader rows keep the swizzle");
+  const int stF = opaque(Lay::oFk + soff<F>(rowF0, 8 * (n0 % VF)));
+  // Raw bf16 q, k of a chunk, then (convert) phi(q), phi(k) as packed bf16.
+  uint4 rq[NLF], rk[NLF];
   auto fetch = [&](int c) {
     const int t0 = c * C;
+    const size_t tb = x.tok_index(a, x.pos_of(a, t0));
+    const uint16_t* kb = a.k + tb * F;
+    const uint16_t* qb = a.q + tb * F;
 #pragma unroll
     for (int t = 0; t < NLF; ++t) {
-      const int n = 64 * u + lane + NL * t;
-      const int row = n / VF, c8 = n % VF;
-      const bool ok = n < C * VF && t0 + row < a.N;
-      const size_t off = ok ? x.tok_index(a, x.pos_of(a, t0 + row)) * F + 8 * c8 : 0;
-      rk[t] = ok ? *reinterpret_cast<const uint4*>(a.k + off) : make_uint4(0, 0, 0, 0);
-      rq[t] = ok && x.want_out ? *reinterpret_cast<const uint4*>(a.q + off)
+      const int n = n0 + NL * t;
+      const bool ok = n < C * VF && t0 + rowF0 + t * (NL / VF) < a.N;
+      rk[t] = ok ? *reinterpret_cast<const uint4*>(kb + lofF[t]) : make_uint4(0, 0, 0, 0);
+      rq[t] = ok && x.want_out ? *reinterpret_cast<const uint4*>(qb + lofF[t])
                                : make_uint4(0, 0, 0, 0);
     }
-#pragma unroll
-    for (int t = 0; t < NLD; ++t) {
-      const int n = 64 * u + lane + NL * t;
-      const int row = n / VD, c8 = n % VD;
-      const bool ok = n < C * VD && t0 + row < a.N;
-      rv[t] = ok ? *reinterpret_cast<const uint4*>(
-                       a.v + x.tok_index(a, x.pos_of(a, t0 + row)) * D + 8 * c8)
-                 : make_uint4(0, 0, 0, 0);
-    }
   };
-  // phi(k), phi(q) and v rows into LDS.  Tokens past N have zero features and values (zeros,
-  // not phi(0)).
-  // Vector n0 + NL t lands at row row0 + t NL/VF: NL/VF is a multiple of 16, so all rows of
-  // one lane share the swizzle and differ by a constant offset.
-  static_assert((NL / VF) % 16 == 0 && (NL / VD) % 16 == 0, "loader rows keep the swizzle");
-  const int stF = opaque(Lay::oFk + soff<F>((64 * u + lane) / VF, 8 * ((64 * u + lane) % VF)));
-  const int stD = opaque(Lay::oV + soff<D>((64 * u + lane) / VD, 8 * ((64 * u + lane) % VD)));
-  auto store = [&](int c) {
-    const int L = min(C, a.N - c * C);
+  // Features in place.  Rows past N get zero features (not phi(0)); their values are zero.
+  auto phi8 = [&](uint4& r, bool ok) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)   // bf16 pair -> two floats -> features -> bf16 pair
+      o[i] = pk_bf16(feature(__uint_as_float(w[i] << 16)),
+                     feature(__uint_as_float(w[i] & 0xffff0000u)));
+    r = ok ? make_uint4(o[0], o[1], o[2], o[3]) : make_uint4(0, 0, 0, 0);
+  };
+  auto convert = [&](int c) {
+    const int L = a.N - c * C;
 #pragma unroll
     for (int t = 0; t < NLF; ++t) {
-      const int n = 64 * u + lane + NL * t;
-      if (n < C * VF) {
-        const int row = n / VF;
+      const bool ok = rowF0 + t * (NL / VF) < L;
+      phi8(rk[t], ok);
+      if (x.want_out) phi8(rq[t], ok);
+    }
+  };
+  auto write_inputs = [&]() {
+#pragma unroll
+    for (int t = 0; t < NLF; ++t)
+      if (n0 + NL * t < C * VF) {
         const int so = stF + t * (NL / VF) * F;
-        const bool ok = row < L;
-        const uint16_t* ek = reinterpret_cast<const uint16_t*>(&rk[t]);
-        float f[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = ok ? feature(bf16_to_f32(ek[e])) : 0.f;
-        *reinterpret_cast<uint4*>(s16 + so) =
-            make_uint4(pk_bf16(f[0], f[1]), pk_bf16(f[2], f[3]), pk_bf16(f[4], f[5]),
-                       pk_bf16(f[6], f[7]));
-        if (x.want_out) {
-          const uint16_t* eq = reinterpret_cast<const uint16_t*>(&rq[t]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = feature(bf16_to_f32(eq[e]));
-          *reinterpret_cast<uint4*>(s16 + so + (Lay::oFq - Lay::oFk)) =
-              make_uint4(pk_bf16(f[0], f[1]), pk_bf16(f[2], f[3]), pk_bf16(f[4], f[5]),
-                         pk_bf16(f[6], f[7]));
-        }
+        *reinterpret_cast<uint4*>(s16 + so) = rk[t];
+        if (x.want_out) *reinterpret_cast<uint4*>(s16 + so + (Lay::oFq - Lay::oFk)) = rq[t];
       }
-    }
-#pragma unroll
-    for (int t = 0; t < NLD; ++t) {
-      const int n = 64 * u + lane + NL * t;
-      if (n < C * VD) {
-        const int row = n / VD;
-        *reinterpret_cast<uint4*>(s16 + stD + t * (NL / VD) * D) =
-            row < L ? rv[t] : make_uint4(0, 0, 0, 0);
-      }
-    }
   };
 
   __syncthreads();  // tables visible
   if (x.c_begin < x.c_end) {
-    publish(x.c_begin);
     fetch(x.c_begin);
-    store(x.c_begin);
+    convert(x.c_begin);
+    if (x.want_out) {
+      pack_state();
+      write_state();
+    }
+    write_tail(x.c_begin);
+    write_inputs();
+    if (x.c_begin + 1 < x.c_end) fetch(x.c_begin + 1);
   }
   __syncthreads();
 
   for (int c = x.c_begin; c < x.c_end; ++c) {
-    if (c + 1 < x.c_end) fetch(c + 1);
     // lam U^T <- lam^L (lam U^T + phi(K)^T (beta lam^-j)),  lam G <- lam^L (lam G + W^T V)
 #pragma unroll
     for (int kb = 0; kb < KC; ++kb) {
@@ -775,22 +874,45 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
       const float2 ge = f2(oLn + (Lay::bGeo - Lay::bLE));
       eta = cmul(f2(oLn + (Lay::bPowL - Lay::bLE)), make_float2(eta.x + ge.x, eta.y + ge.y));
     }
-    __syncthreads();
-    if (c + 1 < x.c_end) {
-      store(c + 1);   // first: frees the fetch registers before publish needs temporaries
-      publish(c + 1);
+    const bool more = c + 1 < x.c_end;
+    if (more) {
+      if (x.want_out) pack_state();
+      convert(c + 1);   // waits for the loads issued one chunk ago
+    }
+    __syncthreads();    // chunk c read by every wave
+    if (more) {
+      if (x.want_out) write_state();
+      write_tail(c + 1);
+      write_inputs();
+      if (c + 2 < x.c_end) fetch(c + 2);
     }
     __syncthreads();
   }
 
-  // Final state (divided by lam).
+  // Segment end state (times lam) into its workspace slot, in the accumulator layout.
+  if (a.seg_end) {
+    float* sl = a.seg_end + ((size_t)x.seq * a.slots_per_seq + x.seg) * a.slot_floats;
+#pragma unroll
+    for (int fi = 0; fi < NFT; ++fi)
+      if (u + NS * fi < F / 16) {
+#pragma unroll
+        for (int kt = 0; kt < TM; ++kt)
+          *reinterpret_cast<float4*>(sl + ((u * SL::NT + fi * TM + kt) * 64 + lane) * 4) =
+              make_float4(accU[fi][kt][0], accU[fi][kt][1], accU[fi][kt][2], accU[fi][kt][3]);
+      }
+#pragma unroll
+    for (int di = 0; di < NDT; ++di)
+      if (u + NS * di < TD) {
+#pragma unroll
+        for (int kt = 0; kt < TM; ++kt)
+          *reinterpret_cast<float4*>(sl + ((u * SL::NT + (NFT + di) * TM + kt) * 64 + lane) * 4) =
+              make_float4(accG[di][kt][0], accG[di][kt][1], accG[di][kt][2], accG[di][kt][3]);
+      }
+    if (u == 0 && lane < M) reinterpret_cast<float2*>(sl + SL::eta)[lane] = eta;
+  }
+  // Final state (divided by lam) in the caller's layout.
   float2 *fU = nullptr, *fG = nullptr, *fE = nullptr;
-  if (a.fin_seg) {
-    float2* base = a.fin_seg + ((size_t)x.seq * a.slots_per_seq + x.seg + 1) * a.slot;
-    fU = base;
-    fG = base + (size_t)M * F;
-    fE = base + (size_t)M * (F + D);
-  } else if (x.last_seg && a.fin_U) {
+  if (!a.seg_end && x.last_seg && a.fin_U) {
     fU = a.fin_U + (size_t)x.seq * M * F;
     fG = a.fin_G + (size_t)x.seq * M * D;
     fE = a.fin_E + (size_t)x.seq * M;

@@ -12,7 +12,7 @@ enum LaunchKind {
   kKindScan = 1,       // token-sequential prefill
   kKindTables = 2,     // per-head decay tables of the chunked prefill
   kKindSummary = 3,    // chunked prefill, segment end states (no outputs)
-  kKindCarry = 4,      // segment carry scan
+  // 4: not used
   kKindChunk = 5,      // chunked prefill with outputs (or the last segment's state)
   kKindDecode = 6,
 };
@@ -65,8 +65,9 @@ struct ScanArgs {
 };
 
 // Chunked MFMA prefill of one direction (bf16 inputs).  The sequence is cut into `segments`
-// runs of `seg_chunks` chunks; with more than one, segment end states go through `slots`
-// (B*H*segments states of M*(F+D+1) complex values) and a carry scan.  `tables` holds
+// runs of `seg_chunks` chunks; with more than one, the end states of all but the last segment
+// go through `slots` (B*H*(segments-1) slots of chunk_slot_floats(F, D, M) floats), from
+// which each segment's workgroup assembles its initial state.  `tables` holds
 // H * chunk_table_bytes(chunk, M) bytes.  U0/G0/E0: initial state or NULL (zeros);
 // U1/G1/E1: final state or NULL.  o NULL: state only.  acc_in: fp32 added to o, or NULL.
 struct ChunkPrefillArgs {
@@ -76,7 +77,7 @@ struct ChunkPrefillArgs {
   const float* acc_in;
   const float2 *U0, *G0, *E0;
   float2 *U1, *G1, *E1;
-  float2* slots;
+  float* slots;                 // (B*H) x (segments-1) segment end states
   unsigned char* tables;
   int B, H, N, F, D, M;
   int chunk, segments, seg_chunks;
@@ -86,6 +87,7 @@ struct ChunkPrefillArgs {
 
 bool chunk_supported(int F, int D, int M);
 long chunk_table_bytes(int chunk, int M);
+long chunk_slot_floats(int F, int D, int M);
 hipError_t launch_chunk_prefill(const ChunkPrefillArgs& a, hipStream_t st);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
