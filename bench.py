@@ -126,7 +126,10 @@ def bench_prefill(args, torch, ia, W):
     flops, byts = alg_counts(B, N, H, F, D, M, dirs=dirs)
     dom = kern_ms["chunk"] * dirs            # the output pass (once per direction)
     roof = {"bound": "hbm", "achieved": byts / (dom * 1e-3) / 1e9, "peak": HBM_PEAK / 1e9,
-            "unit": "GB/s", "frac": byts / (dom * 1e-3) / HBM_PEAK, "traffic": None,
+            "unit": "GB/s", "frac": byts / (dom * 1e-3) / HBM_PEAK,
+            "traffic": None if bidir else profiled_traffic(args.workload),
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, scaled)",
+            "alg_bytes_per_launch": byts / dirs,
             "kernel": "chunk_prefill_kernel (output pass)"}
     mfma = {"achieved": flops / (dom * 1e-3) / 1e12, "peak": BF16_PEAK / 1e12,
             "unit": "TFLOP/s", "frac": flops / (dom * 1e-3) / BF16_PEAK,
@@ -136,6 +139,34 @@ def bench_prefill(args, torch, ia, W):
            "bidirectional": bidir}
     return dict(ms=ms, tokens=B * N, cfg=cfg, roofline=roof, mfma=mfma, kernels_ms=kern_ms,
                 inp=inp)
+
+
+KERNEL_SOURCES = ["ssm_sequence_mixer_amd/csrc/ia_chunk.hpp",
+                  "ssm_sequence_mixer_amd/csrc/ia_device.hpp",
+                  "ssm_sequence_mixer_amd/csrc/ia_kernels.hpp"]
+TRAFFIC_PROFILE = {"1.3b": "profiles/chunk_prefill_1p3b_traffic.md"}
+
+
+def profiled_traffic(workload):
+    """HBM bytes per launch of the output pass from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (counters scaled by a streaming kernel of known size), or None when
+    there is none for this workload or the kernel sources changed since it was taken."""
+    import hashlib
+    path = TRAFFIC_PROFILE.get(workload)
+    if path is None or not os.path.exists(os.path.join(ROOT, path)):
+        return None
+    fields = {}
+    for line in open(os.path.join(ROOT, path)):
+        if ":" in line and line.strip().split(":")[0] in ("traffic_bytes_per_launch",
+                                                          "kernel_sources_sha256"):
+            key, val = line.strip().split(":", 1)
+            fields[key] = val.strip()
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if fields.get("kernel_sources_sha256") != h.hexdigest():
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def bench_decode(torch, ia, W, batches=(1, 16, 64), steps=256):
