@@ -1,11 +1,14 @@
 // ia_chunk.hip — chunked IA prefill: per-head tables and the host-side dispatch over the
 // kernel instantiations (which live in ia_chunk_f*.hip).
 #include "ia_chunk.hpp"
+#include "ia_chunk_state.hpp"
 
 namespace ia {
 
 #define IA_EXTERN(C, FF, MM)                                                              \
   extern template hipError_t launch_chunk_t<C, FF, FF, MM>(const ChunkArgs&, int, hipStream_t, \
+                                                           int);                          \
+  extern template hipError_t launch_state_t<C, FF, FF, MM>(const ChunkArgs&, int, hipStream_t, \
                                                            int);
 #define IA_EXTERN_C(C)                                                                    \
   IA_EXTERN(C, 32, 16) IA_EXTERN(C, 32, 32) IA_EXTERN(C, 32, 64)                          \
@@ -20,9 +23,11 @@ IA_EXTERN_C(64)
 // Once per call.  Block (h, run) holds one thread per (mode m, exponent j) with j in
 // [16 run, 16 run + 16); each entry is a direct complex power exp(n log lam).  Written in the
 // LDS form the prefill kernel copies verbatim: beta lam^-j in bf16 ([Re;Im] rows, j in K-slot
-// order) and in scaled fp16 (row j, modes in K-slot order), both swizzled.  Block run 0 also
-// writes the factors lam^(2i), i < 16, and lam^(32r); per mode lam^C, sum_{j<C} beta lam^-j,
-// the same two for the last chunk's length Lt, lam^Ls for the segment length Ls, and 1/lam.
+// order) and in scaled fp16 (row j, modes in K-slot order), both swizzled, and beta lam^(C-j)
+// in fp32 (the state-only pass's chunk table).  Block run 0 also writes the factors
+// lam^(2i), i < 16, and lam^(32r); per mode lam^C, sum_{j<C} beta lam^-j, the same two for
+// the last chunk's length Lt, sum_{j<C} beta lam^(C-j), lam^Ls for the segment length Ls, and
+// 1/lam.
 template <int C, int M>
 __global__ void __launch_bounds__(16 * M) chunk_tables_kernel(const float2* __restrict__ lam,
                                     const float2* __restrict__ beta, unsigned char* tables,
@@ -42,7 +47,7 @@ __global__ void __launch_bounds__(16 * M) chunk_tables_kernel(const float2* __re
   const float2 l = lam[(size_t)h * M + m];
   const float2 bt = beta[(size_t)h * M + m];
   __shared__ float s_max[16 * M];
-  __shared__ float2 s_geo[16 * M], s_geot[16 * M];
+  __shared__ float2 s_geo[16 * M], s_geot[16 * M], s_geol[16 * M];
 
   // fp16 table exponent: max_j |beta lam^-j| = |beta| |lam|^-(C-1) (|lam| <= 1); every block
   // of the head reduces the same values, so all agree on the scale.
@@ -56,6 +61,7 @@ __global__ void __launch_bounds__(16 * M) chunk_tables_kernel(const float2* __re
   const float wscale = pow2_scale(s_max[0]);
 
   const float2 w = cmul(bt, cpow_f(l, -(float)j));
+  reinterpret_cast<float2*>(tab + TL::oTL)[m * C + j] = cmul(bt, cpow_f(l, (float)(C - j)));
   WT[soff<C>(m, kpos(j))] = __builtin_bit_cast(uint16_t, (__bf16)w.x);
   WT[soff<C>(M + m, kpos(j))] = __builtin_bit_cast(uint16_t, (__bf16)w.y);
   Wb[soff<M2>(j, kpos(m))] = __builtin_bit_cast(uint16_t, (_Float16)(w.x * wscale));
@@ -66,7 +72,7 @@ __global__ void __launch_bounds__(16 * M) chunk_tables_kernel(const float2* __re
   L2lo[jj * L2S + m] = cpow_f(l, 2.f * jj);
   if (jj < RUNS) L2hi[jj * M + m] = cpow_f(l, 32.f * jj);
   // Geometric sums over j < C and j < Lt: thread jj takes j = jj, jj + 16, ...
-  float2 geo = make_float2(0.f, 0.f), geot = geo;
+  float2 geo = make_float2(0.f, 0.f), geot = geo, geol = geo;
   for (int jx = jj; jx < C; jx += 16) {
     const float2 t = cmul(bt, cpow_f(l, -(float)jx));
     geo.x += t.x;
@@ -75,9 +81,13 @@ __global__ void __launch_bounds__(16 * M) chunk_tables_kernel(const float2* __re
       geot.x += t.x;
       geot.y += t.y;
     }
+    const float2 tl = cmul(bt, cpow_f(l, (float)(C - jx)));
+    geol.x += tl.x;
+    geol.y += tl.y;
   }
   s_geo[threadIdx.x] = geo;
   s_geot[threadIdx.x] = geot;
+  s_geol[threadIdx.x] = geol;
   __syncthreads();
   if (jj == 0) {
     for (int k = 1; k < 16; ++k) {
@@ -85,7 +95,10 @@ __global__ void __launch_bounds__(16 * M) chunk_tables_kernel(const float2* __re
       geo.y += s_geo[k * M + m].y;
       geot.x += s_geot[k * M + m].x;
       geot.y += s_geot[k * M + m].y;
+      geol.x += s_geol[k * M + m].x;
+      geol.y += s_geol[k * M + m].y;
     }
+    reinterpret_cast<float2*>(tab + TL::oGeoL)[m] = geol;
     reinterpret_cast<float2*>(tab + TL::oPow)[m] = cpow_f(l, (float)C);
     reinterpret_cast<float2*>(tab + TL::oGeo)[m] = geo;
     reinterpret_cast<float2*>(tab + TL::oPowT)[m] = cpow_f(l, (float)Lt);
@@ -102,6 +115,18 @@ static hipError_t dispatch_fdm(const ChunkArgs& a, int F, int D, int M, int n_wg
                                hipStream_t st, int kind) {
 #define IA_CASE(FF, MM)                                   \
   if (F == FF && D == FF && M == MM) return launch_chunk_t<C, FF, FF, MM>(a, n_wg, st, kind);
+  IA_CASE(32, 16) IA_CASE(32, 32) IA_CASE(32, 64)
+  IA_CASE(64, 16) IA_CASE(64, 32) IA_CASE(64, 64)
+  IA_CASE(128, 16) IA_CASE(128, 32) IA_CASE(128, 64)
+#undef IA_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int C>
+static hipError_t dispatch_state_fdm(const ChunkArgs& a, int F, int D, int M, int n_wg,
+                                     hipStream_t st, int kind) {
+#define IA_CASE(FF, MM)                                   \
+  if (F == FF && D == FF && M == MM) return launch_state_t<C, FF, FF, MM>(a, n_wg, st, kind);
   IA_CASE(32, 16) IA_CASE(32, 32) IA_CASE(32, 64)
   IA_CASE(64, 16) IA_CASE(64, 32) IA_CASE(64, 64)
   IA_CASE(128, 16) IA_CASE(128, 32) IA_CASE(128, 64)
@@ -200,7 +225,8 @@ hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
     s.seg_first = 0;
     s.n_seg = G - 1;
     s.seg_end = p.slots;
-    e = go(s, seqs * (G - 1), kKindSummary);
+    e = C == 64 ? dispatch_state_fdm<64>(s, p.F, p.D, p.M, seqs * (G - 1), st, kKindSummary)
+                : dispatch_state_fdm<32>(s, p.F, p.D, p.M, seqs * (G - 1), st, kKindSummary);
     if (e != hipSuccess) return e;
   }
   // Pass 2: every segment from its initial state, with outputs; the last segment returns the

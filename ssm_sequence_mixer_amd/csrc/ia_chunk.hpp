@@ -285,7 +285,9 @@ struct TableLayout {
   static constexpr long oPowS = oGeoT + 8L * M;       // float2 [M]: lam^(segment length)
   static constexpr long oInv = oPowS + 8L * M;        // float2 [M]: 1 / lam
   static constexpr long oSc = oInv + 8L * M;          // float: 1 / fp16 table scale
-  static constexpr long bytes = (oSc + 16 + 255) / 256 * 256;
+  static constexpr long oTL = oSc + 16;               // float2 [M][C]: beta lam^(C-j)
+  static constexpr long oGeoL = oTL + 8L * M * C;     // float2 [M]: sum_{j<C} beta lam^(C-j)
+  static constexpr long bytes = (oGeoL + 8L * M + 255) / 256 * 256;
 };
 
 // Per-workgroup context shared by the two wave roles.

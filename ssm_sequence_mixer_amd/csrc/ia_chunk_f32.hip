@@ -1,5 +1,6 @@
-// ia_chunk_f32.hip — instantiations of the chunked prefill kernel for F = Dv = 32.
+// ia_chunk_f32.hip — instantiations of the chunked prefill kernels (output and state-only passes) for F = Dv = 32.
 #include "ia_chunk.hpp"
+#include "ia_chunk_state.hpp"
 
 namespace ia {
 
@@ -9,5 +10,11 @@ template hipError_t launch_chunk_t<32, 32, 32, 64>(const ChunkArgs&, int, hipStr
 template hipError_t launch_chunk_t<64, 32, 32, 16>(const ChunkArgs&, int, hipStream_t, int);
 template hipError_t launch_chunk_t<64, 32, 32, 32>(const ChunkArgs&, int, hipStream_t, int);
 template hipError_t launch_chunk_t<64, 32, 32, 64>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_state_t<32, 32, 32, 16>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_state_t<32, 32, 32, 32>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_state_t<32, 32, 32, 64>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_state_t<64, 32, 32, 16>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_state_t<64, 32, 32, 32>(const ChunkArgs&, int, hipStream_t, int);
+template hipError_t launch_state_t<64, 32, 32, 64>(const ChunkArgs&, int, hipStream_t, int);
 
 }  // namespace ia

@@ -1,0 +1,279 @@
+// ia_chunk_state.hpp — state-only pass of the chunked IA prefill on gfx950 MFMA: the end state
+// of a full segment of Ls = nc*C tokens from a zero state.  Included by the per-feature-width
+// translation units that instantiate it.
+//
+// In the frame the prefill carries (X = lam U, lam Gamma, lam eta; "Interdomain Attention:
+// Beyond Token-Level Key-Value Memory", summary page §3.2 for the recurrence, §A.2 for the
+// chunkwise form), the end state of a segment started from zero is a plain contraction over
+// its tokens t:
+//   X[k,f] = sum_t beta_k lam_k^(Ls-t) phi(k_t)[f],   lam G likewise with v_t,
+//   lam eta = sum_t beta lam^(Ls-t).
+// With t = c C + j this is, per chunk c, the table T_c[k,j] = lam^((nc-1-c) C) beta lam^(C-j)
+// against the chunk's features: no per-chunk decay of the accumulators.  Chunks are walked
+// from the segment's last to its first, so the chunk factor pw = lam^(i C) (i = nc-1-c) only
+// shrinks and underflows exactly where the contribution vanishes.
+//
+// Workgroup = one (b, h, segment); NS waves with the tile ownership of the output pass's
+// state waves, so the final accumulators are already in the workspace slot layout.  LDS holds
+// two stages of (phi(k), v, T); each wave keeps three chunks of raw inputs in flight in
+// registers, one barrier per chunk.  (Splitting each wave's U and G tiles over two waves was
+// measured slower: the table is then read twice per chunk.)
+#pragma once
+
+#include <type_traits>
+
+#include "ia_chunk.hpp"
+
+namespace ia {
+
+template <int C, int F, int D, int M>
+struct StateLayout {
+  static constexpr int M2 = 2 * M;
+  // 16-bit element offsets within a stage; every matrix swizzled by row (see soff).
+  static constexpr int oFk = 0;            // [C][F]   bf16 phi(k)
+  static constexpr int oV = C * F;         // [C][D]   bf16 v
+  static constexpr int oT = oV + C * D;    // [2M][C]  bf16 T_c (j in K-slot order)
+  static constexpr int stage = oT + M2 * C;
+  static constexpr int bytes = 2 * stage * 2;
+};
+
+template <int C, int F, int D, int M>
+__global__ void __launch_bounds__((64 * StateWaves<F, D, M>::NS))
+chunk_state_kernel(const ChunkArgs a) {
+  using TL = TableLayout<C, M>;
+  using SL = SlotLayout<F, D, M>;
+  using Lay = StateLayout<C, F, D, M>;
+  constexpr int NS = StateWaves<F, D, M>::NS;
+  constexpr int NFT = SL::NFT, NDT = SL::NDT, TM = SL::TM;
+  constexpr int M2 = 2 * M;
+  constexpr int KC = C / 32;
+  constexpr int TD = D / 16;
+  constexpr int VF = F / 8, VD = D / 8;
+  constexpr int NL = 64 * NS;
+  constexpr int NLK = (C * VF + NL - 1) / NL, NLV = (C * VD + NL - 1) / NL;
+  constexpr int GROUPS = M * C / 4;          // table groups: 4 consecutive j of one mode
+  constexpr int NGR = (GROUPS + NL - 1) / NL;
+  constexpr int ST = Lay::stage;
+  static_assert((NL / VF) % 16 == 0 && (NL / VD) % 16 == 0, "loader rows keep the swizzle");
+  static_assert(Lay::bytes <= 160 * 1024, "LDS budget");
+
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  uint16_t* const s16 = reinterpret_cast<uint16_t*>(smem_raw);
+  const int tid = threadIdx.x, lane = tid & 63, u = tid >> 6;
+  const int il = lane & 15, g = lane >> 4;
+  const int seq = blockIdx.x / a.n_seg;
+  const int seg = a.seg_first + blockIdx.x % a.n_seg;
+  const int b = seq / a.H, h = seq % a.H;
+  const int nc = a.seg_chunks;               // a full segment
+  const int c_first = seg * nc;
+  const unsigned char* tab = a.tables + (size_t)h * a.table_bytes;
+  const float2* powC = reinterpret_cast<const float2*>(tab + TL::oPow);
+
+  // ---- per-lane LDS offsets (stage 0; stage 1 adds the constant ST)
+  int offT[KC], trF[NFT], trD[NDT];
+#pragma unroll
+  for (int kb = 0; kb < KC; ++kb) offT[kb] = opaque(Lay::oT + lane_off<C>(il, 4 * kb + g));
+#pragma unroll
+  for (int fi = 0; fi < NFT; ++fi) trF[fi] = opaque(Lay::oFk + tr_off<F>(u + NS * fi, lane));
+#pragma unroll
+  for (int di = 0; di < NDT; ++di) trD[di] = opaque(Lay::oV + tr_off<D>(u + NS * di, lane));
+
+  // ---- loader: 16-byte vectors n = n0 + NL t of the row-major chunk matrices k ([C][F]) and
+  // v ([C][D]); token rows are H*F (H*D) elements apart, backwards in the reverse direction.
+  const int n0 = 64 * u + lane;
+  const int rowK0 = n0 / VF, rowV0 = n0 / VD;
+  const int sgn = a.dir ? -1 : 1;
+  const int lofK = sgn * rowK0 * (a.H * F) + 8 * (n0 % VF);
+  const int lofV = sgn * rowV0 * (a.H * D) + 8 * (n0 % VD);
+  const int stepK = sgn * (NL / VF) * (a.H * F), stepV = sgn * (NL / VD) * (a.H * D);
+  const int stK = opaque(Lay::oFk + soff<F>(rowK0, 8 * (n0 % VF)));
+  const int stV = opaque(Lay::oV + soff<D>(rowV0, 8 * (n0 % VD)));
+  uint4 rk[3][NLK], rv[3][NLV];
+  // Walk chunk of iteration i: the segment's chunks from last to first.
+  auto chunk_of = [&](int i) { return c_first + nc - 1 - i; };
+  auto fetch = [&](auto R, int i) {
+    constexpr int r = decltype(R)::value;
+    const int t0 = chunk_of(i) * C;
+    const size_t tb = ((size_t)b * a.N + (a.dir ? a.N - 1 - t0 : t0)) * a.H + h;
+    const uint16_t* kb = a.k + tb * F + lofK;
+    const uint16_t* vb = a.v + tb * D + lofV;
+#pragma unroll
+    for (int t = 0; t < NLK; ++t)
+      rk[r][t] = n0 + NL * t < C * VF ? *reinterpret_cast<const uint4*>(kb + t * stepK)
+                                      : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int t = 0; t < NLV; ++t)
+      rv[r][t] = n0 + NL * t < C * VD ? *reinterpret_cast<const uint4*>(vb + t * stepV)
+                                      : make_uint4(0, 0, 0, 0);
+  };
+  // phi(k) in place, then both into the stage.
+  auto write_inputs = [&](auto R, auto S) {
+    constexpr int r = decltype(R)::value, so = decltype(S)::value * ST;
+#pragma unroll
+    for (int t = 0; t < NLK; ++t)
+      if (n0 + NL * t < C * VF) {
+        const uint32_t w[4] = {rk[r][t].x, rk[r][t].y, rk[r][t].z, rk[r][t].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = pk_bf16(feature(__uint_as_float(w[e] << 16)),
+                         feature(__uint_as_float(w[e] & 0xffff0000u)));
+        *reinterpret_cast<uint4*>(s16 + stK + so + t * (NL / VF) * F) =
+            make_uint4(o[0], o[1], o[2], o[3]);
+      }
+#pragma unroll
+    for (int t = 0; t < NLV; ++t)
+      if (n0 + NL * t < C * VD)
+        *reinterpret_cast<uint4*>(s16 + stV + so + t * (NL / VD) * D) = rv[r][t];
+  };
+
+  // ---- chunk table T_i = pw_i beta lam^(C-j), pw_i = lam^(i C): this thread's groups of 4
+  // consecutive j of one mode, beta lam^(C-j) held in registers for the whole segment.
+  float2 tl[NGR][4], pw[NGR], pc[NGR];
+  int tRe[NGR], tIm[NGR];
+#pragma unroll
+  for (int q = 0; q < NGR; ++q) {
+    const int gi = tid + NL * q;
+    const int m = gi < GROUPS ? gi / (C / 4) : 0, j0 = 4 * (gi % (C / 4));
+    const float2* src = reinterpret_cast<const float2*>(tab + TL::oTL) + m * C + j0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tl[q][e] = src[e];
+    pw[q] = make_float2(1.f, 0.f);
+    pc[q] = powC[m];
+    tRe[q] = opaque(Lay::oT + soff<C>(m, kpos(j0)));
+    tIm[q] = opaque(Lay::oT + soff<C>(M + m, kpos(j0)));
+  }
+  auto write_table = [&](auto S) {
+    constexpr int so = decltype(S)::value * ST;
+#pragma unroll
+    for (int q = 0; q < NGR; ++q)
+      if (tid + NL * q < GROUPS) {
+        float2 w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = cmul(pw[q], tl[q][e]);
+        *reinterpret_cast<uint2*>(s16 + tRe[q] + so) = pack4_bf16(w[0].x, w[1].x, w[2].x, w[3].x);
+        *reinterpret_cast<uint2*>(s16 + tIm[q] + so) = pack4_bf16(w[0].y, w[1].y, w[2].y, w[3].y);
+      }
+  };
+  auto advance_table = [&]() {
+#pragma unroll
+    for (int q = 0; q < NGR; ++q) pw[q] = cmul(pw[q], pc[q]);
+  };
+
+  // ---- accumulators (lam U)^T and lam G in the output pass's state-wave layout; lam eta in
+  // wave 0, lane m < M.
+  f32x4 accU[NFT][TM], accG[NDT][TM];
+#pragma unroll
+  for (int fi = 0; fi < NFT; ++fi)
+#pragma unroll
+    for (int kt = 0; kt < TM; ++kt) accU[fi][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int di = 0; di < NDT; ++di)
+#pragma unroll
+    for (int kt = 0; kt < TM; ++kt) accG[di][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float2 eta = make_float2(0.f, 0.f), epw = make_float2(1.f, 0.f), epc = epw, egeo = eta;
+  if (u == 0 && lane < M) {
+    epc = powC[lane];
+    egeo = reinterpret_cast<const float2*>(tab + TL::oGeoL)[lane];
+  }
+
+  auto update = [&](auto S) {
+    constexpr int so = decltype(S)::value * ST;
+#pragma unroll
+    for (int kb = 0; kb < KC; ++kb) {
+      bf16x8 afk[NFT], bv[NDT];
+#pragma unroll
+      for (int fi = 0; fi < NFT; ++fi)
+        if (u + NS * fi < F / 16) afk[fi] = ldtr<F>(s16, trF[fi] + so, kb).b;
+#pragma unroll
+      for (int di = 0; di < NDT; ++di)
+        if (u + NS * di < TD) bv[di] = ldtr<D>(s16, trD[di] + so, kb).b;
+#pragma unroll
+      for (int kt = 0; kt < TM; ++kt) {
+        const bf16x8 w = lds8(s16 + offT[kb] + so + 16 * kt * C).b;
+#pragma unroll
+        for (int fi = 0; fi < NFT; ++fi)
+          if (u + NS * fi < F / 16) accU[fi][kt] = mma_bf16(afk[fi], w, accU[fi][kt]);
+#pragma unroll
+        for (int di = 0; di < NDT; ++di)
+          if (u + NS * di < TD) accG[di][kt] = mma_bf16(w, bv[di], accG[di][kt]);
+      }
+    }
+    if (u == 0 && lane < M) {
+      eta = cfma(epw, egeo, eta);
+      epw = cmul(epw, epc);
+    }
+  };
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  // Iteration i: update from stage i%2; convert chunk i+1 (ring set (i+1)%3, loaded two
+  // iterations ago) into stage (i+1)%2 with its table; load chunk i+3 into set i%3.
+  auto step = [&](auto Rc, auto Rf, auto Sr, auto Sw, int i) {
+    update(Sr);
+    if (i + 1 < nc) {
+      advance_table();
+      write_inputs(Rc, Sw);
+      write_table(Sw);
+      if (i + 3 < nc) fetch(Rf, i + 3);
+    }
+    __syncthreads();
+  };
+
+  fetch(I0{}, 0);
+  if (nc > 1) fetch(I1{}, 1);
+  if (nc > 2) fetch(I2{}, 2);
+  write_inputs(I0{}, I0{});
+  write_table(I0{});
+  __syncthreads();
+  for (int i = 0; i < nc; i += 6) {
+    step(I1{}, I0{}, I0{}, I1{}, i);
+    if (i + 1 < nc) step(I2{}, I1{}, I1{}, I0{}, i + 1);
+    if (i + 2 < nc) step(I0{}, I2{}, I0{}, I1{}, i + 2);
+    if (i + 3 < nc) step(I1{}, I0{}, I1{}, I0{}, i + 3);
+    if (i + 4 < nc) step(I2{}, I1{}, I0{}, I1{}, i + 4);
+    if (i + 5 < nc) step(I0{}, I2{}, I1{}, I0{}, i + 5);
+  }
+
+  // ---- end state into the segment's slot
+  float* sl = a.seg_end + ((size_t)seq * a.slots_per_seq + seg) * a.slot_floats;
+#pragma unroll
+  for (int fi = 0; fi < NFT; ++fi)
+    if (u + NS * fi < F / 16) {
+#pragma unroll
+      for (int kt = 0; kt < TM; ++kt)
+        *reinterpret_cast<float4*>(sl + ((u * SL::NT + fi * TM + kt) * 64 + lane) * 4) =
+            make_float4(accU[fi][kt][0], accU[fi][kt][1], accU[fi][kt][2], accU[fi][kt][3]);
+    }
+#pragma unroll
+  for (int di = 0; di < NDT; ++di)
+    if (u + NS * di < TD) {
+#pragma unroll
+      for (int kt = 0; kt < TM; ++kt)
+        *reinterpret_cast<float4*>(sl + ((u * SL::NT + (NFT + di) * TM + kt) * 64 + lane) * 4) =
+            make_float4(accG[di][kt][0], accG[di][kt][1], accG[di][kt][2], accG[di][kt][3]);
+    }
+  if (u == 0 && lane < M) reinterpret_cast<float2*>(sl + SL::eta)[lane] = eta;
+}
+
+template <int C, int F, int D, int M>
+hipError_t launch_state_t(const ChunkArgs& a, int n_wg, hipStream_t st, int kind) {
+  constexpr int threads = 64 * StateWaves<F, D, M>::NS;
+  constexpr int bytes = StateLayout<C, F, D, M>::bytes;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&chunk_state_kernel<C, F, D, M>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  (void)hipGetLastError();
+  prof_begin(st);
+  hipLaunchKernelGGL((chunk_state_kernel<C, F, D, M>), dim3(n_wg), dim3(threads), bytes, st, a);
+  prof_end(st, kind);
+  return hipGetLastError();
+}
+
+}  // namespace ia
