@@ -53,6 +53,33 @@ def test_decode_steps_match_oracle(in_dtype, out_dtype):
         assert state_rel(tuple(host(s) for s in st), st_ref) < TOL_F32
 
 
+@pytest.mark.parametrize("shape", [(32, 32, 16), (32, 128, 64), (64, 64, 128), (128, 32, 16),
+                                   (64, 128, 32), (128, 128, 64), (128, 128, 128)])
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+def test_decode_row_kernel_shapes(shape, in_dtype):
+    """Decode at the row widths the row-parallel kernel takes (F, Dv in {32, 64, 128}),
+    including passes that cover more rows than there are modes (F=32, M=16)."""
+    torch = _torch()
+    ia = _lib()
+    F, D, M = shape
+    B, H, steps = 3, 2, 3
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    inp = W.make_inputs(B, H, steps, F, D, M, dtype=in_dtype, seed=F + D + M)
+    lam, beta = inp["lam"], inp["beta"]
+    st_ref = _oracle_state(B, H, F, D, M, lam, beta, seed=M + 1)
+    st = tuple(dev(s) for s in st_ref)
+    st_ref = tuple(host(s) for s in st)
+    for t in range(steps):
+        tag(f"decode rows F={F} D={D} M={M} {in_dtype} step {t}")
+        o = ia.decode(dev(inp["q"][:, t], tdt[in_dtype]), dev(inp["k"][:, t], tdt[in_dtype]),
+                      dev(inp["v"][:, t], tdt[in_dtype]), dev(lam), dev(beta), st)
+        o_ref, st_ref = oracle.decode_step(inp["q"][:, t], inp["k"][:, t], inp["v"][:, t], lam,
+                                           beta, st_ref)
+        torch.cuda.synchronize()
+        assert rowrel(host(o), o_ref) < TOL_F32
+        assert state_rel(tuple(host(s) for s in st), st_ref) < TOL_F32
+
+
 def test_fp32_prefill_tiny_workload():
     """The tiny fp32 workload: B=H=1, N=256, F=Dv=M=16, dt=0.01, beta=1; outputs and state."""
     torch = _torch()
@@ -132,30 +159,33 @@ def test_decode_forced_clamp():
         assert rowrel(host(o), o_ref) < TOL_F32
 
 
-def test_decode_1p3b_shape_batch16():
-    """Decode at the 1.3B-shaped layer (H=16, F=Dv=128, M=64), batch 16, from a prefilled state."""
+@pytest.mark.parametrize("Bd", [1, 16, 64])
+def test_decode_1p3b_shape(Bd):
+    """Decode at the 1.3B-shaped layer (H=16, F=Dv=128, M=64) from a 32-token prefilled state,
+    at the benchmark's batch sizes (both decode kernels: 16 and 256 slices take the
+    row-parallel one, 1024 the mode-looping one)."""
     torch = _torch()
     ia = _lib()
-    wl = W.decode(16, steps=4, prefix=32)
+    wl = W.decode(Bd, steps=4, prefix=32)
     pre, stp = wl["prefix"], wl["steps"]
     lam, beta = wl["lam"], wl["beta"]
-    tag("decode 1.3b B=16 prefix")
-    st = ia.new_state(16, 16, 64, 128, 128)
+    tag(f"decode 1.3b B={Bd} prefix")
+    st = ia.new_state(Bd, 16, 64, 128, 128)
     ia.prefill(dev(pre["q"], torch.bfloat16), dev(pre["k"], torch.bfloat16),
                dev(pre["v"], torch.bfloat16), dev(lam), dev(beta), state=st, want_output=False)
     _, _, _, st_ref = oracle.prefill(pre["q"], pre["k"], pre["v"], lam, beta, threads=8)
     torch.cuda.synchronize()
     # the prefix state comes from bf16 inputs through the chunked MFMA path: bf16 tolerance
     err = state_rel(tuple(host(s) for s in st), st_ref)
-    report("decode 1.3b B=16 prefix state", err)
+    report(f"decode 1.3b B={Bd} prefix state", err)
     assert err < TOL_BF16
     for t in range(4):
-        tag(f"decode 1.3b B=16 step {t}")
+        tag(f"decode 1.3b B={Bd} step {t}")
         o = ia.decode(dev(stp["q"][t], torch.bfloat16), dev(stp["k"][t], torch.bfloat16),
                       dev(stp["v"][t], torch.bfloat16), dev(lam), dev(beta), st)
         o_ref, st_ref = oracle.decode_step(stp["q"][t], stp["k"][t], stp["v"][t], lam, beta,
                                            st_ref)
         torch.cuda.synchronize()
         err = rowrel(host(o), o_ref)
-        report(f"decode 1.3b B=16 step {t}", err)
+        report(f"decode 1.3b B={Bd} step {t}", err)
         assert err < TOL_BF16
