@@ -372,6 +372,18 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
   };
 
   __syncthreads();  // tables visible
+  // lam^(2i) for this lane's queries i = 16r + il and modes m = 16mt + 4g + q, for the whole
+  // segment: the product of the two factor tables, formed once.
+  float2 l2[MH][4];
+#pragma unroll
+  for (int mt = 0; mt < MH; ++mt)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int mo = 8 * (16 * mt + q);
+      l2[mt][q] = cmul(*reinterpret_cast<const float2*>(sb + oLo + mo),
+                       *reinterpret_cast<const float2*>(sb + oG + (Lay::bL2hi - Lay::bLE) +
+                                                        8 * r * M + mo));
+    }
   if (x.c_begin < x.c_end) {
     fetch_v(x.c_begin);
     write_v();
@@ -435,11 +447,8 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
         for (int q = 0; q < 4; ++q) {
           // m = 16 mt + 4 g + q
           const int mo = 8 * (16 * mt + q);
-          const float2 lo = *reinterpret_cast<const float2*>(sb + oLo + mo);
-          const float2 hi =
-              *reinterpret_cast<const float2*>(sb + oG + (Lay::bL2hi - Lay::bLE) + 8 * r * M + mo);
           const float2 le = *reinterpret_cast<const float2*>(sb + oG + mo);
-          const float2 L2 = cmul(lo, hi);
+          const float2 L2 = l2[mt][q];
           const float xr = accA[mt][q], yi = accA[mt + MH][q];
           const float ar = xr * L2.x - yi * L2.y, ai = xr * L2.y + yi * L2.x;
           accA[mt][q] = ar;
@@ -491,7 +500,11 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
       // ---- num^T tiles (rows d, columns i): P V (accI) + c_d-scaled Re(A lam G) (accX)
       const int t = c * C + 16 * r + il;
       const bool ok = t < a.N;
-      const size_t obase = ok ? x.tok_index(a, x.pos_of(a, t)) * D : 0;
+      // Output row of query t from this lane's column 4g: dt tiles are constant offsets.
+      const size_t obase = ok ? x.tok_index(a, x.pos_of(a, t)) * D + 4 * g : 0;
+      uint16_t* const o16 = static_cast<uint16_t*>(a.o) + obase;
+      float* const o32 = static_cast<float*>(a.o) + obase;
+      const float* const prev_row = a.acc_in + obase;
 #pragma unroll
       for (int dt = 0; dt < TD; ++dt) {
         f32x4 accI = {0.f, 0.f, 0.f, 0.f}, accX = {0.f, 0.f, 0.f, 0.f};
@@ -506,17 +519,14 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
           const float4 ci = *reinterpret_cast<const float4*>(sb + oCi + 64 * dt);
           float val[4] = {(accI[0] + accX[0] * ci.x) * rd, (accI[1] + accX[1] * ci.y) * rd,
                           (accI[2] + accX[2] * ci.z) * rd, (accI[3] + accX[3] * ci.w) * rd};
-          const size_t oi = obase + 16 * dt + 4 * g;
           if (a.acc_in) {
-            const float4 prev = *reinterpret_cast<const float4*>(a.acc_in + oi);
+            const float4 prev = *reinterpret_cast<const float4*>(prev_row + 16 * dt);
             val[0] += prev.x; val[1] += prev.y; val[2] += prev.z; val[3] += prev.w;
           }
           if (a.out_bf16)
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.o) + oi) =
-                pack4_bf16(val[0], val[1], val[2], val[3]);
+            *reinterpret_cast<uint2*>(o16 + 16 * dt) = pack4_bf16(val[0], val[1], val[2], val[3]);
           else
-            *reinterpret_cast<float4*>(static_cast<float*>(a.o) + oi) =
-                make_float4(val[0], val[1], val[2], val[3]);
+            *reinterpret_cast<float4*>(o32 + 16 * dt) = make_float4(val[0], val[1], val[2], val[3]);
         }
         IA_STEP_FENCE();
       }
