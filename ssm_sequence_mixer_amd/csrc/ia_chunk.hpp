@@ -392,6 +392,10 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
   __syncthreads();  // first chunk in LDS
 
   for (int c = x.c_begin; c < x.c_end; ++c) {
+    // Live across the mid-chunk barrier: the fp16 operand of lam^(2i) A', its per-query
+    // scale and the inter-chunk denominator.
+    f16x8 Af[KM];
+    float si = 1.f, den_inter = 0.f;
     if (x.want_out) {
       // phi(q) of this wave's queries as B operands (K = f)
       bf16x8 fq[KF];
@@ -440,7 +444,7 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
       }
 
       // ---- lam^(2i) A' (fp32), den_inter, per-query scale, fp16 operands [Re | -Im]
-      float den_inter = 0.f, amax = 0.f;
+      float amax = 0.f;
 #pragma unroll
       for (int mt = 0; mt < MH; ++mt) {
 #pragma unroll
@@ -460,8 +464,7 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
       }
       den_inter = xor_sum16_32(den_inter);
       amax = xor_max16_32(amax);
-      const float si = pow2_scale(amax);
-      f16x8 Af[KM];
+      si = pow2_scale(amax);
 #pragma unroll
       for (int kb = 0; kb < KM; ++kb)
 #pragma unroll
@@ -469,6 +472,11 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
           Af[kb][q] = (_Float16)(si * accA[2 * kb][q]);
           Af[kb][4 + q] = (_Float16)(si * accA[2 * kb + 1][q]);
         }
+    }
+    // Mid-chunk barrier: S, A' and its decay are done, so phi(q), phi(k) and lam U of chunk c
+    // are no longer read and the state waves overwrite them with chunk c+1's.
+    __syncthreads();
+    if (x.want_out) {
 
       // ---- P^T tiles (rows j, columns i), causal
       f32x4 accP[NR];
@@ -722,7 +730,7 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
                                  cd * accG[di][kt][2], cd * accG[di][kt][3]);
       }
   };
-  auto write_state = [&]() {
+  auto write_lam_u = [&]() {
 #pragma unroll
     for (int fi = 0; fi < NFT; ++fi)
       if (u + NS * fi < F / 16) {
@@ -735,6 +743,8 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
                          accU[fi][mt + MH][3]);
         }
       }
+  };
+  auto write_state = [&]() {   // lam G copy, its column scales, lam eta
 #pragma unroll
     for (int di = 0; di < NDT; ++di) {
       const int dt = u + NS * di;
@@ -823,6 +833,7 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
     fetch(x.c_begin);
     convert(x.c_begin);
     if (x.want_out) {
+      write_lam_u();
       pack_state();
       write_state();
     }
@@ -887,15 +898,19 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
       eta = cmul(f2(oLn + (Lay::bPowL - Lay::bLE)), make_float2(eta.x + ge.x, eta.y + ge.y));
     }
     const bool more = c + 1 < x.c_end;
+    __syncthreads();    // mid-chunk: phi(q), phi(k), lam U of chunk c no longer read
     if (more) {
-      if (x.want_out) pack_state();
+      if (x.want_out) {
+        write_lam_u();
+        pack_state();
+      }
       convert(c + 1);   // waits for the loads issued one chunk ago
+      write_inputs();
     }
     __syncthreads();    // chunk c read by every wave
     if (more) {
       if (x.want_out) write_state();
       write_tail(c + 1);
-      write_inputs();
       if (c + 2 < x.c_end) fetch(c + 2);
     }
     __syncthreads();
