@@ -21,7 +21,7 @@ IA_EXTERN_C(64)
 
 // ---------------------------------------------------------------- per-head tables
 // Once per call.  Block (h, run) holds one thread per (mode m, exponent j) with j in
-// [16 run, 16 run + 16); each entry is a direct complex power exp(n log lam).  Written in the
+// [16 run, 16 run + 16); beta lam^-j is a direct complex power exp(n log lam) per thread.  Written in the
 // LDS form the prefill kernel copies verbatim: beta lam^-j in bf16 ([Re;Im] rows, j in K-slot
 // order) and in scaled fp16 (row j, modes in K-slot order), both swizzled, and beta lam^(C-j)
 // in fp32 (the state-only pass's chunk table).  Block run 0 also writes the factors
@@ -46,22 +46,31 @@ __global__ void __launch_bounds__(16 * M) chunk_tables_kernel(const float2* __re
   const int j = 16 * run + jj;
   const float2 l = lam[(size_t)h * M + m];
   const float2 bt = beta[(size_t)h * M + m];
-  __shared__ float s_max[16 * M];
-  __shared__ float2 s_geo[16 * M], s_geot[16 * M], s_geol[16 * M];
+  // Per-mode base powers, one per thread jj < 6: lam^C, lam^-1, lam^-16, lam^(C-1), lam^Lt,
+  // lam^Ls.  Every other power below is one direct power per thread or a short product.
+  __shared__ float2 s_base[6][M];
+  __shared__ float s_max[M];
+  __shared__ float2 s_geo[16][M], s_geot[16][M];
+  if (jj < 6) {
+    const float n = jj == 0 ? (float)C : jj == 1 ? -1.f : jj == 2 ? -16.f
+                  : jj == 3 ? (float)(C - 1) : jj == 4 ? (float)Lt : (float)Ls;
+    s_base[jj][m] = cpow_f(l, n);
+  }
+  const float2 w = cmul(bt, cpow_f(l, -(float)j));   // beta lam^-j
+  __syncthreads();
 
   // fp16 table exponent: max_j |beta lam^-j| = |beta| |lam|^-(C-1) (|lam| <= 1); every block
-  // of the head reduces the same values, so all agree on the scale.
-  const float2 pc1 = cpow_f(l, (float)(C - 1));
-  s_max[threadIdx.x] = hypotf(bt.x, bt.y) / hypotf(pc1.x, pc1.y);
+  // of the head reduces the same values in the same order, so all agree on the scale.
+  if (jj == 0) s_max[m] = hypotf(bt.x, bt.y) / hypotf(s_base[3][m].x, s_base[3][m].y);
   __syncthreads();
-  for (int st = 8 * M; st > 0; st >>= 1) {
-    if (threadIdx.x < st) s_max[threadIdx.x] = fmaxf(s_max[threadIdx.x], s_max[threadIdx.x + st]);
+  for (int st = M / 2; st > 0; st >>= 1) {
+    if (jj == 0 && m < st) s_max[m] = fmaxf(s_max[m], s_max[m + st]);
     __syncthreads();
   }
   const float wscale = pow2_scale(s_max[0]);
 
-  const float2 w = cmul(bt, cpow_f(l, -(float)j));
-  reinterpret_cast<float2*>(tab + TL::oTL)[m * C + j] = cmul(bt, cpow_f(l, (float)(C - j)));
+  const float2 powC = s_base[0][m];
+  reinterpret_cast<float2*>(tab + TL::oTL)[m * C + j] = cmul(powC, w);   // beta lam^(C-j)
   WT[soff<C>(m, kpos(j))] = __builtin_bit_cast(uint16_t, (__bf16)w.x);
   WT[soff<C>(M + m, kpos(j))] = __builtin_bit_cast(uint16_t, (__bf16)w.y);
   Wb[soff<M2>(j, kpos(m))] = __builtin_bit_cast(uint16_t, (_Float16)(w.x * wscale));
@@ -71,40 +80,37 @@ __global__ void __launch_bounds__(16 * M) chunk_tables_kernel(const float2* __re
   if (threadIdx.x == 0) *reinterpret_cast<float*>(tab + TL::oSc) = 1.f / wscale;
   L2lo[jj * L2S + m] = cpow_f(l, 2.f * jj);
   if (jj < RUNS) L2hi[jj * M + m] = cpow_f(l, 32.f * jj);
-  // Geometric sums over j < C and j < Lt: thread jj takes j = jj, jj + 16, ...
-  float2 geo = make_float2(0.f, 0.f), geot = geo, geol = geo;
-  for (int jx = jj; jx < C; jx += 16) {
-    const float2 t = cmul(bt, cpow_f(l, -(float)jx));
+  // Geometric sums over j < C and j < Lt: thread jj takes j = jj + 16 i, i < C/16, as
+  // beta lam^-jj (lam^-16)^i.
+  float2 geo = make_float2(0.f, 0.f), geot = geo, t = w;
+  const float2 step = s_base[2][m];
+  for (int i = 0; i < RUNS; ++i) {
+    const int jx = jj + 16 * i;
     geo.x += t.x;
     geo.y += t.y;
     if (jx < Lt) {
       geot.x += t.x;
       geot.y += t.y;
     }
-    const float2 tl = cmul(bt, cpow_f(l, (float)(C - jx)));
-    geol.x += tl.x;
-    geol.y += tl.y;
+    t = cmul(t, step);
   }
-  s_geo[threadIdx.x] = geo;
-  s_geot[threadIdx.x] = geot;
-  s_geol[threadIdx.x] = geol;
+  s_geo[jj][m] = geo;
+  s_geot[jj][m] = geot;
   __syncthreads();
   if (jj == 0) {
     for (int k = 1; k < 16; ++k) {
-      geo.x += s_geo[k * M + m].x;
-      geo.y += s_geo[k * M + m].y;
-      geot.x += s_geot[k * M + m].x;
-      geot.y += s_geot[k * M + m].y;
-      geol.x += s_geol[k * M + m].x;
-      geol.y += s_geol[k * M + m].y;
+      geo.x += s_geo[k][m].x;
+      geo.y += s_geo[k][m].y;
+      geot.x += s_geot[k][m].x;
+      geot.y += s_geot[k][m].y;
     }
-    reinterpret_cast<float2*>(tab + TL::oGeoL)[m] = geol;
-    reinterpret_cast<float2*>(tab + TL::oPow)[m] = cpow_f(l, (float)C);
+    reinterpret_cast<float2*>(tab + TL::oGeoL)[m] = cmul(powC, geo);   // sum beta lam^(C-j)
+    reinterpret_cast<float2*>(tab + TL::oPow)[m] = powC;
     reinterpret_cast<float2*>(tab + TL::oGeo)[m] = geo;
-    reinterpret_cast<float2*>(tab + TL::oPowT)[m] = cpow_f(l, (float)Lt);
+    reinterpret_cast<float2*>(tab + TL::oPowT)[m] = s_base[4][m];
     reinterpret_cast<float2*>(tab + TL::oGeoT)[m] = geot;
-    reinterpret_cast<float2*>(tab + TL::oPowS)[m] = cpow_f(l, (float)Ls);
-    reinterpret_cast<float2*>(tab + TL::oInv)[m] = cpow_f(l, -1.f);
+    reinterpret_cast<float2*>(tab + TL::oPowS)[m] = s_base[5][m];
+    reinterpret_cast<float2*>(tab + TL::oInv)[m] = s_base[1][m];
   }
 }
 
