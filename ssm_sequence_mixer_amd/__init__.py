@@ -87,7 +87,7 @@ lib.ia_last_launch_error.restype = ctypes.c_char_p
 EXPORTS = ("ia_state_init", "ia_prefill_workspace_bytes", "ia_check_lambda", "ia_prefill_fwd",
            "ia_prefill_fwd_profiled", "ia_decode_step", "ia_status_string",
            "ia_last_launch_error")
-KIND_NAMES = {0: "fill", 1: "scan", 2: "tables", 3: "summary", 5: "chunk",
+KIND_NAMES = {0: "fill", 1: "scan", 2: "tables", 3: "summary", 4: "carry", 5: "chunk",
               6: "decode"}
 
 

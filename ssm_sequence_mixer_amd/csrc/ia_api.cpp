@@ -85,8 +85,9 @@ ScanWorkspace scan_workspace(const ia_desc* d, bool have_state) {
 }
 
 // Workspace and segmentation of the chunked (bf16, MFMA) path.  Segments cut each sequence so
-// that B*H*segments workgroups cover the 256 compute units about once.
-constexpr int kTargetWorkgroups = 256;
+// that B*H*segments output-pass workgroups fill the device once: as many as its compute units
+// hold at the same time (their count times the kernel's workgroups per CU), rounded down, so
+// no second, partial round of workgroups follows.
 
 struct ChunkPlan {
   int C, G, seg_chunks;
@@ -102,7 +103,9 @@ ChunkPlan chunk_plan(const ia_desc* d) {
   p.C = d->chunk ? d->chunk : 64;
   const int n_chunks = (d->N + p.C - 1) / p.C;
   const long seqs = long(d->B) * d->H;
-  long G = (kTargetWorkgroups + seqs - 1) / seqs;
+  int per_cu = ia::chunk_wgs_per_cu(p.C, d->F, d->Dv, d->M);
+  if (per_cu <= 0) per_cu = 1;
+  long G = long(ia::device_cus()) * per_cu / seqs;
   if (G > n_chunks) G = n_chunks;
   if (G < 1) G = 1;
   p.seg_chunks = int((n_chunks + G - 1) / G);

@@ -9,7 +9,8 @@ namespace ia {
   extern template hipError_t launch_chunk_t<C, FF, FF, MM>(const ChunkArgs&, int, hipStream_t, \
                                                            int);                          \
   extern template hipError_t launch_state_t<C, FF, FF, MM>(const ChunkArgs&, int, hipStream_t, \
-                                                           int);
+                                                           int);                          \
+  extern template int chunk_occupancy_t<C, FF, FF, MM>();
 #define IA_EXTERN_C(C)                                                                    \
   IA_EXTERN(C, 32, 16) IA_EXTERN(C, 32, 32) IA_EXTERN(C, 32, 64)                          \
   IA_EXTERN(C, 64, 16) IA_EXTERN(C, 64, 32) IA_EXTERN(C, 64, 64)                          \
@@ -114,6 +115,105 @@ __global__ void __launch_bounds__(16 * M) chunk_tables_kernel(const float2* __re
   }
 }
 
+// ---------------------------------------------------------------- segment carry
+// Turns the end states of segments 0..G-2 (each from a zero state, in the state waves'
+// accumulator layout) into the states entering segments 1..G-1, in place:
+//   slot 0 <- lam^Ls (lam init) + slot 0,   slot g <- lam^Ls slot g-1 + slot g.
+// One thread per complex pair (Re tile, Im tile) of a lane's float4s, or per mode of lam eta;
+// segments in order.  Used when the output pass would otherwise combine many slots per
+// workgroup.
+template <int F, int D, int M>
+__global__ void __launch_bounds__(256)
+carry_slots_kernel(float* __restrict__ slots, const float2* __restrict__ U0,
+                   const float2* __restrict__ G0, const float2* __restrict__ E0,
+                   const float2* __restrict__ lam, const unsigned char* __restrict__ tables,
+                   long table_bytes, long pows_off, int H, int nslots, long slot_floats) {
+  using SL = SlotLayout<F, D, M>;
+  constexpr int NS = SL::NS, NFT = SL::NFT, NDT = SL::NDT, TM = SL::TM, MH = M / 16;
+  constexpr int PAIRS = NS * (NFT + NDT) * MH * 64;
+  const int seq = blockIdx.y, h = seq % H;
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= PAIRS + M) return;
+  float* base = slots + (size_t)seq * nslots * slot_floats;
+  const float2* lamh = lam + (size_t)h * M;
+  const float2* pows =
+      reinterpret_cast<const float2*>(tables + (size_t)h * table_bytes + pows_off);
+  if (e >= PAIRS) {   // lam eta, mode m
+    const int m = e - PAIRS;
+    const float2 p = pows[m];
+    float2 c = E0 ? cmul(lamh[m], E0[(size_t)seq * M + m]) : make_float2(0.f, 0.f);
+    for (int g = 0; g < nslots; ++g) {
+      float2* sl = reinterpret_cast<float2*>(base + (size_t)g * slot_floats + SL::eta) + m;
+      c = cfma(p, c, *sl);
+      *sl = c;
+    }
+    return;
+  }
+  const int lane = e & 63, il = lane & 15, gq = lane >> 4;
+  const int mt = (e >> 6) % MH;
+  const int ts = (e >> 6) / MH % (NFT + NDT);   // tile set: f tiles, then d tiles
+  const int u = (e >> 6) / MH / (NFT + NDT);
+  const bool is_u = ts < NFT;
+  const int tile = is_u ? u + NS * ts : u + NS * (ts - NFT);
+  if (tile >= (is_u ? F / 16 : D / 16)) return;   // a tile no wave owns
+  float cr[4], ci[4];
+  for (int q = 0; q < 4; ++q) {
+    cr[q] = 0.f;
+    ci[q] = 0.f;
+    if (U0) {
+      const int m = is_u ? 16 * mt + il : 16 * mt + 4 * gq + q;
+      const float2 v = is_u ? U0[((size_t)seq * M + m) * F + 16 * tile + 4 * gq + q]
+                            : G0[((size_t)seq * M + m) * D + 16 * tile + il];
+      const float2 w = cmul(lamh[m], v);
+      cr[q] = w.x;
+      ci[q] = w.y;
+    }
+  }
+  const size_t re_off = ((size_t)(u * SL::NT + ts * TM + mt) * 64 + lane) * 4;
+  const size_t im_off = ((size_t)(u * SL::NT + ts * TM + mt + MH) * 64 + lane) * 4;
+  for (int g = 0; g < nslots; ++g) {
+    float* sl = base + (size_t)g * slot_floats;
+    const float4 r = *reinterpret_cast<const float4*>(sl + re_off);
+    const float4 i4 = *reinterpret_cast<const float4*>(sl + im_off);
+    const float rr[4] = {r.x, r.y, r.z, r.w}, ii[4] = {i4.x, i4.y, i4.z, i4.w};
+    for (int q = 0; q < 4; ++q) {
+      const int m = is_u ? 16 * mt + il : 16 * mt + 4 * gq + q;
+      const float2 p = pows[m];
+      const float xr = cr[q], yi = ci[q];
+      cr[q] = p.x * xr - p.y * yi + rr[q];
+      ci[q] = p.x * yi + p.y * xr + ii[q];
+    }
+    *reinterpret_cast<float4*>(sl + re_off) = make_float4(cr[0], cr[1], cr[2], cr[3]);
+    *reinterpret_cast<float4*>(sl + im_off) = make_float4(ci[0], ci[1], ci[2], ci[3]);
+  }
+}
+
+template <int F, int D, int M>
+static hipError_t launch_carry_t(const ChunkPrefillArgs& p, long tb, long pows_off, int nslots,
+                                 long slot_floats, hipStream_t st) {
+  using SL = SlotLayout<F, D, M>;
+  constexpr int n = SL::NS * (SL::NFT + SL::NDT) * (M / 16) * 64 + M;
+  (void)hipGetLastError();
+  prof_begin(st);
+  hipLaunchKernelGGL((carry_slots_kernel<F, D, M>), dim3((n + 255) / 256, p.B * p.H), dim3(256),
+                     0, st, p.slots, p.U0, p.G0, p.E0, p.lam, p.tables, tb, pows_off, p.H, nslots,
+                     slot_floats);
+  prof_end(st, kKindCarry);
+  return hipGetLastError();
+}
+
+static hipError_t launch_carry(const ChunkPrefillArgs& p, long tb, long pows_off, int nslots,
+                               long slot_floats, hipStream_t st) {
+#define IA_CARRY(FF, MM) \
+  if (p.F == FF && p.D == FF && p.M == MM)   \
+    return launch_carry_t<FF, FF, MM>(p, tb, pows_off, nslots, slot_floats, st);
+  IA_CARRY(32, 16) IA_CARRY(32, 32) IA_CARRY(32, 64)
+  IA_CARRY(64, 16) IA_CARRY(64, 32) IA_CARRY(64, 64)
+  IA_CARRY(128, 16) IA_CARRY(128, 32) IA_CARRY(128, 64)
+#undef IA_CARRY
+  return hipErrorInvalidValue;
+}
+
 // ---------------------------------------------------------------- launch
 
 template <int C>
@@ -177,6 +277,31 @@ long chunk_table_bytes(int chunk, int M) {
   return 0;
 }
 
+int chunk_wgs_per_cu(int chunk, int F, int D, int M) {
+#define IA_OCC(CC, FF, MM) \
+  if (chunk == CC && F == FF && D == FF && M == MM) return chunk_occupancy_t<CC, FF, FF, MM>();
+  IA_OCC(32, 32, 16) IA_OCC(32, 32, 32) IA_OCC(32, 32, 64)
+  IA_OCC(32, 64, 16) IA_OCC(32, 64, 32) IA_OCC(32, 64, 64)
+  IA_OCC(32, 128, 16) IA_OCC(32, 128, 32) IA_OCC(32, 128, 64)
+  IA_OCC(64, 32, 16) IA_OCC(64, 32, 32) IA_OCC(64, 32, 64)
+  IA_OCC(64, 64, 16) IA_OCC(64, 64, 32) IA_OCC(64, 64, 64)
+  IA_OCC(64, 128, 16) IA_OCC(64, 128, 32) IA_OCC(64, 128, 64)
+#undef IA_OCC
+  return 0;
+}
+
+static long pows_offset(int chunk, int M) {
+  switch (chunk * 1000 + M) {
+    case 32016: return TableLayout<32, 16>::oPowS;
+    case 32032: return TableLayout<32, 32>::oPowS;
+    case 32064: return TableLayout<32, 64>::oPowS;
+    case 64016: return TableLayout<64, 16>::oPowS;
+    case 64032: return TableLayout<64, 32>::oPowS;
+    case 64064: return TableLayout<64, 64>::oPowS;
+  }
+  return 0;
+}
+
 long chunk_slot_floats(int F, int D, int M) {
 #define IA_SLOT(FF, MM) \
   if (F == FF && D == FF && M == MM) return SlotLayout<FF, FF, MM>::floats;
@@ -186,6 +311,10 @@ long chunk_slot_floats(int F, int D, int M) {
 #undef IA_SLOT
   return 0;
 }
+
+// Up to this many predecessor slots an output workgroup combines itself (Horner); beyond, a
+// carry kernel writes inclusive states first.
+constexpr int kHornerSlots = 3;
 
 // Full chunked prefill for one direction: tables; the end states of segments 0..G-2 from a
 // zero state; every segment (or, state only, the last) from its initial state, which each
@@ -225,6 +354,7 @@ hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
                    : dispatch_fdm<32>(x, p.F, p.D, p.M, n_wg, st, kind);
   };
 
+  bool inclusive = false;
   if (G > 1) {
     // Pass 1: end state of segments 0..G-2 from a zero state.
     ChunkArgs s = a;
@@ -234,11 +364,19 @@ hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
     e = C == 64 ? dispatch_state_fdm<64>(s, p.F, p.D, p.M, seqs * (G - 1), st, kKindSummary)
                 : dispatch_state_fdm<32>(s, p.F, p.D, p.M, seqs * (G - 1), st, kKindSummary);
     if (e != hipSuccess) return e;
+    // With many segments, carry once (each slot read and written once) instead of letting
+    // every output workgroup combine all of its predecessors' slots.
+    if (G - 1 > kHornerSlots) {
+      e = launch_carry(p, tb, pows_offset(C, p.M), G - 1, a.slot_floats, st);
+      if (e != hipSuccess) return e;
+      inclusive = true;
+    }
   }
   // Pass 2: every segment from its initial state, with outputs; the last segment returns the
   // final state.  State-only calls run just the last segment.
   ChunkArgs o = a;
   o.seg_prev = G > 1 ? p.slots : nullptr;
+  o.seg_inclusive = inclusive;
   o.init0_U = p.U0;
   o.init0_G = p.G0;
   o.init0_E = p.E0;

@@ -255,13 +255,16 @@ struct ChunkArgs {
   float clamp;
   // Initial state of segment g: the caller's state init0 (or zeros) carried across segments
   // 0..g-1, whose end states (each computed from a zero state) are the workspace slots
-  // seg_prev[seq][0..g-1]: state <- lam^Ls state + slot, Ls the segment length.  Final state:
+  // seg_prev[seq][0..g-1]: state <- lam^Ls state + slot, Ls the segment length (with
+  // seg_inclusive, slot seg_prev[seq][g-1] is already that state).  Final state:
   // with seg_end set, segment g writes slot seg_end[seq][g]; otherwise the segment holding
   // the last token writes the caller's fin (if set).  Slots hold lam U, lam G and lam eta in
   // the state waves' accumulator layout (SlotLayout).
   const float2 *init0_U, *init0_G, *init0_E;   // caller layout: [seq][M][F] etc.
   float2 *fin_U, *fin_G, *fin_E;               // caller layout
   const float* seg_prev;
+  int seg_inclusive;                           // seg_prev[g] already holds the state entering
+                                               // segment g+1 (caller state included)
   float* seg_end;
   long slot_floats;                            // floats per slot
   int slots_per_seq;
@@ -613,7 +616,8 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
   // segments of this sequence.
   using SL = SlotLayout<F, D, M>;
   const float2 *iU = nullptr, *iG = nullptr, *iE = nullptr;
-  if (a.init0_U) {
+  const bool from_slot = a.seg_prev && a.seg_inclusive && x.seg > 0;
+  if (a.init0_U && !from_slot) {
     iU = a.init0_U + (size_t)x.seq * M * F;
     iG = a.init0_G + (size_t)x.seq * M * D;
     iE = a.init0_E + (size_t)x.seq * M;
@@ -656,7 +660,9 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
   }
   if (a.seg_prev && x.seg > 0) {
     const float2* pows = reinterpret_cast<const float2*>(x.tab + TL::oPowS);
-    for (int sp = 0; sp < x.seg; ++sp) {
+    // Horner over the earlier segments; an inclusive slot is the state itself (zero state
+    // times lam^Ls plus the slot).
+    for (int sp = a.seg_inclusive ? x.seg - 1 : 0; sp < x.seg; ++sp) {
       const float* sl = a.seg_prev + ((size_t)x.seq * a.slots_per_seq + sp) * a.slot_floats;
 #pragma unroll
       for (int fi = 0; fi < NFT; ++fi)
@@ -1062,17 +1068,40 @@ chunk_prefill_kernel(const ChunkArgs a) {
 }
 
 template <int C, int F, int D, int M>
-hipError_t launch_chunk_t(const ChunkArgs& a, int n_wg, hipStream_t st, int kind) {
-  constexpr int threads = 64 * (C / 16 + StateWaves<F, D, M>::NS);
-  constexpr int bytes = Layout<C, F, D, M, C / 16>::bytes;
-  static_assert(bytes <= 160 * 1024, "LDS budget");
+hipError_t chunk_kernel_attr() {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&chunk_prefill_kernel<C, F, D, M>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+        hipFuncAttributeMaxDynamicSharedMemorySize, Layout<C, F, D, M, C / 16>::bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
+  }
+  return hipSuccess;
+}
+
+// Workgroups of the output-pass kernel one CU holds at once (LDS, registers, waves), or 0 if
+// the runtime cannot say (no device).
+template <int C, int F, int D, int M>
+int chunk_occupancy_t() {
+  if (chunk_kernel_attr<C, F, D, M>() != hipSuccess) return 0;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(&chunk_prefill_kernel<C, F, D, M>),
+          64 * (C / 16 + StateWaves<F, D, M>::NS), Layout<C, F, D, M, C / 16>::bytes) !=
+      hipSuccess)
+    return 0;
+  return n;
+}
+
+template <int C, int F, int D, int M>
+hipError_t launch_chunk_t(const ChunkArgs& a, int n_wg, hipStream_t st, int kind) {
+  constexpr int threads = 64 * (C / 16 + StateWaves<F, D, M>::NS);
+  constexpr int bytes = Layout<C, F, D, M, C / 16>::bytes;
+  static_assert(bytes <= 160 * 1024, "LDS budget");
+  {
+    hipError_t e = chunk_kernel_attr<C, F, D, M>();
+    if (e != hipSuccess) return e;
   }
   (void)hipGetLastError();
   prof_begin(st);

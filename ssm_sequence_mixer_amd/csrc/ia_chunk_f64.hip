@@ -16,5 +16,11 @@ template hipError_t launch_state_t<32, 64, 64, 64>(const ChunkArgs&, int, hipStr
 template hipError_t launch_state_t<64, 64, 64, 16>(const ChunkArgs&, int, hipStream_t, int);
 template hipError_t launch_state_t<64, 64, 64, 32>(const ChunkArgs&, int, hipStream_t, int);
 template hipError_t launch_state_t<64, 64, 64, 64>(const ChunkArgs&, int, hipStream_t, int);
+template int chunk_occupancy_t<32, 64, 64, 16>();
+template int chunk_occupancy_t<32, 64, 64, 32>();
+template int chunk_occupancy_t<32, 64, 64, 64>();
+template int chunk_occupancy_t<64, 64, 64, 16>();
+template int chunk_occupancy_t<64, 64, 64, 32>();
+template int chunk_occupancy_t<64, 64, 64, 64>();
 
 }  // namespace ia

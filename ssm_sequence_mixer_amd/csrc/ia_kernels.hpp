@@ -12,7 +12,7 @@ enum LaunchKind {
   kKindScan = 1,       // token-sequential prefill
   kKindTables = 2,     // per-head decay tables of the chunked prefill
   kKindSummary = 3,    // chunked prefill, segment end states (no outputs)
-  // 4: not used
+  kKindCarry = 4,      // segment carry (many segments)
   kKindChunk = 5,      // chunked prefill with outputs (or the last segment's state)
   kKindDecode = 6,
 };
@@ -88,6 +88,8 @@ struct ChunkPrefillArgs {
 bool chunk_supported(int F, int D, int M);
 long chunk_table_bytes(int chunk, int M);
 long chunk_slot_floats(int F, int D, int M);
+int chunk_wgs_per_cu(int chunk, int F, int D, int M);   // 0 if unknown (no device)
+int device_cus();                                        // compute units of the current device
 hipError_t launch_chunk_prefill(const ChunkPrefillArgs& a, hipStream_t st);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);

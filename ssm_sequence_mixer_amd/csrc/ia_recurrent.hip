@@ -331,8 +331,8 @@ static void launch_decode_rows(const DecodeArgs& a, hipStream_t st) {
                        a.in_bf16, a.out_bf16, a.clamp);
 }
 
-// Compute units of the current device (cached per device).
-static int device_cus() {
+// Compute units of the current device (cached per device; 256 when there is none).
+int device_cus() {
   static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;

@@ -66,6 +66,28 @@ def test_chunk_many_segments_with_state(chunk):
     assert e_o < TOL_BF16 and e_s < TOL_BF16
 
 
+def test_chunk_few_segments_with_state():
+    """Many (b,h) slices, 2048 tokens, non-zero initial state: a few segments per sequence,
+    whose output workgroups combine their predecessors' end states themselves."""
+    B, H, N, F, M = 6, 16, 2048, 64, 32
+    inp = W.make_inputs(B, H, N, F, F, M, dtype="bf16", seed=17)
+    pre = W.make_inputs(B, H, 24, F, F, M, dtype="bf16", seed=18)
+    st_ref = oracle.prefill(pre["q"], pre["k"], pre["v"], inp["lam"], inp["beta"], threads=8)[3]
+    st = tuple(dev(s) for s in st_ref)
+    st_ref = tuple(host(s) for s in st)
+    tag("chunk prefill few segments with state")
+    o = _run(inp, state=st)
+    slices = [(0, 0), (2, 5), (5, 15)]
+    o_ref, _, _, st_out = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"],
+                                         state=st_ref, threads=8)
+    o = host(o)
+    e_o = max(rowrel(o[b, :, h], o_ref[b, :, h]) for b, h in slices)
+    e_s = state_rel(tuple(host(s) for s in st), st_out)
+    report("few segments output", e_o)
+    report("few segments state", e_s)
+    assert e_o < TOL_BF16 and e_s < TOL_BF16
+
+
 def test_chunk_size_invariance():
     B, H, N, F, M = 2, 2, 300, 64, 64
     inp = W.make_inputs(B, H, N, F, F, M, dtype="bf16", seed=55)
