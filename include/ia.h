@@ -103,9 +103,10 @@ typedef struct ia_state {
 ia_status ia_state_init(const ia_desc* desc, ia_state* st, void* stream);
 
 /* Bytes of device workspace ia_prefill_fwd needs for `desc` (may be 0); 0 also if the desc
- * is invalid.  The workspace holds per-segment state summaries of the chunked scan, a state
- * for state-less fp32 calls, and the first direction's fp32 output for IA_FLAG_BIDIR on the
- * fp32 path.  Its contents need no initialisation and are scratch between calls. */
+ * is invalid.  The workspace holds the per-head tables and per-segment state summaries of the
+ * chunked scan, or a state for state-less fp32 calls.  Its contents need no initialisation
+ * and are scratch between calls.  (The bidirectional layer accumulates its two directions in
+ * o itself, in o's dtype.) */
 size_t ia_prefill_workspace_bytes(const ia_desc* desc);
 
 /* Host-side check of the mode domain for `desc` (lambda_host: [H][M] complex64 in HOST

@@ -65,21 +65,17 @@ ia_status check_state(const ia_desc* d, const ia_state* st) {
   return IA_OK;
 }
 
-// Workspace of the fp32 (token-sequential) prefill path.
+// Workspace of the fp32 (token-sequential) prefill path: a state when the caller passes none.
 struct ScanWorkspace {
-  size_t state_off, acc_off, bytes;
+  size_t state_off, bytes;
 };
 
 ScanWorkspace scan_workspace(const ia_desc* d, bool have_state) {
-  ScanWorkspace w{0, 0, 0};
+  ScanWorkspace w{0, 0};
   const bool bidir = d->flags & IA_FLAG_BIDIR;
   if (!have_state || bidir) {
     w.state_off = 0;
     w.bytes = round_up(state_bytes(d));
-  }
-  if (bidir) {
-    w.acc_off = w.bytes;
-    w.bytes += round_up(size_t(d->B) * d->N * d->H * d->Dv * 4);
   }
   return w;
 }
@@ -91,7 +87,7 @@ ScanWorkspace scan_workspace(const ia_desc* d, bool have_state) {
 
 struct ChunkPlan {
   int C, G, seg_chunks;
-  size_t tables_off, slots_off, acc_off, bytes;
+  size_t tables_off, slots_off, bytes;
 };
 
 bool use_chunk_path(const ia_desc* d) {
@@ -115,8 +111,6 @@ ChunkPlan chunk_plan(const ia_desc* d) {
   p.slots_off = p.bytes;
   if (p.G > 1)
     p.bytes += round_up(size_t(seqs) * (p.G - 1) * ia::chunk_slot_floats(d->F, d->Dv, d->M) * 4);
-  p.acc_off = p.bytes;
-  if (d->flags & IA_FLAG_BIDIR) p.bytes += round_up(size_t(d->B) * d->N * d->H * d->Dv * 4);
   return p;
 }
 
@@ -263,14 +257,10 @@ ia_status ia_prefill_fwd(const ia_desc* d, const void* q, const void* k, const v
     a.out_bf16 = d->out_dtype == IA_BF16;
     a.clamp = d->den_clamp;
     if (!bidir) return launch_status(ia::launch_chunk_prefill(a, hs));
-    float* acc = reinterpret_cast<float*>(ws + pl.acc_off);
-    a.o = acc;
-    a.out_bf16 = 0;
+    // Bidirectional: the forward direction writes o, the reverse direction adds onto it.
     hipError_t e = ia::launch_chunk_prefill(a, hs);
     if (e == hipSuccess) {
-      a.o = o;
-      a.out_bf16 = d->out_dtype == IA_BF16;
-      a.acc_in = acc;
+      a.accumulate = 1;
       a.reverse = 1;
       e = ia::launch_chunk_prefill(a, hs);
     }
@@ -301,19 +291,16 @@ ia_status ia_prefill_fwd(const ia_desc* d, const void* q, const void* k, const v
     if (e != hipSuccess) return launch_status(e);
   }
   ia::ScanArgs a{q, k, v, static_cast<const float2*>(lambda), static_cast<const float2*>(beta),
-                 U, G, E, o, nullptr, d->B, d->H, d->N, d->F, d->Dv, d->M,
+                 U, G, E, o, 0, d->B, d->H, d->N, d->F, d->Dv, d->M,
                  d->in_dtype == IA_BF16, d->out_dtype == IA_BF16, d->den_clamp, 0};
   if (!bidir) return launch_status(ia::launch_scan_prefill(a, hs));
 
-  float* acc = reinterpret_cast<float*>(ws + w.acc_off);
-  a.o = acc;
-  a.out_bf16 = 0;
+  // Bidirectional: the forward direction writes o, the reverse direction (from a zero state
+  // again) adds onto it.
   hipError_t e = ia::launch_scan_prefill(a, hs);
   if (e == hipSuccess) e = ia::launch_fill_zero(ws + w.state_off, state_bytes(d), hs);
   if (e == hipSuccess) {
-    a.o = o;
-    a.out_bf16 = d->out_dtype == IA_BF16;
-    a.acc_in = acc;
+    a.accumulate = 1;
     a.reverse = 1;
     e = ia::launch_scan_prefill(a, hs);
   }

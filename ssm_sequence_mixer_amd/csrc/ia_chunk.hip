@@ -381,7 +381,7 @@ hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
   o.init0_G = p.G0;
   o.init0_E = p.E0;
   o.o = p.o;
-  o.acc_in = p.acc_in;
+  o.accumulate = p.accumulate;
   o.fin_U = p.U1;
   o.fin_G = p.G1;
   o.fin_E = p.E1;

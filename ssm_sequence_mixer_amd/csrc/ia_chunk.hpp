@@ -245,7 +245,7 @@ struct ChunkArgs {
   const uint16_t *q, *k, *v;   // bf16 [B][N][H][F|D]
   const float2 *lam, *beta;    // [H][M]
   void* o;                     // [B][N][H][D] or NULL (state only)
-  const float* acc_in;         // fp32 [B][N][H][D] added to the output, or NULL
+  int accumulate;              // add to the values o holds (second bidirectional direction)
   int N, H;
   int seg_chunks;              // chunks per segment
   int seg_first;               // first segment index handled by this launch
@@ -515,7 +515,6 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
       const size_t obase = ok ? x.tok_index(a, x.pos_of(a, t)) * D + 4 * g : 0;
       uint16_t* const o16 = static_cast<uint16_t*>(a.o) + obase;
       float* const o32 = static_cast<float*>(a.o) + obase;
-      const float* const prev_row = a.acc_in + obase;
 #pragma unroll
       for (int dt = 0; dt < TD; ++dt) {
         f32x4 accI = {0.f, 0.f, 0.f, 0.f}, accX = {0.f, 0.f, 0.f, 0.f};
@@ -530,14 +529,22 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
           const float4 ci = *reinterpret_cast<const float4*>(sb + oCi + 64 * dt);
           float val[4] = {(accI[0] + accX[0] * ci.x) * rd, (accI[1] + accX[1] * ci.y) * rd,
                           (accI[2] + accX[2] * ci.z) * rd, (accI[3] + accX[3] * ci.w) * rd};
-          if (a.acc_in) {
-            const float4 prev = *reinterpret_cast<const float4*>(prev_row + 16 * dt);
-            val[0] += prev.x; val[1] += prev.y; val[2] += prev.z; val[3] += prev.w;
-          }
-          if (a.out_bf16)
+          if (a.out_bf16) {
+            if (a.accumulate) {   // the element's other direction, same lane, read then written
+              const uint2 p = *reinterpret_cast<const uint2*>(o16 + 16 * dt);
+              val[0] += __uint_as_float(p.x << 16);
+              val[1] += __uint_as_float(p.x & 0xffff0000u);
+              val[2] += __uint_as_float(p.y << 16);
+              val[3] += __uint_as_float(p.y & 0xffff0000u);
+            }
             *reinterpret_cast<uint2*>(o16 + 16 * dt) = pack4_bf16(val[0], val[1], val[2], val[3]);
-          else
+          } else {
+            if (a.accumulate) {
+              const float4 p = *reinterpret_cast<const float4*>(o32 + 16 * dt);
+              val[0] += p.x; val[1] += p.y; val[2] += p.z; val[3] += p.w;
+            }
             *reinterpret_cast<float4*>(o32 + 16 * dt) = make_float4(val[0], val[1], val[2], val[3]);
+          }
         }
         IA_STEP_FENCE();
       }

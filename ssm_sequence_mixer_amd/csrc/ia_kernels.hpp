@@ -57,7 +57,7 @@ struct ScanArgs {
   const float2 *lam, *beta;
   float2 *U, *G, *E;
   void* o;
-  const float* acc_in;
+  int accumulate;   // add to the values already in o (second direction of the bidirectional layer)
   int B, H, N, F, D, M;
   int in_bf16, out_bf16;
   float clamp;
@@ -69,12 +69,13 @@ struct ScanArgs {
 // go through `slots` (B*H*(segments-1) slots of chunk_slot_floats(F, D, M) floats), from
 // which each segment's workgroup assembles its initial state.  `tables` holds
 // H * chunk_table_bytes(chunk, M) bytes.  U0/G0/E0: initial state or NULL (zeros);
-// U1/G1/E1: final state or NULL.  o NULL: state only.  acc_in: fp32 added to o, or NULL.
+// U1/G1/E1: final state or NULL.  o NULL: state only.  accumulate: add to the values already
+// in o (in o's dtype).
 struct ChunkPrefillArgs {
   const void *q, *k, *v;
   const float2 *lam, *beta;
   void* o;
-  const float* acc_in;
+  int accumulate;
   const float2 *U0, *G0, *E0;
   float2 *U1, *G1, *E1;
   float* slots;                 // (B*H) x (segments-1) segment end states

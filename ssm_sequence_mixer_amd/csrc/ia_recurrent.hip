@@ -259,14 +259,14 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
 
 // Token-sequential prefill (the fp32 path).  grid = B*H; one workgroup walks all N tokens of
 // its slice, in reverse when `reverse` is set (then token t of the walk is position N-1-t).
-// o (out dtype) receives acc_in[pos] + value when acc_in != NULL (the second direction of the
-// bidirectional layer adds onto the first), else value; o may be NULL (state only).
+// o (out dtype) receives value, or o + value with `accumulate` (the second direction of the
+// bidirectional layer adds onto the first); o may be NULL (state only).
 __global__ void __launch_bounds__(kStepThreads)
 scan_prefill_kernel(const void* __restrict__ q, const void* __restrict__ k,
                     const void* __restrict__ v, const float2* __restrict__ lam,
                     const float2* __restrict__ beta, float2* __restrict__ U,
                     float2* __restrict__ G, float2* __restrict__ E, void* __restrict__ o,
-                    const float* __restrict__ acc_in, int N, int H, int F, int D, int M,
+                    int accumulate, int N, int H, int F, int D, int M,
                     int in_bf16, int out_bf16, float clamp, int reverse) {
   __shared__ StepSmem s;
   const int bh = blockIdx.x;
@@ -288,7 +288,7 @@ scan_prefill_kernel(const void* __restrict__ q, const void* __restrict__ k,
 #pragma unroll
         for (int w = 0; w < kStepWaves; ++w) n += s.num[w][j];
         float val = n / den;
-        if (acc_in) val += acc_in[tok * D + j];
+        if (accumulate) val += load_in(o, tok * D + j, out_bf16);
         store_out(o, tok * D + j, val, out_bf16);
       }
     }
@@ -371,7 +371,7 @@ hipError_t launch_scan_prefill(const ScanArgs& a, hipStream_t st) {
   (void)hipGetLastError();
   prof_begin(st);
   hipLaunchKernelGGL(scan_prefill_kernel, dim3(a.B * a.H), dim3(kStepThreads), 0, st, a.q,
-                     a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.acc_in, a.N, a.H, a.F, a.D,
+                     a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.accumulate, a.N, a.H, a.F, a.D,
                      a.M, a.in_bf16, a.out_bf16, a.clamp, a.reverse);
   prof_end(st, kKindScan);
   return hipGetLastError();
