@@ -91,7 +91,11 @@ struct ChunkPlan {
 };
 
 bool use_chunk_path(const ia_desc* d) {
-  return d->in_dtype == IA_BF16 && ia::chunk_supported(d->F, d->Dv, d->M);
+  // The chunk kernels address a chunk's token rows with 32-bit byte offsets, rows outside a
+  // chunk wrapping to large ones: 64 rows of H * F bf16 values must span at most 1 GiB (else
+  // the token-sequential path runs).
+  return d->in_dtype == IA_BF16 && ia::chunk_supported(d->F, d->Dv, d->M) &&
+         64L * d->H * std::max(d->F, d->Dv) * 2 <= (1L << 30);
 }
 
 ChunkPlan chunk_plan(const ia_desc* d) {

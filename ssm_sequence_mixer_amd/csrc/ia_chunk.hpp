@@ -232,11 +232,13 @@ struct Layout {
   static constexpr int bC = n16 * 2;               // [D]  float  c_d
   static constexpr int bCi = bC + D * 4;           // [D]  float  1 / c_d
   static constexpr int bLE = bCi + D * 4;          // [M]  float2 lam eta_c
-  static constexpr int bLam = bLE + M * 8;         // [M]  float2 lam
-  static constexpr int bPowL = bLam + M * 8;       // [M]  float2 lam^L of the current chunk
-  static constexpr int bGeo = bPowL + M * 8;       // [M]  float2 sum_{j<L} beta lam^-j
+  static constexpr int bPowL = bLE + M * 8;        // [M]  float2 lam^C
+  static constexpr int bGeo = bPowL + M * 8;       // [M]  float2 sum_{j<C} beta lam^-j
+  static constexpr int bPowT = bGeo + M * 8;       // [M]  float2 lam^Lt, last (partial) chunk
+  static constexpr int bGeoT = bPowT + M * 8;      // [M]  float2 sum_{j<Lt} beta lam^-j
+  static constexpr int kTail = bPowT - bPowL;      // offset of the last chunk's pair
   static constexpr int L2S = M + 2;                // row stride of the lam^(2i) factor table
-  static constexpr int bL2lo = bGeo + M * 8;       // [16][L2S] float2 lam^(2i), i = 0..15
+  static constexpr int bL2lo = bGeoT + M * 8;      // [16][L2S] float2 lam^(2i), i = 0..15
   static constexpr int bL2hi = bL2lo + 16 * L2S * 8;  // [NR][M] float2 lam^(32r)
   static constexpr int bytes = bL2hi + NR * M * 8;
 };
@@ -293,12 +295,16 @@ struct TableLayout {
   static constexpr long bytes = (oGeoL + 8L * M + 255) / 256 * 256;
 };
 
+// Word 3 of a CDNA buffer resource for raw (untyped) loads: 32-bit data format, no swizzle,
+// no index stride; offsets at or past the range read as zeros.
+constexpr int kBufferFlags = 0x00020000;
+
 // Per-workgroup context shared by the two wave roles.
 template <int C, int F, int D, int M>
 struct Ctx {
   uint16_t *s16, *sFk, *sFq, *sV, *sWT, *sWb, *sLU, *sGT;
   float *sC, *sCi;
-  float2 *sLE, *sLam, *sPowL, *sGeo, *sL2lo, *sL2hi;
+  float2 *sLE, *sPowL, *sGeo, *sL2lo, *sL2hi;
   const unsigned char* tab;
   int lane, il, g, wave;
   int seq, seg, b, h, c_begin, c_end;
@@ -308,7 +314,33 @@ struct Ctx {
   __device__ size_t tok_index(const ChunkArgs& a, int pos) const {
     return ((size_t)b * a.N + pos) * a.H + h;
   }
+  // The L valid token rows of chunk c of a [B][N][H][width] bf16 tensor as a buffer: based
+  // at the lowest-addressed valid row (row 0 walking forward, row L-1 walking backward),
+  // L row strides long.  Row r (walk order) column e lies at row_off(r, e) - shift; rows at
+  // or past the sequence end fall outside the range (past its end forward, below its base,
+  // wrapping to large offsets, backward) and read as zeros.
+  __device__ __amdgpu_buffer_rsrc_t chunk_rows(const ChunkArgs& a, const uint16_t* t, int width,
+                                               int c, uint32_t& shift) const {
+    const int L = min(C, a.N - c * C);
+    const uint32_t stride = (uint32_t)a.H * width * 2u;
+    shift = a.dir ? (uint32_t)(C - L) * stride : 0u;
+    const uint16_t* p = t + tok_index(a, a.dir ? a.N - c * C - L : c * C) * width;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0,
+                                             (int)((uint32_t)L * stride), kBufferFlags);
+  }
+  // Byte offset of chunk row r (0 = the chunk's first token in walk order), column e, from the
+  // lowest-addressed row of a full chunk.
+  __device__ static uint32_t row_off(const ChunkArgs& a, int width, int r, int e) {
+    return (uint32_t)((a.dir ? C - 1 - r : r) * a.H * width + e) * 2u;
+  }
 };
+
+// 16 bytes through a buffer resource (zeros outside its range).
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef __attribute__((ext_vector_type(4))) unsigned v4u;
+  const v4u v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 // ---------------------------------------------------------------- readout waves
 // Wave R owns queries [16R, 16R+16) of every chunk.
@@ -359,15 +391,13 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
   int stV[NV];
 #pragma unroll
   for (int t = 0; t < NV; ++t) stV[t] = opaque(Lay::oV + soff<D>(16 * r + il, 8 * (g + 4 * t)));
-  const int lofV = (a.dir ? -1 : 1) * (16 * r + il) * (a.H * D) + 8 * g;
+  const uint32_t lofV = x.row_off(a, D, 16 * r + il, 8 * g);
   uint4 rv[NV];
-  auto fetch_v = [&](int c) {
-    const int t0 = c * C;
-    const uint16_t* vb = a.v + x.tok_index(a, x.pos_of(a, t0)) * D + lofV;
-    const bool ok = t0 + 16 * r + il < a.N;
+  auto fetch_v = [&](int c) {   // rows past N read as zeros
+    uint32_t shift;
+    const __amdgpu_buffer_rsrc_t vb = x.chunk_rows(a, a.v, D, c, shift);
 #pragma unroll
-    for (int t = 0; t < NV; ++t)
-      rv[t] = ok ? *reinterpret_cast<const uint4*>(vb + 32 * t) : make_uint4(0, 0, 0, 0);
+    for (int t = 0; t < NV; ++t) rv[t] = load16(vb, lofV - shift + 64 * t);
   };
   auto write_v = [&]() {
 #pragma unroll
@@ -619,6 +649,59 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
 #pragma unroll
     for (int kt = 0; kt < TM; ++kt) accG[di][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // ---- chunk inputs q, k: this wave loads 16-byte vectors n = 64u + lane + NL t of the
+  // row-major chunk matrices ([C][F]); vector n0 + NL t is row row0 + t NL/VF.  Token rows are
+  // H*F elements apart in memory, walking backwards for the reverse direction; per chunk the
+  // wave-uniform base moves, the per-lane offsets stay.  (The readout waves load v.)
+  const int n0 = 64 * u + lane;
+  const int rowF0 = n0 / VF;
+  uint32_t lofF[NLF];
+#pragma unroll
+  for (int t = 0; t < NLF; ++t) lofF[t] = x.row_off(a, F, rowF0 + t * (NL / VF), 8 * (n0 % VF));
+  // LDS rows row0 + t NL/VF share the swizzle of row0 (NL/VF is a multiple of 16).
+  static_assert((NL / VF) % 16 == 0, "loader rows keep the swizzle");
+  const int stF = opaque(Lay::oFk + soff<F>(rowF0, 8 * (n0 % VF)));
+  // Raw bf16 q, k of a chunk, then (convert) phi(q), phi(k) as packed bf16.
+  uint4 rq[NLF], rk[NLF];
+  auto fetch = [&](int c) {   // rows past N (and past the chunk) read as zeros
+    uint32_t shift;
+    const __amdgpu_buffer_rsrc_t kb = x.chunk_rows(a, a.k, F, c, shift);
+    const __amdgpu_buffer_rsrc_t qb = x.chunk_rows(a, a.q, F, c, shift);
+#pragma unroll
+    for (int t = 0; t < NLF; ++t) {
+      rk[t] = load16(kb, lofF[t] - shift);
+      if (x.want_out) rq[t] = load16(qb, lofF[t] - shift);
+    }
+  };
+  // Features in place.  Rows past N get zero features (not phi(0)); their values are zero.
+  auto phi8 = [&](uint4& r, bool ok) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)   // bf16 pair -> two floats -> features -> bf16 pair
+      o[i] = pk_bf16(feature(__uint_as_float(w[i] << 16)),
+                     feature(__uint_as_float(w[i] & 0xffff0000u)));
+    r = ok ? make_uint4(o[0], o[1], o[2], o[3]) : make_uint4(0, 0, 0, 0);
+  };
+  auto convert = [&](int c) {
+    const int L = a.N - c * C;
+#pragma unroll
+    for (int t = 0; t < NLF; ++t) {
+      const bool ok = rowF0 + t * (NL / VF) < L;
+      phi8(rk[t], ok);
+      if (x.want_out) phi8(rq[t], ok);
+    }
+  };
+  auto write_inputs = [&]() {
+#pragma unroll
+    for (int t = 0; t < NLF; ++t)
+      if (n0 + NL * t < C * VF) {
+        const int so = stF + t * (NL / VF) * F;
+        *reinterpret_cast<uint4*>(s16 + so) = rk[t];
+        if (x.want_out) *reinterpret_cast<uint4*>(s16 + so + (Lay::oFq - Lay::oFk)) = rq[t];
+      }
+  };
+
   // Initial state (times lam): the caller's state, then the end states of the earlier
   // segments of this sequence.
   using SL = SlotLayout<F, D, M>;
@@ -774,72 +857,6 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
     }
     if (u == 0 && lane < M) f2(oLn) = eta;
   };
-  // Decay factors of chunk c when it is the last, partial one (read by the state update).
-  auto write_tail = [&](int c) {
-    if (u == 0 && lane < M && a.N - c * C < C) {
-      f2(oLn + (Lay::bPowL - Lay::bLE)) = reinterpret_cast<const float2*>(x.tab + TL::oPowT)[lane];
-      f2(oLn + (Lay::bGeo - Lay::bLE)) = reinterpret_cast<const float2*>(x.tab + TL::oGeoT)[lane];
-    }
-  };
-
-  // ---- chunk inputs q, k: this wave loads 16-byte vectors n = 64u + lane + NL t of the
-  // row-major chunk matrices ([C][F]); vector n0 + NL t is row row0 + t NL/VF.  Token rows are
-  // H*F elements apart in memory, walking backwards for the reverse direction; per chunk the
-  // wave-uniform base moves, the per-lane offsets stay.  (The readout waves load v.)
-  const int n0 = 64 * u + lane;
-  const int rowF0 = n0 / VF;
-  const int sgn = a.dir ? -1 : 1;
-  int lofF[NLF];
-#pragma unroll
-  for (int t = 0; t < NLF; ++t)
-    lofF[t] = sgn * (rowF0 + t * (NL / VF)) * (a.H * F) + 8 * (n0 % VF);
-  // LDS rows row0 + t NL/VF share the swizzle of row0 (NL/VF is a multiple of 16).
-  static_assert((NL / VF) % 16 == 0, "loader rows keep the swizzle");
-  const int stF = opaque(Lay::oFk + soff<F>(rowF0, 8 * (n0 % VF)));
-  // Raw bf16 q, k of a chunk, then (convert) phi(q), phi(k) as packed bf16.
-  uint4 rq[NLF], rk[NLF];
-  auto fetch = [&](int c) {
-    const int t0 = c * C;
-    const size_t tb = x.tok_index(a, x.pos_of(a, t0));
-    const uint16_t* kb = a.k + tb * F;
-    const uint16_t* qb = a.q + tb * F;
-#pragma unroll
-    for (int t = 0; t < NLF; ++t) {
-      const int n = n0 + NL * t;
-      const bool ok = n < C * VF && t0 + rowF0 + t * (NL / VF) < a.N;
-      rk[t] = ok ? *reinterpret_cast<const uint4*>(kb + lofF[t]) : make_uint4(0, 0, 0, 0);
-      rq[t] = ok && x.want_out ? *reinterpret_cast<const uint4*>(qb + lofF[t])
-                               : make_uint4(0, 0, 0, 0);
-    }
-  };
-  // Features in place.  Rows past N get zero features (not phi(0)); their values are zero.
-  auto phi8 = [&](uint4& r, bool ok) {
-    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)   // bf16 pair -> two floats -> features -> bf16 pair
-      o[i] = pk_bf16(feature(__uint_as_float(w[i] << 16)),
-                     feature(__uint_as_float(w[i] & 0xffff0000u)));
-    r = ok ? make_uint4(o[0], o[1], o[2], o[3]) : make_uint4(0, 0, 0, 0);
-  };
-  auto convert = [&](int c) {
-    const int L = a.N - c * C;
-#pragma unroll
-    for (int t = 0; t < NLF; ++t) {
-      const bool ok = rowF0 + t * (NL / VF) < L;
-      phi8(rk[t], ok);
-      if (x.want_out) phi8(rq[t], ok);
-    }
-  };
-  auto write_inputs = [&]() {
-#pragma unroll
-    for (int t = 0; t < NLF; ++t)
-      if (n0 + NL * t < C * VF) {
-        const int so = stF + t * (NL / VF) * F;
-        *reinterpret_cast<uint4*>(s16 + so) = rk[t];
-        if (x.want_out) *reinterpret_cast<uint4*>(s16 + so + (Lay::oFq - Lay::oFk)) = rq[t];
-      }
-  };
 
   __syncthreads();  // tables visible
   if (x.c_begin < x.c_end) {
@@ -850,7 +867,6 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
       pack_state();
       write_state();
     }
-    write_tail(x.c_begin);
     write_inputs();
     if (x.c_begin + 1 < x.c_end) fetch(x.c_begin + 1);
   }
@@ -879,12 +895,14 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
         IA_STEP_FENCE();
       }
     }
+    // lam^L and the geometric sum of chunk c: the full-chunk pair, or the last chunk's
+    const int tsel = a.N - c * C < C ? Lay::kTail : 0;
 #pragma unroll
     for (int fi = 0; fi < NFT; ++fi)
       if (u + NS * fi < F / 16) {
 #pragma unroll
         for (int mt = 0; mt < MH; ++mt) {
-          const float2 p = f2(oPl + 128 * mt);
+          const float2 p = f2(oPl + tsel + 128 * mt);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float xr = accU[fi][mt][q], yi = accU[fi][mt + MH][q];
@@ -900,15 +918,16 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
         for (int mt = 0; mt < MH; ++mt)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float2 p = f2(oPg + 8 * (16 * mt + q));
+            const float2 p = f2(oPg + tsel + 8 * (16 * mt + q));
             const float xr = accG[di][mt][q], yi = accG[di][mt + MH][q];
             accG[di][mt][q] = p.x * xr - p.y * yi;
             accG[di][mt + MH][q] = p.x * yi + p.y * xr;
           }
       }
     if (u == 0 && lane < M) {
-      const float2 ge = f2(oLn + (Lay::bGeo - Lay::bLE));
-      eta = cmul(f2(oLn + (Lay::bPowL - Lay::bLE)), make_float2(eta.x + ge.x, eta.y + ge.y));
+      const float2 ge = f2(oLn + tsel + (Lay::bGeo - Lay::bLE));
+      eta = cmul(f2(oLn + tsel + (Lay::bPowL - Lay::bLE)),
+                 make_float2(eta.x + ge.x, eta.y + ge.y));
     }
     const bool more = c + 1 < x.c_end;
     __syncthreads();    // mid-chunk: phi(q), phi(k), lam U of chunk c no longer read
@@ -923,7 +942,6 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
     __syncthreads();    // chunk c read by every wave
     if (more) {
       if (x.want_out) write_state();
-      write_tail(c + 1);
       if (c + 2 < x.c_end) fetch(c + 2);
     }
     __syncthreads();
@@ -1005,7 +1023,6 @@ __device__ __forceinline__ void dispatch_role(const ChunkArgs& a, const Ctx<C, F
                                               int w, std::integer_sequence<int, Ws...>) {
   ((w == Ws ? (run_role<C, F, D, M, Ws>(a, x), 0) : 0), ...);
 }
-
 template <int C, int F, int D, int M>
 __global__ void __launch_bounds__(64 * (C / 16 + StateWaves<F, D, M>::NS))
 chunk_prefill_kernel(const ChunkArgs a) {
@@ -1026,7 +1043,6 @@ chunk_prefill_kernel(const ChunkArgs a) {
   x.sC = reinterpret_cast<float*>(smem_raw + Lay::bC);
   x.sCi = reinterpret_cast<float*>(smem_raw + Lay::bCi);
   x.sLE = reinterpret_cast<float2*>(smem_raw + Lay::bLE);
-  x.sLam = reinterpret_cast<float2*>(smem_raw + Lay::bLam);
   x.sPowL = reinterpret_cast<float2*>(smem_raw + Lay::bPowL);
   x.sGeo = reinterpret_cast<float2*>(smem_raw + Lay::bGeo);
   x.sL2lo = reinterpret_cast<float2*>(smem_raw + Lay::bL2lo);
@@ -1047,12 +1063,19 @@ chunk_prefill_kernel(const ChunkArgs a) {
   x.want_out = a.o != nullptr;
   x.tab = a.tables + (size_t)x.h * a.table_bytes;
 
-  // Per-head tables -> LDS: the decay tables (adjacent in LDS and in the table) and the two
-  // lam^(2i) factor tables (likewise adjacent).
+  x.wb_unscale = *reinterpret_cast<const float*>(x.tab + TL::oSc);
+  // Both roles run the same sequence of block barriers.  Each wave runs code specialised
+  // for its index, so trip counts and owned tiles are compile-time constants.
+  // Per-head tables -> LDS: the decay tables (adjacent in LDS and in the table), the two
+  // lam^(2i) factor tables (likewise) and the per-mode decay pairs of a full and of the last
+  // chunk.
   static_assert(Lay::oWb == Lay::oWT + 2 * M * C, "decay tables adjacent");
   static_assert(Lay::bL2hi == Lay::bL2lo + 16 * Lay::L2S * 8, "factor tables adjacent");
   static_assert(TL::nW == 2L * (Lay::oLU - Lay::oWT), "decay table size");
   static_assert(TL::nL2 == Lay::bytes - Lay::bL2lo, "factor table size");
+  static_assert(Lay::bGeoT - Lay::bGeo == Lay::kTail, "tail pair at one offset");
+  static_assert(TL::oPowT - TL::oPow == 2 * 8 * M && TL::oGeoT - TL::oGeo == 2 * 8 * M,
+                "decay pairs adjacent in the table");
   {
     const uint4* src = reinterpret_cast<const uint4*>(x.tab + TL::oW);
     uint4* dst = reinterpret_cast<uint4*>(x.sWT);
@@ -1061,15 +1084,12 @@ chunk_prefill_kernel(const ChunkArgs a) {
     uint4* dst2 = reinterpret_cast<uint4*>(x.sL2lo);
     for (int e = tid; e < (int)(TL::nL2 / 16); e += blockDim.x) dst2[e] = src2[e];
   }
-  x.wb_unscale = *reinterpret_cast<const float*>(x.tab + TL::oSc);
-  const float2* lamh = a.lam + (size_t)x.h * M;
   for (int m = tid; m < M; m += blockDim.x) {
-    x.sLam[m] = lamh[m];
     x.sPowL[m] = reinterpret_cast<const float2*>(x.tab + TL::oPow)[m];
     x.sGeo[m] = reinterpret_cast<const float2*>(x.tab + TL::oGeo)[m];
+    x.sPowL[m + 2 * M] = reinterpret_cast<const float2*>(x.tab + TL::oPowT)[m];
+    x.sGeo[m + 2 * M] = reinterpret_cast<const float2*>(x.tab + TL::oGeoT)[m];
   }
-  // Both roles run the same sequence of block barriers.  Each wave runs code specialised
-  // for its index, so trip counts and owned tiles are compile-time constants.
   dispatch_role<C, F, D, M>(
       a, x, x.wave, std::make_integer_sequence<int, C / 16 + StateWaves<F, D, M>::NS>{});
 }
