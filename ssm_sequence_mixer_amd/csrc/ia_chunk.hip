@@ -21,22 +21,25 @@ IA_EXTERN_C(64)
 #undef IA_EXTERN
 
 // ---------------------------------------------------------------- per-head tables
-// Once per call.  Block (h, run) holds one thread per (mode m, exponent j) with j in
-// [16 run, 16 run + 16); beta lam^-j is a direct complex power exp(n log lam) per thread.  Written in the
-// LDS form the prefill kernel copies verbatim: beta lam^-j in bf16 ([Re;Im] rows, j in K-slot
-// order) and in scaled fp16 (row j, modes in K-slot order), both swizzled, and beta lam^(C-j)
-// in fp32 (the state-only pass's chunk table).  Block run 0 also writes the factors
-// lam^(2i), i < 16, and lam^(32r); per mode lam^C, sum_{j<C} beta lam^-j, the same two for
-// the last chunk's length Lt, sum_{j<C} beta lam^(C-j), lam^Ls for the segment length Ls, and
-// 1/lam.
+// Once per call.  Block (h, run) holds one thread per (mode m, exponent j), m = thread % M,
+// j in [4 run, 4 run + 4): C/4 small blocks per head, so the transcendental work spreads over
+// the CUs.  Each thread takes lam to log-polar form once; every power is then
+// exp(n log|lam|) (cos n arg, sin n arg).  Written in the LDS form the prefill kernel copies
+// verbatim: beta lam^-j in bf16 ([Re;Im] rows, j in K-slot order) and in scaled fp16 (row j,
+// modes in K-slot order), both swizzled, and beta lam^(C-j) in fp32 (the state-only pass's
+// chunk table).  Blocks 0..3 also write the factors lam^(2i), i < 16, block 4 the factors
+// lam^(32r); block 0 per mode lam^C, sum_{j<C} beta lam^-j, the same two for the last
+// chunk's length Lt, sum_{j<C} beta lam^(C-j), lam^Ls for the segment length Ls, and 1/lam.
 template <int C, int M>
-__global__ void __launch_bounds__(16 * M) chunk_tables_kernel(const float2* __restrict__ lam,
+__global__ void __launch_bounds__(4 * M) chunk_tables_kernel(const float2* __restrict__ lam,
                                     const float2* __restrict__ beta, unsigned char* tables,
                                     long table_bytes, int Lt, int Ls) {
   using TL = TableLayout<C, M>;
   constexpr int M2 = 2 * M;
-  constexpr int RUNS = C / 16;
+  constexpr int JB = 4;            // exponents per block
+  constexpr int RUNS = C / 16;     // rows of lam^(32r)
   constexpr int L2S = M + 2;
+  static_assert(C / JB > 16 / JB, "a block for the lam^(32r) rows");
   const int h = blockIdx.x, run = blockIdx.y;
   unsigned char* tab = tables + (size_t)h * table_bytes;
   uint16_t* WT = reinterpret_cast<uint16_t*>(tab + TL::oW);
@@ -44,49 +47,43 @@ __global__ void __launch_bounds__(16 * M) chunk_tables_kernel(const float2* __re
   float2* L2lo = reinterpret_cast<float2*>(tab + TL::oL2);
   float2* L2hi = L2lo + 16 * L2S;
   const int m = threadIdx.x % M, jj = threadIdx.x / M;
-  const int j = 16 * run + jj;
+  const int j = JB * run + jj;
   const float2 l = lam[(size_t)h * M + m];
   const float2 bt = beta[(size_t)h * M + m];
-  // Per-mode base powers, one per thread jj < 6: lam^C, lam^-1, lam^-16, lam^(C-1), lam^Lt,
-  // lam^Ls.  Every other power below is one direct power per thread or a short product.
-  __shared__ float2 s_base[6][M];
-  __shared__ float s_max[M];
-  __shared__ float2 s_geo[16][M], s_geot[16][M];
-  if (jj < 6) {
-    const float n = jj == 0 ? (float)C : jj == 1 ? -1.f : jj == 2 ? -16.f
-                  : jj == 3 ? (float)(C - 1) : jj == 4 ? (float)Lt : (float)Ls;
-    s_base[jj][m] = cpow_f(l, n);
-  }
-  const float2 w = cmul(bt, cpow_f(l, -(float)j));   // beta lam^-j
-  __syncthreads();
+  const float lr = 0.5f * logf(l.x * l.x + l.y * l.y);   // log |lam|
+  const float th = atan2f(l.y, l.x);                      // arg lam
+  auto pw = [&](float n) {
+    const float mag = expf(n * lr);
+    float sn, cs;
+    sincosf(n * th, &sn, &cs);
+    return make_float2(mag * cs, mag * sn);
+  };
 
-  // fp16 table exponent: max_j |beta lam^-j| = |beta| |lam|^-(C-1) (|lam| <= 1); every block
-  // of the head reduces the same values in the same order, so all agree on the scale.
-  if (jj == 0) s_max[m] = hypotf(bt.x, bt.y) / hypotf(s_base[3][m].x, s_base[3][m].y);
-  __syncthreads();
-  for (int st = M / 2; st > 0; st >>= 1) {
-    if (jj == 0 && m < st) s_max[m] = fmaxf(s_max[m], s_max[m + st]);
-    __syncthreads();
-  }
-  const float wscale = pow2_scale(s_max[0]);
+  // fp16 table exponent from max_m |beta| |lam|^-(C-1) (= max_j |beta lam^-j| for |lam| <= 1),
+  // reduced over the mode lanes of every wave: all waves of all blocks of the head reduce the
+  // same values, so all agree on the scale.
+  float mx = hypotf(bt.x, bt.y) * expf(-(float)(C - 1) * lr);
+#pragma unroll
+  for (int o = 1; o < (M < 64 ? M : 64); o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  const float wscale = pow2_scale(mx);
 
-  const float2 powC = s_base[0][m];
-  reinterpret_cast<float2*>(tab + TL::oTL)[m * C + j] = cmul(powC, w);   // beta lam^(C-j)
+  const float2 w = cmul(bt, pw(-(float)j));                                          // beta lam^-j
+  reinterpret_cast<float2*>(tab + TL::oTL)[m * C + j] = cmul(bt, pw((float)(C - j)));  // beta lam^(C-j)
   WT[soff<C>(m, kpos(j))] = __builtin_bit_cast(uint16_t, (__bf16)w.x);
   WT[soff<C>(M + m, kpos(j))] = __builtin_bit_cast(uint16_t, (__bf16)w.y);
   Wb[soff<M2>(j, kpos(m))] = __builtin_bit_cast(uint16_t, (_Float16)(w.x * wscale));
   Wb[soff<M2>(j, kpos(M + m))] = __builtin_bit_cast(uint16_t, (_Float16)(w.y * wscale));
+  if (run < 16 / JB) L2lo[j * L2S + m] = pw(2.f * j);              // lam^(2i), i = j < 16
+  if (run == 16 / JB && jj < RUNS) L2hi[jj * M + m] = pw(32.f * jj);   // lam^(32r)
   if (run != 0) return;
 
-  if (threadIdx.x == 0) *reinterpret_cast<float*>(tab + TL::oSc) = 1.f / wscale;
-  L2lo[jj * L2S + m] = cpow_f(l, 2.f * jj);
-  if (jj < RUNS) L2hi[jj * M + m] = cpow_f(l, 32.f * jj);
-  // Geometric sums over j < C and j < Lt: thread jj takes j = jj + 16 i, i < C/16, as
-  // beta lam^-jj (lam^-16)^i.
+  // Block 0: geometric sums over j < C and j < Lt.  Thread jj takes j = jj + JB i, i < C/JB,
+  // as beta lam^-jj (lam^-JB)^i; the JB partial sums meet in LDS.
+  __shared__ float2 s_geo[JB][M], s_geot[JB][M];
   float2 geo = make_float2(0.f, 0.f), geot = geo, t = w;
-  const float2 step = s_base[2][m];
-  for (int i = 0; i < RUNS; ++i) {
-    const int jx = jj + 16 * i;
+  const float2 step = pw(-(float)JB);
+  for (int i = 0; i < C / JB; ++i) {
+    const int jx = jj + JB * i;
     geo.x += t.x;
     geo.y += t.y;
     if (jx < Lt) {
@@ -99,29 +96,31 @@ __global__ void __launch_bounds__(16 * M) chunk_tables_kernel(const float2* __re
   s_geot[jj][m] = geot;
   __syncthreads();
   if (jj == 0) {
-    for (int k = 1; k < 16; ++k) {
+    for (int k = 1; k < JB; ++k) {
       geo.x += s_geo[k][m].x;
       geo.y += s_geo[k][m].y;
       geot.x += s_geot[k][m].x;
       geot.y += s_geot[k][m].y;
     }
+    const float2 powC = pw((float)C);
+    if (m == 0) *reinterpret_cast<float*>(tab + TL::oSc) = 1.f / wscale;
     reinterpret_cast<float2*>(tab + TL::oGeoL)[m] = cmul(powC, geo);   // sum beta lam^(C-j)
     reinterpret_cast<float2*>(tab + TL::oPow)[m] = powC;
     reinterpret_cast<float2*>(tab + TL::oGeo)[m] = geo;
-    reinterpret_cast<float2*>(tab + TL::oPowT)[m] = s_base[4][m];
+    reinterpret_cast<float2*>(tab + TL::oPowT)[m] = pw((float)Lt);
     reinterpret_cast<float2*>(tab + TL::oGeoT)[m] = geot;
-    reinterpret_cast<float2*>(tab + TL::oPowS)[m] = s_base[5][m];
-    reinterpret_cast<float2*>(tab + TL::oInv)[m] = s_base[1][m];
+    reinterpret_cast<float2*>(tab + TL::oPowS)[m] = pw((float)Ls);
+    reinterpret_cast<float2*>(tab + TL::oInv)[m] = pw(-1.f);
   }
 }
 
 // ---------------------------------------------------------------- segment carry
-// Turns the end states of segments 0..G-2 (each from a zero state, in the state waves'
-// accumulator layout) into the states entering segments 1..G-1, in place:
+// Turns the end states of segments 0..G-2 (each from a zero state, in the slot layout) into
+// the states entering segments 1..G-1, in place:
 //   slot 0 <- lam^Ls (lam init) + slot 0,   slot g <- lam^Ls slot g-1 + slot g.
-// One thread per complex pair (Re tile, Im tile) of a lane's float4s, or per mode of lam eta;
-// segments in order.  Used when the output pass would otherwise combine many slots per
-// workgroup.
+// One thread per lane of a tile pair (4 Re, 4 Im values; a wave per pair, whose 16-lane rows
+// requantise it: SlotLayout) or per mode of lam eta; segments in order, the carried state in fp32.  Used
+// when the output pass would otherwise combine many slots per workgroup.
 template <int F, int D, int M>
 __global__ void __launch_bounds__(256)
 carry_slots_kernel(float* __restrict__ slots, const float2* __restrict__ U0,
@@ -129,7 +128,7 @@ carry_slots_kernel(float* __restrict__ slots, const float2* __restrict__ U0,
                    const float2* __restrict__ lam, const unsigned char* __restrict__ tables,
                    long table_bytes, long pows_off, int H, int nslots, long slot_floats) {
   using SL = SlotLayout<F, D, M>;
-  constexpr int NS = SL::NS, NFT = SL::NFT, NDT = SL::NDT, TM = SL::TM, MH = M / 16;
+  constexpr int NS = SL::NS, NFT = SL::NFT, NDT = SL::NDT, MH = M / 16;
   constexpr int PAIRS = NS * (NFT + NDT) * MH * 64;
   const int seq = blockIdx.y, h = seq % H;
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
@@ -169,13 +168,11 @@ carry_slots_kernel(float* __restrict__ slots, const float2* __restrict__ U0,
       ci[q] = w.y;
     }
   }
-  const size_t re_off = ((size_t)(u * SL::NT + ts * TM + mt) * 64 + lane) * 4;
-  const size_t im_off = ((size_t)(u * SL::NT + ts * TM + mt + MH) * 64 + lane) * 4;
+  const long po = SL::pair(u, ts * MH + mt, lane), so = SL::scale_of(u, ts * MH + mt, lane);
   for (int g = 0; g < nslots; ++g) {
     float* sl = base + (size_t)g * slot_floats;
-    const float4 r = *reinterpret_cast<const float4*>(sl + re_off);
-    const float4 i4 = *reinterpret_cast<const float4*>(sl + im_off);
-    const float rr[4] = {r.x, r.y, r.z, r.w}, ii[4] = {i4.x, i4.y, i4.z, i4.w};
+    float rr[4], ii[4];
+    slot_get(sl, po, so, rr, ii);
     for (int q = 0; q < 4; ++q) {
       const int m = is_u ? 16 * mt + il : 16 * mt + 4 * gq + q;
       const float2 p = pows[m];
@@ -183,8 +180,7 @@ carry_slots_kernel(float* __restrict__ slots, const float2* __restrict__ U0,
       cr[q] = p.x * xr - p.y * yi + rr[q];
       ci[q] = p.x * yi + p.y * xr + ii[q];
     }
-    *reinterpret_cast<float4*>(sl + re_off) = make_float4(cr[0], cr[1], cr[2], cr[3]);
-    *reinterpret_cast<float4*>(sl + im_off) = make_float4(ci[0], ci[1], ci[2], ci[3]);
+    slot_put(sl, po, so, lane, cr, ci);
   }
 }
 
@@ -245,7 +241,7 @@ static hipError_t launch_tables_cm(const ChunkPrefillArgs& p, long tb, hipStream
   const int Lt = p.N % C == 0 ? C : p.N % C;
   (void)hipGetLastError();
   prof_begin(st);
-  hipLaunchKernelGGL((chunk_tables_kernel<C, M>), dim3(p.H, C / 16), dim3(16 * M), 0, st,
+  hipLaunchKernelGGL((chunk_tables_kernel<C, M>), dim3(p.H, C / 4), dim3(4 * M), 0, st,
                      p.lam, p.beta, p.tables, tb, Lt, p.seg_chunks * C);
   prof_end(st, kKindTables);
   return hipGetLastError();

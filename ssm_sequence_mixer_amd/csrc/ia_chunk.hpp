@@ -182,16 +182,6 @@ __device__ __forceinline__ float xor_max16_32(float v) {
   return v;
 }
 
-// Complex power lam^n = exp(n log|lam|) (cos n arg, sin n arg), lam != 0.
-__device__ __forceinline__ float2 cpow_f(float2 lam, float n) {
-  const float lr = 0.5f * logf(lam.x * lam.x + lam.y * lam.y);
-  const float th = atan2f(lam.y, lam.x);
-  const float mag = expf(n * lr);
-  float sn, cs;
-  sincosf(n * th, &sn, &cs);
-  return make_float2(mag * cs, mag * sn);
-}
-
 // ---------------------------------------------------------------- wave roles
 // C/16 readout waves and NS state waves.  The widest shapes use 8 state waves (12 waves per
 // workgroup, 3 per SIMD) so that each state wave's share of the fp32 state plus its share of
@@ -201,18 +191,75 @@ struct StateWaves {
   static constexpr int NS = (F + D >= 256 && M >= 64) ? 8 : 4;
 };
 
-// Workspace slot of one segment's end state, in the state waves' accumulator layout: wave u,
-// tile t (f tiles then d tiles), lane l, 4 floats at ((u * NT + t) * 64 + l) * 4; lam eta
-// (complex, per mode) after the NS wave blocks.  Each lane moves 16 contiguous bytes per tile.
+// Workspace slot of one segment's end state (times lam), in the state waves' accumulator
+// layout and in fp16: for wave u and tile pair p = (tile set ts, mode tile mt) -- accumulator
+// tiles ts TM + mt (Re) and ts TM + mt + M/16 (Im), tile sets f tiles then d tiles -- lane l
+// holds 16 bytes at float offset pair(u, p, l): its 4 Re then 4 Im values times 2^s, one
+// power of two per (u, p) and 16-lane row l/16 that puts the row's largest magnitude in
+// [2^14, 2^15).  Then 2^-s per (u, p, row) (fp32) and lam eta (complex fp32, per mode).
+// fp16 halves the bytes every workgroup of a later segment reads; its relative rounding
+// (2^-11 of the row's largest value) is finer than the bf16 / scaled-fp16 operands the
+// readout forms from the state.
 template <int F, int D, int M>
 struct SlotLayout {
   static constexpr int NS = StateWaves<F, D, M>::NS;
   static constexpr int NFT = (F / 16 + NS - 1) / NS, NDT = (D / 16 + NS - 1) / NS;
-  static constexpr int TM = 2 * M / 16;
-  static constexpr int NT = (NFT + NDT) * TM;       // tiles per wave
-  static constexpr long eta = (long)NS * NT * 256;  // float offset of lam eta
+  static constexpr int TM = 2 * M / 16, MH = M / 16;
+  static constexpr int NP = (NFT + NDT) * MH;           // tile pairs per wave
+  static constexpr long scale = (long)NS * NP * 64 * 4;  // float offset of the 2^-s
+  static constexpr long eta = scale + NS * NP * 4;       // float offset of lam eta
   static constexpr long floats = eta + 2L * M;
+  static_assert(scale % 4 == 0 && eta % 4 == 0 && floats % 4 == 0, "16-byte aligned slots");
+  __device__ static long pair(int u, int p, int lane) {
+    return ((long)(u * NP + p) * 64 + lane) * 4;
+  }
+  __device__ static long scale_of(int u, int p, int lane) {
+    return scale + (u * NP + p) * 4 + (lane >> 4);
+  }
 };
+
+// Largest |value| over the 8 values of every lane of this lane's 16-lane row (all 16 active).
+__device__ __forceinline__ float row_absmax8(const float (&re)[4], const float (&im)[4]) {
+  float mx = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) mx = fmaxf(mx, fmaxf(fabsf(re[q]), fabsf(im[q])));
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+  return mx;
+}
+
+// One tile pair of a slot, written by whole 16-lane rows: pair_off = SlotLayout::pair(u, p,
+// lane), scale_off = SlotLayout::scale_of(u, p, lane).
+__device__ __forceinline__ void slot_put(float* slot, long pair_off, long scale_off, int lane,
+                                         const float (&re)[4], const float (&im)[4]) {
+  const float s = pow2_scale(row_absmax8(re, im));
+  const uint2 r = pack4_f16(re[0] * s, re[1] * s, re[2] * s, re[3] * s);
+  const uint2 i = pack4_f16(im[0] * s, im[1] * s, im[2] * s, im[3] * s);
+  *reinterpret_cast<uint4*>(slot + pair_off) = make_uint4(r.x, r.y, i.x, i.y);
+  if ((lane & 15) == 0) slot[scale_off] = 1.f / s;
+}
+
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// One tile pair of a slot, back in fp32.
+__device__ __forceinline__ void slot_get(const float* slot, long pair_off, long scale_off,
+                                         float (&re)[4], float (&im)[4]) {
+  const uint4 v = *reinterpret_cast<const uint4*>(slot + pair_off);
+  const float is = slot[scale_off];
+  re[0] = f16_lo(v.x) * is;
+  re[1] = f16_hi(v.x) * is;
+  re[2] = f16_lo(v.y) * is;
+  re[3] = f16_hi(v.y) * is;
+  im[0] = f16_lo(v.z) * is;
+  im[1] = f16_hi(v.z) * is;
+  im[2] = f16_lo(v.w) * is;
+  im[3] = f16_hi(v.w) * is;
+}
 
 // ---------------------------------------------------------------- LDS layout
 
@@ -760,11 +807,9 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
 #pragma unroll
           for (int mt = 0; mt < MH; ++mt) {
             const float2 p = pows[16 * mt + il];
-            const float4 e0 = *reinterpret_cast<const float4*>(
-                sl + ((u * SL::NT + fi * TM + mt) * 64 + lane) * 4);
-            const float4 e1 = *reinterpret_cast<const float4*>(
-                sl + ((u * SL::NT + fi * TM + mt + MH) * 64 + lane) * 4);
-            const float er[4] = {e0.x, e0.y, e0.z, e0.w}, ei[4] = {e1.x, e1.y, e1.z, e1.w};
+            float er[4], ei[4];
+            slot_get(sl, SL::pair(u, fi * MH + mt, lane), SL::scale_of(u, fi * MH + mt, lane), er,
+                     ei);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const float xr = accU[fi][mt][q], yi = accU[fi][mt + MH][q];
@@ -778,11 +823,9 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
         if (u + NS * di < TD) {
 #pragma unroll
           for (int mt = 0; mt < MH; ++mt) {
-            const float4 e0 = *reinterpret_cast<const float4*>(
-                sl + ((u * SL::NT + (NFT + di) * TM + mt) * 64 + lane) * 4);
-            const float4 e1 = *reinterpret_cast<const float4*>(
-                sl + ((u * SL::NT + (NFT + di) * TM + mt + MH) * 64 + lane) * 4);
-            const float er[4] = {e0.x, e0.y, e0.z, e0.w}, ei[4] = {e1.x, e1.y, e1.z, e1.w};
+            const int pp = (NFT + di) * MH + mt;
+            float er[4], ei[4];
+            slot_get(sl, SL::pair(u, pp, lane), SL::scale_of(u, pp, lane), er, ei);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const float2 p = pows[16 * mt + 4 * g + q];
@@ -947,30 +990,9 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
     __syncthreads();
   }
 
-  // Segment end state (times lam) into its workspace slot, in the accumulator layout.
-  if (a.seg_end) {
-    float* sl = a.seg_end + ((size_t)x.seq * a.slots_per_seq + x.seg) * a.slot_floats;
-#pragma unroll
-    for (int fi = 0; fi < NFT; ++fi)
-      if (u + NS * fi < F / 16) {
-#pragma unroll
-        for (int kt = 0; kt < TM; ++kt)
-          *reinterpret_cast<float4*>(sl + ((u * SL::NT + fi * TM + kt) * 64 + lane) * 4) =
-              make_float4(accU[fi][kt][0], accU[fi][kt][1], accU[fi][kt][2], accU[fi][kt][3]);
-      }
-#pragma unroll
-    for (int di = 0; di < NDT; ++di)
-      if (u + NS * di < TD) {
-#pragma unroll
-        for (int kt = 0; kt < TM; ++kt)
-          *reinterpret_cast<float4*>(sl + ((u * SL::NT + (NFT + di) * TM + kt) * 64 + lane) * 4) =
-              make_float4(accG[di][kt][0], accG[di][kt][1], accG[di][kt][2], accG[di][kt][3]);
-      }
-    if (u == 0 && lane < M) reinterpret_cast<float2*>(sl + SL::eta)[lane] = eta;
-  }
   // Final state (divided by lam) in the caller's layout.
   float2 *fU = nullptr, *fG = nullptr, *fE = nullptr;
-  if (!a.seg_end && x.last_seg && a.fin_U) {
+  if (x.last_seg && a.fin_U) {
     fU = a.fin_U + (size_t)x.seq * M * F;
     fG = a.fin_G + (size_t)x.seq * M * D;
     fE = a.fin_E + (size_t)x.seq * M;

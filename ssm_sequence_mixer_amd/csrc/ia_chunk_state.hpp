@@ -236,23 +236,32 @@ chunk_state_kernel(const ChunkArgs a) {
     if (i + 5 < nc) step(I0{}, I2{}, I1{}, I0{}, i + 5);
   }
 
-  // ---- end state into the segment's slot
+  // ---- end state into the segment's slot (fp16 tile pairs, see SlotLayout)
   float* sl = a.seg_end + ((size_t)seq * a.slots_per_seq + seg) * a.slot_floats;
+  constexpr int MH = M / 16;
 #pragma unroll
   for (int fi = 0; fi < NFT; ++fi)
     if (u + NS * fi < F / 16) {
 #pragma unroll
-      for (int kt = 0; kt < TM; ++kt)
-        *reinterpret_cast<float4*>(sl + ((u * SL::NT + fi * TM + kt) * 64 + lane) * 4) =
-            make_float4(accU[fi][kt][0], accU[fi][kt][1], accU[fi][kt][2], accU[fi][kt][3]);
+      for (int mt = 0; mt < MH; ++mt) {
+        const float re[4] = {accU[fi][mt][0], accU[fi][mt][1], accU[fi][mt][2], accU[fi][mt][3]};
+        const float im[4] = {accU[fi][mt + MH][0], accU[fi][mt + MH][1], accU[fi][mt + MH][2],
+                             accU[fi][mt + MH][3]};
+        slot_put(sl, SL::pair(u, fi * MH + mt, lane), SL::scale_of(u, fi * MH + mt, lane), lane,
+                 re, im);
+      }
     }
 #pragma unroll
   for (int di = 0; di < NDT; ++di)
     if (u + NS * di < TD) {
 #pragma unroll
-      for (int kt = 0; kt < TM; ++kt)
-        *reinterpret_cast<float4*>(sl + ((u * SL::NT + (NFT + di) * TM + kt) * 64 + lane) * 4) =
-            make_float4(accG[di][kt][0], accG[di][kt][1], accG[di][kt][2], accG[di][kt][3]);
+      for (int mt = 0; mt < MH; ++mt) {
+        const int pp = (NFT + di) * MH + mt;
+        const float re[4] = {accG[di][mt][0], accG[di][mt][1], accG[di][mt][2], accG[di][mt][3]};
+        const float im[4] = {accG[di][mt + MH][0], accG[di][mt + MH][1], accG[di][mt + MH][2],
+                             accG[di][mt + MH][3]};
+        slot_put(sl, SL::pair(u, pp, lane), SL::scale_of(u, pp, lane), lane, re, im);
+      }
     }
   if (u == 0 && lane < M) reinterpret_cast<float2*>(sl + SL::eta)[lane] = eta;
 }
