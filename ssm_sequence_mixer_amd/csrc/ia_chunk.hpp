@@ -346,6 +346,31 @@ struct TableLayout {
 // no index stride; offsets at or past the range read as zeros.
 constexpr int kBufferFlags = 0x00020000;
 
+// The L valid token rows of chunk c (C tokens) of sequence (b, h) in a [B][N][H][width] bf16
+// tensor as a buffer: based at the lowest-addressed valid row (row 0 walking forward, row L-1
+// walking backward), L row strides long.  Row r (walk order) column e lies at
+// row_off(r, e) - shift; rows at or past the sequence end fall outside the range (past its end
+// forward, below its base, wrapping to large offsets, backward) and read as zeros.
+template <int C>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rows(const ChunkArgs& a, int b, int h,
+                                                             const uint16_t* t, int width, int c,
+                                                             uint32_t& shift) {
+  const int L = min(C, a.N - c * C);
+  const uint32_t stride = (uint32_t)a.H * width * 2u;
+  shift = a.dir ? (uint32_t)(C - L) * stride : 0u;
+  const int pos = a.dir ? a.N - c * C - L : c * C;
+  const uint16_t* p = t + (((size_t)b * a.N + pos) * a.H + h) * width;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0,
+                                           (int)((uint32_t)L * stride), kBufferFlags);
+}
+
+// Byte offset of chunk row r (0 = the chunk's first token in walk order), column e, from the
+// lowest-addressed row of a full chunk.
+template <int C>
+__device__ __forceinline__ uint32_t row_off(const ChunkArgs& a, int width, int r, int e) {
+  return (uint32_t)((a.dir ? C - 1 - r : r) * a.H * width + e) * 2u;
+}
+
 // Per-workgroup context shared by the two wave roles.
 template <int C, int F, int D, int M>
 struct Ctx {
@@ -361,24 +386,12 @@ struct Ctx {
   __device__ size_t tok_index(const ChunkArgs& a, int pos) const {
     return ((size_t)b * a.N + pos) * a.H + h;
   }
-  // The L valid token rows of chunk c of a [B][N][H][width] bf16 tensor as a buffer: based
-  // at the lowest-addressed valid row (row 0 walking forward, row L-1 walking backward),
-  // L row strides long.  Row r (walk order) column e lies at row_off(r, e) - shift; rows at
-  // or past the sequence end fall outside the range (past its end forward, below its base,
-  // wrapping to large offsets, backward) and read as zeros.
   __device__ __amdgpu_buffer_rsrc_t chunk_rows(const ChunkArgs& a, const uint16_t* t, int width,
                                                int c, uint32_t& shift) const {
-    const int L = min(C, a.N - c * C);
-    const uint32_t stride = (uint32_t)a.H * width * 2u;
-    shift = a.dir ? (uint32_t)(C - L) * stride : 0u;
-    const uint16_t* p = t + tok_index(a, a.dir ? a.N - c * C - L : c * C) * width;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0,
-                                             (int)((uint32_t)L * stride), kBufferFlags);
+    return ia::chunk_rows<C>(a, b, h, t, width, c, shift);
   }
-  // Byte offset of chunk row r (0 = the chunk's first token in walk order), column e, from the
-  // lowest-addressed row of a full chunk.
   __device__ static uint32_t row_off(const ChunkArgs& a, int width, int r, int e) {
-    return (uint32_t)((a.dir ? C - 1 - r : r) * a.H * width + e) * 2u;
+    return ia::row_off<C>(a, width, r, e);
   }
 };
 

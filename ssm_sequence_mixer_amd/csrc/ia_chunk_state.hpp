@@ -236,32 +236,49 @@ chunk_state_kernel(const ChunkArgs a) {
     if (i + 5 < nc) step(I0{}, I2{}, I1{}, I0{}, i + 5);
   }
 
-  // ---- end state into the segment's slot (fp16 tile pairs, see SlotLayout)
+  // ---- end state into the segment's slot (fp16 tile pairs, see SlotLayout).  The row maxima
+  // of all the wave's pairs are reduced together, so their shuffles overlap.
   float* sl = a.seg_end + ((size_t)seq * a.slots_per_seq + seg) * a.slot_floats;
   constexpr int MH = M / 16;
+  constexpr int NPW = (NFT + NDT) * MH;   // tile pairs of this wave, SlotLayout order
+  auto pair_vals = [&](int p, float (&re)[4], float (&im)[4]) {
+    const int ts = p / MH, mt = p % MH;
+    const f32x4& r = ts < NFT ? accU[ts][mt] : accG[ts - NFT][mt];
+    const f32x4& m = ts < NFT ? accU[ts][mt + MH] : accG[ts - NFT][mt + MH];
 #pragma unroll
-  for (int fi = 0; fi < NFT; ++fi)
-    if (u + NS * fi < F / 16) {
-#pragma unroll
-      for (int mt = 0; mt < MH; ++mt) {
-        const float re[4] = {accU[fi][mt][0], accU[fi][mt][1], accU[fi][mt][2], accU[fi][mt][3]};
-        const float im[4] = {accU[fi][mt + MH][0], accU[fi][mt + MH][1], accU[fi][mt + MH][2],
-                             accU[fi][mt + MH][3]};
-        slot_put(sl, SL::pair(u, fi * MH + mt, lane), SL::scale_of(u, fi * MH + mt, lane), lane,
-                 re, im);
-      }
+    for (int q = 0; q < 4; ++q) {
+      re[q] = r[q];
+      im[q] = m[q];
     }
+  };
+  auto owned = [&](int p) {
+    const int ts = p / MH;
+    return ts < NFT ? u + NS * ts < F / 16 : u + NS * (ts - NFT) < TD;
+  };
+  float mx[NPW];
 #pragma unroll
-  for (int di = 0; di < NDT; ++di)
-    if (u + NS * di < TD) {
+  for (int p = 0; p < NPW; ++p) {
+    float re[4], im[4];
+    pair_vals(p, re, im);
+    float v = 0.f;
 #pragma unroll
-      for (int mt = 0; mt < MH; ++mt) {
-        const int pp = (NFT + di) * MH + mt;
-        const float re[4] = {accG[di][mt][0], accG[di][mt][1], accG[di][mt][2], accG[di][mt][3]};
-        const float im[4] = {accG[di][mt + MH][0], accG[di][mt + MH][1], accG[di][mt + MH][2],
-                             accG[di][mt + MH][3]};
-        slot_put(sl, SL::pair(u, pp, lane), SL::scale_of(u, pp, lane), lane, re, im);
-      }
+    for (int q = 0; q < 4; ++q) v = fmaxf(v, fmaxf(fabsf(re[q]), fabsf(im[q])));
+    mx[p] = v;
+  }
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+    for (int p = 0; p < NPW; ++p) mx[p] = fmaxf(mx[p], __shfl_xor(mx[p], o, 16));
+#pragma unroll
+  for (int p = 0; p < NPW; ++p)
+    if (owned(p)) {
+      float re[4], im[4];
+      pair_vals(p, re, im);
+      const float sc = pow2_scale(mx[p]);
+      const uint2 r = pack4_f16(re[0] * sc, re[1] * sc, re[2] * sc, re[3] * sc);
+      const uint2 m = pack4_f16(im[0] * sc, im[1] * sc, im[2] * sc, im[3] * sc);
+      *reinterpret_cast<uint4*>(sl + SL::pair(u, p, lane)) = make_uint4(r.x, r.y, m.x, m.y);
+      if (il == 0) sl[SL::scale_of(u, p, lane)] = 1.f / sc;
     }
   if (u == 0 && lane < M) reinterpret_cast<float2*>(sl + SL::eta)[lane] = eta;
 }
