@@ -29,7 +29,8 @@ IA_EXTERN_C(64)
 // modes in K-slot order), both swizzled, and beta lam^(C-j) in fp32 (the state-only pass's
 // chunk table).  Blocks 0..3 also write the factors lam^(2i), i < 16, block 4 the factors
 // lam^(32r); block 0 per mode lam^C, sum_{j<C} beta lam^-j, the same two for the last
-// chunk's length Lt, sum_{j<C} beta lam^(C-j), lam^Ls for the segment length Ls, and 1/lam.
+// chunk's length Lt, sum_{j<C} beta lam^(C-j), lam^Ls for the segment length Ls, and 1/lam
+// (the sums in closed form).
 template <int C, int M>
 __global__ void __launch_bounds__(4 * M) chunk_tables_kernel(const float2* __restrict__ lam,
                                     const float2* __restrict__ beta, unsigned char* tables,
@@ -77,40 +78,40 @@ __global__ void __launch_bounds__(4 * M) chunk_tables_kernel(const float2* __res
   if (run == 16 / JB && jj < RUNS) L2hi[jj * M + m] = pw(32.f * jj);   // lam^(32r)
   if (run != 0) return;
 
-  // Block 0: geometric sums over j < C and j < Lt.  Thread jj takes j = jj + JB i, i < C/JB,
-  // as beta lam^-jj (lam^-JB)^i; the JB partial sums meet in LDS.
-  __shared__ float2 s_geo[JB][M], s_geot[JB][M];
-  float2 geo = make_float2(0.f, 0.f), geot = geo, t = w;
-  const float2 step = pw(-(float)JB);
-  for (int i = 0; i < C / JB; ++i) {
-    const int jx = jj + JB * i;
-    geo.x += t.x;
-    geo.y += t.y;
-    if (jx < Lt) {
-      geot.x += t.x;
-      geot.y += t.y;
-    }
-    t = cmul(t, step);
-  }
-  s_geo[jj][m] = geo;
-  s_geot[jj][m] = geot;
-  __syncthreads();
+  // Block 0, the four threads of a mode split the rest: the geometric sums over j < n (n = C, Lt) in closed form,
+  // sum_{j<n} lam^-j = (lam^-n - 1) / (lam^-1 - 1), numerator and denominator as expm1 of
+  // -n log lam and -log lam (no cancellation for lam near 1); lam = 1 gives n.
+  auto cexpm1 = [&](float n) {   // exp(-n log lam) - 1
+    const float ar = -n * lr, ai = -n * th;
+    const float e = expm1f(ar);
+    float sn, cs, sh, ch;
+    sincosf(ai, &sn, &cs);
+    sincosf(0.5f * ai, &sh, &ch);
+    return make_float2(e * cs - 2.f * sh * sh, (1.f + e) * sn);   // cos - 1 = -2 sin^2(x/2)
+  };
+  auto geo_sum = [&](float n) {
+    const float2 den = cexpm1(1.f);
+    const float dd = den.x * den.x + den.y * den.y;
+    if (!(dd > 0.f)) return make_float2(n * bt.x, n * bt.y);
+    const float2 num = cexpm1(n);
+    const float2 r = make_float2((num.x * den.x + num.y * den.y) / dd,
+                                 (num.y * den.x - num.x * den.y) / dd);
+    return cmul(bt, r);
+  };
+  float2* const out = reinterpret_cast<float2*>(tab);
   if (jj == 0) {
-    for (int k = 1; k < JB; ++k) {
-      geo.x += s_geo[k][m].x;
-      geo.y += s_geo[k][m].y;
-      geot.x += s_geot[k][m].x;
-      geot.y += s_geot[k][m].y;
-    }
-    const float2 powC = pw((float)C);
+    const float2 geo = geo_sum((float)C);
+    out[TL::oGeo / 8 + m] = geo;
+    out[TL::oGeoL / 8 + m] = cmul(pw((float)C), geo);   // sum beta lam^(C-j)
+  } else if (jj == 1) {
+    out[TL::oGeoT / 8 + m] = geo_sum((float)Lt);
+  } else if (jj == 2) {
+    out[TL::oPow / 8 + m] = pw((float)C);
+    out[TL::oPowT / 8 + m] = pw((float)Lt);
+  } else {
+    out[TL::oPowS / 8 + m] = pw((float)Ls);
+    out[TL::oInv / 8 + m] = pw(-1.f);
     if (m == 0) *reinterpret_cast<float*>(tab + TL::oSc) = 1.f / wscale;
-    reinterpret_cast<float2*>(tab + TL::oGeoL)[m] = cmul(powC, geo);   // sum beta lam^(C-j)
-    reinterpret_cast<float2*>(tab + TL::oPow)[m] = powC;
-    reinterpret_cast<float2*>(tab + TL::oGeo)[m] = geo;
-    reinterpret_cast<float2*>(tab + TL::oPowT)[m] = pw((float)Lt);
-    reinterpret_cast<float2*>(tab + TL::oGeoT)[m] = geot;
-    reinterpret_cast<float2*>(tab + TL::oPowS)[m] = pw((float)Ls);
-    reinterpret_cast<float2*>(tab + TL::oInv)[m] = pw(-1.f);
   }
 }
 
