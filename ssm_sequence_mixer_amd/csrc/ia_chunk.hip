@@ -138,14 +138,25 @@ carry_slots_kernel(float* __restrict__ slots, const float2* __restrict__ U0,
   const float2* lamh = lam + (size_t)h * M;
   const float2* pows =
       reinterpret_cast<const float2*>(tables + (size_t)h * table_bytes + pows_off);
+  // Slots are loaded KB at a time ahead of their combination, so the loads of a batch are in
+  // flight together instead of one round trip per slot.
+  constexpr int KB = 8;
   if (e >= PAIRS) {   // lam eta, mode m
     const int m = e - PAIRS;
     const float2 p = pows[m];
     float2 c = E0 ? cmul(lamh[m], E0[(size_t)seq * M + m]) : make_float2(0.f, 0.f);
-    for (int g = 0; g < nslots; ++g) {
-      float2* sl = reinterpret_cast<float2*>(base + (size_t)g * slot_floats + SL::eta) + m;
-      c = cfma(p, c, *sl);
-      *sl = c;
+    for (int g0 = 0; g0 < nslots; g0 += KB) {
+      float2 x[KB];
+#pragma unroll
+      for (int k = 0; k < KB; ++k)
+        if (g0 + k < nslots)
+          x[k] = reinterpret_cast<const float2*>(base + (size_t)(g0 + k) * slot_floats + SL::eta)[m];
+#pragma unroll
+      for (int k = 0; k < KB; ++k)
+        if (g0 + k < nslots) {
+          c = cfma(p, c, x[k]);
+          reinterpret_cast<float2*>(base + (size_t)(g0 + k) * slot_floats + SL::eta)[m] = c;
+        }
     }
     return;
   }
@@ -170,18 +181,52 @@ carry_slots_kernel(float* __restrict__ slots, const float2* __restrict__ U0,
     }
   }
   const long po = SL::pair(u, ts * MH + mt, lane), so = SL::scale_of(u, ts * MH + mt, lane);
-  for (int g = 0; g < nslots; ++g) {
-    float* sl = base + (size_t)g * slot_floats;
-    float rr[4], ii[4];
-    slot_get(sl, po, so, rr, ii);
-    for (int q = 0; q < 4; ++q) {
-      const int m = is_u ? 16 * mt + il : 16 * mt + 4 * gq + q;
-      const float2 p = pows[m];
-      const float xr = cr[q], yi = ci[q];
-      cr[q] = p.x * xr - p.y * yi + rr[q];
-      ci[q] = p.x * yi + p.y * xr + ii[q];
+  float2 pq[4];
+  for (int q = 0; q < 4; ++q) pq[q] = pows[is_u ? 16 * mt + il : 16 * mt + 4 * gq + q];
+  for (int g0 = 0; g0 < nslots; g0 += KB) {
+    uint4 v[KB];
+    float is[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k)
+      if (g0 + k < nslots) {
+        const float* sl = base + (size_t)(g0 + k) * slot_floats;
+        v[k] = *reinterpret_cast<const uint4*>(sl + po);
+        is[k] = sl[so];
+      }
+    // Carried states of the batch in fp32, then their row maxima reduced together (the
+    // shuffles overlap), then each quantised to its slot.
+    float vr[KB][4], vi[KB][4], mx[KB];
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      mx[k] = 0.f;
+      if (g0 + k < nslots) {   // uniform over the wave
+        float rr[4], ii[4];
+        slot_unpack(v[k], is[k], rr, ii);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float xr = cr[q], yi = ci[q];
+          cr[q] = pq[q].x * xr - pq[q].y * yi + rr[q];
+          ci[q] = pq[q].x * yi + pq[q].y * xr + ii[q];
+          vr[k][q] = cr[q];
+          vi[k][q] = ci[q];
+          mx[k] = fmaxf(mx[k], fmaxf(fabsf(cr[q]), fabsf(ci[q])));
+        }
+      }
     }
-    slot_put(sl, po, so, lane, cr, ci);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+      for (int k = 0; k < KB; ++k) mx[k] = fmaxf(mx[k], __shfl_xor(mx[k], o, 16));
+#pragma unroll
+    for (int k = 0; k < KB; ++k)
+      if (g0 + k < nslots) {
+        float* sl = base + (size_t)(g0 + k) * slot_floats;
+        const float sc = pow2_scale(mx[k]);
+        const uint2 r = pack4_f16(vr[k][0] * sc, vr[k][1] * sc, vr[k][2] * sc, vr[k][3] * sc);
+        const uint2 i = pack4_f16(vi[k][0] * sc, vi[k][1] * sc, vi[k][2] * sc, vi[k][3] * sc);
+        *reinterpret_cast<uint4*>(sl + po) = make_uint4(r.x, r.y, i.x, i.y);
+        if (il == 0) sl[so] = 1.f / sc;
+      }
   }
 }
 

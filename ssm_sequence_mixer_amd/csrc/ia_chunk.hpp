@@ -246,11 +246,8 @@ __device__ __forceinline__ float f16_hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
-// One tile pair of a slot, back in fp32.
-__device__ __forceinline__ void slot_get(const float* slot, long pair_off, long scale_off,
-                                         float (&re)[4], float (&im)[4]) {
-  const uint4 v = *reinterpret_cast<const uint4*>(slot + pair_off);
-  const float is = slot[scale_off];
+// One tile pair of a slot (its 16 bytes v and inverse scale is), back in fp32.
+__device__ __forceinline__ void slot_unpack(uint4 v, float is, float (&re)[4], float (&im)[4]) {
   re[0] = f16_lo(v.x) * is;
   re[1] = f16_hi(v.x) * is;
   re[2] = f16_lo(v.y) * is;
@@ -259,6 +256,12 @@ __device__ __forceinline__ void slot_get(const float* slot, long pair_off, long 
   im[1] = f16_hi(v.z) * is;
   im[2] = f16_lo(v.w) * is;
   im[3] = f16_hi(v.w) * is;
+}
+
+// One tile pair of a slot, back in fp32.
+__device__ __forceinline__ void slot_get(const float* slot, long pair_off, long scale_off,
+                                         float (&re)[4], float (&im)[4]) {
+  slot_unpack(*reinterpret_cast<const uint4*>(slot + pair_off), slot[scale_off], re, im);
 }
 
 // ---------------------------------------------------------------- LDS layout
