@@ -189,3 +189,37 @@ def test_decode_1p3b_shape(Bd):
         err = rowrel(host(o), o_ref)
         report(f"decode 1.3b B={Bd} step {t}", err)
         assert err < TOL_BF16
+
+
+@pytest.mark.parametrize("shape", [(64, 32, 16), (16, 240, 48), (128, 64, 128), (256, 256, 128)])
+def test_bf16_token_sequential_shapes(shape):
+    """bf16 inputs on shapes the chunked kernels do not take (F != Dv, widths 240/256, M=128;
+    256/256/128 is the largest the library accepts): prefill through the token-sequential
+    kernel, then two decode steps (the mode-looping kernel), outputs and state.  The inputs
+    are bf16-exact, so the oracle sees the same values and fp32 arithmetic sets the bar."""
+    torch = _torch()
+    ia = _lib()
+    F, D, M = shape
+    B, H, N = 2, 2, 37
+    inp = W.make_inputs(B, H, N + 2, F, D, M, dtype="bf16", seed=F + 3 * D + 7 * M)
+    lam, beta = inp["lam"], inp["beta"]
+    q, k, v = (inp[n] for n in "qkv")
+    bf = torch.bfloat16
+    tag(f"bf16 token-sequential prefill F={F} D={D} M={M}")
+    st = ia.new_state(B, H, M, F, D)
+    o = ia.prefill(dev(q[:, :N], bf), dev(k[:, :N], bf), dev(v[:, :N], bf), dev(lam), dev(beta),
+                   state=st, out_dtype=torch.float32)
+    o_ref, _, _, st_ref = oracle.prefill(q[:, :N], k[:, :N], v[:, :N], lam, beta)
+    torch.cuda.synchronize()
+    err = rowrel(host(o), o_ref)
+    report(f"bf16 token-sequential F={F} D={D} M={M} output", err)
+    assert err < TOL_F32
+    assert state_rel(tuple(host(s) for s in st), st_ref) < TOL_F32
+    st_ref = tuple(host(s) for s in st)   # both sides continue from the complex64 state
+    for t in range(N, N + 2):
+        tag(f"decode F={F} D={D} M={M} step {t - N}")
+        o = ia.decode(dev(q[:, t], bf), dev(k[:, t], bf), dev(v[:, t], bf), dev(lam), dev(beta), st)
+        o_ref, st_ref = oracle.decode_step(q[:, t], k[:, t], v[:, t], lam, beta, st_ref)
+        torch.cuda.synchronize()
+        assert rowrel(host(o), o_ref) < TOL_F32
+        assert state_rel(tuple(host(s) for s in st), st_ref) < TOL_F32
