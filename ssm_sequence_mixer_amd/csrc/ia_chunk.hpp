@@ -287,8 +287,9 @@ struct Layout {
   static constexpr int bPowT = bGeo + M * 8;       // [M]  float2 lam^Lt, last (partial) chunk
   static constexpr int bGeoT = bPowT + M * 8;      // [M]  float2 sum_{j<Lt} beta lam^-j
   static constexpr int kTail = bPowT - bPowL;      // offset of the last chunk's pair
+  static constexpr int bPowS = bGeoT + M * 8;      // [M]  float2 lam^Ls, segment length Ls
   static constexpr int L2S = M + 2;                // row stride of the lam^(2i) factor table
-  static constexpr int bL2lo = bGeoT + M * 8;      // [16][L2S] float2 lam^(2i), i = 0..15
+  static constexpr int bL2lo = bPowS + M * 8;      // [16][L2S] float2 lam^(2i), i = 0..15
   static constexpr int bL2hi = bL2lo + 16 * L2S * 8;  // [NR][M] float2 lam^(32r)
   static constexpr int bytes = bL2hi + NR * M * 8;
 };
@@ -811,49 +812,67 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
     }
     if (u == 0 && lane < M) eta = cmul(lamh[lane], iE[lane]);
   }
+  __syncthreads();  // tables visible (the Horner step reads lam^Ls from LDS)
   if (a.seg_prev && x.seg > 0) {
-    const float2* pows = reinterpret_cast<const float2*>(x.tab + TL::oPowS);
     // Horner over the earlier segments; an inclusive slot is the state itself (zero state
-    // times lam^Ls plus the slot).
+    // times lam^Ls plus the slot).  lam^Ls comes from LDS, so a slot's loads can all be in
+    // flight before any of it is combined.
+    constexpr int dS = Lay::bPowS - Lay::bPowL;   // lam^Ls beside lam^C (oPl, oPg offsets)
     for (int sp = a.seg_inclusive ? x.seg - 1 : 0; sp < x.seg; ++sp) {
       const float* sl = a.seg_prev + ((size_t)x.seq * a.slots_per_seq + sp) * a.slot_floats;
+      float2 e = make_float2(0.f, 0.f);
+      if (u == 0 && lane < M) e = reinterpret_cast<const float2*>(sl + SL::eta)[lane];
+      // lam U tile pairs: this wave's MH pairs loaded together, then combined
 #pragma unroll
       for (int fi = 0; fi < NFT; ++fi)
         if (u + NS * fi < F / 16) {
+          uint4 v[MH];
+          float is[MH];
 #pragma unroll
           for (int mt = 0; mt < MH; ++mt) {
-            const float2 p = pows[16 * mt + il];
+            v[mt] = *reinterpret_cast<const uint4*>(sl + SL::pair(u, fi * MH + mt, lane));
+            is[mt] = sl[SL::scale_of(u, fi * MH + mt, lane)];
+          }
+#pragma unroll
+          for (int mt = 0; mt < MH; ++mt) {
+            const float2 pw = f2(oPl + dS + 128 * mt);
             float er[4], ei[4];
-            slot_get(sl, SL::pair(u, fi * MH + mt, lane), SL::scale_of(u, fi * MH + mt, lane), er,
-                     ei);
+            slot_unpack(v[mt], is[mt], er, ei);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const float xr = accU[fi][mt][q], yi = accU[fi][mt + MH][q];
-              accU[fi][mt][q] = p.x * xr - p.y * yi + er[q];
-              accU[fi][mt + MH][q] = p.x * yi + p.y * xr + ei[q];
+              accU[fi][mt][q] = pw.x * xr - pw.y * yi + er[q];
+              accU[fi][mt + MH][q] = pw.x * yi + pw.y * xr + ei[q];
             }
           }
         }
+      // lam G tile pairs likewise
 #pragma unroll
       for (int di = 0; di < NDT; ++di)
         if (u + NS * di < TD) {
+          uint4 v[MH];
+          float is[MH];
 #pragma unroll
           for (int mt = 0; mt < MH; ++mt) {
             const int pp = (NFT + di) * MH + mt;
+            v[mt] = *reinterpret_cast<const uint4*>(sl + SL::pair(u, pp, lane));
+            is[mt] = sl[SL::scale_of(u, pp, lane)];
+          }
+#pragma unroll
+          for (int mt = 0; mt < MH; ++mt) {
             float er[4], ei[4];
-            slot_get(sl, SL::pair(u, pp, lane), SL::scale_of(u, pp, lane), er, ei);
+            slot_unpack(v[mt], is[mt], er, ei);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const float2 p = pows[16 * mt + 4 * g + q];
+              const float2 pw = f2(oPg + dS + 8 * (16 * mt + q));
               const float xr = accG[di][mt][q], yi = accG[di][mt + MH][q];
-              accG[di][mt][q] = p.x * xr - p.y * yi + er[q];
-              accG[di][mt + MH][q] = p.x * yi + p.y * xr + ei[q];
+              accG[di][mt][q] = pw.x * xr - pw.y * yi + er[q];
+              accG[di][mt + MH][q] = pw.x * yi + pw.y * xr + ei[q];
             }
           }
         }
       if (u == 0 && lane < M) {
-        const float2 e = reinterpret_cast<const float2*>(sl + SL::eta)[lane];
-        eta = cmul(pows[lane], eta);
+        eta = cmul(f2(oLn + (Lay::bPowS - Lay::bLE)), eta);
         eta.x += e.x;
         eta.y += e.y;
       }
@@ -917,7 +936,6 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
     if (u == 0 && lane < M) f2(oLn) = eta;
   };
 
-  __syncthreads();  // tables visible
   if (x.c_begin < x.c_end) {
     fetch(x.c_begin);
     convert(x.c_begin);
@@ -1112,6 +1130,7 @@ chunk_prefill_kernel(const ChunkArgs a) {
   static_assert(TL::nW == 2L * (Lay::oLU - Lay::oWT), "decay table size");
   static_assert(TL::nL2 == Lay::bytes - Lay::bL2lo, "factor table size");
   static_assert(Lay::bGeoT - Lay::bGeo == Lay::kTail, "tail pair at one offset");
+  static_assert(Lay::bPowS == Lay::bPowL + 4 * 8 * M, "lam^Ls after the decay pairs");
   static_assert(TL::oPowT - TL::oPow == 2 * 8 * M && TL::oGeoT - TL::oGeo == 2 * 8 * M,
                 "decay pairs adjacent in the table");
   {
@@ -1127,6 +1146,7 @@ chunk_prefill_kernel(const ChunkArgs a) {
     x.sGeo[m] = reinterpret_cast<const float2*>(x.tab + TL::oGeo)[m];
     x.sPowL[m + 2 * M] = reinterpret_cast<const float2*>(x.tab + TL::oPowT)[m];
     x.sGeo[m + 2 * M] = reinterpret_cast<const float2*>(x.tab + TL::oGeoT)[m];
+    x.sPowL[m + 4 * M] = reinterpret_cast<const float2*>(x.tab + TL::oPowS)[m];
   }
   dispatch_role<C, F, D, M>(
       a, x, x.wave, std::make_integer_sequence<int, C / 16 + StateWaves<F, D, M>::NS>{});
