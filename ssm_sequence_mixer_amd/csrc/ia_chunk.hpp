@@ -406,6 +406,26 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// n16 16-byte vectors from global memory straight into LDS (no registers), spread over the
+// waves in blocks of 64: lane l of block b moves vector 64 b + l.  Completion is
+// counted with the wave's vector-memory loads (vmcnt), which complete in issue order.
+__device__ __forceinline__ void lds_dma(const unsigned char* src, unsigned char* dst, int n16,
+                                        int wave, int lane, int nwaves) {
+  for (int b = wave; 64 * b < n16; b += nwaves) {
+    const int e = 64 * b + lane;
+    if (e < n16)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(src + 16 * (size_t)e),
+          (__attribute__((address_space(3))) void*)(dst + 1024 * b), 16, 0, 0);
+  }
+}
+
+// Wait until none of this wave's vector-memory loads, LDS DMA included, is outstanding
+// (vmcnt 0; expcnt and lgkmcnt left at their maxima, i.e. not waited on).
+__device__ __forceinline__ void wait_vm_zero() {
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+}
+
 // ---------------------------------------------------------------- readout waves
 // Wave R owns queries [16R, 16R+16) of every chunk.
 template <int C, int F, int D, int M, int R>
@@ -468,6 +488,9 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
     for (int t = 0; t < NV; ++t) *reinterpret_cast<uint4*>(x.s16 + stV[t]) = rv[t];
   };
 
+  // The first chunk's v loads go out before the barrier and land while the state waves copy
+  // the tables.
+  if (x.c_begin < x.c_end) fetch_v(x.c_begin);
   __syncthreads();  // tables visible
   // lam^(2i) for this lane's queries i = 16r + il and modes m = 16mt + 4g + q, for the whole
   // segment: the product of the two factor tables, formed once.
@@ -482,7 +505,6 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
                                                         8 * r * M + mo));
     }
   if (x.c_begin < x.c_end) {
-    fetch_v(x.c_begin);
     write_v();
     if (x.c_begin + 1 < x.c_end) fetch_v(x.c_begin + 1);
   }
@@ -812,6 +834,15 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
     }
     if (u == 0 && lane < M) eta = cmul(lamh[lane], iE[lane]);
   }
+  // The state waves copy the tables straight into LDS, so the readout waves carry no pending
+  // LDS-DMA writes and their first chunk's loads stay in flight across the barrier.
+  {
+    unsigned char* const sb = reinterpret_cast<unsigned char*>(x.s16);
+    lds_dma(x.tab + TL::oW, sb + 2 * Lay::oWT, (int)(TL::nW / 16), u, lane, NS);
+    lds_dma(x.tab + TL::oL2, sb + Lay::bL2lo, (int)(TL::nL2 / 16), u, lane, NS);
+    lds_dma(x.tab + TL::oPow, sb + Lay::bPowL, 40 * M / 16, (u + 1) % NS, lane, NS);
+  }
+  wait_vm_zero();
   __syncthreads();  // tables visible (the Horner step reads lam^Ls from LDS)
   if (a.seg_prev && x.seg > 0) {
     // Horner over the earlier segments; an inclusive slot is the state itself (zero state
@@ -1122,9 +1153,10 @@ chunk_prefill_kernel(const ChunkArgs a) {
   x.wb_unscale = *reinterpret_cast<const float*>(x.tab + TL::oSc);
   // Both roles run the same sequence of block barriers.  Each wave runs code specialised
   // for its index, so trip counts and owned tiles are compile-time constants.
-  // Per-head tables -> LDS: the decay tables (adjacent in LDS and in the table), the two
-  // lam^(2i) factor tables (likewise) and the per-mode decay pairs of a full and of the last
-  // chunk.
+  // The state waves copy the per-head tables to LDS as three contiguous runs: the decay
+  // tables, the two lam^(2i) factor tables, and the per-mode pairs (decay and geometric sum of
+  // a full and of the last chunk, then lam^Ls).  The layouts below make each run contiguous
+  // on both sides.
   static_assert(Lay::oWb == Lay::oWT + 2 * M * C, "decay tables adjacent");
   static_assert(Lay::bL2hi == Lay::bL2lo + 16 * Lay::L2S * 8, "factor tables adjacent");
   static_assert(TL::nW == 2L * (Lay::oLU - Lay::oWT), "decay table size");
@@ -1133,21 +1165,14 @@ chunk_prefill_kernel(const ChunkArgs a) {
   static_assert(Lay::bPowS == Lay::bPowL + 4 * 8 * M, "lam^Ls after the decay pairs");
   static_assert(TL::oPowT - TL::oPow == 2 * 8 * M && TL::oGeoT - TL::oGeo == 2 * 8 * M,
                 "decay pairs adjacent in the table");
-  {
-    const uint4* src = reinterpret_cast<const uint4*>(x.tab + TL::oW);
-    uint4* dst = reinterpret_cast<uint4*>(x.sWT);
-    for (int e = tid; e < (int)(TL::nW / 16); e += blockDim.x) dst[e] = src[e];
-    const uint4* src2 = reinterpret_cast<const uint4*>(x.tab + TL::oL2);
-    uint4* dst2 = reinterpret_cast<uint4*>(x.sL2lo);
-    for (int e = tid; e < (int)(TL::nL2 / 16); e += blockDim.x) dst2[e] = src2[e];
-  }
-  for (int m = tid; m < M; m += blockDim.x) {
-    x.sPowL[m] = reinterpret_cast<const float2*>(x.tab + TL::oPow)[m];
-    x.sGeo[m] = reinterpret_cast<const float2*>(x.tab + TL::oGeo)[m];
-    x.sPowL[m + 2 * M] = reinterpret_cast<const float2*>(x.tab + TL::oPowT)[m];
-    x.sGeo[m + 2 * M] = reinterpret_cast<const float2*>(x.tab + TL::oGeoT)[m];
-    x.sPowL[m + 4 * M] = reinterpret_cast<const float2*>(x.tab + TL::oPowS)[m];
-  }
+  static_assert(Lay::bGeo == Lay::bPowL + 8 * M && Lay::bPowT == Lay::bGeo + 8 * M &&
+                Lay::bGeoT == Lay::bPowT + 8 * M && Lay::bPowS == Lay::bGeoT + 8 * M,
+                "per-mode arrays adjacent in LDS");
+  static_assert(TL::oGeo == TL::oPow + 8 * M && TL::oPowT == TL::oGeo + 8 * M &&
+                TL::oGeoT == TL::oPowT + 8 * M && TL::oPowS == TL::oGeoT + 8 * M,
+                "per-mode arrays adjacent in the table");
+  static_assert((Lay::oWT * 2) % 16 == 0 && Lay::bL2lo % 16 == 0 && Lay::bPowL % 16 == 0 &&
+                TL::nW % 16 == 0 && TL::nL2 % 16 == 0 && (40 * M) % 16 == 0, "16-byte copies");
   dispatch_role<C, F, D, M>(
       a, x, x.wave, std::make_integer_sequence<int, C / 16 + StateWaves<F, D, M>::NS>{});
 }
