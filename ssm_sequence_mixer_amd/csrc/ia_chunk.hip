@@ -2,6 +2,7 @@
 // kernel instantiations (which live in ia_chunk_f*.hip).
 #include "ia_chunk.hpp"
 #include "ia_chunk_state.hpp"
+#include "ia_tables.hpp"
 
 namespace ia {
 
@@ -21,98 +22,13 @@ IA_EXTERN_C(64)
 #undef IA_EXTERN
 
 // ---------------------------------------------------------------- per-head tables
-// Once per call.  Block (h, run) holds one thread per (mode m, exponent j), m = thread % M,
-// j in [4 run, 4 run + 4): C/4 small blocks per head, so the transcendental work spreads over
-// the CUs.  Each thread takes lam to log-polar form once; every power is then
-// exp(n log|lam|) (cos n arg, sin n arg).  Written in the LDS form the prefill kernel copies
-// verbatim: beta lam^-j in bf16 ([Re;Im] rows, j in K-slot order) and in scaled fp16 (row j,
-// modes in K-slot order), both swizzled, and beta lam^(C-j) in fp32 (the state-only pass's
-// chunk table).  Blocks 0..3 also write the factors lam^(2i), i < 16, block 4 the factors
-// lam^(32r); block 0 per mode lam^C, sum_{j<C} beta lam^-j, the same two for the last
-// chunk's length Lt, sum_{j<C} beta lam^(C-j), lam^Ls for the segment length Ls, and 1/lam
-// (the sums in closed form).
+// Once per call, when no state-only pass carries them: block (h, run) is one table run
+// (table_run), C/4 small blocks per head, so the transcendental work spreads over the CUs.
 template <int C, int M>
 __global__ void __launch_bounds__(4 * M) chunk_tables_kernel(const float2* __restrict__ lam,
                                     const float2* __restrict__ beta, unsigned char* tables,
                                     long table_bytes, int Lt, int Ls) {
-  using TL = TableLayout<C, M>;
-  constexpr int M2 = 2 * M;
-  constexpr int JB = 4;            // exponents per block
-  constexpr int RUNS = C / 16;     // rows of lam^(32r)
-  constexpr int L2S = M + 2;
-  static_assert(C / JB > 16 / JB, "a block for the lam^(32r) rows");
-  const int h = blockIdx.x, run = blockIdx.y;
-  unsigned char* tab = tables + (size_t)h * table_bytes;
-  uint16_t* WT = reinterpret_cast<uint16_t*>(tab + TL::oW);
-  uint16_t* Wb = WT + M2 * C;
-  float2* L2lo = reinterpret_cast<float2*>(tab + TL::oL2);
-  float2* L2hi = L2lo + 16 * L2S;
-  const int m = threadIdx.x % M, jj = threadIdx.x / M;
-  const int j = JB * run + jj;
-  const float2 l = lam[(size_t)h * M + m];
-  const float2 bt = beta[(size_t)h * M + m];
-  const float lr = 0.5f * logf(l.x * l.x + l.y * l.y);   // log |lam|
-  const float th = atan2f(l.y, l.x);                      // arg lam
-  auto pw = [&](float n) {
-    const float mag = expf(n * lr);
-    float sn, cs;
-    sincosf(n * th, &sn, &cs);
-    return make_float2(mag * cs, mag * sn);
-  };
-
-  // fp16 table exponent from max_m |beta| |lam|^-(C-1) (= max_j |beta lam^-j| for |lam| <= 1),
-  // reduced over the mode lanes of every wave: all waves of all blocks of the head reduce the
-  // same values, so all agree on the scale.
-  float mx = hypotf(bt.x, bt.y) * expf(-(float)(C - 1) * lr);
-#pragma unroll
-  for (int o = 1; o < (M < 64 ? M : 64); o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  const float wscale = pow2_scale(mx);
-
-  const float2 w = cmul(bt, pw(-(float)j));                                          // beta lam^-j
-  reinterpret_cast<float2*>(tab + TL::oTL)[m * C + j] = cmul(bt, pw((float)(C - j)));  // beta lam^(C-j)
-  WT[soff<C>(m, kpos(j))] = __builtin_bit_cast(uint16_t, (__bf16)w.x);
-  WT[soff<C>(M + m, kpos(j))] = __builtin_bit_cast(uint16_t, (__bf16)w.y);
-  Wb[soff<M2>(j, kpos(m))] = __builtin_bit_cast(uint16_t, (_Float16)(w.x * wscale));
-  Wb[soff<M2>(j, kpos(M + m))] = __builtin_bit_cast(uint16_t, (_Float16)(w.y * wscale));
-  if (run < 16 / JB) L2lo[j * L2S + m] = pw(2.f * j);              // lam^(2i), i = j < 16
-  if (run == 16 / JB && jj < RUNS) L2hi[jj * M + m] = pw(32.f * jj);   // lam^(32r)
-  if (run != 0) return;
-
-  // Block 0, the four threads of a mode split the rest: the geometric sums over j < n (n = C, Lt) in closed form,
-  // sum_{j<n} lam^-j = (lam^-n - 1) / (lam^-1 - 1), numerator and denominator as expm1 of
-  // -n log lam and -log lam (no cancellation for lam near 1); lam = 1 gives n.
-  auto cexpm1 = [&](float n) {   // exp(-n log lam) - 1
-    const float ar = -n * lr, ai = -n * th;
-    const float e = expm1f(ar);
-    float sn, cs, sh, ch;
-    sincosf(ai, &sn, &cs);
-    sincosf(0.5f * ai, &sh, &ch);
-    return make_float2(e * cs - 2.f * sh * sh, (1.f + e) * sn);   // cos - 1 = -2 sin^2(x/2)
-  };
-  auto geo_sum = [&](float n) {
-    const float2 den = cexpm1(1.f);
-    const float dd = den.x * den.x + den.y * den.y;
-    if (!(dd > 0.f)) return make_float2(n * bt.x, n * bt.y);
-    const float2 num = cexpm1(n);
-    const float2 r = make_float2((num.x * den.x + num.y * den.y) / dd,
-                                 (num.y * den.x - num.x * den.y) / dd);
-    return cmul(bt, r);
-  };
-  float2* const out = reinterpret_cast<float2*>(tab);
-  if (jj == 0) {
-    const float2 geo = geo_sum((float)C);
-    out[TL::oGeo / 8 + m] = geo;
-    out[TL::oGeoL / 8 + m] = cmul(pw((float)C), geo);   // sum beta lam^(C-j)
-  } else if (jj == 1) {
-    out[TL::oGeoT / 8 + m] = geo_sum((float)Lt);
-  } else if (jj == 2) {
-    out[TL::oPow / 8 + m] = pw((float)C);
-    out[TL::oPowT / 8 + m] = pw((float)Lt);
-  } else {
-    out[TL::oPowS / 8 + m] = pw((float)Ls);
-    out[TL::oInv / 8 + m] = pw(-1.f);
-    if (m == 0) *reinterpret_cast<float*>(tab + TL::oSc) = 1.f / wscale;
-  }
+  table_run<C, M>(lam, beta, tables, table_bytes, Lt, Ls, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
 // ---------------------------------------------------------------- segment carry
@@ -360,7 +276,10 @@ constexpr int kHornerSlots = 3;
 
 // Full chunked prefill for one direction: tables; the end states of segments 0..G-2 from a
 // zero state; every segment (or, state only, the last) from its initial state, which each
-// workgroup assembles from the caller's state and the earlier segments' end states.
+// workgroup assembles from the caller's state and the earlier segments' end states.  With
+// several segments the tables are computed by extra workgroups of the state-only launch
+// (which itself does not read them), so they cost no launch of their own on the way to the
+// output pass.
 hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
   const int C = p.chunk;
   const int n_chunks = (p.N + C - 1) / C;
@@ -371,8 +290,11 @@ hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
   if (G < 1 || (G - 1) * seg_chunks >= n_chunks || G * seg_chunks < n_chunks)
     return hipErrorInvalidValue;
 
-  hipError_t e = C == 64 ? launch_tables_c<64>(p, tb, st) : launch_tables_c<32>(p, tb, st);
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (G == 1) {
+    e = C == 64 ? launch_tables_c<64>(p, tb, st) : launch_tables_c<32>(p, tb, st);
+    if (e != hipSuccess) return e;
+  }
 
   ChunkArgs a{};
   a.q = static_cast<const uint16_t*>(p.q);
@@ -399,12 +321,17 @@ hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
   bool inclusive = false;
   if (G > 1) {
     // Pass 1: end state of segments 0..G-2 from a zero state.
+    // The launch also computes the tables: one more workgroup per head.
     ChunkArgs s = a;
     s.seg_first = 0;
     s.n_seg = G - 1;
     s.seg_end = p.slots;
-    e = C == 64 ? dispatch_state_fdm<64>(s, p.F, p.D, p.M, seqs * (G - 1), st, kKindSummary)
-                : dispatch_state_fdm<32>(s, p.F, p.D, p.M, seqs * (G - 1), st, kKindSummary);
+    s.tables_out = p.tables;
+    s.n_sum_wg = seqs * (G - 1);
+    s.Lt = p.N % C == 0 ? C : p.N % C;
+    const int n_wg = seqs * (G - 1) + p.H;
+    e = C == 64 ? dispatch_state_fdm<64>(s, p.F, p.D, p.M, n_wg, st, kKindSummary)
+                : dispatch_state_fdm<32>(s, p.F, p.D, p.M, n_wg, st, kKindSummary);
     if (e != hipSuccess) return e;
     // With many segments, carry once (each slot read and written once) instead of letting
     // every output workgroup combine all of its predecessors' slots.

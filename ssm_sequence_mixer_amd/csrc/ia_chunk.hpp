@@ -323,10 +323,16 @@ struct ChunkArgs {
   int slots_per_seq;
   const unsigned char* tables;                 // per-head tables (chunk_tables_kernel)
   long table_bytes;                            // bytes per head
+  // State-only pass: workgroups past the first n_sum_wg compute the per-head tables (one
+  // workgroup per head, table_run) into tables_out, Lt the last chunk's length.
+  unsigned char* tables_out;
+  int n_sum_wg;
+  int Lt;
 };
 
-// Per-head tables, computed once per call by chunk_tables_kernel (byte offsets).  The two
-// decay tables and the two lam^(2i) factor tables are stored exactly as in LDS.
+// Per-head tables, computed once per call by table_run, in the state-only pass's launch or in
+// chunk_tables_kernel (byte offsets).  The two decay tables and the two lam^(2i) factor
+// tables are stored exactly as in LDS.
 template <int C, int M>
 struct TableLayout {
   static constexpr int NR = C / 16;
@@ -341,9 +347,7 @@ struct TableLayout {
   static constexpr long oPowS = oGeoT + 8L * M;       // float2 [M]: lam^(segment length)
   static constexpr long oInv = oPowS + 8L * M;        // float2 [M]: 1 / lam
   static constexpr long oSc = oInv + 8L * M;          // float: 1 / fp16 table scale
-  static constexpr long oTL = oSc + 16;               // float2 [M][C]: beta lam^(C-j)
-  static constexpr long oGeoL = oTL + 8L * M * C;     // float2 [M]: sum_{j<C} beta lam^(C-j)
-  static constexpr long bytes = (oGeoL + 8L * M + 255) / 256 * 256;
+  static constexpr long bytes = (oSc + 16 + 255) / 256 * 256;
 };
 
 // Word 3 of a CDNA buffer resource for raw (untyped) loads: 32-bit data format, no swizzle,

@@ -23,6 +23,7 @@
 #include <type_traits>
 
 #include "ia_chunk.hpp"
+#include "ia_tables.hpp"
 
 namespace ia {
 
@@ -40,7 +41,6 @@ struct StateLayout {
 template <int C, int F, int D, int M>
 __global__ void __launch_bounds__((64 * StateWaves<F, D, M>::NS))
 chunk_state_kernel(const ChunkArgs a) {
-  using TL = TableLayout<C, M>;
   using SL = SlotLayout<F, D, M>;
   using Lay = StateLayout<C, F, D, M>;
   constexpr int NS = StateWaves<F, D, M>::NS;
@@ -54,20 +54,31 @@ chunk_state_kernel(const ChunkArgs a) {
   constexpr int GROUPS = M * C / 4;          // table groups: 4 consecutive j of one mode
   constexpr int NGR = (GROUPS + NL - 1) / NL;
   constexpr int ST = Lay::stage;
+  constexpr int LOGC = C == 64 ? 6 : 5;
+  static_assert(C == 1 << LOGC, "chunk a power of two");
   static_assert((NL / VF) % 16 == 0 && (NL / VD) % 16 == 0, "loader rows keep the swizzle");
   static_assert(Lay::bytes <= 160 * 1024, "LDS budget");
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
   uint16_t* const s16 = reinterpret_cast<uint16_t*>(smem_raw);
   const int tid = threadIdx.x, lane = tid & 63, u = tid >> 6;
+  if (a.tables_out && (int)blockIdx.x >= a.n_sum_wg) {
+    // Table workgroup of head blockIdx.x - n_sum_wg: its C/4 table runs, RPP at a time.  The
+    // state-only workgroups below do not read these tables; the output pass does.
+    constexpr int RPP = 64 * NS / (4 * M);
+    static_assert(RPP >= 1 && (C / 4) % RPP == 0, "whole table runs per pass");
+    const int h = blockIdx.x - a.n_sum_wg;
+    for (int r0 = 0; r0 < C / 4; r0 += RPP)
+      table_run<C, M>(a.lam, a.beta, a.tables_out, a.table_bytes, a.Lt, a.seg_chunks * C, h,
+                      r0 + tid / (4 * M), tid % (4 * M));
+    return;
+  }
   const int il = lane & 15, g = lane >> 4;
   const int seq = blockIdx.x / a.n_seg;
   const int seg = a.seg_first + blockIdx.x % a.n_seg;
   const int b = seq / a.H, h = seq % a.H;
   const int nc = a.seg_chunks;               // a full segment
   const int c_first = seg * nc;
-  const unsigned char* tab = a.tables + (size_t)h * a.table_bytes;
-  const float2* powC = reinterpret_cast<const float2*>(tab + TL::oPow);
 
   // ---- per-lane LDS offsets (stage 0; stage 1 adds the constant ST)
   int offT[KC], trF[NFT], trD[NDT];
@@ -128,21 +139,28 @@ chunk_state_kernel(const ChunkArgs a) {
   };
 
   // ---- chunk table T_i = pw_i beta lam^(C-j), pw_i = lam^(i C): this thread's groups of 4
-  // consecutive j of one mode, beta lam^(C-j) held in registers for the whole segment.
+  // consecutive j of one mode, beta lam^(C-j) held in registers for the whole segment.  The
+  // powers are computed here from lam and beta (binary exponentiation in fp64), while the
+  // first chunks load (init_tables, after those loads are issued), so this pass does not wait
+  // for the per-head tables.
   float2 tl[NGR][4], pw[NGR], pc[NGR];
   int tRe[NGR], tIm[NGR];
+  auto init_tables = [&]() {
 #pragma unroll
-  for (int q = 0; q < NGR; ++q) {
-    const int gi = tid + NL * q;
-    const int m = gi < GROUPS ? gi / (C / 4) : 0, j0 = 4 * (gi % (C / 4));
-    const float2* src = reinterpret_cast<const float2*>(tab + TL::oTL) + m * C + j0;
+    for (int q = 0; q < NGR; ++q) {
+      const int gi = tid + NL * q;
+      const int m = gi < GROUPS ? gi / (C / 4) : 0, j0 = 4 * (gi % (C / 4));
+      const float2 l = a.lam[(size_t)h * M + m];
+      float2 base;   // lam^(C-j0-3), the group's smallest exponent (>= 1)
+      LamSmallPow(l).pow_and_top<LOGC>(C - j0 - 3, base, pc[q]);
+      tl[q][3] = cmul(a.beta[(size_t)h * M + m], base);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) tl[q][e] = src[e];
-    pw[q] = make_float2(1.f, 0.f);
-    pc[q] = powC[m];
-    tRe[q] = opaque(Lay::oT + soff<C>(m, kpos(j0)));
-    tIm[q] = opaque(Lay::oT + soff<C>(M + m, kpos(j0)));
-  }
+      for (int e = 2; e >= 0; --e) tl[q][e] = cmul(tl[q][e + 1], l);
+      pw[q] = make_float2(1.f, 0.f);
+      tRe[q] = opaque(Lay::oT + soff<C>(m, kpos(j0)));
+      tIm[q] = opaque(Lay::oT + soff<C>(M + m, kpos(j0)));
+    }
+  };
   auto write_table = [&](auto S) {
     constexpr int so = decltype(S)::value * ST;
 #pragma unroll
@@ -172,10 +190,15 @@ chunk_state_kernel(const ChunkArgs a) {
 #pragma unroll
     for (int kt = 0; kt < TM; ++kt) accG[di][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float2 eta = make_float2(0.f, 0.f), epw = make_float2(1.f, 0.f), epc = epw, egeo = eta;
-  if (u == 0 && lane < M) {
-    epc = powC[lane];
-    egeo = reinterpret_cast<const float2*>(tab + TL::oGeoL)[lane];
-  }
+  auto init_eta = [&]() {
+    if (u == 0 && lane < M) {   // lam^C and sum_j beta lam^(C-j) of mode `lane`
+      const LamSmallPow lp(a.lam[(size_t)h * M + lane]);
+      double cr, ci;
+      lp.top<LOGC>(cr, ci);
+      epc = make_float2((float)cr, (float)ci);
+      egeo = lp.geo(a.beta[(size_t)h * M + lane], C, cr, ci);
+    }
+  };
 
   auto update = [&](auto S) {
     constexpr int so = decltype(S)::value * ST;
@@ -224,6 +247,8 @@ chunk_state_kernel(const ChunkArgs a) {
   fetch(I0{}, 0);
   if (nc > 1) fetch(I1{}, 1);
   if (nc > 2) fetch(I2{}, 2);
+  init_tables();
+  init_eta();
   write_inputs(I0{}, I0{});
   write_table(I0{});
   __syncthreads();
