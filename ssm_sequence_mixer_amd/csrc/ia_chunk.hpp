@@ -15,14 +15,16 @@
 //   lam U_{c+1} = lam^L (lam U_c + sum_j beta lam^-j phi(k_j)), same for G with v, eta with 1.
 // Complex matrices enter real MFMAs as [Re | Im] blocks of 2M real columns.
 //
-// Workgroup = one (b, h, segment, direction); 64*(C/16 + 4) threads:
+// Workgroup = one (b, h, segment, direction); 64*(C/16 + NS) threads:
 //   readout waves r < C/16 own the 16 queries [16r, 16r+16) of each chunk and chain
 //     S^T -> A'^T -> P^T -> num^T through MFMA accumulators (an accumulator tile of X is the
 //     operand of X^T, with the K index permuted identically on both operands);
 //   state waves own columns of the fp32 state (held as lam U, lam G), kept in MFMA
 //     accumulators for the whole segment, update it with two MFMA contractions per chunk,
 //     publish operand copies of the new state (bf16 lam U, fp16 lam G scaled per column), and
-//     fetch the next chunk's q, k, v into registers while the current chunk computes.
+//     fetch the next chunk's q, k into registers while the current chunk computes (the
+//     readout waves fetch v).  Two barriers per chunk separate a first phase (S, A' and the
+//     lam U update) from a second (P, the numerator and the lam G update).
 // Operand precision: features, S, the decay table, U, P and v in bf16; A, beta lam^-j and G
 // in fp16 after exact power-of-two scaling (per query row for A; per value column for G; per
 // head for the table), which keeps the readout's cancelling sums within the bf16 tolerance.
@@ -508,13 +510,13 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
                        *reinterpret_cast<const float2*>(sb + oG + (Lay::bL2hi - Lay::bLE) +
                                                         8 * r * M + mo));
     }
-  if (x.c_begin < x.c_end) {
-    write_v();
-    if (x.c_begin + 1 < x.c_end) fetch_v(x.c_begin + 1);
-  }
-  __syncthreads();  // first chunk in LDS
+  __syncthreads();  // first chunk's inputs in LDS
 
   for (int c = x.c_begin; c < x.c_end; ++c) {
+    // v of chunk c into LDS (its readers run after the mid-chunk barrier), the next chunk's
+    // loads out.
+    write_v();
+    if (c + 1 < x.c_end) fetch_v(c + 1);
     // Live across the mid-chunk barrier: the fp16 operand of lam^(2i) A', its per-query
     // scale and the inter-chunk denominator.
     f16x8 Af[KM];
@@ -670,11 +672,6 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
       }
     }
     __syncthreads();   // chunk c read by every wave
-    if (c + 1 < x.c_end) {
-      write_v();
-      if (c + 2 < x.c_end) fetch_v(c + 2);
-    }
-    __syncthreads();
   }
 }
 
@@ -914,11 +911,10 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
     }
   }
 
-  // ---- operand copies of the state for the readout of the next chunk, written to LDS between
-  // the two barriers: lam U (bf16), c_d lam G (fp16, c_d a power of two per value column; the
-  // scale and the packing are done while the current chunk's readout runs), lam eta.
-  // (lam U is converted while it is written: 16 conversions, not worth 16 registers held
-  // across the barrier.)
+  // ---- operand copies of the state for the readout: lam U (bf16) and lam eta of chunk c+1,
+  // written in chunk c's second phase (the readout reads them in the first); c_d lam G (fp16,
+  // c_d a power of two per value column) and the column scales of chunk c, written in chunk
+  // c's first phase (the readout reads them in the second).
   uint2 pG[NDT][TM];       // c_d lam G, 4 fp16 each
   float pC[NDT];
   auto pack_state = [&]() {
@@ -953,7 +949,7 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
         }
       }
   };
-  auto write_state = [&]() {   // lam G copy, its column scales, lam eta
+  auto write_g = [&]() {   // lam G copy and its column scales
 #pragma unroll
     for (int di = 0; di < NDT; ++di) {
       const int dt = u + NS * di;
@@ -968,7 +964,26 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
               pG[di][kt];
       }
     }
+  };
+  auto write_eta = [&]() {
     if (u == 0 && lane < M) f2(oLn) = eta;
+  };
+  // lam G <- lam^L lam G with chunk cc's pair (the full-chunk pair, or the last chunk's)
+  auto decay_g = [&](int cc) {
+    const int ts = a.N - cc * C < C ? Lay::kTail : 0;
+#pragma unroll
+    for (int di = 0; di < NDT; ++di)
+      if (u + NS * di < TD) {
+#pragma unroll
+        for (int mt = 0; mt < MH; ++mt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float2 p = f2(oPg + ts + 8 * (16 * mt + q));
+            const float xr = accG[di][mt][q], yi = accG[di][mt + MH][q];
+            accG[di][mt][q] = p.x * xr - p.y * yi;
+            accG[di][mt + MH][q] = p.x * yi + p.y * xr;
+          }
+      }
   };
 
   if (x.c_begin < x.c_end) {
@@ -976,34 +991,37 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
     convert(x.c_begin);
     if (x.want_out) {
       write_lam_u();
-      pack_state();
-      write_state();
+      pack_state();   // written in the first chunk's first phase
+      write_eta();
     }
     write_inputs();
     if (x.c_begin + 1 < x.c_end) fetch(x.c_begin + 1);
   }
   __syncthreads();
 
+  // Two phases per chunk.  First: the lam G copy of chunk c (lam G of chunk c-1, updated in
+  // the previous second phase, is decayed and packed here), then
+  // lam U^T <- lam^L (lam U^T + phi(K)^T (beta lam^-j)).  Second, once v of chunk c is in
+  // LDS: lam G <- lam G + W^T V (its decay waits for the next first phase), and chunk c+1's
+  // copies and inputs.
   for (int c = x.c_begin; c < x.c_end; ++c) {
-    // lam U^T <- lam^L (lam U^T + phi(K)^T (beta lam^-j)),  lam G <- lam^L (lam G + W^T V)
+    if (c > x.c_begin) {
+      decay_g(c - 1);
+      if (x.want_out) pack_state();
+    }
+    if (x.want_out) write_g();
 #pragma unroll
     for (int kb = 0; kb < KC; ++kb) {
-      bf16x8 afk[NFT], bv[NDT];
+      bf16x8 afk[NFT];
 #pragma unroll
       for (int fi = 0; fi < NFT; ++fi)
         if (u + NS * fi < F / 16) afk[fi] = ldtr<F>(s16, trF[fi], kb).b;
-#pragma unroll
-      for (int di = 0; di < NDT; ++di)
-        if (u + NS * di < TD) bv[di] = ldtr<D>(s16, trD[di], kb).b;
 #pragma unroll
       for (int kt = 0; kt < TM; ++kt) {
         const bf16x8 w = lds8(s16 + offC[kb] + 16 * kt * C).b;
 #pragma unroll
         for (int fi = 0; fi < NFT; ++fi)
           if (u + NS * fi < F / 16) accU[fi][kt] = mma_bf16(afk[fi], w, accU[fi][kt]);
-#pragma unroll
-        for (int di = 0; di < NDT; ++di)
-          if (u + NS * di < TD) accG[di][kt] = mma_bf16(w, bv[di], accG[di][kt]);
         IA_STEP_FENCE();
       }
     }
@@ -1023,19 +1041,6 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
           }
         }
       }
-#pragma unroll
-    for (int di = 0; di < NDT; ++di)
-      if (u + NS * di < TD) {
-#pragma unroll
-        for (int mt = 0; mt < MH; ++mt)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float2 p = f2(oPg + tsel + 8 * (16 * mt + q));
-            const float xr = accG[di][mt][q], yi = accG[di][mt + MH][q];
-            accG[di][mt][q] = p.x * xr - p.y * yi;
-            accG[di][mt + MH][q] = p.x * yi + p.y * xr;
-          }
-      }
     if (u == 0 && lane < M) {
       const float2 ge = f2(oLn + tsel + (Lay::bGeo - Lay::bLE));
       eta = cmul(f2(oLn + tsel + (Lay::bPowL - Lay::bLE)),
@@ -1043,21 +1048,33 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
     }
     const bool more = c + 1 < x.c_end;
     __syncthreads();    // mid-chunk: phi(q), phi(k), lam U of chunk c no longer read
+#pragma unroll
+    for (int kb = 0; kb < KC; ++kb) {
+      bf16x8 bv[NDT];
+#pragma unroll
+      for (int di = 0; di < NDT; ++di)
+        if (u + NS * di < TD) bv[di] = ldtr<D>(s16, trD[di], kb).b;
+#pragma unroll
+      for (int kt = 0; kt < TM; ++kt) {
+        const bf16x8 w = lds8(s16 + offC[kb] + 16 * kt * C).b;
+#pragma unroll
+        for (int di = 0; di < NDT; ++di)
+          if (u + NS * di < TD) accG[di][kt] = mma_bf16(w, bv[di], accG[di][kt]);
+        IA_STEP_FENCE();
+      }
+    }
     if (more) {
       if (x.want_out) {
         write_lam_u();
-        pack_state();
+        write_eta();
       }
       convert(c + 1);   // waits for the loads issued one chunk ago
       write_inputs();
-    }
-    __syncthreads();    // chunk c read by every wave
-    if (more) {
-      if (x.want_out) write_state();
       if (c + 2 < x.c_end) fetch(c + 2);
     }
-    __syncthreads();
+    __syncthreads();    // chunk c read by every wave
   }
+  if (x.c_begin < x.c_end) decay_g(x.c_end - 1);
 
   // Final state (divided by lam) in the caller's layout.
   float2 *fU = nullptr, *fG = nullptr, *fE = nullptr;
