@@ -153,6 +153,53 @@ def test_chunk_forced_clamp():
     assert err < TOL_BF16
 
 
+@pytest.mark.parametrize("plan", [(1, 2, 1536), (4, 16, 512)])
+def test_chunk_lambda_edges_multi_segment(plan):
+    """Modes on and near the unit circle among the S4D modes, several segments per sequence:
+    (1, 2, 1536) runs many segments through the carry kernel, (4, 16, 512) four segments
+    through the Horner step.  The segment end states take their powers of lam by binary
+    exponentiation and sum_n beta lam^n in closed form, lam = 1 separately.
+
+    lam = 1 and lam = 1 - 1e-6 (beta = 1): outputs and the final state.  Undamped modes of
+    large argument (lam = -1, i, 0.999 e^(0.999 i pi), e^(-0.01 - 3.1 i)) with random complex
+    beta: the final state only.  With such modes the denominator Re sum_m a_m eta_m is
+    dominated by terms whose phase turns twice as fast as the mode's: it is negative in most
+    rows (the clamp) and a cancelling sum elsewhere, where bf16 operands are not enough (the
+    fp32 path agrees with the oracle to 5e-4 there).  The state has no such division; its
+    features phi(k) = elu(k)+1 have mean about 1, which cancels in an undamped oscillating
+    mode while their bf16 rounding (2^-9 relative) does not, so that case uses q, k of unit
+    scale (the default 1/sqrt(F) would leave the rounding at a few percent of the sum)."""
+    import torch
+    ia = _ia()
+    B, H, N = plan
+    F, M = 64, 32
+    cases = [("near one", np.array([1.0, np.exp(-1e-6 + 1e-6j)], np.complex64), False, None),
+             ("large argument", np.array([-1.0, 1j, 0.999 * np.exp(1j * np.pi * 0.999),
+                                          np.exp(-0.01 - 3.1j)], np.complex64), True, 1.0)]
+    for name, edge, complex_beta, std in cases:
+        inp = W.make_inputs(B, H, N, F, F, M, dtype="bf16", seed=301 + N, std=std)
+        if complex_beta:
+            rng = np.random.default_rng(302)
+            inp["beta"] = (rng.normal(size=(H, M)) +
+                           1j * rng.normal(size=(H, M))).astype(np.complex64)
+        lam = inp["lam"].copy()
+        for h in range(H):
+            lam[h, :len(edge)] = np.roll(edge, h)
+        inp["lam"] = lam
+        st = ia.new_state(B, H, M, F, F)
+        tag(f"chunk lambda edges ({name}) B={B} H={H} N={N}")
+        o = _run(inp, state=st)
+        o_ref, _, _, st_ref = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["lam"],
+                                             inp["beta"], threads=8)
+        e_s = state_rel(tuple(host(s) for s in st), st_ref)
+        report(f"lambda edges ({name}) {plan} state", e_s)
+        assert e_s < TOL_BF16
+        if not complex_beta:
+            e_o = rowrel(host(o), o_ref)
+            report(f"lambda edges ({name}) {plan} output", e_o)
+            assert e_o < TOL_BF16
+
+
 # ---------------------------------------------------------------- full workload sizes
 
 def _sampled(inp, slices, bidir=False, out="f32", threads=8):
