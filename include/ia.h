@@ -148,8 +148,9 @@ ia_status ia_prefill_fwd(const ia_desc* desc,
 /* Profiling variant of ia_prefill_fwd: identical work and results, and in addition, for its
  * i-th kernel launch (i < max_launches, in launch order), records events[2i] before and
  * events[2i+1] after the kernel on `stream` and stores the kernel's kind in kinds[i]
- * (2 decay tables, 3 segment end states, 4 segment carry, 5 chunked prefill with outputs,
- * 0 zero fill, 1 token-sequential prefill).  events: 2*max_launches hipEvent_t handles
+ * (2 decay tables, launched on their own only when a sequence is one segment; 3 segment end
+ * states, whose launch also computes the tables when there are several segments; 4 segment
+ * carry; 5 chunked prefill with outputs; 0 zero fill; 1 token-sequential prefill).  events: 2*max_launches hipEvent_t handles
  * created by the caller.  *n_launches receives the number of launches recorded.  Errors: as
  * ia_prefill_fwd, and IA_ERR_NULL for missing events/kinds/n_launches. */
 ia_status ia_prefill_fwd_profiled(const ia_desc* desc,
