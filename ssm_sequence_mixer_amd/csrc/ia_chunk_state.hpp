@@ -45,7 +45,6 @@ chunk_state_kernel(const ChunkArgs a) {
   using Lay = StateLayout<C, F, D, M>;
   constexpr int NS = StateWaves<F, D, M>::NS;
   constexpr int NFT = SL::NFT, NDT = SL::NDT, TM = SL::TM;
-  constexpr int M2 = 2 * M;
   constexpr int KC = C / 32;
   constexpr int TD = D / 16;
   constexpr int VF = F / 8, VD = D / 8;
