@@ -20,7 +20,8 @@
  *   complex-diagonal modes lambda_m (S4D) [summary §3.2].  The readout at step t includes
  *   token t.  The clamp (default 1e-6) is one-sided: a negative real part is raised to it.
  *
- * Layouts (all row-major, innermost index last, no padding):
+ * Layouts (all row-major, innermost index last, no padding; ia_prefill_fwd_strided also takes
+ * q, k, v with element strides):
  *   q, k        [B][N][H][F]   in_dtype (IA_F32 or IA_BF16)
  *   v           [B][N][H][Dv]  in_dtype
  *   o           [B][N][H][Dv]  out_dtype
@@ -144,6 +145,24 @@ ia_status ia_prefill_fwd(const ia_desc* desc,
                          const void* lambda, const void* beta,
                          ia_state* st, void* o,
                          void* workspace, size_t ws_bytes, void* stream);
+
+/* ia_prefill_fwd with q, k, v in strided layouts, e.g. views of one fused projection
+ * [B][N][3][H][F] (no copy needed).  strides[i] = {b, n, h} element strides of q (i = 0),
+ * k (1) and v (2): element (b, n, h, x) of q lies at q + b*s[0] + n*s[1] + h*s[2] + x, the
+ * feature (value) axis contiguous.  strides == NULL: the dense layouts above (this is what
+ * ia_prefill_fwd does).  o, the state, lambda and beta keep their dense layouts, and the
+ * workspace size is ia_prefill_workspace_bytes(desc) as before.  Ownership and aliasing as
+ * for ia_prefill_fwd, with the inputs' extents taken from the strides.
+ * Errors, besides those of ia_prefill_fwd: IA_ERR_SHAPE (a stride <= 0), IA_ERR_ALIGN (a
+ * stride times the element size not a multiple of 16 bytes), IA_ERR_UNSUPPORTED (q and k
+ * with different strides; with bf16 inputs, 64 token rows of q/k or of v spanning more than
+ * 1 GiB). */
+ia_status ia_prefill_fwd_strided(const ia_desc* desc,
+                                 const void* q, const void* k, const void* v,
+                                 const long long strides[3][3],
+                                 const void* lambda, const void* beta,
+                                 ia_state* st, void* o,
+                                 void* workspace, size_t ws_bytes, void* stream);
 
 /* Profiling variant of ia_prefill_fwd: identical work and results, and in addition, for its
  * i-th kernel launch (i < max_launches, in launch order), records events[2i] before and

@@ -7,13 +7,16 @@ the C ABI declared in ``include/ia.h``.  Functions carry the C names:
     ia_prefill_workspace_bytes(desc)
     ia_check_lambda(desc, lam_host)
     ia_prefill_fwd(desc, q, k, v, lam, beta, state, o, workspace, stream=None)
+    ia_prefill_fwd_strided(desc, q, k, v, lam, beta, state, o, workspace, stream=None)
     ia_decode_step(desc, q_t, k_t, v_t, lam, beta, state, o_t, stream=None)
 
 Tensors are torch tensors on the GPU (PyTorch provides device memory and streams):
 q, k [B,N,H,F], v and o [B,N,H,Dv] in float32 or bfloat16; lam, beta [H,M] complex64; a
 state is a tuple (U [B,H,M,F], Gamma [B,H,M,Dv], eta [B,H,M]) of complex64 tensors.
-``prefill``, ``decode`` and ``new_state`` are conveniences that allocate the outputs with
-torch and then call the same entry points.
+``ia_prefill_fwd_strided`` also accepts q, k, v as strided views (feature axis contiguous, q
+and k with equal strides), e.g. slices of one fused projection.  ``prefill``, ``decode`` and
+``new_state`` are conveniences that allocate the outputs with torch and then call the same
+entry points (``prefill`` passes views through the strided entry point).
 
 Importing fails loudly when libia.so has not been built (``python
 ssm_sequence_mixer_amd/build.py``): there is no fallback implementation.
@@ -72,6 +75,10 @@ lib.ia_check_lambda.argtypes = [_D, _P]
 lib.ia_check_lambda.restype = ctypes.c_int
 lib.ia_prefill_fwd.argtypes = [_D, _P, _P, _P, _P, _P, _S, _P, _P, ctypes.c_size_t, _P]
 lib.ia_prefill_fwd.restype = ctypes.c_int
+_STRIDES = (ctypes.c_longlong * 3) * 3
+lib.ia_prefill_fwd_strided.argtypes = [_D, _P, _P, _P, ctypes.POINTER(_STRIDES), _P, _P, _S,
+                                       _P, _P, ctypes.c_size_t, _P]
+lib.ia_prefill_fwd_strided.restype = ctypes.c_int
 lib.ia_decode_step.argtypes = [_D, _P, _P, _P, _P, _P, _S, _P, _P]
 lib.ia_decode_step.restype = ctypes.c_int
 lib.ia_prefill_fwd_profiled.argtypes = [_D, _P, _P, _P, _P, _P, _S, _P, _P, ctypes.c_size_t,
@@ -85,8 +92,8 @@ lib.ia_last_launch_error.argtypes = []
 lib.ia_last_launch_error.restype = ctypes.c_char_p
 
 EXPORTS = ("ia_state_init", "ia_prefill_workspace_bytes", "ia_check_lambda", "ia_prefill_fwd",
-           "ia_prefill_fwd_profiled", "ia_decode_step", "ia_status_string",
-           "ia_last_launch_error")
+           "ia_prefill_fwd_strided", "ia_prefill_fwd_profiled", "ia_decode_step",
+           "ia_status_string", "ia_last_launch_error")
 KIND_NAMES = {0: "fill", 1: "scan", 2: "tables", 3: "summary", 4: "carry", 5: "chunk",
               6: "decode"}
 
@@ -165,6 +172,23 @@ def ia_prefill_fwd(desc: IADesc, q, k, v, lam, beta, state, o, workspace, stream
                               _stream(stream)), "ia_prefill_fwd")
 
 
+def ia_prefill_fwd_strided(desc: IADesc, q, k, v, lam, beta, state, o, workspace, stream=None):
+    """ia_prefill_fwd for q, k, v of any element strides along (b, n, h) with the last axis
+    contiguous (the strides are the tensors' own); the other tensors dense."""
+    _dense(lam, beta, o, workspace)
+    st = _STRIDES()
+    for i, t in enumerate((q, k, v)):
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError("q, k, v need 4 axes with the last one contiguous")
+        for j in range(3):
+            st[i][j] = t.stride(j)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.ia_prefill_fwd_strided(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                      ctypes.byref(st), _ptr(lam), _ptr(beta), _state(state),
+                                      _ptr(o), _ptr(workspace), ws_bytes, _stream(stream)),
+           "ia_prefill_fwd_strided")
+
+
 def ia_prefill_fwd_profiled(desc: IADesc, q, k, v, lam, beta, state, o, workspace, events,
                             stream=None):
     """As ia_prefill_fwd; `events` is a list of 2*n raw hipEvent_t handles.  Returns the kind
@@ -203,7 +227,8 @@ def new_state(B, H, M, F, Dv, device="cuda", stream=None, zero=True):
 
 def prefill(q, k, v, lam, beta, state=None, out_dtype=None, bidir=False, chunk=0,
             den_clamp=1e-6, want_output=True, stream=None, workspace=None):
-    """Allocate o (and the workspace) with torch and run ia_prefill_fwd; returns o."""
+    """Allocate o (and the workspace) with torch and run ia_prefill_fwd (or, for strided
+    views q, k, v, ia_prefill_fwd_strided); returns o."""
     import torch
     B, N, H, F = q.shape
     Dv, M = v.shape[3], lam.shape[1]
@@ -214,7 +239,10 @@ def prefill(q, k, v, lam, beta, state=None, out_dtype=None, bidir=False, chunk=0
     if workspace is None:
         nb = ia_prefill_workspace_bytes(desc)
         workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device) if nb else None
-    ia_prefill_fwd(desc, q, k, v, lam, beta, state, o, workspace, stream)
+    if all(t.is_contiguous() for t in (q, k, v)):
+        ia_prefill_fwd(desc, q, k, v, lam, beta, state, o, workspace, stream)
+    else:
+        ia_prefill_fwd_strided(desc, q, k, v, lam, beta, state, o, workspace, stream)
     return o
 
 

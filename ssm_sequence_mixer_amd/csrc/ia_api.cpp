@@ -189,8 +189,34 @@ size_t ia_prefill_workspace_bytes(const ia_desc* d) {
 ia_status ia_prefill_fwd(const ia_desc* d, const void* q, const void* k, const void* v,
                          const void* lambda, const void* beta, ia_state* st, void* o,
                          void* workspace, size_t ws_bytes, void* stream) {
+  return ia_prefill_fwd_strided(d, q, k, v, nullptr, lambda, beta, st, o, workspace, ws_bytes,
+                                stream);
+}
+
+ia_status ia_prefill_fwd_strided(const ia_desc* d, const void* q, const void* k, const void* v,
+                                 const long long strides[3][3], const void* lambda,
+                                 const void* beta, ia_state* st, void* o, void* workspace,
+                                 size_t ws_bytes, void* stream) {
   ia_status s = check_desc(d, true);
   if (s != IA_OK) return s;
+  // Element strides (b, n, h) of q, k, v; the feature axis is contiguous.
+  ia::RowStrides sq = ia::dense_strides(d->N, d->H, d->F), sk = sq;
+  ia::RowStrides sv = ia::dense_strides(d->N, d->H, d->Dv);
+  if (strides) {
+    sq = ia::RowStrides{strides[0][0], strides[0][1], strides[0][2]};
+    sk = ia::RowStrides{strides[1][0], strides[1][1], strides[1][2]};
+    sv = ia::RowStrides{strides[2][0], strides[2][1], strides[2][2]};
+    for (const ia::RowStrides& r : {sq, sk, sv}) {
+      if (r.b <= 0 || r.n <= 0 || r.h <= 0) return IA_ERR_SHAPE;
+      const long long es = esize(d->in_dtype);
+      if ((r.b * es) % 16 || (r.n * es) % 16 || (r.h * es) % 16) return IA_ERR_ALIGN;
+    }
+    if (sq.b != sk.b || sq.n != sk.n || sq.h != sk.h) return IA_ERR_UNSUPPORTED;
+    // The chunk kernels address a chunk's rows with 32-bit byte offsets (as for the dense
+    // layout in use_chunk_path).
+    if (use_chunk_path(d) && (64LL * sq.n * 2 > (1LL << 30) || 64LL * sv.n * 2 > (1LL << 30)))
+      return IA_ERR_UNSUPPORTED;
+  }
   const bool bidir = d->flags & IA_FLAG_BIDIR;
   if (!q || !k || !v || !lambda || !beta) return IA_ERR_NULL;
   if (!o && !st) return IA_ERR_NULL;
@@ -202,9 +228,13 @@ ia_status ia_prefill_fwd(const ia_desc* d, const void* q, const void* k, const v
   if (st && (s = check_state(d, st)) != IA_OK) return s;
 
   const size_t tok = size_t(d->B) * d->N * d->H;
-  const Range rq = rng(q, tok * d->F * esize(d->in_dtype));
-  const Range rk = rng(k, tok * d->F * esize(d->in_dtype));
-  const Range rv = rng(v, tok * d->Dv * esize(d->in_dtype));
+  auto extent = [&](const ia::RowStrides& r, int width) {   // bytes from the base pointer
+    return size_t((d->B - 1) * r.b + (d->N - 1) * r.n + (d->H - 1) * r.h + width) *
+           esize(d->in_dtype);
+  };
+  const Range rq = rng(q, extent(sq, d->F));
+  const Range rk = rng(k, extent(sk, d->F));
+  const Range rv = rng(v, extent(sv, d->Dv));
   const Range rl = rng(lambda, size_t(d->H) * d->M * 8);
   const Range rb = rng(beta, size_t(d->H) * d->M * 8);
   const Range ins[] = {rq, rk, rv, rl, rb};
@@ -244,6 +274,8 @@ ia_status ia_prefill_fwd(const ia_desc* d, const void* q, const void* k, const v
     a.q = q;
     a.k = k;
     a.v = v;
+    a.sqk = sq;
+    a.sv = sv;
     a.lam = static_cast<const float2*>(lambda);
     a.beta = static_cast<const float2*>(beta);
     a.o = o;
@@ -294,9 +326,9 @@ ia_status ia_prefill_fwd(const ia_desc* d, const void* q, const void* k, const v
     hipError_t e = ia::launch_fill_zero(ws + w.state_off, state_bytes(d), hs);
     if (e != hipSuccess) return launch_status(e);
   }
-  ia::ScanArgs a{q, k, v, static_cast<const float2*>(lambda), static_cast<const float2*>(beta),
-                 U, G, E, o, 0, d->B, d->H, d->N, d->F, d->Dv, d->M,
-                 d->in_dtype == IA_BF16, d->out_dtype == IA_BF16, d->den_clamp, 0};
+  ia::ScanArgs a{q, k, v, sq, sv, static_cast<const float2*>(lambda),
+                 static_cast<const float2*>(beta), U, G, E, o, 0, d->B, d->H, d->N, d->F, d->Dv,
+                 d->M, d->in_dtype == IA_BF16, d->out_dtype == IA_BF16, d->den_clamp, 0};
   if (!bidir) return launch_status(ia::launch_scan_prefill(a, hs));
 
   // Bidirectional: the forward direction writes o, the reverse direction (from a zero state

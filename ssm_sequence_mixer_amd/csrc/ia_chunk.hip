@@ -300,6 +300,8 @@ hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
   a.q = static_cast<const uint16_t*>(p.q);
   a.k = static_cast<const uint16_t*>(p.k);
   a.v = static_cast<const uint16_t*>(p.v);
+  a.sqk = p.sqk;
+  a.sv = p.sv;
   a.lam = p.lam;
   a.beta = p.beta;
   a.N = p.N;

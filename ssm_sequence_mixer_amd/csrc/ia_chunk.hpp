@@ -297,7 +297,8 @@ struct Layout {
 };
 
 struct ChunkArgs {
-  const uint16_t *q, *k, *v;   // bf16 [B][N][H][F|D]
+  const uint16_t *q, *k, *v;   // bf16, element (b, n, h) strides sqk (q and k) and sv; the
+  RowStrides sqk, sv;          // feature axis contiguous
   const float2 *lam, *beta;    // [H][M]
   void* o;                     // [B][N][H][D] or NULL (state only)
   int accumulate;              // add to the values o holds (second bidirectional direction)
@@ -356,20 +357,22 @@ struct TableLayout {
 // no index stride; offsets at or past the range read as zeros.
 constexpr int kBufferFlags = 0x00020000;
 
-// The L valid token rows of chunk c (C tokens) of sequence (b, h) in a [B][N][H][width] bf16
-// tensor as a buffer: based at the lowest-addressed valid row (row 0 walking forward, row L-1
-// walking backward), L row strides long.  Row r (walk order) column e lies at
-// row_off(r, e) - shift; rows at or past the sequence end fall outside the range (past its end
-// forward, below its base, wrapping to large offsets, backward) and read as zeros.
+// The L valid token rows of chunk c (C tokens) of sequence (b, h) in a bf16 tensor with
+// element strides s (token rows s.n apart) as a buffer: based at the lowest-addressed valid
+// row (row 0 walking forward, row L-1 walking backward), L row strides long.  Row r (walk
+// order) column e lies at row_off(r, e) - shift; rows at or past the sequence end fall
+// outside the range (past its end forward, below its base, wrapping to large offsets,
+// backward) and read as zeros.  (C s.n 2 bytes fit 32 bits; the host checks.)
 template <int C>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rows(const ChunkArgs& a, int b, int h,
-                                                             const uint16_t* t, int width, int c,
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rows(const ChunkArgs& a,
+                                                             const RowStrides& s, int b, int h,
+                                                             const uint16_t* t, int c,
                                                              uint32_t& shift) {
   const int L = min(C, a.N - c * C);
-  const uint32_t stride = (uint32_t)a.H * width * 2u;
+  const uint32_t stride = (uint32_t)s.n * 2u;
   shift = a.dir ? (uint32_t)(C - L) * stride : 0u;
   const int pos = a.dir ? a.N - c * C - L : c * C;
-  const uint16_t* p = t + (((size_t)b * a.N + pos) * a.H + h) * width;
+  const uint16_t* p = t + b * s.b + (long long)pos * s.n + h * s.h;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0,
                                            (int)((uint32_t)L * stride), kBufferFlags);
 }
@@ -377,8 +380,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rows(const ChunkArgs& a,
 // Byte offset of chunk row r (0 = the chunk's first token in walk order), column e, from the
 // lowest-addressed row of a full chunk.
 template <int C>
-__device__ __forceinline__ uint32_t row_off(const ChunkArgs& a, int width, int r, int e) {
-  return (uint32_t)((a.dir ? C - 1 - r : r) * a.H * width + e) * 2u;
+__device__ __forceinline__ uint32_t row_off(const ChunkArgs& a, const RowStrides& s, int r,
+                                            int e) {
+  return (uint32_t)((a.dir ? C - 1 - r : r) * (uint32_t)s.n + e) * 2u;
 }
 
 // Per-workgroup context shared by the two wave roles.
@@ -396,12 +400,12 @@ struct Ctx {
   __device__ size_t tok_index(const ChunkArgs& a, int pos) const {
     return ((size_t)b * a.N + pos) * a.H + h;
   }
-  __device__ __amdgpu_buffer_rsrc_t chunk_rows(const ChunkArgs& a, const uint16_t* t, int width,
-                                               int c, uint32_t& shift) const {
-    return ia::chunk_rows<C>(a, b, h, t, width, c, shift);
+  __device__ __amdgpu_buffer_rsrc_t chunk_rows(const ChunkArgs& a, const RowStrides& s,
+                                               const uint16_t* t, int c, uint32_t& shift) const {
+    return ia::chunk_rows<C>(a, s, b, h, t, c, shift);
   }
-  __device__ static uint32_t row_off(const ChunkArgs& a, int width, int r, int e) {
-    return ia::row_off<C>(a, width, r, e);
+  __device__ static uint32_t row_off(const ChunkArgs& a, const RowStrides& s, int r, int e) {
+    return ia::row_off<C>(a, s, r, e);
   }
 };
 
@@ -481,11 +485,11 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
   int stV[NV];
 #pragma unroll
   for (int t = 0; t < NV; ++t) stV[t] = opaque(Lay::oV + soff<D>(16 * r + il, 8 * (g + 4 * t)));
-  const uint32_t lofV = x.row_off(a, D, 16 * r + il, 8 * g);
+  const uint32_t lofV = x.row_off(a, a.sv, 16 * r + il, 8 * g);
   uint4 rv[NV];
   auto fetch_v = [&](int c) {   // rows past N read as zeros
     uint32_t shift;
-    const __amdgpu_buffer_rsrc_t vb = x.chunk_rows(a, a.v, D, c, shift);
+    const __amdgpu_buffer_rsrc_t vb = x.chunk_rows(a, a.sv, a.v, c, shift);
 #pragma unroll
     for (int t = 0; t < NV; ++t) rv[t] = load16(vb, lofV - shift + 64 * t);
   };
@@ -744,7 +748,8 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
   const int rowF0 = n0 / VF;
   uint32_t lofF[NLF];
 #pragma unroll
-  for (int t = 0; t < NLF; ++t) lofF[t] = x.row_off(a, F, rowF0 + t * (NL / VF), 8 * (n0 % VF));
+  for (int t = 0; t < NLF; ++t)
+    lofF[t] = x.row_off(a, a.sqk, rowF0 + t * (NL / VF), 8 * (n0 % VF));
   // LDS rows row0 + t NL/VF share the swizzle of row0 (NL/VF is a multiple of 16).
   static_assert((NL / VF) % 16 == 0, "loader rows keep the swizzle");
   const int stF = opaque(Lay::oFk + soff<F>(rowF0, 8 * (n0 % VF)));
@@ -752,8 +757,8 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
   uint4 rq[NLF], rk[NLF];
   auto fetch = [&](int c) {   // rows past N (and past the chunk) read as zeros
     uint32_t shift;
-    const __amdgpu_buffer_rsrc_t kb = x.chunk_rows(a, a.k, F, c, shift);
-    const __amdgpu_buffer_rsrc_t qb = x.chunk_rows(a, a.q, F, c, shift);
+    const __amdgpu_buffer_rsrc_t kb = x.chunk_rows(a, a.sqk, a.k, c, shift);
+    const __amdgpu_buffer_rsrc_t qb = x.chunk_rows(a, a.sqk, a.q, c, shift);
 #pragma unroll
     for (int t = 0; t < NLF; ++t) {
       rk[t] = load16(kb, lofF[t] - shift);

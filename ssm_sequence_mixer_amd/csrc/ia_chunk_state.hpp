@@ -89,13 +89,15 @@ chunk_state_kernel(const ChunkArgs a) {
   for (int di = 0; di < NDT; ++di) trD[di] = opaque(Lay::oV + tr_off<D>(u + NS * di, lane));
 
   // ---- loader: 16-byte vectors n = n0 + NL t of the row-major chunk matrices k ([C][F]) and
-  // v ([C][D]); token rows are H*F (H*D) elements apart, backwards in the reverse direction.
+  // v ([C][D]); token rows are sqk.n (sv.n) elements apart, backwards in the reverse
+  // direction.
   const int n0 = 64 * u + lane;
   const int rowK0 = n0 / VF, rowV0 = n0 / VD;
   const int sgn = a.dir ? -1 : 1;
-  const int lofK = sgn * rowK0 * (a.H * F) + 8 * (n0 % VF);
-  const int lofV = sgn * rowV0 * (a.H * D) + 8 * (n0 % VD);
-  const int stepK = sgn * (NL / VF) * (a.H * F), stepV = sgn * (NL / VD) * (a.H * D);
+  const int snK = (int)a.sqk.n, snV = (int)a.sv.n;   // < 2^23 (the host checks)
+  const int lofK = sgn * rowK0 * snK + 8 * (n0 % VF);
+  const int lofV = sgn * rowV0 * snV + 8 * (n0 % VD);
+  const int stepK = sgn * (NL / VF) * snK, stepV = sgn * (NL / VD) * snV;
   const int stK = opaque(Lay::oFk + soff<F>(rowK0, 8 * (n0 % VF)));
   const int stV = opaque(Lay::oV + soff<D>(rowV0, 8 * (n0 % VD)));
   uint4 rk[3][NLK], rv[3][NLV];
@@ -104,9 +106,9 @@ chunk_state_kernel(const ChunkArgs a) {
   auto fetch = [&](auto R, int i) {
     constexpr int r = decltype(R)::value;
     const int t0 = chunk_of(i) * C;
-    const size_t tb = ((size_t)b * a.N + (a.dir ? a.N - 1 - t0 : t0)) * a.H + h;
-    const uint16_t* kb = a.k + tb * F + lofK;
-    const uint16_t* vb = a.v + tb * D + lofV;
+    const long long pos = a.dir ? a.N - 1 - t0 : t0;
+    const uint16_t* kb = a.k + b * a.sqk.b + pos * a.sqk.n + h * a.sqk.h + lofK;
+    const uint16_t* vb = a.v + b * a.sv.b + pos * a.sv.n + h * a.sv.h + lofV;
 #pragma unroll
     for (int t = 0; t < NLK; ++t)
       rk[r][t] = n0 + NL * t < C * VF ? *reinterpret_cast<const uint4*>(kb + t * stepK)

@@ -42,6 +42,14 @@ inline void prof_end(hipStream_t st, int kind) {
 constexpr int kMaxDim = 256;    // largest F and Dv
 constexpr int kMaxModes = 128;  // largest M
 
+// Element strides of a [B][N][H][X] tensor along b, n and h (X contiguous).
+struct RowStrides {
+  long long b, n, h;
+};
+inline RowStrides dense_strides(int N, int H, int X) {
+  return RowStrides{(long long)N * H * X, (long long)H * X, X};
+}
+
 struct DecodeArgs {
   const void *q, *k, *v;
   const float2 *lam, *beta;
@@ -53,7 +61,8 @@ struct DecodeArgs {
 };
 
 struct ScanArgs {
-  const void *q, *k, *v;
+  const void *q, *k, *v;   // element strides sqk (q and k) and sv; o dense
+  RowStrides sqk, sv;
   const float2 *lam, *beta;
   float2 *U, *G, *E;
   void* o;
@@ -72,7 +81,8 @@ struct ScanArgs {
 // U1/G1/E1: final state or NULL.  o NULL: state only.  accumulate: add to the values already
 // in o (in o's dtype).
 struct ChunkPrefillArgs {
-  const void *q, *k, *v;
+  const void *q, *k, *v;   // element strides sqk (q and k) and sv; o dense
+  RowStrides sqk, sv;
   const float2 *lam, *beta;
   void* o;
   int accumulate;

@@ -259,6 +259,7 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
 
 // Token-sequential prefill (the fp32 path).  grid = B*H; one workgroup walks all N tokens of
 // its slice, in reverse when `reverse` is set (then token t of the walk is position N-1-t).
+// q, k and v are addressed through their element strides sqk, sv; o is dense.
 // o (out dtype) receives value, or o + value with `accumulate` (the second direction of the
 // bidirectional layer adds onto the first); o may be NULL (state only).
 __global__ void __launch_bounds__(kStepThreads)
@@ -267,7 +268,8 @@ scan_prefill_kernel(const void* __restrict__ q, const void* __restrict__ k,
                     const float2* __restrict__ beta, float2* __restrict__ U,
                     float2* __restrict__ G, float2* __restrict__ E, void* __restrict__ o,
                     int accumulate, int N, int H, int F, int D, int M,
-                    int in_bf16, int out_bf16, float clamp, int reverse) {
+                    int in_bf16, int out_bf16, float clamp, int reverse, RowStrides sqk,
+                    RowStrides sv) {
   __shared__ StepSmem s;
   const int bh = blockIdx.x;
   const int b = bh / H, h = bh % H;
@@ -278,7 +280,8 @@ scan_prefill_kernel(const void* __restrict__ q, const void* __restrict__ k,
   for (int t = 0; t < N; ++t) {
     const int pos = reverse ? N - 1 - t : t;
     const size_t tok = ((size_t)b * N + pos) * H + h;
-    load_token(s, q, k, v, tok * F, tok * D, F, D, in_bf16);
+    load_token(s, q, k, v, (size_t)(b * sqk.b + pos * sqk.n + h * sqk.h),
+               (size_t)(b * sv.b + pos * sv.n + h * sv.h), F, D, in_bf16);
     __syncthreads();
     step_one(s, Ub, Gb, Eb, F, D, M);
     if (o) {
@@ -372,7 +375,7 @@ hipError_t launch_scan_prefill(const ScanArgs& a, hipStream_t st) {
   prof_begin(st);
   hipLaunchKernelGGL(scan_prefill_kernel, dim3(a.B * a.H), dim3(kStepThreads), 0, st, a.q,
                      a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.accumulate, a.N, a.H, a.F, a.D,
-                     a.M, a.in_bf16, a.out_bf16, a.clamp, a.reverse);
+                     a.M, a.in_bf16, a.out_bf16, a.clamp, a.reverse, a.sqk, a.sv);
   prof_end(st, kKindScan);
   return hipGetLastError();
 }

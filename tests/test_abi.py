@@ -157,3 +157,53 @@ def test_check_lambda_host():
     with pytest.raises(ia.IAError):
         ia.ia_check_lambda(desc(H=1, M=16), mid)
     ia.ia_check_lambda(desc(H=1, M=16, chunk=32), mid)
+
+
+def prefill_strided(d, strides, **kw):
+    """ia_prefill_fwd_strided with the fake addresses of prefill(); strides = 3 (b, n, h)
+    triples for q, k, v, or None."""
+    st = None
+    if strides is not None:
+        st = ((ctypes.c_longlong * 3) * 3)()
+        for i in range(3):
+            for j in range(3):
+                st[i][j] = strides[i][j]
+    a = dict(q=addr(0), k=addr(1), v=addr(2), lam=addr(3), beta=addr(4), st=state(), o=addr(5),
+             ws=addr(6), ws_bytes=1 << 40)
+    a.update(kw)
+    return ia.lib.ia_prefill_fwd_strided(ctypes.byref(d), a["q"], a["k"], a["v"],
+                                         ctypes.byref(st) if st is not None else None,
+                                         a["lam"], a["beta"], a["st"], a["o"], a["ws"],
+                                         a["ws_bytes"], None)
+
+
+def test_strided_validation():
+    """Each case fails validation (nothing is launched on the fake addresses)."""
+    d = desc()                                   # B=2, H=3, N=70, F=32, Dv=16, bf16 inputs
+    qk, vv = (70 * 3 * 32, 3 * 32, 32), (70 * 3 * 16, 3 * 16, 16)
+    fused = (70 * 3 * 96, 3 * 96, 32)            # views of a [B][N][3][H][F] projection
+    # the dense strides pass validation as ia_prefill_fwd does: same errors as there
+    assert prefill_strided(d, [qk, qk, vv], q=P(0)) == 1
+    assert prefill_strided(d, None, q=P(0)) == 1
+    assert prefill_strided(d, [fused, fused, vv], o=addr(5, 8)) == 4
+    # a stride <= 0
+    for i in range(3):
+        for j in range(3):
+            bad = [list(qk), list(qk), list(vv)]
+            bad[i][j] = 0 if j else -bad[i][j]
+            if i < 2:
+                bad[1 - i][j] = bad[i][j]        # keep q and k equal
+            assert prefill_strided(d, bad) == 2, (i, j)
+    # a stride whose byte size is not a multiple of 16 (bf16: 8 elements)
+    assert prefill_strided(d, [(qk[0], qk[1], 36), (qk[0], qk[1], 36), vv]) == 4
+    assert prefill_strided(d, [qk, qk, (vv[0], 52, vv[2])]) == 4
+    # q and k with different strides
+    assert prefill_strided(d, [qk, fused, vv]) == 7
+    # 64 token rows spanning more than 1 GiB (bf16 chunk path, which needs F = Dv)
+    d2 = desc(Dv=32)
+    big = (1 << 24) + 8
+    assert prefill_strided(d2, [(70 * big, big, 32), (70 * big, big, 32), qk]) == 7
+    assert prefill_strided(d2, [qk, qk, (70 * big, big, 32)]) == 7
+    # an input's strided extent reaching o (v's batch stride spans three address gaps)
+    far = (3 * GAP) // 2 + 64
+    assert prefill_strided(d, [qk, qk, (far, vv[1], vv[2])]) == 5

@@ -245,3 +245,89 @@ def test_workload_caduceus_sampled():
     inp = W.caduceus()
     tag("caduceus bidirectional workload")
     _check_workload("caduceus bidir", _sampled(inp, [(0, 1), (1, 6)], bidir=True))
+
+
+# ---------------------------------------------------------------- strided inputs
+
+def _state_from(inp, B, H, F, M, seed):
+    pre = W.make_inputs(B, H, 12, F, F, M, dtype="bf16", seed=seed)
+    st_ref = oracle.prefill(pre["q"], pre["k"], pre["v"], inp["lam"], inp["beta"], threads=8)[3]
+    return st_ref
+
+
+@pytest.mark.parametrize("plan", [(1, 2, 700, 64, 32), (4, 16, 512, 128, 64)])
+@pytest.mark.parametrize("layout", ["qkv fused", "qk fused, v wide"])
+def test_chunk_strided_inputs(plan, layout):
+    """q, k, v as views (ia_prefill_fwd_strided): "qkv fused" slices one [B][N][3][H][F]
+    projection; "qk fused, v wide" slices q, k from [B][N][2][H][F] and v from the first half
+    of a [B][N][H][2F] tensor (v strides differ from q's).  With an initial state, several
+    segments ((1, 2, 700): carry; (4, 16, 512): Horner).  The strided call equals the dense
+    call on contiguous copies exactly, and the oracle within the bf16 tolerance."""
+    import torch
+    ia = _ia()
+    B, H, N, F, M = plan
+    inp = W.make_inputs(B, H, N, F, F, M, dtype="bf16", seed=401 + N + F)
+    q0, k0, v0 = (dev(inp[n], torch.bfloat16) for n in "qkv")
+    if layout == "qkv fused":
+        fused = torch.stack([q0, k0, v0], dim=2)                  # [B, N, 3, H, F]
+        q, k, v = fused[:, :, 0], fused[:, :, 1], fused[:, :, 2]
+    else:
+        fused = torch.stack([q0, k0], dim=2)                      # [B, N, 2, H, F]
+        q, k = fused[:, :, 0], fused[:, :, 1]
+        wide = torch.cat([v0, torch.zeros_like(v0)], dim=3)      # [B, N, H, 2F]
+        v = wide[..., :F]
+    assert not (q.is_contiguous() or k.is_contiguous() or v.is_contiguous())
+    st_ref = _state_from(inp, B, H, F, M, seed=402)
+    st_s = tuple(dev(s) for s in st_ref)
+    st_d = tuple(dev(s) for s in st_ref)
+    st_in = tuple(host(s) for s in st_s)
+    lam, beta = dev(inp["lam"]), dev(inp["beta"])
+    tag(f"strided prefill ({layout}) B={B} H={H} N={N} F={F} M={M}")
+    o_s = ia.prefill(q, k, v, lam, beta, state=st_s, out_dtype=torch.float32)
+    o_d = ia.prefill(q0, k0, v0, lam, beta, state=st_d, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o_d)
+    assert all(torch.equal(a, b) for a, b in zip(st_s, st_d))
+    o_ref, _, _, st_out = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"],
+                                         state=st_in, threads=8)
+    e_o = rowrel(host(o_s), o_ref)
+    e_s = state_rel(tuple(host(s) for s in st_s), st_out)
+    report(f"strided ({layout}) {plan} output", e_o)
+    report(f"strided ({layout}) {plan} state", e_s)
+    assert e_o < TOL_BF16 and e_s < TOL_BF16
+
+
+def test_strided_inputs_bidirectional_and_fp32():
+    """Strided views through the reverse walk (bidirectional, bf16) and through the
+    token-sequential fp32 path: equal to the dense calls, near the oracle."""
+    import torch
+    from helpers import TOL_F32
+    ia = _ia()
+    B, H, N, F, M = 1, 3, 333, 32, 32
+    inp = W.make_inputs(B, H, N, F, F, M, dtype="bf16", seed=91)
+    lam, beta = dev(inp["lam"]), dev(inp["beta"])
+    q0, k0, v0 = (dev(inp[n], torch.bfloat16) for n in "qkv")
+    fused = torch.stack([q0, k0, v0], dim=2)
+    tag("strided bidirectional")
+    o_s = ia.prefill(fused[:, :, 0], fused[:, :, 1], fused[:, :, 2], lam, beta, bidir=True,
+                     out_dtype=torch.float32)
+    o_d = ia.prefill(q0, k0, v0, lam, beta, bidir=True, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o_d)
+    err = rowrel(host(o_s), oracle.bidir(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"]))
+    report("strided bidir", err)
+    assert err < TOL_BF16
+
+    inp = W.make_inputs(1, 2, 150, 32, 32, 16, dtype="f32", seed=92)
+    lam, beta = dev(inp["lam"]), dev(inp["beta"])
+    q0, k0, v0 = (dev(inp[n]) for n in "qkv")
+    fused = torch.stack([q0, k0, v0], dim=2)
+    tag("strided fp32 prefill")
+    o_s = ia.prefill(fused[:, :, 0], fused[:, :, 1], fused[:, :, 2], lam, beta)
+    o_d = ia.prefill(q0, k0, v0, lam, beta)
+    torch.cuda.synchronize()
+    assert torch.equal(o_s, o_d)
+    err = rowrel(host(o_s), oracle.prefill(inp["q"], inp["k"], inp["v"], inp["lam"],
+                                           inp["beta"])[0])
+    report("strided fp32", err)
+    assert err < TOL_F32
