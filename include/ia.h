@@ -73,6 +73,15 @@ typedef enum { IA_F32 = 0, IA_BF16 = 1 } ia_dtype;
  * [summary §5.2, §A.1] run the token mixer over the sequence and its reversal). */
 #define IA_FLAG_BIDIR 1u
 
+/* Readout without the normaliser: o = Re(phi(q) U^T Gamma), no division by Re(phi(q) U^T eta)
+ * and no clamp (the practical readout that drops the denominator [summary §3.1]).  Prefill
+ * (either direction) and decode. */
+#define IA_FLAG_NO_DEN 2u
+
+/* q and k already hold features: no feature map is applied (phi = identity), for callers that
+ * form phi(q), phi(k) themselves.  Prefill and decode. */
+#define IA_FLAG_IDENTITY_FEATURES 4u
+
 typedef struct ia_desc {
   int B;             /* batch rows */
   int H;             /* heads */
@@ -86,7 +95,8 @@ typedef struct ia_desc {
   int out_dtype;     /* ia_dtype of o */
   float den_clamp;   /* lower clamp of Re(den); finite and > 0 (the method uses 1e-6), else
                         IA_ERR_DOMAIN */
-  unsigned flags;    /* IA_FLAG_BIDIR or 0; other bits: IA_ERR_UNSUPPORTED */
+  unsigned flags;    /* IA_FLAG_BIDIR | IA_FLAG_NO_DEN | IA_FLAG_IDENTITY_FEATURES, or 0; other
+                        bits: IA_ERR_UNSUPPORTED */
   int chunk;         /* chunk length of the chunked prefill: 0 (= 64 [summary §A.2]), 32 or
                         64; other values: IA_ERR_UNSUPPORTED */
 } ia_desc;

@@ -31,6 +31,8 @@ LIB_PATH = os.path.join(_HERE, "libia.so")
 
 IA_F32, IA_BF16 = 0, 1
 IA_FLAG_BIDIR = 1
+IA_FLAG_NO_DEN = 2
+IA_FLAG_IDENTITY_FEATURES = 4
 STATUS = ["IA_OK", "IA_ERR_NULL", "IA_ERR_SHAPE", "IA_ERR_DTYPE", "IA_ERR_ALIGN",
           "IA_ERR_ALIAS", "IA_ERR_DOMAIN", "IA_ERR_UNSUPPORTED", "IA_ERR_LAUNCH",
           "IA_ERR_WORKSPACE"]
@@ -99,9 +101,10 @@ KIND_NAMES = {0: "fill", 1: "scan", 2: "tables", 3: "summary", 4: "carry", 5: "c
 
 
 def make_desc(B, H, N, F, Dv, M, in_dtype=IA_BF16, out_dtype=IA_F32, den_clamp=1e-6,
-              bidir=False, chunk=0) -> IADesc:
-    return IADesc(B, H, N, F, Dv, M, in_dtype, out_dtype, den_clamp,
-                  IA_FLAG_BIDIR if bidir else 0, chunk)
+              bidir=False, chunk=0, no_den=False, identity_features=False) -> IADesc:
+    flags = ((IA_FLAG_BIDIR if bidir else 0) | (IA_FLAG_NO_DEN if no_den else 0)
+             | (IA_FLAG_IDENTITY_FEATURES if identity_features else 0))
+    return IADesc(B, H, N, F, Dv, M, in_dtype, out_dtype, den_clamp, flags, chunk)
 
 
 def _ptr(t):
@@ -226,7 +229,8 @@ def new_state(B, H, M, F, Dv, device="cuda", stream=None, zero=True):
 
 
 def prefill(q, k, v, lam, beta, state=None, out_dtype=None, bidir=False, chunk=0,
-            den_clamp=1e-6, want_output=True, stream=None, workspace=None):
+            den_clamp=1e-6, want_output=True, stream=None, workspace=None, no_den=False,
+            identity_features=False):
     """Allocate o (and the workspace) with torch and run ia_prefill_fwd (or, for strided
     views q, k, v, ia_prefill_fwd_strided); returns o."""
     import torch
@@ -234,7 +238,7 @@ def prefill(q, k, v, lam, beta, state=None, out_dtype=None, bidir=False, chunk=0
     Dv, M = v.shape[3], lam.shape[1]
     out_dtype = q.dtype if out_dtype is None else out_dtype
     desc = make_desc(B, H, N, F, Dv, M, dtype_code(q.dtype), dtype_code(out_dtype), den_clamp,
-                     bidir, chunk)
+                     bidir, chunk, no_den, identity_features)
     o = torch.empty((B, N, H, Dv), dtype=out_dtype, device=q.device) if want_output else None
     if workspace is None:
         nb = ia_prefill_workspace_bytes(desc)
@@ -247,13 +251,14 @@ def prefill(q, k, v, lam, beta, state=None, out_dtype=None, bidir=False, chunk=0
 
 
 def decode(q_t, k_t, v_t, lam, beta, state, out_dtype=None,
-           den_clamp=1e-6, stream=None, o_t=None):
+           den_clamp=1e-6, stream=None, o_t=None, no_den=False, identity_features=False):
     """One decode step for every (b,h); allocates o_t unless given; returns o_t."""
     import torch
     B, H, F = q_t.shape
     Dv, M = v_t.shape[2], lam.shape[1]
     out_dtype = torch.float32 if out_dtype is None else out_dtype
-    desc = make_desc(B, H, 1, F, Dv, M, dtype_code(q_t.dtype), dtype_code(out_dtype), den_clamp)
+    desc = make_desc(B, H, 1, F, Dv, M, dtype_code(q_t.dtype), dtype_code(out_dtype), den_clamp,
+                     no_den=no_den, identity_features=identity_features)
     if o_t is None:
         o_t = torch.empty((B, H, Dv), dtype=out_dtype, device=q_t.device)
     ia_decode_step(desc, q_t, k_t, v_t, lam, beta, state, o_t, stream)

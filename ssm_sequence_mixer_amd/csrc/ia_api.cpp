@@ -38,7 +38,8 @@ ia_status check_desc(const ia_desc* d, bool need_n) {
       (d->out_dtype != IA_F32 && d->out_dtype != IA_BF16))
     return IA_ERR_DTYPE;
   if (!(std::isfinite(d->den_clamp) && d->den_clamp > 0.f)) return IA_ERR_DOMAIN;
-  if (d->flags & ~IA_FLAG_BIDIR) return IA_ERR_UNSUPPORTED;
+  if (d->flags & ~(IA_FLAG_BIDIR | IA_FLAG_NO_DEN | IA_FLAG_IDENTITY_FEATURES))
+    return IA_ERR_UNSUPPORTED;
   if (d->chunk != 0 && d->chunk != 32 && d->chunk != 64) return IA_ERR_UNSUPPORTED;
   // Index arithmetic in the kernels is 64-bit for element offsets; keep grid sizes sane.
   const double slices = double(d->B) * d->H;
@@ -89,6 +90,12 @@ struct ChunkPlan {
   int C, G, seg_chunks;
   size_t tables_off, slots_off, bytes;
 };
+
+// Readout options of the desc's flags, in the kernels' encoding.
+int kernel_opt(const ia_desc* d) {
+  return (d->flags & IA_FLAG_NO_DEN ? ia::kOptNoDen : 0) |
+         (d->flags & IA_FLAG_IDENTITY_FEATURES ? ia::kOptIdentity : 0);
+}
 
 bool use_chunk_path(const ia_desc* d) {
   // The chunk kernels address a chunk's token rows with 32-bit byte offsets, rows outside a
@@ -292,6 +299,7 @@ ia_status ia_prefill_fwd_strided(const ia_desc* d, const void* q, const void* k,
     a.seg_chunks = pl.seg_chunks;
     a.out_bf16 = d->out_dtype == IA_BF16;
     a.clamp = d->den_clamp;
+    a.opt = kernel_opt(d);
     if (!bidir) return launch_status(ia::launch_chunk_prefill(a, hs));
     // Bidirectional: the forward direction writes o, the reverse direction adds onto it.
     hipError_t e = ia::launch_chunk_prefill(a, hs);
@@ -329,6 +337,7 @@ ia_status ia_prefill_fwd_strided(const ia_desc* d, const void* q, const void* k,
   ia::ScanArgs a{q, k, v, sq, sv, static_cast<const float2*>(lambda),
                  static_cast<const float2*>(beta), U, G, E, o, 0, d->B, d->H, d->N, d->F, d->Dv,
                  d->M, d->in_dtype == IA_BF16, d->out_dtype == IA_BF16, d->den_clamp, 0};
+  a.opt = kernel_opt(d);
   if (!bidir) return launch_status(ia::launch_scan_prefill(a, hs));
 
   // Bidirectional: the forward direction writes o, the reverse direction (from a zero state
@@ -371,6 +380,7 @@ ia_status ia_decode_step(const ia_desc* d, const void* q_t, const void* k_t, con
                    static_cast<float2*>(st->Gamma), static_cast<float2*>(st->eta), o_t,
                    d->B, d->H, d->F, d->Dv, d->M, d->in_dtype == IA_BF16,
                    d->out_dtype == IA_BF16, d->den_clamp};
+  a.opt = kernel_opt(d);
   return launch_status(ia::launch_decode_step(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -310,6 +310,9 @@ hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
   a.dir = p.reverse;
   a.out_bf16 = p.out_bf16;
   a.clamp = p.clamp;
+  a.opt = p.opt;
+  a.den_w = (p.opt & kOptNoDen) ? 0.f : 1.f;
+  a.den_c = (p.opt & kOptNoDen) ? 1.f : p.clamp;
   a.slot_floats = chunk_slot_floats(p.F, p.D, p.M);
   a.slots_per_seq = G - 1;
   a.tables = p.tables;

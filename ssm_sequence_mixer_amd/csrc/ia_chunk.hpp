@@ -309,6 +309,8 @@ struct ChunkArgs {
   int dir;                     // 1: the walk runs from position N-1 down to 0
   int out_bf16;
   float clamp;
+  int opt;                     // kOptNoDen | kOptIdentity
+  float den_w, den_c;          // 1 and clamp; with kOptNoDen 0 and 1 (the readout divisor)
   // Initial state of segment g: the caller's state init0 (or zeros) carried across segments
   // 0..g-1, whose end states (each computed from a zero state) are the workspace slots
   // seg_prev[seq][0..g-1]: state <- lam^Ls state + slot, Ls the segment length (with
@@ -357,22 +359,21 @@ struct TableLayout {
 // no index stride; offsets at or past the range read as zeros.
 constexpr int kBufferFlags = 0x00020000;
 
-// The L valid token rows of chunk c (C tokens) of sequence (b, h) in a bf16 tensor with
-// element strides s (token rows s.n apart) as a buffer: based at the lowest-addressed valid
-// row (row 0 walking forward, row L-1 walking backward), L row strides long.  Row r (walk
-// order) column e lies at row_off(r, e) - shift; rows at or past the sequence end fall
-// outside the range (past its end forward, below its base, wrapping to large offsets,
-// backward) and read as zeros.  (C s.n 2 bytes fit 32 bits; the host checks.)
+// The L valid token rows of chunk c (C tokens) of one sequence of a bf16 tensor, whose token
+// 0 is at `seq` and whose token rows are sn elements apart, as a buffer: based at the
+// lowest-addressed valid row (row 0 walking forward, row L-1 walking backward), L row strides
+// long.  Row r (walk order) column e lies at row_off(r, e) - shift; rows at or past the
+// sequence end fall outside the range (past its end forward, below its base, wrapping to
+// large offsets, backward) and read as zeros.  (C sn 2 bytes fit 32 bits; the host checks.)
 template <int C>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rows(const ChunkArgs& a,
-                                                             const RowStrides& s, int b, int h,
-                                                             const uint16_t* t, int c,
-                                                             uint32_t& shift) {
+                                                             const uint16_t* seq, int sn,
+                                                             int c, uint32_t& shift) {
   const int L = min(C, a.N - c * C);
-  const uint32_t stride = (uint32_t)s.n * 2u;
+  const uint32_t stride = (uint32_t)sn * 2u;
   shift = a.dir ? (uint32_t)(C - L) * stride : 0u;
   const int pos = a.dir ? a.N - c * C - L : c * C;
-  const uint16_t* p = t + b * s.b + (long long)pos * s.n + h * s.h;
+  const uint16_t* p = seq + (long long)pos * sn;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p), (short)0,
                                            (int)((uint32_t)L * stride), kBufferFlags);
 }
@@ -380,9 +381,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rows(const ChunkArgs& a,
 // Byte offset of chunk row r (0 = the chunk's first token in walk order), column e, from the
 // lowest-addressed row of a full chunk.
 template <int C>
-__device__ __forceinline__ uint32_t row_off(const ChunkArgs& a, const RowStrides& s, int r,
-                                            int e) {
-  return (uint32_t)((a.dir ? C - 1 - r : r) * (uint32_t)s.n + e) * 2u;
+__device__ __forceinline__ uint32_t row_off(const ChunkArgs& a, int sn, int r, int e) {
+  return (uint32_t)((a.dir ? C - 1 - r : r) * (uint32_t)sn + e) * 2u;
 }
 
 // Per-workgroup context shared by the two wave roles.
@@ -400,12 +400,15 @@ struct Ctx {
   __device__ size_t tok_index(const ChunkArgs& a, int pos) const {
     return ((size_t)b * a.N + pos) * a.H + h;
   }
-  __device__ __amdgpu_buffer_rsrc_t chunk_rows(const ChunkArgs& a, const RowStrides& s,
-                                               const uint16_t* t, int c, uint32_t& shift) const {
-    return ia::chunk_rows<C>(a, s, b, h, t, c, shift);
+  // This sequence's token 0 in q, k and v, and their token-row strides (elements).
+  const uint16_t *q0, *k0, *v0;
+  int snqk, snv;
+  __device__ __amdgpu_buffer_rsrc_t chunk_rows(const ChunkArgs& a, const uint16_t* seq, int sn,
+                                               int c, uint32_t& shift) const {
+    return ia::chunk_rows<C>(a, seq, sn, c, shift);
   }
-  __device__ static uint32_t row_off(const ChunkArgs& a, const RowStrides& s, int r, int e) {
-    return ia::row_off<C>(a, s, r, e);
+  __device__ static uint32_t row_off(const ChunkArgs& a, int sn, int r, int e) {
+    return ia::row_off<C>(a, sn, r, e);
   }
 };
 
@@ -485,11 +488,11 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
   int stV[NV];
 #pragma unroll
   for (int t = 0; t < NV; ++t) stV[t] = opaque(Lay::oV + soff<D>(16 * r + il, 8 * (g + 4 * t)));
-  const uint32_t lofV = x.row_off(a, a.sv, 16 * r + il, 8 * g);
+  const uint32_t lofV = x.row_off(a, x.snv, 16 * r + il, 8 * g);
   uint4 rv[NV];
   auto fetch_v = [&](int c) {   // rows past N read as zeros
     uint32_t shift;
-    const __amdgpu_buffer_rsrc_t vb = x.chunk_rows(a, a.sv, a.v, c, shift);
+    const __amdgpu_buffer_rsrc_t vb = x.chunk_rows(a, x.v0, x.snv, c, shift);
 #pragma unroll
     for (int t = 0; t < NV; ++t) rv[t] = load16(vb, lofV - shift + 64 * t);
   };
@@ -629,7 +632,9 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
       }
       den_intra = xor_sum16_32(den_intra);
       const float den = den_intra + si * den_inter;   // in units of si
-      const float rd = 1.f / clamp_den(den, si * a.clamp);
+      // num and den are in units of si (the fp16 scale of A).  Without a denominator
+      // (kOptNoDen) den_w = 0 and den_c = 1: the divisor is max(0, si) = si and o = num.
+      const float rd = 1.f / clamp_den(den * a.den_w, si * a.den_c);
       bf16x8 Pf[KC];
 #pragma unroll
       for (int kb = 0; kb < KC; ++kb) Pf[kb] = pack_bf16(accP[2 * kb], accP[2 * kb + 1]);
@@ -749,7 +754,7 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
   uint32_t lofF[NLF];
 #pragma unroll
   for (int t = 0; t < NLF; ++t)
-    lofF[t] = x.row_off(a, a.sqk, rowF0 + t * (NL / VF), 8 * (n0 % VF));
+    lofF[t] = x.row_off(a, x.snqk, rowF0 + t * (NL / VF), 8 * (n0 % VF));
   // LDS rows row0 + t NL/VF share the swizzle of row0 (NL/VF is a multiple of 16).
   static_assert((NL / VF) % 16 == 0, "loader rows keep the swizzle");
   const int stF = opaque(Lay::oFk + soff<F>(rowF0, 8 * (n0 % VF)));
@@ -757,22 +762,24 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
   uint4 rq[NLF], rk[NLF];
   auto fetch = [&](int c) {   // rows past N (and past the chunk) read as zeros
     uint32_t shift;
-    const __amdgpu_buffer_rsrc_t kb = x.chunk_rows(a, a.sqk, a.k, c, shift);
-    const __amdgpu_buffer_rsrc_t qb = x.chunk_rows(a, a.sqk, a.q, c, shift);
+    const __amdgpu_buffer_rsrc_t kb = x.chunk_rows(a, x.k0, x.snqk, c, shift);
+    const __amdgpu_buffer_rsrc_t qb = x.chunk_rows(a, x.q0, x.snqk, c, shift);
 #pragma unroll
     for (int t = 0; t < NLF; ++t) {
       rk[t] = load16(kb, lofF[t] - shift);
       if (x.want_out) rq[t] = load16(qb, lofF[t] - shift);
     }
   };
-  // Features in place.  Rows past N get zero features (not phi(0)); their values are zero.
+  // Features in place (the values themselves with kOptIdentity).  Rows past N get zero
+  // features (not phi(0)); their values are zero.
+  const float fT = feature_t(a.opt), fC = feature_c(a.opt);
   auto phi8 = [&](uint4& r, bool ok) {
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
     uint32_t o[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)   // bf16 pair -> two floats -> features -> bf16 pair
-      o[i] = pk_bf16(feature(__uint_as_float(w[i] << 16)),
-                     feature(__uint_as_float(w[i] & 0xffff0000u)));
+      o[i] = pk_bf16(feature_tc(__uint_as_float(w[i] << 16), fT, fC),
+                     feature_tc(__uint_as_float(w[i] & 0xffff0000u), fT, fC));
     r = ok ? make_uint4(o[0], o[1], o[2], o[3]) : make_uint4(0, 0, 0, 0);
   };
   auto convert = [&](int c) {
@@ -1169,6 +1176,11 @@ chunk_prefill_kernel(const ChunkArgs a) {
   x.seg = a.seg_first + blockIdx.x % a.n_seg;
   x.b = x.seq / a.H;
   x.h = x.seq % a.H;
+  x.q0 = a.q + x.b * a.sqk.b + x.h * a.sqk.h;
+  x.k0 = a.k + x.b * a.sqk.b + x.h * a.sqk.h;
+  x.v0 = a.v + x.b * a.sv.b + x.h * a.sv.h;
+  x.snqk = (int)a.sqk.n;
+  x.snv = (int)a.sv.n;
   const int n_chunks_total = (a.N + C - 1) / C;
   x.c_begin = x.seg * a.seg_chunks;
   x.c_end = min(x.c_begin + a.seg_chunks, n_chunks_total);

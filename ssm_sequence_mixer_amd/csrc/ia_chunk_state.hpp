@@ -118,7 +118,8 @@ chunk_state_kernel(const ChunkArgs a) {
       rv[r][t] = n0 + NL * t < C * VD ? *reinterpret_cast<const uint4*>(vb + t * stepV)
                                       : make_uint4(0, 0, 0, 0);
   };
-  // phi(k) in place, then both into the stage.
+  // phi(k) in place (k itself with kOptIdentity), then both into the stage.
+  const float fT = feature_t(a.opt), fC = feature_c(a.opt);
   auto write_inputs = [&](auto R, auto S) {
     constexpr int r = decltype(R)::value, so = decltype(S)::value * ST;
 #pragma unroll
@@ -128,8 +129,8 @@ chunk_state_kernel(const ChunkArgs a) {
         uint32_t o[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          o[e] = pk_bf16(feature(__uint_as_float(w[e] << 16)),
-                         feature(__uint_as_float(w[e] & 0xffff0000u)));
+          o[e] = pk_bf16(feature_tc(__uint_as_float(w[e] << 16), fT, fC),
+                         feature_tc(__uint_as_float(w[e] & 0xffff0000u), fT, fC));
         *reinterpret_cast<uint4*>(s16 + stK + so + t * (NL / VF) * F) =
             make_uint4(o[0], o[1], o[2], o[3]);
       }

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ia_kernels.hpp"
+
 namespace ia {
 
 // ---------------------------------------------------------------- scalar conversions
@@ -37,8 +39,25 @@ __device__ __forceinline__ void store_out(void* p, size_t i, float x, int bf16) 
 // Feature map of the layer: elu(x) + 1 (x + 1 above zero, exp(x) at or below).
 __device__ __forceinline__ float feature(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
+// The feature map as x > t ? x + c : exp(x), with (t, c) uniform: (0, 1) is elu(x)+1 and
+// (-inf, 0) the identity (kOptIdentity), the same instructions for both.
+__device__ __forceinline__ float feature_tc(float x, float t, float c) {
+  return x > t ? x + c : __expf(x);
+}
+__device__ __forceinline__ float feature_t(int opt) { return (opt & kOptIdentity) ? -INFINITY : 0.f; }
+__device__ __forceinline__ float feature_c(int opt) { return (opt & kOptIdentity) ? 0.f : 1.f; }
+
+// Feature map, or none with kOptIdentity (ia_kernels.hpp).
+__device__ __forceinline__ float feat(float x, int opt) {
+  return (opt & kOptIdentity) ? x : feature(x);
+}
+
 // Denominator clamp: one-sided, NaN passes through unchanged.
 __device__ __forceinline__ float clamp_den(float d, float c) { return d < c ? c : d; }
+// Output of a readout: num / max(den, clamp), or num with kOptNoDen.
+__device__ __forceinline__ float readout(float num, float den, float clamp, int opt) {
+  return (opt & kOptNoDen) ? num : num / clamp_den(den, clamp);
+}
 
 // ---------------------------------------------------------------- complex (float2)
 

@@ -42,6 +42,10 @@ inline void prof_end(hipStream_t st, int kind) {
 constexpr int kMaxDim = 256;    // largest F and Dv
 constexpr int kMaxModes = 128;  // largest M
 
+// Readout options (the desc's flags, as kernels take them): kOptNoDen, o = Re num with no
+// denominator; kOptIdentity, q and k arrive as features (no feature map).
+constexpr int kOptNoDen = 1, kOptIdentity = 2;
+
 // Element strides of a [B][N][H][X] tensor along b, n and h (X contiguous).
 struct RowStrides {
   long long b, n, h;
@@ -58,6 +62,7 @@ struct DecodeArgs {
   int B, H, F, D, M;
   int in_bf16, out_bf16;
   float clamp;
+  int opt;   // kOptNoDen | kOptIdentity
 };
 
 struct ScanArgs {
@@ -71,6 +76,7 @@ struct ScanArgs {
   int in_bf16, out_bf16;
   float clamp;
   int reverse;
+  int opt;   // kOptNoDen | kOptIdentity
 };
 
 // Chunked MFMA prefill of one direction (bf16 inputs).  The sequence is cut into `segments`
@@ -94,6 +100,7 @@ struct ChunkPrefillArgs {
   int chunk, segments, seg_chunks;
   int reverse, out_bf16;
   float clamp;
+  int opt;   // kOptNoDen | kOptIdentity
 };
 
 bool chunk_supported(int F, int D, int M);

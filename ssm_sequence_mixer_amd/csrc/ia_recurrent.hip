@@ -107,10 +107,10 @@ __device__ __forceinline__ void step_one(StepSmem& s, float2* __restrict__ U,
 // Load phi(q), phi(k), v of one token into shared memory.
 __device__ __forceinline__ void load_token(StepSmem& s, const void* q, const void* k,
                                            const void* v, size_t qk_off, size_t v_off, int F,
-                                           int D, int bf16) {
+                                           int D, int bf16, int opt) {
   for (int i = threadIdx.x; i < F; i += kStepThreads) {
-    s.fq[i] = feature(load_in(q, qk_off + i, bf16));
-    s.fk[i] = feature(load_in(k, qk_off + i, bf16));
+    s.fq[i] = feat(load_in(q, qk_off + i, bf16), opt);
+    s.fk[i] = feat(load_in(k, qk_off + i, bf16), opt);
   }
   for (int i = threadIdx.x; i < D; i += kStepThreads) s.v[i] = load_in(v, v_off + i, bf16);
 }
@@ -131,20 +131,20 @@ decode_step_kernel(const void* __restrict__ q, const void* __restrict__ k,
                    const void* __restrict__ v, const float2* __restrict__ lam,
                    const float2* __restrict__ beta, float2* __restrict__ U,
                    float2* __restrict__ G, float2* __restrict__ E, void* __restrict__ o,
-                   int H, int F, int D, int M, int in_bf16, int out_bf16, float clamp) {
+                   int H, int F, int D, int M, int in_bf16, int out_bf16, float clamp,
+                   int opt) {
   __shared__ StepSmem s;
   const int bh = blockIdx.x;
   const int h = bh % H;
   load_modes(s, lam, beta, h, M);
-  load_token(s, q, k, v, (size_t)bh * F, (size_t)bh * D, F, D, in_bf16);
+  load_token(s, q, k, v, (size_t)bh * F, (size_t)bh * D, F, D, in_bf16, opt);
   __syncthreads();
   step_one(s, U + (size_t)bh * M * F, G + (size_t)bh * M * D, E + (size_t)bh * M, F, D, M);
-  const float den = clamp_den(s.den[0], clamp);
   for (int j = threadIdx.x; j < D; j += kStepThreads) {
     float n = 0.f;
 #pragma unroll
     for (int w = 0; w < kStepWaves; ++w) n += s.num[w][j];
-    store_out(o, (size_t)bh * D + j, n / den, out_bf16);
+    store_out(o, (size_t)bh * D + j, readout(n, s.den[0], clamp, opt), out_bf16);
   }
 }
 
@@ -160,7 +160,7 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
                         const void* __restrict__ v, const float2* __restrict__ lam,
                         const float2* __restrict__ beta, float2* __restrict__ U,
                         float2* __restrict__ G, float2* __restrict__ E, void* __restrict__ o,
-                        int H, int M, int in_bf16, int out_bf16, float clamp) {
+                        int H, int M, int in_bf16, int out_bf16, float clamp, int opt) {
   constexpr int NT = 512, NWV = NT / 64;
   constexpr int RU = F / 2, RD = D / 2;
   static_assert(RU <= 64 && RD <= 64 && NT % RU == 0 && NT % RD == 0, "row width");
@@ -194,10 +194,10 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
     s_beta[tid] = beta[(size_t)h * M + tid];
     e = Eb[tid];
   }
-  const float fk0 = feature(load_in(k, (size_t)bh * F + 2 * pu, in_bf16));
-  const float fk1 = feature(load_in(k, (size_t)bh * F + 2 * pu + 1, in_bf16));
-  const float fq0 = feature(load_in(q, (size_t)bh * F + 2 * pu, in_bf16));
-  const float fq1 = feature(load_in(q, (size_t)bh * F + 2 * pu + 1, in_bf16));
+  const float fk0 = feat(load_in(k, (size_t)bh * F + 2 * pu, in_bf16), opt);
+  const float fk1 = feat(load_in(k, (size_t)bh * F + 2 * pu + 1, in_bf16), opt);
+  const float fq0 = feat(load_in(q, (size_t)bh * F + 2 * pu, in_bf16), opt);
+  const float fq1 = feat(load_in(q, (size_t)bh * F + 2 * pu + 1, in_bf16), opt);
   const float v0 = load_in(v, (size_t)bh * D + 2 * pd, in_bf16);
   const float v1 = load_in(v, (size_t)bh * D + 2 * pd + 1, in_bf16);
   __syncthreads();   // lam, beta
@@ -253,7 +253,7 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
     float den = 0.f;
 #pragma unroll
     for (int w = 0; w < NWV; ++w) den += s_den[w];
-    store_out(o, (size_t)bh * D + tid, n / clamp_den(den, clamp), out_bf16);
+    store_out(o, (size_t)bh * D + tid, readout(n, den, clamp, opt), out_bf16);
   }
 }
 
@@ -269,7 +269,7 @@ scan_prefill_kernel(const void* __restrict__ q, const void* __restrict__ k,
                     float2* __restrict__ G, float2* __restrict__ E, void* __restrict__ o,
                     int accumulate, int N, int H, int F, int D, int M,
                     int in_bf16, int out_bf16, float clamp, int reverse, RowStrides sqk,
-                    RowStrides sv) {
+                    RowStrides sv, int opt) {
   __shared__ StepSmem s;
   const int bh = blockIdx.x;
   const int b = bh / H, h = bh % H;
@@ -281,16 +281,15 @@ scan_prefill_kernel(const void* __restrict__ q, const void* __restrict__ k,
     const int pos = reverse ? N - 1 - t : t;
     const size_t tok = ((size_t)b * N + pos) * H + h;
     load_token(s, q, k, v, (size_t)(b * sqk.b + pos * sqk.n + h * sqk.h),
-               (size_t)(b * sv.b + pos * sv.n + h * sv.h), F, D, in_bf16);
+               (size_t)(b * sv.b + pos * sv.n + h * sv.h), F, D, in_bf16, opt);
     __syncthreads();
     step_one(s, Ub, Gb, Eb, F, D, M);
     if (o) {
-      const float den = clamp_den(s.den[0], clamp);
       for (int j = threadIdx.x; j < D; j += kStepThreads) {
         float n = 0.f;
 #pragma unroll
         for (int w = 0; w < kStepWaves; ++w) n += s.num[w][j];
-        float val = n / den;
+        float val = readout(n, s.den[0], clamp, opt);
         if (accumulate) val += load_in(o, tok * D + j, out_bf16);
         store_out(o, tok * D + j, val, out_bf16);
       }
@@ -327,11 +326,11 @@ static void launch_decode_rows(const DecodeArgs& a, hipStream_t st) {
   if (a.M <= 64)
     hipLaunchKernelGGL((decode_step_rows_kernel<F, D, 64>), dim3(a.B * a.H), dim3(512), 0, st,
                        a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H, a.M, a.in_bf16,
-                       a.out_bf16, a.clamp);
+                       a.out_bf16, a.clamp, a.opt);
   else
     hipLaunchKernelGGL((decode_step_rows_kernel<F, D, kMaxModes>), dim3(a.B * a.H), dim3(512),
                        0, st, a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H, a.M,
-                       a.in_bf16, a.out_bf16, a.clamp);
+                       a.in_bf16, a.out_bf16, a.clamp, a.opt);
 }
 
 // Compute units of the current device (cached per device; 256 when there is none).
@@ -365,7 +364,7 @@ hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t st) {
 #undef IA_DEC
   hipLaunchKernelGGL(decode_step_kernel, dim3(a.B * a.H), dim3(kStepThreads), 0, st, a.q, a.k,
                      a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H, a.F, a.D, a.M, a.in_bf16,
-                     a.out_bf16, a.clamp);
+                     a.out_bf16, a.clamp, a.opt);
   prof_end(st, kKindDecode);
   return hipGetLastError();
 }
@@ -375,7 +374,7 @@ hipError_t launch_scan_prefill(const ScanArgs& a, hipStream_t st) {
   prof_begin(st);
   hipLaunchKernelGGL(scan_prefill_kernel, dim3(a.B * a.H), dim3(kStepThreads), 0, st, a.q,
                      a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.accumulate, a.N, a.H, a.F, a.D,
-                     a.M, a.in_bf16, a.out_bf16, a.clamp, a.reverse, a.sqk, a.sv);
+                     a.M, a.in_bf16, a.out_bf16, a.clamp, a.reverse, a.sqk, a.sv, a.opt);
   prof_end(st, kKindScan);
   return hipGetLastError();
 }
