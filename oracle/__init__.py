@@ -11,6 +11,10 @@ Two independent implementations live here:
   loop over slices and marshal arrays.
 * ``brute.py``: the explicit double sum over s <= t and modes m, in numpy, for tiny inputs.
 
+``scan_bwd``/``prefill_bwd`` give the gradients of the same layer (``ia_oracle_scan_bwd``:
+reverse-mode differentiation of the recurrence, every forward state kept), pinned to the
+forward oracle by finite differences in ``tests/test_oracle_bwd.py``.
+
 The method both follow is stated in the header of ``ia_oracle.c``; the sources are the two
 pages titled "Interdomain Attention: Beyond Token-Level Key-Value Memory" (the paper summary
 page, sections 3.1-3.2, and the AI Radio episode page, "Key Components and Derivation").
@@ -45,6 +49,9 @@ def load_library(path):
     lib.ia_oracle_scan.restype = ctypes.c_int
     lib.ia_oracle_scan.argtypes = [ctypes.c_int] * 4 + [dp] * 5 + [dp] * 3 + [dp] * 3 + [
         ctypes.c_double]
+    lib.ia_oracle_scan_bwd.restype = ctypes.c_int
+    lib.ia_oracle_scan_bwd.argtypes = [ctypes.c_int] * 4 + [dp] * 5 + [dp] * 3 + [
+        dp, ctypes.c_double, ctypes.c_int] + [dp] * 5 + [dp] * 3 + [dp]
     return lib
 
 
@@ -157,3 +164,73 @@ def bidir(q, k, v, lam, beta, clamp=1e-6, slices=None, threads=1):
     fl = lambda a: np.ascontiguousarray(np.asarray(a)[:, ::-1])
     rev = prefill(fl(q), fl(k), fl(v), lam, beta, None, clamp, slices, threads)[0]
     return fwd + rev[:, ::-1]
+
+
+def scan_bwd(q, k, v, lam, beta, dO, state=None, clamp=1e-6, no_den=False, lib=None):
+    """Gradients of one (b,h) slice by reverse-mode differentiation of the recurrence
+    (``ia_oracle_scan_bwd``).  q, k [N,F], v and dO [N,D], lam, beta [M] complex, state as in
+    ``scan``.  Complex gradients are dL/dRe + i dL/dIm.  Returns (dq, dk, dv, dlam, dbeta,
+    (dU0, dG0, de0))."""
+    lib = lib or _load()
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    dO = np.ascontiguousarray(dO, dtype=np.float64)
+    N, F = q.shape
+    D = v.shape[1]
+    M = np.asarray(lam).shape[0]
+    st = [None] * 3 if state is None else [_c2r(x) for x in state]
+    dq, dk = np.empty((N, F)), np.empty((N, F))
+    dv = np.empty((N, D))
+    dl, db = np.empty((M, 2)), np.empty((M, 2))
+    dU, dG, de = np.empty((M, F, 2)), np.empty((M, D, 2)), np.empty((M, 2))
+    work = np.empty((N + 1) * M * (F + D + 1) * 2 + N * M * 2 + N * (D + 1))
+    rc = lib.ia_oracle_scan_bwd(N, F, D, M, _ptr(q), _ptr(k), _ptr(v), _ptr(_c2r(lam)),
+                                _ptr(_c2r(beta)), _ptr(st[0]), _ptr(st[1]), _ptr(st[2]),
+                                _ptr(dO), clamp, int(bool(no_den)), _ptr(dq), _ptr(dk),
+                                _ptr(dv), _ptr(dl), _ptr(db), _ptr(dU), _ptr(dG), _ptr(de),
+                                _ptr(work))
+    if rc != 0:
+        raise MemoryError("ia_oracle_scan_bwd")
+    return dq, dk, dv, _r2c(dl), _r2c(db), (_r2c(dU), _r2c(dG), _r2c(de))
+
+
+def prefill_bwd(q, k, v, lam, beta, dO, state=None, clamp=1e-6, no_den=False, slices=None,
+                threads=1):
+    """Gradients of the causal layer over a batch, slice by slice (``scan_bwd``).
+
+    Shapes as in ``prefill``; dO like o.  Returns (dq, dk, dv, dlam [B,H,M], dbeta [B,H,M],
+    (dU0, dG0, de0)): lambda and beta gradients per slice (a layer's are their sum over b);
+    slices not in ``slices`` are left NaN."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    B, N, H, F = q.shape
+    D = v.shape[3]
+    M = lam.shape[1]
+    dq = np.full((B, N, H, F), np.nan)
+    dk = np.full((B, N, H, F), np.nan)
+    dv = np.full((B, N, H, D), np.nan)
+    dl = np.full((B, H, M), np.nan, dtype=np.complex128)
+    db = np.full((B, H, M), np.nan, dtype=np.complex128)
+    dU = np.full((B, H, M, F), np.nan, dtype=np.complex128)
+    dG = np.full((B, H, M, D), np.nan, dtype=np.complex128)
+    de = np.full((B, H, M), np.nan, dtype=np.complex128)
+    todo = slices if slices is not None else [(b, h) for b in range(B) for h in range(H)]
+
+    def one(bh):
+        b, h = bh
+        st = None if state is None else (state[0][b, h], state[1][b, h], state[2][b, h])
+        return bh, scan_bwd(q[b, :, h], k[b, :, h], v[b, :, h], lam[h], beta[h], dO[b, :, h],
+                            st, clamp, no_den)
+
+    if threads > 1:
+        with ThreadPoolExecutor(threads) as ex:
+            results = list(ex.map(one, todo))
+    else:
+        results = [one(bh) for bh in todo]
+    for (b, h), (a, bk, c, l, be, (u, g, e)) in results:
+        dq[b, :, h], dk[b, :, h], dv[b, :, h] = a, bk, c
+        dl[b, h], db[b, h], dU[b, h], dG[b, h], de[b, h] = l, be, u, g, e
+    return dq, dk, dv, dl, db, (dU, dG, de)

@@ -30,6 +30,7 @@
 #include <complex.h>
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
 
 static double feature(double x) {
   /* elu(x) + 1: x + 1 for x > 0, exp(x) for x <= 0 */
@@ -105,5 +106,169 @@ int ia_oracle_scan(int N, int F, int D, int M,
       if (o) o[(size_t)t * D + j] = n / dc;
     }
   }
+  return 0;
+}
+
+/*
+ * Gradients of one (b,h) slice of the layer above, by reverse-mode differentiation of the same
+ * recurrence: given dL/do for every output, the gradients of a real loss L with respect to q,
+ * k, v, lambda, beta and the initial state.  The training-time claims of the summary page
+ * (§G: a training step is the forward and this backward) are what it serves.
+ *
+ * Convention for a complex quantity z (lambda, beta, the state): its gradient is
+ * dL/dRe z + i dL/dIm z.  With that convention, for w = p z (p fixed) the gradient of z
+ * gathers conj(p) times that of w, and for real x with w = x u it gathers Re(g_w conj(u)).
+ *
+ * Plainly: a forward sweep keeps every state U_t, Gam_t, eta_t (t = -1 for the initial
+ * state), a_t, num_t and den_t; a reverse sweep then carries the state adjoints
+ *   Ubar_t = (readout at t) + conj(lambda) Ubar_{t+1}   (the same for Gam and eta)
+ * and collects every input's gradient at the step that uses it.  The readout
+ * o = num / max(den, clamp) differentiates to dnum = g / c and, when den >= clamp (the
+ * branch the forward takes for den itself), dden = -sum_j g_j num_j / c^2; below the clamp
+ * dden = 0.  With no_den != 0 the output is num itself: dnum = g, dden = 0.
+ *
+ *   dO        [N][D]       dL/do
+ *   U0,G0,e0  initial state as in ia_oracle_scan, or NULL for zeros
+ *   dq, dk    [N][F]       out: dL/dq, dL/dk (through phi' = 1 above 0, exp(x) at or below)
+ *   dv        [N][D]       out
+ *   dlam,dbeta [M][2]      out: complex gradients as above
+ *   dU0,dG0,de0            out: gradients of the initial state, or NULL
+ *   work      (N+1) * M * (F+D+1) * 2 + N * M * 2 + N * (D+1) doubles
+ * Returns 0.
+ */
+static double feature_grad(double x) { return x > 0.0 ? 1.0 : exp(x); }
+
+int ia_oracle_scan_bwd(int N, int F, int D, int M,
+                       const double* q, const double* k, const double* v,
+                       const double* lam, const double* beta,
+                       const double* U0, const double* G0, const double* e0,
+                       const double* dO, double clamp, int no_den,
+                       double* dq, double* dk, double* dv, double* dlam, double* dbeta,
+                       double* dU0, double* dG0, double* de0, double* work) {
+  const size_t SU = (size_t)M * F, SG = (size_t)M * D;   /* complex entries per state */
+  double complex* Us = (double complex*)work;              /* [N+1][M][F], slot t+1 = U_t */
+  double complex* Gs = Us + (size_t)(N + 1) * SU;          /* [N+1][M][D] */
+  double complex* es = Gs + (size_t)(N + 1) * SG;          /* [N+1][M] */
+  double complex* as = es + (size_t)(N + 1) * M;           /* [N][M] */
+  double* nums = (double*)(as + (size_t)N * M);            /* [N][D] */
+  double* dens = nums + (size_t)N * D;                     /* [N] */
+
+  /* forward sweep, every state kept */
+  for (size_t i = 0; i < SU; ++i) Us[i] = U0 ? U0[2 * i] + I * U0[2 * i + 1] : 0.0;
+  for (size_t i = 0; i < SG; ++i) Gs[i] = G0 ? G0[2 * i] + I * G0[2 * i + 1] : 0.0;
+  for (int m = 0; m < M; ++m) es[m] = e0 ? e0[2 * m] + I * e0[2 * m + 1] : 0.0;
+  for (int t = 0; t < N; ++t) {
+    const double complex* Up = Us + (size_t)t * SU;
+    const double complex* Gp = Gs + (size_t)t * SG;
+    const double complex* ep = es + (size_t)t * M;
+    double complex* Un = Us + (size_t)(t + 1) * SU;
+    double complex* Gn = Gs + (size_t)(t + 1) * SG;
+    double complex* en = es + (size_t)(t + 1) * M;
+    double complex denc = 0.0;
+    for (int j = 0; j < D; ++j) nums[(size_t)t * D + j] = 0.0;
+    for (int m = 0; m < M; ++m) {
+      const double complex lm = lam[2 * m] + I * lam[2 * m + 1];
+      const double complex bt = beta[2 * m] + I * beta[2 * m + 1];
+      double complex a = 0.0;
+      for (int r = 0; r < F; ++r) {
+        const size_t i = (size_t)m * F + r;
+        Un[i] = lm * Up[i] + bt * feature(k[(size_t)t * F + r]);
+        a += feature(q[(size_t)t * F + r]) * Un[i];
+      }
+      as[(size_t)t * M + m] = a;
+      for (int j = 0; j < D; ++j) {
+        const size_t i = (size_t)m * D + j;
+        Gn[i] = lm * Gp[i] + bt * v[(size_t)t * D + j];
+        nums[(size_t)t * D + j] += creal(a * Gn[i]);
+      }
+      en[m] = lm * ep[m] + bt;
+      denc += a * en[m];
+    }
+    dens[t] = creal(denc);
+  }
+
+  /* reverse sweep: Ub, Gb, eb hold the adjoints of U_t, Gam_t, eta_t */
+  double complex* Ub = (double complex*)calloc(SU + SG + M, sizeof(double complex));
+  if (!Ub) return 1;
+  double complex* Gb = Ub + SU;
+  double complex* eb = Gb + SG;
+  for (int m = 0; m < M; ++m) { dlam[2 * m] = dlam[2 * m + 1] = 0.0; dbeta[2 * m] = dbeta[2 * m + 1] = 0.0; }
+  for (int t = N - 1; t >= 0; --t) {
+    const double* g = dO + (size_t)t * D;
+    const double d = dens[t];
+    double c = d < clamp ? clamp : d;
+    if (isnan(d)) c = d;
+    double dnum_scale, dden;
+    if (no_den) {
+      dnum_scale = 1.0;
+      dden = 0.0;
+    } else {
+      double gn = 0.0;
+      for (int j = 0; j < D; ++j) gn += g[j] * nums[(size_t)t * D + j];
+      dnum_scale = 1.0 / c;
+      dden = d >= clamp ? -gn / (c * c) : 0.0;
+    }
+    const double complex* Ut = Us + (size_t)(t + 1) * SU;
+    const double complex* Gt = Gs + (size_t)(t + 1) * SG;
+    const double complex* et = es + (size_t)(t + 1) * M;
+    const double complex* Up = Us + (size_t)t * SU;
+    const double complex* Gp = Gs + (size_t)t * SG;
+    const double complex* ep = es + (size_t)t * M;
+    for (int r = 0; r < F; ++r) dq[(size_t)t * F + r] = dk[(size_t)t * F + r] = 0.0;
+    for (int j = 0; j < D; ++j) dv[(size_t)t * D + j] = 0.0;
+    for (int m = 0; m < M; ++m) {
+      const double complex lm = lam[2 * m] + I * lam[2 * m + 1];
+      const double complex bt = beta[2 * m] + I * beta[2 * m + 1];
+      const double complex a = as[(size_t)t * M + m];
+      /* readout: num_j = Re sum_m a_m Gam_mj, den = Re sum_m a_m eta_m */
+      double complex ga = dden * conj(et[m]);                  /* gradient of a_m */
+      for (int j = 0; j < D; ++j) {
+        const size_t i = (size_t)m * D + j;
+        const double dn = dnum_scale * g[j];
+        ga += dn * conj(Gt[i]);
+        Gb[i] += dn * conj(a);
+      }
+      eb[m] += dden * conj(a);
+      /* a_m = sum_r phi(q_r) U_mr */
+      for (int r = 0; r < F; ++r) {
+        const size_t i = (size_t)m * F + r;
+        dq[(size_t)t * F + r] += creal(ga * conj(Ut[i]));
+        Ub[i] += feature(q[(size_t)t * F + r]) * ga;
+      }
+      /* U_t = lambda U_{t-1} + beta phi(k_t), and the same for Gam (with v_t) and eta (with 1) */
+      double complex gl = 0.0, gb = 0.0;
+      for (int r = 0; r < F; ++r) {
+        const size_t i = (size_t)m * F + r;
+        const double fk = feature(k[(size_t)t * F + r]);
+        dk[(size_t)t * F + r] += creal(Ub[i] * conj(bt));
+        gb += Ub[i] * fk;
+        gl += Ub[i] * conj(Up[i]);
+        Ub[i] = conj(lm) * Ub[i];
+      }
+      for (int j = 0; j < D; ++j) {
+        const size_t i = (size_t)m * D + j;
+        dv[(size_t)t * D + j] += creal(Gb[i] * conj(bt));
+        gb += Gb[i] * v[(size_t)t * D + j];
+        gl += Gb[i] * conj(Gp[i]);
+        Gb[i] = conj(lm) * Gb[i];
+      }
+      gb += eb[m];
+      gl += eb[m] * conj(ep[m]);
+      eb[m] = conj(lm) * eb[m];
+      dlam[2 * m] += creal(gl);
+      dlam[2 * m + 1] += cimag(gl);
+      dbeta[2 * m] += creal(gb);
+      dbeta[2 * m + 1] += cimag(gb);
+    }
+    for (int r = 0; r < F; ++r) {
+      dq[(size_t)t * F + r] *= feature_grad(q[(size_t)t * F + r]);
+      dk[(size_t)t * F + r] *= feature_grad(k[(size_t)t * F + r]);
+    }
+  }
+  /* what is left in the adjoints is the gradient of the initial state */
+  for (size_t i = 0; i < SU; ++i) if (dU0) { dU0[2 * i] = creal(Ub[i]); dU0[2 * i + 1] = cimag(Ub[i]); }
+  for (size_t i = 0; i < SG; ++i) if (dG0) { dG0[2 * i] = creal(Gb[i]); dG0[2 * i + 1] = cimag(Gb[i]); }
+  for (int m = 0; m < M; ++m) if (de0) { de0[2 * m] = creal(eb[m]); de0[2 * m + 1] = cimag(eb[m]); }
+  free(Ub);
   return 0;
 }
