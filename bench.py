@@ -1,14 +1,16 @@
 """Benchmark of the IA layer hot path on one MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload 1.3b|125m|1.3b_long|caduceus]
-                    [--no-cpu] [--no-decode]
+                    [--no-cpu] [--no-decode] [--no-backward]
 
 A step is one causal (or, for the genomic workload, bidirectional) IA layer forward over the
 whole synthetic batch, through ia_prefill_fwd: per-head tables, segment end states, carry
 scan and the chunked MFMA pass with outputs.  Inputs are resident in HBM before timing starts.
 Prints one JSON line: prefill tokens/s, the roofline position of the dominant kernel
 (measured with HIP events around that kernel, over a timed loop), decode-step latency at
-batch 1/16/64 (hipGraph-captured and eager), and the CPU oracle's throughput on a sample.
+batch 1/16/64 (hipGraph-captured and eager), the backward pass of the causal workloads (its
+time and its position against the fp32 vector peak), and the CPU oracle's throughput on a
+sample.
 """
 from __future__ import annotations
 
@@ -220,6 +222,52 @@ def bench_decode(torch, ia, W, batches=(1, 16, 64), steps=256):
     return res
 
 
+FP32_PEAK = 157.3e12        # fp32 vector FLOP/s, MI355X
+
+
+def bwd_alg_flops(B, N, H, F, D, M):
+    """Algorithmic FLOPs of the backward pass (fp32 VALU): per token, head and mode, the state
+    recompute 14 (F + D) and the reverse sweep 44 F + 41 D (a complex multiply counted 6, a
+    complex-by-real multiply-add 4)."""
+    return float(14 * (F + D) + 44 * F + 41 * D) * M * B * N * H
+
+
+def bench_backward(torch, ia, inp, steps=5, warmup=2):
+    """ia_prefill_bwd over the prefill workload (bf16 q, k, v; fp32 dO), from a zero state."""
+    sh = inp["shape"]
+    B, H, N, F, D, M = sh["B"], sh["H"], sh["N"], sh["F"], sh["D"], sh["M"]
+    q, k, v = (torch.from_numpy(inp[n]).to(torch.bfloat16).cuda() for n in "qkv")
+    lam = torch.from_numpy(inp["lam"]).cuda()
+    beta = torch.from_numpy(inp["beta"]).cuda()
+    g = torch.Generator(device="cpu").manual_seed(550)
+    dO = torch.randn((B, N, H, D), generator=g, dtype=torch.float32).cuda()
+    desc = ia.make_desc(B, H, N, F, D, M, ia.IA_BF16, ia.IA_F32)
+    ws = torch.empty(ia.ia_prefill_bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dl = torch.empty((H, M), dtype=torch.complex64, device="cuda")
+    db = torch.empty_like(dl)
+
+    def step():
+        ia.ia_prefill_bwd(desc, q, k, v, lam, beta, None, dO, dq, dk, dv, dl, db, None, ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    fl = bwd_alg_flops(B, N, H, F, D, M)
+    return {"us_per_step": us, "tokens_per_s": B * N / (us * 1e-6), "steps": steps,
+            "dtype": "bf16 in, fp32 state and arithmetic", "workspace_bytes": ws.numel(),
+            "alu": {"bound": "alu", "achieved": fl / (us * 1e-6) / 1e12,
+                    "peak": FP32_PEAK / 1e12, "unit": "TFLOP/s",
+                    "frac": fl / (us * 1e-6) / FP32_PEAK, "alg_flops": fl}}
+
+
 def cpu_baseline(inp, bidir, budget_s=12.0):
     """The oracle as it stands, on the host cores, over a bounded sample of (b,h) slices."""
     import oracle
@@ -275,6 +323,7 @@ def main():
     ap.add_argument("--workload", default="1.3b", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain streaming kernel over 256 MiB (read 256 MiB, write "
                          "256 MiB) whose counter readings scale the hardware byte counters")
@@ -294,6 +343,9 @@ def main():
         calib_copy(torch)
     pf = bench_prefill(args, torch, ia, W)
     dec = None if args.no_decode else bench_decode(torch, ia, W)
+    bwd = None
+    if not args.no_backward and not pf["cfg"]["bidirectional"]:
+        bwd = bench_backward(torch, ia, pf["inp"])
     cpu = None if args.no_cpu else cpu_baseline(pf["inp"], pf["cfg"]["bidirectional"])
     line = {
         "metric": "IA layer fwd tokens/s (prefill) + decode step latency; % of MFMA/HBM roofline",
@@ -313,6 +365,7 @@ def main():
         "mfma": pf["mfma"],
         "kernels_ms": pf["kernels_ms"],
         "decode": dec,
+        "backward": bwd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

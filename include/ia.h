@@ -202,6 +202,42 @@ ia_status ia_decode_step(const ia_desc* desc,
                          const void* lambda, const void* beta,
                          ia_state* st, void* o_t, void* stream);
 
+/* Workspace bytes ia_prefill_bwd needs for this descriptor: state checkpoints every 32 tokens
+ * (B*H*ceil(N/32)*M*(F+Dv+1) complex64), per-token partial denominators (B*H*N*M/2 complex64),
+ * per-mode-group gradient rows (M/16 * B*H*N*(2F+Dv) float) and per-slice lambda/beta
+ * gradients, each region 256-byte aligned.  0 on an invalid descriptor. */
+size_t ia_prefill_bwd_workspace_bytes(const ia_desc* desc);
+
+/* Gradients of the causal layer (ia_prefill_fwd's outputs o) for a real loss L, given
+ * dO = dL/do: reverse-mode differentiation of the recurrence and readout above, as the
+ * training step of [summary §G] needs.  The states are recomputed from st0 (not read from a
+ * forward call), checkpointed every 32 tokens, and rebuilt backward inside each interval by
+ * U_{t-1} = (U_t - beta phi(k_t)) / lambda, in fp32.
+ *   q, k, v, lambda, beta   as in ia_prefill_fwd (dense layout, in_dtype).
+ *   st0      initial state the forward started from, or NULL for zeros; read only.
+ *   dO       [B][N][H][Dv] out_dtype.
+ *   dq, dk   [B][N][H][F] in_dtype; dv [B][N][H][Dv] in_dtype (overwritten).
+ *   dlambda, dbeta  [H][M] complex64: dL/dRe + i dL/dIm, summed over the batch.
+ *   dst0     receives dL/d(st0) in the ia_state layout, or NULL.
+ * Readout gradient: dnum = dO / c and, where den >= den_clamp (the branch the forward takes
+ * for den itself), dden = -sum_j dO_j num_j / c^2, with c = max(den, den_clamp); below the
+ * clamp den has no gradient.  IA_FLAG_NO_DEN: dnum = dO, dden = 0.  IA_FLAG_IDENTITY_FEATURES:
+ * phi' = 1.  IA_FLAG_BIDIR: IA_ERR_UNSUPPORTED.
+ * Accuracy: the rebuild grows fp32 rounding by at most |lambda|^-31 inside an interval; for
+ * |lambda| >= 0.9 that is below 30x (an S4D-Lin lambda = exp(dt(-1/2 + i pi m)) with
+ * dt <= 0.1 has |lambda| >= 0.95).
+ * lambda = 0 gives non-finite gradients.
+ * Errors: as ia_prefill_fwd (IA_ERR_NULL for a missing required pointer, IA_ERR_ALIGN for
+ * pointers not 16-byte aligned, IA_ERR_ALIAS when an output overlaps an input, another
+ * output or the workspace, IA_ERR_WORKSPACE when ws_bytes is below
+ * ia_prefill_bwd_workspace_bytes); nothing is launched on error. */
+ia_status ia_prefill_bwd(const ia_desc* desc,
+                         const void* q, const void* k, const void* v,
+                         const void* lambda, const void* beta,
+                         const ia_state* st0, const void* dO,
+                         void* dq, void* dk, void* dv, void* dlambda, void* dbeta,
+                         ia_state* dst0, void* workspace, size_t ws_bytes, void* stream);
+
 /* Static string naming a status code. */
 const char* ia_status_string(ia_status s);
 

@@ -88,6 +88,11 @@ lib.ia_prefill_fwd_profiled.argtypes = [_D, _P, _P, _P, _P, _P, _S, _P, _P, ctyp
                                         ctypes.POINTER(ctypes.c_int), ctypes.c_int,
                                         ctypes.POINTER(ctypes.c_int)]
 lib.ia_prefill_fwd_profiled.restype = ctypes.c_int
+lib.ia_prefill_bwd_workspace_bytes.argtypes = [_D]
+lib.ia_prefill_bwd_workspace_bytes.restype = ctypes.c_size_t
+lib.ia_prefill_bwd.argtypes = [_D, _P, _P, _P, _P, _P, _S, _P, _P, _P, _P, _P, _P, _S, _P,
+                               ctypes.c_size_t, _P]
+lib.ia_prefill_bwd.restype = ctypes.c_int
 lib.ia_status_string.argtypes = [ctypes.c_int]
 lib.ia_status_string.restype = ctypes.c_char_p
 lib.ia_last_launch_error.argtypes = []
@@ -95,9 +100,10 @@ lib.ia_last_launch_error.restype = ctypes.c_char_p
 
 EXPORTS = ("ia_state_init", "ia_prefill_workspace_bytes", "ia_check_lambda", "ia_prefill_fwd",
            "ia_prefill_fwd_strided", "ia_prefill_fwd_profiled", "ia_decode_step",
-           "ia_status_string", "ia_last_launch_error")
+           "ia_prefill_bwd_workspace_bytes", "ia_prefill_bwd", "ia_status_string",
+           "ia_last_launch_error")
 KIND_NAMES = {0: "fill", 1: "scan", 2: "tables", 3: "summary", 4: "carry", 5: "chunk",
-              6: "decode"}
+              6: "decode", 7: "bwd_forward", 8: "bwd_reverse", 9: "bwd_reduce"}
 
 
 def make_desc(B, H, N, F, Dv, M, in_dtype=IA_BF16, out_dtype=IA_F32, den_clamp=1e-6,
@@ -209,6 +215,20 @@ def ia_prefill_fwd_profiled(desc: IADesc, q, k, v, lam, beta, state, o, workspac
     return [kinds[i] for i in range(used.value)]
 
 
+def ia_prefill_bwd_workspace_bytes(desc: IADesc) -> int:
+    return int(lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def ia_prefill_bwd(desc: IADesc, q, k, v, lam, beta, state0, dO, dq, dk, dv, dlam, dbeta,
+                   dstate0, workspace, stream=None):
+    _dense(q, k, v, lam, beta, dO, dq, dk, dv, dlam, dbeta, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.ia_prefill_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(lam),
+                              _ptr(beta), _state(state0), _ptr(dO), _ptr(dq), _ptr(dk),
+                              _ptr(dv), _ptr(dlam), _ptr(dbeta), _state(dstate0),
+                              _ptr(workspace), ws_bytes, _stream(stream)), "ia_prefill_bwd")
+
+
 def ia_decode_step(desc: IADesc, q_t, k_t, v_t, lam, beta, state, o_t, stream=None):
     _dense(q_t, k_t, v_t, lam, beta, o_t)
     _check(lib.ia_decode_step(ctypes.byref(desc), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(lam),
@@ -263,3 +283,24 @@ def decode(q_t, k_t, v_t, lam, beta, state, out_dtype=None,
         o_t = torch.empty((B, H, Dv), dtype=out_dtype, device=q_t.device)
     ia_decode_step(desc, q_t, k_t, v_t, lam, beta, state, o_t, stream)
     return o_t
+
+
+def prefill_bwd(q, k, v, lam, beta, dO, state0=None, den_clamp=1e-6, no_den=False,
+                identity_features=False, want_state_grad=False, stream=None, workspace=None):
+    """Gradients of the causal layer for dL/do = dO: allocates the outputs (and the workspace)
+    with torch and runs ia_prefill_bwd.  Returns (dq, dk, dv, dlam, dbeta, dstate0 or None)."""
+    import torch
+    B, N, H, F = q.shape
+    Dv, M = v.shape[3], lam.shape[1]
+    desc = make_desc(B, H, N, F, Dv, M, dtype_code(q.dtype), dtype_code(dO.dtype), den_clamp,
+                     no_den=no_den, identity_features=identity_features)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dlam = torch.empty((H, M), dtype=torch.complex64, device=q.device)
+    dbeta = torch.empty_like(dlam)
+    dst = new_state(B, H, M, F, Dv, device=q.device, zero=False) if want_state_grad else None
+    if workspace is None:
+        workspace = torch.empty(max(ia_prefill_bwd_workspace_bytes(desc), 16), dtype=torch.uint8,
+                                device=q.device)
+    ia_prefill_bwd(desc, q, k, v, lam, beta, state0, dO, dq, dk, dv, dlam, dbeta, dst, workspace,
+                   stream)
+    return dq, dk, dv, dlam, dbeta, dst

@@ -352,6 +352,95 @@ ia_status ia_prefill_fwd_strided(const ia_desc* d, const void* q, const void* k,
   return launch_status(e);
 }
 
+size_t ia_prefill_bwd_workspace_bytes(const ia_desc* d) {
+  if (check_desc(d, true) != IA_OK) return 0;
+  return ia::bwd_layout(d->B, d->H, d->N, d->F, d->Dv, d->M).bytes;
+}
+
+ia_status ia_prefill_bwd(const ia_desc* d, const void* q, const void* k, const void* v,
+                         const void* lambda, const void* beta, const ia_state* st0,
+                         const void* dO, void* dq, void* dk, void* dv, void* dlambda,
+                         void* dbeta, ia_state* dst0, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  ia_status s = check_desc(d, true);
+  if (s != IA_OK) return s;
+  if (d->flags & IA_FLAG_BIDIR) return IA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !lambda || !beta || !dO || !dq || !dk || !dv || !dlambda || !dbeta)
+    return IA_ERR_NULL;
+  for (const void* p : {q, k, v, lambda, beta, dO, static_cast<const void*>(dq),
+                        static_cast<const void*>(dk), static_cast<const void*>(dv),
+                        static_cast<const void*>(dlambda), static_cast<const void*>(dbeta)})
+    if (!aligned16(p)) return IA_ERR_ALIGN;
+  if (st0 && (s = check_state(d, st0)) != IA_OK) return s;
+  if (dst0 && (s = check_state(d, dst0)) != IA_OK) return s;
+  const ia::BwdLayout L = ia::bwd_layout(d->B, d->H, d->N, d->F, d->Dv, d->M);
+  if (!workspace || ws_bytes < L.bytes) return IA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return IA_ERR_ALIGN;
+
+  const size_t tok = size_t(d->B) * d->N * d->H;
+  const size_t ein = esize(d->in_dtype);
+  Range ins[9] = {rng(q, tok * d->F * ein), rng(k, tok * d->F * ein),
+                  rng(v, tok * d->Dv * ein), rng(lambda, size_t(d->H) * d->M * 8),
+                  rng(beta, size_t(d->H) * d->M * 8),
+                  rng(dO, tok * d->Dv * esize(d->out_dtype))};
+  int n_ins = 6;
+  if (st0) {
+    ins[n_ins++] = rng(st0->U, state_u_bytes(d));
+    ins[n_ins++] = rng(st0->Gamma, state_g_bytes(d));
+    ins[n_ins++] = rng(st0->eta, state_e_bytes(d));
+  }
+  Range outs[9] = {rng(dq, tok * d->F * ein), rng(dk, tok * d->F * ein),
+                   rng(dv, tok * d->Dv * ein), rng(dlambda, size_t(d->H) * d->M * 8),
+                   rng(dbeta, size_t(d->H) * d->M * 8), rng(workspace, L.bytes)};
+  int n_outs = 6;
+  if (dst0) {
+    outs[n_outs++] = rng(dst0->U, state_u_bytes(d));
+    outs[n_outs++] = rng(dst0->Gamma, state_g_bytes(d));
+    outs[n_outs++] = rng(dst0->eta, state_e_bytes(d));
+  }
+  for (int i = 0; i < n_outs; ++i) {
+    for (int j = 0; j < n_ins; ++j)
+      if (overlap(outs[i], ins[j])) return IA_ERR_ALIAS;
+    for (int j = i + 1; j < n_outs; ++j)
+      if (overlap(outs[i], outs[j])) return IA_ERR_ALIAS;
+  }
+
+  char* ws = static_cast<char*>(workspace);
+  ia::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dO = dO;
+  a.lam = static_cast<const float2*>(lambda);
+  a.beta = static_cast<const float2*>(beta);
+  if (st0) {
+    a.U0 = static_cast<const float2*>(st0->U);
+    a.G0 = static_cast<const float2*>(st0->Gamma);
+    a.E0 = static_cast<const float2*>(st0->eta);
+  }
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dlam = static_cast<float2*>(dlambda);
+  a.dbeta = static_cast<float2*>(dbeta);
+  if (dst0) {
+    a.dU0 = static_cast<float2*>(dst0->U);
+    a.dG0 = static_cast<float2*>(dst0->Gamma);
+    a.dE0 = static_cast<float2*>(dst0->eta);
+  }
+  a.ckpt = reinterpret_cast<float2*>(ws + L.ckpt_off);
+  a.dpart = reinterpret_cast<float2*>(ws + L.dpart_off);
+  a.gpart = reinterpret_cast<float*>(ws + L.gpart_off);
+  a.lpart = reinterpret_cast<float2*>(ws + L.lpart_off);
+  a.B = d->B; a.H = d->H; a.N = d->N; a.F = d->F; a.D = d->Dv; a.M = d->M;
+  a.in_bf16 = d->in_dtype == IA_BF16;
+  a.out_bf16 = d->out_dtype == IA_BF16;
+  a.opt = kernel_opt(d);
+  a.clamp = d->den_clamp;
+  a.tb = ia::bwd_block_tokens(d->F, d->Dv, d->M, a.in_bf16, a.out_bf16);
+  return launch_status(ia::launch_prefill_bwd(a, static_cast<hipStream_t>(stream)));
+}
+
 ia_status ia_decode_step(const ia_desc* d, const void* q_t, const void* k_t, const void* v_t,
                          const void* lambda, const void* beta, ia_state* st, void* o_t,
                          void* stream) {

@@ -1,0 +1,698 @@
+// ia_backward.hip — gradients of the causal IA layer: reverse-mode differentiation of the
+// token recurrence, in fp32, token-sequential within each (b,h) slice and parallel over slices
+// and modes.  The training-time figures of "Interdomain Attention: Beyond Token-Level
+// Key-Value Memory" (summary page §G) count this pass beside the forward.
+//
+// The recurrence per mode m (summary page §3.1-§3.2; episode page, derivation):
+//   U_t = lam U_{t-1} + beta phi(k_t),  Gam_t = lam Gam_{t-1} + beta v_t,  eta_t = lam eta_{t-1} + beta
+//   a_t[m] = phi(q_t) . U_t[m],  num_t = Re sum_m a_t[m] Gam_t[m],  den_t = Re sum_m a_t[m] eta_t[m]
+//   o_t = num_t / max(den_t, clamp)
+// Reverse mode carries the state adjoints Ubar_t = (readout at t) + conj(lam) Ubar_{t+1} (the
+// same for Gam and eta); complex gradients are dL/dRe + i dL/dIm.
+//
+// Three launches:
+//  1. bwd_forward_kernel: recompute the states from the initial state, store them every
+//     kBwdCheckpoint tokens (and after the last token), and per token the partial sums over
+//     this wave's modes of den_t and of g_t . num_t (g = dL/do), which the readout gradient
+//     needs in full before any mode can run backward.
+//  2. bwd_reverse_kernel: walk each checkpoint interval backward from its end state,
+//     rebuilding U_{t-1} = (U_t - beta phi(k_t)) / lam (the interval is short, so the growth of
+//     rounding by |lam|^-1 per step stays bounded), carrying the adjoints, and collecting the
+//     gradients of q, k, v (summed over this workgroup's modes), lambda and beta.
+//  3. bwd_reduce_kernel: sum the per-mode-group partials of dq, dk, dv in a fixed order and
+//     store them in the input dtype; sum lambda and beta gradients over the batch.
+//
+// Layout: a workgroup is 4 waves x 4 modes (16 modes, a block of one slice's modes); lane l of
+// a wave owns state columns l, l + 64, ... of U (F wide) and Gam (D wide) for all four of its
+// modes, so every sum over modes of a column is a lane's own, and every sum over a mode's
+// columns is one 16-value wave reduction per token.
+#include "ia_device.hpp"
+#include "ia_kernels.hpp"
+
+namespace ia {
+
+namespace {
+
+constexpr int kModesPerWave = 2;
+constexpr int kWaves = 8;
+constexpr int kRed = 4 * kModesPerWave;   // values a wave sums per token: 4 per mode
+constexpr int kModesPerWg = kModesPerWave * kWaves;
+constexpr int kThreads = 64 * kWaves;
+
+__device__ __forceinline__ float2 cadd(float2 a, float2 b) { return make_float2(a.x + b.x, a.y + b.y); }
+__device__ __forceinline__ float2 cscale(float s, float2 a) { return make_float2(s * a.x, s * a.y); }
+__device__ __forceinline__ float2 conjf2(float2 a) { return make_float2(a.x, -a.y); }
+// a * conj(b)
+__device__ __forceinline__ float2 cmulc(float2 a, float2 b) {
+  return make_float2(a.x * b.x + a.y * b.y, a.y * b.x - a.x * b.y);
+}
+// Re(a * conj(b))
+__device__ __forceinline__ float cdotr(float2 a, float2 b) { return a.x * b.x + a.y * b.y; }
+
+__device__ __forceinline__ float uniform(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// Sums NV values (NV = 8 or 16) over the 64 lanes of a wave by recursive halving: after the
+// exchange steps lane l holds, in v[0], the wave total of value (l / (64 / NV)) % NV.
+// One halving step: lanes with `BIT` set keep the upper HALF values, the others the lower,
+// each adding its partner's copy of the half it keeps.
+template <int NV, int HALF, int BIT>
+__device__ __forceinline__ void halve(float (&v)[NV], int lane) {
+  const bool hi = lane & BIT;
+#pragma unroll
+  for (int i = 0; i < HALF; ++i) {
+    const float keep = hi ? v[i + HALF] : v[i];
+    const float send = hi ? v[i] : v[i + HALF];
+    v[i] = keep + __shfl_xor(send, BIT, 64);
+  }
+}
+template <int NV>
+__device__ __forceinline__ void wave_sum(float (&v)[NV], int lane) {
+  static_assert(NV == 8 || NV == 16, "8 or 16 values");
+  if constexpr (NV == 16) {
+    halve<NV, 8, 32>(v, lane);
+    halve<NV, 4, 16>(v, lane);
+    halve<NV, 2, 8>(v, lane);
+    halve<NV, 1, 4>(v, lane);
+  } else {
+    halve<NV, 4, 32>(v, lane);
+    halve<NV, 2, 16>(v, lane);
+    halve<NV, 1, 8>(v, lane);
+  }
+#pragma unroll
+  for (int bit = 64 / NV / 2; bit >= 1; bit >>= 1) v[0] += __shfl_xor(v[0], bit, 64);
+}
+// Value `i` of a wave_sum<kRed> result, as a wave-uniform scalar.
+__device__ __forceinline__ float sum_get(float r, int i) { return uniform(r, (64 / kRed) * i); }
+
+struct Slice {
+  int lane, wave, slice, grp, b, h, m0, groups;
+};
+
+__device__ __forceinline__ Slice slice_of(const BwdArgs& a) {
+  Slice s;
+  s.lane = threadIdx.x & 63;
+  s.wave = threadIdx.x >> 6;
+  s.groups = a.M / kModesPerWg;
+  s.slice = blockIdx.x / s.groups;
+  s.grp = blockIdx.x % s.groups;
+  s.b = s.slice / a.H;
+  s.h = s.slice % a.H;
+  s.m0 = s.grp * kModesPerWg + s.wave * kModesPerWave;
+  return s;
+}
+
+// The state of this wave's modes at the lane's columns.
+template <int NF, int ND>
+struct State {
+  float2 U[kModesPerWave][NF], G[kModesPerWave][ND], E[kModesPerWave];
+
+  __device__ void zero() {
+#pragma unroll
+    for (int i = 0; i < kModesPerWave; ++i) {
+#pragma unroll
+      for (int j = 0; j < NF; ++j) U[i][j] = make_float2(0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < ND; ++j) G[i][j] = make_float2(0.f, 0.f);
+      E[i] = make_float2(0.f, 0.f);
+    }
+  }
+  // From a caller's state ([slice][M][F], [slice][M][D], [slice][M]); zeros when absent.
+  __device__ void load_state(const BwdArgs& a, const float2* U0, const float2* G0,
+                             const float2* E0, const Slice& s) {
+    if (!U0) {
+      zero();
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < kModesPerWave; ++i) {
+      const size_t m = (size_t)s.slice * a.M + s.m0 + i;
+#pragma unroll
+      for (int j = 0; j < NF; ++j) {
+        const int r = s.lane + 64 * j;
+        U[i][j] = r < a.F ? U0[m * a.F + r] : make_float2(0.f, 0.f);
+      }
+#pragma unroll
+      for (int j = 0; j < ND; ++j) {
+        const int c = s.lane + 64 * j;
+        G[i][j] = c < a.D ? G0[m * a.D + c] : make_float2(0.f, 0.f);
+      }
+      E[i] = E0[m];
+    }
+  }
+  // Checkpoint `ck` of this slice: per mode, F values of U, D of Gam, then eta.
+  __device__ float2* ckpt_row(const BwdArgs& a, const Slice& s, int ck, int i) const {
+    const int nck = (a.N + kBwdCheckpoint - 1) / kBwdCheckpoint;
+    return a.ckpt + (((size_t)s.slice * nck + ck) * a.M + s.m0 + i) * (a.F + a.D + 1);
+  }
+  __device__ void store_ckpt(const BwdArgs& a, const Slice& s, int ck) const {
+#pragma unroll
+    for (int i = 0; i < kModesPerWave; ++i) {
+      float2* row = ckpt_row(a, s, ck, i);
+#pragma unroll
+      for (int j = 0; j < NF; ++j)
+        if (s.lane + 64 * j < a.F) row[s.lane + 64 * j] = U[i][j];
+#pragma unroll
+      for (int j = 0; j < ND; ++j)
+        if (s.lane + 64 * j < a.D) row[a.F + s.lane + 64 * j] = G[i][j];
+      if (s.lane == 0) row[a.F + a.D] = E[i];
+    }
+  }
+  __device__ void load_ckpt(const BwdArgs& a, const Slice& s, int ck) {
+#pragma unroll
+    for (int i = 0; i < kModesPerWave; ++i) {
+      const float2* row = ckpt_row(a, s, ck, i);
+#pragma unroll
+      for (int j = 0; j < NF; ++j)
+        U[i][j] = s.lane + 64 * j < a.F ? row[s.lane + 64 * j] : make_float2(0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < ND; ++j)
+        G[i][j] = s.lane + 64 * j < a.D ? row[a.F + s.lane + 64 * j] : make_float2(0.f, 0.f);
+      E[i] = row[a.F + a.D];
+    }
+  }
+};
+
+// Token rows staged in LDS, as raw bytes in the inputs' own dtypes: one token's q[F], k[F],
+// v[D], g[D] (g = dL/do) and, for the reverse sweep, the per-wave partials of den and g . num
+// of that token (M/4 float pairs), each segment a multiple of 16 bytes.  Blocks of
+// BwdArgs::tb rows are double-buffered: the 16-byte loads of the next block are issued
+// before the current block is processed and land in LDS after it, so their latency hides
+// behind a block of tokens.
+// 16-byte loads per thread that stage one block; the block length (BwdArgs::tb) is chosen on
+// the host so that a block of the reverse sweep's rows fits them.
+constexpr int kPrefetch = kBwdPrefetch;
+
+struct RowLayout {
+  int q, k, v, g, p, bytes;   // byte offsets of the segments in a row, and its length
+};
+
+__device__ __forceinline__ RowLayout row_layout(const BwdArgs& a, bool with_den) {
+  const int ei = a.in_bf16 ? 2 : 4, eo = a.out_bf16 ? 2 : 4;
+  RowLayout l;
+  l.q = 0;
+  l.k = a.F * ei;
+  l.v = 2 * a.F * ei;
+  l.g = l.v + a.D * ei;
+  l.p = l.g + a.D * eo;
+  l.bytes = l.p + (with_den ? 8 * (a.M / kModesPerWave) : 0);
+  return l;
+}
+
+// Issues the loads of the block of rows for tokens t_first, t_first + step, ... (rows of
+// tokens outside [0, N) are not read).
+template <int P>
+__device__ __forceinline__ void stage_issue(const BwdArgs& a, const Slice& s, const RowLayout& l,
+                                            int t_first, int step, int tb, uint4 (&pre)[P]) {
+  const int vec_row = l.bytes / 16, n = tb * vec_row;
+  const int ei = a.in_bf16 ? 2 : 4, eo = a.out_bf16 ? 2 : 4;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int e = threadIdx.x + kThreads * i;
+    uint4 x = make_uint4(0u, 0u, 0u, 0u);
+    if (e < n) {
+      const int j = e / vec_row, o = 16 * (e - j * vec_row);
+      const int t = t_first + step * j;
+      if (t >= 0 && t < a.N) {
+        const size_t row = ((size_t)s.b * a.N + t) * a.H + s.h;
+        const char* src;
+        if (o < l.k)
+          src = static_cast<const char*>(a.q) + row * a.F * ei + o;
+        else if (o < l.v)
+          src = static_cast<const char*>(a.k) + row * a.F * ei + (o - l.k);
+        else if (o < l.g)
+          src = static_cast<const char*>(a.v) + row * a.D * ei + (o - l.v);
+        else if (o < l.p)
+          src = static_cast<const char*>(a.dO) + row * a.D * eo + (o - l.g);
+        else
+          src = reinterpret_cast<const char*>(a.dpart) +
+                ((size_t)s.slice * a.N + t) * (a.M / kModesPerWave) * 8 + (o - l.p);
+        x = *reinterpret_cast<const uint4*>(src);
+      }
+    }
+    pre[i] = x;
+  }
+}
+
+template <int P>
+__device__ __forceinline__ void stage_store(const RowLayout& l, int tb, const uint4 (&pre)[P],
+                                            unsigned char* buf) {
+  const int n = tb * (l.bytes / 16);
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    const int e = threadIdx.x + kThreads * i;
+    if (e < n) reinterpret_cast<uint4*>(buf)[e] = pre[i];
+  }
+}
+
+__device__ __forceinline__ float lds_in(const unsigned char* seg, int i, int bf16) {
+  return bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(seg)[i])
+              : reinterpret_cast<const float*>(seg)[i];
+}
+
+// One token's inputs at the lane's columns, from its staged row: features of q and k (zero
+// past F), their derivatives, v and g (zero past D).
+template <int NF, int ND>
+struct Token {
+  float fq[NF], fk[NF], dq[NF], dk[NF], v[ND], g[ND];
+
+  __device__ void load(const BwdArgs& a, const Slice& s, const RowLayout& l,
+                       const unsigned char* row) {
+    const bool ident = a.opt & kOptIdentity;
+#pragma unroll
+    for (int j = 0; j < NF; ++j) {
+      const int r = s.lane + 64 * j;
+      const bool ok = r < a.F;
+      const float x = ok ? lds_in(row + l.q, r, a.in_bf16) : 0.f;
+      const float y = ok ? lds_in(row + l.k, r, a.in_bf16) : 0.f;
+      // phi(x) = x + 1 above 0, exp(x) at or below; phi'(x) = 1 above 0, exp(x) at or below
+      const float ex = __expf(fminf(x, 0.f)), ey = __expf(fminf(y, 0.f));
+      fq[j] = !ok ? 0.f : ident ? x : (x > 0.f ? x + 1.f : ex);
+      fk[j] = !ok ? 0.f : ident ? y : (y > 0.f ? y + 1.f : ey);
+      dq[j] = ident || x > 0.f ? 1.f : ex;
+      dk[j] = ident || y > 0.f ? 1.f : ey;
+    }
+#pragma unroll
+    for (int j = 0; j < ND; ++j) {
+      const int c = s.lane + 64 * j;
+      const bool ok = c < a.D;
+      v[j] = ok ? lds_in(row + l.v, c, a.in_bf16) : 0.f;
+      g[j] = ok ? lds_in(row + l.g, c, a.out_bf16) : 0.f;
+    }
+  }
+};
+
+template <int NF, int ND>
+__global__ void __launch_bounds__(kThreads) bwd_forward_kernel(const BwdArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];   // two blocks of staged token rows
+  const int TB = a.tb;
+  constexpr int P = kPrefetch;
+  const Slice s = slice_of(a);
+  const RowLayout L = row_layout(a, false);
+  const int R = L.bytes;
+  float2 lam[kModesPerWave], bet[kModesPerWave];
+#pragma unroll
+  for (int i = 0; i < kModesPerWave; ++i) {
+    lam[i] = a.lam[(size_t)s.h * a.M + s.m0 + i];
+    bet[i] = a.beta[(size_t)s.h * a.M + s.m0 + i];
+  }
+  State<NF, ND> st;
+  st.load_state(a, a.U0, a.G0, a.E0, s);
+  const int parts = a.M / kModesPerWave;
+  const int nblk = (a.N + TB - 1) / TB;
+  uint4 pre[P];
+  stage_issue(a, s, L, 0, 1, TB, pre);
+  stage_store(L, TB, pre, smem);
+  __syncthreads();
+  for (int blk = 0; blk < nblk; ++blk) {
+    const unsigned char* rows = smem + (blk & 1) * TB * R;
+    if (blk + 1 < nblk) stage_issue(a, s, L, (blk + 1) * TB, 1, TB, pre);
+    for (int j = 0; j < TB; ++j) {
+      const int t = blk * TB + j;
+      if (t >= a.N) break;
+      Token<NF, ND> x;
+      x.load(a, s, L, rows + j * R);
+      float red[kRed];
+#pragma unroll
+      for (int i = 0; i < kModesPerWave; ++i) {
+        float2 ap = make_float2(0.f, 0.f), sp = make_float2(0.f, 0.f);
+#pragma unroll
+        for (int j2 = 0; j2 < NF; ++j2) {
+          st.U[i][j2] = cadd(cmul(lam[i], st.U[i][j2]), cscale(x.fk[j2], bet[i]));
+          ap = cadd(ap, cscale(x.fq[j2], st.U[i][j2]));
+        }
+#pragma unroll
+        for (int j2 = 0; j2 < ND; ++j2) {
+          st.G[i][j2] = cadd(cmul(lam[i], st.G[i][j2]), cscale(x.v[j2], bet[i]));
+          sp = cadd(sp, cscale(x.g[j2], st.G[i][j2]));
+        }
+        st.E[i] = cadd(cmul(lam[i], st.E[i]), bet[i]);
+        red[4 * i + 0] = ap.x;
+        red[4 * i + 1] = ap.y;
+        red[4 * i + 2] = sp.x;
+        red[4 * i + 3] = sp.y;
+      }
+      wave_sum<kRed>(red, s.lane);
+      // den_t and g_t . num_t over this wave's modes: Re(a eta) and Re(a sum_j g_j Gam_j)
+      float den = 0.f, gn = 0.f;
+#pragma unroll
+      for (int i = 0; i < kModesPerWave; ++i) {
+        const float2 am = make_float2(sum_get(red[0], 4 * i), sum_get(red[0], 4 * i + 1));
+        const float2 sm = make_float2(sum_get(red[0], 4 * i + 2), sum_get(red[0], 4 * i + 3));
+        den += am.x * st.E[i].x - am.y * st.E[i].y;
+        gn += am.x * sm.x - am.y * sm.y;
+      }
+      if (s.lane == 0)
+        a.dpart[((size_t)s.slice * a.N + t) * parts + s.m0 / kModesPerWave] = make_float2(den, gn);
+      if (t % kBwdCheckpoint == kBwdCheckpoint - 1 || t == a.N - 1)
+        st.store_ckpt(a, s, t / kBwdCheckpoint);
+    }
+    if (blk + 1 < nblk) {
+      // the other buffer was last read in the previous block, which every wave has left
+      stage_store(L, TB, pre, smem + ((blk + 1) & 1) * TB * R);
+      __syncthreads();
+    }
+  }
+}
+
+template <int NF, int ND>
+__global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(const BwdArgs a) {
+  // two blocks of staged token rows, then [token][wave][2F + D] gradient rows before the mode
+  // sum
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int TB = a.tb;
+  constexpr int P = kPrefetch;
+  const Slice s = slice_of(a);
+  const RowLayout L = row_layout(a, true);
+  const int R = L.bytes;
+  const int W = 2 * a.F + a.D;
+  float* part = reinterpret_cast<float*>(smem + 2 * TB * R);
+  float2 lam[kModesPerWave], bet[kModesPerWave], linv[kModesPerWave];
+#pragma unroll
+  for (int i = 0; i < kModesPerWave; ++i) {
+    lam[i] = a.lam[(size_t)s.h * a.M + s.m0 + i];
+    bet[i] = a.beta[(size_t)s.h * a.M + s.m0 + i];
+    const float n2 = lam[i].x * lam[i].x + lam[i].y * lam[i].y;
+    linv[i] = make_float2(lam[i].x / n2, -lam[i].y / n2);
+  }
+  const bool noden = a.opt & kOptNoDen;
+  const int parts = a.M / kModesPerWave;
+  // adjoints of U, Gam, eta (eta's is wave-uniform), and the lane's share of the lambda and
+  // beta gradients of each mode
+  float2 Ub[kModesPerWave][NF], Gb[kModesPerWave][ND], Eb[kModesPerWave];
+  float2 gl[kModesPerWave], gb[kModesPerWave];
+#pragma unroll
+  for (int i = 0; i < kModesPerWave; ++i) {
+#pragma unroll
+    for (int j = 0; j < NF; ++j) Ub[i][j] = make_float2(0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < ND; ++j) Gb[i][j] = make_float2(0.f, 0.f);
+    Eb[i] = gl[i] = gb[i] = make_float2(0.f, 0.f);
+  }
+  const int nck = (a.N + kBwdCheckpoint - 1) / kBwdCheckpoint;
+  const int nblk = (a.N + TB - 1) / TB;
+  uint4 pre[P];
+  stage_issue(a, s, L, a.N - 1, -1, TB, pre);
+  stage_store(L, TB, pre, smem);
+  State<NF, ND> cur;
+  cur.load_ckpt(a, s, nck - 1);   // the state after the last token
+  __syncthreads();
+  for (int blk = 0; blk < nblk; ++blk) {
+    const unsigned char* rows = smem + (blk & 1) * TB * R;
+    const int t_hi = a.N - 1 - blk * TB;   // tokens t_hi, t_hi - 1, ... of this block
+    if (blk + 1 < nblk) stage_issue(a, s, L, t_hi - TB, -1, TB, pre);
+    // The readout's gradient factors of the block's tokens, dnum = g rc and dden (0 below the
+    // clamp, and without a denominator): the 8 lanes 8j..8j+7 sum token j's partials of den
+    // and g . num, and lane 8j keeps its factors.
+    float blk_rc = 1.f, blk_dd = 0.f;
+    if (!noden) {
+      const int jt = s.lane >> 3, sub = s.lane & 7;
+      float2 p = make_float2(0.f, 0.f);
+      if (jt < TB && t_hi - jt >= 0) {
+        const float2* dp = reinterpret_cast<const float2*>(rows + jt * R + L.p);
+#pragma unroll
+        for (int k = 0; k < kMaxModes / kModesPerWave / 8; ++k)
+          if (sub + 8 * k < parts) p = cadd(p, dp[sub + 8 * k]);
+      }
+#pragma unroll
+      for (int bit = 4; bit >= 1; bit >>= 1) {
+        p.x += __shfl_xor(p.x, bit, 64);
+        p.y += __shfl_xor(p.y, bit, 64);
+      }
+      const float cl = p.x < a.clamp ? a.clamp : p.x;   // NaN stays NaN
+      blk_rc = 1.f / cl;
+      blk_dd = p.x >= a.clamp ? -p.y * blk_rc * blk_rc : 0.f;
+    }
+    for (int j = 0; j < TB; ++j) {
+      const int t = t_hi - j;
+      if (t < 0) break;
+      const unsigned char* row = rows + j * R;
+      Token<NF, ND> x;
+      x.load(a, s, L, row);
+      const float rc = uniform(blk_rc, 8 * j), dd = uniform(blk_dd, 8 * j);
+      float red[kRed];
+#pragma unroll
+      for (int i = 0; i < kModesPerWave; ++i) {
+        float2 ap = make_float2(0.f, 0.f), hp = make_float2(0.f, 0.f);
+#pragma unroll
+        for (int j2 = 0; j2 < NF; ++j2) ap = cadd(ap, cscale(x.fq[j2], cur.U[i][j2]));
+#pragma unroll
+        for (int j2 = 0; j2 < ND; ++j2) hp = cadd(hp, cscale(x.g[j2], conjf2(cur.G[i][j2])));
+        red[4 * i + 0] = ap.x;
+        red[4 * i + 1] = ap.y;
+        red[4 * i + 2] = hp.x;
+        red[4 * i + 3] = hp.y;
+      }
+      wave_sum<kRed>(red, s.lane);
+      float dfq[NF], dfk[NF], dv[ND];
+#pragma unroll
+      for (int j2 = 0; j2 < NF; ++j2) dfq[j2] = dfk[j2] = 0.f;
+#pragma unroll
+      for (int j2 = 0; j2 < ND; ++j2) dv[j2] = 0.f;
+#pragma unroll
+      for (int i = 0; i < kModesPerWave; ++i) {
+        const float2 am = make_float2(sum_get(red[0], 4 * i), sum_get(red[0], 4 * i + 1));
+        const float2 hm = make_float2(sum_get(red[0], 4 * i + 2), sum_get(red[0], 4 * i + 3));
+        // gradient of a[m]: sum_j dnum_j conj(Gam_mj) + dden conj(eta_m)
+        const float2 ga = cadd(cscale(rc, hm), cscale(dd, conjf2(cur.E[i])));
+        const float2 ca = conjf2(am);
+#pragma unroll
+        for (int j2 = 0; j2 < NF; ++j2) {
+          Ub[i][j2] = cadd(Ub[i][j2], cscale(x.fq[j2], ga));
+          dfq[j2] += cdotr(ga, cur.U[i][j2]);
+          dfk[j2] += cdotr(Ub[i][j2], bet[i]);
+          gb[i] = cadd(gb[i], cscale(x.fk[j2], Ub[i][j2]));
+        }
+#pragma unroll
+        for (int j2 = 0; j2 < ND; ++j2) {
+          Gb[i][j2] = cadd(Gb[i][j2], cscale(rc * x.g[j2], ca));
+          dv[j2] += cdotr(Gb[i][j2], bet[i]);
+          gb[i] = cadd(gb[i], cscale(x.v[j2], Gb[i][j2]));
+        }
+        Eb[i] = cadd(Eb[i], cscale(dd, ca));
+        if (s.lane == 0) gb[i] = cadd(gb[i], Eb[i]);
+      }
+      // the state before token t, in place: rebuilt inside a checkpoint interval, read from
+      // the previous checkpoint (or the initial state) at its start
+      if (t % kBwdCheckpoint != 0) {
+#pragma unroll
+        for (int i = 0; i < kModesPerWave; ++i) {
+#pragma unroll
+          for (int j2 = 0; j2 < NF; ++j2)
+            cur.U[i][j2] = cmul(make_float2(cur.U[i][j2].x - x.fk[j2] * bet[i].x,
+                                            cur.U[i][j2].y - x.fk[j2] * bet[i].y), linv[i]);
+#pragma unroll
+          for (int j2 = 0; j2 < ND; ++j2)
+            cur.G[i][j2] = cmul(make_float2(cur.G[i][j2].x - x.v[j2] * bet[i].x,
+                                            cur.G[i][j2].y - x.v[j2] * bet[i].y), linv[i]);
+          cur.E[i] = cmul(make_float2(cur.E[i].x - bet[i].x, cur.E[i].y - bet[i].y), linv[i]);
+        }
+      } else if (t > 0) {
+        cur.load_ckpt(a, s, t / kBwdCheckpoint - 1);
+      } else {
+        cur.load_state(a, a.U0, a.G0, a.E0, s);
+      }
+#pragma unroll
+      for (int i = 0; i < kModesPerWave; ++i) {
+        const float2 cl = conjf2(lam[i]);
+#pragma unroll
+        for (int j2 = 0; j2 < NF; ++j2) {
+          gl[i] = cadd(gl[i], cmulc(Ub[i][j2], cur.U[i][j2]));
+          Ub[i][j2] = cmul(cl, Ub[i][j2]);
+        }
+#pragma unroll
+        for (int j2 = 0; j2 < ND; ++j2) {
+          gl[i] = cadd(gl[i], cmulc(Gb[i][j2], cur.G[i][j2]));
+          Gb[i][j2] = cmul(cl, Gb[i][j2]);
+        }
+        if (s.lane == 0) gl[i] = cadd(gl[i], cmulc(Eb[i], cur.E[i]));
+        Eb[i] = cmul(cl, Eb[i]);
+      }
+      // this wave's gradient row of token t
+      float* out = part + (size_t)(j * kWaves + s.wave) * W;
+#pragma unroll
+      for (int j2 = 0; j2 < NF; ++j2) {
+        const int r = s.lane + 64 * j2;
+        if (r < a.F) {
+          out[r] = dfq[j2] * x.dq[j2];
+          out[a.F + r] = dfk[j2] * x.dk[j2];
+        }
+      }
+#pragma unroll
+      for (int j2 = 0; j2 < ND; ++j2)
+        if (s.lane + 64 * j2 < a.D) out[2 * a.F + s.lane + 64 * j2] = dv[j2];
+    }
+    __syncthreads();
+    // the four waves' rows summed: this workgroup's partial for the block's tokens; then the
+    // next block's rows land in the buffer just used
+    const int ntok = min(TB, t_hi + 1);
+    for (int e = threadIdx.x; e < ntok * W; e += kThreads) {
+      const int jj = e / W, col = e - jj * W;
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) sum += part[(size_t)(jj * kWaves + w) * W + col];
+      a.gpart[(((size_t)s.grp * a.B * a.H + s.slice) * a.N + (t_hi - jj)) * W + col] = sum;
+    }
+    if (blk + 1 < nblk) stage_store(L, TB, pre, smem + ((blk + 1) & 1) * TB * R);
+    __syncthreads();
+  }
+  // gradients of lambda and beta of this wave's modes, for this slice
+  float red[kRed];
+#pragma unroll
+  for (int i = 0; i < kModesPerWave; ++i) {
+    red[4 * i + 0] = gl[i].x;
+    red[4 * i + 1] = gl[i].y;
+    red[4 * i + 2] = gb[i].x;
+    red[4 * i + 3] = gb[i].y;
+  }
+  wave_sum<kRed>(red, s.lane);
+#pragma unroll
+  for (int i = 0; i < kModesPerWave; ++i) {
+    const size_t m = (size_t)s.slice * a.M + s.m0 + i;
+    const float2 l = make_float2(sum_get(red[0], 4 * i), sum_get(red[0], 4 * i + 1));
+    const float2 bb = make_float2(sum_get(red[0], 4 * i + 2), sum_get(red[0], 4 * i + 3));
+    if (s.lane == 0) {
+      a.lpart[2 * m] = l;
+      a.lpart[2 * m + 1] = bb;
+    }
+    // what is left in the adjoints is the gradient of the initial state
+    if (a.dU0) {
+#pragma unroll
+      for (int j = 0; j < NF; ++j)
+        if (s.lane + 64 * j < a.F) a.dU0[m * a.F + s.lane + 64 * j] = Ub[i][j];
+#pragma unroll
+      for (int j = 0; j < ND; ++j)
+        if (s.lane + 64 * j < a.D) a.dG0[m * a.D + s.lane + 64 * j] = Gb[i][j];
+      if (s.lane == 0) a.dE0[m] = Eb[i];
+    }
+  }
+}
+
+// dq, dk, dv: the mode groups' partials summed in group order, stored in the input dtype;
+// lambda and beta gradients summed over the batch in b order.
+__global__ void __launch_bounds__(256) bwd_reduce_kernel(const BwdArgs a) {
+  const int W = 2 * a.F + a.D;
+  const int groups = a.M / kModesPerWg;
+  const size_t S = (size_t)a.B * a.H;
+  const size_t n = S * a.N * W;
+  for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n;
+       e += (size_t)gridDim.x * blockDim.x) {
+    float sum = 0.f;
+    for (int g = 0; g < groups; ++g) sum += a.gpart[(size_t)g * n + e];
+    const size_t sl = e / ((size_t)a.N * W);
+    const size_t rem = e - sl * a.N * W;
+    const size_t t = rem / W;
+    const int col = (int)(rem - t * W);
+    const size_t b = sl / a.H, h = sl % a.H;
+    const size_t row = (b * a.N + t) * a.H + h;
+    if (col < a.F)
+      store_out(a.dq, row * a.F + col, sum, a.in_bf16);
+    else if (col < 2 * a.F)
+      store_out(a.dk, row * a.F + col - a.F, sum, a.in_bf16);
+    else
+      store_out(a.dv, row * a.D + col - 2 * a.F, sum, a.in_bf16);
+  }
+  const size_t hm = (size_t)a.H * a.M;
+  for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < hm;
+       e += (size_t)gridDim.x * blockDim.x) {
+    float2 l = make_float2(0.f, 0.f), bb = make_float2(0.f, 0.f);
+    for (int b = 0; b < a.B; ++b) {
+      l = cadd(l, a.lpart[2 * ((size_t)b * hm + e)]);
+      bb = cadd(bb, a.lpart[2 * ((size_t)b * hm + e) + 1]);
+    }
+    a.dlam[e] = l;
+    a.dbeta[e] = bb;
+  }
+}
+
+// Dynamic LDS above the default limit needs the kernel's attribute raised first.
+hipError_t allow_lds(const void* kernel, size_t bytes, size_t& allowed) {
+  if (bytes <= allowed) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)bytes);
+  if (e == hipSuccess) allowed = bytes;
+  return e;
+}
+
+template <int NF, int ND>
+hipError_t launch_bwd_nf_nd(const BwdArgs& a, hipStream_t st) {
+  static size_t allowed_fwd = 65536, allowed_rev = 65536;
+  const unsigned grid = (unsigned)((size_t)a.B * a.H * (a.M / kModesPerWg));
+  const size_t lds_fwd = bwd_lds_bytes(a.F, a.D, a.M, a.in_bf16, a.out_bf16, a.tb, false);
+  const size_t lds_rev = bwd_lds_bytes(a.F, a.D, a.M, a.in_bf16, a.out_bf16, a.tb, true);
+  hipError_t e = allow_lds(reinterpret_cast<const void*>(&bwd_forward_kernel<NF, ND>), lds_fwd,
+                           allowed_fwd);
+  if (e == hipSuccess)
+    e = allow_lds(reinterpret_cast<const void*>(&bwd_reverse_kernel<NF, ND>), lds_rev,
+                  allowed_rev);
+  if (e != hipSuccess) return e;
+  prof_begin(st);
+  hipLaunchKernelGGL((bwd_forward_kernel<NF, ND>), dim3(grid), dim3(kThreads), lds_fwd, st, a);
+  prof_end(st, kKindBwdForward);
+  prof_begin(st);
+  hipLaunchKernelGGL((bwd_reverse_kernel<NF, ND>), dim3(grid), dim3(kThreads), lds_rev, st, a);
+  prof_end(st, kKindBwdReverse);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+BwdLayout bwd_layout(int B, int H, int N, int F, int D, int M) {
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t S = (size_t)B * H;
+  const size_t nck = ((size_t)N + kBwdCheckpoint - 1) / kBwdCheckpoint;
+  BwdLayout l{};
+  l.ckpt_off = 0;
+  l.dpart_off = up(S * nck * M * (F + D + 1) * 8);
+  l.gpart_off = l.dpart_off + up(S * N * (M / kModesPerWave) * 8);
+  l.lpart_off = l.gpart_off + up((size_t)(M / kModesPerWg) * S * N * (2 * F + D) * 4);
+  l.bytes = l.lpart_off + up(S * M * 2 * 8);
+  return l;
+}
+
+// Bytes of a staged token row (q, k, v in the input dtype, g in the output dtype and, for the
+// reverse sweep, the per-wave den partials).
+static size_t bwd_row_bytes(int F, int D, int M, int in_bf16, int out_bf16, bool rev) {
+  return (size_t)(2 * F + D) * (in_bf16 ? 2 : 4) + (size_t)D * (out_bf16 ? 2 : 4) +
+         (rev ? (size_t)8 * (M / kModesPerWave) : 0);
+}
+
+size_t bwd_lds_bytes(int F, int D, int M, int in_bf16, int out_bf16, int tb, bool rev) {
+  return 2 * (size_t)tb * bwd_row_bytes(F, D, M, in_bf16, out_bf16, rev) +
+         (rev ? (size_t)tb * kWaves * (2 * F + D) * sizeof(float) : 0);
+}
+
+int bwd_block_tokens(int F, int D, int M, int in_bf16, int out_bf16) {
+  // as many tokens (up to 8) as the prefetch registers stage and 150 KiB of LDS holds
+  const size_t vec = bwd_row_bytes(F, D, M, in_bf16, out_bf16, true) / 16;
+  int tb = (int)((size_t)kPrefetch * kThreads / vec);
+  if (tb > 8) tb = 8;
+  while (tb > 1 && bwd_lds_bytes(F, D, M, in_bf16, out_bf16, tb, true) > 150 * 1024) --tb;
+  return tb < 1 ? 1 : tb;
+}
+
+hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t st) {
+  (void)hipGetLastError();
+  const int nf = (a.F + 63) / 64, nd = (a.D + 63) / 64;
+  hipError_t e = hipErrorInvalidValue;
+#define IA_BWD(X, Y) \
+  if (nf == X && nd == Y) e = launch_bwd_nf_nd<X, Y>(a, st); else
+  IA_BWD(1, 1) IA_BWD(1, 2) IA_BWD(1, 3) IA_BWD(1, 4)
+  IA_BWD(2, 1) IA_BWD(2, 2) IA_BWD(2, 3) IA_BWD(2, 4)
+  IA_BWD(3, 1) IA_BWD(3, 2) IA_BWD(3, 3) IA_BWD(3, 4)
+  IA_BWD(4, 1) IA_BWD(4, 2) IA_BWD(4, 3) IA_BWD(4, 4)
+  {}
+#undef IA_BWD
+  if (e != hipSuccess) return e;
+  const size_t n = (size_t)a.B * a.H * a.N * (2 * a.F + a.D);
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks < 1) blocks = 1;
+  prof_begin(st);
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+  prof_end(st, kKindBwdReduce);
+  return hipGetLastError();
+}
+
+}  // namespace ia

@@ -15,6 +15,9 @@ enum LaunchKind {
   kKindCarry = 4,      // segment carry (many segments)
   kKindChunk = 5,      // chunked prefill with outputs (or the last segment's state)
   kKindDecode = 6,
+  kKindBwdForward = 7,   // backward: state recompute and checkpoints
+  kKindBwdReverse = 8,   // backward: reverse sweep
+  kKindBwdReduce = 9,    // backward: sum of the mode groups' partials
 };
 
 // While set (only inside ia_prefill_fwd_profiled), every launch records events[2i] before
@@ -106,6 +109,35 @@ struct ChunkPrefillArgs {
 bool chunk_supported(int F, int D, int M);
 long chunk_table_bytes(int chunk, int M);
 long chunk_slot_floats(int F, int D, int M);
+// Backward pass (ia_backward.hip).  States are checkpointed every kBwdCheckpoint tokens.
+constexpr int kBwdCheckpoint = 32;
+constexpr int kBwdPrefetch = 2;   // 16-byte loads per thread that stage a block of token rows
+
+struct BwdArgs {
+  const void *q, *k, *v, *dO;
+  const float2 *lam, *beta;
+  const float2 *U0, *G0, *E0;     // initial state, or all NULL (zeros)
+  void *dq, *dk, *dv;             // in dtype
+  float2 *dlam, *dbeta;           // [H][M]
+  float2 *dU0, *dG0, *dE0;        // gradient of the initial state, or all NULL
+  float2* ckpt;                   // workspace regions (BwdLayout)
+  float2* dpart;
+  float* gpart;
+  float2* lpart;
+  int B, H, N, F, D, M;
+  int in_bf16, out_bf16, opt;
+  float clamp;
+  int tb;                         // tokens per staged block (bwd_block_tokens)
+};
+
+struct BwdLayout {
+  size_t ckpt_off, dpart_off, gpart_off, lpart_off, bytes;
+};
+BwdLayout bwd_layout(int B, int H, int N, int F, int D, int M);
+int bwd_block_tokens(int F, int D, int M, int in_bf16, int out_bf16);
+size_t bwd_lds_bytes(int F, int D, int M, int in_bf16, int out_bf16, int tb, bool rev);
+hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t st);
+
 int chunk_wgs_per_cu(int chunk, int F, int D, int M);   // 0 if unknown (no device)
 int device_cus();                                        // compute units of the current device
 hipError_t launch_chunk_prefill(const ChunkPrefillArgs& a, hipStream_t st);

@@ -218,3 +218,52 @@ def test_strided_validation():
     # an input's strided extent reaching o (v's batch stride spans three address gaps)
     far = (3 * GAP) // 2 + 64
     assert prefill_strided(d, [qk, qk, (far, vv[1], vv[2])]) == 5
+
+
+# ---------------------------------------------------------------- ia_prefill_bwd
+
+def bwd(d, ws_bytes=1 << 40, st0=None, dst0=None, **ptrs):
+    p = dict(q=addr(0), k=addr(1), v=addr(2), lam=addr(3), beta=addr(4), dO=addr(5),
+             dq=addr(6), dk=addr(7), dv=addr(8), dlam=addr(9), dbeta=addr(13), ws=addr(14))
+    p.update(ptrs)
+    return ia.lib.ia_prefill_bwd(ctypes.byref(d) if d is not None else None, p["q"], p["k"],
+                                 p["v"], p["lam"], p["beta"], st0, p["dO"], p["dq"], p["dk"],
+                                 p["dv"], p["dlam"], p["dbeta"], dst0, p["ws"], ws_bytes, None)
+
+
+def test_bwd_workspace_bytes_layout():
+    up = lambda x: (x + 255) // 256 * 256
+    for B, H, N, F, D, M in ((2, 3, 70, 32, 16, 16), (4, 16, 2048, 128, 128, 64),
+                             (1, 1, 1, 16, 256, 128)):
+        S, nck = B * H, (N + 31) // 32
+        want = (up(S * nck * M * (F + D + 1) * 8) + up(S * N * (M // 2) * 8)
+                + up((M // 16) * S * N * (2 * F + D) * 4) + up(S * M * 16))
+        d = desc(B=B, H=H, N=N, F=F, Dv=D, M=M)
+        assert ia.lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(d)) == want
+    assert ia.lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(desc(N=0))) == 0
+    assert ia.lib.ia_prefill_bwd_workspace_bytes(None) == 0
+
+
+def test_bwd_validation():
+    d = desc()
+    assert bwd(None) == 1
+    assert bwd(desc(N=0)) == 2
+    assert bwd(desc(M=20)) == 7
+    assert bwd(desc(bidir=True)) == 7
+    for name in ("q", "k", "v", "lam", "beta", "dO", "dq", "dk", "dv", "dlam", "dbeta"):
+        assert bwd(d, **{name: P(0)}) == 1, name
+        assert bwd(d, **{name: addr(["q", "k", "v", "lam", "beta", "dO", "dq", "dk", "dv",
+                                     "dlam", "dbeta"].index(name), 8)}) == 4, name
+    need = ia.lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(d))
+    assert bwd(d, ws=P(0)) == 9
+    assert bwd(d, ws_bytes=need - 1) == 9
+    assert bwd(d, ws=addr(14, 8)) == 4
+    # outputs overlapping inputs, each other or the workspace
+    assert bwd(d, dq=addr(0)) == 5
+    assert bwd(d, dv=addr(5)) == 5
+    assert bwd(d, dk=addr(6, 64)) == 5
+    assert bwd(d, dlam=addr(14, 256)) == 5
+    # a state with a missing tensor, and a state gradient overlapping an input
+    assert bwd(d, st0=ctypes.pointer(ia.IAState(addr(10).value, addr(11).value, 0))) == 1
+    assert bwd(d, dst0=ctypes.pointer(ia.IAState(addr(0).value, addr(11).value,
+                                                 addr(12).value))) == 5
