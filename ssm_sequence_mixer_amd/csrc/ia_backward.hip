@@ -53,38 +53,29 @@ __device__ __forceinline__ float uniform(float x, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
-// Sums NV values (NV = 8 or 16) over the 64 lanes of a wave by recursive halving: after the
-// exchange steps lane l holds, in v[0], the wave total of value (l / (64 / NV)) % NV.
-// One halving step: lanes with `BIT` set keep the upper HALF values, the others the lower,
-// each adding its partner's copy of the half it keeps.
-template <int NV, int HALF, int BIT>
-__device__ __forceinline__ void halve(float (&v)[NV], int lane) {
-  const bool hi = lane & BIT;
-#pragma unroll
-  for (int i = 0; i < HALF; ++i) {
-    const float keep = hi ? v[i + HALF] : v[i];
-    const float send = hi ? v[i] : v[i + HALF];
-    v[i] = keep + __shfl_xor(send, BIT, 64);
-  }
+// Wave total of v as a wave-uniform scalar, through DPP moves (no LDS round trip): swaps
+// within quads (lane ^ 1, lane ^ 2), then mirrors within half-rows and rows, leave every lane
+// of a 16-lane row with the row's sum; row_bcast:15 and row_bcast:31 then fold rows 0-1 into
+// 1 and rows 0-3 into 3, so lane 63 holds the total.
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_plus(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF,
+                                                        false));
+}
+__device__ __forceinline__ float wave_total(float v) {
+  v = dpp_plus<0xB1>(v);         // quad_perm [1,0,3,2]
+  v = dpp_plus<0x4E>(v);         // quad_perm [2,3,0,1]
+  v = dpp_plus<0x141>(v);        // row_half_mirror
+  v = dpp_plus<0x140>(v);        // row_mirror
+  v = dpp_plus<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_plus<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return uniform(v, 63);
 }
 template <int NV>
-__device__ __forceinline__ void wave_sum(float (&v)[NV], int lane) {
-  static_assert(NV == 8 || NV == 16, "8 or 16 values");
-  if constexpr (NV == 16) {
-    halve<NV, 8, 32>(v, lane);
-    halve<NV, 4, 16>(v, lane);
-    halve<NV, 2, 8>(v, lane);
-    halve<NV, 1, 4>(v, lane);
-  } else {
-    halve<NV, 4, 32>(v, lane);
-    halve<NV, 2, 16>(v, lane);
-    halve<NV, 1, 8>(v, lane);
-  }
+__device__ __forceinline__ void wave_totals(float (&v)[NV]) {
 #pragma unroll
-  for (int bit = 64 / NV / 2; bit >= 1; bit >>= 1) v[0] += __shfl_xor(v[0], bit, 64);
+  for (int i = 0; i < NV; ++i) v[i] = wave_total(v[i]);
 }
-// Value `i` of a wave_sum<kRed> result, as a wave-uniform scalar.
-__device__ __forceinline__ float sum_get(float r, int i) { return uniform(r, (64 / kRed) * i); }
 
 struct Slice {
   int lane, wave, slice, grp, b, h, m0, groups;
@@ -247,8 +238,9 @@ __device__ __forceinline__ void stage_store(const RowLayout& l, int tb, const ui
 }
 
 __device__ __forceinline__ float lds_in(const unsigned char* seg, int i, int bf16) {
-  return bf16 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(seg)[i])
-              : reinterpret_cast<const float*>(seg)[i];
+  // bf16: the 16 bits at 2i, widened; fp32: the word at 4i (bf16 is wave-uniform)
+  if (bf16) return bf16_to_f32(reinterpret_cast<const uint16_t*>(seg)[i]);
+  return reinterpret_cast<const float*>(seg)[i];
 }
 
 // One token's inputs at the lane's columns, from its staged row: features of q and k (zero
@@ -262,8 +254,9 @@ struct Token {
     const bool ident = a.opt & kOptIdentity;
 #pragma unroll
     for (int j = 0; j < NF; ++j) {
-      const int r = s.lane + 64 * j;
-      const bool ok = r < a.F;
+      // columns past F read column F-1 (no branch) and are then zeroed
+      const bool ok = s.lane + 64 * j < a.F;
+      const int r = min(s.lane + 64 * j, a.F - 1);
       const float x = ok ? lds_in(row + l.q, r, a.in_bf16) : 0.f;
       const float y = ok ? lds_in(row + l.k, r, a.in_bf16) : 0.f;
       // phi(x) = x + 1 above 0, exp(x) at or below; phi'(x) = 1 above 0, exp(x) at or below
@@ -275,8 +268,8 @@ struct Token {
     }
 #pragma unroll
     for (int j = 0; j < ND; ++j) {
-      const int c = s.lane + 64 * j;
-      const bool ok = c < a.D;
+      const bool ok = s.lane + 64 * j < a.D;
+      const int c = min(s.lane + 64 * j, a.D - 1);
       v[j] = ok ? lds_in(row + l.v, c, a.in_bf16) : 0.f;
       g[j] = ok ? lds_in(row + l.g, c, a.out_bf16) : 0.f;
     }
@@ -333,13 +326,13 @@ __global__ void __launch_bounds__(kThreads) bwd_forward_kernel(const BwdArgs a) 
         red[4 * i + 2] = sp.x;
         red[4 * i + 3] = sp.y;
       }
-      wave_sum<kRed>(red, s.lane);
+      wave_totals(red);
       // den_t and g_t . num_t over this wave's modes: Re(a eta) and Re(a sum_j g_j Gam_j)
       float den = 0.f, gn = 0.f;
 #pragma unroll
       for (int i = 0; i < kModesPerWave; ++i) {
-        const float2 am = make_float2(sum_get(red[0], 4 * i), sum_get(red[0], 4 * i + 1));
-        const float2 sm = make_float2(sum_get(red[0], 4 * i + 2), sum_get(red[0], 4 * i + 3));
+        const float2 am = make_float2(red[4 * i], red[4 * i + 1]);
+        const float2 sm = make_float2(red[4 * i + 2], red[4 * i + 3]);
         den += am.x * st.E[i].x - am.y * st.E[i].y;
         gn += am.x * sm.x - am.y * sm.y;
       }
@@ -444,7 +437,7 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(const BwdArgs a) 
         red[4 * i + 2] = hp.x;
         red[4 * i + 3] = hp.y;
       }
-      wave_sum<kRed>(red, s.lane);
+      wave_totals(red);
       float dfq[NF], dfk[NF], dv[ND];
 #pragma unroll
       for (int j2 = 0; j2 < NF; ++j2) dfq[j2] = dfk[j2] = 0.f;
@@ -452,8 +445,8 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(const BwdArgs a) 
       for (int j2 = 0; j2 < ND; ++j2) dv[j2] = 0.f;
 #pragma unroll
       for (int i = 0; i < kModesPerWave; ++i) {
-        const float2 am = make_float2(sum_get(red[0], 4 * i), sum_get(red[0], 4 * i + 1));
-        const float2 hm = make_float2(sum_get(red[0], 4 * i + 2), sum_get(red[0], 4 * i + 3));
+        const float2 am = make_float2(red[4 * i], red[4 * i + 1]);
+        const float2 hm = make_float2(red[4 * i + 2], red[4 * i + 3]);
         // gradient of a[m]: sum_j dnum_j conj(Gam_mj) + dden conj(eta_m)
         const float2 ga = cadd(cscale(rc, hm), cscale(dd, conjf2(cur.E[i])));
         const float2 ca = conjf2(am);
@@ -546,12 +539,12 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(const BwdArgs a) 
     red[4 * i + 2] = gb[i].x;
     red[4 * i + 3] = gb[i].y;
   }
-  wave_sum<kRed>(red, s.lane);
+  wave_totals(red);
 #pragma unroll
   for (int i = 0; i < kModesPerWave; ++i) {
     const size_t m = (size_t)s.slice * a.M + s.m0 + i;
-    const float2 l = make_float2(sum_get(red[0], 4 * i), sum_get(red[0], 4 * i + 1));
-    const float2 bb = make_float2(sum_get(red[0], 4 * i + 2), sum_get(red[0], 4 * i + 3));
+    const float2 l = make_float2(red[4 * i], red[4 * i + 1]);
+    const float2 bb = make_float2(red[4 * i + 2], red[4 * i + 3]);
     if (s.lane == 0) {
       a.lpart[2 * m] = l;
       a.lpart[2 * m + 1] = bb;
