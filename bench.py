@@ -8,9 +8,8 @@ whole synthetic batch, through ia_prefill_fwd: per-head tables, segment end stat
 scan and the chunked MFMA pass with outputs.  Inputs are resident in HBM before timing starts.
 Prints one JSON line: prefill tokens/s, the roofline position of the dominant kernel
 (measured with HIP events around that kernel, over a timed loop), decode-step latency at
-batch 1/16/64 (hipGraph-captured and eager), the backward pass of the causal workloads (its
-time and its position against the fp32 vector peak), and the CPU oracle's throughput on a
-sample.
+batch 1/16/64 (hipGraph-captured and eager), the backward pass of the same layer (its time and
+its position against the fp32 vector peak), and the CPU oracle's throughput on a sample.
 """
 from __future__ import annotations
 
@@ -232,8 +231,9 @@ def bwd_alg_flops(B, N, H, F, D, M):
     return float(14 * (F + D) + 44 * F + 41 * D) * M * B * N * H
 
 
-def bench_backward(torch, ia, inp, steps=5, warmup=2):
-    """ia_prefill_bwd over the prefill workload (bf16 q, k, v; fp32 dO), from a zero state."""
+def bench_backward(torch, ia, inp, bidir=False, steps=5, warmup=2):
+    """ia_prefill_bwd over the prefill workload (bf16 q, k, v; fp32 dO), from a zero state
+    (both directions for the bidirectional workload)."""
     sh = inp["shape"]
     B, H, N, F, D, M = sh["B"], sh["H"], sh["N"], sh["F"], sh["D"], sh["M"]
     q, k, v = (torch.from_numpy(inp[n]).to(torch.bfloat16).cuda() for n in "qkv")
@@ -241,8 +241,10 @@ def bench_backward(torch, ia, inp, steps=5, warmup=2):
     beta = torch.from_numpy(inp["beta"]).cuda()
     g = torch.Generator(device="cpu").manual_seed(550)
     dO = torch.randn((B, N, H, D), generator=g, dtype=torch.float32).cuda()
-    desc = ia.make_desc(B, H, N, F, D, M, ia.IA_BF16, ia.IA_F32)
+    desc = ia.make_desc(B, H, N, F, D, M, ia.IA_BF16, ia.IA_F32, bidir=bidir)
     ws = torch.empty(ia.ia_prefill_bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    if N > 16384:   # the long genomic sequence: one timed step (a step takes seconds' share)
+        steps, warmup = 1, 1
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dl = torch.empty((H, M), dtype=torch.complex64, device="cuda")
     db = torch.empty_like(dl)
@@ -260,7 +262,7 @@ def bench_backward(torch, ia, inp, steps=5, warmup=2):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) / steps * 1e3
-    fl = bwd_alg_flops(B, N, H, F, D, M)
+    fl = bwd_alg_flops(B, N, H, F, D, M) * (2 if bidir else 1)
     return {"us_per_step": us, "tokens_per_s": B * N / (us * 1e-6), "steps": steps,
             "dtype": "bf16 in, fp32 state and arithmetic", "workspace_bytes": ws.numel(),
             "alu": {"bound": "alu", "achieved": fl / (us * 1e-6) / 1e12,
@@ -344,8 +346,8 @@ def main():
     pf = bench_prefill(args, torch, ia, W)
     dec = None if args.no_decode else bench_decode(torch, ia, W)
     bwd = None
-    if not args.no_backward and not pf["cfg"]["bidirectional"]:
-        bwd = bench_backward(torch, ia, pf["inp"])
+    if not args.no_backward:
+        bwd = bench_backward(torch, ia, pf["inp"], bidir=pf["cfg"]["bidirectional"])
     cpu = None if args.no_cpu else cpu_baseline(pf["inp"], pf["cfg"]["bidirectional"])
     line = {
         "metric": "IA layer fwd tokens/s (prefill) + decode step latency; % of MFMA/HBM roofline",

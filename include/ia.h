@@ -222,7 +222,9 @@ size_t ia_prefill_bwd_workspace_bytes(const ia_desc* desc);
  * Readout gradient: dnum = dO / c and, where den >= den_clamp (the branch the forward takes
  * for den itself), dden = -sum_j dO_j num_j / c^2, with c = max(den, den_clamp); below the
  * clamp den has no gradient.  IA_FLAG_NO_DEN: dnum = dO, dden = 0.  IA_FLAG_IDENTITY_FEATURES:
- * phi' = 1.  IA_FLAG_BIDIR: IA_ERR_UNSUPPORTED.
+ * phi' = 1.  IA_FLAG_BIDIR: gradients of o = IA(x) + flip_t(IA(flip_t x)) (both directions from
+ * zero), the reversed walk's added onto the forward's; st0 and dst0 must then be NULL
+ * (IA_ERR_UNSUPPORTED otherwise).
  * Accuracy: the rebuild grows fp32 rounding by at most |lambda|^-31 inside an interval; for
  * |lambda| >= 0.9 that is below 30x (an S4D-Lin lambda = exp(dt(-1/2 + i pi m)) with
  * dt <= 0.1 has |lambda| >= 0.95).

@@ -234,3 +234,14 @@ def prefill_bwd(q, k, v, lam, beta, dO, state=None, clamp=1e-6, no_den=False, sl
         dq[b, :, h], dk[b, :, h], dv[b, :, h] = a, bk, c
         dl[b, h], db[b, h], dU[b, h], dG[b, h], de[b, h] = l, be, u, g, e
     return dq, dk, dv, dl, db, (dU, dG, de)
+
+
+def bidir_bwd(q, k, v, lam, beta, dO, clamp=1e-6, no_den=False, slices=None, threads=1):
+    """Gradients of ``bidir`` (o = IA(x) + flip_t(IA(flip_t x)), both from zero state): the
+    causal gradients for dO plus, flipped back, those of the reversed sequence for flip_t(dO).
+    Returns (dq, dk, dv, dlam [B,H,M], dbeta [B,H,M])."""
+    fl = lambda a: np.ascontiguousarray(np.asarray(a)[:, ::-1])
+    f = prefill_bwd(q, k, v, lam, beta, dO, None, clamp, no_den, slices, threads)
+    r = prefill_bwd(fl(q), fl(k), fl(v), lam, beta, fl(dO), None, clamp, no_den, slices, threads)
+    return (f[0] + r[0][:, ::-1], f[1] + r[1][:, ::-1], f[2] + r[2][:, ::-1], f[3] + r[3],
+            f[4] + r[4])

@@ -286,14 +286,16 @@ def decode(q_t, k_t, v_t, lam, beta, state, out_dtype=None,
 
 
 def prefill_bwd(q, k, v, lam, beta, dO, state0=None, den_clamp=1e-6, no_den=False,
-                identity_features=False, want_state_grad=False, stream=None, workspace=None):
-    """Gradients of the causal layer for dL/do = dO: allocates the outputs (and the workspace)
-    with torch and runs ia_prefill_bwd.  Returns (dq, dk, dv, dlam, dbeta, dstate0 or None)."""
+                identity_features=False, want_state_grad=False, stream=None, workspace=None,
+                bidir=False):
+    """Gradients of the layer (causal, or bidirectional with bidir=True) for dL/do = dO:
+    allocates the outputs (and the workspace) with torch and runs ia_prefill_bwd.  Returns
+    (dq, dk, dv, dlam, dbeta, dstate0 or None)."""
     import torch
     B, N, H, F = q.shape
     Dv, M = v.shape[3], lam.shape[1]
     desc = make_desc(B, H, N, F, Dv, M, dtype_code(q.dtype), dtype_code(dO.dtype), den_clamp,
-                     no_den=no_den, identity_features=identity_features)
+                     bidir=bidir, no_den=no_den, identity_features=identity_features)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dlam = torch.empty((H, M), dtype=torch.complex64, device=q.device)
     dbeta = torch.empty_like(dlam)

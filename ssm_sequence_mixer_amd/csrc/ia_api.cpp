@@ -364,9 +364,10 @@ ia_status ia_prefill_bwd(const ia_desc* d, const void* q, const void* k, const v
                          void* stream) {
   ia_status s = check_desc(d, true);
   if (s != IA_OK) return s;
-  if (d->flags & IA_FLAG_BIDIR) return IA_ERR_UNSUPPORTED;
+  const bool bidir = d->flags & IA_FLAG_BIDIR;
   if (!q || !k || !v || !lambda || !beta || !dO || !dq || !dk || !dv || !dlambda || !dbeta)
     return IA_ERR_NULL;
+  if (bidir && (st0 || dst0)) return IA_ERR_UNSUPPORTED;   // both directions start from zero
   for (const void* p : {q, k, v, lambda, beta, dO, static_cast<const void*>(dq),
                         static_cast<const void*>(dk), static_cast<const void*>(dv),
                         static_cast<const void*>(dlambda), static_cast<const void*>(dbeta)})
@@ -438,7 +439,16 @@ ia_status ia_prefill_bwd(const ia_desc* d, const void* q, const void* k, const v
   a.opt = kernel_opt(d);
   a.clamp = d->den_clamp;
   a.tb = ia::bwd_block_tokens(d->F, d->Dv, d->M, a.in_bf16, a.out_bf16);
-  return launch_status(ia::launch_prefill_bwd(a, static_cast<hipStream_t>(stream)));
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = ia::launch_prefill_bwd(a, hs);
+  if (e == hipSuccess && bidir) {
+    // o = IA(x) + flip(IA(flip x)): the reversed walk's gradients are added on (the workspace
+    // is reused in stream order)
+    a.dir = 1;
+    a.accumulate = 1;
+    e = ia::launch_prefill_bwd(a, hs);
+  }
+  return launch_status(e);
 }
 
 ia_status ia_decode_step(const ia_desc* d, const void* q_t, const void* k_t, const void* v_t,

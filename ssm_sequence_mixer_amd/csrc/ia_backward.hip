@@ -206,7 +206,8 @@ __device__ __forceinline__ void stage_issue(const BwdArgs& a, const Slice& s, co
       const int j = e / vec_row, o = 16 * (e - j * vec_row);
       const int t = t_first + step * j;
       if (t >= 0 && t < a.N) {
-        const size_t row = ((size_t)s.b * a.N + t) * a.H + s.h;
+        // walk index t is position t, or N-1-t for the reverse direction
+        const size_t row = ((size_t)s.b * a.N + (a.dir ? a.N - 1 - t : t)) * a.H + s.h;
         const char* src;
         if (o < l.k)
           src = static_cast<const char*>(a.q) + row * a.F * ei + o;
@@ -578,13 +579,21 @@ __global__ void __launch_bounds__(256) bwd_reduce_kernel(const BwdArgs a) {
     const size_t t = rem / W;
     const int col = (int)(rem - t * W);
     const size_t b = sl / a.H, h = sl % a.H;
-    const size_t row = (b * a.N + t) * a.H + h;
-    if (col < a.F)
-      store_out(a.dq, row * a.F + col, sum, a.in_bf16);
-    else if (col < 2 * a.F)
-      store_out(a.dk, row * a.F + col - a.F, sum, a.in_bf16);
-    else
-      store_out(a.dv, row * a.D + col - 2 * a.F, sum, a.in_bf16);
+    const size_t row = (b * a.N + (a.dir ? a.N - 1 - t : t)) * a.H + h;
+    void* dst;
+    size_t i;
+    if (col < a.F) {
+      dst = a.dq;
+      i = row * a.F + col;
+    } else if (col < 2 * a.F) {
+      dst = a.dk;
+      i = row * a.F + col - a.F;
+    } else {
+      dst = a.dv;
+      i = row * a.D + col - 2 * a.F;
+    }
+    if (a.accumulate) sum += load_in(dst, i, a.in_bf16);
+    store_out(dst, i, sum, a.in_bf16);
   }
   const size_t hm = (size_t)a.H * a.M;
   for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < hm;
@@ -593,6 +602,10 @@ __global__ void __launch_bounds__(256) bwd_reduce_kernel(const BwdArgs a) {
     for (int b = 0; b < a.B; ++b) {
       l = cadd(l, a.lpart[2 * ((size_t)b * hm + e)]);
       bb = cadd(bb, a.lpart[2 * ((size_t)b * hm + e) + 1]);
+    }
+    if (a.accumulate) {
+      l = cadd(l, a.dlam[e]);
+      bb = cadd(bb, a.dbeta[e]);
     }
     a.dlam[e] = l;
     a.dbeta[e] = bb;

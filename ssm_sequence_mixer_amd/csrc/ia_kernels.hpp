@@ -128,6 +128,8 @@ struct BwdArgs {
   int in_bf16, out_bf16, opt;
   float clamp;
   int tb;                         // tokens per staged block (bwd_block_tokens)
+  int dir;                        // 1: walk index t is position N-1-t (reversed sequence)
+  int accumulate;                 // 1: add the gradients onto dq, dk, dv, dlam, dbeta
 };
 
 struct BwdLayout {

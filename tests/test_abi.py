@@ -249,7 +249,8 @@ def test_bwd_validation():
     assert bwd(None) == 1
     assert bwd(desc(N=0)) == 2
     assert bwd(desc(M=20)) == 7
-    assert bwd(desc(bidir=True)) == 7
+    assert bwd(desc(bidir=True), st0=state()) == 7
+    assert bwd(desc(bidir=True), dst0=state(20)) == 7
     for name in ("q", "k", "v", "lam", "beta", "dO", "dq", "dk", "dv", "dlam", "dbeta"):
         assert bwd(d, **{name: P(0)}) == 1, name
         assert bwd(d, **{name: addr(["q", "k", "v", "lam", "beta", "dO", "dq", "dk", "dv",

@@ -207,3 +207,25 @@ def test_backward_1p3b_workload_sampled():
     for n, e in errs.items():
         report(f"bwd 1.3b {n}", e)
     assert max(errs.values()) < TOL_BF16, errs
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_bidirectional(dtype):
+    """The bidirectional layer (both directions from zero): the causal gradients plus those of
+    the reversed walk, against oracle.bidir_bwd."""
+    import torch
+    ia = _ia()
+    B, H, N, F, D, M = 2, 2, 77, 32, 32, 32
+    inp = W.make_inputs(B, H, N, F, D, M, dtype=dtype, seed=560)
+    dO = np.random.default_rng(561).standard_normal((B, N, H, D)).astype(np.float32)
+    if dtype == "bf16":
+        dO = W.round_bf16(dO)
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tag(f"backward bidirectional {dtype}")
+    q, k, v = (dev(inp[n], td) for n in "qkv")
+    r = ia.prefill_bwd(q, k, v, dev(inp["lam"]), dev(inp["beta"]), dev(dO, td), bidir=True)
+    torch.cuda.synchronize()
+    got = tuple(host(x) for x in r[:5]) + (None,)
+    ref = oracle.bidir_bwd(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"], dO, threads=4)
+    _compare(got, tuple(ref) + (None,), TOL_BF16 if dtype == "bf16" else TOL_F32,
+             f"bwd bidir {dtype}")

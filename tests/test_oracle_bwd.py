@@ -150,3 +150,39 @@ def test_planted_backward_mistake_fails_a_pin(mutant, tmp_path):
     for c, nd in ((_case(1), False), (_case(4, clamped=True), False), (_case(5), True)):
         worst = max(worst, max(_fd_errors(c, no_den=nd, bwd=bwd).values()))
     assert not worst < FD_TOL, f"{mutant} passed every finite-difference pin"
+
+
+def test_bidirectional_backward_matches_finite_differences():
+    """oracle.bidir_bwd against central differences of the bidirectional forward (oracle.bidir)
+    on q, k, v and lambda."""
+    rng = np.random.default_rng(9)
+    B, N, H, F, D, M = 1, 6, 1, 3, 2, 3
+    q, k = rng.standard_normal((B, N, H, F)), rng.standard_normal((B, N, H, F))
+    v = rng.standard_normal((B, N, H, D))
+    lam = (rng.uniform(0.6, 0.95, M) * np.exp(1j * rng.uniform(-0.3, 0.3, M)))[None]
+    beta = (1.0 + 0.2j * rng.uniform(-1, 1, M))[None]
+    dO = rng.standard_normal((B, N, H, D))
+    loss = lambda q_, k_, v_, l_: float(np.sum(dO * oracle.bidir(q_, k_, v_, l_, beta)))
+    dq, dk, dv, dl, _ = oracle.bidir_bwd(q, k, v, lam, beta, dO)
+    errs = []
+    for arr, grad, put in ((q, dq, lambda a: loss(a, k, v, lam)), (k, dk, lambda a: loss(q, a, v, lam)),
+                           (v, dv, lambda a: loss(q, k, a, lam))):
+        fd = np.empty(arr.shape)
+        for idx in np.ndindex(arr.shape):
+            h = 1e-6 * max(1.0, abs(arr[idx]))
+            up, dn = arr.copy(), arr.copy()
+            up[idx] += h
+            dn[idx] -= h
+            fd[idx] = (put(up) - put(dn)) / (2 * h)
+        errs.append(np.max(np.abs(fd - grad)) / np.max(np.abs(grad)))
+    fd = np.zeros(M, dtype=np.complex128)
+    for m in range(M):
+        for part, unit in ((0, 1.0), (1, 1j)):
+            h = 1e-7
+            up, dn = lam.copy(), lam.copy()
+            up[0, m] += h * unit
+            dn[0, m] -= h * unit
+            d = (loss(q, k, v, up) - loss(q, k, v, dn)) / (2 * h)
+            fd[m] += d if part == 0 else 1j * d
+    errs.append(np.max(np.abs(fd - dl[0, 0])) / np.max(np.abs(dl[0, 0])))
+    assert max(errs) < FD_TOL, errs
