@@ -26,6 +26,8 @@
 // a wave owns state columns l, l + 64, ... of U (F wide) and Gam (D wide) for all four of its
 // modes, so every sum over modes of a column is a lane's own, and every sum over a mode's
 // columns is one 16-value wave reduction per token.
+#include <algorithm>
+
 #include "ia_device.hpp"
 #include "ia_kernels.hpp"
 
@@ -78,7 +80,8 @@ __device__ __forceinline__ void wave_totals(float (&v)[NV]) {
 }
 
 struct Slice {
-  int lane, wave, slice, grp, b, h, m0, groups;
+  int lane, wave, slice, grp, seg, b, h, m0, groups;
+  int lo, hi;   // the segment's tokens [lo, hi)
 };
 
 __device__ __forceinline__ Slice slice_of(const BwdArgs& a) {
@@ -86,8 +89,11 @@ __device__ __forceinline__ Slice slice_of(const BwdArgs& a) {
   s.lane = threadIdx.x & 63;
   s.wave = threadIdx.x >> 6;
   s.groups = a.M / kModesPerWg;
-  s.slice = blockIdx.x / s.groups;
-  s.grp = blockIdx.x % s.groups;
+  s.seg = blockIdx.x % a.nseg;
+  s.slice = blockIdx.x / a.nseg / s.groups;
+  s.grp = blockIdx.x / a.nseg % s.groups;
+  s.lo = s.seg * a.seg_len;
+  s.hi = min(a.N, s.lo + a.seg_len);
   s.b = s.slice / a.H;
   s.h = s.slice % a.H;
   s.m0 = s.grp * kModesPerWg + s.wave * kModesPerWave;
@@ -132,15 +138,28 @@ struct State {
       E[i] = E0[m];
     }
   }
-  // Checkpoint `ck` of this slice: per mode, F values of U, D of Gam, then eta.
-  __device__ float2* ckpt_row(const BwdArgs& a, const Slice& s, int ck, int i) const {
-    const int nck = (a.N + kBwdCheckpoint - 1) / kBwdCheckpoint;
-    return a.ckpt + (((size_t)s.slice * nck + ck) * a.M + s.m0 + i) * (a.F + a.D + 1);
+  // Row block `idx` of a [..][M][F + D + 1] array: per mode, F values of U, D of Gam, then
+  // eta (checkpoints: idx = slice * checkpoints + k; segment carries: slice * nseg + seg).
+  __device__ static float2* row_at(const BwdArgs& a, float2* base, size_t idx, const Slice& s,
+                                   int i) {
+    return base + (idx * a.M + s.m0 + i) * (a.F + a.D + 1);
+  }
+  __device__ static size_t ckpt_idx(const BwdArgs& a, const Slice& s, int ck) {
+    return (size_t)s.slice * ((a.N + kBwdCheckpoint - 1) / kBwdCheckpoint) + ck;
+  }
+  __device__ static size_t seg_idx(const BwdArgs& a, const Slice& s) {
+    return (size_t)s.slice * a.nseg + s.seg;
   }
   __device__ void store_ckpt(const BwdArgs& a, const Slice& s, int ck) const {
+    store_rows(a, a.ckpt, ckpt_idx(a, s, ck), s);
+  }
+  __device__ void load_ckpt(const BwdArgs& a, const Slice& s, int ck) {
+    load_rows(a, a.ckpt, ckpt_idx(a, s, ck), s);
+  }
+  __device__ void store_rows(const BwdArgs& a, float2* base, size_t idx, const Slice& s) const {
 #pragma unroll
     for (int i = 0; i < kModesPerWave; ++i) {
-      float2* row = ckpt_row(a, s, ck, i);
+      float2* row = row_at(a, base, idx, s, i);
 #pragma unroll
       for (int j = 0; j < NF; ++j)
         if (s.lane + 64 * j < a.F) row[s.lane + 64 * j] = U[i][j];
@@ -150,10 +169,10 @@ struct State {
       if (s.lane == 0) row[a.F + a.D] = E[i];
     }
   }
-  __device__ void load_ckpt(const BwdArgs& a, const Slice& s, int ck) {
+  __device__ void load_rows(const BwdArgs& a, float2* base, size_t idx, const Slice& s) {
 #pragma unroll
     for (int i = 0; i < kModesPerWave; ++i) {
-      const float2* row = ckpt_row(a, s, ck, i);
+      const float2* row = row_at(a, base, idx, s, i);
 #pragma unroll
       for (int j = 0; j < NF; ++j)
         U[i][j] = s.lane + 64 * j < a.F ? row[s.lane + 64 * j] : make_float2(0.f, 0.f);
@@ -167,7 +186,7 @@ struct State {
 
 // Token rows staged in LDS, as raw bytes in the inputs' own dtypes: one token's q[F], k[F],
 // v[D], g[D] (g = dL/do) and, for the reverse sweep, the per-wave partials of den and g . num
-// of that token (M/4 float pairs), each segment a multiple of 16 bytes.  Blocks of
+// of that token (M/2 float pairs), each segment a multiple of 16 bytes.  Blocks of
 // BwdArgs::tb rows are double-buffered: the 16-byte loads of the next block are issued
 // before the current block is processed and land in LDS after it, so their latency hides
 // behind a block of tokens.
@@ -291,20 +310,27 @@ __global__ void __launch_bounds__(kThreads) bwd_forward_kernel(const BwdArgs a) 
     lam[i] = a.lam[(size_t)s.h * a.M + s.m0 + i];
     bet[i] = a.beta[(size_t)s.h * a.M + s.m0 + i];
   }
+  // the segment's start state: zeros for the local pass (its end state from zero feeds the
+  // carry), else the caller's state for segment 0 and the carried state after it
   State<NF, ND> st;
-  st.load_state(a, a.U0, a.G0, a.E0, s);
+  if (a.local)
+    st.zero();
+  else if (s.seg == 0)
+    st.load_state(a, a.U0, a.G0, a.E0, s);
+  else
+    st.load_rows(a, a.cstate, State<NF, ND>::seg_idx(a, s), s);
   const int parts = a.M / kModesPerWave;
-  const int nblk = (a.N + TB - 1) / TB;
+  const int nblk = (s.hi - s.lo + TB - 1) / TB;
   uint4 pre[P];
-  stage_issue(a, s, L, 0, 1, TB, pre);
+  stage_issue(a, s, L, s.lo, 1, TB, pre);
   stage_store(L, TB, pre, smem);
   __syncthreads();
   for (int blk = 0; blk < nblk; ++blk) {
     const unsigned char* rows = smem + (blk & 1) * TB * R;
-    if (blk + 1 < nblk) stage_issue(a, s, L, (blk + 1) * TB, 1, TB, pre);
+    if (blk + 1 < nblk) stage_issue(a, s, L, s.lo + (blk + 1) * TB, 1, TB, pre);
     for (int j = 0; j < TB; ++j) {
-      const int t = blk * TB + j;
-      if (t >= a.N) break;
+      const int t = s.lo + blk * TB + j;
+      if (t >= s.hi) break;
       Token<NF, ND> x;
       x.load(a, s, L, rows + j * R);
       float red[kRed];
@@ -327,6 +353,7 @@ __global__ void __launch_bounds__(kThreads) bwd_forward_kernel(const BwdArgs a) 
         red[4 * i + 2] = sp.x;
         red[4 * i + 3] = sp.y;
       }
+      if (a.local) continue;   // the local pass only carries the state
       wave_totals(red);
       // den_t and g_t . num_t over this wave's modes: Re(a eta) and Re(a sum_j g_j Gam_j)
       float den = 0.f, gn = 0.f;
@@ -348,6 +375,7 @@ __global__ void __launch_bounds__(kThreads) bwd_forward_kernel(const BwdArgs a) 
       __syncthreads();
     }
   }
+  if (a.local) st.store_rows(a, a.cstate, State<NF, ND>::seg_idx(a, s), s);
 }
 
 template <int NF, int ND>
@@ -374,27 +402,26 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(const BwdArgs a) 
   const int parts = a.M / kModesPerWave;
   // adjoints of U, Gam, eta (eta's is wave-uniform), and the lane's share of the lambda and
   // beta gradients of each mode
-  float2 Ub[kModesPerWave][NF], Gb[kModesPerWave][ND], Eb[kModesPerWave];
+  // Adjoints entering the segment's last token: zeros for the last segment and for the local
+  // pass (whose adjoints leaving the segment feed the carry), else the carried ones.
+  State<NF, ND> adj;
+  if (a.local || s.seg == a.nseg - 1)
+    adj.zero();
+  else
+    adj.load_rows(a, a.cadj, State<NF, ND>::seg_idx(a, s), s);
   float2 gl[kModesPerWave], gb[kModesPerWave];
 #pragma unroll
-  for (int i = 0; i < kModesPerWave; ++i) {
-#pragma unroll
-    for (int j = 0; j < NF; ++j) Ub[i][j] = make_float2(0.f, 0.f);
-#pragma unroll
-    for (int j = 0; j < ND; ++j) Gb[i][j] = make_float2(0.f, 0.f);
-    Eb[i] = gl[i] = gb[i] = make_float2(0.f, 0.f);
-  }
-  const int nck = (a.N + kBwdCheckpoint - 1) / kBwdCheckpoint;
-  const int nblk = (a.N + TB - 1) / TB;
+  for (int i = 0; i < kModesPerWave; ++i) gl[i] = gb[i] = make_float2(0.f, 0.f);
+  const int nblk = (s.hi - s.lo + TB - 1) / TB;
   uint4 pre[P];
-  stage_issue(a, s, L, a.N - 1, -1, TB, pre);
+  stage_issue(a, s, L, s.hi - 1, -1, TB, pre);
   stage_store(L, TB, pre, smem);
   State<NF, ND> cur;
-  cur.load_ckpt(a, s, nck - 1);   // the state after the last token
+  cur.load_ckpt(a, s, (s.hi - 1) / kBwdCheckpoint);   // the state after the segment's last token
   __syncthreads();
   for (int blk = 0; blk < nblk; ++blk) {
     const unsigned char* rows = smem + (blk & 1) * TB * R;
-    const int t_hi = a.N - 1 - blk * TB;   // tokens t_hi, t_hi - 1, ... of this block
+    const int t_hi = s.hi - 1 - blk * TB;   // tokens t_hi, t_hi - 1, ... of this block
     if (blk + 1 < nblk) stage_issue(a, s, L, t_hi - TB, -1, TB, pre);
     // The readout's gradient factors of the block's tokens, dnum = g rc and dden (0 below the
     // clamp, and without a denominator): the 8 lanes 8j..8j+7 sum token j's partials of den
@@ -403,7 +430,7 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(const BwdArgs a) 
     if (!noden) {
       const int jt = s.lane >> 3, sub = s.lane & 7;
       float2 p = make_float2(0.f, 0.f);
-      if (jt < TB && t_hi - jt >= 0) {
+      if (jt < TB && t_hi - jt >= s.lo) {
         const float2* dp = reinterpret_cast<const float2*>(rows + jt * R + L.p);
 #pragma unroll
         for (int k = 0; k < kMaxModes / kModesPerWave / 8; ++k)
@@ -420,7 +447,7 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(const BwdArgs a) 
     }
     for (int j = 0; j < TB; ++j) {
       const int t = t_hi - j;
-      if (t < 0) break;
+      if (t < s.lo) break;
       const unsigned char* row = rows + j * R;
       Token<NF, ND> x;
       x.load(a, s, L, row);
@@ -453,19 +480,19 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(const BwdArgs a) 
         const float2 ca = conjf2(am);
 #pragma unroll
         for (int j2 = 0; j2 < NF; ++j2) {
-          Ub[i][j2] = cadd(Ub[i][j2], cscale(x.fq[j2], ga));
+          adj.U[i][j2] = cadd(adj.U[i][j2], cscale(x.fq[j2], ga));
           dfq[j2] += cdotr(ga, cur.U[i][j2]);
-          dfk[j2] += cdotr(Ub[i][j2], bet[i]);
-          gb[i] = cadd(gb[i], cscale(x.fk[j2], Ub[i][j2]));
+          dfk[j2] += cdotr(adj.U[i][j2], bet[i]);
+          gb[i] = cadd(gb[i], cscale(x.fk[j2], adj.U[i][j2]));
         }
 #pragma unroll
         for (int j2 = 0; j2 < ND; ++j2) {
-          Gb[i][j2] = cadd(Gb[i][j2], cscale(rc * x.g[j2], ca));
-          dv[j2] += cdotr(Gb[i][j2], bet[i]);
-          gb[i] = cadd(gb[i], cscale(x.v[j2], Gb[i][j2]));
+          adj.G[i][j2] = cadd(adj.G[i][j2], cscale(rc * x.g[j2], ca));
+          dv[j2] += cdotr(adj.G[i][j2], bet[i]);
+          gb[i] = cadd(gb[i], cscale(x.v[j2], adj.G[i][j2]));
         }
-        Eb[i] = cadd(Eb[i], cscale(dd, ca));
-        if (s.lane == 0) gb[i] = cadd(gb[i], Eb[i]);
+        adj.E[i] = cadd(adj.E[i], cscale(dd, ca));
+        if (s.lane == 0 && !a.local) gb[i] = cadd(gb[i], adj.E[i]);
       }
       // the state before token t, in place: rebuilt inside a checkpoint interval, read from
       // the previous checkpoint (or the initial state) at its start
@@ -492,17 +519,18 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(const BwdArgs a) 
         const float2 cl = conjf2(lam[i]);
 #pragma unroll
         for (int j2 = 0; j2 < NF; ++j2) {
-          gl[i] = cadd(gl[i], cmulc(Ub[i][j2], cur.U[i][j2]));
-          Ub[i][j2] = cmul(cl, Ub[i][j2]);
+          gl[i] = cadd(gl[i], cmulc(adj.U[i][j2], cur.U[i][j2]));
+          adj.U[i][j2] = cmul(cl, adj.U[i][j2]);
         }
 #pragma unroll
         for (int j2 = 0; j2 < ND; ++j2) {
-          gl[i] = cadd(gl[i], cmulc(Gb[i][j2], cur.G[i][j2]));
-          Gb[i][j2] = cmul(cl, Gb[i][j2]);
+          gl[i] = cadd(gl[i], cmulc(adj.G[i][j2], cur.G[i][j2]));
+          adj.G[i][j2] = cmul(cl, adj.G[i][j2]);
         }
-        if (s.lane == 0) gl[i] = cadd(gl[i], cmulc(Eb[i], cur.E[i]));
-        Eb[i] = cmul(cl, Eb[i]);
+        if (s.lane == 0 && !a.local) gl[i] = cadd(gl[i], cmulc(adj.E[i], cur.E[i]));
+        adj.E[i] = cmul(cl, adj.E[i]);
       }
+      if (a.local) continue;   // the local pass only carries the adjoints
       // this wave's gradient row of token t
       float* out = part + (size_t)(j * kWaves + s.wave) * W;
 #pragma unroll
@@ -520,7 +548,7 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(const BwdArgs a) 
     __syncthreads();
     // the four waves' rows summed: this workgroup's partial for the block's tokens; then the
     // next block's rows land in the buffer just used
-    const int ntok = min(TB, t_hi + 1);
+    const int ntok = a.local ? 0 : min(TB, t_hi - s.lo + 1);
     for (int e = threadIdx.x; e < ntok * W; e += kThreads) {
       const int jj = e / W, col = e - jj * W;
       float sum = 0.f;
@@ -531,7 +559,11 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(const BwdArgs a) 
     if (blk + 1 < nblk) stage_store(L, TB, pre, smem + ((blk + 1) & 1) * TB * R);
     __syncthreads();
   }
-  // gradients of lambda and beta of this wave's modes, for this slice
+  if (a.local) {
+    adj.store_rows(a, a.cadj, State<NF, ND>::seg_idx(a, s), s);
+    return;
+  }
+  // gradients of lambda and beta of this wave's modes, for this slice and segment
   float red[kRed];
 #pragma unroll
   for (int i = 0; i < kModesPerWave; ++i) {
@@ -544,21 +576,22 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(const BwdArgs a) 
 #pragma unroll
   for (int i = 0; i < kModesPerWave; ++i) {
     const size_t m = (size_t)s.slice * a.M + s.m0 + i;
+    const size_t ms = State<NF, ND>::seg_idx(a, s) * a.M + s.m0 + i;
     const float2 l = make_float2(red[4 * i], red[4 * i + 1]);
     const float2 bb = make_float2(red[4 * i + 2], red[4 * i + 3]);
     if (s.lane == 0) {
-      a.lpart[2 * m] = l;
-      a.lpart[2 * m + 1] = bb;
+      a.lpart[2 * ms] = l;
+      a.lpart[2 * ms + 1] = bb;
     }
-    // what is left in the adjoints is the gradient of the initial state
-    if (a.dU0) {
+    // what is left in segment 0's adjoints is the gradient of the initial state
+    if (a.dU0 && s.seg == 0) {
 #pragma unroll
       for (int j = 0; j < NF; ++j)
-        if (s.lane + 64 * j < a.F) a.dU0[m * a.F + s.lane + 64 * j] = Ub[i][j];
+        if (s.lane + 64 * j < a.F) a.dU0[m * a.F + s.lane + 64 * j] = adj.U[i][j];
 #pragma unroll
       for (int j = 0; j < ND; ++j)
-        if (s.lane + 64 * j < a.D) a.dG0[m * a.D + s.lane + 64 * j] = Gb[i][j];
-      if (s.lane == 0) a.dE0[m] = Eb[i];
+        if (s.lane + 64 * j < a.D) a.dG0[m * a.D + s.lane + 64 * j] = adj.G[i][j];
+      if (s.lane == 0) a.dE0[m] = adj.E[i];
     }
   }
 }
@@ -599,10 +632,13 @@ __global__ void __launch_bounds__(256) bwd_reduce_kernel(const BwdArgs a) {
   for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < hm;
        e += (size_t)gridDim.x * blockDim.x) {
     float2 l = make_float2(0.f, 0.f), bb = make_float2(0.f, 0.f);
-    for (int b = 0; b < a.B; ++b) {
-      l = cadd(l, a.lpart[2 * ((size_t)b * hm + e)]);
-      bb = cadd(bb, a.lpart[2 * ((size_t)b * hm + e) + 1]);
-    }
+    const size_t h = e / a.M, m = e % a.M;
+    for (int b = 0; b < a.B; ++b)
+      for (int g = 0; g < a.nseg; ++g) {
+        const size_t i = (((size_t)b * a.H + h) * a.nseg + g) * a.M + m;
+        l = cadd(l, a.lpart[2 * i]);
+        bb = cadd(bb, a.lpart[2 * i + 1]);
+      }
     if (a.accumulate) {
       l = cadd(l, a.dlam[e]);
       bb = cadd(bb, a.dbeta[e]);
@@ -621,10 +657,69 @@ hipError_t allow_lds(const void* kernel, size_t bytes, size_t& allowed) {
   return e;
 }
 
+// z^n for complex z in fp64 by binary exponentiation, rounded once to fp32.
+__device__ __forceinline__ float2 cpow_n(float2 z, int n) {
+  double ar = 1.0, ai = 0.0, sr = z.x, si = z.y;
+  for (; n > 0; n >>= 1) {
+    if (n & 1) {
+      const double tr = ar * sr - ai * si;
+      ai = ar * si + ai * sr;
+      ar = tr;
+    }
+    const double qr = sr * sr - si * si;
+    si = 2.0 * sr * si;
+    sr = qr;
+  }
+  return make_float2((float)ar, (float)ai);
+}
+
+// Segment carry of the state, one thread per (slice, mode, column): the local pass left each
+// segment's end state from zero in `cstate`; replace it by the segment's start state,
+// start(0) = the initial state, start(g + 1) = lam^L(g) start(g) + end(g).  With `adjoint`,
+// the same for the adjoints from the last segment down, with conj(lam): the local reverse
+// pass left in `cadj` what each segment passes on from zero, and the carried adjoints entering
+// segment g are conj(lam)^L(g+1) (those entering g + 1) + what g + 1 passes on.
+__global__ void __launch_bounds__(256) bwd_carry_kernel(const BwdArgs a, int adjoint) {
+  const int C = a.F + a.D + 1;
+  const size_t n = (size_t)a.B * a.H * a.M * C;
+  for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n;
+       e += (size_t)gridDim.x * blockDim.x) {
+    const int col = (int)(e % C);
+    const size_t sm = e / C;
+    const int m = (int)(sm % a.M);
+    const size_t slice = sm / a.M;
+    float2 lam = a.lam[(slice % a.H) * a.M + m];
+    float2* buf = adjoint ? a.cadj : a.cstate;
+    auto at = [&](int g) -> float2& {
+      return buf[(((size_t)slice * a.nseg + g) * a.M + m) * C + col];
+    };
+    auto len = [&](int g) { return min(a.N, (g + 1) * a.seg_len) - g * a.seg_len; };
+    float2 x = make_float2(0.f, 0.f);
+    if (!adjoint) {
+      const size_t sm0 = slice * a.M + m;
+      if (a.U0)
+        x = col < a.F ? a.U0[sm0 * a.F + col]
+                      : col < a.F + a.D ? a.G0[sm0 * a.D + col - a.F] : a.E0[sm0];
+      for (int g = 0; g < a.nseg; ++g) {
+        const float2 end = at(g);
+        at(g) = x;
+        x = cadd(cmul(cpow_n(lam, len(g)), x), end);
+      }
+    } else {
+      lam.y = -lam.y;
+      for (int g = a.nseg - 1; g >= 0; --g) {
+        const float2 out = at(g);
+        at(g) = x;
+        x = cadd(cmul(cpow_n(lam, len(g)), x), out);
+      }
+    }
+  }
+}
+
 template <int NF, int ND>
 hipError_t launch_bwd_nf_nd(const BwdArgs& a, hipStream_t st) {
   static size_t allowed_fwd = 65536, allowed_rev = 65536;
-  const unsigned grid = (unsigned)((size_t)a.B * a.H * (a.M / kModesPerWg));
+  const unsigned grid = (unsigned)((size_t)a.B * a.H * (a.M / kModesPerWg) * a.nseg);
   const size_t lds_fwd = bwd_lds_bytes(a.F, a.D, a.M, a.in_bf16, a.out_bf16, a.tb, false);
   const size_t lds_rev = bwd_lds_bytes(a.F, a.D, a.M, a.in_bf16, a.out_bf16, a.tb, true);
   hipError_t e = allow_lds(reinterpret_cast<const void*>(&bwd_forward_kernel<NF, ND>), lds_fwd,
@@ -633,9 +728,23 @@ hipError_t launch_bwd_nf_nd(const BwdArgs& a, hipStream_t st) {
     e = allow_lds(reinterpret_cast<const void*>(&bwd_reverse_kernel<NF, ND>), lds_rev,
                   allowed_rev);
   if (e != hipSuccess) return e;
+  const size_t carry_n = (size_t)a.B * a.H * a.M * (a.F + a.D + 1);
+  const unsigned carry_grid = (unsigned)std::min<size_t>((carry_n + 255) / 256, 4096);
+  BwdArgs loc = a;
+  loc.local = 1;
+  if (a.nseg > 1) {   // segment end states from zero, then the carry
+    hipLaunchKernelGGL((bwd_forward_kernel<NF, ND>), dim3(grid), dim3(kThreads), lds_fwd, st,
+                       loc);
+    hipLaunchKernelGGL(bwd_carry_kernel, dim3(carry_grid), dim3(256), 0, st, a, 0);
+  }
   prof_begin(st);
   hipLaunchKernelGGL((bwd_forward_kernel<NF, ND>), dim3(grid), dim3(kThreads), lds_fwd, st, a);
   prof_end(st, kKindBwdForward);
+  if (a.nseg > 1) {   // what each segment's adjoints pass on from zero, then the carry
+    hipLaunchKernelGGL((bwd_reverse_kernel<NF, ND>), dim3(grid), dim3(kThreads), lds_rev, st,
+                       loc);
+    hipLaunchKernelGGL(bwd_carry_kernel, dim3(carry_grid), dim3(256), 0, st, a, 1);
+  }
   prof_begin(st);
   hipLaunchKernelGGL((bwd_reverse_kernel<NF, ND>), dim3(grid), dim3(kThreads), lds_rev, st, a);
   prof_end(st, kKindBwdReverse);
@@ -644,16 +753,36 @@ hipError_t launch_bwd_nf_nd(const BwdArgs& a, hipStream_t st) {
 
 }  // namespace
 
+int bwd_segments(int B, int H, int N, int M, int* seg_len) {
+  // Segments of at least kBwdMinSegment tokens (a multiple of the checkpoint interval) while
+  // slices x mode groups leave compute units idle: the walk of one long sequence is cut so
+  // its pieces run side by side.
+  const long wgs = (long)B * H * (M / kModesPerWg);
+  long n = wgs >= device_cus() ? 1 : device_cus() / wgs;
+  const long most = ((long)N + kBwdMinSegment - 1) / kBwdMinSegment;
+  if (n > most) n = most;
+  if (n < 1) n = 1;
+  long len = ((long)N + n - 1) / n;
+  len = (len + kBwdCheckpoint - 1) / kBwdCheckpoint * kBwdCheckpoint;
+  *seg_len = (int)len;
+  return (int)((N + len - 1) / len);
+}
+
 BwdLayout bwd_layout(int B, int H, int N, int F, int D, int M) {
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t S = (size_t)B * H;
   const size_t nck = ((size_t)N + kBwdCheckpoint - 1) / kBwdCheckpoint;
+  int seg_len;
+  const size_t nseg = bwd_segments(B, H, N, M, &seg_len);
+  const size_t carry = nseg > 1 ? up(S * nseg * M * (F + D + 1) * 8) : 0;
   BwdLayout l{};
   l.ckpt_off = 0;
   l.dpart_off = up(S * nck * M * (F + D + 1) * 8);
   l.gpart_off = l.dpart_off + up(S * N * (M / kModesPerWave) * 8);
   l.lpart_off = l.gpart_off + up((size_t)(M / kModesPerWg) * S * N * (2 * F + D) * 4);
-  l.bytes = l.lpart_off + up(S * M * 2 * 8);
+  l.cstate_off = l.lpart_off + up(S * nseg * M * 2 * 8);
+  l.cadj_off = l.cstate_off + carry;
+  l.bytes = l.cadj_off + carry;
   return l;
 }
 

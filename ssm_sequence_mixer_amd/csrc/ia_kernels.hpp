@@ -112,6 +112,7 @@ long chunk_slot_floats(int F, int D, int M);
 // Backward pass (ia_backward.hip).  States are checkpointed every kBwdCheckpoint tokens.
 constexpr int kBwdCheckpoint = 32;
 constexpr int kBwdPrefetch = 2;   // 16-byte loads per thread that stage a block of token rows
+constexpr int kBwdMinSegment = 256;   // shortest sequence segment of the backward sweeps
 
 struct BwdArgs {
   const void *q, *k, *v, *dO;
@@ -130,11 +131,15 @@ struct BwdArgs {
   int tb;                         // tokens per staged block (bwd_block_tokens)
   int dir;                        // 1: walk index t is position N-1-t (reversed sequence)
   int accumulate;                 // 1: add the gradients onto dq, dk, dv, dlam, dbeta
+  int nseg, seg_len;              // sequence segments swept side by side (bwd_segments)
+  int local;                      // 1: the segment-local pass that feeds a carry
+  float2 *cstate, *cadj;          // segment start states and entering adjoints (nseg > 1)
 };
 
 struct BwdLayout {
-  size_t ckpt_off, dpart_off, gpart_off, lpart_off, bytes;
+  size_t ckpt_off, dpart_off, gpart_off, lpart_off, cstate_off, cadj_off, bytes;
 };
+int bwd_segments(int B, int H, int N, int M, int* seg_len);
 BwdLayout bwd_layout(int B, int H, int N, int F, int D, int M);
 int bwd_block_tokens(int F, int D, int M, int in_bf16, int out_bf16);
 size_t bwd_lds_bytes(int F, int D, int M, int in_bf16, int out_bf16, int tb, bool rev);

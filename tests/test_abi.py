@@ -234,10 +234,18 @@ def bwd(d, ws_bytes=1 << 40, st0=None, dst0=None, **ptrs):
 def test_bwd_workspace_bytes_layout():
     up = lambda x: (x + 255) // 256 * 256
     for B, H, N, F, D, M in ((2, 3, 70, 32, 16, 16), (4, 16, 2048, 128, 128, 64),
-                             (1, 1, 1, 16, 256, 128)):
+                             (1, 1, 1, 16, 256, 128), (2, 8, 131072, 32, 32, 32),
+                             (1, 2, 1000, 32, 32, 16)):
         S, nck = B * H, (N + 31) // 32
+        # sequence segments of the backward sweeps (no device: 256 compute units)
+        wgs = S * (M // 16)
+        n = 1 if wgs >= 256 else 256 // wgs
+        n = max(1, min(n, (N + 255) // 256))
+        seg = ((N + n - 1) // n + 31) // 32 * 32
+        nseg = (N + seg - 1) // seg
+        carry = up(S * nseg * M * (F + D + 1) * 8) if nseg > 1 else 0
         want = (up(S * nck * M * (F + D + 1) * 8) + up(S * N * (M // 2) * 8)
-                + up((M // 16) * S * N * (2 * F + D) * 4) + up(S * M * 16))
+                + up((M // 16) * S * N * (2 * F + D) * 4) + up(S * nseg * M * 16) + 2 * carry)
         d = desc(B=B, H=H, N=N, F=F, Dv=D, M=M)
         assert ia.lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(d)) == want
     assert ia.lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(desc(N=0))) == 0

@@ -229,3 +229,38 @@ def test_backward_bidirectional(dtype):
     ref = oracle.bidir_bwd(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"], dO, threads=4)
     _compare(got, tuple(ref) + (None,), TOL_BF16 if dtype == "bf16" else TOL_F32,
              f"bwd bidir {dtype}")
+
+
+@pytest.mark.parametrize("case", ["state_fp32", "bf16", "bidir_fp32", "noden_fp32"])
+def test_backward_sequence_segments(case):
+    """Few slices and long enough sequences that the sweeps are cut into segments of 256+
+    tokens (1000 or 2000 tokens: 4 to 8 segments, the last one ragged), joined by the state
+    and adjoint carries."""
+    import torch
+    ia = _ia()
+    dtype = "bf16" if case == "bf16" else "f32"
+    B, H, N, F, D, M = (1, 2, 2000, 64, 32, 32) if case == "bf16" else (1, 2, 1000, 32, 32, 16)
+    inp = W.make_inputs(B, H, N, F, D, M, dtype=dtype, seed=570 + N)
+    dO = np.random.default_rng(571).standard_normal((B, N, H, D)).astype(np.float32)
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    st = None
+    if case == "state_fp32":
+        pre = W.make_inputs(B, H, 12, F, D, M, dtype="f32", seed=572, std=0.5)
+        st = oracle.prefill(pre["q"], pre["k"], pre["v"], inp["lam"], inp["beta"])[3]
+        st = tuple(np.asarray(x, np.complex64).astype(np.complex128) for x in st)
+    tag(f"backward segments {case} N={N}")
+    q, k, v = (dev(inp[n], td) for n in "qkv")
+    r = ia.prefill_bwd(q, k, v, dev(inp["lam"]), dev(inp["beta"]), dev(dO),
+                       state0=None if st is None else tuple(dev(x) for x in st),
+                       want_state_grad=st is not None, bidir=case == "bidir_fp32",
+                       no_den=case == "noden_fp32")
+    torch.cuda.synchronize()
+    got = tuple(host(x) for x in r[:5]) + (None if r[5] is None else tuple(host(x) for x in r[5]),)
+    if case == "bidir_fp32":
+        ref = tuple(oracle.bidir_bwd(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"], dO,
+                                     threads=2)) + (None,)
+    else:
+        ref = oracle.prefill_bwd(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"], dO,
+                                 state=st, no_den=case == "noden_fp32", threads=2)
+    _compare(got, ref, TOL_BF16 if dtype == "bf16" else TOL_F32, f"bwd segments {case}",
+             state=st is not None)
