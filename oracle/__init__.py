@@ -49,6 +49,9 @@ def load_library(path):
     lib.ia_oracle_scan.restype = ctypes.c_int
     lib.ia_oracle_scan.argtypes = [ctypes.c_int] * 4 + [dp] * 5 + [dp] * 3 + [dp] * 3 + [
         ctypes.c_double]
+    lib.ia_oracle_scan_readout.restype = ctypes.c_int
+    lib.ia_oracle_scan_readout.argtypes = [ctypes.c_int] * 4 + [dp] * 6 + [dp] * 3 + [dp] * 3 + [
+        ctypes.c_double, dp]
     lib.ia_oracle_scan_bwd.restype = ctypes.c_int
     lib.ia_oracle_scan_bwd.argtypes = [ctypes.c_int] * 4 + [dp] * 5 + [dp] * 3 + [
         dp, ctypes.c_double, ctypes.c_int] + [dp] * 5 + [dp] * 3 + [dp]
@@ -245,3 +248,59 @@ def bidir_bwd(q, k, v, lam, beta, dO, clamp=1e-6, no_den=False, slices=None, thr
     r = prefill_bwd(fl(q), fl(k), fl(v), lam, beta, fl(dO), None, clamp, no_den, slices, threads)
     return (f[0] + r[0][:, ::-1], f[1] + r[1][:, ::-1], f[2] + r[2][:, ::-1], f[3] + r[3],
             f[4] + r[4])
+
+
+def scan_readout(q, k, v, lam, beta, readout, state=None, clamp=1e-6, lib=None):
+    """``scan`` with a complex [M, M] readout matrix R (``ia_oracle_scan_readout``): the
+    readouts use a R in place of a.  Returns (o, num, den, (U, G, e))."""
+    lib = lib or _load()
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    N, F = q.shape
+    D = v.shape[1]
+    M = np.asarray(lam).shape[0]
+    if state is None:
+        U, G, e = np.zeros((M, F, 2)), np.zeros((M, D, 2)), np.zeros((M, 2))
+    else:
+        U, G, e = (_c2r(x) for x in state)
+    o, num, den = np.empty((N, D)), np.empty((N, D)), np.empty(N)
+    work = np.empty(4 * M)
+    lib.ia_oracle_scan_readout(N, F, D, M, _ptr(q), _ptr(k), _ptr(v), _ptr(_c2r(lam)),
+                               _ptr(_c2r(beta)), _ptr(_c2r(readout)), _ptr(U), _ptr(G), _ptr(e),
+                               _ptr(o), _ptr(num), _ptr(den), clamp, _ptr(work))
+    return o, num, den, (_r2c(U), _r2c(G), _r2c(e))
+
+
+def prefill_readout(q, k, v, lam, beta, readout, state=None, clamp=1e-6, slices=None,
+                    threads=1):
+    """``prefill`` with a per-head readout matrix, readout [H, M, M] complex."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, N, H, F = q.shape
+    D = v.shape[3]
+    M = lam.shape[1]
+    o = np.full((B, N, H, D), np.nan)
+    num = np.full((B, N, H, D), np.nan)
+    den = np.full((B, N, H), np.nan)
+    U = np.full((B, H, M, F), np.nan, dtype=np.complex128)
+    G = np.full((B, H, M, D), np.nan, dtype=np.complex128)
+    e = np.full((B, H, M), np.nan, dtype=np.complex128)
+    todo = slices if slices is not None else [(b, h) for b in range(B) for h in range(H)]
+
+    def one(bh):
+        b, h = bh
+        st = None if state is None else (state[0][b, h], state[1][b, h], state[2][b, h])
+        return bh, scan_readout(q[b, :, h], k[b, :, h], v[b, :, h], lam[h], beta[h],
+                                readout[h], st, clamp)
+
+    if threads > 1:
+        with ThreadPoolExecutor(threads) as ex:
+            results = list(ex.map(one, todo))
+    else:
+        results = [one(bh) for bh in todo]
+    for (b, h), (ob, nb, db, (Ub, Gb, eb)) in results:
+        o[b, :, h], num[b, :, h], den[b, :, h] = ob, nb, db
+        U[b, h], G[b, h], e[b, h] = Ub, Gb, eb
+    return o, num, den, (U, G, e)

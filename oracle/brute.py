@@ -28,8 +28,9 @@ def powers(lam, n):
     return np.exp(np.asarray(n, dtype=np.float64)[:, None] * np.log(lam)[None, :])
 
 
-def layer(q, k, v, lam, beta, clamp=1e-6):
-    """One (b,h) slice from zero state: q, k [N,F]; v [N,D]; lam, beta [M].
+def layer(q, k, v, lam, beta, clamp=1e-6, readout=None):
+    """One (b,h) slice from zero state: q, k [N,F]; v [N,D]; lam, beta [M]; ``readout`` an
+    optional complex [M, M] mode-mixing matrix R (a -> a R before the readout; None = identity).
 
     Returns (o [N,D], num [N,D], den [N]).
     """
@@ -46,6 +47,8 @@ def layer(q, k, v, lam, beta, clamp=1e-6):
         A = (S[t, : t + 1, None] * dec).sum(axis=0)                 # [m]
         Gam = (dec[:, :, None] * v[: t + 1, None, :]).sum(axis=0)   # [m, D]
         eta = dec.sum(axis=0)                                       # [m]
+        if readout is not None:
+            A = A @ np.asarray(readout, dtype=np.complex128)        # (a R)[n] = sum_m a_m R_mn
         num[t] = np.real((A[:, None] * Gam).sum(axis=0))
         den[t] = np.real((A * eta).sum())
         o[t] = num[t] / max(den[t], clamp)

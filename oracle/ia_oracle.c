@@ -272,3 +272,69 @@ int ia_oracle_scan_bwd(int N, int F, int D, int M,
   free(Ub);
   return 0;
 }
+
+/*
+ * The same layer with a learned complex M x M readout matrix R between phi(q_t) U^T and Gamma
+ * (the full readout matrix listed with the practical layer's dimensions, summary page §A.3,
+ * whose cost per decode step is the M^2 term of §3.2).  Reading: R mixes the modes of a before
+ * both readouts, a'[n] = sum_m a[m] R[m][n], num = Re sum_n a'[n] Gam[n,:],
+ * den = Re sum_n a'[n] eta[n], o = num / max(den, clamp); R = identity is the layer above.
+ *   R   [M][M][2] (re, im), row m, column n.  Other arguments as ia_oracle_scan.
+ *   work  M * 4 doubles.
+ * Returns 0.
+ */
+int ia_oracle_scan_readout(int N, int F, int D, int M,
+                           const double* q, const double* k, const double* v,
+                           const double* lam, const double* beta, const double* R,
+                           double* U, double* G, double* e,
+                           double* o, double* num, double* den, double clamp, double* work) {
+  double complex* av = (double complex*)work;   /* a[m] */
+  double complex* ar = av + M;                  /* (a R)[n] */
+  for (int t = 0; t < N; ++t) {
+    /* every state row advanced by token t; a[m] = phi(q_t) . U[m,:] */
+    for (int m = 0; m < M; ++m) {
+      const double complex lm = lam[2 * m] + I * lam[2 * m + 1];
+      const double complex bt = beta[2 * m] + I * beta[2 * m + 1];
+      double complex acc = 0.0;
+      for (int r = 0; r < F; ++r) {
+        double* u = U + ((size_t)m * F + r) * 2;
+        const double complex uc = lm * (u[0] + I * u[1]) + bt * feature(k[(size_t)t * F + r]);
+        u[0] = creal(uc);
+        u[1] = cimag(uc);
+        acc += feature(q[(size_t)t * F + r]) * uc;
+      }
+      av[m] = acc;
+      for (int j = 0; j < D; ++j) {
+        double* g = G + ((size_t)m * D + j) * 2;
+        const double complex gc = lm * (g[0] + I * g[1]) + bt * v[(size_t)t * D + j];
+        g[0] = creal(gc);
+        g[1] = cimag(gc);
+      }
+      const double complex ec = lm * (e[2 * m] + I * e[2 * m + 1]) + bt;
+      e[2 * m] = creal(ec);
+      e[2 * m + 1] = cimag(ec);
+    }
+    for (int n = 0; n < M; ++n) {
+      double complex acc = 0.0;
+      for (int m = 0; m < M; ++m)
+        acc += av[m] * (R[((size_t)m * M + n) * 2] + I * R[((size_t)m * M + n) * 2 + 1]);
+      ar[n] = acc;
+    }
+    double complex dc = 0.0;
+    for (int n = 0; n < M; ++n) dc += ar[n] * (e[2 * n] + I * e[2 * n + 1]);
+    const double d = creal(dc);
+    double c = d < clamp ? clamp : d;
+    if (isnan(d)) c = d;
+    if (den) den[t] = d;
+    for (int j = 0; j < D; ++j) {
+      double complex nc = 0.0;
+      for (int n = 0; n < M; ++n) {
+        const double* g = G + ((size_t)n * D + j) * 2;
+        nc += ar[n] * (g[0] + I * g[1]);
+      }
+      if (num) num[(size_t)t * D + j] = creal(nc);
+      if (o) o[(size_t)t * D + j] = creal(nc) / c;
+    }
+  }
+  return 0;
+}

@@ -254,3 +254,68 @@ def test_planted_mistake_fails_a_pin(mutant, tmp_path):
     scan = lambda *a: oracle.scan(*a, lib=lib)
     errs = {name: fn(scan) for name, fn in PINS.items()}
     assert any(not (e < TOL) for e in errs.values()), f"{mutant} passed every pin: {errs}"
+
+
+# ---------------------------------------------------------------- readout matrix
+
+def _rm_case(seed, N=9, F=3, D=4, M=5):
+    rng = np.random.default_rng(seed)
+    q, k, v = rng.standard_normal((N, F)), rng.standard_normal((N, F)), rng.standard_normal((N, D))
+    lam = rng.uniform(0.5, 0.95, M) * np.exp(1j * rng.uniform(-1, 1, M))
+    beta = 1.0 + 0.3j * rng.uniform(-1, 1, M)
+    R = np.eye(M) + 0.3 * (rng.standard_normal((M, M)) + 1j * rng.standard_normal((M, M)))
+    return q, k, v, lam, beta, R
+
+
+def test_readout_matrix_identity_is_the_plain_layer():
+    q, k, v, lam, beta, _ = _rm_case(21)
+    o, num, den, st = oracle.scan_readout(q, k, v, lam, beta, np.eye(len(lam)))
+    o2, num2, den2, st2 = oracle.scan(q, k, v, lam, beta)
+    assert _rel(num, num2) < 1e-12 and _rel(den, den2) < 1e-12 and _rel(o, o2) < 1e-12
+    assert max(_rel(a, b) for a, b in zip(st, st2)) < 1e-12
+
+
+@pytest.mark.parametrize("seed", [22, 23])
+def test_readout_matrix_matches_brute_force(seed):
+    """The explicit double sum over s <= t, with (a R) in place of a (brute.layer)."""
+    q, k, v, lam, beta, R = _rm_case(seed)
+    o, num, den, _ = oracle.scan_readout(q, k, v, lam, beta, R)
+    ob, nb, db = brute.layer(q, k, v, lam, beta, readout=R)
+    assert _rel(num, nb) < 1e-10 and _rel(den, db) < 1e-10 and _rel(o, ob) < 1e-10
+
+
+def test_readout_matrix_linearity():
+    """num and den are real-linear in R (the state does not depend on it): R3 = 2 R1 - 0.5 R2
+    gives 2 num1 - 0.5 num2, and likewise den."""
+    q, k, v, lam, beta, R1 = _rm_case(24)
+    R2 = _rm_case(25)[5]
+    _, n1, d1, _ = oracle.scan_readout(q, k, v, lam, beta, R1)
+    _, n2, d2, _ = oracle.scan_readout(q, k, v, lam, beta, R2)
+    _, n3, d3, _ = oracle.scan_readout(q, k, v, lam, beta, 2.0 * R1 - 0.5 * R2)
+    assert _rel(n3, 2.0 * n1 - 0.5 * n2) < 1e-10
+    assert _rel(d3, 2.0 * d1 - 0.5 * d2) < 1e-10
+
+
+READOUT_MUTANTS = {
+    "readout_matrix_transposed": ("acc += av[m] * (R[((size_t)m * M + n) * 2] + I * R[((size_t)m * M + n) * 2 + 1]);",
+                                  "acc += av[m] * (R[((size_t)n * M + m) * 2] + I * R[((size_t)n * M + m) * 2 + 1]);"),
+    "readout_den_unmixed": ("for (int n = 0; n < M; ++n) dc += ar[n] * (e[2 * n] + I * e[2 * n + 1]);",
+                            "for (int n = 0; n < M; ++n) dc += av[n] * (e[2 * n] + I * e[2 * n + 1]);"),
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(READOUT_MUTANTS))
+def test_planted_readout_mistake_fails_brute_force(mutant, tmp_path):
+    src = open(oracle._SRC).read()
+    old, new = READOUT_MUTANTS[mutant]
+    assert src.count(old) == 1, f"mutation anchor for {mutant} not found once"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new))
+    so = tmp_path / "mutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", str(so),
+                           str(path), "-lm"])
+    lib = oracle.load_library(str(so))
+    q, k, v, lam, beta, R = _rm_case(22)
+    o, num, den, _ = oracle.scan_readout(q, k, v, lam, beta, R, lib=lib)
+    ob, nb, db = brute.layer(q, k, v, lam, beta, readout=R)
+    assert not (_rel(num, nb) < 1e-10 and _rel(den, db) < 1e-10), f"{mutant} passed"
