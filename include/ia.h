@@ -240,6 +240,32 @@ ia_status ia_prefill_bwd(const ia_desc* desc,
                          void* dq, void* dk, void* dv, void* dlambda, void* dbeta,
                          ia_state* dst0, void* workspace, size_t ws_bytes, void* stream);
 
+/* Readout matrix variants.  A learned complex M x M matrix R per head mixes the modes of
+ * a = phi(q_t) U^T before both readouts (the full readout matrix listed with the practical
+ * layer's dimensions [summary §A.3], the M^2 term of the decode cost [summary §3.2]):
+ *   a'[n] = sum_m a[m] R[m][n],  o_t = Re(a' Gamma) / max(Re(a' eta), den_clamp)
+ * (or Re(a' Gamma) with IA_FLAG_NO_DEN).  R = identity gives the plain layer.
+ *   readout  [H][M][M] complex64 (row m, column n), device, read only; NULL: IA_ERR_NULL.
+ * Both run the token-sequential fp32 kernels (bf16 inputs included): the chunked factorisation
+ * keeps modes separate.  Other arguments, layouts and errors as ia_prefill_fwd /
+ * ia_decode_step; readout must be 16-byte aligned and must not overlap an output. */
+
+/* Workspace bytes ia_prefill_fwd_readout needs at most: one state,
+ * B*H*M*(F+Dv+1) complex64 rounded up to 256 bytes (used when st is NULL or IA_FLAG_BIDIR is
+ * set; otherwise the workspace may be NULL).  0 on an invalid descriptor. */
+size_t ia_prefill_readout_workspace_bytes(const ia_desc* desc);
+
+ia_status ia_prefill_fwd_readout(const ia_desc* desc,
+                                 const void* q, const void* k, const void* v,
+                                 const void* lambda, const void* beta, const void* readout,
+                                 ia_state* st, void* o,
+                                 void* workspace, size_t ws_bytes, void* stream);
+
+ia_status ia_decode_step_readout(const ia_desc* desc,
+                                 const void* q_t, const void* k_t, const void* v_t,
+                                 const void* lambda, const void* beta, const void* readout,
+                                 ia_state* st, void* o_t, void* stream);
+
 /* Static string naming a status code. */
 const char* ia_status_string(ia_status s);
 

@@ -93,6 +93,13 @@ lib.ia_prefill_bwd_workspace_bytes.restype = ctypes.c_size_t
 lib.ia_prefill_bwd.argtypes = [_D, _P, _P, _P, _P, _P, _S, _P, _P, _P, _P, _P, _P, _S, _P,
                                ctypes.c_size_t, _P]
 lib.ia_prefill_bwd.restype = ctypes.c_int
+lib.ia_prefill_readout_workspace_bytes.argtypes = [_D]
+lib.ia_prefill_readout_workspace_bytes.restype = ctypes.c_size_t
+lib.ia_prefill_fwd_readout.argtypes = [_D, _P, _P, _P, _P, _P, _P, _S, _P, _P, ctypes.c_size_t,
+                                       _P]
+lib.ia_prefill_fwd_readout.restype = ctypes.c_int
+lib.ia_decode_step_readout.argtypes = [_D, _P, _P, _P, _P, _P, _P, _S, _P, _P]
+lib.ia_decode_step_readout.restype = ctypes.c_int
 lib.ia_status_string.argtypes = [ctypes.c_int]
 lib.ia_status_string.restype = ctypes.c_char_p
 lib.ia_last_launch_error.argtypes = []
@@ -100,7 +107,8 @@ lib.ia_last_launch_error.restype = ctypes.c_char_p
 
 EXPORTS = ("ia_state_init", "ia_prefill_workspace_bytes", "ia_check_lambda", "ia_prefill_fwd",
            "ia_prefill_fwd_strided", "ia_prefill_fwd_profiled", "ia_decode_step",
-           "ia_prefill_bwd_workspace_bytes", "ia_prefill_bwd", "ia_status_string",
+           "ia_prefill_bwd_workspace_bytes", "ia_prefill_bwd", "ia_prefill_readout_workspace_bytes",
+           "ia_prefill_fwd_readout", "ia_decode_step_readout", "ia_status_string",
            "ia_last_launch_error")
 KIND_NAMES = {0: "fill", 1: "scan", 2: "tables", 3: "summary", 4: "carry", 5: "chunk",
               6: "decode", 7: "bwd_forward", 8: "bwd_reverse", 9: "bwd_reduce"}
@@ -229,6 +237,28 @@ def ia_prefill_bwd(desc: IADesc, q, k, v, lam, beta, state0, dO, dq, dk, dv, dla
                               _ptr(workspace), ws_bytes, _stream(stream)), "ia_prefill_bwd")
 
 
+def ia_prefill_readout_workspace_bytes(desc: IADesc) -> int:
+    return int(lib.ia_prefill_readout_workspace_bytes(ctypes.byref(desc)))
+
+
+def ia_prefill_fwd_readout(desc: IADesc, q, k, v, lam, beta, readout, state, o, workspace,
+                           stream=None):
+    _dense(q, k, v, lam, beta, readout, o, workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.ia_prefill_fwd_readout(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(lam),
+                                      _ptr(beta), _ptr(readout), _state(state), _ptr(o),
+                                      _ptr(workspace), ws_bytes, _stream(stream)),
+           "ia_prefill_fwd_readout")
+
+
+def ia_decode_step_readout(desc: IADesc, q_t, k_t, v_t, lam, beta, readout, state, o_t,
+                           stream=None):
+    _dense(q_t, k_t, v_t, lam, beta, readout, o_t)
+    _check(lib.ia_decode_step_readout(ctypes.byref(desc), _ptr(q_t), _ptr(k_t), _ptr(v_t),
+                                      _ptr(lam), _ptr(beta), _ptr(readout), _state(state),
+                                      _ptr(o_t), _stream(stream)), "ia_decode_step_readout")
+
+
 def ia_decode_step(desc: IADesc, q_t, k_t, v_t, lam, beta, state, o_t, stream=None):
     _dense(q_t, k_t, v_t, lam, beta, o_t)
     _check(lib.ia_decode_step(ctypes.byref(desc), _ptr(q_t), _ptr(k_t), _ptr(v_t), _ptr(lam),
@@ -250,7 +280,7 @@ def new_state(B, H, M, F, Dv, device="cuda", stream=None, zero=True):
 
 def prefill(q, k, v, lam, beta, state=None, out_dtype=None, bidir=False, chunk=0,
             den_clamp=1e-6, want_output=True, stream=None, workspace=None, no_den=False,
-            identity_features=False):
+            identity_features=False, readout=None):
     """Allocate o (and the workspace) with torch and run ia_prefill_fwd (or, for strided
     views q, k, v, ia_prefill_fwd_strided); returns o."""
     import torch
@@ -260,6 +290,12 @@ def prefill(q, k, v, lam, beta, state=None, out_dtype=None, bidir=False, chunk=0
     desc = make_desc(B, H, N, F, Dv, M, dtype_code(q.dtype), dtype_code(out_dtype), den_clamp,
                      bidir, chunk, no_den, identity_features)
     o = torch.empty((B, N, H, Dv), dtype=out_dtype, device=q.device) if want_output else None
+    if readout is not None:
+        if workspace is None:
+            nb = ia_prefill_readout_workspace_bytes(desc)
+            workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
+        ia_prefill_fwd_readout(desc, q, k, v, lam, beta, readout, state, o, workspace, stream)
+        return o
     if workspace is None:
         nb = ia_prefill_workspace_bytes(desc)
         workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device) if nb else None
@@ -271,7 +307,8 @@ def prefill(q, k, v, lam, beta, state=None, out_dtype=None, bidir=False, chunk=0
 
 
 def decode(q_t, k_t, v_t, lam, beta, state, out_dtype=None,
-           den_clamp=1e-6, stream=None, o_t=None, no_den=False, identity_features=False):
+           den_clamp=1e-6, stream=None, o_t=None, no_den=False, identity_features=False,
+           readout=None):
     """One decode step for every (b,h); allocates o_t unless given; returns o_t."""
     import torch
     B, H, F = q_t.shape
@@ -281,7 +318,10 @@ def decode(q_t, k_t, v_t, lam, beta, state, out_dtype=None,
                      no_den=no_den, identity_features=identity_features)
     if o_t is None:
         o_t = torch.empty((B, H, Dv), dtype=out_dtype, device=q_t.device)
-    ia_decode_step(desc, q_t, k_t, v_t, lam, beta, state, o_t, stream)
+    if readout is not None:
+        ia_decode_step_readout(desc, q_t, k_t, v_t, lam, beta, readout, state, o_t, stream)
+    else:
+        ia_decode_step(desc, q_t, k_t, v_t, lam, beta, state, o_t, stream)
     return o_t
 
 

@@ -193,17 +193,12 @@ size_t ia_prefill_workspace_bytes(const ia_desc* d) {
   return scan_workspace(d, false).bytes;
 }
 
-ia_status ia_prefill_fwd(const ia_desc* d, const void* q, const void* k, const void* v,
-                         const void* lambda, const void* beta, ia_state* st, void* o,
-                         void* workspace, size_t ws_bytes, void* stream) {
-  return ia_prefill_fwd_strided(d, q, k, v, nullptr, lambda, beta, st, o, workspace, ws_bytes,
-                                stream);
-}
-
-ia_status ia_prefill_fwd_strided(const ia_desc* d, const void* q, const void* k, const void* v,
-                                 const long long strides[3][3], const void* lambda,
-                                 const void* beta, ia_state* st, void* o, void* workspace,
-                                 size_t ws_bytes, void* stream) {
+// The prefill behind every prefill entry point: optional (b, n, h) strides of q, k, v, and an
+// optional readout matrix ([H][M][M] complex64), which takes the token-sequential path.
+static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, const void* v,
+                              const long long strides[3][3], const void* lambda,
+                              const void* beta, const void* readout, ia_state* st, void* o,
+                              void* workspace, size_t ws_bytes, void* stream) {
   ia_status s = check_desc(d, true);
   if (s != IA_OK) return s;
   // Element strides (b, n, h) of q, k, v; the feature axis is contiguous.
@@ -221,7 +216,8 @@ ia_status ia_prefill_fwd_strided(const ia_desc* d, const void* q, const void* k,
     if (sq.b != sk.b || sq.n != sk.n || sq.h != sk.h) return IA_ERR_UNSUPPORTED;
     // The chunk kernels address a chunk's rows with 32-bit byte offsets (as for the dense
     // layout in use_chunk_path).
-    if (use_chunk_path(d) && (64LL * sq.n * 2 > (1LL << 30) || 64LL * sv.n * 2 > (1LL << 30)))
+    if (!readout && use_chunk_path(d) &&
+        (64LL * sq.n * 2 > (1LL << 30) || 64LL * sv.n * 2 > (1LL << 30)))
       return IA_ERR_UNSUPPORTED;
   }
   const bool bidir = d->flags & IA_FLAG_BIDIR;
@@ -232,6 +228,7 @@ ia_status ia_prefill_fwd_strided(const ia_desc* d, const void* q, const void* k,
   for (const void* p : {q, k, v, lambda, beta})
     if (!aligned16(p)) return IA_ERR_ALIGN;
   if (o && !aligned16(o)) return IA_ERR_ALIGN;
+  if (readout && !aligned16(readout)) return IA_ERR_ALIGN;
   if (st && (s = check_state(d, st)) != IA_OK) return s;
 
   const size_t tok = size_t(d->B) * d->N * d->H;
@@ -244,7 +241,8 @@ ia_status ia_prefill_fwd_strided(const ia_desc* d, const void* q, const void* k,
   const Range rv = rng(v, extent(sv, d->Dv));
   const Range rl = rng(lambda, size_t(d->H) * d->M * 8);
   const Range rb = rng(beta, size_t(d->H) * d->M * 8);
-  const Range ins[] = {rq, rk, rv, rl, rb};
+  const Range rr = rng(readout, readout ? size_t(d->H) * d->M * d->M * 8 : 0);
+  const Range ins[] = {rq, rk, rv, rl, rb, rr};
   if (o) {
     const Range ro = rng(o, tok * d->Dv * esize(d->out_dtype));
     for (const Range& r : ins)
@@ -264,7 +262,7 @@ ia_status ia_prefill_fwd_strided(const ia_desc* d, const void* q, const void* k,
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
 
-  if (use_chunk_path(d)) {
+  if (!readout && use_chunk_path(d)) {
     const ChunkPlan pl = chunk_plan(d);
     if (!workspace || ws_bytes < pl.bytes) return IA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return IA_ERR_ALIGN;
@@ -338,6 +336,7 @@ ia_status ia_prefill_fwd_strided(const ia_desc* d, const void* q, const void* k,
                  static_cast<const float2*>(beta), U, G, E, o, 0, d->B, d->H, d->N, d->F, d->Dv,
                  d->M, d->in_dtype == IA_BF16, d->out_dtype == IA_BF16, d->den_clamp, 0};
   a.opt = kernel_opt(d);
+  a.readout = static_cast<const float2*>(readout);
   if (!bidir) return launch_status(ia::launch_scan_prefill(a, hs));
 
   // Bidirectional: the forward direction writes o, the reverse direction (from a zero state
@@ -350,6 +349,35 @@ ia_status ia_prefill_fwd_strided(const ia_desc* d, const void* q, const void* k,
     e = ia::launch_scan_prefill(a, hs);
   }
   return launch_status(e);
+}
+
+ia_status ia_prefill_fwd(const ia_desc* d, const void* q, const void* k, const void* v,
+                         const void* lambda, const void* beta, ia_state* st, void* o,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  return prefill_impl(d, q, k, v, nullptr, lambda, beta, nullptr, st, o, workspace, ws_bytes,
+                      stream);
+}
+
+ia_status ia_prefill_fwd_strided(const ia_desc* d, const void* q, const void* k, const void* v,
+                                 const long long strides[3][3], const void* lambda,
+                                 const void* beta, ia_state* st, void* o, void* workspace,
+                                 size_t ws_bytes, void* stream) {
+  return prefill_impl(d, q, k, v, strides, lambda, beta, nullptr, st, o, workspace, ws_bytes,
+                      stream);
+}
+
+size_t ia_prefill_readout_workspace_bytes(const ia_desc* d) {
+  if (check_desc(d, true) != IA_OK) return 0;
+  return scan_workspace(d, false).bytes;
+}
+
+ia_status ia_prefill_fwd_readout(const ia_desc* d, const void* q, const void* k, const void* v,
+                                 const void* lambda, const void* beta, const void* readout,
+                                 ia_state* st, void* o, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  if (!readout) return IA_ERR_NULL;
+  return prefill_impl(d, q, k, v, nullptr, lambda, beta, readout, st, o, workspace, ws_bytes,
+                      stream);
 }
 
 size_t ia_prefill_bwd_workspace_bytes(const ia_desc* d) {
@@ -454,9 +482,10 @@ ia_status ia_prefill_bwd(const ia_desc* d, const void* q, const void* k, const v
   return launch_status(e);
 }
 
-ia_status ia_decode_step(const ia_desc* d, const void* q_t, const void* k_t, const void* v_t,
-                         const void* lambda, const void* beta, ia_state* st, void* o_t,
-                         void* stream) {
+// The decode step behind both decode entry points; readout: [H][M][M] complex64 or NULL.
+static ia_status decode_impl(const ia_desc* d, const void* q_t, const void* k_t,
+                             const void* v_t, const void* lambda, const void* beta,
+                             const void* readout, ia_state* st, void* o_t, void* stream) {
   ia_status s = check_desc(d, false);
   if (s != IA_OK) return s;
   if (d->flags & IA_FLAG_BIDIR) return IA_ERR_UNSUPPORTED;
@@ -464,11 +493,13 @@ ia_status ia_decode_step(const ia_desc* d, const void* q_t, const void* k_t, con
   if ((s = check_state(d, st)) != IA_OK) return s;
   for (const void* p : {q_t, k_t, v_t, lambda, beta, static_cast<const void*>(o_t)})
     if (!aligned16(p)) return IA_ERR_ALIGN;
+  if (readout && !aligned16(readout)) return IA_ERR_ALIGN;
   const size_t bh = size_t(d->B) * d->H;
   const Range ins[] = {rng(q_t, bh * d->F * esize(d->in_dtype)),
                        rng(k_t, bh * d->F * esize(d->in_dtype)),
                        rng(v_t, bh * d->Dv * esize(d->in_dtype)),
-                       rng(lambda, size_t(d->H) * d->M * 8), rng(beta, size_t(d->H) * d->M * 8)};
+                       rng(lambda, size_t(d->H) * d->M * 8), rng(beta, size_t(d->H) * d->M * 8),
+                       rng(readout, readout ? size_t(d->H) * d->M * d->M * 8 : 0)};
   const Range outs[] = {rng(o_t, bh * d->Dv * esize(d->out_dtype)),
                         rng(st->U, state_u_bytes(d)), rng(st->Gamma, state_g_bytes(d)),
                         rng(st->eta, state_e_bytes(d))};
@@ -483,7 +514,21 @@ ia_status ia_decode_step(const ia_desc* d, const void* q_t, const void* k_t, con
                    d->B, d->H, d->F, d->Dv, d->M, d->in_dtype == IA_BF16,
                    d->out_dtype == IA_BF16, d->den_clamp};
   a.opt = kernel_opt(d);
+  a.readout = static_cast<const float2*>(readout);
   return launch_status(ia::launch_decode_step(a, static_cast<hipStream_t>(stream)));
+}
+
+ia_status ia_decode_step(const ia_desc* d, const void* q_t, const void* k_t, const void* v_t,
+                         const void* lambda, const void* beta, ia_state* st, void* o_t,
+                         void* stream) {
+  return decode_impl(d, q_t, k_t, v_t, lambda, beta, nullptr, st, o_t, stream);
+}
+
+ia_status ia_decode_step_readout(const ia_desc* d, const void* q_t, const void* k_t,
+                                 const void* v_t, const void* lambda, const void* beta,
+                                 const void* readout, ia_state* st, void* o_t, void* stream) {
+  if (!readout) return IA_ERR_NULL;
+  return decode_impl(d, q_t, k_t, v_t, lambda, beta, readout, st, o_t, stream);
 }
 
 ia_status ia_prefill_fwd_profiled(const ia_desc* d, const void* q, const void* k,

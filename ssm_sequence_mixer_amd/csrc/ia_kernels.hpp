@@ -66,6 +66,7 @@ struct DecodeArgs {
   int in_bf16, out_bf16;
   float clamp;
   int opt;   // kOptNoDen | kOptIdentity
+  const float2* readout = nullptr;   // [H][M][M] readout matrix, or NULL
 };
 
 struct ScanArgs {
@@ -80,6 +81,7 @@ struct ScanArgs {
   float clamp;
   int reverse;
   int opt;   // kOptNoDen | kOptIdentity
+  const float2* readout = nullptr;   // [H][M][M] readout matrix, or NULL
 };
 
 // Chunked MFMA prefill of one direction (bf16 inputs).  The sequence is cut into `segments`

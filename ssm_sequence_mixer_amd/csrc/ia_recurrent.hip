@@ -26,6 +26,7 @@ struct StepSmem {
   float2 lam[kMaxModes];
   float2 beta[kMaxModes];
   float2 a[kMaxModes];
+  float2 ar[kMaxModes];   // a R, with a readout matrix R
   float2 eta[kMaxModes];
   float num[kStepWaves][kMaxDim];
   float den[kStepWaves];
@@ -33,9 +34,11 @@ struct StepSmem {
 
 // State rows are float2 arrays; lanes take two complex values (one float4) at a time.
 // F and D are multiples of 16, so a row is a whole number of float4 pairs.
+// R: this head's readout matrix [M][M] (row m, column n), or NULL for none: the readouts then
+// use (a R)[n] = sum_m a[m] R[m][n] in place of a.
 __device__ __forceinline__ void step_one(StepSmem& s, float2* __restrict__ U,
                                          float2* __restrict__ G, float2* __restrict__ E,
-                                         int F, int D, int M) {
+                                         int F, int D, int M, const float2* __restrict__ R) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
@@ -65,13 +68,22 @@ __device__ __forceinline__ void step_one(StepSmem& s, float2* __restrict__ U,
     s.eta[m] = e;
   }
   __syncthreads();
+  if (R) {
+    for (int n = threadIdx.x; n < M; n += kStepThreads) {
+      float2 acc = make_float2(0.f, 0.f);
+      for (int m = 0; m < M; ++m) acc = cfma(s.a[m], R[(size_t)m * M + n], acc);
+      s.ar[n] = acc;
+    }
+    __syncthreads();
+  }
+  const float2* A = R ? s.ar : s.a;
 
   // Gamma rows: update in place, accumulate Re(a[m] G[m,:]) per lane.
   float acc[kMaxDim / 64];
 #pragma unroll
   for (int i = 0; i < kMaxDim / 64; ++i) acc[i] = 0.f;
   for (int m = wave; m < M; m += kStepWaves) {
-    const float2 l = s.lam[m], b = s.beta[m], a = s.a[m];
+    const float2 l = s.lam[m], b = s.beta[m], a = A[m];
     float4* row = reinterpret_cast<float4*>(G + (size_t)m * D);
 #pragma unroll
     for (int i = 0; i < kMaxDim / 128; ++i) {
@@ -97,7 +109,7 @@ __device__ __forceinline__ void step_one(StepSmem& s, float2* __restrict__ U,
   }
   if (wave == 0) {
     float d = 0.f;
-    for (int m = lane; m < M; m += 64) d += s.a[m].x * s.eta[m].x - s.a[m].y * s.eta[m].y;
+    for (int m = lane; m < M; m += 64) d += A[m].x * s.eta[m].x - A[m].y * s.eta[m].y;
     d = wave_sum(d);
     if (lane == 0) s.den[0] = d;
   }
@@ -132,14 +144,15 @@ decode_step_kernel(const void* __restrict__ q, const void* __restrict__ k,
                    const float2* __restrict__ beta, float2* __restrict__ U,
                    float2* __restrict__ G, float2* __restrict__ E, void* __restrict__ o,
                    int H, int F, int D, int M, int in_bf16, int out_bf16, float clamp,
-                   int opt) {
+                   int opt, const float2* __restrict__ rmat) {
   __shared__ StepSmem s;
   const int bh = blockIdx.x;
   const int h = bh % H;
   load_modes(s, lam, beta, h, M);
   load_token(s, q, k, v, (size_t)bh * F, (size_t)bh * D, F, D, in_bf16, opt);
   __syncthreads();
-  step_one(s, U + (size_t)bh * M * F, G + (size_t)bh * M * D, E + (size_t)bh * M, F, D, M);
+  step_one(s, U + (size_t)bh * M * F, G + (size_t)bh * M * D, E + (size_t)bh * M, F, D, M,
+           rmat ? rmat + (size_t)h * M * M : nullptr);
   for (int j = threadIdx.x; j < D; j += kStepThreads) {
     float n = 0.f;
 #pragma unroll
@@ -160,13 +173,14 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
                         const void* __restrict__ v, const float2* __restrict__ lam,
                         const float2* __restrict__ beta, float2* __restrict__ U,
                         float2* __restrict__ G, float2* __restrict__ E, void* __restrict__ o,
-                        int H, int M, int in_bf16, int out_bf16, float clamp, int opt) {
+                        int H, int M, int in_bf16, int out_bf16, float clamp, int opt,
+                        const float2* __restrict__ rmat) {
   constexpr int NT = 512, NWV = NT / 64;
   constexpr int RU = F / 2, RD = D / 2;
   static_assert(RU <= 64 && RD <= 64 && NT % RU == 0 && NT % RD == 0, "row width");
   constexpr int SU = NT / RU, SD = NT / RD;                  // rows per pass
   constexpr int IU = (MM + SU - 1) / SU, ID = (MM + SD - 1) / SD;   // M <= MM
-  __shared__ float2 s_lam[kMaxModes], s_beta[kMaxModes], s_a[kMaxModes];
+  __shared__ float2 s_lam[kMaxModes], s_beta[kMaxModes], s_a[kMaxModes], s_ar[kMaxModes];
   __shared__ float s_num[SD][D];
   __shared__ float s_den[NWV];
 
@@ -225,8 +239,19 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
     }
   }
   __syncthreads();   // a[m]
+  // with a readout matrix R ([H][M][M]), the readouts use (a R)[n] = sum_m a[m] R[m][n]
+  if (rmat) {
+    if (tid < M) {
+      const float2* Rh = rmat + (size_t)h * M * M;
+      float2 acc = make_float2(0.f, 0.f);
+      for (int m = 0; m < M; ++m) acc = cfma(s_a[m], Rh[(size_t)m * M + tid], acc);
+      s_ar[tid] = acc;
+    }
+    __syncthreads();
+  }
+  const float2* A = rmat ? s_ar : s_a;
 
-  float dn = tid < M ? s_a[tid].x * e.x - s_a[tid].y * e.y : 0.f;
+  float dn = tid < M ? A[tid].x * e.x - A[tid].y * e.y : 0.f;
   dn = wave_sum(dn);
   if (lane == 0) s_den[wave] = dn;
   // Gamma rows: update, store, accumulate Re(a[m] G[m, 2pd..2pd+1]).
@@ -235,7 +260,7 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
   for (int i = 0; i < ID; ++i) {
     const int m = rd + SD * i;
     if (m < M) {
-      const float2 l = s_lam[m], bt = s_beta[m], am = s_a[m];
+      const float2 l = s_lam[m], bt = s_beta[m], am = A[m];
       const float2 g0 = cfma(l, make_float2(g[i].x, g[i].y), make_float2(bt.x * v0, bt.y * v0));
       const float2 g1 = cfma(l, make_float2(g[i].z, g[i].w), make_float2(bt.x * v1, bt.y * v1));
       Gb[(size_t)m * RD + pd] = make_float4(g0.x, g0.y, g1.x, g1.y);
@@ -269,7 +294,7 @@ scan_prefill_kernel(const void* __restrict__ q, const void* __restrict__ k,
                     float2* __restrict__ G, float2* __restrict__ E, void* __restrict__ o,
                     int accumulate, int N, int H, int F, int D, int M,
                     int in_bf16, int out_bf16, float clamp, int reverse, RowStrides sqk,
-                    RowStrides sv, int opt) {
+                    RowStrides sv, int opt, const float2* __restrict__ rmat) {
   __shared__ StepSmem s;
   const int bh = blockIdx.x;
   const int b = bh / H, h = bh % H;
@@ -283,7 +308,7 @@ scan_prefill_kernel(const void* __restrict__ q, const void* __restrict__ k,
     load_token(s, q, k, v, (size_t)(b * sqk.b + pos * sqk.n + h * sqk.h),
                (size_t)(b * sv.b + pos * sv.n + h * sv.h), F, D, in_bf16, opt);
     __syncthreads();
-    step_one(s, Ub, Gb, Eb, F, D, M);
+    step_one(s, Ub, Gb, Eb, F, D, M, rmat ? rmat + (size_t)h * M * M : nullptr);
     if (o) {
       for (int j = threadIdx.x; j < D; j += kStepThreads) {
         float n = 0.f;
@@ -326,11 +351,11 @@ static void launch_decode_rows(const DecodeArgs& a, hipStream_t st) {
   if (a.M <= 64)
     hipLaunchKernelGGL((decode_step_rows_kernel<F, D, 64>), dim3(a.B * a.H), dim3(512), 0, st,
                        a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H, a.M, a.in_bf16,
-                       a.out_bf16, a.clamp, a.opt);
+                       a.out_bf16, a.clamp, a.opt, a.readout);
   else
     hipLaunchKernelGGL((decode_step_rows_kernel<F, D, kMaxModes>), dim3(a.B * a.H), dim3(512),
                        0, st, a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H, a.M,
-                       a.in_bf16, a.out_bf16, a.clamp, a.opt);
+                       a.in_bf16, a.out_bf16, a.clamp, a.opt, a.readout);
 }
 
 // Compute units of the current device (cached per device; 256 when there is none).
@@ -364,7 +389,7 @@ hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t st) {
 #undef IA_DEC
   hipLaunchKernelGGL(decode_step_kernel, dim3(a.B * a.H), dim3(kStepThreads), 0, st, a.q, a.k,
                      a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H, a.F, a.D, a.M, a.in_bf16,
-                     a.out_bf16, a.clamp, a.opt);
+                     a.out_bf16, a.clamp, a.opt, a.readout);
   prof_end(st, kKindDecode);
   return hipGetLastError();
 }
@@ -374,7 +399,8 @@ hipError_t launch_scan_prefill(const ScanArgs& a, hipStream_t st) {
   prof_begin(st);
   hipLaunchKernelGGL(scan_prefill_kernel, dim3(a.B * a.H), dim3(kStepThreads), 0, st, a.q,
                      a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.accumulate, a.N, a.H, a.F, a.D,
-                     a.M, a.in_bf16, a.out_bf16, a.clamp, a.reverse, a.sqk, a.sv, a.opt);
+                     a.M, a.in_bf16, a.out_bf16, a.clamp, a.reverse, a.sqk, a.sv, a.opt,
+                     a.readout);
   prof_end(st, kKindScan);
   return hipGetLastError();
 }

@@ -276,3 +276,27 @@ def test_bwd_validation():
     assert bwd(d, st0=ctypes.pointer(ia.IAState(addr(10).value, addr(11).value, 0))) == 1
     assert bwd(d, dst0=ctypes.pointer(ia.IAState(addr(0).value, addr(11).value,
                                                  addr(12).value))) == 5
+
+
+def test_readout_variants_validation():
+    d = desc()
+    rd = addr(20)
+    assert ia.lib.ia_prefill_fwd_readout(ctypes.byref(d), addr(0), addr(1), addr(2), addr(3),
+                                         addr(4), None, state(), addr(5), addr(6), 1 << 40,
+                                         None) == 1
+    assert ia.lib.ia_prefill_fwd_readout(ctypes.byref(d), addr(0), addr(1), addr(2), addr(3),
+                                         addr(4), addr(20, 8), state(), addr(5), addr(6),
+                                         1 << 40, None) == 4
+    # readout overlapping the output
+    assert ia.lib.ia_prefill_fwd_readout(ctypes.byref(d), addr(0), addr(1), addr(2), addr(3),
+                                         addr(4), addr(5), state(), addr(5, 256), addr(6),
+                                         1 << 40, None) == 5
+    assert ia.lib.ia_decode_step_readout(ctypes.byref(d), addr(0), addr(1), addr(2), addr(3),
+                                         addr(4), None, state(), addr(5), None) == 1
+    assert ia.lib.ia_decode_step_readout(ctypes.byref(desc(bidir=True)), addr(0), addr(1),
+                                         addr(2), addr(3), addr(4), rd, state(), addr(5),
+                                         None) == 7
+    # readout workspace: one state, rounded up to 256 bytes
+    B, H, M, F, D = 2, 3, 16, 32, 16
+    want = (B * H * M * (F + D + 1) * 8 + 255) // 256 * 256
+    assert ia.lib.ia_prefill_readout_workspace_bytes(ctypes.byref(d)) == want
