@@ -218,6 +218,23 @@ def bench_decode(torch, ia, W, batches=(1, 16, 64), steps=256):
                          "hbm_frac": step_bytes / (graph_us * 1e-6) / HBM_PEAK,
                          "bytes_per_step": step_bytes}
         del g
+        if Bd == 16:
+            # the same steps with a readout matrix R per head (the M^2 term of a decode step)
+            rng = np.random.default_rng(7)
+            R = (np.eye(M) + 0.1 * rng.standard_normal((H, M, M))).astype(np.complex64)
+            Rd = torch.from_numpy(R).cuda()
+            for _ in range(2):
+                for t in range(steps):
+                    ia.ia_decode_step_readout(desc, stp["q"][t], stp["k"][t], stp["v"][t], lam,
+                                              beta, Rd, st, o[t])
+                torch.cuda.synchronize()
+            e0.record()
+            for t in range(steps):
+                ia.ia_decode_step_readout(desc, stp["q"][t], stp["k"][t], stp["v"][t], lam, beta,
+                                          Rd, st, o[t])
+            e1.record()
+            torch.cuda.synchronize()
+            res[f"B{Bd}"]["readout_matrix_eager_us_per_step"] = e0.elapsed_time(e1) / steps * 1e3
     return res
 
 
