@@ -19,6 +19,10 @@ namespace ia {
 constexpr int kStepThreads = 256;
 constexpr int kStepWaves = kStepThreads / 64;
 
+__device__ __forceinline__ float2 cadd2(float2 a, float2 b) {
+  return make_float2(a.x + b.x, a.y + b.y);
+}
+
 struct StepSmem {
   float fq[kMaxDim];
   float fk[kMaxDim];
@@ -27,6 +31,7 @@ struct StepSmem {
   float2 beta[kMaxModes];
   float2 a[kMaxModes];
   float2 ar[kMaxModes];   // a R, with a readout matrix R
+  float2 rp[kStepThreads];   // partial sums of a R
   float2 eta[kMaxModes];
   float num[kStepWaves][kMaxDim];
   float den[kStepWaves];
@@ -69,10 +74,18 @@ __device__ __forceinline__ void step_one(StepSmem& s, float2* __restrict__ U,
   }
   __syncthreads();
   if (R) {
-    for (int n = threadIdx.x; n < M; n += kStepThreads) {
+    // thread t sums the modes m = t / M, t / M + parts, ... of column n = t % M
+    const int parts = kStepThreads / M, n = threadIdx.x % M, part = threadIdx.x / M;
+    if (part < parts) {
       float2 acc = make_float2(0.f, 0.f);
-      for (int m = 0; m < M; ++m) acc = cfma(s.a[m], R[(size_t)m * M + n], acc);
-      s.ar[n] = acc;
+      for (int m = part; m < M; m += parts) acc = cfma(s.a[m], R[(size_t)m * M + n], acc);
+      s.rp[threadIdx.x] = acc;
+    }
+    __syncthreads();
+    if (threadIdx.x < M) {
+      float2 acc = make_float2(0.f, 0.f);
+      for (int p = 0; p < parts; ++p) acc = cadd2(acc, s.rp[p * M + threadIdx.x]);
+      s.ar[threadIdx.x] = acc;
     }
     __syncthreads();
   }
@@ -181,6 +194,7 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
   constexpr int SU = NT / RU, SD = NT / RD;                  // rows per pass
   constexpr int IU = (MM + SU - 1) / SU, ID = (MM + SD - 1) / SD;   // M <= MM
   __shared__ float2 s_lam[kMaxModes], s_beta[kMaxModes], s_a[kMaxModes], s_ar[kMaxModes];
+  __shared__ float2 s_rp[NT];   // partial sums of a R
   __shared__ float s_num[SD][D];
   __shared__ float s_den[NWV];
 
@@ -241,10 +255,19 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
   __syncthreads();   // a[m]
   // with a readout matrix R ([H][M][M]), the readouts use (a R)[n] = sum_m a[m] R[m][n]
   if (rmat) {
-    if (tid < M) {
-      const float2* Rh = rmat + (size_t)h * M * M;
+    // thread t sums the modes m = t / M, t / M + parts, ... of column n = t % M (coalesced
+    // rows of R), then M threads add the parts
+    const float2* Rh = rmat + (size_t)h * M * M;
+    const int parts = NT / M, n = tid % M, part = tid / M;
+    if (part < parts) {
       float2 acc = make_float2(0.f, 0.f);
-      for (int m = 0; m < M; ++m) acc = cfma(s_a[m], Rh[(size_t)m * M + tid], acc);
+      for (int m = part; m < M; m += parts) acc = cfma(s_a[m], Rh[(size_t)m * M + n], acc);
+      s_rp[tid] = acc;
+    }
+    __syncthreads();
+    if (tid < M) {
+      float2 acc = make_float2(0.f, 0.f);
+      for (int p = 0; p < parts; ++p) acc = cadd2(acc, s_rp[p * M + tid]);
       s_ar[tid] = acc;
     }
     __syncthreads();
