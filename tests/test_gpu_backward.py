@@ -264,3 +264,25 @@ def test_backward_sequence_segments(case):
                                  state=st, no_den=case == "noden_fp32", threads=2)
     _compare(got, ref, TOL_BF16 if dtype == "bf16" else TOL_F32, f"bwd segments {case}",
              state=st is not None)
+
+
+@pytest.mark.parametrize("shape,dtype", [((1, 1, 40, 256, 256, 128), "f32"),
+                                         ((2, 1, 70, 256, 128, 128), "bf16"),
+                                         ((1, 2, 33, 16, 256, 16), "f32")])
+def test_backward_largest_sizes(shape, dtype):
+    """The largest F, Dv and M the boundary takes (the widest staged rows: blocks of 3 tokens),
+    and the narrowest F beside the widest Dv."""
+    import torch
+    ia = _ia()
+    B, H, N, F, D, M = shape
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    inp = W.make_inputs(B, H, N, F, D, M, dtype=dtype, seed=580 + F + M)
+    dO = np.random.default_rng(581).standard_normal((B, N, H, D)).astype(np.float32)
+    tag(f"backward largest sizes {shape} {dtype}")
+    q, k, v = (dev(inp[n], td) for n in "qkv")
+    r = ia.prefill_bwd(q, k, v, dev(inp["lam"]), dev(inp["beta"]), dev(dO))
+    torch.cuda.synchronize()
+    got = tuple(host(x) for x in r[:5]) + (None,)
+    ref = oracle.prefill_bwd(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"], dO,
+                             threads=2)
+    _compare(got, ref, TOL_BF16 if dtype == "bf16" else TOL_F32, f"bwd largest {shape}")

@@ -26,10 +26,12 @@ def _R(H, M, seed):
 
 
 @pytest.mark.parametrize("shape", [(2, 3, 32, 48, 16), (1, 16, 128, 128, 64),
-                                   (64, 16, 128, 128, 64)])
+                                   (64, 16, 128, 128, 64), (2, 2, 64, 64, 128),
+                                   (1, 2, 256, 256, 128)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_decode_readout_matrix(shape, dtype):
-    """Generic kernel, row-parallel kernel (16 slices) and mode-looping kernel (1024 slices)."""
+    """Generic kernel, row-parallel kernel (16 slices) and mode-looping kernel (1024 slices),
+    and the largest mode count (M = 128) on both kernels."""
     import torch
     ia = _ia()
     B, H, F, D, M = shape
