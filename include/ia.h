@@ -204,8 +204,10 @@ ia_status ia_decode_step(const ia_desc* desc,
 
 /* Workspace bytes ia_prefill_bwd needs for this descriptor: state checkpoints every 32 tokens
  * (B*H*ceil(N/32)*M*(F+Dv+1) complex64), per-token partial denominators (B*H*N*M/2 complex64),
- * per-mode-group gradient rows (M/16 * B*H*N*(2F+Dv) float) and per-slice lambda/beta
- * gradients, each region 256-byte aligned.  0 on an invalid descriptor. */
+ * per-mode-group gradient rows (M/16 * B*H*N*(2F+Dv) float), per-slice lambda/beta gradients,
+ * the recompute's a = phi(q) U^T per token (B*H*N*M complex64) and, when a long sequence is
+ * cut into segments, their start states and entering adjoints, each region 256-byte aligned.
+ * 0 on an invalid descriptor. */
 size_t ia_prefill_bwd_workspace_bytes(const ia_desc* desc);
 
 /* Gradients of the causal layer (ia_prefill_fwd's outputs o) for a real loss L, given

@@ -461,6 +461,7 @@ ia_status ia_prefill_bwd(const ia_desc* d, const void* q, const void* k, const v
   a.dpart = reinterpret_cast<float2*>(ws + L.dpart_off);
   a.gpart = reinterpret_cast<float*>(ws + L.gpart_off);
   a.lpart = reinterpret_cast<float2*>(ws + L.lpart_off);
+  a.apart = reinterpret_cast<float2*>(ws + L.apart_off);
   a.cstate = reinterpret_cast<float2*>(ws + L.cstate_off);
   a.cadj = reinterpret_cast<float2*>(ws + L.cadj_off);
   a.nseg = ia::bwd_segments(d->B, d->H, d->N, d->M, &a.seg_len);

@@ -195,7 +195,7 @@ struct State {
 constexpr int kPrefetch = kBwdPrefetch;
 
 struct RowLayout {
-  int q, k, v, g, p, bytes;   // byte offsets of the segments in a row, and its length
+  int q, k, v, g, p, a, bytes;   // byte offsets of the segments in a row, and its length
 };
 
 __device__ __forceinline__ RowLayout row_layout(const BwdArgs& a, bool with_den) {
@@ -206,7 +206,8 @@ __device__ __forceinline__ RowLayout row_layout(const BwdArgs& a, bool with_den)
   l.v = 2 * a.F * ei;
   l.g = l.v + a.D * ei;
   l.p = l.g + a.D * eo;
-  l.bytes = l.p + (with_den ? 8 * (a.M / kModesPerWave) : 0);
+  l.a = l.p + (with_den ? 8 * (a.M / kModesPerWave) : 0);
+  l.bytes = l.a + (with_den ? 8 * kModesPerWg : 0);   // the workgroup's a[m] of the token
   return l;
 }
 
@@ -236,9 +237,12 @@ __device__ __forceinline__ void stage_issue(const BwdArgs& a, const Slice& s, co
           src = static_cast<const char*>(a.v) + row * a.D * ei + (o - l.v);
         else if (o < l.p)
           src = static_cast<const char*>(a.dO) + row * a.D * eo + (o - l.g);
-        else
+        else if (o < l.a)
           src = reinterpret_cast<const char*>(a.dpart) +
                 ((size_t)s.slice * a.N + t) * (a.M / kModesPerWave) * 8 + (o - l.p);
+        else
+          src = reinterpret_cast<const char*>(a.apart) +
+                (((size_t)s.slice * a.N + t) * a.M + s.grp * kModesPerWg) * 8 + (o - l.a);
         x = *reinterpret_cast<const uint4*>(src);
       }
     }
@@ -364,8 +368,13 @@ __global__ void __launch_bounds__(kThreads) bwd_forward_kernel(const BwdArgs a) 
         den += am.x * st.E[i].x - am.y * st.E[i].y;
         gn += am.x * sm.x - am.y * sm.y;
       }
-      if (s.lane == 0)
+      if (s.lane == 0) {
         a.dpart[((size_t)s.slice * a.N + t) * parts + s.m0 / kModesPerWave] = make_float2(den, gn);
+#pragma unroll
+        for (int i = 0; i < kModesPerWave; ++i)   // a[m], which the reverse sweep reuses
+          a.apart[((size_t)s.slice * a.N + t) * a.M + s.m0 + i] =
+              make_float2(red[4 * i], red[4 * i + 1]);
+      }
       if (t % kBwdCheckpoint == kBwdCheckpoint - 1 || t == a.N - 1)
         st.store_ckpt(a, s, t / kBwdCheckpoint);
     }
@@ -452,20 +461,18 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(const BwdArgs a) 
       Token<NF, ND> x;
       x.load(a, s, L, row);
       const float rc = uniform(blk_rc, 8 * j), dd = uniform(blk_dd, 8 * j);
-      float red[kRed];
+      // h[m] = sum_j g_j conj(Gam_mj) over the wave; a[m] as the recompute sweep formed it
+      float red[2 * kModesPerWave];
 #pragma unroll
       for (int i = 0; i < kModesPerWave; ++i) {
-        float2 ap = make_float2(0.f, 0.f), hp = make_float2(0.f, 0.f);
-#pragma unroll
-        for (int j2 = 0; j2 < NF; ++j2) ap = cadd(ap, cscale(x.fq[j2], cur.U[i][j2]));
+        float2 hp = make_float2(0.f, 0.f);
 #pragma unroll
         for (int j2 = 0; j2 < ND; ++j2) hp = cadd(hp, cscale(x.g[j2], conjf2(cur.G[i][j2])));
-        red[4 * i + 0] = ap.x;
-        red[4 * i + 1] = ap.y;
-        red[4 * i + 2] = hp.x;
-        red[4 * i + 3] = hp.y;
+        red[2 * i + 0] = hp.x;
+        red[2 * i + 1] = hp.y;
       }
       wave_totals(red);
+      const float2* arow = reinterpret_cast<const float2*>(row + L.a) + s.wave * kModesPerWave;
       float dfq[NF], dfk[NF], dv[ND];
 #pragma unroll
       for (int j2 = 0; j2 < NF; ++j2) dfq[j2] = dfk[j2] = 0.f;
@@ -473,8 +480,8 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(const BwdArgs a) 
       for (int j2 = 0; j2 < ND; ++j2) dv[j2] = 0.f;
 #pragma unroll
       for (int i = 0; i < kModesPerWave; ++i) {
-        const float2 am = make_float2(red[4 * i], red[4 * i + 1]);
-        const float2 hm = make_float2(red[4 * i + 2], red[4 * i + 3]);
+        const float2 am = arow[i];
+        const float2 hm = make_float2(red[2 * i], red[2 * i + 1]);
         // gradient of a[m]: sum_j dnum_j conj(Gam_mj) + dden conj(eta_m)
         const float2 ga = cadd(cscale(rc, hm), cscale(dd, conjf2(cur.E[i])));
         const float2 ca = conjf2(am);
@@ -780,7 +787,8 @@ BwdLayout bwd_layout(int B, int H, int N, int F, int D, int M) {
   l.dpart_off = up(S * nck * M * (F + D + 1) * 8);
   l.gpart_off = l.dpart_off + up(S * N * (M / kModesPerWave) * 8);
   l.lpart_off = l.gpart_off + up((size_t)(M / kModesPerWg) * S * N * (2 * F + D) * 4);
-  l.cstate_off = l.lpart_off + up(S * nseg * M * 2 * 8);
+  l.apart_off = l.lpart_off + up(S * nseg * M * 2 * 8);
+  l.cstate_off = l.apart_off + up(S * N * M * 8);
   l.cadj_off = l.cstate_off + carry;
   l.bytes = l.cadj_off + carry;
   return l;
@@ -790,7 +798,7 @@ BwdLayout bwd_layout(int B, int H, int N, int F, int D, int M) {
 // reverse sweep, the per-wave den partials).
 static size_t bwd_row_bytes(int F, int D, int M, int in_bf16, int out_bf16, bool rev) {
   return (size_t)(2 * F + D) * (in_bf16 ? 2 : 4) + (size_t)D * (out_bf16 ? 2 : 4) +
-         (rev ? (size_t)8 * (M / kModesPerWave) : 0);
+         (rev ? (size_t)8 * (M / kModesPerWave) + 8 * kModesPerWg : 0);
 }
 
 size_t bwd_lds_bytes(int F, int D, int M, int in_bf16, int out_bf16, int tb, bool rev) {

@@ -127,6 +127,7 @@ struct BwdArgs {
   float2* dpart;
   float* gpart;
   float2* lpart;
+  float2* apart;                  // a[m] per token, from the recompute sweep
   int B, H, N, F, D, M;
   int in_bf16, out_bf16, opt;
   float clamp;
@@ -139,7 +140,7 @@ struct BwdArgs {
 };
 
 struct BwdLayout {
-  size_t ckpt_off, dpart_off, gpart_off, lpart_off, cstate_off, cadj_off, bytes;
+  size_t ckpt_off, dpart_off, gpart_off, lpart_off, apart_off, cstate_off, cadj_off, bytes;
 };
 int bwd_segments(int B, int H, int N, int M, int* seg_len);
 BwdLayout bwd_layout(int B, int H, int N, int F, int D, int M);

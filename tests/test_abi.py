@@ -245,7 +245,8 @@ def test_bwd_workspace_bytes_layout():
         nseg = (N + seg - 1) // seg
         carry = up(S * nseg * M * (F + D + 1) * 8) if nseg > 1 else 0
         want = (up(S * nck * M * (F + D + 1) * 8) + up(S * N * (M // 2) * 8)
-                + up((M // 16) * S * N * (2 * F + D) * 4) + up(S * nseg * M * 16) + 2 * carry)
+                + up((M // 16) * S * N * (2 * F + D) * 4) + up(S * nseg * M * 16)
+                + up(S * N * M * 8) + 2 * carry)
         d = desc(B=B, H=H, N=N, F=F, Dv=D, M=M)
         assert ia.lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(d)) == want
     assert ia.lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(desc(N=0))) == 0
