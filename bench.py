@@ -348,7 +348,7 @@ def main():
                          "256 MiB) whose counter readings scale the hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(the layer shards by (b,h) with no communication)", file=sys.stderr)
         sys.exit(2)
 

@@ -61,7 +61,7 @@ typedef enum {
   IA_ERR_ALIGN = 4,        /* a device pointer is not 16-byte aligned */
   IA_ERR_ALIAS = 5,        /* an output overlaps an input or another output */
   IA_ERR_DOMAIN = 6,       /* lambda outside the supported domain (see ia_prefill_fwd) */
-  IA_ERR_UNSUPPORTED = 7,  /* a combination this build does not implement */
+  IA_ERR_UNSUPPORTED = 7,  /* a combination the library does not implement */
   IA_ERR_LAUNCH = 8,       /* the HIP runtime refused a launch */
   IA_ERR_WORKSPACE = 9     /* workspace NULL or smaller than the *_workspace_bytes query */
 } ia_status;
