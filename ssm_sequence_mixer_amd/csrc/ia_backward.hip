@@ -10,22 +10,30 @@
 // Reverse mode carries the state adjoints Ubar_t = (readout at t) + conj(lam) Ubar_{t+1} (the
 // same for Gam and eta); complex gradients are dL/dRe + i dL/dIm.
 //
-// Three launches:
+// Launches:
 //  1. bwd_forward_kernel: recompute the states from the initial state, store them every
 //     kBwdCheckpoint tokens (and after the last token), and per token the partial sums over
 //     this wave's modes of den_t and of g_t . num_t (g = dL/do), which the readout gradient
-//     needs in full before any mode can run backward.
+//     needs in full before any mode can run backward, and a_t[m], which the reverse sweep
+//     reuses.
 //  2. bwd_reverse_kernel: walk each checkpoint interval backward from its end state,
 //     rebuilding U_{t-1} = (U_t - beta phi(k_t)) / lam (the interval is short, so the growth of
 //     rounding by |lam|^-1 per step stays bounded), carrying the adjoints, and collecting the
 //     gradients of q, k, v (summed over this workgroup's modes), lambda and beta.
 //  3. bwd_reduce_kernel: sum the per-mode-group partials of dq, dk, dv in a fixed order and
-//     store them in the input dtype; sum lambda and beta gradients over the batch.
+//     store them in the input dtype; sum lambda and beta gradients over the batch (and over
+//     sequence segments).
+// When slices x mode groups leave compute units idle, each sequence is cut into segments that
+// run side by side; both sweeps are linear recurrences, so each gets a local pass from zero
+// and bwd_carry_kernel (lam^L for the states, conj(lam)^L for the adjoints, across segments)
+// before its full pass.  The bidirectional layer runs all of it twice, the second time on the
+// reversed walk, adding onto the first.
 //
-// Layout: a workgroup is 4 waves x 4 modes (16 modes, a block of one slice's modes); lane l of
-// a wave owns state columns l, l + 64, ... of U (F wide) and Gam (D wide) for all four of its
+// Layout: a workgroup is 8 waves x 2 modes (16 modes, a block of one slice's modes); lane l of
+// a wave owns state columns l, l + 64, ... of U (F wide) and Gam (D wide) for both of its
 // modes, so every sum over modes of a column is a lane's own, and every sum over a mode's
-// columns is one 16-value wave reduction per token.
+// columns is a wave reduction (DPP moves) per token.  Token rows reach LDS in double-buffered
+// blocks.
 #include <algorithm>
 
 #include "ia_device.hpp"
