@@ -561,7 +561,7 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(const BwdArgs a) 
         if (s.lane + 64 * j2 < a.D) out[2 * a.F + s.lane + 64 * j2] = dv[j2];
     }
     __syncthreads();
-    // the four waves' rows summed: this workgroup's partial for the block's tokens; then the
+    // the waves' rows summed: this workgroup's partial for the block's tokens; then the
     // next block's rows land in the buffer just used
     const int ntok = a.local ? 0 : min(TB, t_hi - s.lo + 1);
     for (int e = threadIdx.x; e < ntok * W; e += kThreads) {
