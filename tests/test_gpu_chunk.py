@@ -1,8 +1,8 @@
 """GPU parity of the chunked MFMA prefill (bf16 inputs) against the oracle.
 
-Small cases compare every (b,h) slice; the full workload sizes run in the launch
-configuration the benchmark times and compare sampled (b,h) slices, which the oracle
-computes one by one.  Tolerance: row-wise relative error 2e-2 (bf16 inputs).
+Every case compares every (b,h) slice, the full workload sizes included (in the launch
+configuration the benchmark times), and the final state wherever the call returns one.
+Tolerance: row-wise relative error 2e-2 (bf16 inputs).
 """
 import numpy as np
 import pytest
@@ -77,11 +77,9 @@ def test_chunk_few_segments_with_state():
     st_ref = tuple(host(s) for s in st)
     tag("chunk prefill few segments with state")
     o = _run(inp, state=st)
-    slices = [(0, 0), (2, 5), (5, 15)]
     o_ref, _, _, st_out = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"],
-                                         state=st_ref, threads=8)
-    o = host(o)
-    e_o = max(rowrel(o[b, :, h], o_ref[b, :, h]) for b, h in slices)
+                                         state=st_ref, threads=16)
+    e_o = rowrel(host(o), o_ref)
     e_s = state_rel(tuple(host(s) for s in st), st_out)
     report("few segments output", e_o)
     report("few segments state", e_s)
@@ -201,50 +199,86 @@ def test_chunk_lambda_edges_multi_segment(plan):
 
 
 # ---------------------------------------------------------------- full workload sizes
+# Every (b, h) slice at the full sizes, in the launch configuration the benchmark times; the
+# causal runs pass a zero initial state so the final state is returned and compared too.
+# The worst slice is printed with its head (the smallest-dt heads carry the largest bf16
+# error: their modes remember the most tokens).
 
-def _sampled(inp, slices, bidir=False, out="f32", threads=8):
-    o = host(_run(inp, bidir=bidir, out=out))
-    if bidir:
-        ref = oracle.bidir(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"],
-                           slices=slices, threads=threads)
-    else:
+def _worst_slice(o, ref):
+    B, H = o.shape[0], o.shape[2]
+    errs = np.array([[rowrel(o[b, :, h], ref[b, :, h]) for h in range(H)] for b in range(B)])
+    b, h = np.unravel_index(np.argmax(errs), errs.shape)
+    return float(errs[b, h]), (int(b), int(h)), errs.max(axis=0)
+
+
+def _full(inp, out="f32", with_state=True, threads=16, ref=None):
+    ia = _ia()
+    sh = inp["shape"]
+    B, H, F, D, M = sh["B"], sh["H"], sh["F"], sh["D"], sh["M"]
+    st = ia.new_state(B, H, M, F, D) if with_state else None
+    o = host(_run(inp, state=st, out=out))
+    if ref is None:
         ref = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"],
-                             slices=slices, threads=threads)[0]
-    worst = 0.0
-    for (b, h) in slices:
-        worst = max(worst, rowrel(o[b, :, h], ref[b, :, h]))
-    return worst
+                             threads=threads)
+    o_ref, _, _, st_ref = ref
+    worst, where, per_head = _worst_slice(o, o_ref)
+    e_s = state_rel(tuple(host(s) for s in st), st_ref) if with_state else 0.0
+    return worst, where, e_s, per_head
 
 
-def _check_workload(name, err):
-    report(name, err)
-    assert err < TOL_BF16
+def _check_full(name, inp, res):
+    worst, where, e_s, per_head = res
+    dt = np.asarray(inp["dt"])
+    report(f"{name} output (worst slice b,h={where}, dt={dt[where[1]]:.2e})", worst)
+    report(f"{name} final state", e_s)
+    print(f"[err] {name} per head: " + " ".join(f"h{h}:{e:.1e}" for h, e in enumerate(per_head)),
+          flush=True)
+    assert worst < TOL_BF16 and e_s < TOL_BF16
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_workload_125m_sampled(out):
+def test_workload_125m_all_slices(out):
     inp = W.l125m()
-    tag(f"125m workload out={out}")
-    _check_workload(f"125m out={out}", _sampled(inp, [(0, 0), (3, 5), (7, 11), (5, 2)], out=out))
+    tag(f"125m workload out={out}, every slice and the final state")
+    _check_full(f"125m out={out}", inp, _full(inp, out=out))
 
 
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_workload_1p3b_sampled(out):
+def test_workload_1p3b_all_slices(out):
     inp = W.l1p3b()
-    tag(f"1.3b workload out={out}")
-    _check_workload(f"1.3b out={out}", _sampled(inp, [(0, 0), (1, 7), (2, 13), (3, 15)], out=out))
+    tag(f"1.3b workload out={out}, every slice and the final state")
+    _check_full(f"1.3b out={out}", inp, _full(inp, out=out))
 
 
-def test_workload_1p3b_long_sampled():
+def test_workload_1p3b_long_all_slices():
     inp = W.l1p3b(N=7168)
-    tag("1.3b x3.5 length workload")
-    _check_workload("1.3b x3.5 length", _sampled(inp, [(0, 3), (3, 12)]))
+    tag("1.3b x3.5 length workload, every slice and the final state")
+    _check_full("1.3b x3.5 length", inp, _full(inp, out="bf16"))
 
 
-def test_workload_caduceus_sampled():
+def test_workload_caduceus_all_slices():
+    """The genomic workload on every (b, h) slice: the bidirectional layer as the benchmark
+    runs it (bf16 out, both directions summed), then each direction alone as a causal run with
+    its final state (the forward sequence, and the flipped sequence for the reverse
+    direction).  The oracle's two directions serve all three comparisons."""
     inp = W.caduceus()
-    tag("caduceus bidirectional workload")
-    _check_workload("caduceus bidir", _sampled(inp, [(0, 1), (1, 6)], bidir=True))
+    fl = dict(inp)
+    for n in "qkv":
+        fl[n] = np.ascontiguousarray(inp[n][:, ::-1])
+    ref_f = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"], threads=16)
+    ref_r = oracle.prefill(fl["q"], fl["k"], fl["v"], inp["lam"], inp["beta"], threads=16)
+    tag("caduceus bidirectional workload, every slice")
+    o = host(_run(inp, bidir=True, out="bf16"))
+    worst, where, per_head = _worst_slice(o, ref_f[0] + ref_r[0][:, ::-1])
+    del o
+    report(f"caduceus bidir (worst slice b,h={where}, dt={inp['dt'][where[1]]:.2e})", worst)
+    print("[err] caduceus bidir per head: " +
+          " ".join(f"h{h}:{e:.1e}" for h, e in enumerate(per_head)), flush=True)
+    assert worst < TOL_BF16
+    tag("caduceus forward direction, causal with state")
+    _check_full("caduceus forward", inp, _full(inp, out="bf16", ref=ref_f))
+    tag("caduceus reverse direction, causal with state")
+    _check_full("caduceus reverse", fl, _full(fl, out="bf16", ref=ref_r))
 
 
 # ---------------------------------------------------------------- strided inputs

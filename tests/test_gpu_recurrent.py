@@ -160,35 +160,45 @@ def test_decode_forced_clamp():
 
 
 @pytest.mark.parametrize("Bd", [1, 16, 64])
-def test_decode_1p3b_shape(Bd):
-    """Decode at the 1.3B-shaped layer (H=16, F=Dv=128, M=64) from a 32-token prefilled state,
-    at the benchmark's batch sizes (both decode kernels: 16 and 256 slices take the
-    row-parallel one, 1024 the mode-looping one)."""
+def test_decode_1p3b_workload_all_steps(Bd):
+    """The decode workload in full: at the 1.3B-shaped layer (H=16, F=Dv=128, M=64), a
+    32-token chunked prefill of a random prefix, then all 256 decode steps, at the benchmark's
+    batch sizes (16 and 256 slices take the row-parallel kernel, 1024 the mode-looping one).
+    Every step's output of every (b, h) slice, and the state after the prefix and after the
+    last step, against the oracle's recurrence over all 288 tokens (the scan the decode steps
+    continue)."""
     torch = _torch()
     ia = _lib()
-    wl = W.decode(Bd, steps=4, prefix=32)
+    steps, prefix = 256, 32
+    wl = W.decode(Bd, steps=steps, prefix=prefix)
     pre, stp = wl["prefix"], wl["steps"]
     lam, beta = wl["lam"], wl["beta"]
+    bf = torch.bfloat16
     tag(f"decode 1.3b B={Bd} prefix")
     st = ia.new_state(Bd, 16, 64, 128, 128)
-    ia.prefill(dev(pre["q"], torch.bfloat16), dev(pre["k"], torch.bfloat16),
-               dev(pre["v"], torch.bfloat16), dev(lam), dev(beta), state=st, want_output=False)
-    _, _, _, st_ref = oracle.prefill(pre["q"], pre["k"], pre["v"], lam, beta, threads=8)
+    ia.prefill(dev(pre["q"], bf), dev(pre["k"], bf), dev(pre["v"], bf), dev(lam), dev(beta),
+               state=st, want_output=False)
     torch.cuda.synchronize()
-    # the prefix state comes from bf16 inputs through the chunked MFMA path: bf16 tolerance
-    err = state_rel(tuple(host(s) for s in st), st_ref)
-    report(f"decode 1.3b B={Bd} prefix state", err)
-    assert err < TOL_BF16
-    for t in range(4):
-        tag(f"decode 1.3b B={Bd} step {t}")
-        o = ia.decode(dev(stp["q"][t], torch.bfloat16), dev(stp["k"][t], torch.bfloat16),
-                      dev(stp["v"][t], torch.bfloat16), dev(lam), dev(beta), st)
-        o_ref, st_ref = oracle.decode_step(stp["q"][t], stp["k"][t], stp["v"][t], lam, beta,
-                                           st_ref)
-        torch.cuda.synchronize()
-        err = rowrel(host(o), o_ref)
-        report(f"decode 1.3b B={Bd} step {t}", err)
-        assert err < TOL_BF16
+    st_pre = tuple(host(s) for s in st)
+    sq, sk, sv = (dev(stp[n], bf) for n in "qkv")
+    lam_d, beta_d = dev(lam), dev(beta)
+    o = torch.empty((steps, Bd, 16, 128), dtype=torch.float32, device="cuda")
+    tag(f"decode 1.3b B={Bd} {steps} steps")
+    for t in range(steps):
+        ia.decode(sq[t], sk[t], sv[t], lam_d, beta_d, st, o_t=o[t])
+    torch.cuda.synchronize()
+    o = host(o)
+    # the oracle: one recurrence per slice over the prefix and the steps
+    seq = {n: np.concatenate([pre[n], np.moveaxis(stp[n], 0, 1)], axis=1) for n in "qkv"}
+    _, _, _, st_ref_pre = oracle.prefill(pre["q"], pre["k"], pre["v"], lam, beta, threads=16)
+    o_ref, _, _, st_ref = oracle.prefill(seq["q"], seq["k"], seq["v"], lam, beta, threads=16)
+    e_pre = state_rel(st_pre, st_ref_pre)
+    report(f"decode 1.3b B={Bd} prefix state (chunked bf16 path)", e_pre)
+    worst = max(rowrel(o[t], o_ref[:, prefix + t]) for t in range(steps))
+    report(f"decode 1.3b B={Bd} all {steps} steps, every slice", worst)
+    e_st = state_rel(tuple(host(s) for s in st), st_ref)
+    report(f"decode 1.3b B={Bd} state after the last step", e_st)
+    assert e_pre < TOL_BF16 and worst < TOL_BF16 and e_st < TOL_BF16
 
 
 @pytest.mark.parametrize("shape", [(64, 32, 16), (16, 240, 48), (128, 64, 128), (256, 256, 128)])
