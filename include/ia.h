@@ -35,7 +35,9 @@
  *
  * Conventions for every call:
  *   - All pointers except `desc`, `st` (the struct) are DEVICE pointers, 16-byte aligned.
- *   - The caller owns every buffer.  The library allocates nothing and keeps no global state.
+ *   - The caller owns every buffer.  The library allocates nothing.  Its only state is per
+ *     thread: the text behind the last IA_ERR_LAUNCH (ia_last_launch_error), and, for the
+ *     duration of an ia_prefill_fwd_profiled call, a pointer to that call's event list.
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the null stream);
  *     the call returns without synchronising.  Results are visible after the stream syncs.
  *   - Validation happens on the host before anything is enqueued.  On any error nothing is
@@ -108,36 +110,59 @@ typedef struct ia_state {
   void* eta;
 } ia_state;
 
-/* Zero the state (the recurrence starts from U = Gamma = eta = 0).  Enqueues a fill kernel
- * (no memset node), so it may be captured in a graph.  Errors: IA_ERR_NULL, IA_ERR_SHAPE,
- * IA_ERR_ALIGN, IA_ERR_LAUNCH. */
+/* Zero the state: U = Gamma = eta = 0, the state of the recurrence before its first token
+ * (the fixed-size memory U, Gamma, eta of [summary §3.1], updated token by token by the S4D
+ * recurrence of [summary §3.2]; a chunked prefill that builds only this state [summary §F.2]
+ * or a decode step then continue from it).  Enqueues a fill kernel (no memset node), so it
+ * may be captured in a graph.  Errors: IA_ERR_NULL, IA_ERR_SHAPE, IA_ERR_ALIGN,
+ * IA_ERR_LAUNCH. */
 ia_status ia_state_init(const ia_desc* desc, ia_state* st, void* stream);
 
 /* Bytes of device workspace ia_prefill_fwd needs for `desc` (may be 0); 0 also if the desc
- * is invalid.  The workspace holds the per-head tables and per-segment state summaries of the
- * chunked scan, or a state for state-less fp32 calls.  Its contents need no initialisation
+ * is invalid or has no kernel (bf16 shapes outside the chunked path).  The workspace holds the
+ * per-head tables, the per-segment state summaries and one state (the caller's initial state
+ * copied there when several segments run, or the fp32 route's working state) of the chunked
+ * scan, or a state for state-less fp32 calls.  Its contents need no initialisation
  * and are scratch between calls.  (The bidirectional layer accumulates its two directions in
  * o itself, in o's dtype.) */
 size_t ia_prefill_workspace_bytes(const ia_desc* desc);
 
-/* Host-side check of the mode domain for `desc` (lambda_host: [H][M] complex64 in HOST
- * memory).  lambda lives in device memory in the other calls, which therefore cannot check
- * it without a synchronisation and do not; callers that build lambda call this once.
- * IA_ERR_DOMAIN unless every 0 < |lambda| <= 1 + 1e-6 and, for bf16 inputs (the chunked MFMA
- * path, whose per-chunk decay factorises lambda^(i-j) = lambda^i lambda^(-j)),
- * |lambda|^(chunk-1) >= 2^-8 (|lambda| >= 0.916 at chunk 64, 0.836 at chunk 32).  Outside
- * that domain the chunked path stays finite but may miss the bf16 tolerance. */
-ia_status ia_check_lambda(const ia_desc* desc, const void* lambda_host);
+/* Host-side check of the modes for `desc` (lambda_host: [H][M] complex64 in HOST memory).
+ * Returns IA_ERR_DOMAIN unless every 0 < |lambda| <= 1 + 1e-6 (stable S4D modes
+ * [summary §3.2]; the prefill and decode calls do not reject other values, which they cannot
+ * see without a synchronisation: they compute the recurrence as written).
+ * fp32_heads (may be NULL) receives, for bf16 inputs, the number of heads that the chunked
+ * MFMA prefill runs on the fp32 route instead (0 for fp32 inputs).  A head takes that route
+ * when any of its modes has |lambda| outside (0, 1 + 1e-6], |lambda|^(chunk-1) < 2^-8 (the
+ * chunk's decay tables hold beta lambda^-j for j < chunk with one fp16 scale per head), or
+ * |1 - lambda|^2 > 1000 (1 - |lambda|^2): a mode (nearly) undamped far from lambda = 1, whose
+ * state is an oscillating sum in which the mean feature (about 1) cancels while the bf16
+ * rounding of the features does not.  S4D-Lin modes exp(dt(-1/2 + i pi m)), m < 64, never do
+ * for dt <= 0.17 at chunk 64.
+ * The route is decided on the device from lambda, with this same test, in the prefill's own
+ * launches: the head's first workgroup runs the token-by-token fp32 recurrence over the whole
+ * sequence (about as slow per head as the fp32 prefill below); the other heads are
+ * unaffected. */
+ia_status ia_check_lambda(const ia_desc* desc, const void* lambda_host, int* fp32_heads);
 
 /* Causal (or, with IA_FLAG_BIDIR, bidirectional) forward of one IA layer over N tokens.
  *
- * Runs the chunkwise form of the recurrence: work inside each chunk of `chunk` tokens is done
- * as dense contractions, the state is passed across chunk boundaries, and a second pass
- * recomputes each segment from its corrected initial state [summary §3.2, §A.2].  Results
- * equal the token-by-token recurrence up to rounding and do not depend on `chunk`.
+ * bf16 inputs: the chunkwise form of the recurrence on MFMA.  Work inside each chunk of
+ * `chunk` tokens is done as dense contractions, the state is passed across chunk boundaries,
+ * and a second pass recomputes each segment from its corrected initial state [summary §3.2,
+ * §A.2].  Results equal the token-by-token recurrence up to rounding and do not depend on
+ * `chunk`.  Shapes: F = Dv in {32, 64, 128}, M in {16, 32, 64}, and 64 token rows of one
+ * tensor within 1 GiB; other bf16 shapes return IA_ERR_UNSUPPORTED.  Heads with modes the
+ * chunk factorisation does not resolve run the fp32 recurrence in the same launches (see
+ * ia_check_lambda).  Accuracy: about 1e-2 row-wise relative error with the S4D-Lin modes and
+ * beta = 1; like any finite-precision evaluation of o = num / max(den, clamp), a row whose
+ * Re(den) nearly cancels (terms of both signs, e.g. with complex beta) or lies near the clamp
+ * loses accuracy in proportion, about 2^-8 times the ratio of its terms' size to den.
+ * fp32 inputs: the token-by-token recurrence in fp32, one workgroup per (b,h) slice (a
+ * reference path: about 300x slower than the chunked path at the 1.3B-shaped layer).
  *
  *   q, k, v    inputs, layouts above, read only.
- *   lambda     [H][M] complex64 in the domain of ia_check_lambda (not checked here).
+ *   lambda     [H][M] complex64 modes (see ia_check_lambda), read on the device only.
  *   beta       [H][M] complex64 input vector of the S4D recurrence (B on the pages).
  *   st         NULL: start from zero and do not return a state.  Otherwise st->U/Gamma/eta
  *              hold the initial state on entry and the state after token N-1 on return
@@ -148,8 +173,8 @@ ia_status ia_check_lambda(const ia_desc* desc, const void* lambda_host);
  *   workspace  device scratch of at least ia_prefill_workspace_bytes(desc) bytes.
  * Errors: IA_ERR_NULL, IA_ERR_SHAPE, IA_ERR_DTYPE, IA_ERR_ALIGN, IA_ERR_ALIAS (o overlapping
  * an input, lambda/beta or the state, or state buffers overlapping inputs or each other),
- * IA_ERR_DOMAIN (den_clamp), IA_ERR_UNSUPPORTED (BIDIR with st != NULL, sizes, chunk),
- * IA_ERR_WORKSPACE, IA_ERR_LAUNCH. */
+ * IA_ERR_DOMAIN (den_clamp), IA_ERR_UNSUPPORTED (BIDIR with st != NULL, sizes, chunk, bf16
+ * shapes without a chunk kernel), IA_ERR_WORKSPACE, IA_ERR_LAUNCH. */
 ia_status ia_prefill_fwd(const ia_desc* desc,
                          const void* q, const void* k, const void* v,
                          const void* lambda, const void* beta,
@@ -179,7 +204,8 @@ ia_status ia_prefill_fwd_strided(const ia_desc* desc,
  * events[2i+1] after the kernel on `stream` and stores the kernel's kind in kinds[i]
  * (2 decay tables, launched on their own only when a sequence is one segment; 3 segment end
  * states, whose launch also computes the tables when there are several segments; 4 segment
- * carry; 5 chunked prefill with outputs; 0 zero fill; 1 token-sequential prefill).  events: 2*max_launches hipEvent_t handles
+ * carry; 5 chunked prefill with outputs; 0 zero fill; 1 token-sequential prefill; 10 copy of
+ * the caller's initial state into the workspace).  events: 2*max_launches hipEvent_t handles
  * created by the caller.  *n_launches receives the number of launches recorded.  Errors: as
  * ia_prefill_fwd, and IA_ERR_NULL for missing events/kinds/n_launches. */
 ia_status ia_prefill_fwd_profiled(const ia_desc* desc,

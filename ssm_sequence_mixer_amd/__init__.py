@@ -73,7 +73,7 @@ lib.ia_state_init.argtypes = [_D, _S, _P]
 lib.ia_state_init.restype = ctypes.c_int
 lib.ia_prefill_workspace_bytes.argtypes = [_D]
 lib.ia_prefill_workspace_bytes.restype = ctypes.c_size_t
-lib.ia_check_lambda.argtypes = [_D, _P]
+lib.ia_check_lambda.argtypes = [_D, _P, ctypes.POINTER(ctypes.c_int)]
 lib.ia_check_lambda.restype = ctypes.c_int
 lib.ia_prefill_fwd.argtypes = [_D, _P, _P, _P, _P, _P, _S, _P, _P, ctypes.c_size_t, _P]
 lib.ia_prefill_fwd.restype = ctypes.c_int
@@ -111,7 +111,7 @@ EXPORTS = ("ia_state_init", "ia_prefill_workspace_bytes", "ia_check_lambda", "ia
            "ia_prefill_fwd_readout", "ia_decode_step_readout", "ia_status_string",
            "ia_last_launch_error")
 KIND_NAMES = {0: "fill", 1: "scan", 2: "tables", 3: "summary", 4: "carry", 5: "chunk",
-              6: "decode", 7: "bwd_forward", 8: "bwd_reverse", 9: "bwd_reduce"}
+              6: "decode", 7: "bwd_forward", 8: "bwd_reverse", 9: "bwd_reduce", 10: "copy"}
 
 
 def make_desc(B, H, N, F, Dv, M, in_dtype=IA_BF16, out_dtype=IA_F32, den_clamp=1e-6,
@@ -147,6 +147,19 @@ def _dense(*ts):
             raise ValueError("tensors passed to libia must be contiguous")
 
 
+def _keep_for(t, stream):
+    """Tell torch's caching allocator that `t` (allocated on the current stream) is used by
+    work enqueued on `stream`, so its memory is not reused before that work ends."""
+    if t is None or stream is None:
+        return
+    import torch
+    if isinstance(stream, torch.cuda.Stream):
+        t.record_stream(stream)
+    elif stream != torch.cuda.current_stream().cuda_stream:
+        raise ValueError("pass a torch.cuda.Stream (or a workspace you keep alive) when "
+                         "enqueuing on another stream")
+
+
 def _check(status, where):
     if status != 0:
         detail = lib.ia_last_launch_error().decode() if status == 8 else ""
@@ -173,12 +186,15 @@ def ia_prefill_workspace_bytes(desc: IADesc) -> int:
     return int(lib.ia_prefill_workspace_bytes(ctypes.byref(desc)))
 
 
-def ia_check_lambda(desc: IADesc, lam_host) -> None:
-    """lam_host: numpy complex64 [H, M] in host memory."""
+def ia_check_lambda(desc: IADesc, lam_host) -> int:
+    """lam_host: numpy complex64 [H, M] in host memory.  Raises on IA_ERR_DOMAIN; returns the
+    number of heads the chunked bf16 prefill runs on its fp32 route."""
     import numpy as np
     arr = np.ascontiguousarray(lam_host, dtype=np.complex64)
-    _check(lib.ia_check_lambda(ctypes.byref(desc), arr.ctypes.data_as(ctypes.c_void_p)),
-           "ia_check_lambda")
+    n = ctypes.c_int(-1)
+    _check(lib.ia_check_lambda(ctypes.byref(desc), arr.ctypes.data_as(ctypes.c_void_p),
+                               ctypes.byref(n)), "ia_check_lambda")
+    return n.value
 
 
 def ia_prefill_fwd(desc: IADesc, q, k, v, lam, beta, state, o, workspace, stream=None):
@@ -291,18 +307,24 @@ def prefill(q, k, v, lam, beta, state=None, out_dtype=None, bidir=False, chunk=0
                      bidir, chunk, no_den, identity_features)
     o = torch.empty((B, N, H, Dv), dtype=out_dtype, device=q.device) if want_output else None
     if readout is not None:
-        if workspace is None:
+        own_ws = workspace is None
+        if own_ws:
             nb = ia_prefill_readout_workspace_bytes(desc)
             workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device)
         ia_prefill_fwd_readout(desc, q, k, v, lam, beta, readout, state, o, workspace, stream)
+        if own_ws:
+            _keep_for(workspace, stream)
         return o
-    if workspace is None:
+    own_ws = workspace is None
+    if own_ws:
         nb = ia_prefill_workspace_bytes(desc)
         workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=q.device) if nb else None
     if all(t.is_contiguous() for t in (q, k, v)):
         ia_prefill_fwd(desc, q, k, v, lam, beta, state, o, workspace, stream)
     else:
         ia_prefill_fwd_strided(desc, q, k, v, lam, beta, state, o, workspace, stream)
+    if own_ws:
+        _keep_for(workspace, stream)
     return o
 
 
@@ -340,9 +362,12 @@ def prefill_bwd(q, k, v, lam, beta, dO, state0=None, den_clamp=1e-6, no_den=Fals
     dlam = torch.empty((H, M), dtype=torch.complex64, device=q.device)
     dbeta = torch.empty_like(dlam)
     dst = new_state(B, H, M, F, Dv, device=q.device, zero=False) if want_state_grad else None
-    if workspace is None:
+    own_ws = workspace is None
+    if own_ws:
         workspace = torch.empty(max(ia_prefill_bwd_workspace_bytes(desc), 16), dtype=torch.uint8,
                                 device=q.device)
     ia_prefill_bwd(desc, q, k, v, lam, beta, state0, dO, dq, dk, dv, dlam, dbeta, dst, workspace,
                    stream)
+    if own_ws:
+        _keep_for(workspace, stream)
     return dq, dk, dv, dlam, dbeta, dst

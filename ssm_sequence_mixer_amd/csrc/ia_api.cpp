@@ -88,7 +88,7 @@ ScanWorkspace scan_workspace(const ia_desc* d, bool have_state) {
 
 struct ChunkPlan {
   int C, G, seg_chunks;
-  size_t tables_off, slots_off, bytes;
+  size_t tables_off, slots_off, state_off, bytes;
 };
 
 // Readout options of the desc's flags, in the kernels' encoding.
@@ -99,8 +99,9 @@ int kernel_opt(const ia_desc* d) {
 
 bool use_chunk_path(const ia_desc* d) {
   // The chunk kernels address a chunk's token rows with 32-bit byte offsets, rows outside a
-  // chunk wrapping to large ones: 64 rows of H * F bf16 values must span at most 1 GiB (else
-  // the token-sequential path runs).
+  // chunk wrapping to large ones: 64 rows of H * F bf16 values must span at most 1 GiB.
+  // bf16 calls outside these shapes are refused (IA_ERR_UNSUPPORTED), not sent to the
+  // token-sequential kernel.
   return d->in_dtype == IA_BF16 && ia::chunk_supported(d->F, d->Dv, d->M) &&
          64L * d->H * std::max(d->F, d->Dv) * 2 <= (1L << 30);
 }
@@ -122,6 +123,10 @@ ChunkPlan chunk_plan(const ia_desc* d) {
   p.slots_off = p.bytes;
   if (p.G > 1)
     p.bytes += round_up(size_t(seqs) * (p.G - 1) * ia::chunk_slot_floats(d->F, d->Dv, d->M) * 4);
+  // one state: the copy of a caller's initial state (several segments), or the working state
+  // of heads on the fp32 route when the caller passes none
+  p.state_off = p.bytes;
+  p.bytes += round_up(state_bytes(d));
   return p;
 }
 
@@ -160,19 +165,27 @@ const char* ia_status_string(ia_status s) {
 
 const char* ia_last_launch_error(void) { return t_launch_error; }
 
-ia_status ia_check_lambda(const ia_desc* d, const void* lambda_host) {
+ia_status ia_check_lambda(const ia_desc* d, const void* lambda_host, int* fp32_heads) {
   ia_status s = check_desc(d, false);
   if (s != IA_OK) return s;
   if (!lambda_host) return IA_ERR_NULL;
   const float* l = static_cast<const float*>(lambda_host);
   const int chunk = d->chunk ? d->chunk : 64;
-  for (long i = 0; i < long(d->H) * d->M; ++i) {
-    const double mag = std::hypot(double(l[2 * i]), double(l[2 * i + 1]));
-    if (!(mag > 0.0 && mag <= 1.0 + 1e-6)) return IA_ERR_DOMAIN;
-    if (d->in_dtype == IA_BF16 && std::pow(mag, chunk - 1) < std::ldexp(1.0, -8))
-      return IA_ERR_DOMAIN;
+  const bool chunked = d->in_dtype == IA_BF16;
+  int routed = 0;
+  ia_status st = IA_OK;
+  for (long h = 0; h < d->H; ++h) {
+    bool route = false;
+    for (long m = 0; m < d->M; ++m) {
+      const float x = l[2 * (h * d->M + m)], y = l[2 * (h * d->M + m) + 1];
+      const double mag = std::hypot(double(x), double(y));
+      if (!(mag > 0.0 && mag <= 1.0 + 1e-6)) st = IA_ERR_DOMAIN;
+      route = route || ia::chunk_unresolved(x, y, chunk);
+    }
+    routed += chunked && route;
   }
-  return IA_OK;
+  if (fp32_heads) *fp32_heads = routed;
+  return st;
 }
 
 ia_status ia_state_init(const ia_desc* d, ia_state* st, void* stream) {
@@ -189,6 +202,7 @@ ia_status ia_state_init(const ia_desc* d, ia_state* st, void* stream) {
 size_t ia_prefill_workspace_bytes(const ia_desc* d) {
   if (check_desc(d, true) != IA_OK) return 0;
   if (use_chunk_path(d)) return chunk_plan(d).bytes;
+  if (d->in_dtype == IA_BF16) return 0;   // no bf16 kernel for this shape
   // The state-less case needs the larger workspace; callers size for it.
   return scan_workspace(d, false).bytes;
 }
@@ -276,6 +290,9 @@ static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, co
       return IA_ERR_ALIAS;
     char* ws = static_cast<char*>(workspace);
     ia::ChunkPrefillArgs a{};
+    a.wU = reinterpret_cast<float2*>(ws + pl.state_off);
+    a.wG = reinterpret_cast<float2*>(ws + pl.state_off + state_u_bytes(d));
+    a.wE = reinterpret_cast<float2*>(ws + pl.state_off + state_u_bytes(d) + state_g_bytes(d));
     a.q = q;
     a.k = k;
     a.v = v;
@@ -309,7 +326,12 @@ static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, co
     return launch_status(e);
   }
 
-  // fp32 path (and bf16 shapes without a chunked instantiation): token-sequential recurrence.
+  // bf16 inputs on shapes without a chunk kernel are refused rather than run 300x slower by
+  // the token-sequential kernel (fp32 inputs take that path, and any shape with a readout
+  // matrix).
+  if (!readout && d->in_dtype == IA_BF16) return IA_ERR_UNSUPPORTED;
+
+  // fp32 path: token-sequential recurrence.
   const ScanWorkspace w = scan_workspace(d, st != nullptr);
   if (w.bytes) {
     if (!workspace || ws_bytes < w.bytes) return IA_ERR_WORKSPACE;

@@ -317,6 +317,9 @@ hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
   a.slots_per_seq = G - 1;
   a.tables = p.tables;
   a.table_bytes = tb;
+  a.wU = p.wU;
+  a.wG = p.wG;
+  a.wE = p.wE;
 
   auto go = [&](const ChunkArgs& x, int n_wg, int kind) -> hipError_t {
     return C == 64 ? dispatch_fdm<64>(x, p.F, p.D, p.M, n_wg, st, kind)
@@ -347,13 +350,25 @@ hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
     }
   }
   // Pass 2: every segment from its initial state, with outputs; the last segment returns the
-  // final state.  State-only calls run just the last segment.
+  // final state.  State-only calls run just the last segment.  With several segments each
+  // running, the caller's initial state is read from a copy in the workspace: the last
+  // segment's workgroup writes the final state into the caller's buffers while the others may
+  // still be reading their initial state.
   ChunkArgs o = a;
   o.seg_prev = G > 1 ? p.slots : nullptr;
   o.seg_inclusive = inclusive;
   o.init0_U = p.U0;
   o.init0_G = p.G0;
   o.init0_E = p.E0;
+  if (p.U0 && p.o && G > 1) {
+    const size_t bh = (size_t)p.B * p.H;
+    e = launch_copy3(p.wU, p.U0, bh * p.M * p.F * 8, p.wG, p.G0, bh * p.M * p.D * 8, p.wE, p.E0,
+                     bh * p.M * 8, st);
+    if (e != hipSuccess) return e;
+    o.init0_U = p.wU;
+    o.init0_G = p.wG;
+    o.init0_E = p.wE;
+  }
   o.o = p.o;
   o.accumulate = p.accumulate;
   o.fin_U = p.U1;

@@ -39,6 +39,7 @@
 
 #include "ia_device.hpp"
 #include "ia_kernels.hpp"
+#include "ia_scan.hpp"
 
 namespace ia {
 
@@ -320,6 +321,11 @@ struct ChunkArgs {
   // the state waves' accumulator layout (SlotLayout).
   const float2 *init0_U, *init0_G, *init0_E;   // caller layout: [seq][M][F] etc.
   float2 *fin_U, *fin_G, *fin_E;               // caller layout
+  // Heads whose tables carry the route flag run the fp32 recurrence instead: the first
+  // workgroup of the head in this launch walks the whole sequence, in place on fin_* (which
+  // then hold the initial state) or, without a caller state, on the zeroed workspace state
+  // wU/wG/wE (same layout).
+  float2 *wU, *wG, *wE;
   const float* seg_prev;
   int seg_inclusive;                           // seg_prev[g] already holds the state entering
                                                // segment g+1 (caller state included)
@@ -352,6 +358,7 @@ struct TableLayout {
   static constexpr long oPowS = oGeoT + 8L * M;       // float2 [M]: lam^(segment length)
   static constexpr long oInv = oPowS + 8L * M;        // float2 [M]: 1 / lam
   static constexpr long oSc = oInv + 8L * M;          // float: 1 / fp16 table scale
+  static constexpr long oRoute = oSc + 4;             // int: 1 = the head takes the fp32 route
   static constexpr long bytes = (oSc + 16 + 255) / 256 * 256;
 };
 
@@ -1130,6 +1137,35 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
   }
 }
 
+// The fp32 route of a head whose modes the bf16 chunk factorisation does not resolve
+// (chunk_unresolved): the token-by-token recurrence of slice (b, h) over all N tokens by this
+// workgroup, from the caller's state (updated in place) or from zero in the workspace state.
+template <int C, int F, int D, int M>
+__device__ __forceinline__ void fp32_route(const ChunkArgs& a, int b, int h, unsigned char* smem) {
+  constexpr int NW = C / 16 + StateWaves<F, D, M>::NS;
+  using S = SeqSmem<NW, F, D, M, false>;
+  static_assert(sizeof(S) <= Layout<C, F, D, M, C / 16>::bytes, "fits the kernel's LDS");
+  S& s = *reinterpret_cast<S*>(smem);
+  const size_t seq = (size_t)b * a.H + h;
+  float2 *U, *G, *E;
+  if (a.fin_U) {
+    U = a.fin_U + seq * M * F;
+    G = a.fin_G + seq * M * D;
+    E = a.fin_E + seq * M;
+  } else {
+    U = a.wU + seq * M * F;
+    G = a.wG + seq * M * D;
+    E = a.wE + seq * M;
+    for (int i = threadIdx.x; i < M * F; i += 64 * NW) U[i] = make_float2(0.f, 0.f);
+    for (int i = threadIdx.x; i < M * D; i += 64 * NW) G[i] = make_float2(0.f, 0.f);
+    for (int i = threadIdx.x; i < M; i += 64 * NW) E[i] = make_float2(0.f, 0.f);
+    __syncthreads();
+  }
+  const SeqScanArgs sa{a.q, a.k, a.v, a.sqk, a.sv, a.lam, a.beta, a.o, a.accumulate, a.N, a.H,
+                       F, D, M, 1, a.out_bf16, a.clamp, a.dir, a.opt, nullptr};
+  seq_scan(s, sa, b, h, U, G, E);
+}
+
 template <int C, int F, int D, int M, int W>
 __device__ __forceinline__ void run_role(const ChunkArgs& a, const Ctx<C, F, D, M>& x) {
   if constexpr (W < C / 16)
@@ -1187,6 +1223,10 @@ chunk_prefill_kernel(const ChunkArgs a) {
   x.last_seg = x.c_end == n_chunks_total;
   x.want_out = a.o != nullptr;
   x.tab = a.tables + (size_t)x.h * a.table_bytes;
+  if (__builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(x.tab + TL::oRoute))) {
+    if (x.seg == a.seg_first) fp32_route<C, F, D, M>(a, x.b, x.h, smem_raw);
+    return;
+  }
 
   x.wb_unscale = *reinterpret_cast<const float*>(x.tab + TL::oSc);
   // Both roles run the same sequence of block barriers.  Each wave runs code specialised

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include <cmath>
+
 namespace ia {
 
 // Kernel kinds reported by the profiling entry point, in launch order.
@@ -18,6 +20,7 @@ enum LaunchKind {
   kKindBwdForward = 7,   // backward: state recompute and checkpoints
   kKindBwdReverse = 8,   // backward: reverse sweep
   kKindBwdReduce = 9,    // backward: sum of the mode groups' partials
+  kKindCopy = 10,        // copy of the caller's initial state into the workspace
 };
 
 // While set (only inside ia_prefill_fwd_profiled), every launch records events[2i] before
@@ -89,8 +92,12 @@ struct ScanArgs {
 // go through `slots` (B*H*(segments-1) slots of chunk_slot_floats(F, D, M) floats), from
 // which each segment's workgroup assembles its initial state.  `tables` holds
 // H * chunk_table_bytes(chunk, M) bytes.  U0/G0/E0: initial state or NULL (zeros);
-// U1/G1/E1: final state or NULL.  o NULL: state only.  accumulate: add to the values already
-// in o (in o's dtype).
+// U1/G1/E1: final state or NULL (with a caller state both are the caller's buffers).
+// wU/wG/wE: one state in the workspace ([B][H][M][F], [B][H][M][D], [B][H][M]): with several
+// segments and a caller state, the initial state is copied there first, so that no
+// workgroup reads the caller's buffers while the last segment writes the final state into
+// them; heads that take the fp32 route without a caller state run in it.  o NULL: state only.
+// accumulate: add to the values already in o (in o's dtype).
 struct ChunkPrefillArgs {
   const void *q, *k, *v;   // element strides sqk (q and k) and sv; o dense
   RowStrides sqk, sv;
@@ -101,12 +108,36 @@ struct ChunkPrefillArgs {
   float2 *U1, *G1, *E1;
   float* slots;                 // (B*H) x (segments-1) segment end states
   unsigned char* tables;
+  float2 *wU, *wG, *wE;         // workspace state
   int B, H, N, F, D, M;
   int chunk, segments, seg_chunks;
   int reverse, out_bf16;
   float clamp;
   int opt;   // kOptNoDen | kOptIdentity
 };
+
+// Whether the bf16 chunk factorisation does NOT resolve mode lam = (lx, ly) at chunk length C
+// (its head then runs the fp32 recurrence inside the chunked launches): for
+//   - |lam| outside (0, 1 + 1e-6], or not finite: outside the S4D modes' domain, computed
+//     literally by the fp32 recurrence;
+//   - |lam|^(C-1) < 2^-8: the per-chunk decay tables hold beta lam^-j for j < C with one fp16
+//     scale per head;
+//   - |1 - lam|^2 > 1000 (1 - |lam|^2): a mode (nearly) undamped far from lam = 1.  Its state
+//     is an oscillating sum over ~1/(1 - |lam|^2) tokens in which the mean of phi(k) = elu+1
+//     (about 1) cancels while the bf16 rounding of the features does not: a few percent of
+//     the sum at inputs of scale 1/sqrt(F).  S4D-Lin modes exp(dt(-1/2 + i pi m)) stay below
+//     300 for any dt when m < 64 (the ratio peaks near 4/dt where the argument reaches pi).
+// fp64 keeps the digits of 1 - |lam|^2 near the unit circle (every product below is exact).
+// The device computes it with the tables; ia_check_lambda runs the same function on the host.
+__host__ __device__ inline bool chunk_unresolved(float lx, float ly, int C) {
+  const double x = lx, y = ly;
+  const double mag2 = x * x + y * y;
+  if (!(mag2 > 0.0) || !(mag2 <= (1.0 + 1e-6) * (1.0 + 1e-6))) return true;
+  if (0.5 * (C - 1) * log(mag2) < -8.0 * 0.6931471805599453) return true;
+  const double one_minus = (1.0 - x) * (1.0 + x) - y * y;   // 1 - |lam|^2
+  const double dist2 = (1.0 - x) * (1.0 - x) + y * y;       // |1 - lam|^2
+  return dist2 > 1000.0 * one_minus;
+}
 
 bool chunk_supported(int F, int D, int M);
 long chunk_table_bytes(int chunk, int M);
@@ -153,6 +184,10 @@ int device_cus();                                        // compute units of the
 hipError_t launch_chunk_prefill(const ChunkPrefillArgs& a, hipStream_t st);
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+// dst[i] <- src[i] for up to three (dst, src, bytes) pairs (bytes multiples of 16; a pair
+// with bytes 0 is skipped), one launch.
+hipError_t launch_copy3(void* d0, const void* s0, size_t n0, void* d1, const void* s1,
+                        size_t n1, void* d2, const void* s2, size_t n2, hipStream_t st);
 hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_scan_prefill(const ScanArgs& a, hipStream_t st);
 

@@ -1,152 +1,20 @@
 // ia_recurrent.hip — token-by-token IA kernels (fp32 VALU): the decode step, the
-// token-sequential fp32 prefill, and the state fill.
+// token-sequential fp32 prefill, and the state fill and copy.
 //
 // The step is the recurrence and readout of the layer ("Interdomain Attention: Beyond
 // Token-Level Key-Value Memory": summary page §3.2 for the complex-diagonal S4D recurrence and
 // the O(M(R+d)) per-step decode; episode page, "Key Components and Derivation", for the
-// feature map and the matrix form Fq U^T Gamma / Fq U^T eta):
-//     U[m,:] <- lam_m U[m,:] + beta_m phi(k_t),   a[m] = phi(q_t) . U[m,:]
-//     G[m,:] <- lam_m G[m,:] + beta_m v_t,        eta[m] <- lam_m eta[m] + beta_m
-//     o_t = Re(sum_m a[m] G[m,:]) / max(Re(sum_m a[m] eta[m]), clamp)
-// One workgroup owns one (b,h) slice.  The state stays in global memory (HBM or L2) and is
-// streamed once per token: each wave takes every 4th mode and its lanes cover a state row
-// with 16-byte accesses, so a row of F complex values is one coalesced access.
+// feature map and the matrix form Fq U^T Gamma / Fq U^T eta), written once in ia_scan.hpp.
+// One workgroup owns one (b,h) slice.
 #include "ia_device.hpp"
 #include "ia_kernels.hpp"
+#include "ia_scan.hpp"
 
 namespace ia {
 
 constexpr int kStepThreads = 256;
 constexpr int kStepWaves = kStepThreads / 64;
-
-__device__ __forceinline__ float2 cadd2(float2 a, float2 b) {
-  return make_float2(a.x + b.x, a.y + b.y);
-}
-
-struct StepSmem {
-  float fq[kMaxDim];
-  float fk[kMaxDim];
-  float v[kMaxDim];
-  float2 lam[kMaxModes];
-  float2 beta[kMaxModes];
-  float2 a[kMaxModes];
-  float2 ar[kMaxModes];   // a R, with a readout matrix R
-  float2 rp[kStepThreads];   // partial sums of a R
-  float2 eta[kMaxModes];
-  float num[kStepWaves][kMaxDim];
-  float den[kStepWaves];
-};
-
-// State rows are float2 arrays; lanes take two complex values (one float4) at a time.
-// F and D are multiples of 16, so a row is a whole number of float4 pairs.
-// R: this head's readout matrix [M][M] (row m, column n), or NULL for none: the readouts then
-// use (a R)[n] = sum_m a[m] R[m][n] in place of a.
-__device__ __forceinline__ void step_one(StepSmem& s, float2* __restrict__ U,
-                                         float2* __restrict__ G, float2* __restrict__ E,
-                                         int F, int D, int M, const float2* __restrict__ R) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-
-  // U rows: update in place and contract with phi(q_t).
-  for (int m = wave; m < M; m += kStepWaves) {
-    const float2 l = s.lam[m], b = s.beta[m];
-    float4* row = reinterpret_cast<float4*>(U + (size_t)m * F);
-    float ar = 0.f, ai = 0.f;
-    for (int p = lane; p < F / 2; p += 64) {
-      float4 u = row[p];
-      const float k0 = s.fk[2 * p], k1 = s.fk[2 * p + 1];
-      float2 u0 = cfma(l, make_float2(u.x, u.y), make_float2(b.x * k0, b.y * k0));
-      float2 u1 = cfma(l, make_float2(u.z, u.w), make_float2(b.x * k1, b.y * k1));
-      row[p] = make_float4(u0.x, u0.y, u1.x, u1.y);
-      const float q0 = s.fq[2 * p], q1 = s.fq[2 * p + 1];
-      ar += q0 * u0.x + q1 * u1.x;
-      ai += q0 * u0.y + q1 * u1.y;
-    }
-    ar = wave_sum(ar);
-    ai = wave_sum(ai);
-    if (lane == 0) s.a[m] = make_float2(ar, ai);
-  }
-  // eta: one mode per thread.
-  for (int m = threadIdx.x; m < M; m += kStepThreads) {
-    float2 e = cfma(s.lam[m], E[m], s.beta[m]);
-    E[m] = e;
-    s.eta[m] = e;
-  }
-  __syncthreads();
-  if (R) {
-    // thread t sums the modes m = t / M, t / M + parts, ... of column n = t % M
-    const int parts = kStepThreads / M, n = threadIdx.x % M, part = threadIdx.x / M;
-    if (part < parts) {
-      float2 acc = make_float2(0.f, 0.f);
-      for (int m = part; m < M; m += parts) acc = cfma(s.a[m], R[(size_t)m * M + n], acc);
-      s.rp[threadIdx.x] = acc;
-    }
-    __syncthreads();
-    if (threadIdx.x < M) {
-      float2 acc = make_float2(0.f, 0.f);
-      for (int p = 0; p < parts; ++p) acc = cadd2(acc, s.rp[p * M + threadIdx.x]);
-      s.ar[threadIdx.x] = acc;
-    }
-    __syncthreads();
-  }
-  const float2* A = R ? s.ar : s.a;
-
-  // Gamma rows: update in place, accumulate Re(a[m] G[m,:]) per lane.
-  float acc[kMaxDim / 64];
-#pragma unroll
-  for (int i = 0; i < kMaxDim / 64; ++i) acc[i] = 0.f;
-  for (int m = wave; m < M; m += kStepWaves) {
-    const float2 l = s.lam[m], b = s.beta[m], a = A[m];
-    float4* row = reinterpret_cast<float4*>(G + (size_t)m * D);
-#pragma unroll
-    for (int i = 0; i < kMaxDim / 128; ++i) {
-      const int p = lane + 64 * i;
-      if (p < D / 2) {
-        float4 g = row[p];
-        const float v0 = s.v[2 * p], v1 = s.v[2 * p + 1];
-        float2 g0 = cfma(l, make_float2(g.x, g.y), make_float2(b.x * v0, b.y * v0));
-        float2 g1 = cfma(l, make_float2(g.z, g.w), make_float2(b.x * v1, b.y * v1));
-        row[p] = make_float4(g0.x, g0.y, g1.x, g1.y);
-        acc[2 * i] += a.x * g0.x - a.y * g0.y;
-        acc[2 * i + 1] += a.x * g1.x - a.y * g1.y;
-      }
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < kMaxDim / 128; ++i) {
-    const int p = lane + 64 * i;
-    if (p < D / 2) {
-      s.num[wave][2 * p] = acc[2 * i];
-      s.num[wave][2 * p + 1] = acc[2 * i + 1];
-    }
-  }
-  if (wave == 0) {
-    float d = 0.f;
-    for (int m = lane; m < M; m += 64) d += A[m].x * s.eta[m].x - A[m].y * s.eta[m].y;
-    d = wave_sum(d);
-    if (lane == 0) s.den[0] = d;
-  }
-  __syncthreads();
-}
-
-// Load phi(q), phi(k), v of one token into shared memory.
-__device__ __forceinline__ void load_token(StepSmem& s, const void* q, const void* k,
-                                           const void* v, size_t qk_off, size_t v_off, int F,
-                                           int D, int bf16, int opt) {
-  for (int i = threadIdx.x; i < F; i += kStepThreads) {
-    s.fq[i] = feat(load_in(q, qk_off + i, bf16), opt);
-    s.fk[i] = feat(load_in(k, qk_off + i, bf16), opt);
-  }
-  for (int i = threadIdx.x; i < D; i += kStepThreads) s.v[i] = load_in(v, v_off + i, bf16);
-}
-
-__device__ __forceinline__ void load_modes(StepSmem& s, const float2* lam, const float2* beta,
-                                           int h, int M) {
-  for (int m = threadIdx.x; m < M; m += kStepThreads) {
-    s.lam[m] = lam[(size_t)h * M + m];
-    s.beta[m] = beta[(size_t)h * M + m];
-  }
-}
+using StepSmem = SeqSmem<kStepWaves, kMaxDim, kMaxDim, kMaxModes, true>;
 
 // ---------------------------------------------------------------- kernels
 
@@ -161,17 +29,13 @@ decode_step_kernel(const void* __restrict__ q, const void* __restrict__ k,
   __shared__ StepSmem s;
   const int bh = blockIdx.x;
   const int h = bh % H;
-  load_modes(s, lam, beta, h, M);
-  load_token(s, q, k, v, (size_t)bh * F, (size_t)bh * D, F, D, in_bf16, opt);
+  seq_load_modes(s, lam, beta, h, M);
+  seq_load_token(s, q, k, v, (size_t)bh * F, (size_t)bh * D, F, D, in_bf16, opt);
   __syncthreads();
-  step_one(s, U + (size_t)bh * M * F, G + (size_t)bh * M * D, E + (size_t)bh * M, F, D, M,
+  seq_step(s, U + (size_t)bh * M * F, G + (size_t)bh * M * D, E + (size_t)bh * M, F, D, M,
            rmat ? rmat + (size_t)h * M * M : nullptr);
-  for (int j = threadIdx.x; j < D; j += kStepThreads) {
-    float n = 0.f;
-#pragma unroll
-    for (int w = 0; w < kStepWaves; ++w) n += s.num[w][j];
-    store_out(o, (size_t)bh * D + j, readout(n, s.den[0], clamp, opt), out_bf16);
-  }
+  for (int j = threadIdx.x; j < D; j += kStepThreads)
+    store_out(o, (size_t)bh * D + j, readout(seq_num(s, j), s.den, clamp, opt), out_bf16);
 }
 
 // Decode with the whole state of a slice in flight at once.  grid = B*H; NT threads per slice.
@@ -321,29 +185,9 @@ scan_prefill_kernel(const void* __restrict__ q, const void* __restrict__ k,
   __shared__ StepSmem s;
   const int bh = blockIdx.x;
   const int b = bh / H, h = bh % H;
-  load_modes(s, lam, beta, h, M);
-  float2* Ub = U + (size_t)bh * M * F;
-  float2* Gb = G + (size_t)bh * M * D;
-  float2* Eb = E + (size_t)bh * M;
-  for (int t = 0; t < N; ++t) {
-    const int pos = reverse ? N - 1 - t : t;
-    const size_t tok = ((size_t)b * N + pos) * H + h;
-    load_token(s, q, k, v, (size_t)(b * sqk.b + pos * sqk.n + h * sqk.h),
-               (size_t)(b * sv.b + pos * sv.n + h * sv.h), F, D, in_bf16, opt);
-    __syncthreads();
-    step_one(s, Ub, Gb, Eb, F, D, M, rmat ? rmat + (size_t)h * M * M : nullptr);
-    if (o) {
-      for (int j = threadIdx.x; j < D; j += kStepThreads) {
-        float n = 0.f;
-#pragma unroll
-        for (int w = 0; w < kStepWaves; ++w) n += s.num[w][j];
-        float val = readout(n, s.den[0], clamp, opt);
-        if (accumulate) val += load_in(o, tok * D + j, out_bf16);
-        store_out(o, tok * D + j, val, out_bf16);
-      }
-    }
-    __syncthreads();
-  }
+  const SeqScanArgs a{q, k, v, sqk, sv, lam, beta, o, accumulate, N, H, F, D, M,
+                      in_bf16, out_bf16, clamp, reverse, opt, rmat};
+  seq_scan(s, a, b, h, U + (size_t)bh * M * F, G + (size_t)bh * M * D, E + (size_t)bh * M);
 }
 
 __global__ void fill_zero_kernel(float4* __restrict__ p, size_t n4) {
@@ -352,7 +196,34 @@ __global__ void fill_zero_kernel(float4* __restrict__ p, size_t n4) {
     p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
+// Copy of up to three buffers (16-byte units), in one launch.
+__global__ void copy3_kernel(float4* __restrict__ d0, const float4* __restrict__ s0, size_t n0,
+                             float4* __restrict__ d1, const float4* __restrict__ s1, size_t n1,
+                             float4* __restrict__ d2, const float4* __restrict__ s2, size_t n2) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n0 + n1 + n2; i += stride) {
+    if (i < n0) d0[i] = s0[i];
+    else if (i < n0 + n1) d1[i - n0] = s1[i - n0];
+    else d2[i - n0 - n1] = s2[i - n0 - n1];
+  }
+}
+
 // ---------------------------------------------------------------- launchers
+
+hipError_t launch_copy3(void* d0, const void* s0, size_t n0, void* d1, const void* s1,
+                        size_t n1, void* d2, const void* s2, size_t n2, hipStream_t st) {
+  const size_t n = (n0 + n1 + n2) / 16;
+  if (n == 0) return hipSuccess;
+  unsigned grid = static_cast<unsigned>(n / 256 + 1 < 4096 ? n / 256 + 1 : 4096);
+  (void)hipGetLastError();
+  prof_begin(st);
+  hipLaunchKernelGGL(copy3_kernel, dim3(grid), dim3(256), 0, st, static_cast<float4*>(d0),
+                     static_cast<const float4*>(s0), n0 / 16, static_cast<float4*>(d1),
+                     static_cast<const float4*>(s1), n1 / 16, static_cast<float4*>(d2),
+                     static_cast<const float4*>(s2), n2 / 16);
+  prof_end(st, kKindCopy);
+  return hipGetLastError();
+}
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
   // bytes is a multiple of 16 for every state buffer (F, Dv, M multiples of 16).

@@ -99,7 +99,8 @@ struct LamSmallPow {
 // rows, j in K-slot order) and in scaled fp16 (row j, modes in K-slot order), both swizzled.
 // Runs 0..3 also write the factors lam^(2i), i < 16, run 4 the factors lam^(32r); run 0 per
 // mode lam^C, sum_{j<C} beta lam^-j, the same two for the last chunk's length Lt, lam^Ls for
-// the segment length Ls, and 1/lam, the four threads of a mode splitting that work.  The
+// the segment length Ls, and 1/lam, the four threads of a mode splitting that work, and the
+// head's route flag (chunk_unresolved for any of its modes).  The
 // fp16 scale comes from max_m |beta| |lam|^-(C-1), reduced over the mode lanes of each wave:
 // every wave of every run of the head reduces the same values, so all agree on it.
 template <int C, int M>
@@ -124,8 +125,13 @@ __device__ __forceinline__ void table_run(const float2* __restrict__ lam,
   const LamPow lp(lam[(size_t)h * M + m], beta[(size_t)h * M + m]);
 
   float mx = hypotf(lp.bt.x, lp.bt.y) * expf(-(float)(C - 1) * lp.lr);
+  const float2 lm = lam[(size_t)h * M + m];
+  int route = chunk_unresolved(lm.x, lm.y, C);
 #pragma unroll
-  for (int o = 1; o < (M < 64 ? M : 64); o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  for (int o = 1; o < (M < 64 ? M : 64); o <<= 1) {
+    mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    route |= __shfl_xor(route, o, 64);
+  }
   const float wscale = pow2_scale(mx);
 
   const float2 w = cmul(lp.bt, lp.pw(-(float)j));   // beta lam^-j
@@ -148,7 +154,10 @@ __device__ __forceinline__ void table_run(const float2* __restrict__ lam,
   } else {
     out[TL::oPowS / 8 + m] = lp.pw((float)Ls);
     out[TL::oInv / 8 + m] = lp.pw(-1.f);
-    if (m == 0) *reinterpret_cast<float*>(tab + TL::oSc) = 1.f / wscale;
+    if (m == 0) {
+      *reinterpret_cast<float*>(tab + TL::oSc) = 1.f / wscale;
+      *reinterpret_cast<int*>(tab + TL::oRoute) = route;
+    }
   }
 }
 

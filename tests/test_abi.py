@@ -144,7 +144,7 @@ def test_bidir_rules():
 
 def test_workspace_checks():
     for in_dtype in (ia.IA_F32, ia.IA_BF16):
-        d = desc(in_dtype=in_dtype)
+        d = desc(in_dtype=in_dtype, Dv=32)
         need = ia.lib.ia_prefill_workspace_bytes(ctypes.byref(d))
         assert need > 0
         assert prefill(d, st=None, ws=P(0)) == 9
@@ -153,21 +153,68 @@ def test_workspace_checks():
         assert prefill(d, st=None, ws=addr(1, 32)) in (5,)
 
 
+@pytest.mark.parametrize("shape", [dict(F=32, Dv=16), dict(F=64, Dv=128), dict(F=256, Dv=256),
+                                   dict(F=128, Dv=128, M=128), dict(F=16, Dv=16)])
+def test_bf16_shapes_without_chunk_kernel_are_refused(shape):
+    """bf16 inputs take the chunked MFMA kernels only (F = Dv in {32, 64, 128}, M <= 64); any
+    other bf16 shape is refused, not run by the token-sequential kernel, and has no workspace
+    size.  The same shapes in fp32 are accepted by validation (they reach the workspace
+    check here)."""
+    d = desc(**shape)
+    assert ia.lib.ia_prefill_workspace_bytes(ctypes.byref(d)) == 0
+    assert prefill(d) == 7
+    assert prefill_strided(d, None) == 7
+    f = desc(in_dtype=ia.IA_F32, **shape)
+    assert ia.lib.ia_prefill_workspace_bytes(ctypes.byref(f)) > 0
+    assert prefill(f, st=None, ws=P(0)) == 9
+
+
+def test_bf16_rows_beyond_32bit_offsets_are_refused():
+    # 64 token rows of H*F bf16 values must span at most 1 GiB for the chunk kernels
+    d = desc(H=65540, F=128, Dv=128, M=16, B=1, N=1)
+    assert prefill(d, st=None) == 7
+
+
+def s4d(dt, M):
+    return np.exp(dt * (-0.5 + 1j * np.pi * np.arange(M))).astype(np.complex64)
+
+
 def test_check_lambda_host():
+    """IA_ERR_DOMAIN outside 0 < |lambda| <= 1 + 1e-6; the count of heads the chunked bf16
+    prefill runs on its fp32 route (the same test the device applies to its tables)."""
     d = desc(H=1, M=16)
-    ok = np.exp(0.05 * (-0.5 + 1j * np.pi * np.arange(16))).astype(np.complex64)[None]
-    ia.ia_check_lambda(d, ok)
-    for bad in (np.zeros(16), 1.1 * np.ones(16), 0.5 * np.ones(16)):
+    assert ia.ia_check_lambda(d, s4d(0.05, 16)[None]) == 0
+    for bad in (np.zeros(16), 1.1 * np.ones(16), np.full(16, np.nan)):
         with pytest.raises(ia.IAError) as e:
             ia.ia_check_lambda(d, bad.astype(np.complex64)[None])
         assert e.value.status == 6
-    # fast modes are fine on the fp32 path, which does not factorise the decay
-    ia.ia_check_lambda(desc(H=1, M=16, in_dtype=ia.IA_F32), (0.5 * np.ones(16, np.complex64))[None])
-    # chunk 32 widens the bf16 domain
+    # a fast mode: |lambda|^63 < 2^-8 at chunk 64, not at chunk 32 (0.9^31 = 0.038)
     mid = (0.9 * np.ones(16, np.complex64))[None]
-    with pytest.raises(ia.IAError):
-        ia.ia_check_lambda(desc(H=1, M=16), mid)
-    ia.ia_check_lambda(desc(H=1, M=16, chunk=32), mid)
+    assert ia.ia_check_lambda(desc(H=1, M=16), mid) == 1
+    assert ia.ia_check_lambda(desc(H=1, M=16, chunk=32), mid) == 0
+    # fp32 inputs never take the chunked path
+    assert ia.ia_check_lambda(desc(H=1, M=16, in_dtype=ia.IA_F32), (0.5 * mid)) == 0
+    # undamped modes: lambda = 1 (and next to it) stays, -1, i and 0.999 e^(0.999 i pi) route
+    near = s4d(0.05, 16)
+    near[:2] = [1.0, np.exp(-1e-6 + 1e-6j)]
+    assert ia.ia_check_lambda(d, near[None]) == 0
+    for edge in (-1.0, 1j, 0.999 * np.exp(1j * np.pi * 0.999)):
+        lam = s4d(0.05, 16)
+        lam[3] = edge
+        assert ia.ia_check_lambda(d, lam[None]) == 1, edge
+    # damped enough: exp(-0.01 - 3.1 i) has |1 - lam|^2 / (1 - |lam|^2) of about 200
+    lam = s4d(0.05, 16)
+    lam[3] = np.exp(-0.01 - 3.1j)
+    assert ia.ia_check_lambda(d, lam[None]) == 0
+    # S4D-Lin modes stay on the chunked path (M = 64) for every dt up to 0.17, past the
+    # workloads' range [1e-3, 1e-1]; beyond, |lambda|^63 < 2^-8 routes them
+    dts = np.exp(np.linspace(np.log(1e-4), np.log(0.17), 41))
+    assert ia.ia_check_lambda(desc(H=41, M=64), np.stack([s4d(t, 64) for t in dts])) == 0
+    assert ia.ia_check_lambda(desc(H=1, M=64), s4d(0.2, 64)[None]) == 1
+    # heads are counted one by one
+    two = np.stack([s4d(0.01, 16), s4d(0.01, 16)])
+    two[1, 5] = -1.0
+    assert ia.ia_check_lambda(desc(H=2, M=16), two) == 1
 
 
 def prefill_strided(d, strides, **kw):

@@ -155,47 +155,107 @@ def test_chunk_forced_clamp():
 def test_chunk_lambda_edges_multi_segment(plan):
     """Modes on and near the unit circle among the S4D modes, several segments per sequence:
     (1, 2, 1536) runs many segments through the carry kernel, (4, 16, 512) four segments
-    through the Horner step.  The segment end states take their powers of lam by binary
-    exponentiation and sum_n beta lam^n in closed form, lam = 1 separately.
+    through the Horner step; outputs and the final state in every case, beta = 1.
 
-    lam = 1 and lam = 1 - 1e-6 (beta = 1): outputs and the final state.  Undamped modes of
-    large argument (lam = -1, i, 0.999 e^(0.999 i pi), e^(-0.01 - 3.1 i)) with random complex
-    beta: the final state only.  With such modes the denominator Re sum_m a_m eta_m is
-    dominated by terms whose phase turns twice as fast as the mode's: it is negative in most
-    rows (the clamp) and a cancelling sum elsewhere, where bf16 operands are not enough (the
-    fp32 path agrees with the oracle to 5e-4 there).  The state has no such division; its
-    features phi(k) = elu(k)+1 have mean about 1, which cancels in an undamped oscillating
-    mode while their bf16 rounding (2^-9 relative) does not, so that case uses q, k of unit
-    scale (the default 1/sqrt(F) would leave the rounding at a few percent of the sum)."""
+    - near one (lam = 1, exp(-1e-6 + 1e-6 i)): the chunked path (its segment end states take
+      the powers of lam by binary exponentiation and sum_n beta lam^n in closed form);
+    - damped large arguments (exp(-0.01 - 3.1 i), exp(-0.003 + 2.5 i), 0.995 e^(0.9 i pi),
+      |1 - lam|^2 / (1 - |lam|^2) from 200 to 900): the chunked path;
+    - undamped large arguments (-1, i, 0.999 e^(0.999 i pi)): every head holds one, so every
+      head runs the fp32 route inside the chunked launches, at the fp32 tolerance (the inputs
+      are bf16-exact, the oracle sees the same values).
+    ia_check_lambda's count of routed heads is checked against each case.  (A head without
+    a slow non-rotating mode, e.g. with these modes in place of mode 0, has Re(den) negative
+    in most rows and cancelling in the rest: ill-conditioned for any precision, and beyond
+    what bf16 operands resolve.)"""
     import torch
     ia = _ia()
+    from helpers import TOL_F32
     B, H, N = plan
     F, M = 64, 32
-    cases = [("near one", np.array([1.0, np.exp(-1e-6 + 1e-6j)], np.complex64), False, None),
-             ("large argument", np.array([-1.0, 1j, 0.999 * np.exp(1j * np.pi * 0.999),
-                                          np.exp(-0.01 - 3.1j)], np.complex64), True, 1.0)]
-    for name, edge, complex_beta, std in cases:
-        inp = W.make_inputs(B, H, N, F, F, M, dtype="bf16", seed=301 + N, std=std)
-        if complex_beta:
-            rng = np.random.default_rng(302)
-            inp["beta"] = (rng.normal(size=(H, M)) +
-                           1j * rng.normal(size=(H, M))).astype(np.complex64)
+    cases = [
+        ("near one", [1.0, np.exp(-1e-6 + 1e-6j)], False),
+        ("damped large argument", [np.exp(-0.01 - 3.1j), np.exp(-0.003 + 2.5j),
+                                   0.995 * np.exp(0.9j * np.pi)], False),
+        ("undamped large argument", [-1.0, 1j, 0.999 * np.exp(1j * np.pi * 0.999)], True)]
+    for name, edge, routed in cases:
+        edge = np.array(edge, np.complex64)
+        inp = W.make_inputs(B, H, N, F, F, M, dtype="bf16", seed=301 + N)
         lam = inp["lam"].copy()
+        # near one: in place of the slowest modes; the others among the fast ones, next to
+        # mode 0 (exp(-dt/2), real), whose large positive eta keeps Re(den) well conditioned
+        at = slice(0, len(edge)) if name == "near one" else slice(M - len(edge), M)
         for h in range(H):
-            lam[h, :len(edge)] = np.roll(edge, h)
+            lam[h, at] = np.roll(edge, h)
         inp["lam"] = lam
+        desc = ia.make_desc(B, H, N, F, F, M)
+        assert ia.ia_check_lambda(desc, lam) == (H if routed else 0)
         st = ia.new_state(B, H, M, F, F)
         tag(f"chunk lambda edges ({name}) B={B} H={H} N={N}")
         o = _run(inp, state=st)
         o_ref, _, _, st_ref = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["lam"],
                                              inp["beta"], threads=8)
+        tol = TOL_F32 if routed else TOL_BF16
         e_s = state_rel(tuple(host(s) for s in st), st_ref)
+        e_o = rowrel(host(o), o_ref)
         report(f"lambda edges ({name}) {plan} state", e_s)
-        assert e_s < TOL_BF16
-        if not complex_beta:
-            e_o = rowrel(host(o), o_ref)
-            report(f"lambda edges ({name}) {plan} output", e_o)
-            assert e_o < TOL_BF16
+        report(f"lambda edges ({name}) {plan} output", e_o)
+        assert e_s < tol and e_o < tol
+
+
+@pytest.mark.parametrize("kind", ["fast", "undamped"])
+@pytest.mark.parametrize("mode", ["state", "several segments", "no state", "state only",
+                                  "bidirectional"])
+def test_fp32_route_heads(kind, mode):
+    """Heads the chunk factorisation does not resolve run the fp32 recurrence inside the
+    chunked launches, next to heads that take the chunked path: "fast" gives head 1 S4D-Lin
+    modes at dt = 0.3 (|lam|^63 < 2^-8), "undamped" gives head 1 a mode at -1.  Head 0 stays
+    chunked.  Each call form: with a caller state (one segment: 16 slices fill the device
+    with G = 1 only when N is short, so the plan varies), with a state and several segments
+    (the initial state read from its workspace copy), without a state (the route's working
+    state in the workspace), state only, and bidirectional (both walks on the route)."""
+    import torch
+    ia = _ia()
+    from helpers import TOL_F32
+    B, H, F, M = 2, 2, 64, 32
+    N = 700 if mode != "state" else 64
+    inp = W.make_inputs(B, H, N, F, F, M, dtype="bf16", seed=611 + N)
+    lam = inp["lam"].copy()
+    if kind == "fast":
+        lam[1] = W.s4d_lin(np.array([0.3]), M)[0]
+    else:
+        lam[1, 7] = -1.0
+    inp["lam"] = lam
+    assert ia.ia_check_lambda(ia.make_desc(B, H, N, F, F, M), lam) == 1
+    tag(f"fp32 route ({kind}, {mode}) B={B} H={H} N={N}")
+    if mode == "bidirectional":
+        o = host(_run(inp, bidir=True))
+        ref = oracle.bidir(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"])
+        e0, e1 = rowrel(o[:, :, 0], ref[:, :, 0]), rowrel(o[:, :, 1], ref[:, :, 1])
+        report(f"fp32 route ({kind}, {mode}) chunked head / routed head", max(e0, e1))
+        assert e0 < TOL_BF16 and e1 < TOL_F32
+        return
+    st = None
+    st_ref0 = None
+    if mode in ("state", "several segments", "state only"):
+        pre = W.make_inputs(B, H, 10, F, F, M, dtype="bf16", seed=612)
+        st_ref0 = oracle.prefill(pre["q"], pre["k"], pre["v"], lam, inp["beta"])[3]
+        st = tuple(dev(x) for x in st_ref0)
+        st_ref0 = tuple(host(x) for x in st)
+    o = _run(inp, state=st, want_output=mode != "state only")
+    o_ref, _, _, st_ref = oracle.prefill(inp["q"], inp["k"], inp["v"], lam, inp["beta"],
+                                         state=st_ref0)
+    if o is not None:
+        o = host(o)
+        e0, e1 = rowrel(o[:, :, 0], o_ref[:, :, 0]), rowrel(o[:, :, 1], o_ref[:, :, 1])
+        report(f"fp32 route ({kind}, {mode}) outputs chunked head / routed head", max(e0, e1))
+        assert e0 < TOL_BF16 and e1 < TOL_F32
+    if st is not None:
+        got = tuple(host(x) for x in st)
+        e0 = state_rel(tuple(x[:, :1] for x in got), tuple(x[:, :1] for x in st_ref))
+        e1 = state_rel(tuple(x[:, 1:] for x in got), tuple(x[:, 1:] for x in st_ref))
+        report(f"fp32 route ({kind}, {mode}) states chunked head / routed head", max(e0, e1))
+        assert e0 < TOL_BF16 and e1 < TOL_F32
 
 
 # ---------------------------------------------------------------- full workload sizes

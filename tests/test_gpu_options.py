@@ -197,16 +197,13 @@ def test_identity_fp32_scan_with_state():
     assert state_rel(tuple(host(s) for s in st), st_ref) < TOL_F32
 
 
-def test_no_den_1p3b_workload_sampled():
+def test_no_den_1p3b_workload_all_slices():
     """The 1.3B-shaped prefill (B=4, H=16, N=2048, F=Dv=128, M=64) in the benchmark's launch
-    configuration, numerator readout, on sampled (b, h) slices."""
+    configuration, numerator readout, on every (b, h) slice."""
     wl = W.l1p3b()
     tag("no-den 1.3b workload")
     o = host(_prefill(wl, no_den=True))
-    slices = [(0, 0), (1, 7), (3, 15)]
-    num = oracle.prefill(wl["q"], wl["k"], wl["v"], wl["lam"], wl["beta"], slices=slices,
-                         threads=3)[1]
-    for b, h in slices:
-        err = rowrel(o[b, :, h], num[b, :, h])
-        report(f"no-den 1.3b slice {(b, h)}", err)
-        assert err < TOL_BF16
+    num = oracle.prefill(wl["q"], wl["k"], wl["v"], wl["lam"], wl["beta"], threads=16)[1]
+    err = rowrel(o, num)
+    report("no-den 1.3b, every slice", err)
+    assert err < TOL_BF16

@@ -202,11 +202,12 @@ def test_decode_1p3b_workload_all_steps(Bd):
 
 
 @pytest.mark.parametrize("shape", [(64, 32, 16), (16, 240, 48), (128, 64, 128), (256, 256, 128)])
-def test_bf16_token_sequential_shapes(shape):
-    """bf16 inputs on shapes the chunked kernels do not take (F != Dv, widths 240/256, M=128;
-    256/256/128 is the largest the library accepts): prefill through the token-sequential
-    kernel, then two decode steps (the mode-looping kernel), outputs and state.  The inputs
-    are bf16-exact, so the oracle sees the same values and fp32 arithmetic sets the bar."""
+def test_shapes_outside_the_chunk_kernels(shape):
+    """Shapes the chunked kernels do not take (F != Dv, widths 240/256, M=128; 256/256/128 is
+    the largest the library accepts): a bf16 prefill is refused (IA_ERR_UNSUPPORTED, no slow
+    fallback); the same bf16-exact values in fp32 run the token-sequential prefill, then two
+    bf16 decode steps (the mode-looping kernel), outputs and state.  The oracle sees the same
+    values, so fp32 arithmetic sets the bar."""
     torch = _torch()
     ia = _lib()
     F, D, M = shape
@@ -215,14 +216,19 @@ def test_bf16_token_sequential_shapes(shape):
     lam, beta = inp["lam"], inp["beta"]
     q, k, v = (inp[n] for n in "qkv")
     bf = torch.bfloat16
-    tag(f"bf16 token-sequential prefill F={F} D={D} M={M}")
+    tag(f"bf16 prefill refused F={F} D={D} M={M}")
     st = ia.new_state(B, H, M, F, D)
-    o = ia.prefill(dev(q[:, :N], bf), dev(k[:, :N], bf), dev(v[:, :N], bf), dev(lam), dev(beta),
+    with pytest.raises(ia.IAError) as e:
+        ia.prefill(dev(q[:, :N], bf), dev(k[:, :N], bf), dev(v[:, :N], bf), dev(lam), dev(beta),
                    state=st, out_dtype=torch.float32)
+    assert e.value.status == 7
+    tag(f"fp32 token-sequential prefill F={F} D={D} M={M}")
+    o = ia.prefill(dev(q[:, :N]), dev(k[:, :N]), dev(v[:, :N]), dev(lam), dev(beta), state=st,
+                   out_dtype=torch.float32)
     o_ref, _, _, st_ref = oracle.prefill(q[:, :N], k[:, :N], v[:, :N], lam, beta)
     torch.cuda.synchronize()
     err = rowrel(host(o), o_ref)
-    report(f"bf16 token-sequential F={F} D={D} M={M} output", err)
+    report(f"token-sequential F={F} D={D} M={M} output", err)
     assert err < TOL_F32
     assert state_rel(tuple(host(s) for s in st), st_ref) < TOL_F32
     st_ref = tuple(host(s) for s in st)   # both sides continue from the complex64 state
