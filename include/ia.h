@@ -199,6 +199,27 @@ ia_status ia_prefill_fwd_strided(const ia_desc* desc,
                                  ia_state* st, void* o,
                                  void* workspace, size_t ws_bytes, void* stream);
 
+/* Bytes of the device array that ia_prefill_fwd_noalloc uses as its workspace. */
+#define IA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* ia_prefill_fwd with no workspace argument that allocates nothing, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  Its workspace is a fixed array of IA_NOALLOC_SCRATCH_BYTES bytes inside
+ * the library, one per device, which each device holds until the process ends (the first call
+ * on a device looks its address up; that lookup failing returns IA_ERR_LAUNCH).
+ *   - A call whose workspace (ia_prefill_workspace_bytes) exceeds the array returns
+ *     IA_ERR_WORKSPACE and enqueues nothing (the 1.3B-shaped layer, B=4 H=16 N=2048 F=Dv=128
+ *     M=64, needs 21 MiB).
+ *   - All calls on one device share the array.  Calls ordered on one stream are safe; calls
+ *     that can overlap in time on one device (other streams, other threads) race on it.
+ *   - The array's contents are scratch: nothing in it needs to start at zero, and it keeps
+ *     whatever the last call left.
+ * Other arguments, results and errors as ia_prefill_fwd. */
+ia_status ia_prefill_fwd_noalloc(const ia_desc* desc,
+                                 const void* q, const void* k, const void* v,
+                                 const void* lambda, const void* beta,
+                                 ia_state* st, void* o, void* stream);
+
 /* Profiling variant of ia_prefill_fwd: identical work and results, and in addition, for its
  * i-th kernel launch (i < max_launches, in launch order), records events[2i] before and
  * events[2i+1] after the kernel on `stream` and stores the kernel's kind in kinds[i]

@@ -8,6 +8,7 @@ the C ABI declared in ``include/ia.h``.  Functions carry the C names:
     ia_check_lambda(desc, lam_host)
     ia_prefill_fwd(desc, q, k, v, lam, beta, state, o, workspace, stream=None)
     ia_prefill_fwd_strided(desc, q, k, v, lam, beta, state, o, workspace, stream=None)
+    ia_prefill_fwd_noalloc(desc, q, k, v, lam, beta, state, o, stream=None)
     ia_decode_step(desc, q_t, k_t, v_t, lam, beta, state, o_t, stream=None)
 
 Tensors are torch tensors on the GPU (PyTorch provides device memory and streams):
@@ -81,6 +82,8 @@ _STRIDES = (ctypes.c_longlong * 3) * 3
 lib.ia_prefill_fwd_strided.argtypes = [_D, _P, _P, _P, ctypes.POINTER(_STRIDES), _P, _P, _S,
                                        _P, _P, ctypes.c_size_t, _P]
 lib.ia_prefill_fwd_strided.restype = ctypes.c_int
+lib.ia_prefill_fwd_noalloc.argtypes = [_D, _P, _P, _P, _P, _P, _S, _P, _P]
+lib.ia_prefill_fwd_noalloc.restype = ctypes.c_int
 lib.ia_decode_step.argtypes = [_D, _P, _P, _P, _P, _P, _S, _P, _P]
 lib.ia_decode_step.restype = ctypes.c_int
 lib.ia_prefill_fwd_profiled.argtypes = [_D, _P, _P, _P, _P, _P, _S, _P, _P, ctypes.c_size_t,
@@ -106,7 +109,7 @@ lib.ia_last_launch_error.argtypes = []
 lib.ia_last_launch_error.restype = ctypes.c_char_p
 
 EXPORTS = ("ia_state_init", "ia_prefill_workspace_bytes", "ia_check_lambda", "ia_prefill_fwd",
-           "ia_prefill_fwd_strided", "ia_prefill_fwd_profiled", "ia_decode_step",
+           "ia_prefill_fwd_strided", "ia_prefill_fwd_noalloc", "ia_prefill_fwd_profiled", "ia_decode_step",
            "ia_prefill_bwd_workspace_bytes", "ia_prefill_bwd", "ia_prefill_readout_workspace_bytes",
            "ia_prefill_fwd_readout", "ia_decode_step_readout", "ia_status_string",
            "ia_last_launch_error")
@@ -220,6 +223,18 @@ def ia_prefill_fwd_strided(desc: IADesc, q, k, v, lam, beta, state, o, workspace
                                       ctypes.byref(st), _ptr(lam), _ptr(beta), _state(state),
                                       _ptr(o), _ptr(workspace), ws_bytes, _stream(stream)),
            "ia_prefill_fwd_strided")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def ia_prefill_fwd_noalloc(desc: IADesc, q, k, v, lam, beta, state, o, stream=None):
+    """ia_prefill_fwd with the library's own fixed workspace (no workspace argument, nothing
+    allocated)."""
+    _dense(q, k, v, lam, beta, o)
+    _check(lib.ia_prefill_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(lam),
+                                      _ptr(beta), _state(state), _ptr(o), _stream(stream)),
+           "ia_prefill_fwd_noalloc")
 
 
 def ia_prefill_fwd_profiled(desc: IADesc, q, k, v, lam, beta, state, o, workspace, events,

@@ -380,6 +380,23 @@ ia_status ia_prefill_fwd(const ia_desc* d, const void* q, const void* k, const v
                       stream);
 }
 
+}  // extern "C"
+
+namespace ia {
+// Status of a HIP error, keeping its text for ia_last_launch_error.
+ia_status status_of(hipError_t e) { return launch_status(e); }
+
+// ia_prefill_fwd on a workspace the caller does not pass (the no-allocation entry point).
+ia_status prefill_on_workspace(const ia_desc* d, const void* q, const void* k, const void* v,
+                               const void* lambda, const void* beta, ia_state* st, void* o,
+                               void* workspace, size_t ws_bytes, void* stream) {
+  return prefill_impl(d, q, k, v, nullptr, lambda, beta, nullptr, st, o, workspace, ws_bytes,
+                      stream);
+}
+}  // namespace ia
+
+extern "C" {
+
 ia_status ia_prefill_fwd_strided(const ia_desc* d, const void* q, const void* k, const void* v,
                                  const long long strides[3][3], const void* lambda,
                                  const void* beta, ia_state* st, void* o, void* workspace,
