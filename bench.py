@@ -131,15 +131,22 @@ def bench_prefill(args, torch, ia, W):
             "traffic": None if bidir else profiled_traffic(args.workload),
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, scaled)",
             "alg_bytes_per_launch": byts / dirs,
-            "kernel": "chunk_prefill_kernel (output pass)"}
-    mfma = {"achieved": flops / (dom * 1e-3) / 1e12, "peak": BF16_PEAK / 1e12,
-            "unit": "TFLOP/s", "frac": flops / (dom * 1e-3) / BF16_PEAK,
-            "whole_step_frac": flops / (ms * 1e-3) / BF16_PEAK}
+            "scope": "dominant kernel only: the output pass's algorithmic bytes over its own "
+                     "mean launch time (HIP events on its stream)",
+            "kernel": "chunk_prefill_kernel (output pass)",
+            "kernel_us": dom * 1e3 / dirs}
+    mfma = {"scope": "dominant kernel only", "achieved": flops / (dom * 1e-3) / 1e12,
+            "peak": BF16_PEAK / 1e12, "unit": "TFLOP/s", "frac": flops / (dom * 1e-3) / BF16_PEAK}
+    whole = {"scope": "whole step (every launch of ia_prefill_fwd), ms_per_step",
+             "hbm_achieved_GBps": byts / (ms * 1e-3) / 1e9,
+             "hbm_frac": byts / (ms * 1e-3) / HBM_PEAK,
+             "mfma_achieved_TFLOPs": flops / (ms * 1e-3) / 1e12,
+             "mfma_frac": flops / (ms * 1e-3) / BF16_PEAK}
     cfg = {"workload": title, "B": B, "H": H, "N": N, "F": F, "Dv": D, "M": M,
            "chunk": 64, "in_dtype": "bf16", "out_dtype": "bf16",
            "bidirectional": bidir}
-    return dict(ms=ms, tokens=B * N, cfg=cfg, roofline=roof, mfma=mfma, kernels_ms=kern_ms,
-                inp=inp)
+    return dict(ms=ms, tokens=B * N, cfg=cfg, roofline=roof, mfma=mfma, whole=whole,
+                kernels_ms=kern_ms, inp=inp)
 
 
 KERNEL_SOURCES = ["ssm_sequence_mixer_amd/csrc/ia_chunk.hpp",
@@ -170,7 +177,35 @@ def profiled_traffic(workload):
     return float(fields["traffic_bytes_per_launch"])
 
 
+MALL_BYTES = 256 * 2 ** 20   # MI355X Infinity Cache
+
+
+def _graph_us(torch, run, reps=1):
+    """Per-call time of run() captured in one hipGraph (run enqueues `reps` steps)."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            run()
+    torch.cuda.current_stream().wait_stream(s)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
 def bench_decode(torch, ia, W, batches=(1, 16, 64), steps=256):
+    """Decode-step latency after a 32-token chunked prefill, 256 steps, eager and graph-
+    captured.  "hot": one state, resident in the MALL between steps at these sizes; "cold":
+    the same steps rotating over enough copies of the state that their total exceeds the
+    MALL, so every step reads its state from HBM.  "prefix_16k": graph latency after a
+    16,384-token prefix instead (the step's work does not depend on the prefix)."""
     res = {}
     for Bd in batches:
         wl = W.decode(Bd, steps=steps, prefix=32)
@@ -184,11 +219,14 @@ def bench_decode(torch, ia, W, batches=(1, 16, 64), steps=256):
         ia.prefill(pre["q"], pre["k"], pre["v"], lam, beta, state=st, want_output=False)
         o = torch.empty((steps, Bd, H, D), dtype=torch.float32, device="cuda")
         desc = ia.make_desc(Bd, H, 1, F, D, M, ia.IA_BF16, ia.IA_F32)
+        qs = [stp["q"][t] for t in range(steps)]
+        ks = [stp["k"][t] for t in range(steps)]
+        vs = [stp["v"][t] for t in range(steps)]
 
-        def run_all():
+        def run_all(states=(st,)):
             for t in range(steps):
-                ia.ia_decode_step(desc, stp["q"][t], stp["k"][t], stp["v"][t], lam, beta, st,
-                                  o[t])
+                ia.ia_decode_step(desc, qs[t], ks[t], vs[t], lam, beta,
+                                  states[t % len(states)], o[t])
 
         run_all()
         torch.cuda.synchronize()
@@ -198,26 +236,34 @@ def bench_decode(torch, ia, W, batches=(1, 16, 64), steps=256):
         e1.record()
         torch.cuda.synchronize()
         eager_us = e0.elapsed_time(e1) / steps * 1e3
-        g = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(g, stream=s):
-                run_all()
-        torch.cuda.current_stream().wait_stream(s)
-        g.replay()
-        torch.cuda.synchronize()
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        graph_us = e0.elapsed_time(e1) / steps * 1e3
+        graph_us = _graph_us(torch, run_all, steps)
+        state_bytes = Bd * H * 8 * M * (F + D + 1)
         step_bytes = Bd * H * (16 * M * (F + D + 1) + (2 * F + D) * 2 + D * 4)
-        res[f"B{Bd}"] = {"graph_us_per_step": graph_us, "eager_us_per_step": eager_us,
-                         "tokens_per_s": Bd / (graph_us * 1e-6),
-                         "hbm_frac": step_bytes / (graph_us * 1e-6) / HBM_PEAK,
-                         "bytes_per_step": step_bytes}
-        del g
+        # cold: copies of the state whose total exceeds the MALL
+        n_sets = max(2, -(-2 * MALL_BYTES // state_bytes))
+        sets = [tuple(x.clone() for x in st) for _ in range(n_sets)]
+        cold_us = _graph_us(torch, lambda: run_all(sets), steps)
+        del sets
+        r = {"graph_us_per_step": graph_us, "eager_us_per_step": eager_us,
+             "tokens_per_s": Bd / (graph_us * 1e-6),
+             "hbm_frac_hot": step_bytes / (graph_us * 1e-6) / HBM_PEAK,
+             "cold_graph_us_per_step": cold_us,
+             "hbm_frac_cold": step_bytes / (cold_us * 1e-6) / HBM_PEAK,
+             "cold_state_sets": n_sets, "bytes_per_step": step_bytes,
+             "state_bytes": state_bytes}
+        if Bd in (1, 16):
+            # prefix flatness: the state after 16,384 tokens (state-only chunked prefill)
+            rng = np.random.default_rng([55, Bd])
+            long = {n: torch.from_numpy(W.round_bf16(
+                rng.standard_normal((Bd, 16384, H, F if n != "v" else D), dtype=np.float32)
+                / np.sqrt(F))).to(torch.bfloat16).cuda() for n in "qkv"}
+            st_long = ia.new_state(Bd, H, M, F, D)
+            ia.prefill(long["q"], long["k"], long["v"], lam, beta, state=st_long,
+                       want_output=False)
+            del long
+            long_us = _graph_us(torch, lambda: run_all((st_long,)), steps)
+            r["prefix_16k_graph_us_per_step"] = long_us
+            r["prefix_16k_over_32"] = long_us / graph_us
         if Bd == 16:
             # the same steps with a readout matrix R per head (the M^2 term of a decode step)
             rng = np.random.default_rng(7)
@@ -225,16 +271,15 @@ def bench_decode(torch, ia, W, batches=(1, 16, 64), steps=256):
             Rd = torch.from_numpy(R).cuda()
             for _ in range(2):
                 for t in range(steps):
-                    ia.ia_decode_step_readout(desc, stp["q"][t], stp["k"][t], stp["v"][t], lam,
-                                              beta, Rd, st, o[t])
+                    ia.ia_decode_step_readout(desc, qs[t], ks[t], vs[t], lam, beta, Rd, st, o[t])
                 torch.cuda.synchronize()
             e0.record()
             for t in range(steps):
-                ia.ia_decode_step_readout(desc, stp["q"][t], stp["k"][t], stp["v"][t], lam, beta,
-                                          Rd, st, o[t])
+                ia.ia_decode_step_readout(desc, qs[t], ks[t], vs[t], lam, beta, Rd, st, o[t])
             e1.record()
             torch.cuda.synchronize()
-            res[f"B{Bd}"]["readout_matrix_eager_us_per_step"] = e0.elapsed_time(e1) / steps * 1e3
+            r["readout_matrix_eager_us_per_step"] = e0.elapsed_time(e1) / steps * 1e3
+        res[f"B{Bd}"] = r
     return res
 
 
@@ -343,6 +388,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="run only the decode measurements (for profiling them); prints their "
+                         "JSON object alone")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain streaming kernel over 256 MiB (read 256 MiB, write "
                          "256 MiB) whose counter readings scale the hardware byte counters")
@@ -360,6 +408,9 @@ def main():
     torch.cuda.init()
     if args.calib_copy:
         calib_copy(torch)
+    if args.decode_only:
+        print(json.dumps({"decode": bench_decode(torch, ia, W)}), flush=True)
+        return
     pf = bench_prefill(args, torch, ia, W)
     dec = None if args.no_decode else bench_decode(torch, ia, W)
     bwd = None
@@ -382,6 +433,7 @@ def main():
         "config": pf["cfg"],
         "roofline": pf["roofline"],
         "mfma": pf["mfma"],
+        "whole_step": pf["whole"],
         "kernels_ms": pf["kernels_ms"],
         "decode": dec,
         "backward": bwd,

@@ -29,6 +29,25 @@ __device__ __forceinline__ float load_in(const void* p, size_t i, int bf16) {
               : static_cast<const float*>(p)[i];
 }
 
+// Input element i with the dtype a compile-time flag (BF: bf16, else f32).  Kernels that
+// take their dtype as a template parameter load without branches, so the compiler can keep
+// later loads in flight behind these instead of waiting for every outstanding load.
+template <bool BF>
+__device__ __forceinline__ float load_t(const void* p, size_t i) {
+  if constexpr (BF) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+  else return static_cast<const float*>(p)[i];
+}
+// Elements i and i+1 (i even) in one load.
+template <bool BF>
+__device__ __forceinline__ float2 load_pair_t(const void* p, size_t i) {
+  if constexpr (BF) {
+    const uint32_t w = static_cast<const uint32_t*>(p)[i / 2];
+    return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+  } else {
+    return static_cast<const float2*>(p)[i / 2];
+  }
+}
+
 __device__ __forceinline__ void store_out(void* p, size_t i, float x, int bf16) {
   if (bf16)
     static_cast<uint16_t*>(p)[i] = f32_to_bf16(x);
@@ -76,6 +95,39 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
+}
+
+// Lane-group totals of N values at once through DPP moves (VALU, no LDS round trip), the N
+// chains interleaved stage by stage so their hazards overlap: swaps within quads (lane ^ 1,
+// lane ^ 2) and mirrors within half-rows and rows leave every lane of a 16-lane row with the
+// row's sum; row_bcast:15 then folds rows 0-1 into 1 and 2-3 into 3 (32-lane totals in lanes
+// 31 and 63), row_bcast:31 rows 0-3 into 3 (the wave total in lane 63).
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF,
+                                                        false));
+}
+// Sums over aligned groups of W lanes (W = 16, 32 or 64) of N values at once; the group's last
+// lane ends with each total (W = 16: every lane of the 16-lane row).
+template <int W, int N>
+__device__ __forceinline__ void row_totals(float (&v)[N]) {
+  static_assert(W == 16 || W == 32 || W == 64, "16, 32 or 64 lanes");
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = dpp_add<0xB1>(v[i]);         // quad_perm [1,0,3,2]
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = dpp_add<0x4E>(v[i]);         // quad_perm [2,3,0,1]
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = dpp_add<0x141>(v[i]);        // row_half_mirror
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = dpp_add<0x140>(v[i]);        // row_mirror
+  if constexpr (W >= 32) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = dpp_add<0x142, 0xA>(v[i]);   // row_bcast:15
+  }
+  if constexpr (W == 64) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = dpp_add<0x143, 0xC>(v[i]);   // row_bcast:31
+  }
 }
 
 }  // namespace ia

@@ -14,23 +14,27 @@ namespace ia {
 
 constexpr int kStepThreads = 256;
 constexpr int kStepWaves = kStepThreads / 64;
-using StepSmem = SeqSmem<kStepWaves, kMaxDim, kMaxDim, kMaxModes, true>;
+// MM: the largest M a kernel instance takes (64 or kMaxModes; the smaller set keeps the per-wave
+// row partials, and so the registers, small for the common sizes).
+template <int MM>
+using StepSmem = SeqSmem<kStepWaves, kMaxDim, kMaxDim, MM, true>;
 
 // ---------------------------------------------------------------- kernels
 
-// Decode: one step for every (b,h).  grid = B*H.
+// Decode: one step for every (b,h).  grid = B*H.  BF: bf16 inputs; M <= MM.
+template <bool BF, int MM>
 __global__ void __launch_bounds__(kStepThreads)
 decode_step_kernel(const void* __restrict__ q, const void* __restrict__ k,
                    const void* __restrict__ v, const float2* __restrict__ lam,
                    const float2* __restrict__ beta, float2* __restrict__ U,
                    float2* __restrict__ G, float2* __restrict__ E, void* __restrict__ o,
-                   int H, int F, int D, int M, int in_bf16, int out_bf16, float clamp,
+                   int H, int F, int D, int M, int out_bf16, float clamp,
                    int opt, const float2* __restrict__ rmat) {
-  __shared__ StepSmem s;
+  __shared__ StepSmem<MM> s;
   const int bh = blockIdx.x;
   const int h = bh % H;
   seq_load_modes(s, lam, beta, h, M);
-  seq_load_token(s, q, k, v, (size_t)bh * F, (size_t)bh * D, F, D, in_bf16, opt);
+  seq_load_token<BF>(s, q, k, v, (size_t)bh * F, (size_t)bh * D, F, D, opt);
   __syncthreads();
   seq_step(s, U + (size_t)bh * M * F, G + (size_t)bh * M * D, E + (size_t)bh * M, F, D, M,
            rmat ? rmat + (size_t)h * M * M : nullptr);
@@ -44,13 +48,13 @@ decode_step_kernel(const void* __restrict__ q, const void* __restrict__ k,
 // Gamma rows, so its inputs are two entries each of phi(q), phi(k) and v.  Every row load is
 // issued before any arithmetic; a[m] needs all of row m (a reduction over the F/2 lanes that
 // share it), then the Gamma rows, whose column sums over rows go through LDS in a fixed order.
-template <int F, int D, int MM>
+template <int F, int D, int MM, bool BF>
 __global__ void __launch_bounds__(512)
 decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
                         const void* __restrict__ v, const float2* __restrict__ lam,
                         const float2* __restrict__ beta, float2* __restrict__ U,
                         float2* __restrict__ G, float2* __restrict__ E, void* __restrict__ o,
-                        int H, int M, int in_bf16, int out_bf16, float clamp, int opt,
+                        int H, int M, int out_bf16, float clamp, int opt,
                         const float2* __restrict__ rmat) {
   constexpr int NT = 512, NWV = NT / 64;
   constexpr int RU = F / 2, RD = D / 2;
@@ -68,6 +72,16 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
   float4* Ub = reinterpret_cast<float4*>(U + (size_t)bh * M * F);
   float4* Gb = reinterpret_cast<float4*>(G + (size_t)bh * M * D);
   float2* Eb = E + (size_t)bh * M;
+  // this token's inputs first: the state loads below stay in flight behind them
+  const float2 kk = load_pair_t<BF>(k, (size_t)bh * F + 2 * pu);
+  const float2 qq = load_pair_t<BF>(q, (size_t)bh * F + 2 * pu);
+  const float2 vv = load_pair_t<BF>(v, (size_t)bh * D + 2 * pd);
+  float2 e = make_float2(0.f, 0.f);
+  if (tid < M) {
+    s_lam[tid] = lam[(size_t)h * M + tid];
+    s_beta[tid] = beta[(size_t)h * M + tid];
+    e = Eb[tid];
+  }
 
   float4 u[IU], g[ID];
 #pragma unroll
@@ -80,18 +94,9 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
     const int m = rd + SD * i;
     if (m < M) g[i] = Gb[(size_t)m * RD + pd];
   }
-  float2 e = make_float2(0.f, 0.f);
-  if (tid < M) {
-    s_lam[tid] = lam[(size_t)h * M + tid];
-    s_beta[tid] = beta[(size_t)h * M + tid];
-    e = Eb[tid];
-  }
-  const float fk0 = feat(load_in(k, (size_t)bh * F + 2 * pu, in_bf16), opt);
-  const float fk1 = feat(load_in(k, (size_t)bh * F + 2 * pu + 1, in_bf16), opt);
-  const float fq0 = feat(load_in(q, (size_t)bh * F + 2 * pu, in_bf16), opt);
-  const float fq1 = feat(load_in(q, (size_t)bh * F + 2 * pu + 1, in_bf16), opt);
-  const float v0 = load_in(v, (size_t)bh * D + 2 * pd, in_bf16);
-  const float v1 = load_in(v, (size_t)bh * D + 2 * pd + 1, in_bf16);
+  const float fk0 = feat(kk.x, opt), fk1 = feat(kk.y, opt);
+  const float fq0 = feat(qq.x, opt), fq1 = feat(qq.y, opt);
+  const float v0 = vv.x, v1 = vv.y;
   __syncthreads();   // lam, beta
 
   if (tid < M) {
@@ -99,21 +104,30 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
     Eb[tid] = e;
   }
   // U rows: update, store, contract with phi(q) over the row's lanes.
+  float ar[IU], ai[IU];
 #pragma unroll
   for (int i = 0; i < IU; ++i) {
     const int m = ru + SU * i;
-    if (m < M) {   // uniform over the row's F/2 lanes, which the shuffles below combine
+    if (m < M) {
       const float2 l = s_lam[m], bt = s_beta[m];
       const float2 u0 = cfma(l, make_float2(u[i].x, u[i].y), make_float2(bt.x * fk0, bt.y * fk0));
       const float2 u1 = cfma(l, make_float2(u[i].z, u[i].w), make_float2(bt.x * fk1, bt.y * fk1));
       Ub[(size_t)m * RU + pu] = make_float4(u0.x, u0.y, u1.x, u1.y);
-      float ar = fq0 * u0.x + fq1 * u1.x, ai = fq0 * u0.y + fq1 * u1.y;
+      ar[i] = fq0 * u0.x + fq1 * u1.x;
+      ai[i] = fq0 * u0.y + fq1 * u1.y;
+    } else {
+      ar[i] = ai[i] = 0.f;
+    }
+  }
+  // each row's RU lane partials summed by DPP moves, all rows' chains interleaved; the row's
+  // last lane holds its total
+  row_totals<RU>(ar);
+  row_totals<RU>(ai);
+  if (pu == RU - 1) {
 #pragma unroll
-      for (int off = RU / 2; off > 0; off >>= 1) {
-        ar += __shfl_xor(ar, off, 64);
-        ai += __shfl_xor(ai, off, 64);
-      }
-      if (pu == 0) s_a[m] = make_float2(ar, ai);
+    for (int i = 0; i < IU; ++i) {
+      const int m = ru + SU * i;
+      if (m < M) s_a[m] = make_float2(ar[i], ai[i]);
     }
   }
   __syncthreads();   // a[m]
@@ -169,11 +183,12 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
   }
 }
 
-// Token-sequential prefill (the fp32 path).  grid = B*H; one workgroup walks all N tokens of
+// Token-sequential prefill (the fp32 path).  M <= MM.  grid = B*H; one workgroup walks all N tokens of
 // its slice, in reverse when `reverse` is set (then token t of the walk is position N-1-t).
 // q, k and v are addressed through their element strides sqk, sv; o is dense.
 // o (out dtype) receives value, or o + value with `accumulate` (the second direction of the
 // bidirectional layer adds onto the first); o may be NULL (state only).
+template <int MM>
 __global__ void __launch_bounds__(kStepThreads)
 scan_prefill_kernel(const void* __restrict__ q, const void* __restrict__ k,
                     const void* __restrict__ v, const float2* __restrict__ lam,
@@ -182,7 +197,7 @@ scan_prefill_kernel(const void* __restrict__ q, const void* __restrict__ k,
                     int accumulate, int N, int H, int F, int D, int M,
                     int in_bf16, int out_bf16, float clamp, int reverse, RowStrides sqk,
                     RowStrides sv, int opt, const float2* __restrict__ rmat) {
-  __shared__ StepSmem s;
+  __shared__ StepSmem<MM> s;
   const int bh = blockIdx.x;
   const int b = bh / H, h = bh % H;
   const SeqScanArgs a{q, k, v, sqk, sv, lam, beta, o, accumulate, N, H, F, D, M,
@@ -238,18 +253,26 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int F, int D>
-static void launch_decode_rows(const DecodeArgs& a, hipStream_t st) {
+template <int F, int D, bool BF>
+static void launch_decode_rows_t(const DecodeArgs& a, hipStream_t st) {
   // The per-thread row registers are sized for M <= 64 or M <= 128: the smaller set lets two
   // workgroups share a CU.
   if (a.M <= 64)
-    hipLaunchKernelGGL((decode_step_rows_kernel<F, D, 64>), dim3(a.B * a.H), dim3(512), 0, st,
-                       a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H, a.M, a.in_bf16,
+    hipLaunchKernelGGL((decode_step_rows_kernel<F, D, 64, BF>), dim3(a.B * a.H), dim3(512), 0,
+                       st, a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H, a.M,
                        a.out_bf16, a.clamp, a.opt, a.readout);
   else
-    hipLaunchKernelGGL((decode_step_rows_kernel<F, D, kMaxModes>), dim3(a.B * a.H), dim3(512),
-                       0, st, a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H, a.M,
-                       a.in_bf16, a.out_bf16, a.clamp, a.opt, a.readout);
+    hipLaunchKernelGGL((decode_step_rows_kernel<F, D, kMaxModes, BF>), dim3(a.B * a.H),
+                       dim3(512), 0, st, a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H,
+                       a.M, a.out_bf16, a.clamp, a.opt, a.readout);
+}
+
+template <int F, int D>
+static void launch_decode_rows(const DecodeArgs& a, hipStream_t st) {
+  if (a.in_bf16)
+    launch_decode_rows_t<F, D, true>(a, st);
+  else
+    launch_decode_rows_t<F, D, false>(a, st);
 }
 
 // Compute units of the current device (cached per device; 256 when there is none).
@@ -271,19 +294,27 @@ hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t st) {
   (void)hipGetLastError();
   prof_begin(st);
   // Row-parallel kernel (row widths up to 64 float4: F, Dv in {32, 64, 128}) while there are
-  // fewer than four slices per CU; with more, the small mode-looping kernel keeps every slice
-  // resident at once and streams better (measured on MI355X at H=16, F=Dv=128, M=64: rows
-  // 11.1 us vs 20.9 us at B=16, 46.0 us vs 42.8 us at B=64).
-  const bool rows = (long)a.B * a.H < 4L * device_cus();
+  // fewer than eight slices per CU; with more, the small mode-looping kernel keeps every slice
+  // resident at once.  (Measured on MI355X at H=16, F=Dv=128, M=64, graph-captured: rows
+  // 39.5 us against 41.7 us at B=64; the row kernel's loads and reductions were since made
+  // latency-lean, which moved the crossover up from four slices per CU.)
+  const bool rows = (long)a.B * a.H < 8L * device_cus();
 #define IA_DEC(FF, DD) \
   if (rows && a.F == FF && a.D == DD) { launch_decode_rows<FF, DD>(a, st); } else
   IA_DEC(32, 32) IA_DEC(32, 64) IA_DEC(32, 128)
   IA_DEC(64, 32) IA_DEC(64, 64) IA_DEC(64, 128)
   IA_DEC(128, 32) IA_DEC(128, 64) IA_DEC(128, 128)
 #undef IA_DEC
-  hipLaunchKernelGGL(decode_step_kernel, dim3(a.B * a.H), dim3(kStepThreads), 0, st, a.q, a.k,
-                     a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H, a.F, a.D, a.M, a.in_bf16,
-                     a.out_bf16, a.clamp, a.opt, a.readout);
+#define IA_DSK(BF, MM)                                                                      \
+  hipLaunchKernelGGL((decode_step_kernel<BF, MM>), dim3(a.B * a.H), dim3(kStepThreads), 0, st, \
+                     a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H, a.F, a.D, a.M,      \
+                     a.out_bf16, a.clamp, a.opt, a.readout)
+  if (a.in_bf16) {
+    if (a.M <= 64) IA_DSK(true, 64); else IA_DSK(true, kMaxModes);
+  } else {
+    if (a.M <= 64) IA_DSK(false, 64); else IA_DSK(false, kMaxModes);
+  }
+#undef IA_DSK
   prof_end(st, kKindDecode);
   return hipGetLastError();
 }
@@ -291,10 +322,16 @@ hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t st) {
 hipError_t launch_scan_prefill(const ScanArgs& a, hipStream_t st) {
   (void)hipGetLastError();
   prof_begin(st);
-  hipLaunchKernelGGL(scan_prefill_kernel, dim3(a.B * a.H), dim3(kStepThreads), 0, st, a.q,
-                     a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.accumulate, a.N, a.H, a.F, a.D,
-                     a.M, a.in_bf16, a.out_bf16, a.clamp, a.reverse, a.sqk, a.sv, a.opt,
-                     a.readout);
+#define IA_SCAN(MM)                                                                          \
+  hipLaunchKernelGGL((scan_prefill_kernel<MM>), dim3(a.B * a.H), dim3(kStepThreads), 0, st,    \
+                     a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.accumulate, a.N, a.H, \
+                     a.F, a.D, a.M, a.in_bf16, a.out_bf16, a.clamp, a.reverse, a.sqk, a.sv,   \
+                     a.opt, a.readout)
+  if (a.M <= 64)
+    IA_SCAN(64);
+  else
+    IA_SCAN(kMaxModes);
+#undef IA_SCAN
   prof_end(st, kKindScan);
   return hipGetLastError();
 }

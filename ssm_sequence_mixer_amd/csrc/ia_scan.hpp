@@ -53,24 +53,38 @@ __device__ __forceinline__ void seq_step(SeqSmem<NW, MF, MD, MM, WR>& s, float2*
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
 
-  // U rows: update in place and contract with phi(q_t).
-  for (int m = wave; m < M; m += NW) {
-    const float2 l = s.lam[m], b = s.beta[m];
-    float4* row = reinterpret_cast<float4*>(U + (size_t)m * F);
-    float ar = 0.f, ai = 0.f;
-    for (int p = lane; p < F / 2; p += 64) {
-      float4 u = row[p];
-      const float k0 = s.fk[2 * p], k1 = s.fk[2 * p + 1];
-      float2 u0 = cfma(l, make_float2(u.x, u.y), make_float2(b.x * k0, b.y * k0));
-      float2 u1 = cfma(l, make_float2(u.z, u.w), make_float2(b.x * k1, b.y * k1));
-      row[p] = make_float4(u0.x, u0.y, u1.x, u1.y);
-      const float q0 = s.fq[2 * p], q1 = s.fq[2 * p + 1];
-      ar += q0 * u0.x + q1 * u1.x;
-      ai += q0 * u0.y + q1 * u1.y;
+  // U rows: update in place and contract with phi(q_t).  Each wave takes rows wave, wave+NW,
+  // ...: every row's lane partials first, then their wave totals together (DPP, the rows'
+  // chains interleaved), lane 63 holding them.
+  constexpr int RW = (MM + NW - 1) / NW;   // rows per wave at most
+  float ar[RW], ai[RW];
+#pragma unroll
+  for (int i = 0; i < RW; ++i) {
+    const int m = wave + NW * i;
+    ar[i] = ai[i] = 0.f;
+    if (m < M) {
+      const float2 l = s.lam[m], b = s.beta[m];
+      float4* row = reinterpret_cast<float4*>(U + (size_t)m * F);
+      for (int p = lane; p < F / 2; p += 64) {
+        float4 u = row[p];
+        const float k0 = s.fk[2 * p], k1 = s.fk[2 * p + 1];
+        float2 u0 = cfma(l, make_float2(u.x, u.y), make_float2(b.x * k0, b.y * k0));
+        float2 u1 = cfma(l, make_float2(u.z, u.w), make_float2(b.x * k1, b.y * k1));
+        row[p] = make_float4(u0.x, u0.y, u1.x, u1.y);
+        const float q0 = s.fq[2 * p], q1 = s.fq[2 * p + 1];
+        ar[i] += q0 * u0.x + q1 * u1.x;
+        ai[i] += q0 * u0.y + q1 * u1.y;
+      }
     }
-    ar = wave_sum(ar);
-    ai = wave_sum(ai);
-    if (lane == 0) s.a[m] = make_float2(ar, ai);
+  }
+  row_totals<64>(ar);
+  row_totals<64>(ai);
+  if (lane == 63) {
+#pragma unroll
+    for (int i = 0; i < RW; ++i) {
+      const int m = wave + NW * i;
+      if (m < M) s.a[m] = make_float2(ar[i], ai[i]);
+    }
   }
   // eta: one mode per thread.
   for (int m = threadIdx.x; m < M; m += NT) {
@@ -138,16 +152,25 @@ __device__ __forceinline__ void seq_step(SeqSmem<NW, MF, MD, MM, WR>& s, float2*
   __syncthreads();
 }
 
-// phi(q), phi(k), v of one token into shared memory.
-template <int NW, int MF, int MD, int MM, bool WR>
+// phi(q), phi(k), v of one token into shared memory (BF: bf16 inputs, else f32).  Each thread
+// issues its loads before converting any of them.
+template <bool BF, int NW, int MF, int MD, int MM, bool WR>
 __device__ __forceinline__ void seq_load_token(SeqSmem<NW, MF, MD, MM, WR>& s, const void* q,
                                                const void* k, const void* v, size_t qk_off,
-                                               size_t v_off, int F, int D, int bf16, int opt) {
-  for (int i = threadIdx.x; i < F; i += 64 * NW) {
-    s.fq[i] = feat(load_in(q, qk_off + i, bf16), opt);
-    s.fk[i] = feat(load_in(k, qk_off + i, bf16), opt);
+                                               size_t v_off, int F, int D, int opt) {
+  for (int i = threadIdx.x; i < F || i < D; i += 64 * NW) {
+    float xq = 0.f, xk = 0.f, xv = 0.f;
+    if (i < F) {
+      xq = load_t<BF>(q, qk_off + i);
+      xk = load_t<BF>(k, qk_off + i);
+    }
+    if (i < D) xv = load_t<BF>(v, v_off + i);
+    if (i < F) {
+      s.fq[i] = feat(xq, opt);
+      s.fk[i] = feat(xk, opt);
+    }
+    if (i < D) s.v[i] = xv;
   }
-  for (int i = threadIdx.x; i < D; i += 64 * NW) s.v[i] = load_in(v, v_off + i, bf16);
 }
 
 template <int NW, int MF, int MD, int MM, bool WR>
@@ -187,16 +210,16 @@ struct SeqScanArgs {
   const float2* readout;   // [H][M][M] or NULL
 };
 
-template <int NW, int MF, int MD, int MM, bool WR>
-__device__ __forceinline__ void seq_scan(SeqSmem<NW, MF, MD, MM, WR>& s, const SeqScanArgs& a,
-                                         int b, int h, float2* U, float2* G, float2* E) {
+template <bool BF, int NW, int MF, int MD, int MM, bool WR>
+__device__ __forceinline__ void seq_scan_t(SeqSmem<NW, MF, MD, MM, WR>& s, const SeqScanArgs& a,
+                                           int b, int h, float2* U, float2* G, float2* E) {
   seq_load_modes(s, a.lam, a.beta, h, a.M);
   const float2* R = a.readout ? a.readout + (size_t)h * a.M * a.M : nullptr;
   for (int t = 0; t < a.N; ++t) {
     const int pos = a.reverse ? a.N - 1 - t : t;
     const size_t tok = ((size_t)b * a.N + pos) * a.H + h;
-    seq_load_token(s, a.q, a.k, a.v, (size_t)(b * a.sqk.b + pos * a.sqk.n + h * a.sqk.h),
-                   (size_t)(b * a.sv.b + pos * a.sv.n + h * a.sv.h), a.F, a.D, a.in_bf16, a.opt);
+    seq_load_token<BF>(s, a.q, a.k, a.v, (size_t)(b * a.sqk.b + pos * a.sqk.n + h * a.sqk.h),
+                       (size_t)(b * a.sv.b + pos * a.sv.n + h * a.sv.h), a.F, a.D, a.opt);
     __syncthreads();
     seq_step(s, U, G, E, a.F, a.D, a.M, R);
     if (a.o) {
@@ -208,6 +231,15 @@ __device__ __forceinline__ void seq_scan(SeqSmem<NW, MF, MD, MM, WR>& s, const S
     }
     __syncthreads();
   }
+}
+
+template <int NW, int MF, int MD, int MM, bool WR>
+__device__ __forceinline__ void seq_scan(SeqSmem<NW, MF, MD, MM, WR>& s, const SeqScanArgs& a,
+                                         int b, int h, float2* U, float2* G, float2* E) {
+  if (a.in_bf16)
+    seq_scan_t<true>(s, a, b, h, U, G, E);
+  else
+    seq_scan_t<false>(s, a, b, h, U, G, E);
 }
 
 }  // namespace ia

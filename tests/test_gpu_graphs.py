@@ -40,10 +40,10 @@ def _replays(torch, fn, reset, outputs, eager):
     del g
 
 
-@pytest.mark.parametrize("B", [2, 256])
+@pytest.mark.parametrize("B", [2, 512])
 def test_graph_decode_steps(B):
-    """Row-parallel kernel (B=2, H=4: 8 slices) and mode-looping kernel (B=256: 1024 slices,
-    four per compute unit); 6 steps per graph."""
+    """Row-parallel kernel (B=2, H=4: 8 slices) and mode-looping kernel (B=512: 2048 slices,
+    eight per compute unit); 6 steps per graph."""
     import torch
     ia = _ia()
     H, F, D, M, steps = 4, 128, 128, 64, 6

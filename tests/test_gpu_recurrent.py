@@ -80,6 +80,60 @@ def test_decode_row_kernel_shapes(shape, in_dtype):
         assert state_rel(tuple(host(s) for s in st), st_ref) < TOL_F32
 
 
+@pytest.mark.parametrize("BH", [(1, 16), (3, 8), (4, 16), (8, 16), (1, 5)])
+@pytest.mark.parametrize("M", [16, 32, 64])
+@pytest.mark.parametrize("FD", [(128, 128), (64, 32), (32, 64)])
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+def test_decode_rows_few_slices(BH, M, FD, in_dtype):
+    """The row-parallel kernel at few slices (5 to 128) and the row widths whose lane sums take
+    one, two or four 16-lane rows (F/2 = 64, 32, 16 lanes per state row): outputs and every
+    state tensor against the oracle over three steps from a non-zero state."""
+    torch = _torch()
+    ia = _lib()
+    B, H = BH
+    F, D = FD
+    steps = 3
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    inp = W.make_inputs(B, H, steps, F, D, M, dtype=in_dtype, seed=900 + B * H + M + F)
+    lam, beta = inp["lam"], inp["beta"] * np.complex64(0.9 + 0.3j)
+    st_ref = _oracle_state(B, H, F, D, M, lam, beta, seed=901 + M)
+    st = tuple(dev(s) for s in st_ref)
+    st_ref = tuple(host(s) for s in st)
+    for t in range(steps):
+        tag(f"decode rows B={B} H={H} F={F} D={D} M={M} {in_dtype} step {t}")
+        o = ia.decode(dev(inp["q"][:, t], tdt[in_dtype]), dev(inp["k"][:, t], tdt[in_dtype]),
+                      dev(inp["v"][:, t], tdt[in_dtype]), dev(lam), dev(beta), st)
+        o_ref, st_ref = oracle.decode_step(inp["q"][:, t], inp["k"][:, t], inp["v"][:, t], lam,
+                                           beta, st_ref)
+        torch.cuda.synchronize()
+        assert rowrel(host(o), o_ref) < TOL_F32
+        assert state_rel(tuple(host(s) for s in st), st_ref) < TOL_F32
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+def test_decode_mode_looping_kernel_many_slices(in_dtype):
+    """2048 slices (B=128, H=16) at F = Dv = 128, M = 16: eight slices per compute unit take
+    the mode-looping kernel.  Outputs and state over two steps from a non-zero state."""
+    torch = _torch()
+    ia = _lib()
+    B, H, F, D, M, steps = 128, 16, 128, 128, 16, 2
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16}
+    inp = W.make_inputs(B, H, steps, F, D, M, dtype=in_dtype, seed=950)
+    lam, beta = inp["lam"], inp["beta"]
+    st_ref = _oracle_state(B, H, F, D, M, lam, beta, seed=951)
+    st = tuple(dev(s) for s in st_ref)
+    st_ref = tuple(host(s) for s in st)
+    for t in range(steps):
+        tag(f"decode mode-looping B={B} H={H} {in_dtype} step {t}")
+        o = ia.decode(dev(inp["q"][:, t], tdt[in_dtype]), dev(inp["k"][:, t], tdt[in_dtype]),
+                      dev(inp["v"][:, t], tdt[in_dtype]), dev(lam), dev(beta), st)
+        o_ref, st_ref = oracle.decode_step(inp["q"][:, t], inp["k"][:, t], inp["v"][:, t], lam,
+                                           beta, st_ref)
+        torch.cuda.synchronize()
+        assert rowrel(host(o), o_ref) < TOL_F32
+        assert state_rel(tuple(host(s) for s in st), st_ref) < TOL_F32
+
+
 def test_fp32_prefill_tiny_workload():
     """The tiny fp32 workload: B=H=1, N=256, F=Dv=M=16, dt=0.01, beta=1; outputs and state."""
     torch = _torch()
@@ -163,7 +217,7 @@ def test_decode_forced_clamp():
 def test_decode_1p3b_workload_all_steps(Bd):
     """The decode workload in full: at the 1.3B-shaped layer (H=16, F=Dv=128, M=64), a
     32-token chunked prefill of a random prefix, then all 256 decode steps, at the benchmark's
-    batch sizes (16 and 256 slices take the row-parallel kernel, 1024 the mode-looping one).
+    batch sizes (16, 256 and 1024 slices, all on the row-parallel kernel).
     Every step's output of every (b, h) slice, and the state after the prefix and after the
     last step, against the oracle's recurrence over all 288 tokens (the scan the decode steps
     continue)."""
