@@ -11,6 +11,9 @@ Two independent implementations live here:
   loop over slices and marshal arrays.
 * ``brute.py``: the explicit double sum over s <= t and modes m, in numpy, for tiny inputs.
 
+``scan_gated``/``prefill_gated`` run the layer with selective writing and memory decay (a
+write gate and a decay gate per token), pinned in ``tests/test_oracle.py``.
+
 ``scan_bwd``/``prefill_bwd`` give the gradients of the same layer (``ia_oracle_scan_bwd``:
 reverse-mode differentiation of the recurrence, every forward state kept), pinned to the
 forward oracle by finite differences in ``tests/test_oracle_bwd.py``.
@@ -52,6 +55,9 @@ def load_library(path):
     lib.ia_oracle_scan_readout.restype = ctypes.c_int
     lib.ia_oracle_scan_readout.argtypes = [ctypes.c_int] * 4 + [dp] * 6 + [dp] * 3 + [dp] * 3 + [
         ctypes.c_double, dp]
+    lib.ia_oracle_scan_gated.restype = ctypes.c_int
+    lib.ia_oracle_scan_gated.argtypes = [ctypes.c_int] * 4 + [dp] * 7 + [dp] * 3 + [dp] * 3 + [
+        ctypes.c_double]
     lib.ia_oracle_scan_bwd.restype = ctypes.c_int
     lib.ia_oracle_scan_bwd.argtypes = [ctypes.c_int] * 4 + [dp] * 5 + [dp] * 3 + [
         dp, ctypes.c_double, ctypes.c_int] + [dp] * 5 + [dp] * 3 + [dp]
@@ -294,6 +300,65 @@ def prefill_readout(q, k, v, lam, beta, readout, state=None, clamp=1e-6, slices=
         st = None if state is None else (state[0][b, h], state[1][b, h], state[2][b, h])
         return bh, scan_readout(q[b, :, h], k[b, :, h], v[b, :, h], lam[h], beta[h],
                                 readout[h], st, clamp)
+
+    if threads > 1:
+        with ThreadPoolExecutor(threads) as ex:
+            results = list(ex.map(one, todo))
+    else:
+        results = [one(bh) for bh in todo]
+    for (b, h), (ob, nb, db, (Ub, Gb, eb)) in results:
+        o[b, :, h], num[b, :, h], den[b, :, h] = ob, nb, db
+        U[b, h], G[b, h], e[b, h] = Ub, Gb, eb
+    return o, num, den, (U, G, e)
+
+
+def scan_gated(q, k, v, lam, beta, wgate, dgate, state=None, clamp=1e-6, lib=None):
+    """``scan`` with selective writing and memory decay (``ia_oracle_scan_gated``): per token
+    t a write gate wgate[t] on what the token writes and a decay gate dgate[t] on every
+    mode's lambda.  Returns (o, num, den, (U, G, e))."""
+    lib = lib or _load()
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    wg = np.ascontiguousarray(wgate, dtype=np.float64)
+    dg = np.ascontiguousarray(dgate, dtype=np.float64)
+    N, F = q.shape
+    D = v.shape[1]
+    M = np.asarray(lam).shape[0]
+    assert wg.shape == (N,) and dg.shape == (N,)
+    if state is None:
+        U, G, e = np.zeros((M, F, 2)), np.zeros((M, D, 2)), np.zeros((M, 2))
+    else:
+        U, G, e = (_c2r(x) for x in state)
+    o, num, den = np.empty((N, D)), np.empty((N, D)), np.empty(N)
+    lib.ia_oracle_scan_gated(N, F, D, M, _ptr(q), _ptr(k), _ptr(v), _ptr(_c2r(lam)),
+                             _ptr(_c2r(beta)), _ptr(wg), _ptr(dg), _ptr(U), _ptr(G), _ptr(e),
+                             _ptr(o), _ptr(num), _ptr(den), float(clamp))
+    return o, num, den, (_r2c(U), _r2c(G), _r2c(e))
+
+
+def prefill_gated(q, k, v, lam, beta, wgate, dgate, state=None, clamp=1e-6, slices=None,
+                  threads=1):
+    """``prefill`` with the gates of ``scan_gated``: wgate, dgate [B, N, H]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, N, H, F = q.shape
+    D = v.shape[3]
+    M = lam.shape[1]
+    o = np.full((B, N, H, D), np.nan)
+    num = np.full((B, N, H, D), np.nan)
+    den = np.full((B, N, H), np.nan)
+    U = np.full((B, H, M, F), np.nan, dtype=np.complex128)
+    G = np.full((B, H, M, D), np.nan, dtype=np.complex128)
+    e = np.full((B, H, M), np.nan, dtype=np.complex128)
+    todo = slices if slices is not None else [(b, h) for b in range(B) for h in range(H)]
+
+    def one(bh):
+        b, h = bh
+        st = None if state is None else (state[0][b, h], state[1][b, h], state[2][b, h])
+        return bh, scan_gated(q[b, :, h], k[b, :, h], v[b, :, h], lam[h], beta[h],
+                              wgate[b, :, h], dgate[b, :, h], st, clamp)
 
     if threads > 1:
         with ThreadPoolExecutor(threads) as ex:

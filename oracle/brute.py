@@ -28,9 +28,12 @@ def powers(lam, n):
     return np.exp(np.asarray(n, dtype=np.float64)[:, None] * np.log(lam)[None, :])
 
 
-def layer(q, k, v, lam, beta, clamp=1e-6, readout=None):
+def layer(q, k, v, lam, beta, clamp=1e-6, readout=None, gates=None):
     """One (b,h) slice from zero state: q, k [N,F]; v [N,D]; lam, beta [M]; ``readout`` an
-    optional complex [M, M] mode-mixing matrix R (a -> a R before the readout; None = identity).
+    optional complex [M, M] mode-mixing matrix R (a -> a R before the readout; None = identity);
+    ``gates`` an optional pair (w, a) of per-token write and decay gates [N] (a > 0): token s
+    then enters with weight w_s and is carried to t by prod_{s<u<=t} a_u lambda^(t-s), the
+    product taken as exp(sum of log a_u).
 
     Returns (o [N,D], num [N,D], den [N]).
     """
@@ -39,11 +42,17 @@ def layer(q, k, v, lam, beta, clamp=1e-6, readout=None):
     beta = np.asarray(beta, dtype=np.complex128)
     N = fq.shape[0]
     S = fq @ fk.T                                   # <phi(q_t), phi(k_s)>
+    if gates is not None:
+        w = np.asarray(gates[0], dtype=np.float64)
+        cl = np.cumsum(np.log(np.asarray(gates[1], dtype=np.float64)))   # sum_{u<=t} log a_u
     o = np.empty((N, v.shape[1]))
     num = np.empty_like(o)
     den = np.empty(N)
     for t in range(N):
         dec = powers(lam, t - np.arange(t + 1)) * beta[None, :]     # [s, m] = beta lam^(t-s)
+        if gates is not None:
+            s = np.arange(t + 1)
+            dec = dec * (w[s] * np.exp(cl[t] - cl[s]))[:, None]
         A = (S[t, : t + 1, None] * dec).sum(axis=0)                 # [m]
         Gam = (dec[:, :, None] * v[: t + 1, None, :]).sum(axis=0)   # [m, D]
         eta = dec.sum(axis=0)                                       # [m]

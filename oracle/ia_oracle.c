@@ -338,3 +338,66 @@ int ia_oracle_scan_readout(int N, int F, int D, int M,
   }
   return 0;
 }
+
+/*
+ * The layer with selective writing and memory decay: the optional enhancement in which
+ * input-dependent gates control what the memory stores and how fast it forgets (summary page
+ * §3.3; ablated as selective vs non-selective in §B.3, Table 7).  The pages give no formula;
+ * the reading taken here, per token t of the slice, with two real gates the caller computes
+ * from the input:
+ *   write gate  w_t  scales what token t writes into every memory (U, Gam and eta alike);
+ *   decay gate  a_t  scales every mode's lambda at step t (0 < a_t <= 1 forgets faster).
+ * For every mode m
+ *     U[m,:]   <- a_t lambda_m U[m,:]   + w_t beta_m phi(k_t)
+ *     Gam[m,:] <- a_t lambda_m Gam[m,:] + w_t beta_m v_t
+ *     eta[m]   <- a_t lambda_m eta[m]   + w_t beta_m
+ * and the readout of ia_oracle_scan, unchanged.  w = a = 1 is the plain layer.
+ *   wgate, dgate  [N]  write and decay gates of the slice's tokens
+ * Other arguments as ia_oracle_scan.  Returns 0.
+ */
+int ia_oracle_scan_gated(int N, int F, int D, int M,
+                         const double* q, const double* k, const double* v,
+                         const double* lam, const double* beta,
+                         const double* wgate, const double* dgate,
+                         double* U, double* G, double* e,
+                         double* o, double* num, double* den, double clamp) {
+  for (int t = 0; t < N; ++t) {
+    const double w = wgate[t], at = dgate[t];
+    double complex nsum[D];
+    for (int j = 0; j < D; ++j) nsum[j] = 0.0;
+    double complex dsum = 0.0;
+    for (int m = 0; m < M; ++m) {
+      const double complex l = at * (lam[2 * m] + I * lam[2 * m + 1]);
+      const double complex wb = w * (beta[2 * m] + I * beta[2 * m + 1]);
+      double complex a = 0.0;
+      for (int r = 0; r < F; ++r) {
+        double* u = U + ((size_t)m * F + r) * 2;
+        const double complex uc = l * (u[0] + I * u[1]) + wb * feature(k[(size_t)t * F + r]);
+        u[0] = creal(uc);
+        u[1] = cimag(uc);
+        a += feature(q[(size_t)t * F + r]) * uc;
+      }
+      for (int j = 0; j < D; ++j) {
+        double* g = G + ((size_t)m * D + j) * 2;
+        const double complex gc = l * (g[0] + I * g[1]) + wb * v[(size_t)t * D + j];
+        g[0] = creal(gc);
+        g[1] = cimag(gc);
+        nsum[j] += a * gc;
+      }
+      const double complex ec = l * (e[2 * m] + I * e[2 * m + 1]) + wb;
+      e[2 * m] = creal(ec);
+      e[2 * m + 1] = cimag(ec);
+      dsum += a * ec;
+    }
+    const double dr = creal(dsum);
+    double c = dr < clamp ? clamp : dr;
+    if (isnan(dr)) c = dr;
+    if (den) den[t] = dr;
+    for (int j = 0; j < D; ++j) {
+      const double n = creal(nsum[j]);
+      if (num) num[(size_t)t * D + j] = n;
+      if (o) o[(size_t)t * D + j] = n / c;
+    }
+  }
+  return 0;
+}

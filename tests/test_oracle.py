@@ -319,3 +319,107 @@ def test_planted_readout_mistake_fails_brute_force(mutant, tmp_path):
     o, num, den, _ = oracle.scan_readout(q, k, v, lam, beta, R, lib=lib)
     ob, nb, db = brute.layer(q, k, v, lam, beta, readout=R)
     assert not (_rel(num, nb) < 1e-10 and _rel(den, db) < 1e-10), f"{mutant} passed"
+
+
+# ---------------------------------------------------------------- selective writing, memory decay
+# ia_oracle_scan_gated: a write gate w_t on what token t writes (U, Gamma, eta) and a decay gate
+# a_t scaling every mode's lambda at step t.  Pinned to the pinned plain layer (unit gates; a
+# constant decay gate is the plain layer with a scaled lambda), to the explicit double sum with
+# the gates' cumulative products (brute.layer(gates=...)), and to two invariances.
+
+def _gate_case(seed, N=11, F=3, D=4, M=5):
+    rng = np.random.default_rng(seed)
+    q, k, v = rng.standard_normal((N, F)), rng.standard_normal((N, F)), rng.standard_normal((N, D))
+    lam = rng.uniform(0.5, 0.95, M) * np.exp(1j * rng.uniform(-1, 1, M))
+    beta = 1.0 + 0.3j * rng.uniform(-1, 1, M)
+    w = rng.uniform(0.0, 1.5, N)
+    a = rng.uniform(0.2, 1.0, N)
+    return q, k, v, lam, beta, w, a
+
+
+def test_gated_unit_gates_are_the_plain_layer():
+    q, k, v, lam, beta, _, _ = _gate_case(31)
+    ones = np.ones(len(q))
+    o1, n1, d1, s1 = oracle.scan_gated(q, k, v, lam, beta, ones, ones)
+    o2, n2, d2, s2 = oracle.scan(q, k, v, lam, beta)
+    assert np.array_equal(n1, n2) and np.array_equal(d1, d2) and np.array_equal(o1, o2)
+    assert all(np.array_equal(x, y) for x, y in zip(s1, s2))
+
+
+@pytest.mark.parametrize("seed", [32, 33, 34])
+def test_gated_matches_brute_force(seed):
+    """The explicit double sum over s <= t with weight w_s prod_{s<u<=t} a_u lambda^(t-s),
+    the products as exp of summed logs and lambda^n as exp(n Log lambda)."""
+    q, k, v, lam, beta, w, a = _gate_case(seed)
+    o, num, den, _ = oracle.scan_gated(q, k, v, lam, beta, w, a)
+    ob, nb, db = brute.layer(q, k, v, lam, beta, gates=(w, a))
+    assert _rel(num, nb) < 1e-10 and _rel(den, db) < 1e-10
+    ok = db > 1e-6
+    assert _rel(o[ok], ob[ok]) < 1e-10
+
+
+def test_gated_constant_decay_is_a_scaled_lambda():
+    """a_t = c at every step (w = 1) is the plain layer with modes c lambda."""
+    q, k, v, lam, beta, _, _ = _gate_case(35)
+    c = 0.83
+    o1, n1, d1, s1 = oracle.scan_gated(q, k, v, lam, beta, np.ones(len(q)), np.full(len(q), c))
+    o2, n2, d2, s2 = oracle.scan(q, k, v, c * lam, beta)
+    assert _rel(n1, n2) < 1e-12 and _rel(d1, d2) < 1e-12
+    assert max(_rel(x, y) for x, y in zip(s1, s2)) < 1e-12
+
+
+def test_gated_zero_write_gate_drops_the_token():
+    """w_t = 0: token t writes nothing, so its k_t and v_t change no output and no state."""
+    q, k, v, lam, beta, w, a = _gate_case(36)
+    t0 = 4
+    w = w.copy()
+    w[t0] = 0.0
+    o1, _, _, s1 = oracle.scan_gated(q, k, v, lam, beta, w, a)
+    k2, v2 = k.copy(), v.copy()
+    k2[t0] += 3.0
+    v2[t0] -= 5.0
+    o2, _, _, s2 = oracle.scan_gated(q, k2, v2, lam, beta, w, a)
+    assert _rel(o1, o2) < 1e-13 and max(_rel(x, y) for x, y in zip(s1, s2)) < 1e-13
+
+
+def test_gated_common_write_scale():
+    """Scaling every write gate by c scales U, Gamma, eta by c, so num and den by c^2 and o is
+    unchanged wherever den stays above the clamp."""
+    q, k, v, lam, beta, w, a = _gate_case(37)
+    c = 1.7
+    o1, n1, d1, _ = oracle.scan_gated(q, k, v, lam, beta, w, a)
+    o2, n2, d2, _ = oracle.scan_gated(q, k, v, lam, beta, c * w, a)
+    assert _rel(n2, c * c * n1) < 1e-12 and _rel(d2, c * c * d1) < 1e-12
+    ok = (d1 > 1e-6) & (d2 > 1e-6)
+    assert ok.any() and _rel(o1[ok], o2[ok]) < 1e-12
+
+
+GATE_MUTANTS = {
+    "decay_gate_on_the_write_too": ("const double complex wb = w * (beta[2 * m] + I * beta[2 * m + 1]);",
+                                    "const double complex wb = at * w * (beta[2 * m] + I * beta[2 * m + 1]);"),
+    "eta_not_gated": ("const double complex ec = l * (e[2 * m] + I * e[2 * m + 1]) + wb;",
+                      "const double complex ec = l * (e[2 * m] + I * e[2 * m + 1]) + (beta[2 * m] + I * beta[2 * m + 1]);"),
+    "value_write_not_gated": ("const double complex gc = l * (g[0] + I * g[1]) + wb * v[(size_t)t * D + j];",
+                              "const double complex gc = l * (g[0] + I * g[1]) + (beta[2 * m] + I * beta[2 * m + 1]) * v[(size_t)t * D + j];"),
+    "decay_gate_as_power": ("const double complex l = at * (lam[2 * m] + I * lam[2 * m + 1]);",
+                            "const double complex l = cpow(lam[2 * m] + I * lam[2 * m + 1], at);"),
+    "gates_one_token_late": ("const double w = wgate[t], at = dgate[t];",
+                             "const double w = wgate[t > 0 ? t - 1 : 0], at = dgate[t > 0 ? t - 1 : 0];"),
+}
+
+
+@pytest.mark.parametrize("mutant", sorted(GATE_MUTANTS))
+def test_planted_gate_mistake_fails_a_pin(mutant, tmp_path):
+    src = open(oracle._SRC).read()
+    old, new = GATE_MUTANTS[mutant]
+    assert src.count(old) == 1, f"mutation anchor for {mutant} not found once"
+    path = tmp_path / "mutant.c"
+    path.write_text(src.replace(old, new))
+    so = tmp_path / "mutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-o", str(so),
+                           str(path), "-lm"])
+    lib = oracle.load_library(str(so))
+    q, k, v, lam, beta, w, a = _gate_case(32)
+    _, num, den, _ = oracle.scan_gated(q, k, v, lam, beta, w, a, lib=lib)
+    _, nb, db = brute.layer(q, k, v, lam, beta, gates=(w, a))
+    assert not (_rel(num, nb) < 1e-10 and _rel(den, db) < 1e-10), f"{mutant} passed"
