@@ -315,6 +315,38 @@ ia_status ia_decode_step_readout(const ia_desc* desc,
                                  const void* lambda, const void* beta, const void* readout,
                                  ia_state* st, void* o_t, void* stream);
 
+/* Selective writing and memory decay.  Input-dependent gates, computed by the caller for every
+ * token, control what the memory stores and how fast it forgets (the optional enhancement of
+ * [summary §3.3], ablated as selective vs non-selective in [summary §B.3, Table 7]).  The pages
+ * give no formula; the reading implemented, with a write gate w and a decay gate a per token
+ * and head:
+ *   U[m,:]   <- a_t lambda_m U[m,:]   + w_t beta_m phi(k_t)
+ *   Gam[m,:] <- a_t lambda_m Gam[m,:] + w_t beta_m v_t
+ *   eta[m]   <- a_t lambda_m eta[m]   + w_t beta_m
+ * and the readout unchanged (w = a = 1 is the plain layer; 0 < a <= 1 forgets faster).
+ *   wgate, dgate  float, device, read only: [B][N][H] for the prefill (dense, element
+ *                 (b, n, h) at (b N + n) H + h), [B][H] for the decode step; NULL:
+ *                 IA_ERR_NULL; 16-byte aligned; must not overlap an output.
+ * The gated prefill runs the token-by-token fp32 kernel for either input dtype, one workgroup
+ * per (b,h) slice (the chunked kernels take no gates): about as fast as the fp32 prefill.
+ * IA_FLAG_BIDIR: both directions use the gates of the positions they walk.  Other arguments,
+ * layouts and errors as ia_prefill_fwd / ia_decode_step.  The workspace (one state, used when
+ * st is NULL or IA_FLAG_BIDIR is set) is ia_prefill_gated_workspace_bytes(desc) bytes. */
+size_t ia_prefill_gated_workspace_bytes(const ia_desc* desc);
+
+ia_status ia_prefill_fwd_gated(const ia_desc* desc,
+                               const void* q, const void* k, const void* v,
+                               const void* wgate, const void* dgate,
+                               const void* lambda, const void* beta,
+                               ia_state* st, void* o,
+                               void* workspace, size_t ws_bytes, void* stream);
+
+ia_status ia_decode_step_gated(const ia_desc* desc,
+                               const void* q_t, const void* k_t, const void* v_t,
+                               const void* wgate, const void* dgate,
+                               const void* lambda, const void* beta,
+                               ia_state* st, void* o_t, void* stream);
+
 /* Static string naming a status code. */
 const char* ia_status_string(ia_status s);
 

@@ -207,14 +207,17 @@ size_t ia_prefill_workspace_bytes(const ia_desc* d) {
   return scan_workspace(d, false).bytes;
 }
 
-// The prefill behind every prefill entry point: optional (b, n, h) strides of q, k, v, and an
-// optional readout matrix ([H][M][M] complex64), which takes the token-sequential path.
+// The prefill behind every prefill entry point: optional (b, n, h) strides of q, k, v, an
+// optional readout matrix ([H][M][M] complex64), and optional write / decay gates ([B][N][H]
+// float); a readout matrix or gates take the token-sequential path.
 static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, const void* v,
                               const long long strides[3][3], const void* lambda,
                               const void* beta, const void* readout, ia_state* st, void* o,
-                              void* workspace, size_t ws_bytes, void* stream) {
+                              void* workspace, size_t ws_bytes, void* stream,
+                              const float* wgate = nullptr, const float* dgate = nullptr) {
   ia_status s = check_desc(d, true);
   if (s != IA_OK) return s;
+  const bool gated = wgate || dgate;
   // Element strides (b, n, h) of q, k, v; the feature axis is contiguous.
   ia::RowStrides sq = ia::dense_strides(d->N, d->H, d->F), sk = sq;
   ia::RowStrides sv = ia::dense_strides(d->N, d->H, d->Dv);
@@ -230,7 +233,7 @@ static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, co
     if (sq.b != sk.b || sq.n != sk.n || sq.h != sk.h) return IA_ERR_UNSUPPORTED;
     // The chunk kernels address a chunk's rows with 32-bit byte offsets (as for the dense
     // layout in use_chunk_path).
-    if (!readout && use_chunk_path(d) &&
+    if (!readout && !gated && use_chunk_path(d) &&
         (64LL * sq.n * 2 > (1LL << 30) || 64LL * sv.n * 2 > (1LL << 30)))
       return IA_ERR_UNSUPPORTED;
   }
@@ -243,6 +246,7 @@ static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, co
     if (!aligned16(p)) return IA_ERR_ALIGN;
   if (o && !aligned16(o)) return IA_ERR_ALIGN;
   if (readout && !aligned16(readout)) return IA_ERR_ALIGN;
+  if ((wgate && !aligned16(wgate)) || (dgate && !aligned16(dgate))) return IA_ERR_ALIGN;
   if (st && (s = check_state(d, st)) != IA_OK) return s;
 
   const size_t tok = size_t(d->B) * d->N * d->H;
@@ -256,7 +260,8 @@ static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, co
   const Range rl = rng(lambda, size_t(d->H) * d->M * 8);
   const Range rb = rng(beta, size_t(d->H) * d->M * 8);
   const Range rr = rng(readout, readout ? size_t(d->H) * d->M * d->M * 8 : 0);
-  const Range ins[] = {rq, rk, rv, rl, rb, rr};
+  const Range rwg = rng(wgate, wgate ? tok * 4 : 0), rdg = rng(dgate, dgate ? tok * 4 : 0);
+  const Range ins[] = {rq, rk, rv, rl, rb, rr, rwg, rdg};
   if (o) {
     const Range ro = rng(o, tok * d->Dv * esize(d->out_dtype));
     for (const Range& r : ins)
@@ -276,7 +281,7 @@ static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, co
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
 
-  if (!readout && use_chunk_path(d)) {
+  if (!readout && !gated && use_chunk_path(d)) {
     const ChunkPlan pl = chunk_plan(d);
     if (!workspace || ws_bytes < pl.bytes) return IA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return IA_ERR_ALIGN;
@@ -329,7 +334,7 @@ static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, co
   // bf16 inputs on shapes without a chunk kernel are refused rather than run 300x slower by
   // the token-sequential kernel (fp32 inputs take that path, and any shape with a readout
   // matrix).
-  if (!readout && d->in_dtype == IA_BF16) return IA_ERR_UNSUPPORTED;
+  if (!readout && !gated && d->in_dtype == IA_BF16) return IA_ERR_UNSUPPORTED;
 
   // fp32 path: token-sequential recurrence.
   const ScanWorkspace w = scan_workspace(d, st != nullptr);
@@ -359,6 +364,8 @@ static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, co
                  d->M, d->in_dtype == IA_BF16, d->out_dtype == IA_BF16, d->den_clamp, 0};
   a.opt = kernel_opt(d);
   a.readout = static_cast<const float2*>(readout);
+  a.wgate = wgate;
+  a.dgate = dgate;
   if (!bidir) return launch_status(ia::launch_scan_prefill(a, hs));
 
   // Bidirectional: the forward direction writes o, the reverse direction (from a zero state
@@ -417,6 +424,20 @@ ia_status ia_prefill_fwd_readout(const ia_desc* d, const void* q, const void* k,
   if (!readout) return IA_ERR_NULL;
   return prefill_impl(d, q, k, v, nullptr, lambda, beta, readout, st, o, workspace, ws_bytes,
                       stream);
+}
+
+size_t ia_prefill_gated_workspace_bytes(const ia_desc* d) {
+  if (check_desc(d, true) != IA_OK) return 0;
+  return scan_workspace(d, false).bytes;
+}
+
+ia_status ia_prefill_fwd_gated(const ia_desc* d, const void* q, const void* k, const void* v,
+                               const void* wgate, const void* dgate, const void* lambda,
+                               const void* beta, ia_state* st, void* o, void* workspace,
+                               size_t ws_bytes, void* stream) {
+  if (!wgate || !dgate) return IA_ERR_NULL;
+  return prefill_impl(d, q, k, v, nullptr, lambda, beta, nullptr, st, o, workspace, ws_bytes,
+                      stream, static_cast<const float*>(wgate), static_cast<const float*>(dgate));
 }
 
 size_t ia_prefill_bwd_workspace_bytes(const ia_desc* d) {
@@ -525,7 +546,8 @@ ia_status ia_prefill_bwd(const ia_desc* d, const void* q, const void* k, const v
 // The decode step behind both decode entry points; readout: [H][M][M] complex64 or NULL.
 static ia_status decode_impl(const ia_desc* d, const void* q_t, const void* k_t,
                              const void* v_t, const void* lambda, const void* beta,
-                             const void* readout, ia_state* st, void* o_t, void* stream) {
+                             const void* readout, ia_state* st, void* o_t, void* stream,
+                             const float* wgate = nullptr, const float* dgate = nullptr) {
   ia_status s = check_desc(d, false);
   if (s != IA_OK) return s;
   if (d->flags & IA_FLAG_BIDIR) return IA_ERR_UNSUPPORTED;
@@ -534,12 +556,14 @@ static ia_status decode_impl(const ia_desc* d, const void* q_t, const void* k_t,
   for (const void* p : {q_t, k_t, v_t, lambda, beta, static_cast<const void*>(o_t)})
     if (!aligned16(p)) return IA_ERR_ALIGN;
   if (readout && !aligned16(readout)) return IA_ERR_ALIGN;
+  if ((wgate && !aligned16(wgate)) || (dgate && !aligned16(dgate))) return IA_ERR_ALIGN;
   const size_t bh = size_t(d->B) * d->H;
   const Range ins[] = {rng(q_t, bh * d->F * esize(d->in_dtype)),
                        rng(k_t, bh * d->F * esize(d->in_dtype)),
                        rng(v_t, bh * d->Dv * esize(d->in_dtype)),
                        rng(lambda, size_t(d->H) * d->M * 8), rng(beta, size_t(d->H) * d->M * 8),
-                       rng(readout, readout ? size_t(d->H) * d->M * d->M * 8 : 0)};
+                       rng(readout, readout ? size_t(d->H) * d->M * d->M * 8 : 0),
+                       rng(wgate, wgate ? bh * 4 : 0), rng(dgate, dgate ? bh * 4 : 0)};
   const Range outs[] = {rng(o_t, bh * d->Dv * esize(d->out_dtype)),
                         rng(st->U, state_u_bytes(d)), rng(st->Gamma, state_g_bytes(d)),
                         rng(st->eta, state_e_bytes(d))};
@@ -555,6 +579,8 @@ static ia_status decode_impl(const ia_desc* d, const void* q_t, const void* k_t,
                    d->out_dtype == IA_BF16, d->den_clamp};
   a.opt = kernel_opt(d);
   a.readout = static_cast<const float2*>(readout);
+  a.wgate = wgate;
+  a.dgate = dgate;
   return launch_status(ia::launch_decode_step(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -562,6 +588,15 @@ ia_status ia_decode_step(const ia_desc* d, const void* q_t, const void* k_t, con
                          const void* lambda, const void* beta, ia_state* st, void* o_t,
                          void* stream) {
   return decode_impl(d, q_t, k_t, v_t, lambda, beta, nullptr, st, o_t, stream);
+}
+
+ia_status ia_decode_step_gated(const ia_desc* d, const void* q_t, const void* k_t,
+                               const void* v_t, const void* wgate, const void* dgate,
+                               const void* lambda, const void* beta, ia_state* st, void* o_t,
+                               void* stream) {
+  if (!wgate || !dgate) return IA_ERR_NULL;
+  return decode_impl(d, q_t, k_t, v_t, lambda, beta, nullptr, st, o_t, stream,
+                     static_cast<const float*>(wgate), static_cast<const float*>(dgate));
 }
 
 ia_status ia_decode_step_readout(const ia_desc* d, const void* q_t, const void* k_t,

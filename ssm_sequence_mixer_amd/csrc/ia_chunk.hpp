@@ -540,7 +540,8 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
       bf16x8 fq[KF];
 #pragma unroll
       for (int s = 0; s < KF; ++s) fq[s] = lds8(s16 + oF[s] + (Lay::oFq - Lay::oFk) + 16 * r * F).b;
-      // ---- S^T tiles (rows j, columns i), causal: tiles jt <= r
+      // ---- S^T tiles (rows j, columns i), causal: tiles jt <= r.  Their results are read
+      // only after the inter-chunk MFMAs below, which cover the latency.
       f32x4 accS[NR];
 #pragma unroll
       for (int jt = 0; jt < NR; ++jt) {
@@ -549,23 +550,29 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
 #pragma unroll
           for (int s = 0; s < KF; ++s)
             acc = mma_bf16(lds8(s16 + oF[s] + 16 * jt * F).b, fq[s], acc);
-          if (jt == r) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              if (4 * g + q > il) acc[q] = 0.f;
-          }
         }
         accS[jt] = acc;
-        IA_STEP_FENCE();
       }
-      bf16x8 Sf[KC];
-#pragma unroll
-      for (int kb = 0; kb < KC; ++kb) Sf[kb] = pack_bf16(accS[2 * kb], accS[2 * kb + 1]);
+      IA_STEP_FENCE();
 
-      // ---- A'^T tiles (rows k, columns i)
+      // ---- A'^T tiles (rows k, columns i): the inter-chunk term (lam U_c) Fq^T first
       f32x4 accA[TM];
 #pragma unroll
       for (int kt = 0; kt < TM; ++kt) accA[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KF; ++s) {
+#pragma unroll
+        for (int kt = 0; kt < TM; ++kt)
+          accA[kt] = mma_bf16(lds8(s16 + oLU[s] + 16 * kt * F).b, fq[s], accA[kt]);
+        IA_STEP_FENCE();
+      }
+      // causal mask of the diagonal S tile, then S as the bf16 operand of WT^T S
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (4 * g + q > il) accS[r][q] = 0.f;
+      bf16x8 Sf[KC];
+#pragma unroll
+      for (int kb = 0; kb < KC; ++kb) Sf[kb] = pack_bf16(accS[2 * kb], accS[2 * kb + 1]);
 #pragma unroll
       for (int kb = 0; kb < KC; ++kb)
         if (32 * kb <= 16 * r + 15) {
@@ -574,13 +581,6 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
             accA[kt] = mma_bf16(lds8(s16 + oWT[kb] + 16 * kt * C).b, Sf[kb], accA[kt]);
           IA_STEP_FENCE();
         }
-#pragma unroll
-      for (int s = 0; s < KF; ++s) {
-#pragma unroll
-        for (int kt = 0; kt < TM; ++kt)
-          accA[kt] = mma_bf16(lds8(s16 + oLU[s] + 16 * kt * F).b, fq[s], accA[kt]);
-        IA_STEP_FENCE();
-      }
 
       // ---- lam^(2i) A' (fp32), den_inter, per-query scale, fp16 operands [Re | -Im]
       float amax = 0.f;
@@ -617,9 +617,9 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
     __syncthreads();
     if (x.want_out) {
 
-      // ---- P^T tiles (rows j, columns i), causal
+      // ---- P^T tiles (rows j, columns i), causal; their results are read after the
+      // inter-chunk numerator MFMAs below
       f32x4 accP[NR];
-      float den_intra = 0.f;
 #pragma unroll
       for (int jt = 0; jt < NR; ++jt) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -627,16 +627,33 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
 #pragma unroll
           for (int kb = 0; kb < KM; ++kb)
             acc = mma_f16(lds8(s16 + oWb[kb] + 16 * jt * M2).h, Af[kb], acc);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[q] *= x.wb_unscale;
-            if (jt == r && 4 * g + q > il) acc[q] = 0.f;
-            den_intra += acc[q];
-          }
         }
         accP[jt] = acc;
+      }
+      IA_STEP_FENCE();
+      // ---- c_d-scaled Re(A lam G) per value tile (rows d, columns i)
+      f32x4 accX[TD];
+#pragma unroll
+      for (int dt = 0; dt < TD; ++dt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < KM; ++kb)
+          acc = mma_f16(lds8(s16 + oGT[kb] + 16 * dt * M2).h, Af[kb], acc);
+        accX[dt] = acc;
         IA_STEP_FENCE();
       }
+      float den_intra = 0.f;
+#pragma unroll
+      for (int jt = 0; jt < NR; ++jt)
+        if (jt <= r) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float p = accP[jt][q] * x.wb_unscale;
+            if (jt == r && 4 * g + q > il) p = 0.f;
+            accP[jt][q] = p;
+            den_intra += p;
+          }
+        }
       den_intra = xor_sum16_32(den_intra);
       const float den = den_intra + si * den_inter;   // in units of si
       // num and den are in units of si (the fp16 scale of A).  Without a denominator
@@ -646,7 +663,7 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
 #pragma unroll
       for (int kb = 0; kb < KC; ++kb) Pf[kb] = pack_bf16(accP[2 * kb], accP[2 * kb + 1]);
 
-      // ---- num^T tiles (rows d, columns i): P V (accI) + c_d-scaled Re(A lam G) (accX)
+      // ---- num^T tiles (rows d, columns i): P V (accI) + the inter-chunk part (accX)
       const int t = c * C + 16 * r + il;
       const bool ok = t < a.N;
       // Output row of query t from this lane's column 4g: dt tiles are constant offsets.
@@ -655,18 +672,16 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
       float* const o32 = static_cast<float*>(a.o) + obase;
 #pragma unroll
       for (int dt = 0; dt < TD; ++dt) {
-        f32x4 accI = {0.f, 0.f, 0.f, 0.f}, accX = {0.f, 0.f, 0.f, 0.f};
+        f32x4 accI = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KC; ++kb)
           if (32 * kb <= 16 * r + 15)
             accI = mma_bf16(ldtr<D>(s16, oV[dt], kb).b, Pf[kb], accI);
-#pragma unroll
-        for (int kb = 0; kb < KM; ++kb)
-          accX = mma_f16(lds8(s16 + oGT[kb] + 16 * dt * M2).h, Af[kb], accX);
+        const f32x4 accXd = accX[dt];
         if (ok) {
           const float4 ci = *reinterpret_cast<const float4*>(sb + oCi + 64 * dt);
-          float val[4] = {(accI[0] + accX[0] * ci.x) * rd, (accI[1] + accX[1] * ci.y) * rd,
-                          (accI[2] + accX[2] * ci.z) * rd, (accI[3] + accX[3] * ci.w) * rd};
+          float val[4] = {(accI[0] + accXd[0] * ci.x) * rd, (accI[1] + accXd[1] * ci.y) * rd,
+                          (accI[2] + accXd[2] * ci.z) * rd, (accI[3] + accXd[3] * ci.w) * rd};
           if (a.out_bf16) {
             if (a.accumulate) {   // the element's other direction, same lane, read then written
               const uint2 p = *reinterpret_cast<const uint2*>(o16 + 16 * dt);

@@ -70,6 +70,7 @@ struct DecodeArgs {
   float clamp;
   int opt;   // kOptNoDen | kOptIdentity
   const float2* readout = nullptr;   // [H][M][M] readout matrix, or NULL
+  const float *wgate = nullptr, *dgate = nullptr;   // [B][H] write / decay gates, or NULL
 };
 
 struct ScanArgs {
@@ -85,6 +86,7 @@ struct ScanArgs {
   int reverse;
   int opt;   // kOptNoDen | kOptIdentity
   const float2* readout = nullptr;   // [H][M][M] readout matrix, or NULL
+  const float *wgate = nullptr, *dgate = nullptr;   // [B][N][H] write / decay gates, or NULL
 };
 
 // Chunked MFMA prefill of one direction (bf16 inputs).  The sequence is cut into `segments`

@@ -29,7 +29,8 @@ decode_step_kernel(const void* __restrict__ q, const void* __restrict__ k,
                    const float2* __restrict__ beta, float2* __restrict__ U,
                    float2* __restrict__ G, float2* __restrict__ E, void* __restrict__ o,
                    int H, int F, int D, int M, int out_bf16, float clamp,
-                   int opt, const float2* __restrict__ rmat) {
+                   int opt, const float2* __restrict__ rmat, const float* __restrict__ wgate,
+                   const float* __restrict__ dgate) {
   __shared__ StepSmem<MM> s;
   const int bh = blockIdx.x;
   const int h = bh % H;
@@ -37,7 +38,8 @@ decode_step_kernel(const void* __restrict__ q, const void* __restrict__ k,
   seq_load_token<BF>(s, q, k, v, (size_t)bh * F, (size_t)bh * D, F, D, opt);
   __syncthreads();
   seq_step(s, U + (size_t)bh * M * F, G + (size_t)bh * M * D, E + (size_t)bh * M, F, D, M,
-           rmat ? rmat + (size_t)h * M * M : nullptr);
+           rmat ? rmat + (size_t)h * M * M : nullptr, wgate ? wgate[bh] : 1.f,
+           dgate ? dgate[bh] : 1.f);
   for (int j = threadIdx.x; j < D; j += kStepThreads)
     store_out(o, (size_t)bh * D + j, readout(seq_num(s, j), s.den, clamp, opt), out_bf16);
 }
@@ -55,7 +57,8 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
                         const float2* __restrict__ beta, float2* __restrict__ U,
                         float2* __restrict__ G, float2* __restrict__ E, void* __restrict__ o,
                         int H, int M, int out_bf16, float clamp, int opt,
-                        const float2* __restrict__ rmat) {
+                        const float2* __restrict__ rmat, const float* __restrict__ wgate,
+                        const float* __restrict__ dgate) {
   constexpr int NT = 512, NWV = NT / 64;
   constexpr int RU = F / 2, RD = D / 2;
   static_assert(RU <= 64 && RD <= 64 && NT % RU == 0 && NT % RD == 0, "row width");
@@ -76,10 +79,13 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
   const float2 kk = load_pair_t<BF>(k, (size_t)bh * F + 2 * pu);
   const float2 qq = load_pair_t<BF>(q, (size_t)bh * F + 2 * pu);
   const float2 vv = load_pair_t<BF>(v, (size_t)bh * D + 2 * pd);
+  // with gates, lambda_m and beta_m of this slice's step times its decay and write gate
+  const float wg = wgate ? wgate[bh] : 1.f, dg = dgate ? dgate[bh] : 1.f;
   float2 e = make_float2(0.f, 0.f);
   if (tid < M) {
-    s_lam[tid] = lam[(size_t)h * M + tid];
-    s_beta[tid] = beta[(size_t)h * M + tid];
+    const float2 l = lam[(size_t)h * M + tid], bt = beta[(size_t)h * M + tid];
+    s_lam[tid] = make_float2(dg * l.x, dg * l.y);
+    s_beta[tid] = make_float2(wg * bt.x, wg * bt.y);
     e = Eb[tid];
   }
 
@@ -196,12 +202,13 @@ scan_prefill_kernel(const void* __restrict__ q, const void* __restrict__ k,
                     float2* __restrict__ G, float2* __restrict__ E, void* __restrict__ o,
                     int accumulate, int N, int H, int F, int D, int M,
                     int in_bf16, int out_bf16, float clamp, int reverse, RowStrides sqk,
-                    RowStrides sv, int opt, const float2* __restrict__ rmat) {
+                    RowStrides sv, int opt, const float2* __restrict__ rmat,
+                    const float* __restrict__ wgate, const float* __restrict__ dgate) {
   __shared__ StepSmem<MM> s;
   const int bh = blockIdx.x;
   const int b = bh / H, h = bh % H;
   const SeqScanArgs a{q, k, v, sqk, sv, lam, beta, o, accumulate, N, H, F, D, M,
-                      in_bf16, out_bf16, clamp, reverse, opt, rmat};
+                      in_bf16, out_bf16, clamp, reverse, opt, rmat, wgate, dgate};
   seq_scan(s, a, b, h, U + (size_t)bh * M * F, G + (size_t)bh * M * D, E + (size_t)bh * M);
 }
 
@@ -260,11 +267,11 @@ static void launch_decode_rows_t(const DecodeArgs& a, hipStream_t st) {
   if (a.M <= 64)
     hipLaunchKernelGGL((decode_step_rows_kernel<F, D, 64, BF>), dim3(a.B * a.H), dim3(512), 0,
                        st, a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H, a.M,
-                       a.out_bf16, a.clamp, a.opt, a.readout);
+                       a.out_bf16, a.clamp, a.opt, a.readout, a.wgate, a.dgate);
   else
     hipLaunchKernelGGL((decode_step_rows_kernel<F, D, kMaxModes, BF>), dim3(a.B * a.H),
                        dim3(512), 0, st, a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H,
-                       a.M, a.out_bf16, a.clamp, a.opt, a.readout);
+                       a.M, a.out_bf16, a.clamp, a.opt, a.readout, a.wgate, a.dgate);
 }
 
 template <int F, int D>
@@ -308,7 +315,7 @@ hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t st) {
 #define IA_DSK(BF, MM)                                                                      \
   hipLaunchKernelGGL((decode_step_kernel<BF, MM>), dim3(a.B * a.H), dim3(kStepThreads), 0, st, \
                      a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H, a.F, a.D, a.M,      \
-                     a.out_bf16, a.clamp, a.opt, a.readout)
+                     a.out_bf16, a.clamp, a.opt, a.readout, a.wgate, a.dgate)
   if (a.in_bf16) {
     if (a.M <= 64) IA_DSK(true, 64); else IA_DSK(true, kMaxModes);
   } else {
@@ -326,7 +333,7 @@ hipError_t launch_scan_prefill(const ScanArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((scan_prefill_kernel<MM>), dim3(a.B * a.H), dim3(kStepThreads), 0, st,    \
                      a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.accumulate, a.N, a.H, \
                      a.F, a.D, a.M, a.in_bf16, a.out_bf16, a.clamp, a.reverse, a.sqk, a.sv,   \
-                     a.opt, a.readout)
+                     a.opt, a.readout, a.wgate, a.dgate)
   if (a.M <= 64)
     IA_SCAN(64);
   else

@@ -45,10 +45,13 @@ struct SeqSmem {
 // F and D are multiples of 16, so a row is a whole number of float4 pairs.
 // R: this head's readout matrix [M][M] (row m, column n), or NULL for none: the readouts then
 // use (a R)[n] = sum_m a[m] R[m][n] in place of a.
+// wg, dg: this token's write and decay gates (1 and 1 without gating): every lambda_m is
+// taken times dg and every beta_m times wg.
 template <int NW, int MF, int MD, int MM, bool WR>
 __device__ __forceinline__ void seq_step(SeqSmem<NW, MF, MD, MM, WR>& s, float2* __restrict__ U,
                                          float2* __restrict__ G, float2* __restrict__ E, int F,
-                                         int D, int M, const float2* __restrict__ R) {
+                                         int D, int M, const float2* __restrict__ R,
+                                         float wg = 1.f, float dg = 1.f) {
   constexpr int NT = 64 * NW;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -63,7 +66,8 @@ __device__ __forceinline__ void seq_step(SeqSmem<NW, MF, MD, MM, WR>& s, float2*
     const int m = wave + NW * i;
     ar[i] = ai[i] = 0.f;
     if (m < M) {
-      const float2 l = s.lam[m], b = s.beta[m];
+      const float2 l = make_float2(dg * s.lam[m].x, dg * s.lam[m].y);
+      const float2 b = make_float2(wg * s.beta[m].x, wg * s.beta[m].y);
       float4* row = reinterpret_cast<float4*>(U + (size_t)m * F);
       for (int p = lane; p < F / 2; p += 64) {
         float4 u = row[p];
@@ -88,7 +92,8 @@ __device__ __forceinline__ void seq_step(SeqSmem<NW, MF, MD, MM, WR>& s, float2*
   }
   // eta: one mode per thread.
   for (int m = threadIdx.x; m < M; m += NT) {
-    float2 e = cfma(s.lam[m], E[m], s.beta[m]);
+    float2 e = cfma(make_float2(dg * s.lam[m].x, dg * s.lam[m].y), E[m],
+                    make_float2(wg * s.beta[m].x, wg * s.beta[m].y));
     E[m] = e;
     s.eta[m] = e;
   }
@@ -119,7 +124,8 @@ __device__ __forceinline__ void seq_step(SeqSmem<NW, MF, MD, MM, WR>& s, float2*
 #pragma unroll
   for (int i = 0; i < 2 * NP; ++i) acc[i] = 0.f;
   for (int m = wave; m < M; m += NW) {
-    const float2 l = s.lam[m], b = s.beta[m], a = A[m];
+    const float2 l = make_float2(dg * s.lam[m].x, dg * s.lam[m].y);
+    const float2 b = make_float2(wg * s.beta[m].x, wg * s.beta[m].y), a = A[m];
     float4* row = reinterpret_cast<float4*>(G + (size_t)m * D);
 #pragma unroll
     for (int i = 0; i < NP; ++i) {
@@ -193,7 +199,9 @@ __device__ __forceinline__ float seq_num(const SeqSmem<NW, MF, MD, MM, WR>& s, i
 }
 
 // The whole sequence of slice (b, h) from the state (U, G, E) (updated in place to the state
-// after the last token), walking positions N-1 .. 0 when `reverse` is set.  q, k and v are
+// after the last token), walking positions N-1 .. 0 when `reverse` is set, with the write and
+// decay gates of each position when given (selective writing and memory decay, summary page
+// §3.3: lambda_m -> dg lambda_m, beta_m -> wg beta_m at that token).  q, k and v are
 // addressed through their element strides; o is dense [B][N][H][D] (o + value with
 // `accumulate`), or NULL for a state-only walk.
 struct SeqScanArgs {
@@ -208,6 +216,7 @@ struct SeqScanArgs {
   int reverse;
   int opt;
   const float2* readout;   // [H][M][M] or NULL
+  const float *wgate = nullptr, *dgate = nullptr;   // [B][N][H] write / decay gates, or NULL
 };
 
 template <bool BF, int NW, int MF, int MD, int MM, bool WR>
@@ -220,8 +229,10 @@ __device__ __forceinline__ void seq_scan_t(SeqSmem<NW, MF, MD, MM, WR>& s, const
     const size_t tok = ((size_t)b * a.N + pos) * a.H + h;
     seq_load_token<BF>(s, a.q, a.k, a.v, (size_t)(b * a.sqk.b + pos * a.sqk.n + h * a.sqk.h),
                        (size_t)(b * a.sv.b + pos * a.sv.n + h * a.sv.h), a.F, a.D, a.opt);
+    const size_t gi = ((size_t)b * a.N + pos) * a.H + h;
+    const float wg = a.wgate ? a.wgate[gi] : 1.f, dg = a.dgate ? a.dgate[gi] : 1.f;
     __syncthreads();
-    seq_step(s, U, G, E, a.F, a.D, a.M, R);
+    seq_step(s, U, G, E, a.F, a.D, a.M, R, wg, dg);
     if (a.o) {
       for (int j = threadIdx.x; j < a.D; j += 64 * NW) {
         float val = readout(seq_num(s, j), s.den, a.clamp, a.opt);

@@ -348,3 +348,29 @@ def test_readout_variants_validation():
     B, H, M, F, D = 2, 3, 16, 32, 16
     want = (B * H * M * (F + D + 1) * 8 + 255) // 256 * 256
     assert ia.lib.ia_prefill_readout_workspace_bytes(ctypes.byref(d)) == want
+
+
+def test_gated_variants_validation():
+    d = desc(Dv=32)
+    g = lambda *a: ia.lib.ia_prefill_fwd_gated(ctypes.byref(d), *a)
+    base = [addr(0), addr(1), addr(2), addr(20), addr(21), addr(3), addr(4), state(), addr(5),
+            addr(6), 1 << 40, None]
+    for i in (3, 4):                         # a gate array missing
+        a = list(base)
+        a[i] = P(0)
+        assert g(*a) == 1
+    a = list(base)
+    a[3] = addr(20, 8)                       # misaligned gate array
+    assert g(*a) == 4
+    a = list(base)
+    a[8] = addr(20, 64)                      # o overlapping the write gates
+    assert g(*a) == 5
+    assert ia.lib.ia_decode_step_gated(ctypes.byref(d), addr(0), addr(1), addr(2), P(0),
+                                       addr(21), addr(3), addr(4), state(), addr(5), None) == 1
+    assert ia.lib.ia_decode_step_gated(ctypes.byref(d), addr(0), addr(1), addr(2), addr(20),
+                                       addr(21), addr(3), addr(4), state(), addr(21, 16),
+                                       None) == 5
+    # workspace: one state, rounded up to 256 bytes
+    B, H, M, F, D = 2, 3, 16, 32, 32
+    want = (B * H * M * (F + D + 1) * 8 + 255) // 256 * 256
+    assert ia.lib.ia_prefill_gated_workspace_bytes(ctypes.byref(d)) == want

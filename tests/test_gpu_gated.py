@@ -1,0 +1,144 @@
+"""GPU parity of selective writing and memory decay (ia_prefill_fwd_gated, ia_decode_step_gated)
+against the oracle's gated recurrence (oracle.scan_gated, pinned in tests/test_oracle.py).
+
+The gated layer runs the token-by-token fp32 kernels for either input dtype, so the inputs
+(bf16-exact values for bf16) reach both sides as the same numbers and the fp32 tolerance
+applies.  Gates: write gates in (0, 1.5), decay gates in (0.5, 1]."""
+import numpy as np
+import pytest
+
+import ia_workloads as W
+import oracle
+from helpers import TOL_F32, dev, host, report, rowrel, state_rel, tag
+
+pytestmark = pytest.mark.gpu
+
+
+def _ia():
+    import ssm_sequence_mixer_amd as ia
+    return ia
+
+
+def _gates(rng, shape):
+    return (rng.uniform(0.0, 1.5, shape).astype(np.float32),
+            rng.uniform(0.5, 1.0, shape).astype(np.float32))
+
+
+def _flip(a):
+    return np.ascontiguousarray(np.asarray(a)[:, ::-1])
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 150, 32, 16, 16), (1, 2, 300, 64, 64, 32),
+                                   (2, 2, 97, 128, 128, 64)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gated_prefill_matches_oracle(shape, dtype):
+    import torch
+    ia = _ia()
+    B, H, N, F, D, M = shape
+    inp = W.make_inputs(B, H, N, F, D, M, dtype=dtype, seed=1000 + N + F)
+    wg, dg = _gates(np.random.default_rng(1001 + N), (B, N, H))
+    td = torch.float32 if dtype == "f32" else torch.bfloat16
+    pre = W.make_inputs(B, H, 7, F, D, M, dtype="f32", seed=1002, std=0.5)
+    st_ref = oracle.prefill(pre["q"], pre["k"], pre["v"], inp["lam"], inp["beta"])[3]
+    st = tuple(dev(x) for x in st_ref)
+    st_ref = tuple(host(x) for x in st)
+    tag(f"gated prefill {shape} {dtype}")
+    o = ia.prefill(dev(inp["q"], td), dev(inp["k"], td), dev(inp["v"], td), dev(inp["lam"]),
+                   dev(inp["beta"]), state=st, out_dtype=torch.float32,
+                   gates=(dev(wg), dev(dg)))
+    torch.cuda.synchronize()
+    o_ref, _, _, st_out = oracle.prefill_gated(inp["q"], inp["k"], inp["v"], inp["lam"],
+                                               inp["beta"], wg, dg, state=st_ref, threads=8)
+    e_o = rowrel(host(o), o_ref)
+    e_s = state_rel(tuple(host(x) for x in st), st_out)
+    report(f"gated prefill {shape} {dtype} output / state", max(e_o, e_s))
+    assert e_o < TOL_F32 and e_s < TOL_F32
+
+
+def test_gated_unit_gates_equal_the_plain_fp32_prefill():
+    """Gates of one give the ungated fp32 prefill bit for bit (the same kernel, times 1)."""
+    import torch
+    ia = _ia()
+    B, H, N, F, D, M = 2, 2, 120, 32, 32, 16
+    inp = W.make_inputs(B, H, N, F, D, M, dtype="f32", seed=1010)
+    args = [dev(inp[n]) for n in "qkv"] + [dev(inp["lam"]), dev(inp["beta"])]
+    ones = torch.ones((B, N, H), dtype=torch.float32, device="cuda")
+    tag("gated prefill, unit gates")
+    o1 = ia.prefill(*args, gates=(ones, ones))
+    o2 = ia.prefill(*args)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gated_decode_steps_continue_the_prefill(dtype):
+    """A gated prefill of the first tokens, then gated decode steps (row-parallel kernel at
+    these sizes, mode-looping at F = 256), equal the oracle's gated recurrence over all
+    tokens, outputs and final state."""
+    import torch
+    ia = _ia()
+    for (B, H, F, D, M) in [(2, 4, 128, 128, 64), (1, 2, 256, 48, 32)]:
+        N0, steps = 20, 5
+        inp = W.make_inputs(B, H, N0 + steps, F, D, M, dtype=dtype, seed=1020 + F)
+        wg, dg = _gates(np.random.default_rng(1021 + F), (B, N0 + steps, H))
+        td = torch.float32 if dtype == "f32" else torch.bfloat16
+        st = ia.new_state(B, H, M, F, D)
+        tag(f"gated prefill then decode B={B} H={H} F={F} D={D} M={M} {dtype}")
+        ia.prefill(*(dev(inp[n][:, :N0], td) for n in "qkv"), dev(inp["lam"]), dev(inp["beta"]),
+                   state=st, want_output=False,
+                   gates=(dev(wg[:, :N0]), dev(dg[:, :N0])))
+        outs = []
+        for t in range(N0, N0 + steps):
+            outs.append(host(ia.decode(*(dev(inp[n][:, t], td) for n in "qkv"), dev(inp["lam"]),
+                                       dev(inp["beta"]), st,
+                                       gates=(dev(wg[:, t]), dev(dg[:, t])))))
+        torch.cuda.synchronize()
+        o_ref, _, _, st_ref = oracle.prefill_gated(inp["q"], inp["k"], inp["v"], inp["lam"],
+                                                   inp["beta"], wg, dg, threads=8)
+        e_o = rowrel(np.stack(outs, axis=1), o_ref[:, N0:])
+        e_s = state_rel(tuple(host(x) for x in st), st_ref)
+        report(f"gated decode F={F} {dtype} outputs / state", max(e_o, e_s))
+        assert e_o < TOL_F32 and e_s < TOL_F32
+
+
+def test_gated_bidirectional():
+    """Both directions with the gates of the positions they walk: o = IA_g(x) +
+    flip(IA_{flip g}(flip x))."""
+    import torch
+    ia = _ia()
+    B, H, N, F, D, M = 1, 3, 211, 32, 32, 32
+    inp = W.make_inputs(B, H, N, F, D, M, dtype="bf16", seed=1030)
+    wg, dg = _gates(np.random.default_rng(1031), (B, N, H))
+    tag("gated bidirectional prefill")
+    o = ia.prefill(*(dev(inp[n], torch.bfloat16) for n in "qkv"), dev(inp["lam"]),
+                   dev(inp["beta"]), bidir=True, out_dtype=torch.float32,
+                   gates=(dev(wg), dev(dg)))
+    torch.cuda.synchronize()
+    f = oracle.prefill_gated(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"], wg, dg)[0]
+    r = oracle.prefill_gated(_flip(inp["q"]), _flip(inp["k"]), _flip(inp["v"]), inp["lam"],
+                             inp["beta"], _flip(wg), _flip(dg))[0]
+    err = rowrel(host(o), f + r[:, ::-1])
+    report("gated bidirectional", err)
+    assert err < TOL_F32
+
+
+def test_gated_1p3b_workload_every_slice():
+    """The 1.3B-shaped layer (B=4, H=16, N=2048, F=Dv=128, M=64, bf16 inputs) with gates, every
+    (b, h) slice, outputs and final state."""
+    import torch
+    ia = _ia()
+    inp = W.l1p3b()
+    B, H, N = 4, 16, 2048
+    wg, dg = _gates(np.random.default_rng(1040), (B, N, H))
+    st = ia.new_state(B, H, 64, 128, 128)
+    tag("gated 1.3b workload")
+    o = ia.prefill(*(dev(inp[n], torch.bfloat16) for n in "qkv"), dev(inp["lam"]),
+                   dev(inp["beta"]), state=st, out_dtype=torch.float32,
+                   gates=(dev(wg), dev(dg)))
+    torch.cuda.synchronize()
+    o_ref, _, _, st_ref = oracle.prefill_gated(inp["q"], inp["k"], inp["v"], inp["lam"],
+                                               inp["beta"], wg, dg, threads=16)
+    e_o = rowrel(host(o), o_ref)
+    e_s = state_rel(tuple(host(x) for x in st), st_ref)
+    report("gated 1.3b every slice, output / state", max(e_o, e_s))
+    assert e_o < TOL_F32 and e_s < TOL_F32
