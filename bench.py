@@ -142,11 +142,36 @@ def bench_prefill(args, torch, ia, W):
              "hbm_frac": byts / (ms * 1e-3) / HBM_PEAK,
              "mfma_achieved_TFLOPs": flops / (ms * 1e-3) / 1e12,
              "mfma_frac": flops / (ms * 1e-3) / BF16_PEAK}
+    # The readout-matrix variant (a R in place of a, R a per-head M x M complex matrix) on the
+    # same inputs, timed the same way; chunk 32 where its 64-token LDS layout has no room.
+    rng = np.random.default_rng(7)
+    R = np.eye(M)[None] + 0.05 * (rng.standard_normal((H, M, M)) +
+                                  1j * rng.standard_normal((H, M, M))) / np.sqrt(M)
+    Rd = torch.from_numpy(R.astype(np.complex64)).cuda()
+    ws_r = torch.empty(max(ia.ia_prefill_readout_workspace_bytes(desc), 16), dtype=torch.uint8,
+                       device="cuda")
+
+    def step_r():
+        ia.ia_prefill_fwd_readout(desc, q, k, v, lam, beta, Rd, None, o, ws_r)
+
+    for _ in range(args.warmup):
+        step_r()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step_r()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_r = t0.elapsed_time(t1) / args.steps
+    readout = {"scope": "ia_prefill_fwd_readout on the same inputs, ms_per_step",
+               "ms_per_step": ms_r, "vs_plain": ms_r / ms,
+               "chunk": 32 if (F == 128 and D == 128 and M == 64) else 64}
+
     cfg = {"workload": title, "B": B, "H": H, "N": N, "F": F, "Dv": D, "M": M,
            "chunk": 64, "in_dtype": "bf16", "out_dtype": "bf16",
            "bidirectional": bidir}
     return dict(ms=ms, tokens=B * N, cfg=cfg, roofline=roof, mfma=mfma, whole=whole,
-                kernels_ms=kern_ms, inp=inp)
+                kernels_ms=kern_ms, inp=inp, readout=readout)
 
 
 KERNEL_SOURCES = ["ssm_sequence_mixer_amd/csrc/ia_chunk.hpp",
@@ -435,6 +460,7 @@ def main():
         "mfma": pf["mfma"],
         "whole_step": pf["whole"],
         "kernels_ms": pf["kernels_ms"],
+        "readout_matrix": pf["readout"],
         "decode": dec,
         "backward": bwd,
         "cpu_baseline": cpu,

@@ -295,13 +295,22 @@ ia_status ia_prefill_bwd(const ia_desc* desc,
  *   a'[n] = sum_m a[m] R[m][n],  o_t = Re(a' Gamma) / max(Re(a' eta), den_clamp)
  * (or Re(a' Gamma) with IA_FLAG_NO_DEN).  R = identity gives the plain layer.
  *   readout  [H][M][M] complex64 (row m, column n), device, read only; NULL: IA_ERR_NULL.
- * Both run the token-sequential fp32 kernels (bf16 inputs included): the chunked factorisation
- * keeps modes separate.  Other arguments, layouts and errors as ia_prefill_fwd /
- * ia_decode_step; readout must be 16-byte aligned and must not overlap an output. */
+ * The decode step runs its fp32 kernels.  The prefill with bf16 inputs on the chunk kernels'
+ * shapes (ia_prefill_fwd's) runs the chunked path: the readouts' query-mode rows a (C x M per
+ * chunk) take a R on MFMA before both readouts, the state pass unchanged [summary §A.2, §A.3].
+ * Its chunk length is desc->chunk, or with chunk 0 64, except F = Dv = 128 with M = 64, whose
+ * 64-token layout has no room for R in LDS: there 32, and an explicit chunk 64 returns
+ * IA_ERR_UNSUPPORTED.  The same accuracy note as ia_prefill_fwd applies, with the denominator's
+ * conditioning that of Re(a R eta): a strongly mixing R can raise the terms over the
+ * denominator.  fp32 inputs, and bf16 shapes without chunk kernels, run the token-sequential
+ * fp32 kernel.  Other arguments, layouts and errors as ia_prefill_fwd / ia_decode_step;
+ * readout must be 16-byte aligned and must not overlap an output. */
 
-/* Workspace bytes ia_prefill_fwd_readout needs at most: one state,
- * B*H*M*(F+Dv+1) complex64 rounded up to 256 bytes (used when st is NULL or IA_FLAG_BIDIR is
- * set; otherwise the workspace may be NULL).  0 on an invalid descriptor. */
+/* Workspace bytes ia_prefill_fwd_readout needs at most: on the chunked path its plan (as
+ * ia_prefill_workspace_bytes, at its chunk length) plus each head's readout-matrix operand,
+ * 8*M*M bytes and a scale, 256-byte aligned; otherwise one state, B*H*M*(F+Dv+1) complex64
+ * rounded up to 256 bytes (used when st is NULL or IA_FLAG_BIDIR is set; otherwise the
+ * workspace may be NULL).  0 on an invalid descriptor. */
 size_t ia_prefill_readout_workspace_bytes(const ia_desc* desc);
 
 ia_status ia_prefill_fwd_readout(const ia_desc* desc,

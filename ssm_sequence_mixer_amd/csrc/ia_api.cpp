@@ -88,7 +88,7 @@ ScanWorkspace scan_workspace(const ia_desc* d, bool have_state) {
 
 struct ChunkPlan {
   int C, G, seg_chunks;
-  size_t tables_off, slots_off, state_off, bytes;
+  size_t tables_off, slots_off, state_off, rtab_off, bytes;
 };
 
 // Readout options of the desc's flags, in the kernels' encoding.
@@ -106,12 +106,26 @@ bool use_chunk_path(const ia_desc* d) {
          64L * d->H * std::max(d->F, d->Dv) * 2 <= (1L << 30);
 }
 
-ChunkPlan chunk_plan(const ia_desc* d) {
+// Chunk length of a call: the descriptor's, else 64, or 32 for a readout matrix whose
+// 64-token layout does not fit the LDS.
+int chunk_len(const ia_desc* d, bool rm) {
+  if (d->chunk) return d->chunk;
+  return rm && !ia::chunk_rm_supported(64, d->F, d->Dv, d->M) ? 32 : 64;
+}
+
+// The chunked path serves a call: bf16 chunk shapes (use_chunk_path), no gates, and with a
+// readout matrix a chunk length that has its instantiation.
+bool chunk_path_for(const ia_desc* d, bool rm, bool gated) {
+  if (gated || !use_chunk_path(d)) return false;
+  return !rm || ia::chunk_rm_supported(chunk_len(d, true), d->F, d->Dv, d->M);
+}
+
+ChunkPlan chunk_plan(const ia_desc* d, bool rm = false) {
   ChunkPlan p{};
-  p.C = d->chunk ? d->chunk : 64;
+  p.C = chunk_len(d, rm);
   const int n_chunks = (d->N + p.C - 1) / p.C;
   const long seqs = long(d->B) * d->H;
-  int per_cu = ia::chunk_wgs_per_cu(p.C, d->F, d->Dv, d->M);
+  int per_cu = ia::chunk_wgs_per_cu(p.C, d->F, d->Dv, d->M, rm);
   if (per_cu <= 0) per_cu = 1;
   long G = long(ia::device_cus()) * per_cu / seqs;
   if (G > n_chunks) G = n_chunks;
@@ -127,6 +141,8 @@ ChunkPlan chunk_plan(const ia_desc* d) {
   // of heads on the fp32 route when the caller passes none
   p.state_off = p.bytes;
   p.bytes += round_up(state_bytes(d));
+  p.rtab_off = p.bytes;
+  if (rm) p.bytes += round_up(size_t(d->H) * ia::readout_table_bytes(d->M));
   return p;
 }
 
@@ -281,8 +297,8 @@ static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, co
 
   hipStream_t hs = static_cast<hipStream_t>(stream);
 
-  if (!readout && !gated && use_chunk_path(d)) {
-    const ChunkPlan pl = chunk_plan(d);
+  if (chunk_path_for(d, readout != nullptr, gated)) {
+    const ChunkPlan pl = chunk_plan(d, readout != nullptr);
     if (!workspace || ws_bytes < pl.bytes) return IA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return IA_ERR_ALIGN;
     const Range rw = rng(workspace, pl.bytes);
@@ -313,6 +329,8 @@ static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, co
     }
     a.slots = reinterpret_cast<float*>(ws + pl.slots_off);
     a.tables = reinterpret_cast<unsigned char*>(ws + pl.tables_off);
+    a.readout = static_cast<const float2*>(readout);
+    a.rtab = readout ? reinterpret_cast<unsigned char*>(ws + pl.rtab_off) : nullptr;
     a.B = d->B; a.H = d->H; a.N = d->N; a.F = d->F; a.D = d->Dv; a.M = d->M;
     a.chunk = pl.C;
     a.segments = pl.G;
@@ -332,9 +350,12 @@ static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, co
   }
 
   // bf16 inputs on shapes without a chunk kernel are refused rather than run 300x slower by
-  // the token-sequential kernel (fp32 inputs take that path, and any shape with a readout
-  // matrix).
-  if (!readout && !gated && d->in_dtype == IA_BF16) return IA_ERR_UNSUPPORTED;
+  // the token-sequential kernel (fp32 inputs take that path, as do gated calls).  A readout
+  // matrix with bf16 inputs runs the token-sequential kernel only on shapes the chunk kernels
+  // do not take at all; a chunk shape whose requested chunk length has no readout-matrix
+  // instantiation is refused.
+  if (!gated && d->in_dtype == IA_BF16 && (!readout || use_chunk_path(d)))
+    return IA_ERR_UNSUPPORTED;
 
   // fp32 path: token-sequential recurrence.
   const ScanWorkspace w = scan_workspace(d, st != nullptr);
@@ -414,6 +435,7 @@ ia_status ia_prefill_fwd_strided(const ia_desc* d, const void* q, const void* k,
 
 size_t ia_prefill_readout_workspace_bytes(const ia_desc* d) {
   if (check_desc(d, true) != IA_OK) return 0;
+  if (chunk_path_for(d, true, false)) return chunk_plan(d, true).bytes;
   return scan_workspace(d, false).bytes;
 }
 

@@ -20,15 +20,48 @@ IA_EXTERN_C(32)
 IA_EXTERN_C(64)
 #undef IA_EXTERN_C
 #undef IA_EXTERN
+// The readout-matrix variant, for every shape whose LDS layout fits (all but C = 64 with
+// F = Dv = 128 and M = 64).
+#define IA_EXTERN_RM(C, FF, MM)                                                           \
+  extern template hipError_t launch_chunk_t<C, FF, FF, MM, true>(const ChunkArgs&, int,    \
+                                                                 hipStream_t, int);       \
+  extern template int chunk_occupancy_t<C, FF, FF, MM, true>();
+IA_EXTERN_RM(32, 32, 16) IA_EXTERN_RM(32, 32, 32) IA_EXTERN_RM(32, 32, 64)
+IA_EXTERN_RM(32, 64, 16) IA_EXTERN_RM(32, 64, 32) IA_EXTERN_RM(32, 64, 64)
+IA_EXTERN_RM(32, 128, 16) IA_EXTERN_RM(32, 128, 32) IA_EXTERN_RM(32, 128, 64)
+IA_EXTERN_RM(64, 32, 16) IA_EXTERN_RM(64, 32, 32) IA_EXTERN_RM(64, 32, 64)
+IA_EXTERN_RM(64, 64, 16) IA_EXTERN_RM(64, 64, 32) IA_EXTERN_RM(64, 64, 64)
+IA_EXTERN_RM(64, 128, 16) IA_EXTERN_RM(64, 128, 32)
+#undef IA_EXTERN_RM
+
+bool chunk_rm_supported(int chunk, int F, int D, int M) {
+  return chunk_supported(F, D, M) && (chunk == 32 || chunk == 64) &&
+         !(chunk == 64 && F == 128 && D == 128 && M == 64);
+}
+
+long readout_table_bytes(int M) {
+  switch (M) {
+    case 16: return ReadoutTable<16>::bytes;
+    case 32: return ReadoutTable<32>::bytes;
+    case 64: return ReadoutTable<64>::bytes;
+  }
+  return 0;
+}
 
 // ---------------------------------------------------------------- per-head tables
 // Once per call, when no state-only pass carries them: block (h, run) is one table run
 // (table_run), C/4 small blocks per head, so the transcendental work spreads over the CUs.
+// Block (h, 0) also writes the head's readout-matrix operand when rtab is set.
 template <int C, int M>
 __global__ void __launch_bounds__(4 * M) chunk_tables_kernel(const float2* __restrict__ lam,
                                     const float2* __restrict__ beta, unsigned char* tables,
-                                    long table_bytes, int Lt, int Ls) {
-  table_run<C, M>(lam, beta, tables, table_bytes, Lt, Ls, blockIdx.x, blockIdx.y, threadIdx.x);
+                                    long table_bytes, int Lt, int Ls, int half,
+                                    const float2* __restrict__ R, unsigned char* rtab,
+                                    long rtab_bytes) {
+  table_run<C, M>(lam, beta, tables, table_bytes, Lt, Ls, blockIdx.x, blockIdx.y, threadIdx.x,
+                  half);
+  if (rtab && blockIdx.y == 0)
+    readout_table_run<M>(R, rtab, rtab_bytes, blockIdx.x, threadIdx.x, 4 * M);
 }
 
 // ---------------------------------------------------------------- segment carry
@@ -187,6 +220,21 @@ static hipError_t dispatch_fdm(const ChunkArgs& a, int F, int D, int M, int n_wg
 }
 
 template <int C>
+static hipError_t dispatch_fdm_rm(const ChunkArgs& a, int F, int D, int M, int n_wg,
+                                  hipStream_t st, int kind) {
+#define IA_CASE(FF, MM)                                   \
+  if (F == FF && D == FF && M == MM) return launch_chunk_t<C, FF, FF, MM, true>(a, n_wg, st, kind);
+  IA_CASE(32, 16) IA_CASE(32, 32) IA_CASE(32, 64)
+  IA_CASE(64, 16) IA_CASE(64, 32) IA_CASE(64, 64)
+  IA_CASE(128, 16) IA_CASE(128, 32)
+  if constexpr (C == 32) {
+    IA_CASE(128, 64)
+  }
+#undef IA_CASE
+  return hipErrorInvalidValue;
+}
+
+template <int C>
 static hipError_t dispatch_state_fdm(const ChunkArgs& a, int F, int D, int M, int n_wg,
                                      hipStream_t st, int kind) {
 #define IA_CASE(FF, MM)                                   \
@@ -204,7 +252,8 @@ static hipError_t launch_tables_cm(const ChunkPrefillArgs& p, long tb, hipStream
   (void)hipGetLastError();
   prof_begin(st);
   hipLaunchKernelGGL((chunk_tables_kernel<C, M>), dim3(p.H, C / 4), dim3(4 * M), 0, st,
-                     p.lam, p.beta, p.tables, tb, Lt, p.seg_chunks * C);
+                     p.lam, p.beta, p.tables, tb, Lt, p.seg_chunks * C, p.readout ? 1 : 0,
+                     p.readout, p.rtab, readout_table_bytes(M));
   prof_end(st, kKindTables);
   return hipGetLastError();
 }
@@ -235,7 +284,19 @@ long chunk_table_bytes(int chunk, int M) {
   return 0;
 }
 
-int chunk_wgs_per_cu(int chunk, int F, int D, int M) {
+int chunk_wgs_per_cu(int chunk, int F, int D, int M, bool rm) {
+  if (rm) {
+#define IA_OCC(CC, FF, MM) \
+  if (chunk == CC && F == FF && D == FF && M == MM) return chunk_occupancy_t<CC, FF, FF, MM, true>();
+    IA_OCC(32, 32, 16) IA_OCC(32, 32, 32) IA_OCC(32, 32, 64)
+    IA_OCC(32, 64, 16) IA_OCC(32, 64, 32) IA_OCC(32, 64, 64)
+    IA_OCC(32, 128, 16) IA_OCC(32, 128, 32) IA_OCC(32, 128, 64)
+    IA_OCC(64, 32, 16) IA_OCC(64, 32, 32) IA_OCC(64, 32, 64)
+    IA_OCC(64, 64, 16) IA_OCC(64, 64, 32) IA_OCC(64, 64, 64)
+    IA_OCC(64, 128, 16) IA_OCC(64, 128, 32)
+#undef IA_OCC
+    return 0;
+  }
 #define IA_OCC(CC, FF, MM) \
   if (chunk == CC && F == FF && D == FF && M == MM) return chunk_occupancy_t<CC, FF, FF, MM>();
   IA_OCC(32, 32, 16) IA_OCC(32, 32, 32) IA_OCC(32, 32, 64)
@@ -317,11 +378,18 @@ hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
   a.slots_per_seq = G - 1;
   a.tables = p.tables;
   a.table_bytes = tb;
+  a.tables_half = p.readout ? 1 : 0;
+  a.readout = p.readout;
+  a.rtab = p.rtab;
+  a.rtab_bytes = readout_table_bytes(p.M);
   a.wU = p.wU;
   a.wG = p.wG;
   a.wE = p.wE;
 
   auto go = [&](const ChunkArgs& x, int n_wg, int kind) -> hipError_t {
+    if (p.readout)
+      return C == 64 ? dispatch_fdm_rm<64>(x, p.F, p.D, p.M, n_wg, st, kind)
+                     : dispatch_fdm_rm<32>(x, p.F, p.D, p.M, n_wg, st, kind);
     return C == 64 ? dispatch_fdm<64>(x, p.F, p.D, p.M, n_wg, st, kind)
                    : dispatch_fdm<32>(x, p.F, p.D, p.M, n_wg, st, kind);
   };
@@ -335,6 +403,7 @@ hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
     s.n_seg = G - 1;
     s.seg_end = p.slots;
     s.tables_out = p.tables;
+    s.rtab_out = p.readout ? p.rtab : nullptr;
     s.n_sum_wg = seqs * (G - 1);
     s.Lt = p.N % C == 0 ? C : p.N % C;
     const int n_wg = seqs * (G - 1) + p.H;

@@ -269,7 +269,7 @@ __device__ __forceinline__ void slot_get(const float* slot, long pair_off, long 
 
 // ---------------------------------------------------------------- LDS layout
 
-template <int C, int F, int D, int M, int NR>
+template <int C, int F, int D, int M, int NR, bool RM = false>
 struct Layout {
   static constexpr int M2 = 2 * M;
   // 16-bit element offsets; every matrix is swizzled by row (see soff).
@@ -280,7 +280,9 @@ struct Layout {
   static constexpr int oWb = oWT + M2 * C;         // [C][2M]  fp16 scaled beta lam^-j (k slots)
   static constexpr int oLU = oWb + C * M2;         // [2M][F]  bf16 lam U_c          (f order)
   static constexpr int oGT = oLU + M2 * F;         // [D][2M]  fp16 c_d lam G_c      (k slots)
-  static constexpr int n16 = oGT + D * M2;
+  static constexpr int oR = oGT + D * M2;          // [2M][2M] fp16 scaled readout matrix
+                                                   //          (k slots; RM only)
+  static constexpr int n16 = oR + (RM ? M2 * M2 : 0);
   // 32-bit arrays (byte offsets)
   static constexpr int bC = n16 * 2;               // [D]  float  c_d
   static constexpr int bCi = bC + D * 4;           // [D]  float  1 / c_d
@@ -334,6 +336,14 @@ struct ChunkArgs {
   int slots_per_seq;
   const unsigned char* tables;                 // per-head tables (chunk_tables_kernel)
   long table_bytes;                            // bytes per head
+  int tables_half;                             // factor tables of lam^i (readout matrix)
+                                               // instead of lam^(2i)
+  // Readout matrix (kernels instantiated with RM): R [H][M][M] for the fp32 route, and its
+  // per-head MFMA operand (readout_table_kernel): fp16 [2M][2M], then 1 / its scale.
+  const float2* readout;
+  const unsigned char* rtab;
+  long rtab_bytes;
+  unsigned char* rtab_out;   // state-only pass: its table workgroups also write rtab
   // State-only pass: workgroups past the first n_sum_wg compute the per-head tables (one
   // workgroup per head, table_run) into tables_out, Lt the last chunk's length.
   unsigned char* tables_out;
@@ -360,6 +370,19 @@ struct TableLayout {
   static constexpr long oSc = oInv + 8L * M;          // float: 1 / fp16 table scale
   static constexpr long oRoute = oSc + 4;             // int: 1 = the head takes the fp32 route
   static constexpr long bytes = (oSc + 16 + 255) / 256 * 256;
+};
+
+// Per-head MFMA operand of the readout matrix R (readout_table_kernel).  With the query-mode
+// row a = lam^i A' held as the operand [Re a | -Im a] (the same convention as every other
+// contraction here), (a R)^T = R_op [Re a | -Im a]^T for the real 2M x 2M matrix
+//   row n     (Re (aR)_n):  Re R[m][n] at column m,  Im R[m][n] at column M + m
+//   row M + n (Im (aR)_n):  Im R[m][n] at column m, -Re R[m][n] at column M + m,
+// stored in fp16 times a power-of-two scale (max |entry| in [2^14, 2^15)), columns in K-slot
+// order, 16-byte blocks swizzled by row as in LDS; then the float 1 / scale.
+template <int M>
+struct ReadoutTable {
+  static constexpr long oScale = 8L * M * M;
+  static constexpr long bytes = (oScale + 4 + 255) / 256 * 256;
 };
 
 // Word 3 of a CDNA buffer resource for raw (untyped) loads: 32-bit data format, no swizzle,
@@ -403,6 +426,7 @@ struct Ctx {
   int seq, seg, b, h, c_begin, c_end;
   bool last_seg, want_out;
   float wb_unscale;
+  float r_unscale;   // 1 / scale of the readout-matrix operand (RM)
   __device__ int pos_of(const ChunkArgs& a, int t) const { return a.dir ? a.N - 1 - t : t; }
   __device__ size_t tok_index(const ChunkArgs& a, int pos) const {
     return ((size_t)b * a.N + pos) * a.H + h;
@@ -448,9 +472,9 @@ __device__ __forceinline__ void wait_vm_zero() {
 
 // ---------------------------------------------------------------- readout waves
 // Wave R owns queries [16R, 16R+16) of every chunk.
-template <int C, int F, int D, int M, int R>
+template <int C, int F, int D, int M, int R, bool RM>
 __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F, D, M>& x) {
-  using Lay = Layout<C, F, D, M, C / 16>;
+  using Lay = Layout<C, F, D, M, C / 16, RM>;
   constexpr int NR = C / 16;
   constexpr int M2 = 2 * M;
   constexpr int MH = M / 16;
@@ -464,7 +488,7 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
   // Per-lane LDS offsets, one per K step (row il, block 4 step + g); tiles add constants.
   // Offsets from the LDS base (matrix start included, see opaque): phi(k) / phi(q) (one set,
   // phi(q) is at a constant distance below 64 KiB), lam U, the two decay tables, lam G, v.
-  int oF[KF], oLU[KF], oWT[KC], oWb[KM], oGT[KM], oV[TD];
+  int oF[KF], oLU[KF], oWT[KC], oWb[KM], oGT[KM], oV[TD], oRm[RM ? KM : 1];
 #pragma unroll
   for (int s = 0; s < KF; ++s) {
     oF[s] = opaque(Lay::oFk + lane_off<F>(il, 4 * s + g));
@@ -476,6 +500,7 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
   for (int kb = 0; kb < KM; ++kb) {
     oWb[kb] = opaque(Lay::oWb + lane_off<M2>(il, 4 * kb + g));
     oGT[kb] = opaque(Lay::oGT + lane_off<M2>(il, 4 * kb + g));
+    if constexpr (RM) oRm[kb] = opaque(Lay::oR + lane_off<M2>(il, 4 * kb + g));
   }
 #pragma unroll
   for (int dt = 0; dt < TD; ++dt) oV[dt] = opaque(Lay::oV + tr_off<D>(dt, lane));
@@ -513,7 +538,8 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
   if (x.c_begin < x.c_end) fetch_v(x.c_begin);
   __syncthreads();  // tables visible
   // lam^(2i) for this lane's queries i = 16r + il and modes m = 16mt + 4g + q, for the whole
-  // segment: the product of the two factor tables, formed once.
+  // segment: the product of the two factor tables, formed once.  With a readout matrix the
+  // tables hold lam^i factors instead: A = lam^i A' before the mixing, lam^i (A R) after it.
   float2 l2[MH][4];
 #pragma unroll
   for (int mt = 0; mt < MH; ++mt)
@@ -582,6 +608,44 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
           IA_STEP_FENCE();
         }
 
+      // ---- readout matrix: A = lam^i A' as the fp16 operand [Re | -Im] (scaled per query),
+      // then (A R)^T = R_op A^T on MFMA into the same accumulators, whose [Re; Im] rows the
+      // step below takes as it takes A' (times 1 / both scales).
+      float ru = 1.f;
+      if constexpr (RM) {
+        float xmax = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MH; ++mt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float2 L = l2[mt][q];
+            const float xr = accA[mt][q], yi = accA[mt + MH][q];
+            const float ar = xr * L.x - yi * L.y, ai = xr * L.y + yi * L.x;
+            accA[mt][q] = ar;
+            accA[mt + MH][q] = -ai;
+            xmax = fmaxf(xmax, fmaxf(fabsf(ar), fabsf(ai)));
+          }
+        const float sx = pow2_scale(xor_max16_32(xmax));
+        ru = x.r_unscale / sx;
+        f16x8 Xf[KM];
+#pragma unroll
+        for (int kb = 0; kb < KM; ++kb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            Xf[kb][q] = (_Float16)(sx * accA[2 * kb][q]);
+            Xf[kb][4 + q] = (_Float16)(sx * accA[2 * kb + 1][q]);
+          }
+#pragma unroll
+        for (int nt = 0; nt < TM; ++nt) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < KM; ++kb)
+            acc = mma_f16(lds8(s16 + oRm[kb] + 16 * nt * M2).h, Xf[kb], acc);
+          accA[nt] = acc;
+        }
+        IA_STEP_FENCE();
+      }
+
       // ---- lam^(2i) A' (fp32), den_inter, per-query scale, fp16 operands [Re | -Im]
       float amax = 0.f;
 #pragma unroll
@@ -591,7 +655,11 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
           // m = 16 mt + 4 g + q
           const int mo = 8 * (16 * mt + q);
           const float2 le = *reinterpret_cast<const float2*>(sb + oG + mo);
-          const float2 L2 = l2[mt][q];
+          float2 L2 = l2[mt][q];
+          if constexpr (RM) {
+            L2.x *= ru;
+            L2.y *= ru;
+          }
           const float xr = accA[mt][q], yi = accA[mt + MH][q];
           const float ar = xr * L2.x - yi * L2.y, ai = xr * L2.y + yi * L2.x;
           accA[mt][q] = ar;
@@ -710,10 +778,10 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
 // State wave U owns feature tiles ft = U, U+NS, ... of (lam U)^T and value tiles dt = U,
 // U+NS, ... of lam G, in fp32 MFMA accumulators for the whole segment; wave 0 also owns
 // lam eta.
-template <int C, int F, int D, int M, int U>
+template <int C, int F, int D, int M, int U, bool RM>
 __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D, M>& x) {
   using TL = TableLayout<C, M>;
-  using Lay = Layout<C, F, D, M, C / 16>;
+  using Lay = Layout<C, F, D, M, C / 16, RM>;
   constexpr int M2 = 2 * M;
   constexpr int MH = M / 16;
   constexpr int TM = M2 / 16;
@@ -876,6 +944,9 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
     lds_dma(x.tab + TL::oW, sb + 2 * Lay::oWT, (int)(TL::nW / 16), u, lane, NS);
     lds_dma(x.tab + TL::oL2, sb + Lay::bL2lo, (int)(TL::nL2 / 16), u, lane, NS);
     lds_dma(x.tab + TL::oPow, sb + Lay::bPowL, 40 * M / 16, (u + 1) % NS, lane, NS);
+    if constexpr (RM)
+      lds_dma(a.rtab + (size_t)x.h * a.rtab_bytes, sb + 2 * Lay::oR, 8 * M * M / 16,
+              (u + 2) % NS, lane, NS);
   }
   wait_vm_zero();
   __syncthreads();  // tables visible (the Horner step reads lam^Ls from LDS)
@@ -1155,11 +1226,11 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
 // The fp32 route of a head whose modes the bf16 chunk factorisation does not resolve
 // (chunk_unresolved): the token-by-token recurrence of slice (b, h) over all N tokens by this
 // workgroup, from the caller's state (updated in place) or from zero in the workspace state.
-template <int C, int F, int D, int M>
+template <int C, int F, int D, int M, bool RM>
 __device__ __forceinline__ void fp32_route(const ChunkArgs& a, int b, int h, unsigned char* smem) {
   constexpr int NW = C / 16 + StateWaves<F, D, M>::NS;
-  using S = SeqSmem<NW, F, D, M, false>;
-  static_assert(sizeof(S) <= Layout<C, F, D, M, C / 16>::bytes, "fits the kernel's LDS");
+  using S = SeqSmem<NW, F, D, M, RM>;
+  static_assert(sizeof(S) <= Layout<C, F, D, M, C / 16, RM>::bytes, "fits the kernel's LDS");
   S& s = *reinterpret_cast<S*>(smem);
   const size_t seq = (size_t)b * a.H + h;
   float2 *U, *G, *E;
@@ -1177,27 +1248,29 @@ __device__ __forceinline__ void fp32_route(const ChunkArgs& a, int b, int h, uns
     __syncthreads();
   }
   const SeqScanArgs sa{a.q, a.k, a.v, a.sqk, a.sv, a.lam, a.beta, a.o, a.accumulate, a.N, a.H,
-                       F, D, M, 1, a.out_bf16, a.clamp, a.dir, a.opt, nullptr};
+                       F, D, M, 1, a.out_bf16, a.clamp, a.dir, a.opt,
+                       RM ? a.readout : nullptr};
   seq_scan(s, sa, b, h, U, G, E);
 }
 
-template <int C, int F, int D, int M, int W>
+template <int C, int F, int D, int M, bool RM, int W>
 __device__ __forceinline__ void run_role(const ChunkArgs& a, const Ctx<C, F, D, M>& x) {
   if constexpr (W < C / 16)
-    readout_main<C, F, D, M, W>(a, x);
+    readout_main<C, F, D, M, W, RM>(a, x);
   else
-    state_main<C, F, D, M, W - C / 16>(a, x);
+    state_main<C, F, D, M, W - C / 16, RM>(a, x);
 }
 
-template <int C, int F, int D, int M, int... Ws>
+template <int C, int F, int D, int M, bool RM, int... Ws>
 __device__ __forceinline__ void dispatch_role(const ChunkArgs& a, const Ctx<C, F, D, M>& x,
                                               int w, std::integer_sequence<int, Ws...>) {
-  ((w == Ws ? (run_role<C, F, D, M, Ws>(a, x), 0) : 0), ...);
+  ((w == Ws ? (run_role<C, F, D, M, RM, Ws>(a, x), 0) : 0), ...);
 }
-template <int C, int F, int D, int M>
+// RM: the readout matrix variant (a R in place of a before both readouts).
+template <int C, int F, int D, int M, bool RM>
 __global__ void __launch_bounds__(64 * (C / 16 + StateWaves<F, D, M>::NS))
 chunk_prefill_kernel(const ChunkArgs a) {
-  using Lay = Layout<C, F, D, M, C / 16>;
+  using Lay = Layout<C, F, D, M, C / 16, RM>;
   using TL = TableLayout<C, M>;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   uint16_t* s16 = reinterpret_cast<uint16_t*>(smem_raw);
@@ -1239,11 +1312,14 @@ chunk_prefill_kernel(const ChunkArgs a) {
   x.want_out = a.o != nullptr;
   x.tab = a.tables + (size_t)x.h * a.table_bytes;
   if (__builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(x.tab + TL::oRoute))) {
-    if (x.seg == a.seg_first) fp32_route<C, F, D, M>(a, x.b, x.h, smem_raw);
+    if (x.seg == a.seg_first) fp32_route<C, F, D, M, RM>(a, x.b, x.h, smem_raw);
     return;
   }
 
   x.wb_unscale = *reinterpret_cast<const float*>(x.tab + TL::oSc);
+  x.r_unscale = RM ? *reinterpret_cast<const float*>(a.rtab + (size_t)x.h * a.rtab_bytes +
+                                                     ReadoutTable<M>::oScale)
+                   : 1.f;
   // Both roles run the same sequence of block barriers.  Each wave runs code specialised
   // for its index, so trip counts and owned tiles are compile-time constants.
   // The state waves copy the per-head tables to LDS as three contiguous runs: the decay
@@ -1266,17 +1342,17 @@ chunk_prefill_kernel(const ChunkArgs a) {
                 "per-mode arrays adjacent in the table");
   static_assert((Lay::oWT * 2) % 16 == 0 && Lay::bL2lo % 16 == 0 && Lay::bPowL % 16 == 0 &&
                 TL::nW % 16 == 0 && TL::nL2 % 16 == 0 && (40 * M) % 16 == 0, "16-byte copies");
-  dispatch_role<C, F, D, M>(
+  dispatch_role<C, F, D, M, RM>(
       a, x, x.wave, std::make_integer_sequence<int, C / 16 + StateWaves<F, D, M>::NS>{});
 }
 
-template <int C, int F, int D, int M>
+template <int C, int F, int D, int M, bool RM>
 hipError_t chunk_kernel_attr() {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&chunk_prefill_kernel<C, F, D, M>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, Layout<C, F, D, M, C / 16>::bytes);
+        reinterpret_cast<const void*>(&chunk_prefill_kernel<C, F, D, M, RM>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, Layout<C, F, D, M, C / 16, RM>::bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -1285,30 +1361,30 @@ hipError_t chunk_kernel_attr() {
 
 // Workgroups of the output-pass kernel one CU holds at once (LDS, registers, waves), or 0 if
 // the runtime cannot say (no device).
-template <int C, int F, int D, int M>
+template <int C, int F, int D, int M, bool RM = false>
 int chunk_occupancy_t() {
-  if (chunk_kernel_attr<C, F, D, M>() != hipSuccess) return 0;
+  if (chunk_kernel_attr<C, F, D, M, RM>() != hipSuccess) return 0;
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&chunk_prefill_kernel<C, F, D, M>),
-          64 * (C / 16 + StateWaves<F, D, M>::NS), Layout<C, F, D, M, C / 16>::bytes) !=
+          &n, reinterpret_cast<const void*>(&chunk_prefill_kernel<C, F, D, M, RM>),
+          64 * (C / 16 + StateWaves<F, D, M>::NS), Layout<C, F, D, M, C / 16, RM>::bytes) !=
       hipSuccess)
     return 0;
   return n;
 }
 
-template <int C, int F, int D, int M>
+template <int C, int F, int D, int M, bool RM = false>
 hipError_t launch_chunk_t(const ChunkArgs& a, int n_wg, hipStream_t st, int kind) {
   constexpr int threads = 64 * (C / 16 + StateWaves<F, D, M>::NS);
-  constexpr int bytes = Layout<C, F, D, M, C / 16>::bytes;
+  constexpr int bytes = Layout<C, F, D, M, C / 16, RM>::bytes;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   {
-    hipError_t e = chunk_kernel_attr<C, F, D, M>();
+    hipError_t e = chunk_kernel_attr<C, F, D, M, RM>();
     if (e != hipSuccess) return e;
   }
   (void)hipGetLastError();
   prof_begin(st);
-  hipLaunchKernelGGL((chunk_prefill_kernel<C, F, D, M>), dim3(n_wg), dim3(threads), bytes, st,
+  hipLaunchKernelGGL((chunk_prefill_kernel<C, F, D, M, RM>), dim3(n_wg), dim3(threads), bytes, st,
                      a);
   prof_end(st, kind);
   return hipGetLastError();

@@ -69,7 +69,8 @@ chunk_state_kernel(const ChunkArgs a) {
     const int h = blockIdx.x - a.n_sum_wg;
     for (int r0 = 0; r0 < C / 4; r0 += RPP)
       table_run<C, M>(a.lam, a.beta, a.tables_out, a.table_bytes, a.Lt, a.seg_chunks * C, h,
-                      r0 + tid / (4 * M), tid % (4 * M));
+                      r0 + tid / (4 * M), tid % (4 * M), a.tables_half);
+    if (a.rtab_out) readout_table_run<M>(a.readout, a.rtab_out, a.rtab_bytes, h, tid, 64 * NS);
     return;
   }
   const int il = lane & 15, g = lane >> 4;

@@ -111,6 +111,8 @@ struct ChunkPrefillArgs {
   float* slots;                 // (B*H) x (segments-1) segment end states
   unsigned char* tables;
   float2 *wU, *wG, *wE;         // workspace state
+  const float2* readout;        // [H][M][M] readout matrix, or NULL (plain layer)
+  unsigned char* rtab;          // its per-head MFMA operand (readout_table_bytes(M) each)
   int B, H, N, F, D, M;
   int chunk, segments, seg_chunks;
   int reverse, out_bf16;
@@ -143,6 +145,10 @@ __host__ __device__ inline bool chunk_unresolved(float lx, float ly, int C) {
 
 bool chunk_supported(int F, int D, int M);
 long chunk_table_bytes(int chunk, int M);
+// Shapes and chunk lengths with a readout-matrix instantiation of the output pass, and the
+// bytes of one head's readout-matrix operand.
+bool chunk_rm_supported(int chunk, int F, int D, int M);
+long readout_table_bytes(int M);
 long chunk_slot_floats(int F, int D, int M);
 // Backward pass (ia_backward.hip).  States are checkpointed every kBwdCheckpoint tokens.
 constexpr int kBwdCheckpoint = 32;
@@ -181,7 +187,8 @@ int bwd_block_tokens(int F, int D, int M, int in_bf16, int out_bf16);
 size_t bwd_lds_bytes(int F, int D, int M, int in_bf16, int out_bf16, int tb, bool rev);
 hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t st);
 
-int chunk_wgs_per_cu(int chunk, int F, int D, int M);   // 0 if unknown (no device)
+int chunk_wgs_per_cu(int chunk, int F, int D, int M,
+                     bool rm = false);   // 0 if unknown (no device)
 int device_cus();                                        // compute units of the current device
 hipError_t launch_chunk_prefill(const ChunkPrefillArgs& a, hipStream_t st);
 

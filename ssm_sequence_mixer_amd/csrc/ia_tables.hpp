@@ -97,7 +97,8 @@ struct LamSmallPow {
 // Table run `run` of head h, thread t < 4M: mode m = t % M, exponent j = 4 run + t / M.
 // Written in the LDS form the prefill kernel copies verbatim: beta lam^-j in bf16 ([Re;Im]
 // rows, j in K-slot order) and in scaled fp16 (row j, modes in K-slot order), both swizzled.
-// Runs 0..3 also write the factors lam^(2i), i < 16, run 4 the factors lam^(32r); run 0 per
+// Runs 0..3 also write the factors lam^(2i), i < 16, run 4 the factors lam^(32r) (with
+// `half`, for the readout-matrix variant: lam^i and lam^(16r)); run 0 per
 // mode lam^C, sum_{j<C} beta lam^-j, the same two for the last chunk's length Lt, lam^Ls for
 // the segment length Ls, and 1/lam, the four threads of a mode splitting that work, and the
 // head's route flag (chunk_unresolved for any of its modes).  The
@@ -107,7 +108,7 @@ template <int C, int M>
 __device__ __forceinline__ void table_run(const float2* __restrict__ lam,
                                           const float2* __restrict__ beta,
                                           unsigned char* tables, long table_bytes, int Lt,
-                                          int Ls, int h, int run, int t) {
+                                          int Ls, int h, int run, int t, int half) {
   using TL = TableLayout<C, M>;
   constexpr int M2 = 2 * M;
   constexpr int JB = 4;            // exponents per run
@@ -139,8 +140,9 @@ __device__ __forceinline__ void table_run(const float2* __restrict__ lam,
   WT[soff<C>(M + m, kpos(j))] = __builtin_bit_cast(uint16_t, (__bf16)w.y);
   Wb[soff<M2>(j, kpos(m))] = __builtin_bit_cast(uint16_t, (_Float16)(w.x * wscale));
   Wb[soff<M2>(j, kpos(M + m))] = __builtin_bit_cast(uint16_t, (_Float16)(w.y * wscale));
-  if (run < 16 / JB) L2lo[j * L2S + m] = lp.pw(2.f * j);                   // lam^(2i), i = j
-  if (run == 16 / JB && jj < RUNS) L2hi[jj * M + m] = lp.pw(32.f * jj);    // lam^(32r)
+  const float fe = half ? 1.f : 2.f;   // factor exponent: lam^(2i), or lam^i with `half`
+  if (run < 16 / JB) L2lo[j * L2S + m] = lp.pw(fe * j);                    // i = j
+  if (run == 16 / JB && jj < RUNS) L2hi[jj * M + m] = lp.pw(16.f * fe * jj);   // i = 16r
   if (run != 0) return;
 
   float2* const out = reinterpret_cast<float2*>(tab);
@@ -159,6 +161,44 @@ __device__ __forceinline__ void table_run(const float2* __restrict__ lam,
       *reinterpret_cast<int*>(tab + TL::oRoute) = route;
     }
   }
+}
+
+// The readout-matrix operand of head h (ReadoutTable), by threads tid < nt (nt a multiple of
+// 64, at most 1024) of one workgroup: the power-of-two scale from the largest |Re| or |Im|
+// of R's entries (NaN entries do not count: they reach the output through the products), then
+// the four fp16 entries each R[m][n] gives.
+template <int M>
+__device__ __forceinline__ void readout_table_run(const float2* __restrict__ R,
+                                                  unsigned char* rtab, long rtab_bytes, int h,
+                                                  int tid, int nt) {
+  constexpr int M2 = 2 * M;
+  __shared__ float red[16];
+  const float2* Rh = R + (size_t)h * M * M;
+  float mx = 0.f;
+  for (int i = tid; i < M * M; i += nt) {
+    const float2 r = Rh[i];
+    mx = fmaxf(mx, fmaxf(fabsf(r.x), fabsf(r.y)));
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  mx = 0.f;
+  for (int w = 0; w < nt / 64; ++w) mx = fmaxf(mx, red[w]);
+  const float sc = pow2_scale(mx);
+  uint16_t* T = reinterpret_cast<uint16_t*>(rtab + (size_t)h * rtab_bytes);
+  for (int i = tid; i < M * M; i += nt) {
+    const int m = i / M, n = i % M;
+    const float2 r = Rh[i];
+    const uint16_t re = __builtin_bit_cast(uint16_t, (_Float16)(r.x * sc));
+    const uint16_t im = __builtin_bit_cast(uint16_t, (_Float16)(r.y * sc));
+    T[soff<M2>(n, kpos(m))] = re;
+    T[soff<M2>(n, kpos(M + m))] = im;
+    T[soff<M2>(M + n, kpos(m))] = im;
+    T[soff<M2>(M + n, kpos(M + m))] = re ^ 0x8000u;   // -Re
+  }
+  if (tid == 0)
+    *reinterpret_cast<float*>(rtab + (size_t)h * rtab_bytes + ReadoutTable<M>::oScale) = 1.f / sc;
 }
 
 }  // namespace ia

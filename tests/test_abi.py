@@ -29,6 +29,11 @@ def desc(**kw):
     return ia.make_desc(**d)
 
 
+def _has_device():
+    import torch
+    return torch.cuda.device_count() > 0
+
+
 def state(i=10):
     return ctypes.pointer(ia.IAState(addr(i).value, addr(i + 1).value, addr(i + 2).value))
 
@@ -348,6 +353,19 @@ def test_readout_variants_validation():
     B, H, M, F, D = 2, 3, 16, 32, 16
     want = (B * H * M * (F + D + 1) * 8 + 255) // 256 * 256
     assert ia.lib.ia_prefill_readout_workspace_bytes(ctypes.byref(d)) == want
+    # bf16 chunk shapes take the chunked path: its plan plus each head's readout-matrix
+    # operand (fp16 2M x 2M and its scale, 256-byte aligned).  Without a device the plans
+    # assume one workgroup per CU either way.
+    dc = desc(F=64, Dv=64, M=64)
+    extra = (3 * ((8 * 64 * 64 + 4 + 255) // 256 * 256) + 255) // 256 * 256
+    if not _has_device():
+        assert (ia.lib.ia_prefill_readout_workspace_bytes(ctypes.byref(dc))
+                == ia.lib.ia_prefill_workspace_bytes(ctypes.byref(dc)) + extra)
+    # F = Dv = 128 with M = 64: no 64-token readout-matrix instantiation
+    big = desc(F=128, Dv=128, M=64, chunk=64)
+    assert ia.lib.ia_prefill_fwd_readout(ctypes.byref(big), addr(0), addr(1), addr(2), addr(3),
+                                         addr(4), rd, state(), addr(5), addr(6), 1 << 40,
+                                         None) == 7
 
 
 def test_gated_variants_validation():
