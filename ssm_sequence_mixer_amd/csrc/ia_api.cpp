@@ -88,7 +88,7 @@ ScanWorkspace scan_workspace(const ia_desc* d, bool have_state) {
 
 struct ChunkPlan {
   int C, G, seg_chunks;
-  size_t tables_off, slots_off, state_off, rtab_off, bytes;
+  size_t tables_off, slots_off, slots_rev_off, state_off, rtab_off, bytes;
 };
 
 // Readout options of the desc's flags, in the kernels' encoding.
@@ -135,8 +135,13 @@ ChunkPlan chunk_plan(const ia_desc* d, bool rm = false) {
   p.tables_off = 0;
   p.bytes = round_up(size_t(d->H) * ia::chunk_table_bytes(p.C, d->M));
   p.slots_off = p.bytes;
-  if (p.G > 1)
-    p.bytes += round_up(size_t(seqs) * (p.G - 1) * ia::chunk_slot_floats(d->F, d->Dv, d->M) * 4);
+  const size_t slot_bytes =
+      p.G > 1 ? round_up(size_t(seqs) * (p.G - 1) * ia::chunk_slot_floats(d->F, d->Dv, d->M) * 4)
+              : 0;
+  p.bytes += slot_bytes;
+  // bidirectional: the reverse walk's slots (both walks' state-only passes run in one launch)
+  p.slots_rev_off = p.bytes;
+  if (d->flags & IA_FLAG_BIDIR) p.bytes += slot_bytes;
   // one state: the copy of a caller's initial state (several segments), or the working state
   // of heads on the fp32 route when the caller passes none
   p.state_off = p.bytes;
@@ -338,15 +343,19 @@ static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, co
     a.out_bf16 = d->out_dtype == IA_BF16;
     a.clamp = d->den_clamp;
     a.opt = kernel_opt(d);
-    if (!bidir) return launch_status(ia::launch_chunk_prefill(a, hs));
-    // Bidirectional: the forward direction writes o, the reverse direction adds onto it.
-    hipError_t e = ia::launch_chunk_prefill(a, hs);
-    if (e == hipSuccess) {
-      a.accumulate = 1;
-      a.reverse = 1;
-      e = ia::launch_chunk_prefill(a, hs);
+    // Bidirectional: both walks in one call; the forward one writes o, the reverse one adds
+    // onto it.
+    if (bidir) a.slots_rev = pl.G > 1 ? reinterpret_cast<float*>(ws + pl.slots_rev_off) : nullptr;
+    if (bidir && pl.G == 1) {
+      hipError_t e = ia::launch_chunk_prefill(a, hs);
+      if (e == hipSuccess) {
+        a.accumulate = 1;
+        a.reverse = 1;
+        e = ia::launch_chunk_prefill(a, hs);
+      }
+      return launch_status(e);
     }
-    return launch_status(e);
+    return launch_status(ia::launch_chunk_prefill(a, hs));
   }
 
   // bf16 inputs on shapes without a chunk kernel are refused rather than run 300x slower by

@@ -70,20 +70,29 @@ __global__ void __launch_bounds__(4 * M) chunk_tables_kernel(const float2* __res
 //   slot 0 <- lam^Ls (lam init) + slot 0,   slot g <- lam^Ls slot g-1 + slot g.
 // One thread per lane of a tile pair (4 Re, 4 Im values; a wave per pair, whose 16-lane rows
 // requantise it: SlotLayout) or per mode of lam eta; segments in order, the carried state in fp32.  Used
-// when the output pass would otherwise combine many slots per workgroup.
+// when the output pass would otherwise combine many slots per workgroup.  With slots_rev set
+// (a bidirectional call, no initial state) rows y >= nseq of the grid carry the reverse walk's
+// slots.
 template <int F, int D, int M>
 __global__ void __launch_bounds__(256)
-carry_slots_kernel(float* __restrict__ slots, const float2* __restrict__ U0,
+carry_slots_kernel(float* __restrict__ slots, float* __restrict__ slots_rev, int nseq,
+                   const float2* __restrict__ U0,
                    const float2* __restrict__ G0, const float2* __restrict__ E0,
                    const float2* __restrict__ lam, const unsigned char* __restrict__ tables,
                    long table_bytes, long pows_off, int H, int nslots, long slot_floats) {
   using SL = SlotLayout<F, D, M>;
   constexpr int NS = SL::NS, NFT = SL::NFT, NDT = SL::NDT, MH = M / 16;
   constexpr int PAIRS = NS * (NFT + NDT) * MH * 64;
-  const int seq = blockIdx.y, h = seq % H;
+  int seq = blockIdx.y;
+  float* walk_slots = slots;
+  if (slots_rev && seq >= nseq) {
+    seq -= nseq;
+    walk_slots = slots_rev;
+  }
+  const int h = seq % H;
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= PAIRS + M) return;
-  float* base = slots + (size_t)seq * nslots * slot_floats;
+  float* base = walk_slots + (size_t)seq * nslots * slot_floats;
   const float2* lamh = lam + (size_t)h * M;
   const float2* pows =
       reinterpret_cast<const float2*>(tables + (size_t)h * table_bytes + pows_off);
@@ -184,11 +193,13 @@ static hipError_t launch_carry_t(const ChunkPrefillArgs& p, long tb, long pows_o
                                  long slot_floats, hipStream_t st) {
   using SL = SlotLayout<F, D, M>;
   constexpr int n = SL::NS * (SL::NFT + SL::NDT) * (M / 16) * 64 + M;
+  const int seqs = p.B * p.H;
   (void)hipGetLastError();
   prof_begin(st);
-  hipLaunchKernelGGL((carry_slots_kernel<F, D, M>), dim3((n + 255) / 256, p.B * p.H), dim3(256),
-                     0, st, p.slots, p.U0, p.G0, p.E0, p.lam, p.tables, tb, pows_off, p.H, nslots,
-                     slot_floats);
+  hipLaunchKernelGGL((carry_slots_kernel<F, D, M>),
+                     dim3((n + 255) / 256, p.slots_rev ? 2 * seqs : seqs), dim3(256), 0, st,
+                     p.slots, p.slots_rev, seqs, p.U0, p.G0, p.E0, p.lam, p.tables, tb, pows_off,
+                     p.H, nslots, slot_floats);
   prof_end(st, kKindCarry);
   return hipGetLastError();
 }
@@ -335,12 +346,14 @@ long chunk_slot_floats(int F, int D, int M) {
 // carry kernel writes inclusive states first.
 constexpr int kHornerSlots = 3;
 
-// Full chunked prefill for one direction: tables; the end states of segments 0..G-2 from a
-// zero state; every segment (or, state only, the last) from its initial state, which each
-// workgroup assembles from the caller's state and the earlier segments' end states.  With
-// several segments the tables are computed by extra workgroups of the state-only launch
-// (which itself does not read them), so they cost no launch of their own on the way to the
-// output pass.
+// Full chunked prefill for one direction (or, with p.slots_rev set, both walks of a
+// bidirectional call): tables; the end states of segments 0..G-2 from a zero state; every
+// segment (or, state only, the last) from its initial state, which each workgroup assembles
+// from the caller's state and the earlier segments' end states.  With several segments the
+// tables are computed by extra workgroups of the state-only launch (which itself does not read
+// them), so they cost no launch of their own on the way to the output pass.  A bidirectional
+// call runs one state-only launch and one carry for both walks (the tables serve both), then
+// the forward output pass, which writes o, and the reverse one, which adds onto it.
 hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
   const int C = p.chunk;
   const int n_chunks = (p.N + C - 1) / C;
@@ -348,8 +361,10 @@ hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
   const int G = p.segments;
   const int seg_chunks = p.seg_chunks;
   const long tb = chunk_table_bytes(C, p.M);
+  const bool both = p.slots_rev != nullptr;
   if (G < 1 || (G - 1) * seg_chunks >= n_chunks || G * seg_chunks < n_chunks)
     return hipErrorInvalidValue;
+  if (both && (p.reverse || p.accumulate || p.U0 || !p.o)) return hipErrorInvalidValue;
 
   hipError_t e = hipSuccess;
   if (G == 1) {
@@ -367,6 +382,11 @@ hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
   a.beta = p.beta;
   a.N = p.N;
   a.H = p.H;
+  a.B = p.B;
+  // token rows of 32 bf16 features are half a cache line: order the workgroups so neighbouring
+  // heads share each line's fetch (pair_wg)
+  const bool pairs = (p.F < 64 || p.D < 64) && p.H % 2 == 0;
+  a.pair_heads = pairs;
   a.seg_chunks = seg_chunks;
   a.dir = p.reverse;
   a.out_bf16 = p.out_bf16;
@@ -396,17 +416,19 @@ hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
 
   bool inclusive = false;
   if (G > 1) {
-    // Pass 1: end state of segments 0..G-2 from a zero state.
-    // The launch also computes the tables: one more workgroup per head.
+    // Pass 1: end state of segments 0..G-2 from a zero state (both walks in one launch for a
+    // bidirectional call).  The launch also computes the tables: one more workgroup per head.
     ChunkArgs s = a;
     s.seg_first = 0;
     s.n_seg = G - 1;
     s.seg_end = p.slots;
+    s.seg_end_rev = p.slots_rev;
+    s.n_dir_wg = pair_wg_count(seqs, G - 1, pairs);
     s.tables_out = p.tables;
     s.rtab_out = p.readout ? p.rtab : nullptr;
-    s.n_sum_wg = seqs * (G - 1);
+    s.n_sum_wg = s.n_dir_wg * (both ? 2 : 1);
     s.Lt = p.N % C == 0 ? C : p.N % C;
-    const int n_wg = seqs * (G - 1) + p.H;
+    const int n_wg = s.n_sum_wg + p.H;
     e = C == 64 ? dispatch_state_fdm<64>(s, p.F, p.D, p.M, n_wg, st, kKindSummary)
                 : dispatch_state_fdm<32>(s, p.F, p.D, p.M, n_wg, st, kKindSummary);
     if (e != hipSuccess) return e;
@@ -445,7 +467,14 @@ hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
   o.fin_E = p.E1;
   o.seg_first = p.o ? 0 : G - 1;
   o.n_seg = p.o ? G : 1;
-  return go(o, seqs * o.n_seg, kKindChunk);
+  const int n_out = pair_wg_count(seqs, o.n_seg, pairs);
+  e = go(o, n_out, kKindChunk);
+  if (e != hipSuccess || !both) return e;
+  // The reverse walk: its slots, adding onto the forward walk's outputs.
+  o.dir = 1;
+  o.accumulate = 1;
+  o.seg_prev = G > 1 ? p.slots_rev : nullptr;
+  return go(o, n_out, kKindChunk);
 }
 
 }  // namespace ia

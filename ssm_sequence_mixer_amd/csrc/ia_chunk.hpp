@@ -309,6 +309,7 @@ struct ChunkArgs {
   int seg_chunks;              // chunks per segment
   int seg_first;               // first segment index handled by this launch
   int n_seg;                   // segments in this launch, per sequence
+  int pair_heads;              // workgroup order pairs heads 2j, 2j+1 (pair_wg)
   int dir;                     // 1: the walk runs from position N-1 down to 0
   int out_bf16;
   float clamp;
@@ -332,6 +333,10 @@ struct ChunkArgs {
   int seg_inclusive;                           // seg_prev[g] already holds the state entering
                                                // segment g+1 (caller state included)
   float* seg_end;
+  // State-only pass of a bidirectional call: the reverse walk's slots, and the workgroups per
+  // walk (the first n_dir_wg walk forward, the next n_dir_wg backward into seg_end_rev).
+  float* seg_end_rev;
+  int n_dir_wg;
   long slot_floats;                            // floats per slot
   int slots_per_seq;
   const unsigned char* tables;                 // per-head tables (chunk_tables_kernel)
@@ -348,6 +353,7 @@ struct ChunkArgs {
   // workgroup per head, table_run) into tables_out, Lt the last chunk's length.
   unsigned char* tables_out;
   int n_sum_wg;
+  int B;                                       // batch (sequences = B H)
   int Lt;
 };
 
@@ -413,6 +419,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rows(const ChunkArgs& a,
 template <int C>
 __device__ __forceinline__ uint32_t row_off(const ChunkArgs& a, int sn, int r, int e) {
   return (uint32_t)((a.dir ? C - 1 - r : r) * (uint32_t)sn + e) * 2u;
+}
+
+// Workgroup w of a launch over (sequence, segment) pairs, n_seg segments per sequence: the
+// plain order is w = seq n_seg + seg.  With `pairs` (H even, bf16 token rows of 32 features:
+// 64 bytes, half a 128-byte cache line shared with the neighbouring head) heads 2j and 2j+1 of
+// one segment run as workgroups 8 apart, on the same XCD (workgroups go round-robin over the 8)
+// at about the same time, so the line comes from HBM once and the second head reads it from
+// that XCD's L2: w = 16 (p / 8) + 8 (h & 1) + p % 8 for pair p = (seq / 2) n_seg + seg.  The
+// host launches pair_wg_count workgroups; false: a padding workgroup (no work).
+__host__ __device__ inline int pair_wg_count(int seqs, int n_seg, bool pairs) {
+  return pairs ? 16 * ((seqs / 2 * n_seg + 7) / 8) : seqs * n_seg;
+}
+__device__ inline bool pair_wg(int w, int seqs, int n_seg, bool pairs, int& seq, int& seg) {
+  if (!pairs) {
+    seq = w / n_seg;
+    seg = w % n_seg;
+    return true;
+  }
+  const int p = 8 * (w / 16) + w % 8;
+  if (p >= seqs / 2 * n_seg) return false;
+  seq = 2 * (p / n_seg) + (w / 8) % 2;
+  seg = p % n_seg;
+  return true;
 }
 
 // Per-workgroup context shared by the two wave roles.
@@ -1296,8 +1325,12 @@ chunk_prefill_kernel(const ChunkArgs a) {
   x.wave = tid >> 6;
   x.il = x.lane & 15;
   x.g = x.lane >> 4;
-  x.seq = blockIdx.x / a.n_seg;
-  x.seg = a.seg_first + blockIdx.x % a.n_seg;
+  {
+    int seq, seg;
+    if (!pair_wg(blockIdx.x, a.H * a.B, a.n_seg, a.pair_heads, seq, seg)) return;
+    x.seq = seq;
+    x.seg = a.seg_first + seg;
+  }
   x.b = x.seq / a.H;
   x.h = x.seq % a.H;
   x.q0 = a.q + x.b * a.sqk.b + x.h * a.sqk.h;

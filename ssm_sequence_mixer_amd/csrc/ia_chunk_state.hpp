@@ -74,8 +74,18 @@ chunk_state_kernel(const ChunkArgs a) {
     return;
   }
   const int il = lane & 15, g = lane >> 4;
-  const int seq = blockIdx.x / a.n_seg;
-  const int seg = a.seg_first + blockIdx.x % a.n_seg;
+  // Both walks of a bidirectional call in one launch (seg_end_rev set): workgroups from
+  // n_dir_wg on take the reverse walk and its slots.
+  int wg = blockIdx.x, dir = a.dir;
+  float* seg_end = a.seg_end;
+  if (a.seg_end_rev && wg >= a.n_dir_wg) {
+    wg -= a.n_dir_wg;
+    dir = 1;
+    seg_end = a.seg_end_rev;
+  }
+  int seq, seg;
+  if (!pair_wg(wg, a.H * a.B, a.n_seg, a.pair_heads, seq, seg)) return;
+  seg += a.seg_first;
   const int b = seq / a.H, h = seq % a.H;
   const int nc = a.seg_chunks;               // a full segment
   const int c_first = seg * nc;
@@ -94,7 +104,7 @@ chunk_state_kernel(const ChunkArgs a) {
   // direction.
   const int n0 = 64 * u + lane;
   const int rowK0 = n0 / VF, rowV0 = n0 / VD;
-  const int sgn = a.dir ? -1 : 1;
+  const int sgn = dir ? -1 : 1;
   const int snK = (int)a.sqk.n, snV = (int)a.sv.n;   // < 2^23 (the host checks)
   const int lofK = sgn * rowK0 * snK + 8 * (n0 % VF);
   const int lofV = sgn * rowV0 * snV + 8 * (n0 % VD);
@@ -107,7 +117,7 @@ chunk_state_kernel(const ChunkArgs a) {
   auto fetch = [&](auto R, int i) {
     constexpr int r = decltype(R)::value;
     const int t0 = chunk_of(i) * C;
-    const long long pos = a.dir ? a.N - 1 - t0 : t0;
+    const long long pos = dir ? a.N - 1 - t0 : t0;
     const uint16_t* kb = a.k + b * a.sqk.b + pos * a.sqk.n + h * a.sqk.h + lofK;
     const uint16_t* vb = a.v + b * a.sv.b + pos * a.sv.n + h * a.sv.h + lofV;
 #pragma unroll
@@ -266,7 +276,7 @@ chunk_state_kernel(const ChunkArgs a) {
 
   // ---- end state into the segment's slot (fp16 tile pairs, see SlotLayout).  The row maxima
   // of all the wave's pairs are reduced together, so their shuffles overlap.
-  float* sl = a.seg_end + ((size_t)seq * a.slots_per_seq + seg) * a.slot_floats;
+  float* sl = seg_end + ((size_t)seq * a.slots_per_seq + seg) * a.slot_floats;
   constexpr int MH = M / 16;
   constexpr int NPW = (NFT + NDT) * MH;   // tile pairs of this wave, SlotLayout order
   auto pair_vals = [&](int p, float (&re)[4], float (&im)[4]) {

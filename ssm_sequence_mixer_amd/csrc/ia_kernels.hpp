@@ -109,6 +109,8 @@ struct ChunkPrefillArgs {
   const float2 *U0, *G0, *E0;
   float2 *U1, *G1, *E1;
   float* slots;                 // (B*H) x (segments-1) segment end states
+  float* slots_rev;             // bidirectional, both walks in one call: the reverse walk's
+                                // slots (same size); NULL otherwise
   unsigned char* tables;
   float2 *wU, *wG, *wE;         // workspace state
   const float2* readout;        // [H][M][M] readout matrix, or NULL (plain layer)
