@@ -96,8 +96,19 @@ def bench_prefill(args, torch, ia, W):
     def step():
         ia.ia_prefill_fwd(desc, q, k, v, lam, beta, None, o, ws)
 
-    for _ in range(args.warmup):
-        step()
+    if args.warmup is None:
+        # Untimed steps until the GPU has run the workload for half a second: the clocks ramp
+        # up over the first ~100 ms of load, and a short warmup times the ramp, not the kernels.
+        args.warmup = 0
+        t_start = time.perf_counter()
+        while args.warmup < 3 or time.perf_counter() - t_start < 0.5:
+            for _ in range(10):
+                step()
+            args.warmup += 10
+            torch.cuda.synchronize()
+    else:
+        for _ in range(args.warmup):
+            step()
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
@@ -408,7 +419,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps before the timed ones (default: as many as run in "
+                         "half a second, at least 3; the JSON line reports the count)")
     ap.add_argument("--workload", default="1.3b", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
