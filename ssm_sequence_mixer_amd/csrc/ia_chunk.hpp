@@ -581,11 +581,33 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
     }
   __syncthreads();  // first chunk's inputs in LDS
 
+  // The second walk of a bidirectional call adds onto the first walk's outputs: with narrow
+  // values (D <= 32, a few registers) this lane's o entries of the chunk are loaded at the
+  // chunk's start, their latency covered by the chunk's work instead of stalling the output.
+  constexpr bool kEarlyO = D <= 32;
+  uint4 o_prev[kEarlyO ? TD : 1];
   for (int c = x.c_begin; c < x.c_end; ++c) {
     // v of chunk c into LDS (its readers run after the mid-chunk barrier), the next chunk's
     // loads out.
     write_v();
     if (c + 1 < x.c_end) fetch_v(c + 1);
+    if constexpr (kEarlyO) {
+      const int t = c * C + 16 * r + il;
+      if (a.accumulate && x.want_out && t < a.N) {
+        const size_t ob = x.tok_index(a, x.pos_of(a, t)) * D + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < TD; ++dt) {
+          if (a.out_bf16) {
+            const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.o) +
+                                                            ob + 16 * dt);
+            o_prev[dt] = make_uint4(w.x, w.y, 0u, 0u);
+          } else {
+            o_prev[dt] = *reinterpret_cast<const uint4*>(static_cast<const float*>(a.o) + ob +
+                                                         16 * dt);
+          }
+        }
+      }
+    }
     // Live across the mid-chunk barrier: the fp16 operand of lam^(2i) A', its per-query
     // scale and the inter-chunk denominator.
     f16x8 Af[KM];
@@ -781,7 +803,9 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
                           (accI[2] + accXd[2] * ci.z) * rd, (accI[3] + accXd[3] * ci.w) * rd};
           if (a.out_bf16) {
             if (a.accumulate) {   // the element's other direction, same lane, read then written
-              const uint2 p = *reinterpret_cast<const uint2*>(o16 + 16 * dt);
+              uint2 p;
+              if constexpr (kEarlyO) p = make_uint2(o_prev[dt].x, o_prev[dt].y);
+              else p = *reinterpret_cast<const uint2*>(o16 + 16 * dt);
               val[0] += __uint_as_float(p.x << 16);
               val[1] += __uint_as_float(p.x & 0xffff0000u);
               val[2] += __uint_as_float(p.y << 16);
@@ -790,7 +814,9 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
             *reinterpret_cast<uint2*>(o16 + 16 * dt) = pack4_bf16(val[0], val[1], val[2], val[3]);
           } else {
             if (a.accumulate) {
-              const float4 p = *reinterpret_cast<const float4*>(o32 + 16 * dt);
+              float4 p;
+              if constexpr (kEarlyO) p = __builtin_bit_cast(float4, o_prev[dt]);
+              else p = *reinterpret_cast<const float4*>(o32 + 16 * dt);
               val[0] += p.x; val[1] += p.y; val[2] += p.z; val[3] += p.w;
             }
             *reinterpret_cast<float4*>(o32 + 16 * dt) = make_float4(val[0], val[1], val[2], val[3]);
