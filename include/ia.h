@@ -122,9 +122,9 @@ ia_status ia_state_init(const ia_desc* desc, ia_state* st, void* stream);
  * is invalid or has no kernel (bf16 shapes outside the chunked path).  The workspace holds the
  * per-head tables, the per-segment state summaries and one state (the caller's initial state
  * copied there when several segments run, or the fp32 route's working state) of the chunked
- * scan, or a state for state-less fp32 calls.  Its contents need no initialisation
- * and are scratch between calls.  (The bidirectional layer accumulates its two directions in
- * o itself, in o's dtype.) */
+ * scan (for IA_FLAG_BIDIR a second set of summaries, the reverse walk's), or a state for
+ * state-less fp32 calls.  Its contents need no initialisation and are scratch between calls.
+ * (The bidirectional layer accumulates its two directions in o itself, in o's dtype.) */
 size_t ia_prefill_workspace_bytes(const ia_desc* desc);
 
 /* Host-side check of the modes for `desc` (lambda_host: [H][M] complex64 in HOST memory).
