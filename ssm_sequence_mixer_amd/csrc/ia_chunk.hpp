@@ -174,15 +174,24 @@ __device__ __forceinline__ float pow2_scale(float mx) {
   return ldexpf(1.f, 14 - e);
 }
 
+// Sum (max) of a value over lanes l, l^16, l^32, l^48 (one column of the four 16-lane rows), in
+// every lane, by two cross-row swaps on the VALU instead of LDS permutes: permlane16_swap(v, v)
+// returns v with rows 1, 3 replaced by rows 0, 2 and v with rows 0, 2 replaced by rows 1, 3,
+// whose sum pairs rows 0+1 and 2+3; permlane32_swap(v, v) likewise pairs the two halves.  Each
+// lane adds the same two values in the same order as with shuffles, so results are unchanged.
 __device__ __forceinline__ float xor_sum16_32(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+  const unsigned b = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  const unsigned c = __float_as_uint(__uint_as_float(p[0]) + __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 __device__ __forceinline__ float xor_max16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
+  const unsigned b = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  const unsigned c = __float_as_uint(fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1])));
+  const auto q = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
 // ---------------------------------------------------------------- wave roles
