@@ -14,6 +14,10 @@ Two independent implementations live here:
 ``scan_gated``/``prefill_gated`` run the layer with selective writing and memory decay (a
 write gate and a decay gate per token), pinned in ``tests/test_oracle.py``.
 
+``block.py`` (numpy) holds the pieces at the layer's edges in the model block (short
+convolutions, RoPE, the RMS normalisation of the SSM input, the output gate), pinned in
+``tests/test_oracle_block.py``.
+
 ``scan_bwd``/``prefill_bwd`` give the gradients of the same layer (``ia_oracle_scan_bwd``:
 reverse-mode differentiation of the recurrence, every forward state kept), pinned to the
 forward oracle by finite differences in ``tests/test_oracle_bwd.py``.
