@@ -319,6 +319,84 @@ def bench_decode(torch, ia, W, batches=(1, 16, 64), steps=256):
     return res
 
 
+def bench_block(torch, ia, W, inp, layers=24, reps=20):
+    """The block's edges on the prefill workload (ia_block_prologue with a 4-tap convolution,
+    RoPE and the normalisation; ia_block_gate on o), and a graph-captured decode of a stack of
+    `layers` blocks at batch 1 (per layer: prologue of one token, ia_decode_step with identity
+    features, gate), the 1.3B-shaped layer's sizes."""
+    sh = inp["shape"]
+    B, H, N, F, D, M = sh["B"], sh["H"], sh["N"], sh["F"], sh["D"], sh["M"]
+    tb = torch.bfloat16
+    q, k, v = (torch.from_numpy(inp[n]).to(tb).cuda() for n in "qkv")
+    rng = np.random.default_rng(11)
+    conv = tuple(torch.from_numpy((rng.standard_normal((H, C, 4)) * 0.4).astype(np.float32)).cuda()
+                 for C in (F, F, D))
+    norm = (torch.ones((H, F + D), device="cuda"), torch.zeros((H, F + D), device="cuda"))
+    desc = ia.make_desc(B, H, N, F, D, M, ia.IA_BF16, ia.IA_BF16)
+    p = ia.block_params(conv, 1e4, 0, norm)
+    fq, fk, vo = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    g = torch.randn((B, N, H, D), device="cuda").to(tb)
+    o = torch.randn((B, N, H, D), device="cuda").to(tb)
+    out = torch.empty_like(o)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps * 1e3
+    pro_us = timed(lambda: ia.ia_block_prologue(desc, p, q, k, v, None, None, fq, fk, vo))
+    gate_us = timed(lambda: ia.ia_block_gate(desc, o, g, out))
+    pro_bytes = 2.0 * B * N * H * (2 * F + D) * 2
+    gate_bytes = 3.0 * B * N * H * D * 2
+    res = {"scope": "1.3B-shaped prefill workload, bf16",
+           "prologue_us": pro_us, "prologue_hbm_frac": pro_bytes / (pro_us * 1e-6) / HBM_PEAK,
+           "gate_us": gate_us, "gate_hbm_frac": gate_bytes / (gate_us * 1e-6) / HBM_PEAK}
+
+    # stack decode, batch 1: `layers` blocks with their own states, two tokens per replay (the
+    # convolution state alternates between two buffers)
+    Bd = 1
+    wl = W.decode(Bd, steps=2, prefix=32)
+    lam = torch.from_numpy(wl["lam"]).cuda()
+    beta = torch.from_numpy(wl["beta"]).cuda()
+    dd = ia.make_desc(Bd, H, 1, F, D, M, ia.IA_BF16, ia.IA_BF16, identity_features=True)
+    d1 = ia.make_desc(Bd, H, 1, F, D, M, ia.IA_BF16, ia.IA_BF16)
+    xs = [tuple(torch.randn((Bd, 1, H, C), device="cuda").to(tb) for C in (F, F, D))
+          for _ in range(2)]
+    gts = [torch.randn((Bd, 1, H, D), device="cuda").to(tb) for _ in range(2)]
+    L = []
+    for _ in range(layers):
+        st = ia.new_state(Bd, H, M, F, D)
+        cs = [torch.zeros((Bd, H, 3, 2 * F + D), device="cuda") for _ in range(2)]
+        feats = tuple(torch.empty((Bd, 1, H, C), device="cuda", dtype=tb) for C in (F, F, D))
+        ot = torch.empty((Bd, 1, H, D), device="cuda", dtype=tb)
+        L.append((st, cs, feats, ot))
+    ps = [ia.block_params(conv, 1e4, pos, norm) for pos in (32, 33)]
+
+    def run_stack():
+        for t in range(2):
+            x, gt = xs[t], gts[t]
+            for st, cs, feats, ot in L:
+                ia.ia_block_prologue(d1, ps[t], x[0], x[1], x[2], cs[t], cs[1 - t], *feats)
+                ia.ia_decode_step(dd, feats[0][:, 0], feats[1][:, 0], feats[2][:, 0], lam, beta,
+                                  st, ot[:, 0])
+                ia.ia_block_gate(d1, ot, gt, ot)
+    run_stack()
+    torch.cuda.synchronize()
+    stack_us = _graph_us(torch, run_stack, 2)
+    res.update({"stack_layers": layers, "stack_batch": Bd,
+                "stack_graph_us_per_token": stack_us,
+                "stack_graph_us_per_layer": stack_us / layers,
+                "stack_scope": "per layer: prologue (conv state, RoPE, norm) of one token, "
+                               "ia_decode_step with identity features, gate; one hipGraph"})
+    return res
+
+
 FP32_PEAK = 157.3e12        # fp32 vector FLOP/s, MI355X
 
 
@@ -454,6 +532,9 @@ def main():
     bwd = None
     if not args.no_backward:
         bwd = bench_backward(torch, ia, pf["inp"], bidir=pf["cfg"]["bidirectional"])
+    block = None
+    if not args.no_decode and args.workload == "1.3b":
+        block = bench_block(torch, ia, W, pf["inp"])
     cpu = None if args.no_cpu else cpu_baseline(pf["inp"], pf["cfg"]["bidirectional"])
     line = {
         "metric": "IA layer fwd tokens/s (prefill) + decode step latency; % of MFMA/HBM roofline",
@@ -475,6 +556,7 @@ def main():
         "kernels_ms": pf["kernels_ms"],
         "readout_matrix": pf["readout"],
         "decode": dec,
+        "block_edges": block,
         "backward": bwd,
         "cpu_baseline": cpu,
     }

@@ -324,6 +324,61 @@ ia_status ia_decode_step_readout(const ia_desc* desc,
                                  const void* lambda, const void* beta, const void* readout,
                                  ia_state* st, void* o_t, void* stream);
 
+/* The block's edges around the layer: the pieces the pages place before and after the IA
+ * mixer in their model blocks, named there without formulas.  Readings taken:
+ *   - short convolutions on q, k (summary §5.3, the ablations of §B.1) and on v: causal and
+ *     depthwise along time, conv_width taps per channel (tap 0 on the current token), the
+ *     conv_width-1 raw tokens before token 0 taken from conv_state_in (zeros if NULL), then
+ *     SiLU (x * sigmoid(x));
+ *   - RoPE on q and k (the language models of summary §A.1): feature pairs (2i, 2i+1) turned
+ *     by the angle p * rope_base^(-2i/F) at position p = pos0 + n;
+ *   - the feature map elu+1 on q and k, after the two steps above;
+ *   - the SSM input z = [phi(k), v] (F + Dv entries) normalised per token and head, as the
+ *     episode page's implementation details describe it (an RMS normalisation with a learned
+ *     per-head bias): z' = g * z / sqrt(mean(z^2) + norm_eps) + b;
+ *   - the output gate (summary §3.3): out = o * SiLU(gate), gate the caller's projection.
+ * ia_block_prologue writes phi(q'), phi(k')'s and v''s normalised values: the inputs of
+ * ia_prefill_fwd / ia_decode_step with IA_FLAG_IDENTITY_FEATURES.  It streams each input once
+ * (one workgroup per 64 tokens of a (b,h) slice).  For decode, call it with N = 1 and the
+ * token's position in pos0, carrying the convolution state from call to call.
+ *   desc          B, H, N, F, Dv and in_dtype (inputs and outputs; M unused but checked).
+ *   p->conv_width 0 (no convolution, no SiLU) to 8; p->conv_q, p->conv_k [H][F][conv_width],
+ *                 p->conv_v [H][Dv][conv_width] float, tap tau weighting the token tau steps
+ *                 back, required with conv_width > 0.
+ *   p->rope_base  > 0: RoPE with that base; 0: none.  p->pos0 >= 0, pos0 + N - 1 (the
+ *                 last position) at most 2^31 - 1.
+ *   p->norm_gain, p->norm_bias  [H][F+Dv] float each, both or neither (no normalisation);
+ *                 p->norm_eps >= 0.
+ *   q, k, v       raw [B][N][H][F|Dv] in_dtype, read only.
+ *   conv_state_in, conv_state_out  [B][H][conv_width-1][2F+Dv] float (q, k, v channels side
+ *                 by side, oldest token first): the raw tokens before token 0, and those
+ *                 ending at token N-1 (NULL: none); distinct buffers; unused for
+ *                 conv_width <= 1.
+ *   fq, fk, vo    [B][N][H][F|Dv] in_dtype outputs.
+ * Parameter arrays 16-byte aligned; outputs must not overlap any input or each other.
+ * Errors as ia_prefill_fwd, IA_ERR_UNSUPPORTED for conv_width > 8 or a token row of one
+ * tensor (H * max(F, Dv) elements) of 16 MiB or more, IA_ERR_DOMAIN for a negative or
+ * non-finite rope_base or norm_eps, or positions outside 0 .. 2^31 - 1. */
+typedef struct ia_block_params {
+  int conv_width;
+  const void *conv_q, *conv_k, *conv_v;
+  float rope_base;
+  int pos0;
+  const void *norm_gain, *norm_bias;
+  float norm_eps;
+} ia_block_params;
+
+ia_status ia_block_prologue(const ia_desc* desc, const ia_block_params* p,
+                            const void* q, const void* k, const void* v,
+                            const void* conv_state_in, void* conv_state_out,
+                            void* fq, void* fk, void* vo, void* stream);
+
+/* out = o * SiLU(gate) elementwise over [B][N][H][Dv] (desc->N = 1 for a decode step's o_t);
+ * o, gate and out in desc->out_dtype; out may be o itself (in place), and must not overlap
+ * gate.  Errors as ia_prefill_fwd. */
+ia_status ia_block_gate(const ia_desc* desc, const void* o, const void* gate, void* out,
+                        void* stream);
+
 /* Selective writing and memory decay.  Input-dependent gates, computed by the caller for every
  * token, control what the memory stores and how fast it forgets (the optional enhancement of
  * [summary §3.3], ablated as selective vs non-selective in [summary §B.3, Table 7]).  The pages

@@ -28,16 +28,20 @@ def powers(lam, n):
     return np.exp(np.asarray(n, dtype=np.float64)[:, None] * np.log(lam)[None, :])
 
 
-def layer(q, k, v, lam, beta, clamp=1e-6, readout=None, gates=None):
+def layer(q, k, v, lam, beta, clamp=1e-6, readout=None, gates=None, features_given=False):
     """One (b,h) slice from zero state: q, k [N,F]; v [N,D]; lam, beta [M]; ``readout`` an
     optional complex [M, M] mode-mixing matrix R (a -> a R before the readout; None = identity);
     ``gates`` an optional pair (w, a) of per-token write and decay gates [N] (a > 0): token s
     then enters with weight w_s and is carried to t by prod_{s<u<=t} a_u lambda^(t-s), the
-    product taken as exp(sum of log a_u).
+    product taken as exp(sum of log a_u); ``features_given``: q and k are already the features
+    phi(q), phi(k) (the layer behind the block's input prologue).
 
     Returns (o [N,D], num [N,D], den [N]).
     """
-    fq, fk = feature(q), feature(k)
+    if features_given:
+        fq, fk = np.asarray(q, dtype=np.float64), np.asarray(k, dtype=np.float64)
+    else:
+        fq, fk = feature(q), feature(k)
     v = np.asarray(v, dtype=np.float64)
     beta = np.asarray(beta, dtype=np.complex128)
     N = fq.shape[0]

@@ -51,6 +51,14 @@ class IAState(ctypes.Structure):
     _fields_ = [("U", ctypes.c_void_p), ("Gamma", ctypes.c_void_p), ("eta", ctypes.c_void_p)]
 
 
+class IABlockParams(ctypes.Structure):
+    _fields_ = [("conv_width", ctypes.c_int), ("conv_q", ctypes.c_void_p),
+                ("conv_k", ctypes.c_void_p), ("conv_v", ctypes.c_void_p),
+                ("rope_base", ctypes.c_float), ("pos0", ctypes.c_int),
+                ("norm_gain", ctypes.c_void_p), ("norm_bias", ctypes.c_void_p),
+                ("norm_eps", ctypes.c_float)]
+
+
 class IAError(RuntimeError):
     def __init__(self, status: int, where: str, detail: str = ""):
         self.status = status
@@ -110,6 +118,11 @@ lib.ia_prefill_fwd_gated.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _S, _P, _P,
 lib.ia_prefill_fwd_gated.restype = ctypes.c_int
 lib.ia_decode_step_gated.argtypes = [_D, _P, _P, _P, _P, _P, _P, _P, _S, _P, _P]
 lib.ia_decode_step_gated.restype = ctypes.c_int
+lib.ia_block_prologue.argtypes = [_D, ctypes.POINTER(IABlockParams), _P, _P, _P, _P, _P, _P,
+                                  _P, _P, _P]
+lib.ia_block_prologue.restype = ctypes.c_int
+lib.ia_block_gate.argtypes = [_D, _P, _P, _P, _P]
+lib.ia_block_gate.restype = ctypes.c_int
 lib.ia_status_string.argtypes = [ctypes.c_int]
 lib.ia_status_string.restype = ctypes.c_char_p
 lib.ia_last_launch_error.argtypes = []
@@ -119,10 +132,11 @@ EXPORTS = ("ia_state_init", "ia_prefill_workspace_bytes", "ia_check_lambda", "ia
            "ia_prefill_fwd_strided", "ia_prefill_fwd_noalloc", "ia_prefill_fwd_profiled", "ia_decode_step",
            "ia_prefill_bwd_workspace_bytes", "ia_prefill_bwd", "ia_prefill_readout_workspace_bytes",
            "ia_prefill_fwd_readout", "ia_decode_step_readout", "ia_prefill_gated_workspace_bytes",
-           "ia_prefill_fwd_gated", "ia_decode_step_gated", "ia_status_string",
-           "ia_last_launch_error")
+           "ia_prefill_fwd_gated", "ia_decode_step_gated", "ia_block_prologue", "ia_block_gate",
+           "ia_status_string", "ia_last_launch_error")
 KIND_NAMES = {0: "fill", 1: "scan", 2: "tables", 3: "summary", 4: "carry", 5: "chunk",
-              6: "decode", 7: "bwd_forward", 8: "bwd_reverse", 9: "bwd_reduce", 10: "copy"}
+              6: "decode", 7: "bwd_forward", 8: "bwd_reverse", 9: "bwd_reduce", 10: "copy",
+              11: "block"}
 
 
 def make_desc(B, H, N, F, Dv, M, in_dtype=IA_BF16, out_dtype=IA_F32, den_clamp=1e-6,
@@ -328,6 +342,35 @@ def ia_decode_step(desc: IADesc, q_t, k_t, v_t, lam, beta, state, o_t, stream=No
            "ia_decode_step")
 
 
+def block_params(conv=None, rope_base=0.0, pos0=0, norm=None, eps=1e-6) -> IABlockParams:
+    """conv: (wq [H,F,W], wk [H,F,W], wv [H,Dv,W]) float32 device tensors or None; norm:
+    (gain [H,F+Dv], bias [H,F+Dv]) float32 device tensors or None.  The structure holds their
+    addresses only: the caller keeps the tensors alive while it is in use."""
+    if conv is not None:
+        _dense(*conv)
+    if norm is not None:
+        _dense(*norm)
+    W = 0 if conv is None else int(conv[0].shape[2])
+    return IABlockParams(W, *(None if conv is None else c.data_ptr() for c in
+                              (conv or (None,) * 3)), float(rope_base), int(pos0),
+                         *(None if norm is None else t.data_ptr() for t in (norm or (None,) * 2)),
+                         float(eps))
+
+
+def ia_block_prologue(desc: IADesc, params: IABlockParams, q, k, v, state_in, state_out, fq, fk,
+                      vo, stream=None):
+    _dense(q, k, v, state_in, state_out, fq, fk, vo)
+    _check(lib.ia_block_prologue(ctypes.byref(desc), ctypes.byref(params), _ptr(q), _ptr(k),
+                                 _ptr(v), _ptr(state_in), _ptr(state_out), _ptr(fq), _ptr(fk),
+                                 _ptr(vo), _stream(stream)), "ia_block_prologue")
+
+
+def ia_block_gate(desc: IADesc, o, gate, out, stream=None):
+    _dense(o, gate, out)
+    _check(lib.ia_block_gate(ctypes.byref(desc), _ptr(o), _ptr(gate), _ptr(out),
+                             _stream(stream)), "ia_block_gate")
+
+
 # ---------------------------------------------------------------- conveniences (torch alloc)
 
 def new_state(B, H, M, F, Dv, device="cuda", stream=None, zero=True):
@@ -406,6 +449,39 @@ def decode(q_t, k_t, v_t, lam, beta, state, out_dtype=None,
     else:
         ia_decode_step(desc, q_t, k_t, v_t, lam, beta, state, o_t, stream)
     return o_t
+
+
+def block_prologue(q, k, v, conv=None, state=None, rope_base=0.0, pos0=0, norm=None, eps=1e-6,
+                   M=16, stream=None):
+    """Run ia_block_prologue on raw q, k [B,N,H,F], v [B,N,H,Dv] (bf16 or float32); returns
+    (phi(q'), phi(k') and v' after the normalisation, the new convolution state or None), the
+    inputs of the layer with identity_features=True.  state: [B,H,W-1,2F+Dv] float32."""
+    import torch
+    B, N, H, F = q.shape
+    Dv = v.shape[3]
+    desc = make_desc(B, H, N, F, Dv, M, dtype_code(q.dtype), dtype_code(q.dtype))
+    p = block_params(conv, rope_base, pos0, norm, eps)
+    fq, fk, vo = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st_out = None
+    if conv is not None and p.conv_width > 1:
+        st_out = torch.empty((B, H, p.conv_width - 1, 2 * F + Dv), dtype=torch.float32,
+                             device=q.device)
+    ia_block_prologue(desc, p, q, k, v, state, st_out, fq, fk, vo, stream)
+    return fq, fk, vo, st_out
+
+
+def block_gate(o, gate, out=None, stream=None):
+    """out = o * SiLU(gate) (ia_block_gate); o, gate [B,N,H,Dv] (or [B,H,Dv]) of one dtype."""
+    import torch
+    if o.dim() == 3:
+        B, H, Dv = o.shape
+        N = 1
+    else:
+        B, N, H, Dv = o.shape
+    desc = make_desc(B, H, N, 16, Dv, 16, dtype_code(o.dtype), dtype_code(o.dtype))
+    out = torch.empty_like(o) if out is None else out
+    ia_block_gate(desc, o, gate, out, stream)
+    return out
 
 
 def prefill_bwd(q, k, v, lam, beta, dO, state0=None, den_clamp=1e-6, no_den=False,

@@ -19,9 +19,10 @@ struct Range {
   uintptr_t lo, hi;  // [lo, hi)
 };
 
+// The bytes [p, p + bytes) of an argument; a NULL argument covers nothing.
 Range rng(const void* p, size_t bytes) {
   uintptr_t a = reinterpret_cast<uintptr_t>(p);
-  return {a, a + bytes};
+  return {a, p ? a + bytes : a};
 }
 
 bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
@@ -635,6 +636,86 @@ ia_status ia_decode_step_readout(const ia_desc* d, const void* q_t, const void* 
                                  const void* readout, ia_state* st, void* o_t, void* stream) {
   if (!readout) return IA_ERR_NULL;
   return decode_impl(d, q_t, k_t, v_t, lambda, beta, readout, st, o_t, stream);
+}
+
+// ---------------------------------------------------------------- the block's edges
+
+ia_status ia_block_prologue(const ia_desc* d, const ia_block_params* p, const void* q,
+                            const void* k, const void* v, const void* conv_state_in,
+                            void* conv_state_out, void* fq, void* fk, void* vo, void* stream) {
+  ia_status s = check_desc(d, true);
+  if (s != IA_OK) return s;
+  if (!p || !q || !k || !v || !fq || !fk || !vo) return IA_ERR_NULL;
+  const int W = p->conv_width;
+  if (W < 0 || W > ia::kMaxConvTaps) return IA_ERR_UNSUPPORTED;
+  if (W > 0 && (!p->conv_q || !p->conv_k || !p->conv_v)) return IA_ERR_NULL;
+  if (!(std::isfinite(p->rope_base) && p->rope_base >= 0.f) || p->pos0 < 0 ||
+      (long long)p->pos0 + d->N - 1 > 2147483647LL)
+    return IA_ERR_DOMAIN;
+  if ((long long)d->H * (d->F > d->Dv ? d->F : d->Dv) * esize(d->in_dtype) >= (1LL << 24))
+    return IA_ERR_UNSUPPORTED;   // a token's row of one tensor: under 16 MiB
+  if ((p->norm_gain == nullptr) != (p->norm_bias == nullptr)) return IA_ERR_NULL;
+  if (p->norm_gain && !(std::isfinite(p->norm_eps) && p->norm_eps >= 0.f)) return IA_ERR_DOMAIN;
+  const void* params[] = {p->conv_q, p->conv_k, p->conv_v, p->norm_gain, p->norm_bias};
+  for (const void* x : {q, k, v, static_cast<const void*>(fq), static_cast<const void*>(fk),
+                        static_cast<const void*>(vo)})
+    if (!aligned16(x)) return IA_ERR_ALIGN;
+  for (const void* x : params)
+    if (x && !aligned16(x)) return IA_ERR_ALIGN;
+  const bool st_used = W > 1;
+  if (st_used && ((conv_state_in && !aligned16(conv_state_in)) ||
+                  (conv_state_out && !aligned16(conv_state_out))))
+    return IA_ERR_ALIGN;
+  const size_t tok = size_t(d->B) * d->N * d->H, es = esize(d->in_dtype);
+  const size_t st_bytes = st_used ? size_t(d->B) * d->H * (W - 1) * (2 * d->F + d->Dv) * 4 : 0;
+  const Range ins[] = {rng(q, tok * d->F * es), rng(k, tok * d->F * es), rng(v, tok * d->Dv * es),
+                       rng(p->conv_q, W ? size_t(d->H) * d->F * W * 4 : 0),
+                       rng(p->conv_k, W ? size_t(d->H) * d->F * W * 4 : 0),
+                       rng(p->conv_v, W ? size_t(d->H) * d->Dv * W * 4 : 0),
+                       rng(p->norm_gain, p->norm_gain ? size_t(d->H) * (d->F + d->Dv) * 4 : 0),
+                       rng(p->norm_bias, p->norm_bias ? size_t(d->H) * (d->F + d->Dv) * 4 : 0),
+                       rng(st_used ? conv_state_in : nullptr, st_bytes)};
+  const Range outs[] = {rng(fq, tok * d->F * es), rng(fk, tok * d->F * es),
+                        rng(vo, tok * d->Dv * es),
+                        rng(st_used ? conv_state_out : nullptr, st_bytes)};
+  for (const Range& a : outs)
+    for (const Range& r : ins)
+      if (overlap(a, r)) return IA_ERR_ALIAS;
+  for (int i = 0; i < 4; ++i)
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return IA_ERR_ALIAS;
+  ia::BlockArgs a{};
+  a.q = q; a.k = k; a.v = v; a.fq = fq; a.fk = fk; a.vo = vo;
+  a.conv_q = static_cast<const float*>(p->conv_q);
+  a.conv_k = static_cast<const float*>(p->conv_k);
+  a.conv_v = static_cast<const float*>(p->conv_v);
+  a.state_in = st_used ? static_cast<const float*>(conv_state_in) : nullptr;
+  a.state_out = st_used ? static_cast<float*>(conv_state_out) : nullptr;
+  a.norm_gain = static_cast<const float*>(p->norm_gain);
+  a.norm_bias = static_cast<const float*>(p->norm_bias);
+  a.norm_eps = p->norm_eps;
+  a.rope_base = p->rope_base;
+  a.B = d->B; a.H = d->H; a.N = d->N; a.F = d->F; a.D = d->Dv;
+  a.conv_width = W;
+  a.pos0 = p->pos0;
+  a.bf16 = d->in_dtype == IA_BF16;
+  return launch_status(ia::launch_block_prologue(a, static_cast<hipStream_t>(stream)));
+}
+
+ia_status ia_block_gate(const ia_desc* d, const void* o, const void* g, void* out,
+                        void* stream) {
+  ia_status s = check_desc(d, true);
+  if (s != IA_OK) return s;
+  if (!o || !g || !out) return IA_ERR_NULL;
+  for (const void* x : {o, g, static_cast<const void*>(out)})
+    if (!aligned16(x)) return IA_ERR_ALIGN;
+  const size_t n = size_t(d->B) * d->N * d->H * d->Dv;
+  const size_t bytes = n * esize(d->out_dtype);
+  const Range ro = rng(o, bytes), rg = rng(g, bytes), rout = rng(out, bytes);
+  // out may be o itself (each element is read, then written, by one thread), not part of it
+  if (overlap(rout, rg) || (overlap(rout, ro) && out != o)) return IA_ERR_ALIAS;
+  return launch_status(ia::launch_block_gate(o, g, out, n, d->out_dtype == IA_BF16,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 ia_status ia_prefill_fwd_profiled(const ia_desc* d, const void* q, const void* k,

@@ -21,6 +21,7 @@ enum LaunchKind {
   kKindBwdReverse = 8,   // backward: reverse sweep
   kKindBwdReduce = 9,    // backward: sum of the mode groups' partials
   kKindCopy = 10,        // copy of the caller's initial state into the workspace
+  kKindBlock = 11,       // the block's edges: input prologue, output gate
 };
 
 // While set (only inside ia_prefill_fwd_profiled), every launch records events[2i] before
@@ -72,6 +73,24 @@ struct DecodeArgs {
   const float2* readout = nullptr;   // [H][M][M] readout matrix, or NULL
   const float *wgate = nullptr, *dgate = nullptr;   // [B][H] write / decay gates, or NULL
 };
+
+// The block's edges (ia_block.hip): short convolutions of up to kMaxConvTaps taps.
+constexpr int kMaxConvTaps = 8;
+
+struct BlockArgs {
+  const void *q, *k, *v;          // raw [B][N][H][F|D], bf16 or f32 (bf16 flag)
+  void *fq, *fk, *vo;             // outputs, same dtype and layout
+  const float *conv_q, *conv_k, *conv_v;   // [H][F|D][W] or NULL (conv_width 0)
+  const float* state_in;          // [B][H][W-1][2F+D] raw tokens before token 0, or NULL
+  float* state_out;               // the same for the last W-1 tokens, or NULL
+  const float *norm_gain, *norm_bias;      // [H][F+D] or NULL
+  float norm_eps, rope_base;
+  int B, H, N, F, D, conv_width, pos0, bf16;
+};
+hipError_t launch_block_prologue(const BlockArgs& a, hipStream_t st);
+// out = o * SiLU(g) over n elements (n even), bf16 or f32
+hipError_t launch_block_gate(const void* o, const void* g, void* out, size_t n, int bf16,
+                             hipStream_t st);
 
 struct ScanArgs {
   const void *q, *k, *v;   // element strides sqk (q and k) and sv; o dense

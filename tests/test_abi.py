@@ -368,6 +368,46 @@ def test_readout_variants_validation():
                                          None) == 7
 
 
+def test_block_edges_validation():
+    d = desc(Dv=32)   # B=2, H=3, N=70, F=32, Dv=32
+    W = 4
+
+    def params(**kw):
+        p = dict(conv_width=W, conv_q=addr(20).value, conv_k=addr(21).value,
+                 conv_v=addr(22).value, rope_base=1e4, pos0=0, norm_gain=addr(23).value,
+                 norm_bias=addr(24).value, norm_eps=1e-6)
+        p.update(kw)
+        return ia.IABlockParams(**p)
+
+    def pro(p=None, d=d, q=0, st_in=None, st_out=None, fq=5, fk=6, vo=7):
+        return ia.lib.ia_block_prologue(
+            ctypes.byref(d), None if p is False else ctypes.byref(p or params()),
+            None if q is None else addr(q),
+            addr(1), addr(2), st_in, st_out, addr(fq), addr(fk), addr(vo), None)
+    assert pro(False) == 1
+    assert pro(params(conv_width=9)) == 7
+    assert pro(params(conv_width=-1)) == 7
+    assert pro(params(conv_k=None)) == 1
+    assert pro(params(rope_base=-1.0)) == 6
+    assert pro(params(rope_base=float("nan"))) == 6
+    assert pro(params(pos0=-3)) == 6
+    assert pro(params(pos0=2**31 - 69)) == 6       # the last position past 2^31 - 1
+    assert pro(params(norm_bias=None)) == 1
+    assert pro(params(norm_eps=-1.0)) == 6
+    assert pro(params(conv_q=addr(20, 4).value)) == 4
+    assert pro(q=None) == 1
+    assert pro(fq=1) == 5                          # an output over an input
+    assert pro(fk=5) == 5                          # two outputs over each other
+    assert pro(st_in=addr(30), st_out=addr(30)) == 5   # the two states in one buffer
+    assert pro(st_out=addr(1)) == 5                # the new state over k
+    assert pro(d=desc(Dv=32, N=0)) == 2
+    g = lambda o, gt, out: ia.lib.ia_block_gate(ctypes.byref(d), o, gt, out, None)
+    assert g(addr(0), None, addr(2)) == 1
+    assert g(addr(0), addr(1), addr(1)) == 5      # out over the gate
+    assert g(addr(0), addr(1), addr(0, 64)) == 5  # out over part of o
+    assert g(addr(0, 8), addr(1), addr(2)) == 4
+
+
 def test_gated_variants_validation():
     d = desc(Dv=32)
     g = lambda *a: ia.lib.ia_prefill_fwd_gated(ctypes.byref(d), *a)
