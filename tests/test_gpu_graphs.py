@@ -136,3 +136,91 @@ def test_graph_backward(bidir):
     torch.cuda.synchronize()
     eager = [x.clone() for x in outs]
     _replays(torch, run, reset, outs, eager)
+
+
+def test_graph_block_decode_stack():
+    """Three blocks decoding four tokens in one graph.  Per token and layer: the prologue
+    (convolution state in two buffers taken in turn, RoPE at the token's position, the
+    normalisation), ia_decode_step with identity features, the output gate in place; layer
+    l > 0 takes layer l-1's gated output as its v, so the graph's order matters.  Replays equal
+    the eager run exactly; the eager run equals the oracle's prologue, brute-force layer and
+    gate, layer by layer on that layer's own inputs."""
+    import torch
+    import oracle.block as blk
+    from oracle import brute
+    from helpers import TOL_BF16, host, report, rowrel
+    ia = _ia()
+    B, H, F, D, M, Wd, L, T, pos0 = 2, 4, 64, 64, 16, 4, 3, 4, 7
+    tb = torch.bfloat16
+    r = np.random.default_rng(730)
+    bf = lambda *shape, s=1.0: W.round_bf16((r.standard_normal(shape) * s).astype(np.float32))
+    qs = [bf(T, B, 1, H, F, s=0.5) for _ in range(L)]
+    ks = [bf(T, B, 1, H, F, s=0.5) for _ in range(L)]
+    v0 = bf(T, B, 1, H, D)
+    gs = [bf(T, B, 1, H, D) for _ in range(L)]
+    convs = [tuple((r.standard_normal((H, C, Wd)) * 0.4).astype(np.float32) for C in (F, F, D))
+             for _ in range(L)]
+    norms = [((1 + 0.1 * r.standard_normal((H, F + D))).astype(np.float32),
+              (0.05 * r.standard_normal((H, F + D))).astype(np.float32)) for _ in range(L)]
+    lams = [W.s4d_lin(np.exp(r.uniform(np.log(1e-3), np.log(1e-1), H)), M) for _ in range(L)]
+    beta = np.ones((H, M), np.complex64)
+
+    qd = [[dev(x[t], tb) for t in range(T)] for x in qs]
+    kd = [[dev(x[t], tb) for t in range(T)] for x in ks]
+    gd = [[dev(x[t], tb) for t in range(T)] for x in gs]
+    v0d = [dev(v0[t], tb) for t in range(T)]
+    convd = [tuple(dev(w) for w in c) for c in convs]    # kept alive: params hold addresses
+    normd = [tuple(dev(w) for w in n) for n in norms]
+    ps = [[ia.block_params(convd[l], 1e4, pos0 + t, normd[l]) for t in range(T)]
+          for l in range(L)]
+    lamd, betad = [dev(x) for x in lams], dev(beta)
+    d1 = ia.make_desc(B, H, 1, F, D, M, ia.IA_BF16, ia.IA_BF16)
+    dd = ia.make_desc(B, H, 1, F, D, M, ia.IA_BF16, ia.IA_BF16, identity_features=True)
+    sts = [ia.new_state(B, H, M, F, D) for _ in range(L)]
+    cs = [[torch.zeros((B, H, Wd - 1, 2 * F + D), device="cuda") for _ in range(2)]
+          for _ in range(L)]
+    feats = [tuple(torch.empty((B, 1, H, C), dtype=tb, device="cuda") for C in (F, F, D))
+             for _ in range(L)]
+    out = [torch.empty((T, B, 1, H, D), dtype=tb, device="cuda") for _ in range(L)]
+
+    def run():
+        for t in range(T):
+            for l in range(L):
+                vin = v0d[t] if l == 0 else out[l - 1][t]
+                fq, fk, vo = feats[l]
+                ia.ia_block_prologue(d1, ps[l][t], qd[l][t], kd[l][t], vin, cs[l][t % 2],
+                                     cs[l][1 - t % 2], fq, fk, vo)
+                ia.ia_decode_step(dd, fq[:, 0], fk[:, 0], vo[:, 0], lamd[l], betad, sts[l],
+                                  out[l][t][:, 0])
+                ia.ia_block_gate(d1, out[l][t], gd[l][t], out[l][t])
+
+    def reset():
+        for l in range(L):
+            for x in sts[l] + tuple(cs[l]):
+                x.zero_()
+
+    tag("graph block decode stack")
+    reset()
+    run()
+    torch.cuda.synchronize()
+    outputs = out + [x for l in range(L) for x in sts[l] + tuple(cs[l])]
+    eager = [x.clone() for x in outputs]
+
+    # the oracle, layer by layer on the layer's inputs as the GPU saw them
+    seq = lambda a: np.transpose(a[:, :, 0], (1, 0, 2, 3)).astype(np.float64)   # [B,T,H,C]
+    for l in range(L):
+        vin = v0 if l == 0 else host(out[l - 1])
+        fq, fk, vo, _ = blk.prologue(seq(qs[l]), seq(ks[l]), seq(vin), convs[l], None, 1e4,
+                                     pos0, norms[l], 1e-6)
+        o = np.empty((B, T, H, D))
+        for b in range(B):
+            for h in range(H):
+                o[b, :, h] = brute.layer(fq[b, :, h], fk[b, :, h], vo[b, :, h], lams[l][h],
+                                         beta[h], features_given=True)[0]
+        err = rowrel(seq(host(out[l])), blk.gate(o, seq(gs[l])))
+        report(f"graph block decode stack, layer {l}", err)
+        assert err < TOL_BF16, (l, err)
+
+    for x in out:
+        x.zero_()
+    _replays(torch, run, reset, outputs, eager)
