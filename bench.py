@@ -386,14 +386,25 @@ def bench_block(torch, ia, W, inp, layers=24, reps=20):
                 ia.ia_decode_step(dd, feats[0][:, 0], feats[1][:, 0], feats[2][:, 0], lam, beta,
                                   st, ot[:, 0])
                 ia.ia_block_gate(d1, ot, gt, ot)
+    def run_stack_fused():
+        for t in range(2):
+            x, gt = xs[t], gts[t]
+            for st, cs, feats, ot in L:
+                ia.ia_block_decode_step(d1, ps[t], x[0][:, 0], x[1][:, 0], x[2][:, 0], cs[t],
+                                        cs[1 - t], gt[:, 0], lam, beta, st, ot[:, 0])
     run_stack()
+    run_stack_fused()
     torch.cuda.synchronize()
     stack_us = _graph_us(torch, run_stack, 2)
+    fused_us = _graph_us(torch, run_stack_fused, 2)
     res.update({"stack_layers": layers, "stack_batch": Bd,
                 "stack_graph_us_per_token": stack_us,
                 "stack_graph_us_per_layer": stack_us / layers,
                 "stack_scope": "per layer: prologue (conv state, RoPE, norm) of one token, "
-                               "ia_decode_step with identity features, gate; one hipGraph"})
+                               "ia_decode_step with identity features, gate; one hipGraph",
+                "stack_fused_graph_us_per_token": fused_us,
+                "stack_fused_graph_us_per_layer": fused_us / layers,
+                "stack_fused_scope": "the same with one ia_block_decode_step per layer"})
     return res
 
 

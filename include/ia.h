@@ -379,6 +379,28 @@ ia_status ia_block_prologue(const ia_desc* desc, const ia_block_params* p,
 ia_status ia_block_gate(const ia_desc* desc, const void* o, const void* gate, void* out,
                         void* stream);
 
+/* One decode step of the whole block, in one kernel: ia_block_prologue of the token (N = 1,
+ * position p->pos0, the convolution state carried from conv_state_in to conv_state_out), the
+ * layer's step as ia_decode_step on its outputs, then the output gate, out = o * SiLU(gate).
+ * The prologue's outputs stay in fp32 inside the kernel (ia_block_prologue followed by
+ * ia_decode_step rounds them to in_dtype in between), so the two routes agree to rounding.
+ * For callers that run a stack of layers token by token, one kernel node per layer.
+ *   desc        as ia_decode_step (N unused); IA_FLAG_BIDIR and IA_FLAG_IDENTITY_FEATURES
+ *               return IA_ERR_UNSUPPORTED (the prologue applies the feature map itself).
+ *   p           as ia_block_prologue, pos0 the token's position.
+ *   q_t, k_t, v_t  raw [B][H][F|Dv] in_dtype.
+ *   conv_state_in, conv_state_out  as ia_block_prologue ([B][H][conv_width-1][2F+Dv] float).
+ *   gate_t      [B][H][Dv] in_dtype, or NULL for no gate.
+ *   lambda, beta, st  as ia_decode_step; st updated in place.
+ *   out_t       [B][H][Dv] out_dtype.
+ * Outputs (out_t, the state, conv_state_out) must not overlap any input or each other.
+ * Errors as ia_decode_step and ia_block_prologue. */
+ia_status ia_block_decode_step(const ia_desc* desc, const ia_block_params* p,
+                               const void* q_t, const void* k_t, const void* v_t,
+                               const void* conv_state_in, void* conv_state_out,
+                               const void* gate_t, const void* lambda, const void* beta,
+                               ia_state* st, void* out_t, void* stream);
+
 /* Selective writing and memory decay.  Input-dependent gates, computed by the caller for every
  * token, control what the memory stores and how fast it forgets (the optional enhancement of
  * [summary §3.3], ablated as selective vs non-selective in [summary §B.3, Table 7]).  The pages

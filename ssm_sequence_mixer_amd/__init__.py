@@ -123,6 +123,9 @@ lib.ia_block_prologue.argtypes = [_D, ctypes.POINTER(IABlockParams), _P, _P, _P,
 lib.ia_block_prologue.restype = ctypes.c_int
 lib.ia_block_gate.argtypes = [_D, _P, _P, _P, _P]
 lib.ia_block_gate.restype = ctypes.c_int
+lib.ia_block_decode_step.argtypes = [_D, ctypes.POINTER(IABlockParams), _P, _P, _P, _P, _P, _P,
+                                     _P, _P, _S, _P, _P]
+lib.ia_block_decode_step.restype = ctypes.c_int
 lib.ia_status_string.argtypes = [ctypes.c_int]
 lib.ia_status_string.restype = ctypes.c_char_p
 lib.ia_last_launch_error.argtypes = []
@@ -133,7 +136,7 @@ EXPORTS = ("ia_state_init", "ia_prefill_workspace_bytes", "ia_check_lambda", "ia
            "ia_prefill_bwd_workspace_bytes", "ia_prefill_bwd", "ia_prefill_readout_workspace_bytes",
            "ia_prefill_fwd_readout", "ia_decode_step_readout", "ia_prefill_gated_workspace_bytes",
            "ia_prefill_fwd_gated", "ia_decode_step_gated", "ia_block_prologue", "ia_block_gate",
-           "ia_status_string", "ia_last_launch_error")
+           "ia_block_decode_step", "ia_status_string", "ia_last_launch_error")
 KIND_NAMES = {0: "fill", 1: "scan", 2: "tables", 3: "summary", 4: "carry", 5: "chunk",
               6: "decode", 7: "bwd_forward", 8: "bwd_reverse", 9: "bwd_reduce", 10: "copy",
               11: "block"}
@@ -369,6 +372,15 @@ def ia_block_gate(desc: IADesc, o, gate, out, stream=None):
     _dense(o, gate, out)
     _check(lib.ia_block_gate(ctypes.byref(desc), _ptr(o), _ptr(gate), _ptr(out),
                              _stream(stream)), "ia_block_gate")
+
+
+def ia_block_decode_step(desc: IADesc, params: IABlockParams, q_t, k_t, v_t, state_in,
+                         state_out, gate_t, lam, beta, state, out_t, stream=None):
+    _dense(q_t, k_t, v_t, state_in, state_out, gate_t, lam, beta, out_t)
+    _check(lib.ia_block_decode_step(ctypes.byref(desc), ctypes.byref(params), _ptr(q_t),
+                                    _ptr(k_t), _ptr(v_t), _ptr(state_in), _ptr(state_out),
+                                    _ptr(gate_t), _ptr(lam), _ptr(beta), _state(state),
+                                    _ptr(out_t), _stream(stream)), "ia_block_decode_step")
 
 
 # ---------------------------------------------------------------- conveniences (torch alloc)

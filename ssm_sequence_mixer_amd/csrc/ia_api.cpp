@@ -640,41 +640,57 @@ ia_status ia_decode_step_readout(const ia_desc* d, const void* q_t, const void* 
 
 // ---------------------------------------------------------------- the block's edges
 
+// Checks of ia_block_params shared by the prologue and the fused decode step: the tap count,
+// the weight and normalisation arrays, RoPE's base and the positions pos0 .. pos0 + n - 1.
+static ia_status check_block_params(const ia_block_params* p, long n) {
+  const int W = p->conv_width;
+  if (W < 0 || W > ia::kMaxConvTaps) return IA_ERR_UNSUPPORTED;
+  if (W > 0 && (!p->conv_q || !p->conv_k || !p->conv_v)) return IA_ERR_NULL;
+  if (!(std::isfinite(p->rope_base) && p->rope_base >= 0.f) || p->pos0 < 0 ||
+      (long long)p->pos0 + n - 1 > 2147483647LL)
+    return IA_ERR_DOMAIN;
+  if ((p->norm_gain == nullptr) != (p->norm_bias == nullptr)) return IA_ERR_NULL;
+  if (p->norm_gain && !(std::isfinite(p->norm_eps) && p->norm_eps >= 0.f)) return IA_ERR_DOMAIN;
+  for (const void* x : {p->conv_q, p->conv_k, p->conv_v, p->norm_gain, p->norm_bias})
+    if (x && !aligned16(x)) return IA_ERR_ALIGN;
+  return IA_OK;
+}
+
+// The parameter arrays of p (five ranges) and the convolution state's bytes.
+static void block_param_ranges(const ia_desc* d, const ia_block_params* p, Range* r) {
+  const int W = p->conv_width;
+  r[0] = rng(p->conv_q, W ? size_t(d->H) * d->F * W * 4 : 0);
+  r[1] = rng(p->conv_k, W ? size_t(d->H) * d->F * W * 4 : 0);
+  r[2] = rng(p->conv_v, W ? size_t(d->H) * d->Dv * W * 4 : 0);
+  r[3] = rng(p->norm_gain, p->norm_gain ? size_t(d->H) * (d->F + d->Dv) * 4 : 0);
+  r[4] = rng(p->norm_bias, p->norm_bias ? size_t(d->H) * (d->F + d->Dv) * 4 : 0);
+}
+static size_t conv_state_bytes(const ia_desc* d, int W) {
+  return W > 1 ? size_t(d->B) * d->H * (W - 1) * (2 * d->F + d->Dv) * 4 : 0;
+}
+
 ia_status ia_block_prologue(const ia_desc* d, const ia_block_params* p, const void* q,
                             const void* k, const void* v, const void* conv_state_in,
                             void* conv_state_out, void* fq, void* fk, void* vo, void* stream) {
   ia_status s = check_desc(d, true);
   if (s != IA_OK) return s;
   if (!p || !q || !k || !v || !fq || !fk || !vo) return IA_ERR_NULL;
-  const int W = p->conv_width;
-  if (W < 0 || W > ia::kMaxConvTaps) return IA_ERR_UNSUPPORTED;
-  if (W > 0 && (!p->conv_q || !p->conv_k || !p->conv_v)) return IA_ERR_NULL;
-  if (!(std::isfinite(p->rope_base) && p->rope_base >= 0.f) || p->pos0 < 0 ||
-      (long long)p->pos0 + d->N - 1 > 2147483647LL)
-    return IA_ERR_DOMAIN;
+  if ((s = check_block_params(p, d->N)) != IA_OK) return s;
   if ((long long)d->H * (d->F > d->Dv ? d->F : d->Dv) * esize(d->in_dtype) >= (1LL << 24))
     return IA_ERR_UNSUPPORTED;   // a token's row of one tensor: under 16 MiB
-  if ((p->norm_gain == nullptr) != (p->norm_bias == nullptr)) return IA_ERR_NULL;
-  if (p->norm_gain && !(std::isfinite(p->norm_eps) && p->norm_eps >= 0.f)) return IA_ERR_DOMAIN;
-  const void* params[] = {p->conv_q, p->conv_k, p->conv_v, p->norm_gain, p->norm_bias};
+  const int W = p->conv_width;
   for (const void* x : {q, k, v, static_cast<const void*>(fq), static_cast<const void*>(fk),
                         static_cast<const void*>(vo)})
     if (!aligned16(x)) return IA_ERR_ALIGN;
-  for (const void* x : params)
-    if (x && !aligned16(x)) return IA_ERR_ALIGN;
   const bool st_used = W > 1;
   if (st_used && ((conv_state_in && !aligned16(conv_state_in)) ||
                   (conv_state_out && !aligned16(conv_state_out))))
     return IA_ERR_ALIGN;
   const size_t tok = size_t(d->B) * d->N * d->H, es = esize(d->in_dtype);
-  const size_t st_bytes = st_used ? size_t(d->B) * d->H * (W - 1) * (2 * d->F + d->Dv) * 4 : 0;
-  const Range ins[] = {rng(q, tok * d->F * es), rng(k, tok * d->F * es), rng(v, tok * d->Dv * es),
-                       rng(p->conv_q, W ? size_t(d->H) * d->F * W * 4 : 0),
-                       rng(p->conv_k, W ? size_t(d->H) * d->F * W * 4 : 0),
-                       rng(p->conv_v, W ? size_t(d->H) * d->Dv * W * 4 : 0),
-                       rng(p->norm_gain, p->norm_gain ? size_t(d->H) * (d->F + d->Dv) * 4 : 0),
-                       rng(p->norm_bias, p->norm_bias ? size_t(d->H) * (d->F + d->Dv) * 4 : 0),
-                       rng(st_used ? conv_state_in : nullptr, st_bytes)};
+  const size_t st_bytes = conv_state_bytes(d, W);
+  Range ins[9] = {rng(q, tok * d->F * es), rng(k, tok * d->F * es), rng(v, tok * d->Dv * es)};
+  block_param_ranges(d, p, ins + 3);
+  ins[8] = rng(st_used ? conv_state_in : nullptr, st_bytes);
   const Range outs[] = {rng(fq, tok * d->F * es), rng(fk, tok * d->F * es),
                         rng(vo, tok * d->Dv * es),
                         rng(st_used ? conv_state_out : nullptr, st_bytes)};
@@ -700,6 +716,63 @@ ia_status ia_block_prologue(const ia_desc* d, const ia_block_params* p, const vo
   a.pos0 = p->pos0;
   a.bf16 = d->in_dtype == IA_BF16;
   return launch_status(ia::launch_block_prologue(a, static_cast<hipStream_t>(stream)));
+}
+
+ia_status ia_block_decode_step(const ia_desc* d, const ia_block_params* p, const void* q_t,
+                               const void* k_t, const void* v_t, const void* conv_state_in,
+                               void* conv_state_out, const void* gate_t, const void* lambda,
+                               const void* beta, ia_state* st, void* out_t, void* stream) {
+  ia_status s = check_desc(d, false);
+  if (s != IA_OK) return s;
+  if (d->flags & (IA_FLAG_BIDIR | IA_FLAG_IDENTITY_FEATURES)) return IA_ERR_UNSUPPORTED;
+  if (!p || !q_t || !k_t || !v_t || !lambda || !beta || !out_t) return IA_ERR_NULL;
+  if ((s = check_state(d, st)) != IA_OK) return s;
+  if ((s = check_block_params(p, 1)) != IA_OK) return s;
+  const int W = p->conv_width;
+  for (const void* x : {q_t, k_t, v_t, lambda, beta, static_cast<const void*>(out_t)})
+    if (!aligned16(x)) return IA_ERR_ALIGN;
+  if (gate_t && !aligned16(gate_t)) return IA_ERR_ALIGN;
+  const bool st_used = W > 1;
+  if (st_used && ((conv_state_in && !aligned16(conv_state_in)) ||
+                  (conv_state_out && !aligned16(conv_state_out))))
+    return IA_ERR_ALIGN;
+  const size_t bh = size_t(d->B) * d->H, es = esize(d->in_dtype);
+  const size_t st_bytes = conv_state_bytes(d, W);
+  Range ins[12] = {rng(q_t, bh * d->F * es), rng(k_t, bh * d->F * es),
+                   rng(v_t, bh * d->Dv * es), rng(gate_t, gate_t ? bh * d->Dv * es : 0),
+                   rng(lambda, size_t(d->H) * d->M * 8), rng(beta, size_t(d->H) * d->M * 8),
+                   rng(st_used ? conv_state_in : nullptr, st_bytes)};
+  block_param_ranges(d, p, ins + 7);
+  const Range outs[] = {rng(out_t, bh * d->Dv * esize(d->out_dtype)),
+                        rng(st->U, state_u_bytes(d)), rng(st->Gamma, state_g_bytes(d)),
+                        rng(st->eta, state_e_bytes(d)),
+                        rng(st_used ? conv_state_out : nullptr, st_bytes)};
+  for (const Range& a : outs)
+    for (const Range& r : ins)
+      if (overlap(a, r)) return IA_ERR_ALIAS;
+  for (int i = 0; i < 5; ++i)
+    for (int j = i + 1; j < 5; ++j)
+      if (overlap(outs[i], outs[j])) return IA_ERR_ALIAS;
+  ia::DecodeArgs a{q_t, k_t, v_t, static_cast<const float2*>(lambda),
+                   static_cast<const float2*>(beta), static_cast<float2*>(st->U),
+                   static_cast<float2*>(st->Gamma), static_cast<float2*>(st->eta), out_t,
+                   d->B, d->H, d->F, d->Dv, d->M, d->in_dtype == IA_BF16,
+                   d->out_dtype == IA_BF16, d->den_clamp};
+  a.opt = kernel_opt(d);
+  a.block = 1;
+  a.blk.conv_q = static_cast<const float*>(p->conv_q);
+  a.blk.conv_k = static_cast<const float*>(p->conv_k);
+  a.blk.conv_v = static_cast<const float*>(p->conv_v);
+  a.blk.state_in = st_used ? static_cast<const float*>(conv_state_in) : nullptr;
+  a.blk.state_out = st_used ? static_cast<float*>(conv_state_out) : nullptr;
+  a.blk.norm_gain = static_cast<const float*>(p->norm_gain);
+  a.blk.norm_bias = static_cast<const float*>(p->norm_bias);
+  a.blk.norm_eps = p->norm_eps;
+  a.blk.rope_base = p->rope_base;
+  a.blk.pos = p->pos0;
+  a.blk.conv_width = W;
+  a.blk.gate = gate_t;
+  return launch_status(ia::launch_decode_step(a, static_cast<hipStream_t>(stream)));
 }
 
 ia_status ia_block_gate(const ia_desc* d, const void* o, const void* g, void* out,

@@ -15,6 +15,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "ia_block_step.hpp"
 #include "ia_device.hpp"
 #include "ia_kernels.hpp"
 
@@ -24,10 +25,6 @@ namespace {
 
 constexpr int kBlockTokens = 64;   // tokens per workgroup
 constexpr int kNormGroup = 16;     // tokens whose normalisation sums are reduced together
-
-__device__ __forceinline__ float silu_f(float y) {
-  return y * __builtin_amdgcn_rcpf(1.f + __expf(-y));
-}
 
 // A channel pair: bf16 as one packed word, fp32 as two words.
 template <bool BF>
@@ -135,7 +132,7 @@ block_prologue_kernel(const BlockArgs a) {
   // from its own position (in fp64, reduced to [0, 1) turns), so that a call's split into
   // pieces does not change it
   const bool rope = a.rope_base > 0.f && kind != 2;
-  const double rev = rope ? pow((double)a.rope_base, -2.0 * i / F) * 0.15915494309189535 : 0.0;
+  const double rev = rope ? rope_rate(a.rope_base, i, F) : 0.0;
   const float inv_e = 1.f / (float)(F + D);
   const bool summed = active && kind != 0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = (blockDim.x + 63) >> 6;
@@ -174,10 +171,9 @@ block_prologue_kernel(const BlockArgs a) {
         a1 = silu_f(s1);
       }
       if (kind != 2) {
-        if (rope) {   // the hardware sine and cosine take turns
-          const float tr = (float)__builtin_amdgcn_fract((p0 + (double)j) * rev);
-          const float rs = __builtin_amdgcn_sinf(tr), rc = __builtin_amdgcn_cosf(tr);
-          const float r0 = a0 * rc - a1 * rs, r1 = a0 * rs + a1 * rc;
+        if (rope) {
+          const float2 cs = rope_cs(p0 + (double)j, rev);
+          const float r0 = a0 * cs.x - a1 * cs.y, r1 = a0 * cs.y + a1 * cs.x;
           a0 = r0;
           a1 = r1;
         }

@@ -61,6 +61,18 @@ inline RowStrides dense_strides(int N, int H, int X) {
   return RowStrides{(long long)N * H * X, (long long)H * X, X};
 }
 
+// One token of the block's prologue and the output gate around a decode step
+// (ia_block_decode_step): q, k, v of the step are then the raw projections.
+struct BlockStepArgs {
+  const float *conv_q, *conv_k, *conv_v;   // [H][F|D][W] or NULL (conv_width 0)
+  const float* state_in;                   // [B][H][W-1][2F+D] raw tokens before, or NULL
+  float* state_out;                        // the same ending at this token, or NULL
+  const float *norm_gain, *norm_bias;      // [H][F+D] or NULL
+  float norm_eps, rope_base;               // rope_base 0: no RoPE
+  int pos, conv_width;                     // the token's position; taps (0..kMaxConvTaps)
+  const void* gate;                        // [B][H][D] in the input dtype, or NULL
+};
+
 struct DecodeArgs {
   const void *q, *k, *v;
   const float2 *lam, *beta;
@@ -72,6 +84,8 @@ struct DecodeArgs {
   int opt;   // kOptNoDen | kOptIdentity
   const float2* readout = nullptr;   // [H][M][M] readout matrix, or NULL
   const float *wgate = nullptr, *dgate = nullptr;   // [B][H] write / decay gates, or NULL
+  int block = 0;          // q, k, v raw: the block prologue runs first (blk), the gate after
+  BlockStepArgs blk{};
 };
 
 // The block's edges (ia_block.hip): short convolutions of up to kMaxConvTaps taps.

@@ -6,6 +6,7 @@
 // the O(M(R+d)) per-step decode; episode page, "Key Components and Derivation", for the
 // feature map and the matrix form Fq U^T Gamma / Fq U^T eta), written once in ia_scan.hpp.
 // One workgroup owns one (b,h) slice.
+#include "ia_block_step.hpp"
 #include "ia_device.hpp"
 #include "ia_kernels.hpp"
 #include "ia_scan.hpp"
@@ -21,8 +22,10 @@ using StepSmem = SeqSmem<kStepWaves, kMaxDim, kMaxDim, MM, true>;
 
 // ---------------------------------------------------------------- kernels
 
-// Decode: one step for every (b,h).  grid = B*H.  BF: bf16 inputs; M <= MM.
-template <bool BF, int MM>
+// Decode: one step for every (b,h).  grid = B*H.  BF: bf16 inputs; M <= MM.  PRO: q, k, v
+// are the raw projections, the block's prologue (blk) makes the step's inputs and its output
+// gate scales the readout.
+template <bool BF, int MM, bool PRO>
 __global__ void __launch_bounds__(kStepThreads)
 decode_step_kernel(const void* __restrict__ q, const void* __restrict__ k,
                    const void* __restrict__ v, const float2* __restrict__ lam,
@@ -30,18 +33,31 @@ decode_step_kernel(const void* __restrict__ q, const void* __restrict__ k,
                    float2* __restrict__ G, float2* __restrict__ E, void* __restrict__ o,
                    int H, int F, int D, int M, int out_bf16, float clamp,
                    int opt, const float2* __restrict__ rmat, const float* __restrict__ wgate,
-                   const float* __restrict__ dgate) {
+                   const float* __restrict__ dgate, const BlockStepArgs blk) {
   __shared__ StepSmem<MM> s;
+  __shared__ float s_red[kStepWaves];
+  __shared__ __align__(16) float s_w[PRO ? 3 * kMaxDim * kMaxConvTaps : 4];
   const int bh = blockIdx.x;
   const int h = bh % H;
   seq_load_modes(s, lam, beta, h, M);
-  seq_load_token<BF>(s, q, k, v, (size_t)bh * F, (size_t)bh * D, F, D, opt);
+  if constexpr (PRO) {
+    static_assert(2 * kStepThreads >= kMaxDim + kMaxDim / 2, "two channel pairs per thread");
+    constexpr int NW4 = (3 * kMaxDim * kMaxConvTaps / 4 + kStepThreads - 1) / kStepThreads;
+    BlockToken<2, NW4> tok;
+    tok.template load<BF>(blk, q, k, v, bh, h, F, D);
+    tok.finish(blk, bh, F, D, s.fq, s.fk, s.v, s_w, s_red);
+  } else {
+    seq_load_token<BF>(s, q, k, v, (size_t)bh * F, (size_t)bh * D, F, D, opt);
+  }
   __syncthreads();
   seq_step(s, U + (size_t)bh * M * F, G + (size_t)bh * M * D, E + (size_t)bh * M, F, D, M,
            rmat ? rmat + (size_t)h * M * M : nullptr, wgate ? wgate[bh] : 1.f,
            dgate ? dgate[bh] : 1.f);
-  for (int j = threadIdx.x; j < D; j += kStepThreads)
-    store_out(o, (size_t)bh * D + j, readout(seq_num(s, j), s.den, clamp, opt), out_bf16);
+  for (int j = threadIdx.x; j < D; j += kStepThreads) {
+    float y = readout(seq_num(s, j), s.den, clamp, opt);
+    if (PRO && blk.gate) y *= silu_f(load_t<BF>(blk.gate, (size_t)bh * D + j));
+    store_out(o, (size_t)bh * D + j, y, out_bf16);
+  }
 }
 
 // Decode with the whole state of a slice in flight at once.  grid = B*H; NT threads per slice.
@@ -50,7 +66,8 @@ decode_step_kernel(const void* __restrict__ q, const void* __restrict__ k,
 // Gamma rows, so its inputs are two entries each of phi(q), phi(k) and v.  Every row load is
 // issued before any arithmetic; a[m] needs all of row m (a reduction over the F/2 lanes that
 // share it), then the Gamma rows, whose column sums over rows go through LDS in a fixed order.
-template <int F, int D, int MM, bool BF>
+// PRO: as decode_step_kernel; the prologue's loads go out before the state's.
+template <int F, int D, int MM, bool BF, bool PRO>
 __global__ void __launch_bounds__(512)
 decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
                         const void* __restrict__ v, const float2* __restrict__ lam,
@@ -58,7 +75,7 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
                         float2* __restrict__ G, float2* __restrict__ E, void* __restrict__ o,
                         int H, int M, int out_bf16, float clamp, int opt,
                         const float2* __restrict__ rmat, const float* __restrict__ wgate,
-                        const float* __restrict__ dgate) {
+                        const float* __restrict__ dgate, const BlockStepArgs blk) {
   constexpr int NT = 512, NWV = NT / 64;
   constexpr int RU = F / 2, RD = D / 2;
   static_assert(RU <= 64 && RD <= 64 && NT % RU == 0 && NT % RD == 0, "row width");
@@ -68,6 +85,8 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
   __shared__ float2 s_rp[NT];   // partial sums of a R
   __shared__ float s_num[SD][D];
   __shared__ float s_den[NWV];
+  __shared__ float s_pro[PRO ? 2 * F + D : 1];   // phi(q'), then the normalised phi(k'), v'
+  __shared__ __align__(16) float s_w[PRO ? (2 * F + D) * kMaxConvTaps : 4];   // the taps
 
   const int bh = blockIdx.x, h = bh % H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -76,33 +95,60 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
   float4* Gb = reinterpret_cast<float4*>(G + (size_t)bh * M * D);
   float2* Eb = E + (size_t)bh * M;
   // this token's inputs first: the state loads below stay in flight behind them
-  const float2 kk = load_pair_t<BF>(k, (size_t)bh * F + 2 * pu);
-  const float2 qq = load_pair_t<BF>(q, (size_t)bh * F + 2 * pu);
-  const float2 vv = load_pair_t<BF>(v, (size_t)bh * D + 2 * pd);
-  // with gates, lambda_m and beta_m of this slice's step times its decay and write gate
-  const float wg = wgate ? wgate[bh] : 1.f, dg = dgate ? dgate[bh] : 1.f;
-  float2 e = make_float2(0.f, 0.f);
-  if (tid < M) {
-    const float2 l = lam[(size_t)h * M + tid], bt = beta[(size_t)h * M + tid];
-    s_lam[tid] = make_float2(dg * l.x, dg * l.y);
-    s_beta[tid] = make_float2(wg * bt.x, wg * bt.y);
-    e = Eb[tid];
+  float2 kk, qq, vv;
+  BlockToken<1, ((2 * F + D) * kMaxConvTaps / 4 + NT - 1) / NT> tok;
+  float gt = 0.f;
+  if constexpr (PRO) {
+    static_assert(NT >= F + D / 2, "one channel pair per thread");
+    tok.template load<BF>(blk, q, k, v, bh, h, F, D);
+    // the gate of output tid (tid < D), loaded unconditionally from a valid address (q's own
+    // row without a gate) so that no branch holds the loads above waiting
+    gt = blk.gate ? load_t<BF>(blk.gate, (size_t)bh * D + min(tid, D - 1))
+                  : load_t<BF>(q, (size_t)bh * F + min(tid, F - 1));
+  } else {
+    kk = load_pair_t<BF>(k, (size_t)bh * F + 2 * pu);
+    qq = load_pair_t<BF>(q, (size_t)bh * F + 2 * pu);
+    vv = load_pair_t<BF>(v, (size_t)bh * D + 2 * pd);
   }
+  // lambda, beta, eta and the gates: loads without branches (indices clamped, lambda standing
+  // in for a missing gate) so that none of them waits before the state's loads go out
+  const int mt = min(tid, M - 1);
+  const float2 lv = lam[(size_t)h * M + mt], bv = beta[(size_t)h * M + mt];
+  float2 e = Eb[mt];   // used by threads tid < M only
+  const float wgv = *(wgate ? wgate + bh : reinterpret_cast<const float*>(lam));
+  const float dgv = *(dgate ? dgate + bh : reinterpret_cast<const float*>(lam));
 
+  // the whole state, U and Gamma rows together; unconditional (rows past M read row M-1 and
+  // go unused) so that the compiler keeps them here, ahead of any arithmetic, and waits for
+  // the earlier loads only where those are used
   float4 u[IU], g[ID];
 #pragma unroll
-  for (int i = 0; i < IU; ++i) {
-    const int m = ru + SU * i;
-    if (m < M) u[i] = Ub[(size_t)m * RU + pu];
-  }
+  for (int i = 0; i < IU; ++i) u[i] = Ub[(size_t)min(ru + SU * i, M - 1) * RU + pu];
 #pragma unroll
-  for (int i = 0; i < ID; ++i) {
-    const int m = rd + SD * i;
-    if (m < M) g[i] = Gb[(size_t)m * RD + pd];
+  for (int i = 0; i < ID; ++i) g[i] = Gb[(size_t)min(rd + SD * i, M - 1) * RD + pd];
+  float fk0, fk1, fq0, fq1, v0, v1;
+  if constexpr (PRO) {
+    tok.finish(blk, bh, F, D, s_pro, s_pro + F, s_pro + 2 * F, s_w, s_den);
+    fq0 = s_pro[2 * pu];
+    fq1 = s_pro[2 * pu + 1];
+    fk0 = s_pro[F + 2 * pu];
+    fk1 = s_pro[F + 2 * pu + 1];
+    v0 = s_pro[2 * F + 2 * pd];
+    v1 = s_pro[2 * F + 2 * pd + 1];
+  } else {
+    fk0 = feat(kk.x, opt);
+    fk1 = feat(kk.y, opt);
+    fq0 = feat(qq.x, opt);
+    fq1 = feat(qq.y, opt);
+    v0 = vv.x;
+    v1 = vv.y;
   }
-  const float fk0 = feat(kk.x, opt), fk1 = feat(kk.y, opt);
-  const float fq0 = feat(qq.x, opt), fq1 = feat(qq.y, opt);
-  const float v0 = vv.x, v1 = vv.y;
+  // with gates, lambda_m and beta_m of this slice's step times its decay and write gate
+  const float wg = wgate ? wgv : 1.f, dg = dgate ? dgv : 1.f;
+  if (tid < M) {
+    s_lam[tid] = make_float2(dg * lv.x, dg * lv.y);
+    s_beta[tid] = make_float2(wg * bv.x, wg * bv.y);
+  }
   __syncthreads();   // lam, beta
 
   if (tid < M) {
@@ -185,7 +231,9 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
     float den = 0.f;
 #pragma unroll
     for (int w = 0; w < NWV; ++w) den += s_den[w];
-    store_out(o, (size_t)bh * D + tid, readout(n, den, clamp, opt), out_bf16);
+    float y = readout(n, den, clamp, opt);
+    if (PRO && blk.gate) y *= silu_f(gt);
+    store_out(o, (size_t)bh * D + tid, y, out_bf16);
   }
 }
 
@@ -260,26 +308,29 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int F, int D, bool BF>
+template <int F, int D, bool BF, bool PRO>
 static void launch_decode_rows_t(const DecodeArgs& a, hipStream_t st) {
   // The per-thread row registers are sized for M <= 64 or M <= 128: the smaller set lets two
   // workgroups share a CU.
   if (a.M <= 64)
-    hipLaunchKernelGGL((decode_step_rows_kernel<F, D, 64, BF>), dim3(a.B * a.H), dim3(512), 0,
-                       st, a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H, a.M,
-                       a.out_bf16, a.clamp, a.opt, a.readout, a.wgate, a.dgate);
+    hipLaunchKernelGGL((decode_step_rows_kernel<F, D, 64, BF, PRO>), dim3(a.B * a.H), dim3(512),
+                       0, st, a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H, a.M,
+                       a.out_bf16, a.clamp, a.opt, a.readout, a.wgate, a.dgate, a.blk);
   else
-    hipLaunchKernelGGL((decode_step_rows_kernel<F, D, kMaxModes, BF>), dim3(a.B * a.H),
+    hipLaunchKernelGGL((decode_step_rows_kernel<F, D, kMaxModes, BF, PRO>), dim3(a.B * a.H),
                        dim3(512), 0, st, a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H,
-                       a.M, a.out_bf16, a.clamp, a.opt, a.readout, a.wgate, a.dgate);
+                       a.M, a.out_bf16, a.clamp, a.opt, a.readout, a.wgate, a.dgate, a.blk);
 }
 
 template <int F, int D>
 static void launch_decode_rows(const DecodeArgs& a, hipStream_t st) {
-  if (a.in_bf16)
-    launch_decode_rows_t<F, D, true>(a, st);
-  else
-    launch_decode_rows_t<F, D, false>(a, st);
+  if (a.in_bf16) {
+    if (a.block) launch_decode_rows_t<F, D, true, true>(a, st);
+    else launch_decode_rows_t<F, D, true, false>(a, st);
+  } else {
+    if (a.block) launch_decode_rows_t<F, D, false, true>(a, st);
+    else launch_decode_rows_t<F, D, false, false>(a, st);
+  }
 }
 
 // Compute units of the current device (cached per device; 256 when there is none).
@@ -312,15 +363,18 @@ hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t st) {
   IA_DEC(64, 32) IA_DEC(64, 64) IA_DEC(64, 128)
   IA_DEC(128, 32) IA_DEC(128, 64) IA_DEC(128, 128)
 #undef IA_DEC
-#define IA_DSK(BF, MM)                                                                      \
-  hipLaunchKernelGGL((decode_step_kernel<BF, MM>), dim3(a.B * a.H), dim3(kStepThreads), 0, st, \
-                     a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H, a.F, a.D, a.M,      \
-                     a.out_bf16, a.clamp, a.opt, a.readout, a.wgate, a.dgate)
+#define IA_DSK(BF, MM, PRO)                                                                \
+  hipLaunchKernelGGL((decode_step_kernel<BF, MM, PRO>), dim3(a.B * a.H), dim3(kStepThreads), 0, \
+                     st, a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.H, a.F, a.D, a.M,  \
+                     a.out_bf16, a.clamp, a.opt, a.readout, a.wgate, a.dgate, a.blk)
+#define IA_DSK_M(BF, PRO) \
+  if (a.M <= 64) IA_DSK(BF, 64, PRO); else IA_DSK(BF, kMaxModes, PRO);
   if (a.in_bf16) {
-    if (a.M <= 64) IA_DSK(true, 64); else IA_DSK(true, kMaxModes);
+    if (a.block) { IA_DSK_M(true, true) } else { IA_DSK_M(true, false) }
   } else {
-    if (a.M <= 64) IA_DSK(false, 64); else IA_DSK(false, kMaxModes);
+    if (a.block) { IA_DSK_M(false, true) } else { IA_DSK_M(false, false) }
   }
+#undef IA_DSK_M
 #undef IA_DSK
   prof_end(st, kKindDecode);
   return hipGetLastError();

@@ -110,6 +110,31 @@ int main() {
                                                       addr(21), addr(3), addr(4), &st,
                                                       addr(21, 16), nullptr), IA_ERR_ALIAS);
   }
+  // the block's edges
+  {
+    ia_block_params p{};
+    p.conv_width = 4;
+    p.conv_q = addr(20); p.conv_k = addr(21); p.conv_v = addr(22);
+    p.rope_base = 1e4f; p.pos0 = 0;
+    p.norm_gain = addr(23); p.norm_bias = addr(24); p.norm_eps = 1e-6f;
+    expect("prologue taps", [&] { ia_block_params b = p; b.conv_width = 9;
+      return ia_block_prologue(&d, &b, addr(0), addr(1), addr(2), nullptr, nullptr, addr(5),
+                               addr(6), addr(7), nullptr); }(), IA_ERR_UNSUPPORTED);
+    expect("prologue positions", [&] { ia_block_params b = p; b.pos0 = 2147483647 - 68;
+      return ia_block_prologue(&d, &b, addr(0), addr(1), addr(2), nullptr, nullptr, addr(5),
+                               addr(6), addr(7), nullptr); }(), IA_ERR_DOMAIN);
+    expect("prologue state alias", ia_block_prologue(&d, &p, addr(0), addr(1), addr(2), addr(30),
+                                                     addr(30), addr(5), addr(6), addr(7),
+                                                     nullptr), IA_ERR_ALIAS);
+    expect("gate alias", ia_block_gate(&d, addr(0), addr(1), addr(1, 64), nullptr),
+           IA_ERR_ALIAS);
+    expect("block step null gain", [&] { ia_block_params b = p; b.norm_gain = nullptr;
+      return ia_block_decode_step(&d, &b, addr(0), addr(1), addr(2), nullptr, nullptr, nullptr,
+                                  addr(3), addr(4), &st, addr(5), nullptr); }(), IA_ERR_NULL);
+    expect("block step alias", ia_block_decode_step(&d, &p, addr(0), addr(1), addr(2), addr(30),
+                                                    addr(5), nullptr, addr(3), addr(4), &st,
+                                                    addr(5), nullptr), IA_ERR_ALIAS);
+  }
   for (int s = 0; s <= IA_ERR_WORKSPACE; ++s)
     if (!ia_status_string(static_cast<ia_status>(s))) ++failures;
   std::printf("%s (%d failure(s))\n", failures ? "FAILED" : "ok", failures);

@@ -408,6 +408,41 @@ def test_block_edges_validation():
     assert g(addr(0, 8), addr(1), addr(2)) == 4
 
 
+def test_block_decode_step_validation():
+    d = desc(Dv=32)   # B=2, H=3, F=32, Dv=32, M=16
+    W = 4
+
+    def params(**kw):
+        p = dict(conv_width=W, conv_q=addr(20).value, conv_k=addr(21).value,
+                 conv_v=addr(22).value, rope_base=1e4, pos0=9, norm_gain=addr(23).value,
+                 norm_bias=addr(24).value, norm_eps=1e-6)
+        p.update(kw)
+        return ia.IABlockParams(**p)
+
+    def step(p=None, d=d, q=0, st_in=None, st_out=None, gate=None, out=5, st=None):
+        return ia.lib.ia_block_decode_step(
+            ctypes.byref(d), None if p is False else ctypes.byref(p or params()),
+            None if q is None else addr(q), addr(1), addr(2), st_in, st_out, gate,
+            addr(3), addr(4), st or state(), addr(out), None)
+    assert step(False) == 1
+    assert step(q=None) == 1
+    assert step(params(conv_width=9)) == 7
+    assert step(params(conv_k=None)) == 1
+    assert step(params(pos0=-1)) == 6
+    assert step(params(norm_gain=None)) == 1
+    assert step(params(norm_eps=float("inf"))) == 6
+    assert step(params(norm_bias=addr(24, 4).value)) == 4
+    assert step(gate=addr(30, 8)) == 4
+    assert step(st_in=addr(31, 8)) == 4
+    assert step(d=desc(Dv=32, bidir=True)) == 7
+    assert step(d=desc(Dv=32, identity_features=True)) == 7
+    assert step(out=1) == 5                          # the output over k
+    assert step(gate=addr(5)) == 5                   # the output over the gate
+    assert step(st_in=addr(30), st_out=addr(30)) == 5   # the two convolution states in one
+    assert step(st_out=addr(5)) == 5                 # the new convolution state over the output
+    assert step(st_out=addr(23)) == 5                # ... over the normalisation gain
+
+
 def test_gated_variants_validation():
     d = desc(Dv=32)
     g = lambda *a: ia.lib.ia_prefill_fwd_gated(ctypes.byref(d), *a)

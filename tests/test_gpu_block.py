@@ -190,3 +190,116 @@ def test_whole_block_matches_oracle():
     # ... and the oracle's own prologue against the GPU's, so the chain is covered end to end
     rq, rk, rv, _ = blk.prologue(q, k, v, conv, None, rope, 0, nrm, 1e-6)
     assert max(rowrel(lf[0], rq), rowrel(lf[1], rk), rowrel(lf[2], rv)) < 1e-2
+
+
+def _step_inputs(B, H, T, F, D, M, Wd, dtype, seed):
+    r = np.random.default_rng(seed)
+    raw = [(r.standard_normal((T, B, H, C)) * 0.7).astype(np.float32) for C in (F, F, D)]
+    g = r.standard_normal((T, B, H, D)).astype(np.float32)
+    if dtype == "bf16":
+        raw, g = [W.round_bf16(a) for a in raw], W.round_bf16(g)
+    lam = W.s4d_lin(np.exp(r.uniform(np.log(1e-3), np.log(1e-1), H)), M)
+    return raw, g, lam
+
+
+def _step_oracle(raw, g, lam, conv, rope, pos0, nrm, gated, no_den=False):
+    """The oracle's prologue over the T tokens, the brute-force layer from zero state with the
+    features given, the gate: [T, B, H, D]."""
+    T, B, H, F = raw[0].shape
+    D = raw[2].shape[3]
+    seq = [np.transpose(a, (1, 0, 2, 3)).astype(np.float64) for a in raw]   # [B,T,H,C]
+    fq, fk, vo, _ = blk.prologue(*seq, conv, None, rope, pos0, nrm, 1e-6)
+    o = np.empty((B, T, H, D))
+    beta = np.ones(lam.shape[1], np.complex128)
+    for b in range(B):
+        for h in range(H):
+            res = brute.layer(fq[b, :, h], fk[b, :, h], vo[b, :, h], lam[h], beta,
+                              features_given=True)
+            o[b, :, h] = res[1] if no_den else res[0]
+    if gated:
+        o = blk.gate(o, np.transpose(g, (1, 0, 2, 3)))
+    return np.transpose(o, (1, 0, 2, 3))
+
+
+def _run_steps(ia, raw, g, lam, conv, rope, pos0, nrm, dtype, gated, fused, no_den=False):
+    """T decode tokens through ia_block_decode_step (fused) or through ia_block_prologue,
+    ia_decode_step with identity features and ia_block_gate; returns the outputs [T,B,H,D]
+    (float) and the final convolution state."""
+    import torch
+    t_dt = _tdt(dtype)
+    T, B, H, F = raw[0].shape
+    D, M = raw[2].shape[3], lam.shape[1]
+    Wd = 0 if conv is None else conv[0].shape[2]
+    c = None if conv is None else tuple(dev(w) for w in conv)
+    n = None if nrm is None else tuple(dev(w) for w in nrm)
+    lamd, betad = dev(lam), dev(np.ones((H, M), np.complex64))
+    st = ia.new_state(B, H, M, F, D)
+    cs = [torch.zeros((B, H, max(Wd - 1, 1), 2 * F + D), device="cuda") for _ in range(2)]
+    d1 = ia.make_desc(B, H, 1, F, D, M, ia.dtype_code(t_dt), ia.dtype_code(t_dt), no_den=no_den)
+    di = ia.make_desc(B, H, 1, F, D, M, ia.dtype_code(t_dt), ia.dtype_code(t_dt), no_den=no_den,
+                      identity_features=True)
+    outs = []
+    for t in range(T):
+        p = ia.block_params(c, rope, pos0 + t, n)
+        sin, sout = (cs[t % 2], cs[1 - t % 2]) if Wd > 1 else (None, None)
+        q, k, v = (dev(a[t], t_dt) for a in raw)
+        gt = dev(g[t], t_dt) if gated else None
+        out = torch.empty((B, H, D), dtype=t_dt, device="cuda")
+        if fused:
+            ia.ia_block_decode_step(d1, p, q, k, v, sin, sout, gt, lamd, betad, st, out)
+        else:
+            f = tuple(torch.empty_like(x) for x in (q, k, v))
+            ia.ia_block_prologue(d1, p, q, k, v, sin, sout, *f)
+            ia.ia_decode_step(di, *f, lamd, betad, st, out)
+            if gated:
+                ia.ia_block_gate(d1, out, gt, out)
+        torch.cuda.synchronize()
+        outs.append(host(out))
+    return np.stack(outs), (host(cs[T % 2]) if Wd > 1 else None)
+
+
+# (B, H, F, D, M, W): row-parallel decode kernel (M <= 64 and M = 80), the mode-looping one
+# (F = 256, and 2048 slices), the latter with two channel pairs per thread at F = Dv = 256
+STEP_SHAPES = [(2, 3, 64, 64, 16, 4), (1, 2, 128, 128, 64, 3), (1, 1, 32, 128, 80, 2),
+               (1, 2, 256, 64, 16, 4), (1, 1, 256, 256, 32, 8), (128, 16, 32, 32, 16, 4)]
+
+
+@pytest.mark.parametrize("shape", STEP_SHAPES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_block_decode_step_matches_oracle(shape, dtype):
+    """Five tokens through the fused block step from zero states (RoPE from position 11, the
+    normalisation, the gate) against the oracle's prologue, layer and gate, and against the
+    three-call route; the final convolution state equal to the three-call route's."""
+    ia = _ia()
+    B, H, F, D, M, Wd = shape
+    T = 3 if B * H > 1000 else 5
+    raw, g, lam = _step_inputs(B, H, T, F, D, M, Wd, dtype, 400 + F + D + M)
+    conv, rope, nrm = _params(H, F, D, Wd, 401)
+    tag(f"block decode step {shape} {dtype}")
+    got, st = _run_steps(ia, raw, g, lam, conv, rope, 11, nrm, dtype, True, True)
+    three, st3 = _run_steps(ia, raw, g, lam, conv, rope, 11, nrm, dtype, True, False)
+    ref = _step_oracle(raw, g, lam, conv, rope, 11, nrm, True)
+    tol = TOL_BF16 if dtype == "bf16" else 2e-3
+    err, err3 = rowrel(got, ref), rowrel(got, three)
+    report(f"block decode step {shape} {dtype}", err)
+    assert err < tol, (err, err3)
+    assert err3 < tol, (err, err3)
+    if st is not None:
+        np.testing.assert_array_equal(st, st3)
+
+
+@pytest.mark.parametrize("opts", ["no_gate", "no_rope_no_norm", "no_conv", "one_tap", "no_den"])
+def test_block_decode_step_options(opts):
+    ia = _ia()
+    B, H, F, D, M = 2, 2, 64, 32, 16
+    Wd = {"no_conv": 0, "one_tap": 1}.get(opts, 3)
+    raw, g, lam = _step_inputs(B, H, 4, F, D, M, Wd, "f32", 410)
+    conv, rope, nrm = _params(H, F, D, Wd, 411, rope=opts != "no_rope_no_norm",
+                              norm=opts != "no_rope_no_norm")
+    gated, no_den = opts != "no_gate", opts == "no_den"
+    tag(f"block decode step {opts}")
+    got, _ = _run_steps(ia, raw, g, lam, conv, rope, 0, nrm, "f32", gated, True, no_den)
+    ref = _step_oracle(raw, g, lam, conv, rope, 0, nrm, gated, no_den)
+    err = rowrel(got, ref)
+    report(f"block decode step {opts}", err)
+    assert err < 2e-3, err

@@ -138,13 +138,14 @@ def test_graph_backward(bidir):
     _replays(torch, run, reset, outs, eager)
 
 
-def test_graph_block_decode_stack():
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_block_decode_stack(fused):
     """Three blocks decoding four tokens in one graph.  Per token and layer: the prologue
     (convolution state in two buffers taken in turn, RoPE at the token's position, the
-    normalisation), ia_decode_step with identity features, the output gate in place; layer
-    l > 0 takes layer l-1's gated output as its v, so the graph's order matters.  Replays equal
-    the eager run exactly; the eager run equals the oracle's prologue, brute-force layer and
-    gate, layer by layer on that layer's own inputs."""
+    normalisation), ia_decode_step with identity features, the output gate in place -- or, fused,
+    ia_block_decode_step doing all three; layer l > 0 takes layer l-1's gated output as its v,
+    so the graph's order matters.  Replays equal the eager run exactly; the eager run equals the
+    oracle's prologue, brute-force layer and gate, layer by layer on that layer's own inputs."""
     import torch
     import oracle.block as blk
     from oracle import brute
@@ -187,6 +188,12 @@ def test_graph_block_decode_stack():
         for t in range(T):
             for l in range(L):
                 vin = v0d[t] if l == 0 else out[l - 1][t]
+                if fused:
+                    ia.ia_block_decode_step(d1, ps[l][t], qd[l][t][:, 0], kd[l][t][:, 0],
+                                            vin[:, 0], cs[l][t % 2], cs[l][1 - t % 2],
+                                            gd[l][t][:, 0], lamd[l], betad, sts[l],
+                                            out[l][t][:, 0])
+                    continue
                 fq, fk, vo = feats[l]
                 ia.ia_block_prologue(d1, ps[l][t], qd[l][t], kd[l][t], vin, cs[l][t % 2],
                                      cs[l][1 - t % 2], fq, fk, vo)
@@ -199,7 +206,7 @@ def test_graph_block_decode_stack():
             for x in sts[l] + tuple(cs[l]):
                 x.zero_()
 
-    tag("graph block decode stack")
+    tag(f"graph block decode stack fused={fused}")
     reset()
     run()
     torch.cuda.synchronize()
@@ -218,7 +225,7 @@ def test_graph_block_decode_stack():
                 o[b, :, h] = brute.layer(fq[b, :, h], fk[b, :, h], vo[b, :, h], lams[l][h],
                                          beta[h], features_given=True)[0]
         err = rowrel(seq(host(out[l])), blk.gate(o, seq(gs[l])))
-        report(f"graph block decode stack, layer {l}", err)
+        report(f"graph block decode stack fused={fused}, layer {l}", err)
         assert err < TOL_BF16, (l, err)
 
     for x in out:
