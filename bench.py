@@ -518,6 +518,9 @@ def main():
     ap.add_argument("--decode-only", action="store_true",
                     help="run only the decode measurements (for profiling them); prints their "
                          "JSON object alone")
+    ap.add_argument("--block-only", action="store_true",
+                    help="run only the block-edge measurements on the 1.3B-shaped tensors (for "
+                         "profiling them); prints their JSON object alone")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain streaming kernel over 256 MiB (read 256 MiB, write "
                          "256 MiB) whose counter readings scale the hardware byte counters")
@@ -537,6 +540,10 @@ def main():
         calib_copy(torch)
     if args.decode_only:
         print(json.dumps({"decode": bench_decode(torch, ia, W)}), flush=True)
+        return
+    if args.block_only:
+        inp = WORKLOADS["1.3b"][1](W)
+        print(json.dumps({"block_edges": bench_block(torch, ia, W, inp)}), flush=True)
         return
     pf = bench_prefill(args, torch, ia, W)
     dec = None if args.no_decode else bench_decode(torch, ia, W)
