@@ -26,6 +26,41 @@ namespace {
 constexpr int kBlockTokens = 64;   // tokens per workgroup
 constexpr int kNormGroup = 16;     // tokens whose normalisation sums are reduced together
 
+// Totals over the 64 lanes of a wave of 16 values v[0..15], scattered over the lanes: lane l
+// ends with the totals of values T and T + 1 in z0 and z1, T = 2 b + 4 (r & 1) + 8 (r >> 1),
+// r = l / 16 and b = (l / 8) & 1 (all eight lanes of a group hold the same two).  The first
+// two rounds pair lane halves and then rows with the cross-row swaps (each instruction serves
+// two values), the third pairs lanes l, l ^ 8 by a row rotation, the last three sum within
+// groups of eight by DPP: 36 instructions where a full reduction of every value takes 96.
+__device__ __forceinline__ void scatter_totals16(const float (&v)[16], float& z0, float& z1) {
+  float u[8], w[4];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {   // u[j]: lanes 0-31 value j, 32-63 value j + 8
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[j]),
+                                                    __float_as_uint(v[j + 8]), false, false);
+    u[j] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {   // w[j], row r: value j + 4 (r & 1) + 8 (r >> 1)
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(u[j]),
+                                                    __float_as_uint(u[j + 4]), false, false);
+    w[j] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+  const bool hi = threadIdx.x & 8;
+  float z[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {   // lanes l, l ^ 8: each keeps one value and sends the other
+    const float keep = hi ? w[j + 2] : w[j], send = hi ? w[j] : w[j + 2];
+    z[j] = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), 0x128,
+                                                             0xF, 0xF, false));   // row_ror:8
+    z[j] = dpp_add<0xB1>(z[j]);    // quad_perm [1,0,3,2]
+    z[j] = dpp_add<0x4E>(z[j]);    // quad_perm [2,3,0,1]
+    z[j] = dpp_add<0x141>(z[j]);   // row_half_mirror
+  }
+  z0 = z[0];
+  z1 = z[1];
+}
+
 // A channel pair: bf16 as one packed word, fp32 as two words.
 template <bool BF>
 struct PairIO;
@@ -128,11 +163,11 @@ block_prologue_kernel(const BlockArgs a) {
     c0 = bp[0];
     c1 = bp[1];
   }
-  // RoPE: the pair turns by base^(-2i/F) / (2 pi) turns per position; each token's angle comes
-  // from its own position (in fp64, reduced to [0, 1) turns), so that a call's split into
-  // pieces does not change it
+  // RoPE: the pair turns by base^(-2i/F) / (2 pi) turns per position, its angles stepped from
+  // anchors (rope_cs_at), so that a call's split into pieces does not change them
   const bool rope = a.rope_base > 0.f && kind != 2;
   const double rev = rope ? rope_rate(a.rope_base, i, F) : 0.0;
+  const float2 step = rope ? rope_step(rev) : make_float2(1.f, 0.f);
   const float inv_e = 1.f / (float)(F + D);
   const bool summed = active && kind != 0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = (blockDim.x + 63) >> 6;
@@ -145,8 +180,15 @@ block_prologue_kernel(const BlockArgs a) {
     const char* gp = sp + (size_t)t0 * tsb;
     float2 xin[kNormGroup];
 #pragma unroll
-    for (int j = 0; j < kNormGroup; ++j) xin[j] = IO::load(gp + __umul24(min(j, jmax), tsb));
-    const double p0 = (double)(a.pos0 + t0);   // position of token t0 (< 2^31)
+    for (int j = 0; j < kNormGroup; ++j)
+      xin[j] = IO::load(gp + (uint32_t)__umul24((uint32_t)min(j, jmax), tsb));
+    // (cos, sin) of token t0's angle, and of the next anchor, where the group may cross one
+    const int p0 = a.pos0 + t0;   // < 2^31
+    float2 rc = make_float2(1.f, 0.f), rc_next = rc;
+    if (rope) {
+      rc = rope_cs_at(p0, rev, step);
+      rc_next = rope_cs((double)(p0 | (kRopeAnchor - 1)) + 1.0, rev);
+    }
     float y0[kNormGroup], y1[kNormGroup], sq[kNormGroup];
 #pragma unroll
     for (int j = 0; j < kNormGroup; ++j) {
@@ -172,10 +214,12 @@ block_prologue_kernel(const BlockArgs a) {
       }
       if (kind != 2) {
         if (rope) {
-          const float2 cs = rope_cs(p0 + (double)j, rev);
-          const float r0 = a0 * cs.x - a1 * cs.y, r1 = a0 * cs.y + a1 * cs.x;
+          const float r0 = a0 * rc.x - a1 * rc.y, r1 = a0 * rc.y + a1 * rc.x;
           a0 = r0;
           a1 = r1;
+          // the next position's angle: an anchor's own, else one more step
+          const bool anchor = (((uint32_t)p0 + j + 1) & (kRopeAnchor - 1)) == 0;
+          rc = anchor ? rc_next : rope_advance(rc, step);
         }
         a0 = feature(a0);
         a1 = feature(a1);
@@ -185,36 +229,26 @@ block_prologue_kernel(const BlockArgs a) {
       sq[j] = summed && j <= jmax ? a0 * a0 + a1 * a1 : 0.f;
     }
     if (norm) {
-      if (wave_sums) row_totals<64, kNormGroup>(sq);   // wave totals in lane 63
-      if (lane == 63) {
-        float4* dst4 = reinterpret_cast<float4*>(s_red[parity][wave]);
-#pragma unroll
-        for (int q4 = 0; q4 < kNormGroup / 4; ++q4)
-          dst4[q4] = wave_sums ? make_float4(sq[4 * q4], sq[4 * q4 + 1], sq[4 * q4 + 2],
-                                             sq[4 * q4 + 3])
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
+      // the wave's totals of the 16 tokens, two per group of eight lanes
+      float z0 = 0.f, z1 = 0.f;
+      if (wave_sums) scatter_totals16(sq, z0, z1);
+      if ((lane & 7) == 0) {
+        const int T = 2 * ((lane >> 3) & 1) + 4 * ((lane >> 4) & 1) + 8 * (lane >> 5);
+        *reinterpret_cast<float2*>(&s_red[parity][wave][T]) = make_float2(z0, z1);
       }
       __syncthreads();   // (the next group writes the other half of s_red)
-      float tot[kNormGroup];
-#pragma unroll
-      for (int j = 0; j < kNormGroup; ++j) tot[j] = 0.f;
-#pragma unroll
-      for (int w2 = 0; w2 < 8; ++w2)
-        if (w2 < nwave) {
-          const float4* src4 = reinterpret_cast<const float4*>(s_red[parity][w2]);
-#pragma unroll
-          for (int q4 = 0; q4 < kNormGroup / 4; ++q4) {
-            const float4 v4 = src4[q4];
-            tot[4 * q4] += v4.x;
-            tot[4 * q4 + 1] += v4.y;
-            tot[4 * q4 + 2] += v4.z;
-            tot[4 * q4 + 3] += v4.w;
-          }
-        }
+      // lane j of every wave: token j's total and 1 / rms; then read out lane by lane
+      float rj = 0.f;
+      if (lane < kNormGroup) {
+        float s = 0.f;
+        for (int w2 = 0; w2 < nwave; ++w2) s += s_red[parity][w2][lane];
+        rj = __builtin_amdgcn_rsqf(s * inv_e + a.norm_eps);
+      }
       if (kind != 0) {
 #pragma unroll
         for (int j = 0; j < kNormGroup; ++j) {
-          const float r = __builtin_amdgcn_rsqf(tot[j] * inv_e + a.norm_eps);
+          const float r = __builtin_bit_cast(
+              float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rj), j));
           y0[j] = y0[j] * (g0 * r) + c0;
           y1[j] = y1[j] * (g1 * r) + c1;
         }
@@ -225,7 +259,7 @@ block_prologue_kernel(const BlockArgs a) {
       char* gd = dp + (size_t)t0 * tsb;
 #pragma unroll
       for (int j = 0; j < kNormGroup; ++j)
-        if (j <= jmax) IO::store(gd + __umul24(j, tsb), y0[j], y1[j]);
+        if (j <= jmax) IO::store(gd + (uint32_t)__umul24((uint32_t)j, tsb), y0[j], y1[j]);
     }
   }
 

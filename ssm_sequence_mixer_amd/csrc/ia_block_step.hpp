@@ -31,6 +31,25 @@ __device__ __forceinline__ float2 rope_cs(double pos, double rate) {
   return make_float2(__builtin_amdgcn_cosf(tr), __builtin_amdgcn_sinf(tr));
 }
 
+// RoPE angles stepped from anchors.  Positions that are multiples of kRopeAnchor take their
+// (cos, sin) from rope_cs; a position after an anchor multiplies the anchor's value by the
+// one-position turn (rope_cs(1, rate)) once per position, in order.  A position's value thus
+// depends on the position alone, so a call split into pieces gives the same bits, while 15 of
+// 16 positions cost a complex multiplication instead of a sine and a cosine (the products
+// drift by a few fp32 ulps at most).
+constexpr int kRopeAnchor = 16;
+__device__ __forceinline__ float2 rope_step(double rate) { return rope_cs(1.0, rate); }
+// c times the step, with its roundings spelled out (explicit fmaf: the same bits wherever it
+// is inlined, which plain a*b - c*d, left to the compiler's contraction, does not promise)
+__device__ __forceinline__ float2 rope_advance(float2 c, float2 step) {
+  return make_float2(fmaf(c.x, step.x, -(c.y * step.y)), fmaf(c.x, step.y, c.y * step.x));
+}
+__device__ __forceinline__ float2 rope_cs_at(int pos, double rate, float2 step) {
+  float2 c = rope_cs((double)(pos & ~(kRopeAnchor - 1)), rate);
+  for (int k = 0; k < (pos & (kRopeAnchor - 1)); ++k) c = rope_advance(c, step);
+  return c;
+}
+
 // Channel pair c of the head's [q | k | v]: kind (0 q, 1 k, 2 v) and pair index in its tensor.
 struct PairIndex {
   int kind, i, width;
@@ -141,7 +160,8 @@ struct BlockToken {
       }
       if (pi.kind != 2) {
         if (p.rope_base > 0.f) {
-          const float2 cs = rope_cs((double)p.pos, rope_rate(p.rope_base, pi.i, F));
+          const double rate = rope_rate(p.rope_base, pi.i, F);
+          const float2 cs = rope_cs_at(p.pos, rate, rope_step(rate));
           const float r0 = a0 * cs.x - a1 * cs.y, r1 = a0 * cs.y + a1 * cs.x;
           a0 = r0;
           a1 = r1;
