@@ -237,6 +237,178 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
   }
 }
 
+// Token-sequential prefill with the slice's whole state in registers: one 512-thread
+// workgroup per (b,h) slice walks its N tokens (positions N-1..0 with `reverse`) in the layout
+// of decode_step_rows_kernel -- thread t holds float4 column pu of the U rows ru + SU i and
+// column pd of the Gamma rows rd + SD i -- reading the state once before the first token and
+// writing it once after the last.  Each token's q, k, v pairs and gates are loaded one token
+// ahead.  Per token: the U rows' update and their a[m] (DPP row totals, LDS), a barrier, the
+// readout matrix if any, the Gamma rows' update and their column sums (LDS), a barrier, the
+// output.  Arithmetic as seq_step (gates: lambda times the decay gate, beta times the write
+// gate), with its own summation order.
+template <int F, int D, int MM, bool BF>
+__global__ void __launch_bounds__(512)
+scan_rows_kernel(const ScanArgs a) {
+  constexpr int NT = 512, NWV = NT / 64;
+  constexpr int RU = F / 2, RD = D / 2;
+  static_assert(RU <= 64 && RD <= 64 && NT % RU == 0 && NT % RD == 0, "row width");
+  constexpr int SU = NT / RU, SD = NT / RD;
+  constexpr int IU = (MM + SU - 1) / SU, ID = (MM + SD - 1) / SD;
+  __shared__ float2 s_lam[kMaxModes], s_beta[kMaxModes], s_a[kMaxModes], s_ar[kMaxModes];
+  __shared__ float2 s_rp[NT];
+  __shared__ float s_num[SD][D];
+  __shared__ float s_den[NWV];
+
+  const int M = a.M, N = a.N, H = a.H;
+  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int pu = tid % RU, ru = tid / RU, pd = tid % RD, rd = tid / RD;
+  float4* Ub = reinterpret_cast<float4*>(a.U + (size_t)bh * M * F);
+  float4* Gb = reinterpret_cast<float4*>(a.G + (size_t)bh * M * D);
+  float2* Eb = a.E + (size_t)bh * M;
+  const float2* R = a.readout ? a.readout + (size_t)h * M * M : nullptr;
+  const float* dummy = reinterpret_cast<const float*>(a.lam);   // a valid address
+
+  // one token's inputs: the thread's pairs and the gates (loads without branches)
+  struct Tok {
+    float2 q, k, v;
+    float wg, dg;
+  };
+  auto load_tok = [&](int t) {
+    const int pos = a.reverse ? N - 1 - t : t;
+    const size_t qk = (size_t)(b * a.sqk.b + pos * a.sqk.n + h * a.sqk.h);
+    const size_t vo = (size_t)(b * a.sv.b + pos * a.sv.n + h * a.sv.h);
+    const size_t gi = ((size_t)b * N + pos) * H + h;
+    Tok x;
+    x.k = load_pair_t<BF>(a.k, qk + 2 * pu);
+    x.q = load_pair_t<BF>(a.q, qk + 2 * pu);
+    x.v = load_pair_t<BF>(a.v, vo + 2 * pd);
+    x.wg = *(a.wgate ? a.wgate + gi : dummy);
+    x.dg = *(a.dgate ? a.dgate + gi : dummy);
+    return x;
+  };
+  Tok nxt = load_tok(0);
+
+  // the state, unconditional loads (rows past M read row M-1 and stay unused)
+  float4 u[IU], g[ID];
+#pragma unroll
+  for (int i = 0; i < IU; ++i) u[i] = Ub[(size_t)min(ru + SU * i, M - 1) * RU + pu];
+#pragma unroll
+  for (int i = 0; i < ID; ++i) g[i] = Gb[(size_t)min(rd + SD * i, M - 1) * RD + pd];
+  const int mt = min(tid, M - 1);
+  float2 e = Eb[mt];   // used by threads tid < M only
+  const float2 lv = a.lam[(size_t)h * M + mt], bv = a.beta[(size_t)h * M + mt];
+  if (tid < M) {
+    s_lam[tid] = lv;
+    s_beta[tid] = bv;
+  }
+  __syncthreads();
+
+  for (int t = 0; t < N; ++t) {
+    const Tok cur = nxt;
+    nxt = load_tok(min(t + 1, N - 1));
+    const float wg = a.wgate ? cur.wg : 1.f, dg = a.dgate ? cur.dg : 1.f;
+    const float fk0 = feat(cur.k.x, a.opt), fk1 = feat(cur.k.y, a.opt);
+    const float fq0 = feat(cur.q.x, a.opt), fq1 = feat(cur.q.y, a.opt);
+    const float v0 = cur.v.x, v1 = cur.v.y;
+
+    if (tid < M) {
+      const float2 l = s_lam[tid], bt = s_beta[tid];
+      e = cfma(make_float2(dg * l.x, dg * l.y), e, make_float2(wg * bt.x, wg * bt.y));
+    }
+    // U rows: update in registers, contract with phi(q) over the row's lanes
+    float ar[IU], ai[IU];
+#pragma unroll
+    for (int i = 0; i < IU; ++i) {
+      const int m = ru + SU * i;
+      if (m < M) {
+        const float2 l0 = s_lam[m], b0 = s_beta[m];
+        const float2 l = make_float2(dg * l0.x, dg * l0.y), bt = make_float2(wg * b0.x, wg * b0.y);
+        const float2 u0 = cfma(l, make_float2(u[i].x, u[i].y), make_float2(bt.x * fk0, bt.y * fk0));
+        const float2 u1 = cfma(l, make_float2(u[i].z, u[i].w), make_float2(bt.x * fk1, bt.y * fk1));
+        u[i] = make_float4(u0.x, u0.y, u1.x, u1.y);
+        ar[i] = fq0 * u0.x + fq1 * u1.x;
+        ai[i] = fq0 * u0.y + fq1 * u1.y;
+      } else {
+        ar[i] = ai[i] = 0.f;
+      }
+    }
+    row_totals<RU>(ar);
+    row_totals<RU>(ai);
+    if (pu == RU - 1) {
+#pragma unroll
+      for (int i = 0; i < IU; ++i) {
+        const int m = ru + SU * i;
+        if (m < M) s_a[m] = make_float2(ar[i], ai[i]);
+      }
+    }
+    __syncthreads();   // a[m]
+    if (R) {   // (a R)[n] = sum_m a[m] R[m][n], as the decode step
+      const int parts = NT / M, n = tid % M, part = tid / M;
+      if (part < parts) {
+        float2 acc = make_float2(0.f, 0.f);
+        for (int m = part; m < M; m += parts) acc = cfma(s_a[m], R[(size_t)m * M + n], acc);
+        s_rp[tid] = acc;
+      }
+      __syncthreads();
+      if (tid < M) {
+        float2 acc = make_float2(0.f, 0.f);
+        for (int p = 0; p < parts; ++p) acc = cadd2(acc, s_rp[p * M + tid]);
+        s_ar[tid] = acc;
+      }
+      __syncthreads();
+    }
+    const float2* A = R ? s_ar : s_a;
+    float dn = tid < M ? A[tid].x * e.x - A[tid].y * e.y : 0.f;
+    dn = wave_sum(dn);
+    if (lane == 0) s_den[wave] = dn;
+    // Gamma rows: update in registers, accumulate Re(a[m] G[m, 2pd..2pd+1])
+    float n0 = 0.f, n1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < ID; ++i) {
+      const int m = rd + SD * i;
+      if (m < M) {
+        const float2 l0 = s_lam[m], b0 = s_beta[m], am = A[m];
+        const float2 l = make_float2(dg * l0.x, dg * l0.y), bt = make_float2(wg * b0.x, wg * b0.y);
+        const float2 g0 = cfma(l, make_float2(g[i].x, g[i].y), make_float2(bt.x * v0, bt.y * v0));
+        const float2 g1 = cfma(l, make_float2(g[i].z, g[i].w), make_float2(bt.x * v1, bt.y * v1));
+        g[i] = make_float4(g0.x, g0.y, g1.x, g1.y);
+        n0 += am.x * g0.x - am.y * g0.y;
+        n1 += am.x * g1.x - am.y * g1.y;
+      }
+    }
+    s_num[rd][2 * pd] = n0;
+    s_num[rd][2 * pd + 1] = n1;
+    __syncthreads();   // numerator parts, den
+    if (a.o && tid < D) {
+      float n = 0.f;
+#pragma unroll
+      for (int r = 0; r < SD; ++r) n += s_num[r][tid];
+      float den = 0.f;
+#pragma unroll
+      for (int w = 0; w < NWV; ++w) den += s_den[w];
+      const int pos = a.reverse ? N - 1 - t : t;
+      const size_t oi = (((size_t)b * N + pos) * H + h) * D + tid;
+      float val = readout(n, den, a.clamp, a.opt);
+      if (a.accumulate) val += load_in(a.o, oi, a.out_bf16);
+      store_out(a.o, oi, val, a.out_bf16);
+    }
+  }
+
+  // the state after the last token
+#pragma unroll
+  for (int i = 0; i < IU; ++i) {
+    const int m = ru + SU * i;
+    if (m < M) Ub[(size_t)m * RU + pu] = u[i];
+  }
+#pragma unroll
+  for (int i = 0; i < ID; ++i) {
+    const int m = rd + SD * i;
+    if (m < M) Gb[(size_t)m * RD + pd] = g[i];
+  }
+  if (tid < M) Eb[tid] = e;
+}
+
 // Token-sequential prefill (the fp32 path).  M <= MM.  grid = B*H; one workgroup walks all N tokens of
 // its slice, in reverse when `reverse` is set (then token t of the walk is position N-1-t).
 // q, k and v are addressed through their element strides sqk, sv; o is dense.
@@ -380,9 +552,32 @@ hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int F, int D>
+static void launch_scan_rows(const ScanArgs& a, hipStream_t st) {
+  if (a.in_bf16) {
+    if (a.M <= 64) hipLaunchKernelGGL((scan_rows_kernel<F, D, 64, true>), dim3(a.B * a.H), dim3(512), 0, st, a);
+    else hipLaunchKernelGGL((scan_rows_kernel<F, D, kMaxModes, true>), dim3(a.B * a.H), dim3(512), 0, st, a);
+  } else {
+    if (a.M <= 64) hipLaunchKernelGGL((scan_rows_kernel<F, D, 64, false>), dim3(a.B * a.H), dim3(512), 0, st, a);
+    else hipLaunchKernelGGL((scan_rows_kernel<F, D, kMaxModes, false>), dim3(a.B * a.H), dim3(512), 0, st, a);
+  }
+}
+
 hipError_t launch_scan_prefill(const ScanArgs& a, hipStream_t st) {
   (void)hipGetLastError();
   prof_begin(st);
+  // the state in registers (scan_rows_kernel) for row widths up to 64 float4; the mode-looping
+  // kernel with the state in memory otherwise
+#define IA_SR(FF, DD)                         \
+  if (a.F == FF && a.D == DD) {               \
+    launch_scan_rows<FF, DD>(a, st);          \
+    prof_end(st, kKindScan);                  \
+    return hipGetLastError();                 \
+  }
+  IA_SR(32, 32) IA_SR(32, 64) IA_SR(32, 128)
+  IA_SR(64, 32) IA_SR(64, 64) IA_SR(64, 128)
+  IA_SR(128, 32) IA_SR(128, 64) IA_SR(128, 128)
+#undef IA_SR
 #define IA_SCAN(MM)                                                                          \
   hipLaunchKernelGGL((scan_prefill_kernel<MM>), dim3(a.B * a.H), dim3(kStepThreads), 0, st,    \
                      a.q, a.k, a.v, a.lam, a.beta, a.U, a.G, a.E, a.o, a.accumulate, a.N, a.H, \
