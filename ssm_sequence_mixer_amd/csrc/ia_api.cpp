@@ -67,17 +67,42 @@ ia_status check_state(const ia_desc* d, const ia_state* st) {
   return IA_OK;
 }
 
-// Workspace of the fp32 (token-sequential) prefill path: a state when the caller passes none.
+// Workspace of the token-sequential prefill path: a state when the caller passes none (or the
+// call is bidirectional), and, for the register-resident kernel, the slots and decay products
+// of its sequence segments.  Segments give every compute unit one slice's workgroup
+// (B*H*segments up to the CU count), at least kMinScanSegment tokens each; their count is the
+// largest whose bytes fit `avail` (the workspace queries pass no limit, a call its ws_bytes),
+// so a smaller workspace runs fewer segments, down to one.
+constexpr int kMinScanSegment = 64;
 struct ScanWorkspace {
   size_t state_off, bytes;
+  int n_seg, seg_len;
+  size_t slots_off, dec_off;
 };
 
-ScanWorkspace scan_workspace(const ia_desc* d, bool have_state) {
-  ScanWorkspace w{0, 0};
+ScanWorkspace scan_workspace(const ia_desc* d, bool have_state, size_t avail = SIZE_MAX) {
+  ScanWorkspace w{0, 0, 1, d->N, 0, 0};
   const bool bidir = d->flags & IA_FLAG_BIDIR;
   if (!have_state || bidir) {
     w.state_off = 0;
     w.bytes = round_up(state_bytes(d));
+  }
+  if (!ia::scan_rows_supported(d->F, d->Dv)) return w;
+  const long bh = long(d->B) * d->H;
+  long S = std::min<long>(ia::device_cus() / bh, d->N / kMinScanSegment);
+  for (; S > 1; --S) {
+    const int len = int((d->N + S - 1) / S);
+    const int n = (d->N + len - 1) / len;
+    const size_t slots = round_up(size_t(n) * bh * ia::scan_slot_float2(d->F, d->Dv, d->M) * 8);
+    const size_t dec = round_up(size_t(n - 1) * bh * d->M * 8);
+    if (w.bytes + slots + dec <= avail) {
+      w.n_seg = n;
+      w.seg_len = len;
+      w.slots_off = w.bytes;
+      w.dec_off = w.bytes + slots;
+      w.bytes += slots + dec;
+      break;
+    }
   }
   return w;
 }
@@ -368,7 +393,7 @@ static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, co
     return IA_ERR_UNSUPPORTED;
 
   // fp32 path: token-sequential recurrence.
-  const ScanWorkspace w = scan_workspace(d, st != nullptr);
+  const ScanWorkspace w = scan_workspace(d, st != nullptr, workspace ? ws_bytes : 0);
   if (w.bytes) {
     if (!workspace || ws_bytes < w.bytes) return IA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return IA_ERR_ALIGN;
@@ -397,6 +422,12 @@ static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, co
   a.readout = static_cast<const float2*>(readout);
   a.wgate = wgate;
   a.dgate = dgate;
+  if (w.n_seg > 1) {
+    a.n_seg = w.n_seg;
+    a.seg_len = w.seg_len;
+    a.slots = reinterpret_cast<float2*>(ws + w.slots_off);
+    a.dec = reinterpret_cast<float2*>(ws + w.dec_off);
+  }
   if (!bidir) return launch_status(ia::launch_scan_prefill(a, hs));
 
   // Bidirectional: the forward direction writes o, the reverse direction (from a zero state

@@ -120,7 +120,17 @@ struct ScanArgs {
   int opt;   // kOptNoDen | kOptIdentity
   const float2* readout = nullptr;   // [H][M][M] readout matrix, or NULL
   const float *wgate = nullptr, *dgate = nullptr;   // [B][N][H] write / decay gates, or NULL
+  // Sequence segments of the register-resident kernel (n_seg > 1, shapes it takes): each
+  // segment's end state from zero and its decay product (state-only pass), the segment
+  // starts (carry), then every segment from its start with outputs.  slots: n_seg states of
+  // all B*H slices (the slice layout of U, Gamma, eta side by side), dec: (n_seg - 1) * B*H*M.
+  int n_seg = 1, seg_len = 0;
+  float2 *slots = nullptr, *dec = nullptr;
 };
+// Whether the register-resident kernel takes a shape (F, D in {32, 64, 128}).
+bool scan_rows_supported(int F, int D);
+// Complex floats of one slice's state, M (F + D + 1).
+__host__ __device__ inline long scan_slot_float2(int F, int D, int M) { return (long)M * (F + D + 1); }
 
 // Chunked MFMA prefill of one direction (bf16 inputs).  The sequence is cut into `segments`
 // runs of `seg_chunks` chunks; with more than one, the end states of all but the last segment

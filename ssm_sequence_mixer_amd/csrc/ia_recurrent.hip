@@ -246,7 +246,12 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
 // readout matrix if any, the Gamma rows' update and their column sums (LDS), a barrier, the
 // output.  Arithmetic as seq_step (gates: lambda times the decay gate, beta times the write
 // gate), with its own summation order.
-template <int F, int D, int MM, bool BF>
+// Segments (a.n_seg > 1): blockIdx.y is the segment, walk steps [y L, min(N, (y+1) L)).
+// LOCAL: the state-only pass of segments 0..n_seg-2 from a zero state: their end states go to
+// slots y+1 and the products of the per-token decays (decay gate times lambda, per mode) to
+// dec; no output.  Otherwise segment y starts from slot y (n_seg > 1) or from U, Gamma, eta,
+// and the last segment writes the final state to U, Gamma, eta.
+template <int F, int D, int MM, bool BF, bool LOCAL>
 __global__ void __launch_bounds__(512)
 scan_rows_kernel(const ScanArgs a) {
   constexpr int NT = 512, NWV = NT / 64;
@@ -260,12 +265,22 @@ scan_rows_kernel(const ScanArgs a) {
   __shared__ float s_den[NWV];
 
   const int M = a.M, N = a.N, H = a.H;
-  const int bh = blockIdx.x, b = bh / H, h = bh % H;
+  const int bh = blockIdx.x, b = bh / H, h = bh % H, BH = a.B * H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int pu = tid % RU, ru = tid / RU, pd = tid % RD, rd = tid / RD;
-  float4* Ub = reinterpret_cast<float4*>(a.U + (size_t)bh * M * F);
-  float4* Gb = reinterpret_cast<float4*>(a.G + (size_t)bh * M * D);
-  float2* Eb = a.E + (size_t)bh * M;
+  const int seg = blockIdx.y, segmented = a.n_seg > 1;
+  const int t_begin = segmented ? seg * a.seg_len : 0;
+  const int t_end = segmented ? min(N, t_begin + a.seg_len) : N;
+  // where this workgroup's state starts and ends
+  const long slot = scan_slot_float2(F, D, M);
+  auto slot_of = [&](int g) { return a.slots + ((size_t)g * BH + bh) * slot; };
+  float2* const in = LOCAL ? nullptr
+                           : (segmented ? slot_of(seg) : nullptr);
+  float2* const out = LOCAL ? slot_of(seg + 1) : nullptr;
+  const bool last = !LOCAL && (!segmented || seg == a.n_seg - 1);
+  float4* Ub = reinterpret_cast<float4*>(in ? in : a.U + (size_t)bh * M * F);
+  float4* Gb = reinterpret_cast<float4*>(in ? in + (size_t)M * F : a.G + (size_t)bh * M * D);
+  float2* Eb = in ? in + (size_t)M * (F + D) : a.E + (size_t)bh * M;
   const float2* R = a.readout ? a.readout + (size_t)h * M * M : nullptr;
   const float* dummy = reinterpret_cast<const float*>(a.lam);   // a valid address
 
@@ -287,16 +302,27 @@ scan_rows_kernel(const ScanArgs a) {
     x.dg = *(a.dgate ? a.dgate + gi : dummy);
     return x;
   };
-  Tok nxt = load_tok(0);
+  Tok nxt = load_tok(t_begin);
 
-  // the state, unconditional loads (rows past M read row M-1 and stay unused)
+  // the state (zero for the state-only pass), unconditional loads (rows past M read row M-1
+  // and stay unused)
   float4 u[IU], g[ID];
-#pragma unroll
-  for (int i = 0; i < IU; ++i) u[i] = Ub[(size_t)min(ru + SU * i, M - 1) * RU + pu];
-#pragma unroll
-  for (int i = 0; i < ID; ++i) g[i] = Gb[(size_t)min(rd + SD * i, M - 1) * RD + pd];
   const int mt = min(tid, M - 1);
-  float2 e = Eb[mt];   // used by threads tid < M only
+  float2 e;   // used by threads tid < M only
+  if constexpr (LOCAL) {
+#pragma unroll
+    for (int i = 0; i < IU; ++i) u[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int i = 0; i < ID; ++i) g[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    e = make_float2(0.f, 0.f);
+  } else {
+#pragma unroll
+    for (int i = 0; i < IU; ++i) u[i] = Ub[(size_t)min(ru + SU * i, M - 1) * RU + pu];
+#pragma unroll
+    for (int i = 0; i < ID; ++i) g[i] = Gb[(size_t)min(rd + SD * i, M - 1) * RD + pd];
+    e = Eb[mt];
+  }
+  float2 dprod = make_float2(1.f, 0.f);   // LOCAL: product of the decays, mode tid
   const float2 lv = a.lam[(size_t)h * M + mt], bv = a.beta[(size_t)h * M + mt];
   if (tid < M) {
     s_lam[tid] = lv;
@@ -304,9 +330,9 @@ scan_rows_kernel(const ScanArgs a) {
   }
   __syncthreads();
 
-  for (int t = 0; t < N; ++t) {
+  for (int t = t_begin; t < t_end; ++t) {
     const Tok cur = nxt;
-    nxt = load_tok(min(t + 1, N - 1));
+    nxt = load_tok(min(t + 1, t_end - 1));
     const float wg = a.wgate ? cur.wg : 1.f, dg = a.dgate ? cur.dg : 1.f;
     const float fk0 = feat(cur.k.x, a.opt), fk1 = feat(cur.k.y, a.opt);
     const float fq0 = feat(cur.q.x, a.opt), fq1 = feat(cur.q.y, a.opt);
@@ -314,7 +340,39 @@ scan_rows_kernel(const ScanArgs a) {
 
     if (tid < M) {
       const float2 l = s_lam[tid], bt = s_beta[tid];
-      e = cfma(make_float2(dg * l.x, dg * l.y), e, make_float2(wg * bt.x, wg * bt.y));
+      const float2 ld = make_float2(dg * l.x, dg * l.y);
+      e = cfma(ld, e, make_float2(wg * bt.x, wg * bt.y));
+      if constexpr (LOCAL) dprod = cmul(ld, dprod);
+    }
+    if constexpr (LOCAL) {
+      // the state update alone: no readout, so no barrier
+#pragma unroll
+      for (int i = 0; i < IU; ++i) {
+        const int m = ru + SU * i;
+        if (m < M) {
+          const float2 l0 = s_lam[m], b0 = s_beta[m];
+          const float2 l = make_float2(dg * l0.x, dg * l0.y);
+          const float2 bt = make_float2(wg * b0.x, wg * b0.y);
+          const float2 u0 =
+              cfma(l, make_float2(u[i].x, u[i].y), make_float2(bt.x * fk0, bt.y * fk0));
+          const float2 u1 =
+              cfma(l, make_float2(u[i].z, u[i].w), make_float2(bt.x * fk1, bt.y * fk1));
+          u[i] = make_float4(u0.x, u0.y, u1.x, u1.y);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < ID; ++i) {
+        const int m = rd + SD * i;
+        if (m < M) {
+          const float2 l0 = s_lam[m], b0 = s_beta[m];
+          const float2 l = make_float2(dg * l0.x, dg * l0.y);
+          const float2 bt = make_float2(wg * b0.x, wg * b0.y);
+          const float2 g0 = cfma(l, make_float2(g[i].x, g[i].y), make_float2(bt.x * v0, bt.y * v0));
+          const float2 g1 = cfma(l, make_float2(g[i].z, g[i].w), make_float2(bt.x * v1, bt.y * v1));
+          g[i] = make_float4(g0.x, g0.y, g1.x, g1.y);
+        }
+      }
+      continue;
     }
     // U rows: update in registers, contract with phi(q) over the row's lanes
     float ar[IU], ai[IU];
@@ -395,18 +453,51 @@ scan_rows_kernel(const ScanArgs a) {
     }
   }
 
-  // the state after the last token
+  // the state after the segment's last token: the slot of the next segment's start (LOCAL),
+  // or the final state (the last segment)
+  if (!LOCAL && !last) return;
+  float4* Uo = reinterpret_cast<float4*>(LOCAL ? out : a.U + (size_t)bh * M * F);
+  float4* Go = reinterpret_cast<float4*>(LOCAL ? out + (size_t)M * F : a.G + (size_t)bh * M * D);
+  float2* Eo = LOCAL ? out + (size_t)M * (F + D) : a.E + (size_t)bh * M;
 #pragma unroll
   for (int i = 0; i < IU; ++i) {
     const int m = ru + SU * i;
-    if (m < M) Ub[(size_t)m * RU + pu] = u[i];
+    if (m < M) Uo[(size_t)m * RU + pu] = u[i];
   }
 #pragma unroll
   for (int i = 0; i < ID; ++i) {
     const int m = rd + SD * i;
-    if (m < M) Gb[(size_t)m * RD + pd] = g[i];
+    if (m < M) Go[(size_t)m * RD + pd] = g[i];
   }
-  if (tid < M) Eb[tid] = e;
+  if (tid < M) {
+    Eo[tid] = e;
+    if constexpr (LOCAL) a.dec[((size_t)seg * BH + bh) * M + tid] = dprod;
+  }
+}
+
+// The segment starts: slot 0 takes the initial state (U, Gamma, eta), then slot g+1 (holding
+// segment g's end state from zero) becomes dec_g * slot g + slot g+1, per complex entry and its
+// mode.  One thread per complex entry of all slices' states, the segments in order.
+__global__ void __launch_bounds__(256)
+scan_carry_kernel(const ScanArgs a) {
+  const int M = a.M, F = a.F, D = a.D, BH = a.B * a.H;
+  const long per = scan_slot_float2(F, D, M);
+  const long x = blockIdx.x * 256L + threadIdx.x;
+  if (x >= per * BH) return;
+  const int bh = (int)(x / per);
+  const long r = x % per;
+  const int m = r < (long)M * F ? (int)(r / F)
+                : r < (long)M * (F + D) ? (int)((r - (long)M * F) / D)
+                                        : (int)(r - (long)M * (F + D));
+  float2 s = r < (long)M * F ? a.U[(size_t)bh * M * F + r]
+             : r < (long)M * (F + D) ? a.G[(size_t)bh * M * D + (r - (long)M * F)]
+                                     : a.E[(size_t)bh * M + (r - (long)M * (F + D))];
+  a.slots[(size_t)bh * per + r] = s;
+  for (int g = 0; g + 1 < a.n_seg; ++g) {
+    float2* nx = a.slots + ((size_t)(g + 1) * BH + bh) * per + r;
+    s = cfma(a.dec[((size_t)g * BH + bh) * M + m], s, *nx);
+    *nx = s;
+  }
 }
 
 // Token-sequential prefill (the fp32 path).  M <= MM.  grid = B*H; one workgroup walks all N tokens of
@@ -552,15 +643,38 @@ hipError_t launch_decode_step(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int F, int D, bool LOCAL>
+static void launch_scan_rows_t(const ScanArgs& a, dim3 grid, hipStream_t st) {
+  if (a.in_bf16) {
+    if (a.M <= 64)
+      hipLaunchKernelGGL((scan_rows_kernel<F, D, 64, true, LOCAL>), grid, dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((scan_rows_kernel<F, D, kMaxModes, true, LOCAL>), grid, dim3(512), 0,
+                         st, a);
+  } else {
+    if (a.M <= 64)
+      hipLaunchKernelGGL((scan_rows_kernel<F, D, 64, false, LOCAL>), grid, dim3(512), 0, st, a);
+    else
+      hipLaunchKernelGGL((scan_rows_kernel<F, D, kMaxModes, false, LOCAL>), grid, dim3(512), 0,
+                         st, a);
+  }
+}
+
+// One segment: the walk.  Several: the state-only pass, the carry, the walk of every segment.
 template <int F, int D>
 static void launch_scan_rows(const ScanArgs& a, hipStream_t st) {
-  if (a.in_bf16) {
-    if (a.M <= 64) hipLaunchKernelGGL((scan_rows_kernel<F, D, 64, true>), dim3(a.B * a.H), dim3(512), 0, st, a);
-    else hipLaunchKernelGGL((scan_rows_kernel<F, D, kMaxModes, true>), dim3(a.B * a.H), dim3(512), 0, st, a);
-  } else {
-    if (a.M <= 64) hipLaunchKernelGGL((scan_rows_kernel<F, D, 64, false>), dim3(a.B * a.H), dim3(512), 0, st, a);
-    else hipLaunchKernelGGL((scan_rows_kernel<F, D, kMaxModes, false>), dim3(a.B * a.H), dim3(512), 0, st, a);
+  const int BH = a.B * a.H;
+  if (a.n_seg > 1) {
+    launch_scan_rows_t<F, D, true>(a, dim3(BH, a.n_seg - 1), st);
+    const long n = scan_slot_float2(F, D, a.M) * BH;
+    hipLaunchKernelGGL(scan_carry_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       a);
   }
+  launch_scan_rows_t<F, D, false>(a, dim3(BH, a.n_seg > 1 ? a.n_seg : 1), st);
+}
+
+bool scan_rows_supported(int F, int D) {
+  return (F == 32 || F == 64 || F == 128) && (D == 32 || D == 64 || D == 128);
 }
 
 hipError_t launch_scan_prefill(const ScanArgs& a, hipStream_t st) {

@@ -293,3 +293,65 @@ def test_shapes_outside_the_chunk_kernels(shape):
         torch.cuda.synchronize()
         assert rowrel(host(o), o_ref) < TOL_F32
         assert state_rel(tuple(host(s) for s in st), st_ref) < TOL_F32
+
+
+@pytest.mark.parametrize("case", ["plain", "gated", "readout", "bidir"])
+def test_fp32_prefill_segments_match_one_walk(case):
+    """The register-resident walk cut into sequence segments (state-only pass from zero, the
+    carry of the segment starts, every segment from its start; the workspace the query returns)
+    against one walk of the whole sequence (a workspace too small for segments) and against
+    the oracle: fp32 inputs, 4 slices of 700 tokens, a caller state (except bidirectional)."""
+    torch = _torch()
+    ia = _lib()
+    B, H, N, F, D, M = 2, 2, 700, 64, 32, 16
+    inp = W.make_inputs(B, H, N, F, D, M, dtype="f32", seed=40)
+    q, k, v = (dev(inp[n]) for n in "qkv")
+    lam, beta = dev(inp["lam"]), dev(inp["beta"])
+    rng = np.random.default_rng(41)
+    kw, wg, dg, R = {}, None, None, None
+    if case == "gated":
+        wg = rng.uniform(0.0, 1.5, (B, N, H)).astype(np.float32)
+        dg = rng.uniform(0.5, 1.0, (B, N, H)).astype(np.float32)
+        kw["gates"] = (dev(wg), dev(dg))
+    if case == "readout":
+        X = rng.standard_normal((H, M, M)) + 1j * rng.standard_normal((H, M, M))
+        R = (np.eye(M)[None] + 0.3 * X / np.sqrt(M)).astype(np.complex64)
+        kw["readout"] = dev(R)
+    bidir = case == "bidir"
+    st0 = None
+    if not bidir:
+        pre = W.make_inputs(B, H, 9, F, D, M, dtype="f32", seed=42, std=0.5)
+        st0 = tuple(host(dev(x)) for x in
+                    oracle.prefill(pre["q"], pre["k"], pre["v"], inp["lam"], inp["beta"])[3])
+    one_walk = B * H * M * (F + D + 1) * 8 + 256   # a state: no room for segment slots
+    runs = []
+    for ws_bytes in (None, one_walk):
+        tag(f"fp32 prefill segments {case} ws={ws_bytes}")
+        st = None if bidir else tuple(dev(x) for x in st0)
+        ws = None if ws_bytes is None else torch.empty(ws_bytes, dtype=torch.uint8,
+                                                       device="cuda")
+        o = ia.prefill(q, k, v, lam, beta, state=st, out_dtype=torch.float32, bidir=bidir,
+                       workspace=ws, **kw)
+        torch.cuda.synchronize()
+        runs.append((host(o), None if st is None else tuple(host(x) for x in st)))
+    (o_seg, s_seg), (o_one, s_one) = runs
+    assert rowrel(o_seg, o_one) < 1e-4
+    if not bidir:
+        assert state_rel(s_seg, s_one) < 1e-4
+    if case == "plain":
+        o_ref, _, _, s_ref = oracle.prefill(inp["q"], inp["k"], inp["v"], inp["lam"],
+                                            inp["beta"], state=st0, threads=8)
+    elif case == "gated":
+        o_ref, _, _, s_ref = oracle.prefill_gated(inp["q"], inp["k"], inp["v"], inp["lam"],
+                                                  inp["beta"], wg, dg, state=st0, threads=8)
+    elif case == "readout":
+        o_ref, _, _, s_ref = oracle.prefill_readout(inp["q"], inp["k"], inp["v"], inp["lam"],
+                                                    inp["beta"], R, state=st0, threads=8)
+    else:
+        o_ref, s_ref = oracle.bidir(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"],
+                                    threads=8), None
+    err = rowrel(o_seg, o_ref)
+    report(f"fp32 prefill segments {case}", err)
+    assert err < TOL_F32
+    if s_ref is not None:
+        assert state_rel(s_seg, s_ref) < TOL_F32
