@@ -122,9 +122,19 @@ ia_status ia_state_init(const ia_desc* desc, ia_state* st, void* stream);
  * is invalid or has no kernel (bf16 shapes outside the chunked path).  The workspace holds the
  * per-head tables, the per-segment state summaries and one state (the caller's initial state
  * copied there when several segments run, or the fp32 route's working state) of the chunked
- * scan (for IA_FLAG_BIDIR a second set of summaries, the reverse walk's), or a state for
- * state-less fp32 calls.  Its contents need no initialisation and are scratch between calls.
- * (The bidirectional layer accumulates its two directions in o itself, in o's dtype.) */
+ * scan (for IA_FLAG_BIDIR a second set of summaries, the reverse walk's), or, for the fp32
+ * token-sequential path, a state (state-less or bidirectional calls) and the slots of its
+ * sequence segments (see below).  Its contents need no initialisation and are scratch between
+ * calls.  (The bidirectional layer accumulates its two directions in o itself, in o's dtype.)
+ *
+ * Sequence segments of the token-sequential path (F, Dv in {32, 64, 128}): when the B*H slices
+ * leave compute units idle, each sequence is cut into up to CUs / (B*H) segments of at least
+ * 64 tokens, each walked by its own workgroup from its start state (a state-only pass from
+ * zero per segment, then a carry of the starts).  The query returns the bytes of the full
+ * count: per segment one state of all slices, B*H*M*(F+Dv+1) complex64, plus B*H*M complex64
+ * of decay products; a call runs as many segments as its ws_bytes holds, down to one (then
+ * the workspace may be NULL when st is given and IA_FLAG_BIDIR is not set).  The results
+ * agree with one walk to rounding. */
 size_t ia_prefill_workspace_bytes(const ia_desc* desc);
 
 /* Host-side check of the modes for `desc` (lambda_host: [H][M] complex64 in HOST memory).
@@ -308,9 +318,9 @@ ia_status ia_prefill_bwd(const ia_desc* desc,
 
 /* Workspace bytes ia_prefill_fwd_readout needs at most: on the chunked path its plan (as
  * ia_prefill_workspace_bytes, at its chunk length) plus each head's readout-matrix operand,
- * 8*M*M bytes and a scale, 256-byte aligned; otherwise one state, B*H*M*(F+Dv+1) complex64
- * rounded up to 256 bytes (used when st is NULL or IA_FLAG_BIDIR is set; otherwise the
- * workspace may be NULL).  0 on an invalid descriptor. */
+ * 8*M*M bytes and a scale, 256-byte aligned; otherwise that of the token-sequential path
+ * (ia_prefill_workspace_bytes: a state and the segments' slots).  0 on an invalid
+ * descriptor. */
 size_t ia_prefill_readout_workspace_bytes(const ia_desc* desc);
 
 ia_status ia_prefill_fwd_readout(const ia_desc* desc,
@@ -413,11 +423,12 @@ ia_status ia_block_decode_step(const ia_desc* desc, const ia_block_params* p,
  *   wgate, dgate  float, device, read only: [B][N][H] for the prefill (dense, element
  *                 (b, n, h) at (b N + n) H + h), [B][H] for the decode step; NULL:
  *                 IA_ERR_NULL; 16-byte aligned; must not overlap an output.
- * The gated prefill runs the token-by-token fp32 kernel for either input dtype, one workgroup
- * per (b,h) slice (the chunked kernels take no gates): about as fast as the fp32 prefill.
- * IA_FLAG_BIDIR: both directions use the gates of the positions they walk.  Other arguments,
- * layouts and errors as ia_prefill_fwd / ia_decode_step.  The workspace (one state, used when
- * st is NULL or IA_FLAG_BIDIR is set) is ia_prefill_gated_workspace_bytes(desc) bytes. */
+ * The gated prefill runs the token-sequential fp32 kernels for either input dtype (the chunked
+ * kernels take no gates), with sequence segments as the fp32 prefill.  IA_FLAG_BIDIR: both
+ * directions use the gates of the positions they walk.  Other arguments, layouts and errors as
+ * ia_prefill_fwd / ia_decode_step.  The workspace (as the fp32 path's of
+ * ia_prefill_workspace_bytes: a state and the segments' slots) is
+ * ia_prefill_gated_workspace_bytes(desc) bytes. */
 size_t ia_prefill_gated_workspace_bytes(const ia_desc* desc);
 
 ia_status ia_prefill_fwd_gated(const ia_desc* desc,
