@@ -411,6 +411,43 @@ def bench_block(torch, ia, W, inp, layers=24, reps=20):
 FP32_PEAK = 157.3e12        # fp32 vector FLOP/s, MI355X
 
 
+def bench_gated(torch, ia, inp, reps=5):
+    """Selective writing and memory decay (ia_prefill_fwd_gated, token-sequential fp32
+    kernels with sequence segments) on the prefill workload's bf16 q, k, v, with write gates
+    in [0.5, 1) and decay gates in [0.9, 1): per-step time, tokens/s and the fp32 vector
+    fraction of its algorithmic FLOPs, 12 M (F + Dv) per token and head (the state updates,
+    8 per complex entry, and the two readout contractions, 4 each)."""
+    sh = inp["shape"]
+    B, H, N, F, D, M = sh["B"], sh["H"], sh["N"], sh["F"], sh["D"], sh["M"]
+    q, k, v = (torch.from_numpy(inp[n]).to(torch.bfloat16).cuda() for n in "qkv")
+    lam = torch.from_numpy(inp["lam"]).cuda()
+    beta = torch.from_numpy(inp["beta"]).cuda()
+    g = torch.Generator(device="cpu").manual_seed(560)
+    wg = (torch.rand((B, N, H), generator=g) * 0.5 + 0.5).cuda()
+    dg = (torch.rand((B, N, H), generator=g) * 0.1 + 0.9).cuda()
+    desc = ia.make_desc(B, H, N, F, D, M, ia.IA_BF16, ia.IA_F32)
+    ws = torch.empty(max(ia.ia_prefill_gated_workspace_bytes(desc), 16), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty((B, N, H, D), dtype=torch.float32, device="cuda")
+
+    def step():
+        ia.ia_prefill_fwd_gated(desc, q, k, v, wg, dg, lam, beta, None, o, ws)
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 12.0 * M * (F + D) * B * N * H
+    return {"ms_per_step": ms, "tokens_per_s": B * N / (ms * 1e-3),
+            "fp32_frac": flops / (ms * 1e-3) / FP32_PEAK,
+            "scope": "ia_prefill_fwd_gated on the prefill workload (bf16 q, k, v; fp32 out)"}
+
+
 def bwd_alg_flops(B, N, H, F, D, M):
     """Algorithmic FLOPs of the backward pass (fp32 VALU): per token, head and mode, the state
     recompute 14 (F + D) and the reverse sweep 44 F + 41 D (a complex multiply counted 6, a
@@ -521,6 +558,9 @@ def main():
     ap.add_argument("--block-only", action="store_true",
                     help="run only the block-edge measurements on the 1.3B-shaped tensors (for "
                          "profiling them); prints their JSON object alone")
+    ap.add_argument("--gated-only", action="store_true",
+                    help="run only the gated prefill measurement on the 1.3B-shaped workload "
+                         "(for profiling it); prints its JSON object alone")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run a plain streaming kernel over 256 MiB (read 256 MiB, write "
                          "256 MiB) whose counter readings scale the hardware byte counters")
@@ -545,14 +585,19 @@ def main():
         inp = WORKLOADS["1.3b"][1](W)
         print(json.dumps({"block_edges": bench_block(torch, ia, W, inp)}), flush=True)
         return
+    if args.gated_only:
+        inp = WORKLOADS["1.3b"][1](W)
+        print(json.dumps({"gated": bench_gated(torch, ia, inp)}), flush=True)
+        return
     pf = bench_prefill(args, torch, ia, W)
     dec = None if args.no_decode else bench_decode(torch, ia, W)
     bwd = None
     if not args.no_backward:
         bwd = bench_backward(torch, ia, pf["inp"], bidir=pf["cfg"]["bidirectional"])
-    block = None
+    block = gated = None
     if not args.no_decode and args.workload == "1.3b":
         block = bench_block(torch, ia, W, pf["inp"])
+        gated = bench_gated(torch, ia, pf["inp"])
     cpu = None if args.no_cpu else cpu_baseline(pf["inp"], pf["cfg"]["bidirectional"])
     line = {
         "metric": "IA layer fwd tokens/s (prefill) + decode step latency; % of MFMA/HBM roofline",
@@ -575,6 +620,7 @@ def main():
         "readout_matrix": pf["readout"],
         "decode": dec,
         "block_edges": block,
+        "gated": gated,
         "backward": bwd,
         "cpu_baseline": cpu,
     }
