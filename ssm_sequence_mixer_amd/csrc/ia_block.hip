@@ -11,7 +11,7 @@
 // (each input read once, each output written once), one workgroup per (block of 64 tokens,
 // b, h), one thread per pair of adjacent channels: the q pairs, then the k pairs, then the
 // v pairs of the head, so a RoPE pair (2i, 2i+1) sits in one thread and the convolution keeps
-// its window of the last W raw tokens in that thread's registers.
+// its window of the W-1 previous raw tokens in that thread's registers.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 

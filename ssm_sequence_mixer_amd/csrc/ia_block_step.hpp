@@ -7,8 +7,9 @@
 // z = [phi(k), v] scaled to unit RMS with a per-head gain and bias.
 //
 // Split in two so that a decode kernel can issue its state loads between them: load() issues
-// every global load of the token's inputs, finish() computes, writes phi(q'), phi(k')', v'' to
-// LDS and the new convolution state.
+// every global load of the token's inputs, finish() computes and writes phi(q') and the
+// normalised phi(k') and v' to LDS, and the new convolution state to memory.  The SiLU and
+// RoPE helpers here serve the prefill prologue of ia_block.hip too.
 #pragma once
 
 #include "ia_device.hpp"
