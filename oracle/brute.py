@@ -68,6 +68,28 @@ def layer(q, k, v, lam, beta, clamp=1e-6, readout=None, gates=None, features_giv
     return o, num, den
 
 
+def den_condition(q, k, lam, beta, t, gates=None):
+    """The conditioning of the denominator at token t of one slice (from zero state), as
+    ``layer`` defines it: den = Re sum_m a_m eta_m, returned with
+    kappa = sum_m |Re(a_m eta_m)| / |den|, the factor by which the cancellation in that sum
+    amplifies relative errors of its terms (1 when no term cancels another).  A diagnostic for
+    tolerances: a recurrence carried in a precision eps resolves den only to about kappa eps.
+
+    Returns (kappa, den)."""
+    fq, fk = feature(q), feature(k)
+    beta = np.asarray(beta, dtype=np.complex128)
+    s = np.arange(t + 1)
+    dec = powers(lam, t - s) * beta[None, :]
+    if gates is not None:
+        w = np.asarray(gates[0], dtype=np.float64)
+        cl = np.cumsum(np.log(np.asarray(gates[1], dtype=np.float64)))
+        dec = dec * (w[s] * np.exp(cl[t] - cl[s]))[:, None]
+    S = fk[: t + 1] @ fq[t]                          # <phi(q_t), phi(k_s)>
+    terms = np.real((S[:, None] * dec).sum(axis=0) * dec.sum(axis=0))
+    den = terms.sum()
+    return float(np.abs(terms).sum() / abs(den)), float(den)
+
+
 def layer_batched(q, k, v, lam, beta, clamp=1e-6):
     """[B,N,H,X] layout wrapper around ``layer``."""
     B, N, H, _ = q.shape

@@ -423,3 +423,34 @@ def test_planted_gate_mistake_fails_a_pin(mutant, tmp_path):
     _, num, den, _ = oracle.scan_gated(q, k, v, lam, beta, w, a, lib=lib)
     _, nb, db = brute.layer(q, k, v, lam, beta, gates=(w, a))
     assert not (_rel(num, nb) < 1e-10 and _rel(den, db) < 1e-10), f"{mutant} passed"
+
+
+# ---------------------------------------------------------------- denominator conditioning
+
+def test_den_condition_pins():
+    """brute.den_condition: its denominator is the layer's (with and without gates); kappa = 1
+    when no term can cancel (real positive lambda and beta: every a_m eta_m > 0, the features
+    being positive); and two equal modes with beta = (1, i r) give a_1 eta_1 = -r^2 a_0 eta_0,
+    so kappa = (1 + r^2) / |1 - r^2| whatever the data."""
+    r = np.random.default_rng(60)
+    N, F, D = 40, 8, 4
+    q, k, v = (r.standard_normal((N, X)) for X in (F, F, D))
+    lam = np.array([0.95 * np.exp(0.3j), 0.9 * np.exp(-1.1j), 0.99])
+    beta = np.array([1.0, 0.5 - 0.7j, 2.0j])
+    gates = (r.uniform(0.2, 1.4, N), r.uniform(0.6, 1.0, N))
+    for g in (None, gates):
+        _, _, den = brute.layer(q, k, v, lam, beta, gates=g)
+        for t in (0, 7, N - 1):
+            kappa, d = brute.den_condition(q, k, lam, beta, t, gates=g)
+            assert abs(d - den[t]) <= 1e-12 * max(1.0, abs(den[t]))
+            assert kappa >= 1.0 - 1e-12
+    lam_pos, beta_pos = np.array([0.9, 0.5, 0.99]), np.array([1.0, 0.3, 2.0])
+    for t in (0, 11, N - 1):
+        assert abs(brute.den_condition(q, k, lam_pos, beta_pos, t)[0] - 1.0) < 1e-12
+    for rr in (0.5, 0.99, 1.01, 3.0):
+        lam2 = np.array([0.93 * np.exp(0.4j)] * 2)
+        beta2 = np.array([1.0, 1j * rr])
+        for t in (3, N - 1):
+            kappa = brute.den_condition(q, k, lam2, beta2, t)[0]
+            want = (1 + rr ** 2) / abs(1 - rr ** 2)
+            assert abs(kappa - want) <= 1e-9 * want, (rr, t, kappa, want)
