@@ -130,4 +130,39 @@ __device__ __forceinline__ void row_totals(float (&v)[N]) {
   }
 }
 
+// Totals over the 64 lanes of a wave of 16 values v[0..15], scattered over the lanes: lane l
+// ends with the totals of values T and T + 1 in z0 and z1, T = 2 b + 4 (r & 1) + 8 (r >> 1),
+// r = l / 16 and b = (l / 8) & 1 (all eight lanes of a group hold the same two).  The first
+// two rounds pair lane halves and then rows with the cross-row swaps (each instruction serves
+// two values), the third pairs lanes l, l ^ 8 by a row rotation, the last three sum within
+// groups of eight by DPP: 36 instructions where a full reduction of every value takes 96.
+__device__ __forceinline__ void scatter_totals16(const float (&v)[16], float& z0, float& z1) {
+  float u[8], w[4];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {   // u[j]: lanes 0-31 value j, 32-63 value j + 8
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[j]),
+                                                    __float_as_uint(v[j + 8]), false, false);
+    u[j] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {   // w[j], row r: value j + 4 (r & 1) + 8 (r >> 1)
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(u[j]),
+                                                    __float_as_uint(u[j + 4]), false, false);
+    w[j] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  }
+  const bool hi = threadIdx.x & 8;
+  float z[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {   // lanes l, l ^ 8: each keeps one value and sends the other
+    const float keep = hi ? w[j + 2] : w[j], send = hi ? w[j] : w[j + 2];
+    z[j] = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), 0x128,
+                                                             0xF, 0xF, false));   // row_ror:8
+    z[j] = dpp_add<0xB1>(z[j]);    // quad_perm [1,0,3,2]
+    z[j] = dpp_add<0x4E>(z[j]);    // quad_perm [2,3,0,1]
+    z[j] = dpp_add<0x141>(z[j]);   // row_half_mirror
+  }
+  z0 = z[0];
+  z1 = z[1];
+}
+
 }  // namespace ia

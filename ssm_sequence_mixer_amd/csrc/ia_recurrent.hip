@@ -60,6 +60,46 @@ decode_step_kernel(const void* __restrict__ q, const void* __restrict__ k,
   }
 }
 
+// The row sums a[m] = (sum of ar, sum of ai over the RU lanes holding row m's columns) of the
+// rows m = ru + SU i (i < IU) into s_a[m].  With 64-lane rows (RU = 64: a wave holds rows ru +
+// SU i of one set of columns) the 2 IU values reduce-scatter over the wave (scatter_totals16,
+// 16 values at a time) and one lane of each group of eight writes its row; otherwise each row's
+// lanes sum by DPP moves (row_totals), all rows' chains interleaved, and the row's last lane
+// writes it.
+template <int RU, int SU, int IU>
+__device__ __forceinline__ void row_sums_to_lds(float (&ar)[IU], float (&ai)[IU], int ru, int M,
+                                                float2* s_a) {
+  const int lane = threadIdx.x & 63;
+  if constexpr (RU == 64 && IU % 8 == 0) {
+#pragma unroll
+    for (int i0 = 0; i0 < IU; i0 += 8) {
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[2 * i] = ar[i0 + i];
+        v[2 * i + 1] = ai[i0 + i];
+      }
+      float z0, z1;
+      scatter_totals16(v, z0, z1);
+      if ((lane & 7) == 0) {   // this group holds values T, T + 1: row i0 + T / 2
+        const int i = i0 + ((lane >> 3) & 1) + 2 * ((lane >> 4) & 1) + 4 * (lane >> 5);
+        const int m = ru + SU * i;
+        if (m < M) s_a[m] = make_float2(z0, z1);
+      }
+    }
+  } else {
+    row_totals<RU>(ar);
+    row_totals<RU>(ai);
+    if (threadIdx.x % RU == RU - 1) {
+#pragma unroll
+      for (int i = 0; i < IU; ++i) {
+        const int m = ru + SU * i;
+        if (m < M) s_a[m] = make_float2(ar[i], ai[i]);
+      }
+    }
+  }
+}
+
 // Decode with the whole state of a slice in flight at once.  grid = B*H; NT threads per slice.
 // A state row of F complex values is F/2 float4 (2 complex each); thread t owns float4 column
 // pu = t % (F/2) of the U rows m = t / (F/2) + (NT/(F/2)) i, and likewise column pd of the
@@ -171,17 +211,8 @@ decode_step_rows_kernel(const void* __restrict__ q, const void* __restrict__ k,
       ar[i] = ai[i] = 0.f;
     }
   }
-  // each row's RU lane partials summed by DPP moves, all rows' chains interleaved; the row's
-  // last lane holds its total
-  row_totals<RU>(ar);
-  row_totals<RU>(ai);
-  if (pu == RU - 1) {
-#pragma unroll
-    for (int i = 0; i < IU; ++i) {
-      const int m = ru + SU * i;
-      if (m < M) s_a[m] = make_float2(ar[i], ai[i]);
-    }
-  }
+  // each row's RU lane partials summed (row_sums_to_lds), a[m] into LDS
+  row_sums_to_lds<RU, SU, IU>(ar, ai, ru, M, s_a);
   __syncthreads();   // a[m]
   // with a readout matrix R ([H][M][M]), the readouts use (a R)[n] = sum_m a[m] R[m][n]
   if (rmat) {
@@ -391,15 +422,7 @@ scan_rows_kernel(const ScanArgs a) {
         ar[i] = ai[i] = 0.f;
       }
     }
-    row_totals<RU>(ar);
-    row_totals<RU>(ai);
-    if (pu == RU - 1) {
-#pragma unroll
-      for (int i = 0; i < IU; ++i) {
-        const int m = ru + SU * i;
-        if (m < M) s_a[m] = make_float2(ar[i], ai[i]);
-      }
-    }
+    row_sums_to_lds<RU, SU, IU>(ar, ai, ru, M, s_a);
     __syncthreads();   // a[m]
     if (R) {   // (a R)[n] = sum_m a[m] R[m][n], as the decode step
       const int parts = NT / M, n = tid % M, part = tid / M;

@@ -9,6 +9,7 @@ import pytest
 
 import ia_workloads as W
 import oracle
+from oracle import brute
 from helpers import TOL_F32, dev, host, report, rowrel, state_rel, tag
 
 pytestmark = pytest.mark.gpu
@@ -124,7 +125,11 @@ def test_gated_bidirectional():
 
 def test_gated_1p3b_workload_every_slice():
     """The 1.3B-shaped layer (B=4, H=16, N=2048, F=Dv=128, M=64, bf16 inputs) with gates, every
-    (b, h) slice, outputs and final state."""
+    (b, h) slice, outputs and final state.  The decay gates damp the slow mode that otherwise
+    dominates eta, and a few rows' denominators then cancel: den = Re sum_m a_m eta_m with
+    kappa = sum_m |Re(a_m eta_m)| / |den| up to 1e5, which an fp32 recurrence resolves only to
+    about kappa 2^-24.  Rows above the fp32 bound are therefore held to 4 kappa 2^-24 (kappa in
+    fp64 from oracle.brute.den_condition), and may be at most one in ten thousand."""
     import torch
     ia = _ia()
     inp = W.l1p3b()
@@ -138,7 +143,16 @@ def test_gated_1p3b_workload_every_slice():
     torch.cuda.synchronize()
     o_ref, _, _, st_ref = oracle.prefill_gated(inp["q"], inp["k"], inp["v"], inp["lam"],
                                                inp["beta"], wg, dg, threads=16)
-    e_o = rowrel(host(o), o_ref)
+    oh = host(o)
     e_s = state_rel(tuple(host(x) for x in st), st_ref)
-    report("gated 1.3b every slice, output / state", max(e_o, e_s))
-    assert e_o < TOL_F32 and e_s < TOL_F32
+    err = np.max(np.abs(oh - o_ref), axis=-1) / np.maximum(np.max(np.abs(o_ref), axis=-1), 1e-30)
+    over = np.argwhere(err >= TOL_F32)
+    report("gated 1.3b every slice, output (rows within the fp32 bound) / state",
+           max(float(np.max(np.where(err < TOL_F32, err, 0.0))), e_s))
+    assert e_s < TOL_F32
+    assert len(over) <= err.size // 10000, len(over)
+    for b, n, h in over:
+        kappa, _ = brute.den_condition(inp["q"][b, :, h], inp["k"][b, :, h], inp["lam"][h],
+                                       inp["beta"][h], n, gates=(wg[b, :, h], dg[b, :, h]))
+        report(f"gated 1.3b row (b={b}, n={n}, h={h}): kappa {kappa:.3g}", err[b, n, h])
+        assert err[b, n, h] < 4 * 2.0 ** -24 * kappa, (b, n, h, err[b, n, h], kappa)
