@@ -90,6 +90,61 @@ def den_condition(q, k, lam, beta, t, gates=None):
     return float(np.abs(terms).sum() / abs(den)), float(den)
 
 
+def gated_condition(q, k, v, lam, beta, wgate, dgate, state=None, tokens=None):
+    """The conditioning of the readout sums of the gated layer (``layer`` with gates, any real
+    gates, zeros and negative values included), at every token t of one slice.  Unrolled, the
+    denominator is a sum over triples (s, j, m) -- key s through A, key j through eta, mode m
+    -- of phi(q_t).phi(k_s) g_s g_j beta_m^2 lambda_m^(2t-s-j), with g_s = w_s prod_{s<u<=t} a_u
+    (products taken directly), plus the terms of the entries of an initial state (U0, G0, E0),
+    carried by lambda^(t+1) prod_{u<=t} a_u; the numerator likewise with v_j[d].  Returned per
+    token:
+        kappa_den = sum |terms of den| / |den|,
+        kappa_num = max_d sum |terms of num[d]| / max_d |num[d]|,
+    the factors by which the cancellation in those sums amplifies relative errors of their
+    terms.  An evaluation that rounds each term's factors to a unit roundoff eps (whatever order
+    it sums in) has relative errors up to about (kappa_den + kappa_num) eps; the sum over modes
+    alone (``den_condition``) is one of its partial sums.  O(t M (F + D)) per token t:
+    ``tokens`` limits the evaluation to those tokens (the others are returned as NaN).
+
+    Returns (kappa_den [N], kappa_num [N])."""
+    fq, fk = feature(q), feature(k)
+    v = np.asarray(v, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.complex128)
+    w = np.asarray(wgate, dtype=np.float64)
+    a = np.asarray(dgate, dtype=np.float64)
+    N = fq.shape[0]
+    if state is not None:
+        U0, G0, E0 = (np.asarray(x, dtype=np.complex128) for x in state)
+    kd, kn = np.full(N, np.nan), np.full(N, np.nan)
+    for t in (range(N) if tokens is None else sorted(set(int(x) for x in tokens))):
+        r = np.ones(t + 1)                      # prod_{s<u<=t} a_u
+        if t > 0:
+            r[:t] = np.cumprod(a[t:0:-1])[::-1]
+        g = w[: t + 1] * r
+        lp = powers(lam, t - np.arange(t + 1))
+        dec = lp * beta[None, :] * g[:, None]                       # [s, m]
+        dab = np.abs(lp) * np.abs(beta)[None, :] * np.abs(g)[:, None]
+        St = fk[: t + 1] @ fq[t]                                    # phi(q_t).phi(k_s)
+        A = (St[:, None] * dec).sum(axis=0)
+        Aab = (St[:, None] * dab).sum(axis=0)
+        Gam = (dec[:, :, None] * v[: t + 1, None, :]).sum(axis=0)
+        Gab = (dab[:, :, None] * np.abs(v[: t + 1, None, :])).sum(axis=0)
+        eta, eab = dec.sum(axis=0), dab.sum(axis=0)
+        if state is not None:
+            p = powers(lam, [t + 1])[0] * (r[0] * a[0])             # lam^(t+1) prod_{u<=t} a_u
+            A = A + p * (U0 @ fq[t])
+            Aab = Aab + np.abs(p) * (np.abs(U0) @ fq[t])
+            Gam = Gam + p[:, None] * G0
+            Gab = Gab + np.abs(p)[:, None] * np.abs(G0)
+            eta = eta + p * E0
+            eab = eab + np.abs(p) * np.abs(E0)
+        den = np.real((A * eta).sum())
+        num = np.real((A[:, None] * Gam).sum(axis=0))
+        kd[t] = (Aab * eab).sum() / abs(den)
+        kn[t] = (Aab[:, None] * Gab).sum(axis=0).max() / np.abs(num).max()
+    return kd, kn
+
+
 def layer_batched(q, k, v, lam, beta, clamp=1e-6):
     """[B,N,H,X] layout wrapper around ``layer``."""
     B, N, H, _ = q.shape

@@ -427,6 +427,64 @@ def test_planted_gate_mistake_fails_a_pin(mutant, tmp_path):
 
 # ---------------------------------------------------------------- denominator conditioning
 
+def test_gated_condition_pins():
+    """brute.gated_condition (the conditioning of the gated layer's readout sums, expanded over
+    key pairs and modes): equal to an explicit loop over every (s, j, m) term on a tiny slice
+    with signed gates, a zero decay and an initial state; exactly 1 when no term can be
+    negative (real positive lambda, beta, gates and values); (1 + r^2) / |1 - r^2| for two equal
+    real modes with beta = (1, i r), whose terms are those of the first mode times -r^2; never
+    below the modes-only partial sum of den_condition.  (A term of a_m from the state is one
+    entry U0[m, f] phi(q_t)[f]: the readout sums the entries like the keys.)"""
+    r = np.random.default_rng(61)
+    N, F, D, M = 7, 3, 2, 3
+    q, k, v = (r.standard_normal((N, X)) for X in (F, F, D))
+    lam = np.array([0.9 * np.exp(0.5j), 0.8 * np.exp(-2.0j), 0.97])
+    beta = np.array([1.0, 0.4 - 0.9j, 1.5j])
+    w = np.array([0.7, -0.4, 1.2, 0.0, 0.9, -1.1, 0.5])
+    a = np.array([0.9, -0.6, 0.0, 0.8, -0.95, 0.7, 1.0])
+    U0, G0, E0 = (r.standard_normal(sh) + 1j * r.standard_normal(sh) for sh in ((M, F), (M, D), (M,)))
+    fq, fk = brute.feature(q), brute.feature(k)
+    kd, kn = brute.gated_condition(q, k, v, lam, beta, w, a, state=(U0, G0, E0))
+    for t in range(N):
+        def g(s):   # w_s prod_{s<u<=t} a_u; s = -1: the state, carried by prod_{u<=t} a_u
+            return (w[s] if s >= 0 else 1.0) * np.prod(a[s + 1: t + 1])
+        den, dab = 0.0, 0.0
+        num, nab = np.zeros(D), np.zeros(D)
+        for m in range(M):
+            # terms of a_m: one per key s, one per entry (m, f) of the state
+            ta_all = [fq[t] @ fk[s] * g(s) * beta[m] * lam[m] ** (t - s) for s in range(t + 1)]
+            ta_all += [fq[t][f] * U0[m, f] * g(-1) * lam[m] ** (t + 1) for f in range(F)]
+            for ta in ta_all:
+                for j in range(-1, t + 1):
+                    if j >= 0:
+                        te, tg = g(j) * beta[m] * lam[m] ** (t - j), g(j) * beta[m] * lam[m] ** (t - j) * v[j]
+                    else:
+                        te, tg = g(-1) * lam[m] ** (t + 1) * E0[m], g(-1) * lam[m] ** (t + 1) * G0[m]
+                    den += np.real(ta * te)
+                    dab += abs(ta) * abs(te)
+                    num += np.real(ta * tg)
+                    nab += abs(ta) * np.abs(tg)
+        assert abs(kd[t] - dab / abs(den)) <= 1e-10 * kd[t], (t, kd[t], dab / abs(den))
+        want_n = nab.max() / np.abs(num).max()
+        assert abs(kn[t] - want_n) <= 1e-10 * want_n, (t, kn[t], want_n)
+    # no cancellation possible: kappa = 1
+    N = 30
+    q, k = r.standard_normal((N, 6)), r.standard_normal((N, 6))
+    vp = np.abs(r.standard_normal((N, 4)))
+    wp, ap = r.uniform(0.1, 1.5, N), r.uniform(0.3, 1.0, N)
+    kd, kn = brute.gated_condition(q, k, vp, np.array([0.9, 0.5, 0.99]), np.array([1.0, 0.3, 2.0]), wp, ap)
+    assert np.all(np.abs(kd - 1.0) < 1e-12) and np.all(np.abs(kn - 1.0) < 1e-12)
+    for rr in (0.5, 0.99, 1.01, 3.0):
+        kd, kn = brute.gated_condition(q, k, vp, np.array([0.93, 0.93]), np.array([1.0, 1j * rr]), wp, ap)
+        want = (1 + rr ** 2) / abs(1 - rr ** 2)
+        assert np.all(np.abs(kd - want) <= 1e-9 * want) and np.all(np.abs(kn - want) <= 1e-9 * want)
+    lam3 = np.array([0.95 * np.exp(0.3j), 0.9 * np.exp(-1.1j), 0.99])
+    beta3 = np.array([1.0, 0.5 - 0.7j, 2.0j])
+    kd, _ = brute.gated_condition(q, k, vp, lam3, beta3, wp, ap)
+    for t in (0, 9, N - 1):
+        assert kd[t] >= brute.den_condition(q, k, lam3, beta3, t, gates=(wp, ap))[0] * (1 - 1e-12)
+
+
 def test_den_condition_pins():
     """brute.den_condition: its denominator is the layer's (with and without gates); kappa = 1
     when no term can cancel (real positive lambda and beta: every a_m eta_m > 0, the features
