@@ -423,11 +423,16 @@ ia_status ia_block_decode_step(const ia_desc* desc, const ia_block_params* p,
  *   wgate, dgate  float, device, read only: [B][N][H] for the prefill (dense, element
  *                 (b, n, h) at (b N + n) H + h), [B][H] for the decode step; NULL:
  *                 IA_ERR_NULL; 16-byte aligned; must not overlap an output.
- * The gated prefill runs the token-sequential fp32 kernels for either input dtype (the chunked
- * kernels take no gates), with sequence segments as the fp32 prefill.  IA_FLAG_BIDIR: both
- * directions use the gates of the positions they walk.  Other arguments, layouts and errors as
- * ia_prefill_fwd / ia_decode_step.  The workspace (as the fp32 path's of
- * ia_prefill_workspace_bytes: a state and the segments' slots) is
+ * Paths: bf16 inputs on the shapes of the chunked kernels (as ia_prefill_fwd's) run the
+ * chunked MFMA prefill with the gates folded into each chunk (per token, the running sum of
+ * log2|a| and the sign of the running product of a within the chunk; a decay gate with
+ * |a| < 2^-64, zero included, counts as 2^-64 there, so the carried state falls to 2^-64 of
+ * itself instead of to zero); fp32 inputs, and bf16 inputs on other shapes, run the
+ * token-sequential fp32 kernels with sequence segments as the fp32 prefill.  Gates may take any
+ * real value; rows whose readout sums cancel are resolved to the precision of each path.
+ * IA_FLAG_BIDIR: both directions use the gates of the positions they walk.  Other arguments,
+ * layouts and errors as ia_prefill_fwd / ia_decode_step.  The workspace (the chunked plan's,
+ * or the fp32 path's: a state and the segments' slots) is
  * ia_prefill_gated_workspace_bytes(desc) bytes. */
 size_t ia_prefill_gated_workspace_bytes(const ia_desc* desc);
 

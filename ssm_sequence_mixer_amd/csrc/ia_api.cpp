@@ -139,19 +139,19 @@ int chunk_len(const ia_desc* d, bool rm) {
   return rm && !ia::chunk_rm_supported(64, d->F, d->Dv, d->M) ? 32 : 64;
 }
 
-// The chunked path serves a call: bf16 chunk shapes (use_chunk_path), no gates, and with a
-// readout matrix a chunk length that has its instantiation.
+// The chunked path serves a call: bf16 chunk shapes (use_chunk_path), with a readout matrix a
+// chunk length that has its instantiation (no gates: the gated entry point takes no matrix).
 bool chunk_path_for(const ia_desc* d, bool rm, bool gated) {
-  if (gated || !use_chunk_path(d)) return false;
+  if ((rm && gated) || !use_chunk_path(d)) return false;
   return !rm || ia::chunk_rm_supported(chunk_len(d, true), d->F, d->Dv, d->M);
 }
 
-ChunkPlan chunk_plan(const ia_desc* d, bool rm = false) {
+ChunkPlan chunk_plan(const ia_desc* d, bool rm = false, bool gated = false) {
   ChunkPlan p{};
   p.C = chunk_len(d, rm);
   const int n_chunks = (d->N + p.C - 1) / p.C;
   const long seqs = long(d->B) * d->H;
-  int per_cu = ia::chunk_wgs_per_cu(p.C, d->F, d->Dv, d->M, rm);
+  int per_cu = ia::chunk_wgs_per_cu(p.C, d->F, d->Dv, d->M, rm, gated);
   if (per_cu <= 0) per_cu = 1;
   long G = long(ia::device_cus()) * per_cu / seqs;
   if (G > n_chunks) G = n_chunks;
@@ -256,7 +256,7 @@ size_t ia_prefill_workspace_bytes(const ia_desc* d) {
 
 // The prefill behind every prefill entry point: optional (b, n, h) strides of q, k, v, an
 // optional readout matrix ([H][M][M] complex64), and optional write / decay gates ([B][N][H]
-// float); a readout matrix or gates take the token-sequential path.
+// float).
 static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, const void* v,
                               const long long strides[3][3], const void* lambda,
                               const void* beta, const void* readout, ia_state* st, void* o,
@@ -280,7 +280,7 @@ static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, co
     if (sq.b != sk.b || sq.n != sk.n || sq.h != sk.h) return IA_ERR_UNSUPPORTED;
     // The chunk kernels address a chunk's rows with 32-bit byte offsets (as for the dense
     // layout in use_chunk_path).
-    if (!readout && !gated && use_chunk_path(d) &&
+    if (!readout && use_chunk_path(d) &&
         (64LL * sq.n * 2 > (1LL << 30) || 64LL * sv.n * 2 > (1LL << 30)))
       return IA_ERR_UNSUPPORTED;
   }
@@ -329,7 +329,7 @@ static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, co
   hipStream_t hs = static_cast<hipStream_t>(stream);
 
   if (chunk_path_for(d, readout != nullptr, gated)) {
-    const ChunkPlan pl = chunk_plan(d, readout != nullptr);
+    const ChunkPlan pl = chunk_plan(d, readout != nullptr, gated);
     if (!workspace || ws_bytes < pl.bytes) return IA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return IA_ERR_ALIGN;
     const Range rw = rng(workspace, pl.bytes);
@@ -362,6 +362,8 @@ static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, co
     a.tables = reinterpret_cast<unsigned char*>(ws + pl.tables_off);
     a.readout = static_cast<const float2*>(readout);
     a.rtab = readout ? reinterpret_cast<unsigned char*>(ws + pl.rtab_off) : nullptr;
+    a.wgate = wgate;
+    a.dgate = dgate;
     a.B = d->B; a.H = d->H; a.N = d->N; a.F = d->F; a.D = d->Dv; a.M = d->M;
     a.chunk = pl.C;
     a.segments = pl.G;
@@ -385,7 +387,8 @@ static ia_status prefill_impl(const ia_desc* d, const void* q, const void* k, co
   }
 
   // bf16 inputs on shapes without a chunk kernel are refused rather than run 300x slower by
-  // the token-sequential kernel (fp32 inputs take that path, as do gated calls).  A readout
+  // the token-sequential kernel (fp32 inputs take that path, as do gated calls on shapes
+  // without a chunk kernel).  A readout
   // matrix with bf16 inputs runs the token-sequential kernel only on shapes the chunk kernels
   // do not take at all; a chunk shape whose requested chunk length has no readout-matrix
   // instantiation is refused.
@@ -491,6 +494,7 @@ ia_status ia_prefill_fwd_readout(const ia_desc* d, const void* q, const void* k,
 
 size_t ia_prefill_gated_workspace_bytes(const ia_desc* d) {
   if (check_desc(d, true) != IA_OK) return 0;
+  if (chunk_path_for(d, false, true)) return chunk_plan(d, false, true).bytes;
   return scan_workspace(d, false).bytes;
 }
 

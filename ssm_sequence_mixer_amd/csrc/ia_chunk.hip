@@ -12,13 +12,24 @@ namespace ia {
   extern template hipError_t launch_state_t<C, FF, FF, MM>(const ChunkArgs&, int, hipStream_t, \
                                                            int);                          \
   extern template int chunk_occupancy_t<C, FF, FF, MM>();
+// The gated layer's kernels (ia_chunk_g*.hip).
+#define IA_EXTERN_G(C, FF, MM)                                                            \
+  extern template hipError_t launch_chunk_t<C, FF, FF, MM, false, true>(                   \
+      const ChunkArgs&, int, hipStream_t, int);                                           \
+  extern template hipError_t launch_state_t<C, FF, FF, MM, true>(const ChunkArgs&, int,    \
+                                                                 hipStream_t, int);       \
+  extern template int chunk_occupancy_t<C, FF, FF, MM, false, true>();
 #define IA_EXTERN_C(C)                                                                    \
   IA_EXTERN(C, 32, 16) IA_EXTERN(C, 32, 32) IA_EXTERN(C, 32, 64)                          \
   IA_EXTERN(C, 64, 16) IA_EXTERN(C, 64, 32) IA_EXTERN(C, 64, 64)                          \
-  IA_EXTERN(C, 128, 16) IA_EXTERN(C, 128, 32) IA_EXTERN(C, 128, 64)
+  IA_EXTERN(C, 128, 16) IA_EXTERN(C, 128, 32) IA_EXTERN(C, 128, 64)                       \
+  IA_EXTERN_G(C, 32, 16) IA_EXTERN_G(C, 32, 32) IA_EXTERN_G(C, 32, 64)                    \
+  IA_EXTERN_G(C, 64, 16) IA_EXTERN_G(C, 64, 32) IA_EXTERN_G(C, 64, 64)                    \
+  IA_EXTERN_G(C, 128, 16) IA_EXTERN_G(C, 128, 32) IA_EXTERN_G(C, 128, 64)
 IA_EXTERN_C(32)
 IA_EXTERN_C(64)
 #undef IA_EXTERN_C
+#undef IA_EXTERN_G
 #undef IA_EXTERN
 // The readout-matrix variant, for every shape whose LDS layout fits (all but C = 64 with
 // F = Dv = 128 and M = 64).
@@ -67,7 +78,8 @@ __global__ void __launch_bounds__(4 * M) chunk_tables_kernel(const float2* __res
 // ---------------------------------------------------------------- segment carry
 // Turns the end states of segments 0..G-2 (each from a zero state, in the slot layout) into
 // the states entering segments 1..G-1, in place:
-//   slot 0 <- lam^Ls (lam init) + slot 0,   slot g <- lam^Ls slot g-1 + slot g.
+//   slot 0 <- lam^Ls (lam init) + slot 0,   slot g <- lam^Ls slot g-1 + slot g
+// (gated: lam^Ls times segment g's decay product, held by slot g).
 // One thread per lane of a tile pair (4 Re, 4 Im values; a wave per pair, whose 16-lane rows
 // requantise it: SlotLayout) or per mode of lam eta; segments in order, the carried state in fp32.  Used
 // when the output pass would otherwise combine many slots per workgroup.  With slots_rev set
@@ -79,7 +91,8 @@ carry_slots_kernel(float* __restrict__ slots, float* __restrict__ slots_rev, int
                    const float2* __restrict__ U0,
                    const float2* __restrict__ G0, const float2* __restrict__ E0,
                    const float2* __restrict__ lam, const unsigned char* __restrict__ tables,
-                   long table_bytes, long pows_off, int H, int nslots, long slot_floats) {
+                   long table_bytes, long pows_off, int H, int nslots, long slot_floats,
+                   int gated) {
   using SL = SlotLayout<F, D, M>;
   constexpr int NS = SL::NS, NFT = SL::NFT, NDT = SL::NDT, MH = M / 16;
   constexpr int PAIRS = NS * (NFT + NDT) * MH * 64;
@@ -105,14 +118,18 @@ carry_slots_kernel(float* __restrict__ slots, float* __restrict__ slots_rev, int
     float2 c = E0 ? cmul(lamh[m], E0[(size_t)seq * M + m]) : make_float2(0.f, 0.f);
     for (int g0 = 0; g0 < nslots; g0 += KB) {
       float2 x[KB];
-#pragma unroll
-      for (int k = 0; k < KB; ++k)
-        if (g0 + k < nslots)
-          x[k] = reinterpret_cast<const float2*>(base + (size_t)(g0 + k) * slot_floats + SL::eta)[m];
+      float ds[KB];
 #pragma unroll
       for (int k = 0; k < KB; ++k)
         if (g0 + k < nslots) {
-          c = cfma(p, c, x[k]);
+          const float* sl = base + (size_t)(g0 + k) * slot_floats;
+          x[k] = reinterpret_cast<const float2*>(sl + SL::eta)[m];
+          ds[k] = gated ? sl[SL::dseg] : 1.f;
+        }
+#pragma unroll
+      for (int k = 0; k < KB; ++k)
+        if (g0 + k < nslots) {
+          c = cfma(make_float2(p.x * ds[k], p.y * ds[k]), c, x[k]);
           reinterpret_cast<float2*>(base + (size_t)(g0 + k) * slot_floats + SL::eta)[m] = c;
         }
     }
@@ -143,13 +160,14 @@ carry_slots_kernel(float* __restrict__ slots, float* __restrict__ slots_rev, int
   for (int q = 0; q < 4; ++q) pq[q] = pows[is_u ? 16 * mt + il : 16 * mt + 4 * gq + q];
   for (int g0 = 0; g0 < nslots; g0 += KB) {
     uint4 v[KB];
-    float is[KB];
+    float is[KB], ds[KB];
 #pragma unroll
     for (int k = 0; k < KB; ++k)
       if (g0 + k < nslots) {
         const float* sl = base + (size_t)(g0 + k) * slot_floats;
         v[k] = *reinterpret_cast<const uint4*>(sl + po);
         is[k] = sl[so];
+        ds[k] = gated ? sl[SL::dseg] : 1.f;
       }
     // Carried states of the batch in fp32, then their row maxima reduced together (the
     // shuffles overlap), then each quantised to its slot.
@@ -163,8 +181,9 @@ carry_slots_kernel(float* __restrict__ slots, float* __restrict__ slots_rev, int
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float xr = cr[q], yi = ci[q];
-          cr[q] = pq[q].x * xr - pq[q].y * yi + rr[q];
-          ci[q] = pq[q].x * yi + pq[q].y * xr + ii[q];
+          const float px = pq[q].x * ds[k], py = pq[q].y * ds[k];
+          cr[q] = px * xr - py * yi + rr[q];
+          ci[q] = px * yi + py * xr + ii[q];
           vr[k][q] = cr[q];
           vi[k][q] = ci[q];
           mx[k] = fmaxf(mx[k], fmaxf(fabsf(cr[q]), fabsf(ci[q])));
@@ -199,7 +218,7 @@ static hipError_t launch_carry_t(const ChunkPrefillArgs& p, long tb, long pows_o
   hipLaunchKernelGGL((carry_slots_kernel<F, D, M>),
                      dim3((n + 255) / 256, p.slots_rev ? 2 * seqs : seqs), dim3(256), 0, st,
                      p.slots, p.slots_rev, seqs, p.U0, p.G0, p.E0, p.lam, p.tables, tb, pows_off,
-                     p.H, nslots, slot_floats);
+                     p.H, nslots, slot_floats, p.wgate != nullptr);
   prof_end(st, kKindCarry);
   return hipGetLastError();
 }
@@ -221,8 +240,11 @@ static hipError_t launch_carry(const ChunkPrefillArgs& p, long tb, long pows_off
 template <int C>
 static hipError_t dispatch_fdm(const ChunkArgs& a, int F, int D, int M, int n_wg,
                                hipStream_t st, int kind) {
-#define IA_CASE(FF, MM)                                   \
-  if (F == FF && D == FF && M == MM) return launch_chunk_t<C, FF, FF, MM>(a, n_wg, st, kind);
+  const bool gt = a.wgate != nullptr;
+#define IA_CASE(FF, MM)                                                                 \
+  if (F == FF && D == FF && M == MM)                                                    \
+    return gt ? launch_chunk_t<C, FF, FF, MM, false, true>(a, n_wg, st, kind)           \
+              : launch_chunk_t<C, FF, FF, MM>(a, n_wg, st, kind);
   IA_CASE(32, 16) IA_CASE(32, 32) IA_CASE(32, 64)
   IA_CASE(64, 16) IA_CASE(64, 32) IA_CASE(64, 64)
   IA_CASE(128, 16) IA_CASE(128, 32) IA_CASE(128, 64)
@@ -248,8 +270,11 @@ static hipError_t dispatch_fdm_rm(const ChunkArgs& a, int F, int D, int M, int n
 template <int C>
 static hipError_t dispatch_state_fdm(const ChunkArgs& a, int F, int D, int M, int n_wg,
                                      hipStream_t st, int kind) {
-#define IA_CASE(FF, MM)                                   \
-  if (F == FF && D == FF && M == MM) return launch_state_t<C, FF, FF, MM>(a, n_wg, st, kind);
+  const bool gt = a.wgate != nullptr;
+#define IA_CASE(FF, MM)                                                                 \
+  if (F == FF && D == FF && M == MM)                                                    \
+    return gt ? launch_state_t<C, FF, FF, MM, true>(a, n_wg, st, kind)                  \
+              : launch_state_t<C, FF, FF, MM>(a, n_wg, st, kind);
   IA_CASE(32, 16) IA_CASE(32, 32) IA_CASE(32, 64)
   IA_CASE(64, 16) IA_CASE(64, 32) IA_CASE(64, 64)
   IA_CASE(128, 16) IA_CASE(128, 32) IA_CASE(128, 64)
@@ -295,7 +320,19 @@ long chunk_table_bytes(int chunk, int M) {
   return 0;
 }
 
-int chunk_wgs_per_cu(int chunk, int F, int D, int M, bool rm) {
+int chunk_wgs_per_cu(int chunk, int F, int D, int M, bool rm, bool gated) {
+  if (gated) {
+#define IA_OCC(CC, FF, MM) \
+  if (chunk == CC && F == FF && D == FF && M == MM) return chunk_occupancy_t<CC, FF, FF, MM, false, true>();
+    IA_OCC(32, 32, 16) IA_OCC(32, 32, 32) IA_OCC(32, 32, 64)
+    IA_OCC(32, 64, 16) IA_OCC(32, 64, 32) IA_OCC(32, 64, 64)
+    IA_OCC(32, 128, 16) IA_OCC(32, 128, 32) IA_OCC(32, 128, 64)
+    IA_OCC(64, 32, 16) IA_OCC(64, 32, 32) IA_OCC(64, 32, 64)
+    IA_OCC(64, 64, 16) IA_OCC(64, 64, 32) IA_OCC(64, 64, 64)
+    IA_OCC(64, 128, 16) IA_OCC(64, 128, 32) IA_OCC(64, 128, 64)
+#undef IA_OCC
+    return 0;
+  }
   if (rm) {
 #define IA_OCC(CC, FF, MM) \
   if (chunk == CC && F == FF && D == FF && M == MM) return chunk_occupancy_t<CC, FF, FF, MM, true>();
@@ -405,6 +442,8 @@ hipError_t launch_chunk_prefill(const ChunkPrefillArgs& p, hipStream_t st) {
   a.wU = p.wU;
   a.wG = p.wG;
   a.wE = p.wE;
+  a.wgate = p.wgate;
+  a.dgate = p.dgate;
 
   auto go = [&](const ChunkArgs& x, int n_wg, int kind) -> hipError_t {
     if (p.readout)

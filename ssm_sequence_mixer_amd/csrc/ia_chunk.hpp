@@ -220,7 +220,9 @@ struct SlotLayout {
   static constexpr int NP = (NFT + NDT) * MH;           // tile pairs per wave
   static constexpr long scale = (long)NS * NP * 64 * 4;  // float offset of the 2^-s
   static constexpr long eta = scale + NS * NP * 4;       // float offset of lam eta
-  static constexpr long floats = eta + 2L * M;
+  static constexpr long dseg = eta + 2L * M;             // gated layer: the segment's decay
+                                                         // product (prod of its a_t)
+  static constexpr long floats = dseg + 4;
   static_assert(scale % 4 == 0 && eta % 4 == 0 && floats % 4 == 0, "16-byte aligned slots");
   __device__ static long pair(int u, int p, int lane) {
     return ((long)(u * NP + p) * 64 + lane) * 4;
@@ -278,7 +280,7 @@ __device__ __forceinline__ void slot_get(const float* slot, long pair_off, long 
 
 // ---------------------------------------------------------------- LDS layout
 
-template <int C, int F, int D, int M, int NR, bool RM = false>
+template <int C, int F, int D, int M, int NR, bool RM = false, bool GT = false>
 struct Layout {
   static constexpr int M2 = 2 * M;
   // 16-bit element offsets; every matrix is swizzled by row (see soff).
@@ -305,7 +307,25 @@ struct Layout {
   static constexpr int L2S = M + 2;                // row stride of the lam^(2i) factor table
   static constexpr int bL2lo = bPowS + M * 8;      // [16][L2S] float2 lam^(2i), i = 0..15
   static constexpr int bL2hi = bL2lo + 16 * L2S * 8;  // [NR][M] float2 lam^(32r)
-  static constexpr int bytes = bL2hi + NR * M * 8;
+  static constexpr int bL2end = bL2hi + NR * M * 8;
+  // Gated layer: two buffers of a chunk's gate records (GateRec), chunk c in buffer c % 2.
+  static constexpr int bRec = bL2end;
+  static constexpr int recBytes = (3 * C + 4) * 4;
+  static constexpr int bytes = bRec + (GT ? 2 * recBytes : 0);
+};
+
+// Gate records of one chunk (gated layer), float offsets within a record buffer.  With a_s, w_s
+// the decay and write gates of the chunk's tokens s = 0..C-1 in walk order (a = 1, w = 0 past
+// the sequence end), L_j = sum_{s<=j} log2|a_s| and sigma_j the sign of prod_{s<=j} a_s:
+//   L[j] = L_j,   W[j] = sigma_j w_j,
+//   E[j] = w_j prod_{s=j+1}^{C-1} a_s = sigma_{C-1} W[j] 2^(L_{C-1} - L_j),
+//   D    = prod_s a_s = sigma_{C-1} 2^(L_{C-1}).
+// Then w_j prod_{s=j+1}^{i} a_s = sigma_i W[j] 2^(L_i - L_j) and prod_{s<=i} a_s =
+// sigma_i 2^(L_i); the factor sigma_i of query i multiplies its numerator and denominator
+// alike and is dropped.  |a| below 2^-64 counts as 2^-64 (the log stays finite).
+template <int C>
+struct GateRec {
+  static constexpr int L = 0, W = C, E = 2 * C, D = 3 * C, floats = 3 * C + 4;
 };
 
 struct ChunkArgs {
@@ -338,6 +358,8 @@ struct ChunkArgs {
   // then hold the initial state) or, without a caller state, on the zeroed workspace state
   // wU/wG/wE (same layout).
   float2 *wU, *wG, *wE;
+  // Gated layer: write and decay gates, float [B][N][H] (element (b, n, h) at (b N + n) H + h).
+  const float *wgate, *dgate;
   const float* seg_prev;
   int seg_inclusive;                           // seg_prev[g] already holds the state entering
                                                // segment g+1 (caller state included)
@@ -508,11 +530,99 @@ __device__ __forceinline__ void wait_vm_zero() {
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 }
 
+// ---------------------------------------------------------------- gate records (gated layer)
+// Raw gates (decay, write) of token `lane` of chunk c in walk order for one wave; tokens past
+// the sequence end read its last token, and gate_scan clears them.
+__device__ __forceinline__ float2 gate_fetch(const ChunkArgs& a, int b, int h, int dir, int c,
+                                             int C, int lane) {
+  const int t = min(c * C + lane, a.N - 1);
+  const size_t gi = ((size_t)b * a.N + (dir ? a.N - 1 - t : t)) * a.H + h;
+  return make_float2(a.dgate[gi], a.wgate[gi]);
+}
+
+// Lane j of a wave, token j of a chunk (valid: inside the chunk and the sequence): the
+// records of GateRec by inclusive scans over the wave's lanes (padding tokens a = 1, w = 0, so
+// lane 63 holds the chunk's totals whatever C).
+struct GateScan {
+  float l;     // L_j
+  float w;     // sigma_j w_j
+  float e;     // w_j prod_{s=j+1}^{C-1} a_s
+  float d;     // prod_s a_s (every lane)
+};
+__device__ __forceinline__ GateScan gate_scan(float2 raw, bool valid, int lane) {
+  const float av = valid ? raw.x : 1.f, wv = valid ? raw.y : 0.f;
+  const float mag = fabsf(av);
+  float l = mag < 0x1p-64f ? -64.f : __builtin_amdgcn_logf(mag);   // log2 (NaN stays NaN)
+  int neg = av < 0.f ? 1 : 0;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float lu = __shfl_up(l, o);
+    const int nu = __shfl_up(neg, o);
+    if (lane >= o) {
+      l += lu;
+      neg += nu;
+    }
+  }
+  const float l_last = __shfl(l, 63);
+  const float s_last = (__shfl(neg, 63) & 1) ? -1.f : 1.f;
+  GateScan r;
+  r.l = l;
+  r.w = (neg & 1) ? -wv : wv;
+  r.e = s_last * r.w * __builtin_amdgcn_exp2f(l_last - l);
+  r.d = s_last * __builtin_amdgcn_exp2f(l_last);
+  return r;
+}
+
+// A chunk's gate records into one record buffer (GateRec).
+template <int C>
+__device__ __forceinline__ void gate_records(float2 raw, bool valid, int lane, float* rec) {
+  using GR = GateRec<C>;
+  const GateScan g = gate_scan(raw, valid, lane);
+  if (lane < C) {
+    rec[GR::L + lane] = g.l;
+    rec[GR::W + lane] = g.w;
+    rec[GR::E + lane] = g.e;
+  }
+  if (lane == 0) rec[GR::D] = g.d;
+}
+
+// Gate factors of one 16 x 16 accumulator tile whose rows are keys j = j0 + q (q = 0..3, this
+// lane's entries) and whose column is query i (this lane): S[i,j] and P[i,j] times
+// W[j] 2^(L_i - L_j), zero past the causal diagonal (diag: the tile holding j = i).
+template <int C>
+__device__ __forceinline__ void gate_tile(f32x4& t, const float* rec, float li, int j0,
+                                          bool diag, int g, int il) {
+  using GR = GateRec<C>;
+  const float4 L4 = *reinterpret_cast<const float4*>(rec + GR::L + j0);
+  const float4 W4 = *reinterpret_cast<const float4*>(rec + GR::W + j0);
+  const float lj[4] = {L4.x, L4.y, L4.z, L4.w}, wj[4] = {W4.x, W4.y, W4.z, W4.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float f = __builtin_amdgcn_exp2f(li - lj[q]) * wj[q];
+    t[q] *= (!diag || 4 * g + q <= il) ? f : 0.f;
+  }
+}
+
+// A state operand fragment whose K slots are keys 32kb + 4g + (0..3) (slots 0..3) and
+// 32kb + 16 + 4g + (0..3) (slots 4..7), times those keys' end factors E[j] (GateRec).
+template <int C>
+__device__ __forceinline__ bf16x8 gate_frag(bf16x8 f, const float* rec, int kb, int g) {
+  using GR = GateRec<C>;
+  const float4 e0 = *reinterpret_cast<const float4*>(rec + GR::E + 32 * kb + 4 * g);
+  const float4 e1 = *reinterpret_cast<const float4*>(rec + GR::E + 32 * kb + 16 + 4 * g);
+  const float e[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+  bf16x8 r;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) r[k] = (__bf16)((float)f[k] * e[k]);
+  return r;
+}
+
 // ---------------------------------------------------------------- readout waves
 // Wave R owns queries [16R, 16R+16) of every chunk.
-template <int C, int F, int D, int M, int R, bool RM>
+template <int C, int F, int D, int M, int R, bool RM, bool GT>
 __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F, D, M>& x) {
-  using Lay = Layout<C, F, D, M, C / 16, RM>;
+  using Lay = Layout<C, F, D, M, C / 16, RM, GT>;
+  using GR = GateRec<C>;
   constexpr int NR = C / 16;
   constexpr int M2 = 2 * M;
   constexpr int MH = M / 16;
@@ -571,10 +681,23 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
     for (int t = 0; t < NV; ++t) *reinterpret_cast<uint4*>(x.s16 + stV[t]) = rv[t];
   };
 
+  // Gated layer: wave 0 turns each chunk's gates into its records (GateRec), chunk c into
+  // buffer c % 2: the first chunk's before the loop, chunk c+1's in chunk c's second phase
+  // (chunk c-1, the buffer's last reader, is done), from gates loaded at chunk c's start.
+  float* const recb = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(x.s16) + Lay::bRec);
+  auto rec_of = [&](int c) { return recb + (c & 1) * GR::floats; };
+  float2 graw = make_float2(1.f, 0.f);
+  auto gate_valid = [&](int c) { return lane < C && c * C + lane < a.N; };
+
   // The first chunk's v loads go out before the barrier and land while the state waves copy
   // the tables.
-  if (x.c_begin < x.c_end) fetch_v(x.c_begin);
+  if (x.c_begin < x.c_end) {
+    fetch_v(x.c_begin);
+    if constexpr (GT && r == 0) graw = gate_fetch(a, x.b, x.h, a.dir, x.c_begin, C, lane);
+  }
   __syncthreads();  // tables visible
+  if constexpr (GT && r == 0)
+    if (x.c_begin < x.c_end) gate_records<C>(graw, gate_valid(x.c_begin), lane, rec_of(x.c_begin));
   // lam^(2i) for this lane's queries i = 16r + il and modes m = 16mt + 4g + q, for the whole
   // segment: the product of the two factor tables, formed once.  With a readout matrix the
   // tables hold lam^i factors instead: A = lam^i A' before the mixing, lam^i (A R) after it.
@@ -599,7 +722,11 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
     // v of chunk c into LDS (its readers run after the mid-chunk barrier), the next chunk's
     // loads out.
     write_v();
-    if (c + 1 < x.c_end) fetch_v(c + 1);
+    if (c + 1 < x.c_end) {
+      fetch_v(c + 1);
+      if constexpr (GT && r == 0) graw = gate_fetch(a, x.b, x.h, a.dir, c + 1, C, lane);
+    }
+    const float* const rec = rec_of(c);
     if constexpr (kEarlyO) {
       const int t = c * C + 16 * r + il;
       if (a.accumulate && x.want_out && t < a.N) {
@@ -621,6 +748,7 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
     // scale and the inter-chunk denominator.
     f16x8 Af[KM];
     float si = 1.f, den_inter = 0.f;
+    float li = 0.f, di = 1.f;   // gated: L_i and 2^(L_i) of this lane's query
     if (x.want_out) {
       // phi(q) of this wave's queries as B operands (K = f)
       bf16x8 fq[KF];
@@ -651,6 +779,18 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
         for (int kt = 0; kt < TM; ++kt)
           accA[kt] = mma_bf16(lds8(s16 + oLU[s] + 16 * kt * F).b, fq[s], accA[kt]);
         IA_STEP_FENCE();
+      }
+      // Gated: the inter-chunk term times the decay since the chunk start, 2^(L_i), and each
+      // S[i,j] times the gate factor W[j] 2^(L_i - L_j) (zero past the diagonal).
+      if constexpr (GT) {
+        li = rec[GR::L + 16 * r + il];
+        di = __builtin_amdgcn_exp2f(li);
+#pragma unroll
+        for (int kt = 0; kt < TM; ++kt)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) accA[kt][q] *= di;
+#pragma unroll
+        for (int jt = 0; jt <= r; ++jt) gate_tile<C>(accS[jt], rec, li, 16 * jt + 4 * g, jt == r, g, il);
       }
       // causal mask of the diagonal S tile, then S as the bf16 operand of WT^T S
 #pragma unroll
@@ -730,6 +870,7 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
         IA_STEP_FENCE();
       }
       den_inter = xor_sum16_32(den_inter);
+      if constexpr (GT) den_inter *= di;   // eta_c decays by 2^(L_i) as well
       amax = xor_max16_32(amax);
       si = pow2_scale(amax);
 #pragma unroll
@@ -759,6 +900,10 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
         accP[jt] = acc;
       }
       IA_STEP_FENCE();
+      if constexpr (GT) {
+#pragma unroll
+        for (int jt = 0; jt <= r; ++jt) gate_tile<C>(accP[jt], rec, li, 16 * jt + 4 * g, jt == r, g, il);
+      }
       // ---- c_d-scaled Re(A lam G) per value tile (rows d, columns i)
       f32x4 accX[TD];
 #pragma unroll
@@ -807,7 +952,10 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
             accI = mma_bf16(ldtr<D>(s16, oV[dt], kb).b, Pf[kb], accI);
         const f32x4 accXd = accX[dt];
         if (ok) {
-          const float4 ci = *reinterpret_cast<const float4*>(sb + oCi + 64 * dt);
+          float4 ci = *reinterpret_cast<const float4*>(sb + oCi + 64 * dt);
+          if constexpr (GT) {   // G_c decays by 2^(L_i) as well
+            ci.x *= di; ci.y *= di; ci.z *= di; ci.w *= di;
+          }
           float val[4] = {(accI[0] + accXd[0] * ci.x) * rd, (accI[1] + accXd[1] * ci.y) * rd,
                           (accI[2] + accXd[2] * ci.z) * rd, (accI[3] + accXd[3] * ci.w) * rd};
           if (a.out_bf16) {
@@ -834,6 +982,8 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
         IA_STEP_FENCE();
       }
     }
+    if constexpr (GT && r == 0)
+      if (c + 1 < x.c_end) gate_records<C>(graw, gate_valid(c + 1), lane, rec_of(c + 1));
     __syncthreads();   // chunk c read by every wave
   }
 }
@@ -842,10 +992,11 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
 // State wave U owns feature tiles ft = U, U+NS, ... of (lam U)^T and value tiles dt = U,
 // U+NS, ... of lam G, in fp32 MFMA accumulators for the whole segment; wave 0 also owns
 // lam eta.
-template <int C, int F, int D, int M, int U, bool RM>
+template <int C, int F, int D, int M, int U, bool RM, bool GT>
 __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D, M>& x) {
   using TL = TableLayout<C, M>;
-  using Lay = Layout<C, F, D, M, C / 16, RM>;
+  using Lay = Layout<C, F, D, M, C / 16, RM, GT>;
+  using GR = GateRec<C>;
   constexpr int M2 = 2 * M;
   constexpr int MH = M / 16;
   constexpr int TM = M2 / 16;
@@ -1023,6 +1174,9 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
       const float* sl = a.seg_prev + ((size_t)x.seq * a.slots_per_seq + sp) * a.slot_floats;
       float2 e = make_float2(0.f, 0.f);
       if (u == 0 && lane < M) e = reinterpret_cast<const float2*>(sl + SL::eta)[lane];
+      // gated: the state entering segment sp also decays by the segment's gate product
+      const float ds = GT ? sl[SL::dseg] : 1.f;
+      auto pws = [&](float2 p) { return GT ? make_float2(p.x * ds, p.y * ds) : p; };
       // lam U tile pairs: this wave's MH pairs loaded together, then combined
 #pragma unroll
       for (int fi = 0; fi < NFT; ++fi)
@@ -1036,7 +1190,7 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
           }
 #pragma unroll
           for (int mt = 0; mt < MH; ++mt) {
-            const float2 pw = f2(oPl + dS + 128 * mt);
+            const float2 pw = pws(f2(oPl + dS + 128 * mt));
             float er[4], ei[4];
             slot_unpack(v[mt], is[mt], er, ei);
 #pragma unroll
@@ -1065,7 +1219,7 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
             slot_unpack(v[mt], is[mt], er, ei);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const float2 pw = f2(oPg + dS + 8 * (16 * mt + q));
+              const float2 pw = pws(f2(oPg + dS + 8 * (16 * mt + q)));
               const float xr = accG[di][mt][q], yi = accG[di][mt + MH][q];
               accG[di][mt][q] = pw.x * xr - pw.y * yi + er[q];
               accG[di][mt + MH][q] = pw.x * yi + pw.y * xr + ei[q];
@@ -1073,7 +1227,7 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
           }
         }
       if (u == 0 && lane < M) {
-        eta = cmul(f2(oLn + (Lay::bPowS - Lay::bLE)), eta);
+        eta = cmul(pws(f2(oLn + (Lay::bPowS - Lay::bLE))), eta);
         eta.x += e.x;
         eta.y += e.y;
       }
@@ -1173,18 +1327,44 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
   // lam U^T <- lam^L (lam U^T + phi(K)^T (beta lam^-j)).  Second, once v of chunk c is in
   // LDS: lam G <- lam G + W^T V (its decay waits for the next first phase), and chunk c+1's
   // copies and inputs.
+  // Gated: this chunk's records (GateRec; buffer c % 2, written by readout wave 0), and
+  // lam beta of mode `lane` for the eta update.
+  const float* const recb =
+      reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(x.s16) + Lay::bRec);
+  float2 lam_m = make_float2(0.f, 0.f), lb_m = lam_m;
+  if constexpr (GT && u == 0) {
+    const int m = lane < M ? lane : 0;
+    lam_m = lamh[m];
+    lb_m = cmul(lam_m, a.beta[(size_t)x.h * M + m]);
+  }
   for (int c = x.c_begin; c < x.c_end; ++c) {
+    const float* const rec = recb + (c & 1) * GR::floats;
+    const float dl = GT ? rec[GR::D] : 1.f;   // gated: the chunk's decay product
     if (c > x.c_begin) {
       decay_g(c - 1);
       if (x.want_out) pack_state();
     }
     if (x.want_out) write_g();
+    // Gated: lam U_{c+1} = lam^L (D lam U_c + sum_j beta lam^-j E[j] phi(k_j)).
+    if constexpr (GT) {
+#pragma unroll
+      for (int fi = 0; fi < NFT; ++fi)
+        if (u + NS * fi < F / 16) {
+#pragma unroll
+          for (int kt = 0; kt < TM; ++kt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) accU[fi][kt][q] *= dl;
+        }
+    }
 #pragma unroll
     for (int kb = 0; kb < KC; ++kb) {
       bf16x8 afk[NFT];
 #pragma unroll
       for (int fi = 0; fi < NFT; ++fi)
-        if (u + NS * fi < F / 16) afk[fi] = ldtr<F>(s16, trF[fi], kb).b;
+        if (u + NS * fi < F / 16) {
+          afk[fi] = ldtr<F>(s16, trF[fi], kb).b;
+          if constexpr (GT) afk[fi] = gate_frag<C>(afk[fi], rec, kb, g);
+        }
 #pragma unroll
       for (int kt = 0; kt < TM; ++kt) {
         const bf16x8 w = lds8(s16 + offC[kb] + 16 * kt * C).b;
@@ -1211,18 +1391,47 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
         }
       }
     if (u == 0 && lane < M) {
-      const float2 ge = f2(oLn + tsel + (Lay::bGeo - Lay::bLE));
-      eta = cmul(f2(oLn + tsel + (Lay::bPowL - Lay::bLE)),
-                 make_float2(eta.x + ge.x, eta.y + ge.y));
+      if constexpr (GT) {
+        // lam eta <- lam^L D lam eta + lam beta sum_{j<L} lam^(L-1-j) E[j] (Horner in fp32)
+        const int Lc = min(C, a.N - c * C);
+        float2 hs = make_float2(0.f, 0.f);
+        for (int j4 = 0; j4 < C; j4 += 4) {
+          const float4 e4 = *reinterpret_cast<const float4*>(rec + GR::E + j4);
+          const float ev[4] = {e4.x, e4.y, e4.z, e4.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (j4 + q < Lc) hs = cfma(lam_m, hs, make_float2(ev[q], 0.f));
+        }
+        const float2 pl = f2(oLn + tsel + (Lay::bPowL - Lay::bLE));
+        eta = cfma(lb_m, hs, cmul(pl, make_float2(dl * eta.x, dl * eta.y)));
+      } else {
+        const float2 ge = f2(oLn + tsel + (Lay::bGeo - Lay::bLE));
+        eta = cmul(f2(oLn + tsel + (Lay::bPowL - Lay::bLE)),
+                   make_float2(eta.x + ge.x, eta.y + ge.y));
+      }
     }
     const bool more = c + 1 < x.c_end;
     __syncthreads();    // mid-chunk: phi(q), phi(k), lam U of chunk c no longer read
+    // Gated: lam G <- D lam G + W^T (E V) (lam G_c was packed for the readout in phase one).
+    if constexpr (GT) {
+#pragma unroll
+      for (int di = 0; di < NDT; ++di)
+        if (u + NS * di < TD) {
+#pragma unroll
+          for (int kt = 0; kt < TM; ++kt)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) accG[di][kt][q] *= dl;
+        }
+    }
 #pragma unroll
     for (int kb = 0; kb < KC; ++kb) {
       bf16x8 bv[NDT];
 #pragma unroll
       for (int di = 0; di < NDT; ++di)
-        if (u + NS * di < TD) bv[di] = ldtr<D>(s16, trD[di], kb).b;
+        if (u + NS * di < TD) {
+          bv[di] = ldtr<D>(s16, trD[di], kb).b;
+          if constexpr (GT) bv[di] = gate_frag<C>(bv[di], rec, kb, g);
+        }
 #pragma unroll
       for (int kt = 0; kt < TM; ++kt) {
         const bf16x8 w = lds8(s16 + offC[kb] + 16 * kt * C).b;
@@ -1290,11 +1499,11 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
 // The fp32 route of a head whose modes the bf16 chunk factorisation does not resolve
 // (chunk_unresolved): the token-by-token recurrence of slice (b, h) over all N tokens by this
 // workgroup, from the caller's state (updated in place) or from zero in the workspace state.
-template <int C, int F, int D, int M, bool RM>
+template <int C, int F, int D, int M, bool RM, bool GT>
 __device__ __forceinline__ void fp32_route(const ChunkArgs& a, int b, int h, unsigned char* smem) {
   constexpr int NW = C / 16 + StateWaves<F, D, M>::NS;
   using S = SeqSmem<NW, F, D, M, RM>;
-  static_assert(sizeof(S) <= Layout<C, F, D, M, C / 16, RM>::bytes, "fits the kernel's LDS");
+  static_assert(sizeof(S) <= Layout<C, F, D, M, C / 16, RM, GT>::bytes, "fits the kernel's LDS");
   S& s = *reinterpret_cast<S*>(smem);
   const size_t seq = (size_t)b * a.H + h;
   float2 *U, *G, *E;
@@ -1311,30 +1520,35 @@ __device__ __forceinline__ void fp32_route(const ChunkArgs& a, int b, int h, uns
     for (int i = threadIdx.x; i < M; i += 64 * NW) E[i] = make_float2(0.f, 0.f);
     __syncthreads();
   }
-  const SeqScanArgs sa{a.q, a.k, a.v, a.sqk, a.sv, a.lam, a.beta, a.o, a.accumulate, a.N, a.H,
-                       F, D, M, 1, a.out_bf16, a.clamp, a.dir, a.opt,
-                       RM ? a.readout : nullptr};
+  SeqScanArgs sa{a.q, a.k, a.v, a.sqk, a.sv, a.lam, a.beta, a.o, a.accumulate, a.N, a.H,
+                 F, D, M, 1, a.out_bf16, a.clamp, a.dir, a.opt,
+                 RM ? a.readout : nullptr};
+  if constexpr (GT) {
+    sa.wgate = a.wgate;
+    sa.dgate = a.dgate;
+  }
   seq_scan(s, sa, b, h, U, G, E);
 }
 
-template <int C, int F, int D, int M, bool RM, int W>
+template <int C, int F, int D, int M, bool RM, bool GT, int W>
 __device__ __forceinline__ void run_role(const ChunkArgs& a, const Ctx<C, F, D, M>& x) {
   if constexpr (W < C / 16)
-    readout_main<C, F, D, M, W, RM>(a, x);
+    readout_main<C, F, D, M, W, RM, GT>(a, x);
   else
-    state_main<C, F, D, M, W - C / 16, RM>(a, x);
+    state_main<C, F, D, M, W - C / 16, RM, GT>(a, x);
 }
 
-template <int C, int F, int D, int M, bool RM, int... Ws>
+template <int C, int F, int D, int M, bool RM, bool GT, int... Ws>
 __device__ __forceinline__ void dispatch_role(const ChunkArgs& a, const Ctx<C, F, D, M>& x,
                                               int w, std::integer_sequence<int, Ws...>) {
-  ((w == Ws ? (run_role<C, F, D, M, RM, Ws>(a, x), 0) : 0), ...);
+  ((w == Ws ? (run_role<C, F, D, M, RM, GT, Ws>(a, x), 0) : 0), ...);
 }
-// RM: the readout matrix variant (a R in place of a before both readouts).
-template <int C, int F, int D, int M, bool RM>
+// RM: the readout matrix variant (a R in place of a before both readouts).  GT: the gated
+// layer (write and decay gates per token, GateRec).
+template <int C, int F, int D, int M, bool RM, bool GT>
 __global__ void __launch_bounds__(64 * (C / 16 + StateWaves<F, D, M>::NS))
 chunk_prefill_kernel(const ChunkArgs a) {
-  using Lay = Layout<C, F, D, M, C / 16, RM>;
+  using Lay = Layout<C, F, D, M, C / 16, RM, GT>;
   using TL = TableLayout<C, M>;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   uint16_t* s16 = reinterpret_cast<uint16_t*>(smem_raw);
@@ -1380,7 +1594,7 @@ chunk_prefill_kernel(const ChunkArgs a) {
   x.want_out = a.o != nullptr;
   x.tab = a.tables + (size_t)x.h * a.table_bytes;
   if (__builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(x.tab + TL::oRoute))) {
-    if (x.seg == a.seg_first) fp32_route<C, F, D, M, RM>(a, x.b, x.h, smem_raw);
+    if (x.seg == a.seg_first) fp32_route<C, F, D, M, RM, GT>(a, x.b, x.h, smem_raw);
     return;
   }
 
@@ -1397,7 +1611,7 @@ chunk_prefill_kernel(const ChunkArgs a) {
   static_assert(Lay::oWb == Lay::oWT + 2 * M * C, "decay tables adjacent");
   static_assert(Lay::bL2hi == Lay::bL2lo + 16 * Lay::L2S * 8, "factor tables adjacent");
   static_assert(TL::nW == 2L * (Lay::oLU - Lay::oWT), "decay table size");
-  static_assert(TL::nL2 == Lay::bytes - Lay::bL2lo, "factor table size");
+  static_assert(TL::nL2 == Lay::bL2end - Lay::bL2lo, "factor table size");
   static_assert(Lay::bGeoT - Lay::bGeo == Lay::kTail, "tail pair at one offset");
   static_assert(Lay::bPowS == Lay::bPowL + 4 * 8 * M, "lam^Ls after the decay pairs");
   static_assert(TL::oPowT - TL::oPow == 2 * 8 * M && TL::oGeoT - TL::oGeo == 2 * 8 * M,
@@ -1410,17 +1624,17 @@ chunk_prefill_kernel(const ChunkArgs a) {
                 "per-mode arrays adjacent in the table");
   static_assert((Lay::oWT * 2) % 16 == 0 && Lay::bL2lo % 16 == 0 && Lay::bPowL % 16 == 0 &&
                 TL::nW % 16 == 0 && TL::nL2 % 16 == 0 && (40 * M) % 16 == 0, "16-byte copies");
-  dispatch_role<C, F, D, M, RM>(
+  dispatch_role<C, F, D, M, RM, GT>(
       a, x, x.wave, std::make_integer_sequence<int, C / 16 + StateWaves<F, D, M>::NS>{});
 }
 
-template <int C, int F, int D, int M, bool RM>
+template <int C, int F, int D, int M, bool RM, bool GT>
 hipError_t chunk_kernel_attr() {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&chunk_prefill_kernel<C, F, D, M, RM>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, Layout<C, F, D, M, C / 16, RM>::bytes);
+        reinterpret_cast<const void*>(&chunk_prefill_kernel<C, F, D, M, RM, GT>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, Layout<C, F, D, M, C / 16, RM, GT>::bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -1429,31 +1643,31 @@ hipError_t chunk_kernel_attr() {
 
 // Workgroups of the output-pass kernel one CU holds at once (LDS, registers, waves), or 0 if
 // the runtime cannot say (no device).
-template <int C, int F, int D, int M, bool RM = false>
+template <int C, int F, int D, int M, bool RM = false, bool GT = false>
 int chunk_occupancy_t() {
-  if (chunk_kernel_attr<C, F, D, M, RM>() != hipSuccess) return 0;
+  if (chunk_kernel_attr<C, F, D, M, RM, GT>() != hipSuccess) return 0;
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&chunk_prefill_kernel<C, F, D, M, RM>),
-          64 * (C / 16 + StateWaves<F, D, M>::NS), Layout<C, F, D, M, C / 16, RM>::bytes) !=
+          &n, reinterpret_cast<const void*>(&chunk_prefill_kernel<C, F, D, M, RM, GT>),
+          64 * (C / 16 + StateWaves<F, D, M>::NS), Layout<C, F, D, M, C / 16, RM, GT>::bytes) !=
       hipSuccess)
     return 0;
   return n;
 }
 
-template <int C, int F, int D, int M, bool RM = false>
+template <int C, int F, int D, int M, bool RM = false, bool GT = false>
 hipError_t launch_chunk_t(const ChunkArgs& a, int n_wg, hipStream_t st, int kind) {
   constexpr int threads = 64 * (C / 16 + StateWaves<F, D, M>::NS);
-  constexpr int bytes = Layout<C, F, D, M, C / 16, RM>::bytes;
+  constexpr int bytes = Layout<C, F, D, M, C / 16, RM, GT>::bytes;
   static_assert(bytes <= 160 * 1024, "LDS budget");
   {
-    hipError_t e = chunk_kernel_attr<C, F, D, M, RM>();
+    hipError_t e = chunk_kernel_attr<C, F, D, M, RM, GT>();
     if (e != hipSuccess) return e;
   }
   (void)hipGetLastError();
   prof_begin(st);
-  hipLaunchKernelGGL((chunk_prefill_kernel<C, F, D, M, RM>), dim3(n_wg), dim3(threads), bytes, st,
-                     a);
+  hipLaunchKernelGGL((chunk_prefill_kernel<C, F, D, M, RM, GT>), dim3(n_wg), dim3(threads), bytes,
+                     st, a);
   prof_end(st, kind);
   return hipGetLastError();
 }

@@ -27,7 +27,7 @@
 
 namespace ia {
 
-template <int C, int F, int D, int M>
+template <int C, int F, int D, int M, bool GT = false>
 struct StateLayout {
   static constexpr int M2 = 2 * M;
   // 16-bit element offsets within a stage; every matrix swizzled by row (see soff).
@@ -35,14 +35,21 @@ struct StateLayout {
   static constexpr int oV = C * F;         // [C][D]   bf16 v
   static constexpr int oT = oV + C * D;    // [2M][C]  bf16 T_c (j in K-slot order)
   static constexpr int stage = oT + M2 * C;
-  static constexpr int bytes = 2 * stage * 2;
+  // Gated layer: three buffers of per-token gate factors (walk iteration i in buffer i % 3).
+  static constexpr int bFac = 2 * stage * 2;
+  static constexpr int bytes = bFac + (GT ? 3 * C * 4 : 0);
 };
 
-template <int C, int F, int D, int M>
+// Gated layer (GT): token j of the chunk of walk iteration i enters the segment's end state
+// with the factor w_j prod_{s > j in the segment} a_s = E_i[j] P_i (GateRec's E of that chunk,
+// P_i the decay product of the chunks walked before it, which lie after it), folded into the
+// chunk's table T_i; lam eta is the sum of the tables' fp32 entries; the slot also receives
+// the segment's decay product.
+template <int C, int F, int D, int M, bool GT>
 __global__ void __launch_bounds__((64 * StateWaves<F, D, M>::NS))
 chunk_state_kernel(const ChunkArgs a) {
   using SL = SlotLayout<F, D, M>;
-  using Lay = StateLayout<C, F, D, M>;
+  using Lay = StateLayout<C, F, D, M, GT>;
   constexpr int NS = StateWaves<F, D, M>::NS;
   constexpr int NFT = SL::NFT, NDT = SL::NDT, TM = SL::TM;
   constexpr int KC = C / 32;
@@ -174,17 +181,62 @@ chunk_state_kernel(const ChunkArgs a) {
       tIm[q] = opaque(Lay::oT + soff<C>(M + m, kpos(j0)));
     }
   };
-  auto write_table = [&](auto S) {
+  // Gated: per-token factors of walk iteration i in buffer i % 3 (wave 0 writes iteration
+  // i + 2's during iteration i), and this thread's share of lam eta: the fp32 sum of its groups'
+  // table entries over the 16-lane row's C/4 groups of one mode, kept by the row's first lane.
+  float* const fac = reinterpret_cast<float*>(smem_raw + Lay::bFac);
+  float2 eta_g[NGR];
+#pragma unroll
+  for (int q = 0; q < NGR; ++q) eta_g[q] = make_float2(0.f, 0.f);
+  auto write_table = [&](auto S, int i) {
     constexpr int so = decltype(S)::value * ST;
 #pragma unroll
-    for (int q = 0; q < NGR; ++q)
-      if (tid + NL * q < GROUPS) {
-        float2 w[4];
+    for (int q = 0; q < NGR; ++q) {
+      float2 w[4];
+      const bool own = tid + NL * q < GROUPS;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = cmul(pw[q], tl[q][e]);
+      for (int e = 0; e < 4; ++e) w[e] = cmul(pw[q], tl[q][e]);
+      if constexpr (GT) {
+        const int j0 = 4 * ((tid + NL * q) % (C / 4));
+        const float4 f4 = *reinterpret_cast<const float4*>(fac + (i % 3) * C + j0);
+        const float f[4] = {f4.x, f4.y, f4.z, f4.w};
+        float2 sum = make_float2(0.f, 0.f);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w[e].x *= f[e];
+          w[e].y *= f[e];
+          sum.x += w[e].x;
+          sum.y += w[e].y;
+        }
+#pragma unroll
+        for (int o = 1; o < C / 4; o <<= 1) {
+          sum.x += __shfl_xor(sum.x, o, 16);
+          sum.y += __shfl_xor(sum.y, o, 16);
+        }
+        eta_g[q].x += sum.x;
+        eta_g[q].y += sum.y;
+      }
+      if (own) {
         *reinterpret_cast<uint2*>(s16 + tRe[q] + so) = pack4_bf16(w[0].x, w[1].x, w[2].x, w[3].x);
         *reinterpret_cast<uint2*>(s16 + tIm[q] + so) = pack4_bf16(w[0].y, w[1].y, w[2].y, w[3].y);
       }
+    }
+  };
+  // Gated: wave 0 turns the gates of walk iteration k into its factors (buffer k % 3), keeping
+  // P (the decay product of the iterations before) and the raw gates of the next iteration.
+  // (Gate loads go out before the same iteration's input loads, so waiting for them does not
+  // wait for those.)
+  float2 graw = make_float2(1.f, 0.f);
+  float gP = 1.f;
+  auto gate_load = [&](int k) {
+    return u == 0 ? gate_fetch(a, b, h, dir, chunk_of(k), C, lane) : make_float2(1.f, 0.f);
+  };
+  auto gate_factors = [&](float2 raw, int k) {
+    if (u == 0) {
+      const GateScan gs = gate_scan(raw, lane < C, lane);   // segments hold full chunks
+      if (lane < C) fac[(k % 3) * C + lane] = gs.e * gP;
+      gP *= gs.d;
+    }
   };
   auto advance_table = [&]() {
 #pragma unroll
@@ -235,9 +287,11 @@ chunk_state_kernel(const ChunkArgs a) {
           if (u + NS * di < TD) accG[di][kt] = mma_bf16(w, bv[di], accG[di][kt]);
       }
     }
-    if (u == 0 && lane < M) {
-      eta = cfma(epw, egeo, eta);
-      epw = cmul(epw, epc);
+    if constexpr (!GT) {
+      if (u == 0 && lane < M) {
+        eta = cfma(epw, egeo, eta);
+        epw = cmul(epw, epc);
+      }
     }
   };
 
@@ -251,19 +305,34 @@ chunk_state_kernel(const ChunkArgs a) {
     if (i + 1 < nc) {
       advance_table();
       write_inputs(Rc, Sw);
-      write_table(Sw);
+      write_table(Sw, i + 1);
+      if constexpr (GT) {
+        if (i + 2 < nc) gate_factors(graw, i + 2);
+        if (i + 3 < nc) graw = gate_load(i + 3);
+      }
       if (i + 3 < nc) fetch(Rf, i + 3);
     }
     __syncthreads();
   };
 
+  float2 g0 = graw, g1 = graw;
+  if constexpr (GT) {
+    g0 = gate_load(0);
+    if (nc > 1) g1 = gate_load(1);
+    if (nc > 2) graw = gate_load(2);
+  }
   fetch(I0{}, 0);
   if (nc > 1) fetch(I1{}, 1);
   if (nc > 2) fetch(I2{}, 2);
+  if constexpr (GT) {
+    gate_factors(g0, 0);
+    if (nc > 1) gate_factors(g1, 1);
+  }
   init_tables();
-  init_eta();
+  if constexpr (!GT) init_eta();
   write_inputs(I0{}, I0{});
-  write_table(I0{});
+  if constexpr (GT) __syncthreads();   // iteration 0's factors visible
+  write_table(I0{}, 0);
   __syncthreads();
   for (int i = 0; i < nc; i += 6) {
     step(I1{}, I0{}, I0{}, I1{}, i);
@@ -318,24 +387,36 @@ chunk_state_kernel(const ChunkArgs a) {
       *reinterpret_cast<uint4*>(sl + SL::pair(u, p, lane)) = make_uint4(r.x, r.y, m.x, m.y);
       if (il == 0) sl[SL::scale_of(u, p, lane)] = 1.f / sc;
     }
-  if (u == 0 && lane < M) reinterpret_cast<float2*>(sl + SL::eta)[lane] = eta;
+  if constexpr (GT) {
+#pragma unroll
+    for (int q = 0; q < NGR; ++q) {
+      const int gi = tid + NL * q;
+      if (gi < GROUPS && gi % (C / 4) == 0)
+        reinterpret_cast<float2*>(sl + SL::eta)[gi / (C / 4)] = eta_g[q];
+    }
+    if (tid == 0) sl[SL::dseg] = gP;
+  } else {
+    if (u == 0 && lane < M) reinterpret_cast<float2*>(sl + SL::eta)[lane] = eta;
+  }
 }
 
-template <int C, int F, int D, int M>
+template <int C, int F, int D, int M, bool GT = false>
 hipError_t launch_state_t(const ChunkArgs& a, int n_wg, hipStream_t st, int kind) {
   constexpr int threads = 64 * StateWaves<F, D, M>::NS;
-  constexpr int bytes = StateLayout<C, F, D, M>::bytes;
+  constexpr int bytes = StateLayout<C, F, D, M, GT>::bytes;
+  static_assert(bytes <= 160 * 1024, "LDS budget");
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&chunk_state_kernel<C, F, D, M>),
+        reinterpret_cast<const void*>(&chunk_state_kernel<C, F, D, M, GT>),
         hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   (void)hipGetLastError();
   prof_begin(st);
-  hipLaunchKernelGGL((chunk_state_kernel<C, F, D, M>), dim3(n_wg), dim3(threads), bytes, st, a);
+  hipLaunchKernelGGL((chunk_state_kernel<C, F, D, M, GT>), dim3(n_wg), dim3(threads), bytes, st,
+                     a);
   prof_end(st, kind);
   return hipGetLastError();
 }

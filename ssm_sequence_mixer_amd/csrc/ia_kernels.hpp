@@ -158,6 +158,7 @@ struct ChunkPrefillArgs {
   float2 *wU, *wG, *wE;         // workspace state
   const float2* readout;        // [H][M][M] readout matrix, or NULL (plain layer)
   unsigned char* rtab;          // its per-head MFMA operand (readout_table_bytes(M) each)
+  const float *wgate, *dgate;   // gated layer: [B][N][H] write / decay gates, or NULL
   int B, H, N, F, D, M;
   int chunk, segments, seg_chunks;
   int reverse, out_bf16;
@@ -232,8 +233,8 @@ int bwd_block_tokens(int F, int D, int M, int in_bf16, int out_bf16);
 size_t bwd_lds_bytes(int F, int D, int M, int in_bf16, int out_bf16, int tb, bool rev);
 hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t st);
 
-int chunk_wgs_per_cu(int chunk, int F, int D, int M,
-                     bool rm = false);   // 0 if unknown (no device)
+int chunk_wgs_per_cu(int chunk, int F, int D, int M, bool rm = false,
+                     bool gated = false);   // 0 if unknown (no device)
 int device_cus();                                        // compute units of the current device
 hipError_t launch_chunk_prefill(const ChunkPrefillArgs& a, hipStream_t st);
 

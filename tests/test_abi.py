@@ -463,7 +463,13 @@ def test_gated_variants_validation():
     assert ia.lib.ia_decode_step_gated(ctypes.byref(d), addr(0), addr(1), addr(2), addr(20),
                                        addr(21), addr(3), addr(4), state(), addr(21, 16),
                                        None) == 5
-    # workspace: one state, rounded up to 256 bytes
+    # workspace: fp32 inputs, the token-sequential path's (one state, rounded up to 256 bytes);
+    # bf16 inputs on a chunk shape, the chunked plan's (the plain prefill's, when no device
+    # reports the kernels' occupancy)
     B, H, M, F, D = 2, 3, 16, 32, 32
     want = (B * H * M * (F + D + 1) * 8 + 255) // 256 * 256
-    assert ia.lib.ia_prefill_gated_workspace_bytes(ctypes.byref(d)) == want
+    d32 = desc(Dv=32, in_dtype=ia.IA_F32)
+    assert ia.lib.ia_prefill_gated_workspace_bytes(ctypes.byref(d32)) == want
+    if not _has_device():
+        assert (ia.lib.ia_prefill_gated_workspace_bytes(ctypes.byref(d)) ==
+                ia.lib.ia_prefill_workspace_bytes(ctypes.byref(d)))
