@@ -411,12 +411,13 @@ def bench_block(torch, ia, W, inp, layers=24, reps=20):
 FP32_PEAK = 157.3e12        # fp32 vector FLOP/s, MI355X
 
 
-def bench_gated(torch, ia, inp, reps=5):
-    """Selective writing and memory decay (ia_prefill_fwd_gated, token-sequential fp32
-    kernels with sequence segments) on the prefill workload's bf16 q, k, v, with write gates
-    in [0.5, 1) and decay gates in [0.9, 1): per-step time, tokens/s and the fp32 vector
-    fraction of its algorithmic FLOPs, 12 M (F + Dv) per token and head (the state updates,
-    8 per complex entry, and the two readout contractions, 4 each)."""
+def bench_gated(torch, ia, inp, plain_ms=None, reps=20):
+    """Selective writing and memory decay (ia_prefill_fwd_gated: bf16 inputs on the chunked
+    MFMA prefill with the gates folded into each chunk) on the prefill workload's q, k, v, with
+    write gates in [0.5, 1) and decay gates in [0.9, 1), bf16 output: per-step time, tokens/s,
+    the ratio to the ungated step, and the fractions of the bf16 MFMA peak (the ungated layer's
+    algorithmic FLOPs: the gates add element-wise work only) and of HBM (the ungated bytes
+    plus the two fp32 gates per token and head)."""
     sh = inp["shape"]
     B, H, N, F, D, M = sh["B"], sh["H"], sh["N"], sh["F"], sh["D"], sh["M"]
     q, k, v = (torch.from_numpy(inp[n]).to(torch.bfloat16).cuda() for n in "qkv")
@@ -425,14 +426,14 @@ def bench_gated(torch, ia, inp, reps=5):
     g = torch.Generator(device="cpu").manual_seed(560)
     wg = (torch.rand((B, N, H), generator=g) * 0.5 + 0.5).cuda()
     dg = (torch.rand((B, N, H), generator=g) * 0.1 + 0.9).cuda()
-    desc = ia.make_desc(B, H, N, F, D, M, ia.IA_BF16, ia.IA_F32)
+    desc = ia.make_desc(B, H, N, F, D, M, ia.IA_BF16, ia.IA_BF16)
     ws = torch.empty(max(ia.ia_prefill_gated_workspace_bytes(desc), 16), dtype=torch.uint8,
                      device="cuda")
-    o = torch.empty((B, N, H, D), dtype=torch.float32, device="cuda")
+    o = torch.empty((B, N, H, D), dtype=torch.bfloat16, device="cuda")
 
     def step():
         ia.ia_prefill_fwd_gated(desc, q, k, v, wg, dg, lam, beta, None, o, ws)
-    for _ in range(2):
+    for _ in range(10):
         step()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -442,10 +443,14 @@ def bench_gated(torch, ia, inp, reps=5):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    flops = 12.0 * M * (F + D) * B * N * H
+    flops, byts = alg_counts(B, N, H, F, D, M)
+    byts += 8.0 * B * N * H
     return {"ms_per_step": ms, "tokens_per_s": B * N / (ms * 1e-3),
-            "fp32_frac": flops / (ms * 1e-3) / FP32_PEAK,
-            "scope": "ia_prefill_fwd_gated on the prefill workload (bf16 q, k, v; fp32 out)"}
+            "vs_ungated": None if plain_ms is None else ms / plain_ms,
+            "mfma_frac": flops / (ms * 1e-3) / BF16_PEAK,
+            "hbm_frac": byts / (ms * 1e-3) / HBM_PEAK,
+            "scope": "ia_prefill_fwd_gated on the prefill workload (bf16 q, k, v and output; "
+                     "chunked MFMA path), whole step"}
 
 
 def bwd_alg_flops(B, N, H, F, D, M):
@@ -597,7 +602,7 @@ def main():
     block = gated = None
     if not args.no_decode and args.workload == "1.3b":
         block = bench_block(torch, ia, W, pf["inp"])
-        gated = bench_gated(torch, ia, pf["inp"])
+        gated = bench_gated(torch, ia, pf["inp"], pf["ms"])
     cpu = None if args.no_cpu else cpu_baseline(pf["inp"], pf["cfg"]["bidirectional"])
     line = {
         "metric": "IA layer fwd tokens/s (prefill) + decode step latency; % of MFMA/HBM roofline",
