@@ -549,22 +549,14 @@ struct GateScan {
   float e;     // w_j prod_{s=j+1}^{C-1} a_s
   float d;     // prod_s a_s (every lane)
 };
-__device__ __forceinline__ GateScan gate_scan(float2 raw, bool valid, int lane) {
+__device__ __forceinline__ GateScan gate_scan(float2 raw, bool valid) {
   const float av = valid ? raw.x : 1.f, wv = valid ? raw.y : 0.f;
   const float mag = fabsf(av);
-  float l = mag < 0x1p-64f ? -64.f : __builtin_amdgcn_logf(mag);   // log2 (NaN stays NaN)
-  int neg = av < 0.f ? 1 : 0;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float lu = __shfl_up(l, o);
-    const int nu = __shfl_up(neg, o);
-    if (lane >= o) {
-      l += lu;
-      neg += nu;
-    }
-  }
-  const float l_last = __shfl(l, 63);
-  const float s_last = (__shfl(neg, 63) & 1) ? -1.f : 1.f;
+  // log2 (NaN stays NaN); the count of negative gates is scanned as a float (exact to 2^24)
+  const float l = wave_scan_incl(mag < 0x1p-64f ? -64.f : __builtin_amdgcn_logf(mag));
+  const int neg = (int)wave_scan_incl(av < 0.f ? 1.f : 0.f);
+  const float l_last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l), 63));
+  const float s_last = (__builtin_amdgcn_readlane(neg, 63) & 1) ? -1.f : 1.f;
   GateScan r;
   r.l = l;
   r.w = (neg & 1) ? -wv : wv;
@@ -577,7 +569,7 @@ __device__ __forceinline__ GateScan gate_scan(float2 raw, bool valid, int lane) 
 template <int C>
 __device__ __forceinline__ void gate_records(float2 raw, bool valid, int lane, float* rec) {
   using GR = GateRec<C>;
-  const GateScan g = gate_scan(raw, valid, lane);
+  const GateScan g = gate_scan(raw, valid);
   if (lane < C) {
     rec[GR::L + lane] = g.l;
     rec[GR::W + lane] = g.w;
@@ -722,10 +714,7 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
     // v of chunk c into LDS (its readers run after the mid-chunk barrier), the next chunk's
     // loads out.
     write_v();
-    if (c + 1 < x.c_end) {
-      fetch_v(c + 1);
-      if constexpr (GT && r == 0) graw = gate_fetch(a, x.b, x.h, a.dir, c + 1, C, lane);
-    }
+    if (c + 1 < x.c_end) fetch_v(c + 1);
     const float* const rec = rec_of(c);
     if constexpr (kEarlyO) {
       const int t = c * C + 16 * r + il;
@@ -748,7 +737,6 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
     // scale and the inter-chunk denominator.
     f16x8 Af[KM];
     float si = 1.f, den_inter = 0.f;
-    float li = 0.f, di = 1.f;   // gated: L_i and 2^(L_i) of this lane's query
     if (x.want_out) {
       // phi(q) of this wave's queries as B operands (K = f)
       bf16x8 fq[KF];
@@ -783,8 +771,8 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
       // Gated: the inter-chunk term times the decay since the chunk start, 2^(L_i), and each
       // S[i,j] times the gate factor W[j] 2^(L_i - L_j) (zero past the diagonal).
       if constexpr (GT) {
-        li = rec[GR::L + 16 * r + il];
-        di = __builtin_amdgcn_exp2f(li);
+        const float li = rec[GR::L + 16 * r + il];
+        const float di = __builtin_amdgcn_exp2f(li);
 #pragma unroll
         for (int kt = 0; kt < TM; ++kt)
 #pragma unroll
@@ -870,7 +858,8 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
         IA_STEP_FENCE();
       }
       den_inter = xor_sum16_32(den_inter);
-      if constexpr (GT) den_inter *= di;   // eta_c decays by 2^(L_i) as well
+      if constexpr (GT)   // eta_c decays by 2^(L_i) as well
+        den_inter *= __builtin_amdgcn_exp2f(rec[GR::L + 16 * r + il]);
       amax = xor_max16_32(amax);
       si = pow2_scale(amax);
 #pragma unroll
@@ -884,7 +873,13 @@ __device__ __forceinline__ void readout_main(const ChunkArgs& a, const Ctx<C, F,
     // Mid-chunk barrier: S, A' and its decay are done, so phi(q), phi(k) and lam U of chunk c
     // are no longer read and the state waves overwrite them with chunk c+1's.
     __syncthreads();
+    // (gated: chunk c+1's gates load during this second phase, whose registers are fewer)
+    if constexpr (GT && r == 0)
+      if (c + 1 < x.c_end) graw = gate_fetch(a, x.b, x.h, a.dir, c + 1, C, lane);
     if (x.want_out) {
+      // gated: L_i and 2^(L_i) again (the records stay until chunk c+1's second phase)
+      const float li = GT ? rec[GR::L + 16 * r + il] : 0.f;
+      const float di = GT ? __builtin_amdgcn_exp2f(li) : 1.f;
 
       // ---- P^T tiles (rows j, columns i), causal; their results are read after the
       // inter-chunk numerator MFMAs below
@@ -1327,16 +1322,9 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
   // lam U^T <- lam^L (lam U^T + phi(K)^T (beta lam^-j)).  Second, once v of chunk c is in
   // LDS: lam G <- lam G + W^T V (its decay waits for the next first phase), and chunk c+1's
   // copies and inputs.
-  // Gated: this chunk's records (GateRec; buffer c % 2, written by readout wave 0), and
-  // lam beta of mode `lane` for the eta update.
+  // Gated: this chunk's records (GateRec; buffer c % 2, written by readout wave 0).
   const float* const recb =
       reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(x.s16) + Lay::bRec);
-  float2 lam_m = make_float2(0.f, 0.f), lb_m = lam_m;
-  if constexpr (GT && u == 0) {
-    const int m = lane < M ? lane : 0;
-    lam_m = lamh[m];
-    lb_m = cmul(lam_m, a.beta[(size_t)x.h * M + m]);
-  }
   for (int c = x.c_begin; c < x.c_end; ++c) {
     const float* const rec = recb + (c & 1) * GR::floats;
     const float dl = GT ? rec[GR::D] : 1.f;   // gated: the chunk's decay product
@@ -1390,21 +1378,8 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
           }
         }
       }
-    if (u == 0 && lane < M) {
-      if constexpr (GT) {
-        // lam eta <- lam^L D lam eta + lam beta sum_{j<L} lam^(L-1-j) E[j] (Horner in fp32)
-        const int Lc = min(C, a.N - c * C);
-        float2 hs = make_float2(0.f, 0.f);
-        for (int j4 = 0; j4 < C; j4 += 4) {
-          const float4 e4 = *reinterpret_cast<const float4*>(rec + GR::E + j4);
-          const float ev[4] = {e4.x, e4.y, e4.z, e4.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (j4 + q < Lc) hs = cfma(lam_m, hs, make_float2(ev[q], 0.f));
-        }
-        const float2 pl = f2(oLn + tsel + (Lay::bPowL - Lay::bLE));
-        eta = cfma(lb_m, hs, cmul(pl, make_float2(dl * eta.x, dl * eta.y)));
-      } else {
+    if constexpr (!GT) {
+      if (u == 0 && lane < M) {
         const float2 ge = f2(oLn + tsel + (Lay::bGeo - Lay::bLE));
         eta = cmul(f2(oLn + tsel + (Lay::bPowL - Lay::bLE)),
                    make_float2(eta.x + ge.x, eta.y + ge.y));
@@ -1439,6 +1414,34 @@ __device__ __forceinline__ void state_main(const ChunkArgs& a, const Ctx<C, F, D
         for (int di = 0; di < NDT; ++di)
           if (u + NS * di < TD) accG[di][kt] = mma_bf16(w, bv[di], accG[di][kt]);
         IA_STEP_FENCE();
+      }
+    }
+    // Gated: lam eta <- lam^L D lam eta + lam beta sum_{j<L} lam^(L-1-j) E[j] (Horner in
+    // fp32), in the second phase, whose registers are fewer.
+    if constexpr (GT) {
+      if (u == 0 && lane < M) {
+        // Four tokens per Horner step, hs <- lam^4 hs + (lam^3 E[j] + lam^2 E[j+1] +
+        // lam E[j+2] + E[j+3]), the four products independent; the padding tokens past the
+        // sequence end (E = 0) would still multiply by lam, so a last, partial chunk takes the
+        // one-token steps.
+        const int Lc = min(C, a.N - c * C);
+        const float2 l1 = lamh[lane];   // (loaded here: not held across the chunk loop)
+        const float2 lb_m = cmul(l1, a.beta[(size_t)x.h * M + lane]);
+        float2 hs = make_float2(0.f, 0.f);
+        if (Lc == C) {
+          const float2 l2 = cmul(l1, l1), l3 = cmul(l2, l1), l4 = cmul(l2, l2);
+#pragma unroll 4
+          for (int j4 = 0; j4 < C; j4 += 4) {
+            const float4 e4 = *reinterpret_cast<const float4*>(rec + GR::E + j4);
+            const float2 t = make_float2(l3.x * e4.x + l2.x * e4.y + l1.x * e4.z + e4.w,
+                                         l3.y * e4.x + l2.y * e4.y + l1.y * e4.z);
+            hs = cfma(l4, hs, t);
+          }
+        } else {
+          for (int j = 0; j < Lc; ++j) hs = cfma(l1, hs, make_float2(rec[GR::E + j], 0.f));
+        }
+        const float2 pl = f2(oLn + tsel + (Lay::bPowL - Lay::bLE));
+        eta = cfma(lb_m, hs, cmul(pl, make_float2(dl * eta.x, dl * eta.y)));
       }
     }
     if (more) {

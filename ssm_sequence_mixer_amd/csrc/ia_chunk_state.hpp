@@ -208,11 +208,14 @@ chunk_state_kernel(const ChunkArgs a) {
           sum.x += w[e].x;
           sum.y += w[e].y;
         }
-#pragma unroll
-        for (int o = 1; o < C / 4; o <<= 1) {
-          sum.x += __shfl_xor(sum.x, o, 16);
-          sum.y += __shfl_xor(sum.y, o, 16);
+        // over the C/4 lanes of the mode (DPP: quad swaps, then half-row and row mirrors)
+        sum.x = dpp_add<0x141>(dpp_add<0x4E>(dpp_add<0xB1>(sum.x)));
+        sum.y = dpp_add<0x141>(dpp_add<0x4E>(dpp_add<0xB1>(sum.y)));
+        if constexpr (C / 4 == 16) {
+          sum.x = dpp_add<0x140>(sum.x);
+          sum.y = dpp_add<0x140>(sum.y);
         }
+        static_assert(C / 4 == 8 || C / 4 == 16, "8 or 16 groups per mode");
         eta_g[q].x += sum.x;
         eta_g[q].y += sum.y;
       }
@@ -233,7 +236,7 @@ chunk_state_kernel(const ChunkArgs a) {
   };
   auto gate_factors = [&](float2 raw, int k) {
     if (u == 0) {
-      const GateScan gs = gate_scan(raw, lane < C, lane);   // segments hold full chunks
+      const GateScan gs = gate_scan(raw, lane < C);   // segments hold full chunks
       if (lane < C) fac[(k % 3) * C + lane] = gs.e * gP;
       gP *= gs.d;
     }

@@ -107,6 +107,20 @@ __device__ __forceinline__ float dpp_add(float v) {
   return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF,
                                                         false));
 }
+// Inclusive prefix sum over the wave's 64 lanes through DPP moves: row_shr 1, 2, 4, 8 (a lane
+// whose source lies before its 16-lane row adds zero) give prefix sums within each row;
+// row_bcast:15 then adds row 0's total to row 1 and row 2's to row 3, and row_bcast:31 the
+// total of rows 0-1 to rows 2 and 3.
+__device__ __forceinline__ float wave_scan_incl(float v) {
+  v = dpp_add<0x111>(v);        // row_shr:1
+  v = dpp_add<0x112>(v);        // row_shr:2
+  v = dpp_add<0x114>(v);        // row_shr:4
+  v = dpp_add<0x118>(v);        // row_shr:8
+  v = dpp_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 // Sums over aligned groups of W lanes (W = 16, 32 or 64) of N values at once; the group's last
 // lane ends with each total (W = 16: every lane of the 16-lane row).
 template <int W, int N>
