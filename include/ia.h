@@ -35,9 +35,10 @@
  *
  * Conventions for every call:
  *   - All pointers except `desc`, `st` (the struct) are DEVICE pointers, 16-byte aligned.
- *   - The caller owns every buffer.  The library allocates nothing.  Its only state is per
- *     thread: the text behind the last IA_ERR_LAUNCH (ia_last_launch_error), and, for the
- *     duration of an ia_prefill_fwd_profiled call, a pointer to that call's event list.
+ *   - The caller owns every buffer.  The library allocates nothing at run time.  Its state:
+ *     per thread, the text behind the last IA_ERR_LAUNCH (ia_last_launch_error) and, for the
+ *     duration of an ia_prefill_fwd_profiled call, a pointer to that call's event list; per
+ *     device, the fixed workspace array of ia_prefill_fwd_noalloc (part of the loaded code).
  *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the null stream);
  *     the call returns without synchronising.  Results are visible after the stream syncs.
  *   - Validation happens on the host before anything is enqueued.  On any error nothing is
@@ -453,8 +454,7 @@ ia_status ia_decode_step_gated(const ia_desc* desc,
 const char* ia_status_string(ia_status s);
 
 /* Static string: the HIP runtime's text for the error behind the calling thread's most recent
- * IA_ERR_LAUNCH ("no launch error" if there was none).  The one piece of per-thread state
- * the library keeps. */
+ * IA_ERR_LAUNCH ("no launch error" if there was none), kept per thread. */
 const char* ia_last_launch_error(void);
 
 #ifdef __cplusplus
