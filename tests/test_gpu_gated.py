@@ -337,3 +337,49 @@ def test_gated_1p3b_workload_fp32_path():
                                        inp["beta"][h], n, gates=(wg[b, :, h], dg[b, :, h]))
         report(f"gated 1.3b row (b={b}, n={n}, h={h}): kappa {kappa:.3g}", err[b, n, h])
         assert err[b, n, h] < 4 * 2.0 ** -24 * kappa, (b, n, h, err[b, n, h], kappa)
+
+
+@pytest.mark.parametrize("mode", ["state", "bidirectional"])
+def test_gated_fp32_route_head(mode):
+    """A head the chunk factorisation does not resolve (S4D-Lin modes at dt = 0.3, so
+    |lam|^63 < 2^-8) runs the fp32 recurrence with its gates inside the gated chunked launches,
+    next to a head on the chunked path: with a caller state (outputs and final state), and
+    bidirectional (both walks with the gates of the positions they walk)."""
+    import torch
+    ia = _ia()
+    B, H, N, F, M = 2, 2, 700, 64, 32
+    inp = W.make_inputs(B, H, N, F, F, M, dtype="bf16", seed=1080)
+    lam = inp["lam"].copy()
+    lam[1] = W.s4d_lin(np.array([0.3]), M)[0]
+    inp["lam"] = lam
+    assert ia.ia_check_lambda(ia.make_desc(B, H, N, F, F, M), lam) == 1
+    wg, dg = _mild_gates(np.random.default_rng(1081), (B, N, H))
+    args = [dev(inp[n], torch.bfloat16) for n in "qkv"] + [dev(lam), dev(inp["beta"])]
+    tag(f"gated fp32 route head ({mode})")
+    if mode == "bidirectional":
+        o = host(ia.prefill(*args, bidir=True, out_dtype=torch.float32,
+                            gates=(dev(wg), dev(dg))))
+        f = oracle.prefill_gated(inp["q"], inp["k"], inp["v"], lam, inp["beta"], wg, dg,
+                                 threads=8)[0]
+        r = oracle.prefill_gated(_flip(inp["q"]), _flip(inp["k"]), _flip(inp["v"]), lam,
+                                 inp["beta"], _flip(wg), _flip(dg), threads=8)[0]
+        ref = f + r[:, ::-1]
+        e0, e1 = rowrel(o[:, :, 0], ref[:, :, 0]), rowrel(o[:, :, 1], ref[:, :, 1])
+        report("gated fp32 route (bidirectional) chunked head / routed head", max(e0, e1))
+        assert e0 < TOL_BF16 and e1 < TOL_F32
+        return
+    pre = W.make_inputs(B, H, 10, F, F, M, dtype="bf16", seed=1082)
+    st_ref0 = oracle.prefill(pre["q"], pre["k"], pre["v"], lam, inp["beta"])[3]
+    st = tuple(dev(x) for x in st_ref0)
+    st_ref0 = tuple(host(x) for x in st)
+    o = host(ia.prefill(*args, state=st, out_dtype=torch.float32, gates=(dev(wg), dev(dg))))
+    torch.cuda.synchronize()
+    o_ref, _, _, st_ref = oracle.prefill_gated(inp["q"], inp["k"], inp["v"], lam, inp["beta"],
+                                               wg, dg, state=st_ref0, threads=8)
+    e0, e1 = rowrel(o[:, :, 0], o_ref[:, :, 0]), rowrel(o[:, :, 1], o_ref[:, :, 1])
+    got = tuple(host(x) for x in st)
+    s0 = state_rel(tuple(x[:, :1] for x in got), tuple(x[:, :1] for x in st_ref))
+    s1 = state_rel(tuple(x[:, 1:] for x in got), tuple(x[:, 1:] for x in st_ref))
+    report("gated fp32 route (state) chunked head / routed head: outputs, states",
+           max(e0, e1, s0, s1))
+    assert e0 < TOL_BF16 and s0 < TOL_BF16 and e1 < TOL_F32 and s1 < TOL_F32
