@@ -383,3 +383,43 @@ def test_gated_fp32_route_head(mode):
     report("gated fp32 route (state) chunked head / routed head: outputs, states",
            max(e0, e1, s0, s1))
     assert e0 < TOL_BF16 and s0 < TOL_BF16 and e1 < TOL_F32 and s1 < TOL_F32
+
+
+def _features_bf16(x):
+    """elu(x) + 1 rounded to bf16, and its preimage under elu + 1 (the oracle's input)."""
+    f = np.asarray(W.round_bf16(np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))),
+                   np.float64)
+    return f, np.where(f > 1.0, f - 1.0, np.log(np.minimum(f, 1.0)))
+
+
+@pytest.mark.parametrize("opts", ["no_den", "identity", "identity no_den"])
+def test_gated_chunked_readout_options(opts):
+    """The readout options on the gated chunked path, with a caller state: no denominator
+    (o = num of the oracle's gated recurrence) and identity features (the kernel given
+    phi(q), phi(k), the oracle their preimages under elu + 1)."""
+    import torch
+    ia = _ia()
+    B, H, N, F, M = 2, 2, 300, 64, 32
+    inp = W.make_inputs(B, H, N, F, F, M, dtype="bf16", seed=1090)
+    wg, dg = _mild_gates(np.random.default_rng(1091), (B, N, H))
+    identity, no_den = "identity" in opts, "no_den" in opts
+    qk, kk, qo, ko = inp["q"], inp["k"], inp["q"], inp["k"]
+    if identity:
+        qk, qo = _features_bf16(inp["q"])
+        kk, ko = _features_bf16(inp["k"])
+    pre = W.make_inputs(B, H, 9, F, F, M, dtype="f32", seed=1092, std=0.5)
+    st_ref0 = oracle.prefill(pre["q"], pre["k"], pre["v"], inp["lam"], inp["beta"])[3]
+    st = tuple(dev(x) for x in st_ref0)
+    st_ref0 = tuple(host(x) for x in st)
+    tag(f"gated chunked prefill, {opts}")
+    o = ia.prefill(dev(qk, torch.bfloat16), dev(kk, torch.bfloat16),
+                   dev(inp["v"], torch.bfloat16), dev(inp["lam"]), dev(inp["beta"]), state=st,
+                   out_dtype=torch.float32, gates=(dev(wg), dev(dg)), no_den=no_den,
+                   identity_features=identity)
+    torch.cuda.synchronize()
+    o_ref, num, _, st_ref = oracle.prefill_gated(qo, ko, inp["v"], inp["lam"], inp["beta"],
+                                                 wg, dg, state=st_ref0, threads=8)
+    e_o = rowrel(host(o), num if no_den else o_ref)
+    e_s = state_rel(tuple(host(x) for x in st), st_ref)
+    report(f"gated chunked prefill, {opts}: output / state", max(e_o, e_s))
+    assert e_o < TOL_BF16 and e_s < TOL_BF16
