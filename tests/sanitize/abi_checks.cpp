@@ -106,6 +106,11 @@ int main() {
     expect("gated null", ia_prefill_fwd_gated(&d, addr(0), addr(1), addr(2), nullptr, addr(21),
                                               addr(3), addr(4), &st, addr(5), addr(6), big,
                                               nullptr), IA_ERR_NULL);
+    const size_t gneed = ia_prefill_gated_workspace_bytes(&d);   // the chunked plan's
+    expect("gated small workspace",
+           ia_prefill_fwd_gated(&d, addr(0), addr(1), addr(2), addr(20), addr(21), addr(3),
+                                addr(4), &st, addr(5), addr(6), gneed - 1, nullptr),
+           IA_ERR_WORKSPACE);
     expect("gated decode alias", ia_decode_step_gated(&d, addr(0), addr(1), addr(2), addr(20),
                                                       addr(21), addr(3), addr(4), &st,
                                                       addr(21, 16), nullptr), IA_ERR_ALIAS);
