@@ -433,9 +433,11 @@ def bench_gated(torch, ia, inp, plain_ms=None, reps=20):
 
     def step():
         ia.ia_prefill_fwd_gated(desc, q, k, v, wg, dg, lam, beta, None, o, ws)
-    for _ in range(10):
-        step()
-    torch.cuda.synchronize()
+    t_start = time.perf_counter()   # half a second of warm-up, as for the prefill step
+    while time.perf_counter() - t_start < 0.5:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(reps):
