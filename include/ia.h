@@ -85,6 +85,15 @@ typedef enum { IA_F32 = 0, IA_BF16 = 1 } ia_dtype;
  * form phi(q), phi(k) themselves.  Prefill and decode. */
 #define IA_FLAG_IDENTITY_FEATURES 4u
 
+/* ia_prefill_bwd only (ignored elsewhere): which of its two implementations runs.  Without
+ * either flag the chunked kernels run where they exist (F == Dv in {32, 64, 128}) unless the
+ * (b,h) slices and mode groups are so few that the token-sequential sweeps would cut each
+ * sequence into more than two segments; IA_FLAG_SEQUENTIAL_BWD forces the token-sequential
+ * kernels, IA_FLAG_CHUNKED_BWD the chunked ones (IA_ERR_UNSUPPORTED on other shapes, and with
+ * both flags).  Both give the same gradients up to fp32 rounding. */
+#define IA_FLAG_SEQUENTIAL_BWD 8u
+#define IA_FLAG_CHUNKED_BWD 16u
+
 typedef struct ia_desc {
   int B;             /* batch rows */
   int H;             /* heads */
@@ -98,8 +107,9 @@ typedef struct ia_desc {
   int out_dtype;     /* ia_dtype of o */
   float den_clamp;   /* lower clamp of Re(den); finite and > 0 (the method uses 1e-6), else
                         IA_ERR_DOMAIN */
-  unsigned flags;    /* IA_FLAG_BIDIR | IA_FLAG_NO_DEN | IA_FLAG_IDENTITY_FEATURES, or 0; other
-                        bits: IA_ERR_UNSUPPORTED */
+  unsigned flags;    /* IA_FLAG_BIDIR | IA_FLAG_NO_DEN | IA_FLAG_IDENTITY_FEATURES |
+                        IA_FLAG_SEQUENTIAL_BWD | IA_FLAG_CHUNKED_BWD, or 0; other bits:
+                        IA_ERR_UNSUPPORTED */
   int chunk;         /* chunk length of the chunked prefill: 0 (= 64 [summary §A.2]), 32 or
                         64; other values: IA_ERR_UNSUPPORTED */
 } ia_desc;

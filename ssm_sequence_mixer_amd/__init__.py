@@ -34,6 +34,8 @@ IA_F32, IA_BF16 = 0, 1
 IA_FLAG_BIDIR = 1
 IA_FLAG_NO_DEN = 2
 IA_FLAG_IDENTITY_FEATURES = 4
+IA_FLAG_SEQUENTIAL_BWD = 8
+IA_FLAG_CHUNKED_BWD = 16
 STATUS = ["IA_OK", "IA_ERR_NULL", "IA_ERR_SHAPE", "IA_ERR_DTYPE", "IA_ERR_ALIGN",
           "IA_ERR_ALIAS", "IA_ERR_DOMAIN", "IA_ERR_UNSUPPORTED", "IA_ERR_LAUNCH",
           "IA_ERR_WORKSPACE"]
@@ -143,9 +145,15 @@ KIND_NAMES = {0: "fill", 1: "scan", 2: "tables", 3: "summary", 4: "carry", 5: "c
 
 
 def make_desc(B, H, N, F, Dv, M, in_dtype=IA_BF16, out_dtype=IA_F32, den_clamp=1e-6,
-              bidir=False, chunk=0, no_den=False, identity_features=False) -> IADesc:
+              bidir=False, chunk=0, no_den=False, identity_features=False,
+              bwd_path="auto") -> IADesc:
+    """bwd_path: "auto", "chunked" or "sequential", the backward kernels ia_prefill_bwd runs."""
+    if bwd_path not in ("auto", "chunked", "sequential"):
+        raise ValueError(f"bwd_path {bwd_path!r}")
     flags = ((IA_FLAG_BIDIR if bidir else 0) | (IA_FLAG_NO_DEN if no_den else 0)
-             | (IA_FLAG_IDENTITY_FEATURES if identity_features else 0))
+             | (IA_FLAG_IDENTITY_FEATURES if identity_features else 0)
+             | (IA_FLAG_SEQUENTIAL_BWD if bwd_path == "sequential" else 0)
+             | (IA_FLAG_CHUNKED_BWD if bwd_path == "chunked" else 0))
     return IADesc(B, H, N, F, Dv, M, in_dtype, out_dtype, den_clamp, flags, chunk)
 
 
@@ -498,15 +506,17 @@ def block_gate(o, gate, out=None, stream=None):
 
 def prefill_bwd(q, k, v, lam, beta, dO, state0=None, den_clamp=1e-6, no_den=False,
                 identity_features=False, want_state_grad=False, stream=None, workspace=None,
-                bidir=False):
+                bidir=False, path="auto"):
     """Gradients of the layer (causal, or bidirectional with bidir=True) for dL/do = dO:
-    allocates the outputs (and the workspace) with torch and runs ia_prefill_bwd.  Returns
-    (dq, dk, dv, dlam, dbeta, dstate0 or None)."""
+    allocates the outputs (and the workspace) with torch and runs ia_prefill_bwd (path:
+    "auto", "chunked" or "sequential", its kernels).  Returns (dq, dk, dv, dlam, dbeta,
+    dstate0 or None)."""
     import torch
     B, N, H, F = q.shape
     Dv, M = v.shape[3], lam.shape[1]
     desc = make_desc(B, H, N, F, Dv, M, dtype_code(q.dtype), dtype_code(dO.dtype), den_clamp,
-                     bidir=bidir, no_den=no_den, identity_features=identity_features)
+                     bidir=bidir, no_den=no_den, identity_features=identity_features,
+                     bwd_path=path)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dlam = torch.empty((H, M), dtype=torch.complex64, device=q.device)
     dbeta = torch.empty_like(dlam)

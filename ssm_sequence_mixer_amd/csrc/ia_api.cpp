@@ -39,7 +39,8 @@ ia_status check_desc(const ia_desc* d, bool need_n) {
       (d->out_dtype != IA_F32 && d->out_dtype != IA_BF16))
     return IA_ERR_DTYPE;
   if (!(std::isfinite(d->den_clamp) && d->den_clamp > 0.f)) return IA_ERR_DOMAIN;
-  if (d->flags & ~(IA_FLAG_BIDIR | IA_FLAG_NO_DEN | IA_FLAG_IDENTITY_FEATURES))
+  if (d->flags & ~(IA_FLAG_BIDIR | IA_FLAG_NO_DEN | IA_FLAG_IDENTITY_FEATURES |
+                   IA_FLAG_SEQUENTIAL_BWD | IA_FLAG_CHUNKED_BWD))
     return IA_ERR_UNSUPPORTED;
   if (d->chunk != 0 && d->chunk != 32 && d->chunk != 64) return IA_ERR_UNSUPPORTED;
   // Index arithmetic in the kernels is 64-bit for element offsets; keep grid sizes sane.
@@ -507,9 +508,33 @@ ia_status ia_prefill_fwd_gated(const ia_desc* d, const void* q, const void* k, c
                       stream, static_cast<const float*>(wgate), static_cast<const float*>(dgate));
 }
 
+// Which backward serves a call: the flag's, else the chunked one where it exists, unless the
+// slices and mode groups are too few to fill the device: the token-sequential sweeps then cut
+// each sequence into segments that run side by side, which the chunked walk does not.
+static bool bwd_chunked(const ia_desc* d) {
+  if (d->flags & IA_FLAG_SEQUENTIAL_BWD) return false;
+  if (d->flags & IA_FLAG_CHUNKED_BWD) return true;
+  int seg_len;
+  return ia::bwd_chunked_supported(d->F, d->Dv, d->M) &&
+         ia::bwd_segments(d->B, d->H, d->N, d->M, &seg_len) <= 2;
+}
+
+static ia_status check_bwd_path(const ia_desc* d) {
+  const unsigned both = IA_FLAG_SEQUENTIAL_BWD | IA_FLAG_CHUNKED_BWD;
+  if ((d->flags & both) == both) return IA_ERR_UNSUPPORTED;
+  if ((d->flags & IA_FLAG_CHUNKED_BWD) && !ia::bwd_chunked_supported(d->F, d->Dv, d->M))
+    return IA_ERR_UNSUPPORTED;
+  return IA_OK;
+}
+
+static ia::BwdLayout bwd_plan(const ia_desc* d) {
+  return bwd_chunked(d) ? ia::bwd_chunked_layout(d->B, d->H, d->N, d->F, d->Dv, d->M)
+                        : ia::bwd_layout(d->B, d->H, d->N, d->F, d->Dv, d->M);
+}
+
 size_t ia_prefill_bwd_workspace_bytes(const ia_desc* d) {
-  if (check_desc(d, true) != IA_OK) return 0;
-  return ia::bwd_layout(d->B, d->H, d->N, d->F, d->Dv, d->M).bytes;
+  if (check_desc(d, true) != IA_OK || check_bwd_path(d) != IA_OK) return 0;
+  return bwd_plan(d).bytes;
 }
 
 ia_status ia_prefill_bwd(const ia_desc* d, const void* q, const void* k, const void* v,
@@ -519,6 +544,7 @@ ia_status ia_prefill_bwd(const ia_desc* d, const void* q, const void* k, const v
                          void* stream) {
   ia_status s = check_desc(d, true);
   if (s != IA_OK) return s;
+  if ((s = check_bwd_path(d)) != IA_OK) return s;
   const bool bidir = d->flags & IA_FLAG_BIDIR;
   if (!q || !k || !v || !lambda || !beta || !dO || !dq || !dk || !dv || !dlambda || !dbeta)
     return IA_ERR_NULL;
@@ -529,7 +555,8 @@ ia_status ia_prefill_bwd(const ia_desc* d, const void* q, const void* k, const v
     if (!aligned16(p)) return IA_ERR_ALIGN;
   if (st0 && (s = check_state(d, st0)) != IA_OK) return s;
   if (dst0 && (s = check_state(d, dst0)) != IA_OK) return s;
-  const ia::BwdLayout L = ia::bwd_layout(d->B, d->H, d->N, d->F, d->Dv, d->M);
+  const bool chunked = bwd_chunked(d);
+  const ia::BwdLayout L = bwd_plan(d);
   if (!workspace || ws_bytes < L.bytes) return IA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return IA_ERR_ALIGN;
 
@@ -591,7 +618,12 @@ ia_status ia_prefill_bwd(const ia_desc* d, const void* q, const void* k, const v
   a.apart = reinterpret_cast<float2*>(ws + L.apart_off);
   a.cstate = reinterpret_cast<float2*>(ws + L.cstate_off);
   a.cadj = reinterpret_cast<float2*>(ws + L.cadj_off);
-  a.nseg = ia::bwd_segments(d->B, d->H, d->N, d->M, &a.seg_len);
+  if (chunked) {
+    a.nseg = 1;
+    a.seg_len = d->N;
+  } else {
+    a.nseg = ia::bwd_segments(d->B, d->H, d->N, d->M, &a.seg_len);
+  }
   a.B = d->B; a.H = d->H; a.N = d->N; a.F = d->F; a.D = d->Dv; a.M = d->M;
   a.in_bf16 = d->in_dtype == IA_BF16;
   a.out_bf16 = d->out_dtype == IA_BF16;
@@ -599,13 +631,14 @@ ia_status ia_prefill_bwd(const ia_desc* d, const void* q, const void* k, const v
   a.clamp = d->den_clamp;
   a.tb = ia::bwd_block_tokens(d->F, d->Dv, d->M, a.in_bf16, a.out_bf16);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  hipError_t e = ia::launch_prefill_bwd(a, hs);
+  auto launch = chunked ? ia::launch_prefill_bwd_chunked : ia::launch_prefill_bwd;
+  hipError_t e = launch(a, hs);
   if (e == hipSuccess && bidir) {
     // o = IA(x) + flip(IA(flip x)): the reversed walk's gradients are added on (the workspace
     // is reused in stream order)
     a.dir = 1;
     a.accumulate = 1;
-    e = ia::launch_prefill_bwd(a, hs);
+    e = launch(a, hs);
   }
   return launch_status(e);
 }

@@ -836,6 +836,10 @@ hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t st) {
   {}
 #undef IA_BWD
   if (e != hipSuccess) return e;
+  return launch_bwd_reduce(a, st);
+}
+
+hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t st) {
   const size_t n = (size_t)a.B * a.H * a.N * (2 * a.F + a.D);
   size_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;

@@ -232,6 +232,14 @@ BwdLayout bwd_layout(int B, int H, int N, int F, int D, int M);
 int bwd_block_tokens(int F, int D, int M, int in_bf16, int out_bf16);
 size_t bwd_lds_bytes(int F, int D, int M, int in_bf16, int out_bf16, int tb, bool rev);
 hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t st);
+// The sum of the mode groups' partial rows (gpart) and of the lambda/beta partials (lpart).
+hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t st);
+// Chunked backward on fp32 MFMA (ia_backward_chunk.hip): F == Dv in {32, 64, 128}, M a
+// multiple of 16, no sequence segments.  Its workspace: chunk start states (ckpt), per-token
+// den and g.num partials (dpart), gpart and lpart as the token-sequential path.
+bool bwd_chunked_supported(int F, int D, int M);
+BwdLayout bwd_chunked_layout(int B, int H, int N, int F, int D, int M);
+hipError_t launch_prefill_bwd_chunked(const BwdArgs& a, hipStream_t st);
 
 int chunk_wgs_per_cu(int chunk, int F, int D, int M, bool rm = false,
                      bool gated = false);   // 0 if unknown (no device)

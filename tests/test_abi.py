@@ -83,16 +83,16 @@ def test_desc_validation(field, value, status):
 
 
 def test_unknown_flag_bits():
-    for bits in (8, 16, 1 << 31, 1 | 8):
+    for bits in (32, 64, 1 << 31, 1 | 32):
         d = desc()
         d.flags = bits
         assert prefill(d) == 7, bits
 
 
 def test_known_flag_combinations_accepted_by_validation():
-    # Bits 1, 2 and 4 are defined: every combination passes the flag check (the call then
-    # fails on the bad shape, not on the flags).
-    for bits in range(8):
+    # Bits 1 to 16 are defined: every combination passes the flag check (the call then fails
+    # on the bad shape, not on the flags).
+    for bits in range(32):
         d = desc()
         d.flags = bits
         d.N = 0
@@ -283,11 +283,27 @@ def bwd(d, ws_bytes=1 << 40, st0=None, dst0=None, **ptrs):
                                  p["dv"], p["dlam"], p["dbeta"], dst0, p["ws"], ws_bytes, None)
 
 
+def _bwd_chunked_bytes(B, H, N, F, D, M):
+    """Workspace of the chunked backward (F == Dv in {32, 64, 128}): every 16-token chunk's
+    start state per group of 16 modes (Re and Im rows of U, Gamma, eta, fp32), the per-token
+    den and g.num partials per group, the groups' gradient rows, the lambda/beta partials."""
+    up = lambda x: (x + 255) // 256 * 256
+    S, G, nch = B * H, M // 16, (N + 15) // 16
+    return (up(S * G * nch * 32 * (F + D + 1) * 4) + up(S * N * G * 8)
+            + up(G * S * N * (2 * F + D) * 4) + up(S * M * 16))
+
+
 def test_bwd_workspace_bytes_layout():
     up = lambda x: (x + 255) // 256 * 256
     for B, H, N, F, D, M in ((2, 3, 70, 32, 16, 16), (4, 16, 2048, 128, 128, 64),
                              (1, 1, 1, 16, 256, 128), (2, 8, 131072, 32, 32, 32),
                              (1, 2, 1000, 32, 32, 16)):
+        chunked = F == D and F in (32, 64, 128)
+        if chunked:
+            d = desc(B=B, H=H, N=N, F=F, Dv=D, M=M)
+            d.flags = ia.IA_FLAG_CHUNKED_BWD
+            assert (ia.lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(d))
+                    == _bwd_chunked_bytes(B, H, N, F, D, M))
         S, nck = B * H, (N + 31) // 32
         # sequence segments of the backward sweeps (no device: 256 compute units)
         wgs = S * (M // 16)
@@ -300,9 +316,28 @@ def test_bwd_workspace_bytes_layout():
                 + up((M // 16) * S * N * (2 * F + D) * 4) + up(S * nseg * M * 16)
                 + up(S * N * M * 8) + 2 * carry)
         d = desc(B=B, H=H, N=N, F=F, Dv=D, M=M)
+        d.flags = ia.IA_FLAG_SEQUENTIAL_BWD   # the token-sequential kernels' layout
         assert ia.lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(d)) == want
+        if not chunked:
+            d.flags = 0
+            assert ia.lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(d)) == want
     assert ia.lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(desc(N=0))) == 0
     assert ia.lib.ia_prefill_bwd_workspace_bytes(None) == 0
+    # automatic choice: few slices and a long sequence take the token-sequential sweeps (cut
+    # into segments); the chunked flag forces the chunked kernels' layout
+    d = desc(B=1, H=2, N=1000, F=32, Dv=32, M=16)
+    assert ia.lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(d)) != _bwd_chunked_bytes(
+        1, 2, 1000, 32, 32, 16)
+    d.flags = ia.IA_FLAG_CHUNKED_BWD
+    assert ia.lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(d)) == _bwd_chunked_bytes(
+        1, 2, 1000, 32, 32, 16)
+    # the chunked kernels exist for F == Dv in {32, 64, 128} only; both flags: unsupported
+    d = desc(B=1, H=1, N=10, F=64, Dv=32, M=16)
+    d.flags = ia.IA_FLAG_CHUNKED_BWD
+    assert ia.lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(d)) == 0
+    d = desc(B=1, H=1, N=10, F=32, Dv=32, M=16)
+    d.flags = ia.IA_FLAG_CHUNKED_BWD | ia.IA_FLAG_SEQUENTIAL_BWD
+    assert ia.lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(d)) == 0
 
 
 def test_bwd_validation():
@@ -310,6 +345,9 @@ def test_bwd_validation():
     assert bwd(None) == 1
     assert bwd(desc(N=0)) == 2
     assert bwd(desc(M=20)) == 7
+    dc = desc(Dv=48)
+    dc.flags = ia.IA_FLAG_CHUNKED_BWD
+    assert bwd(dc) == 7
     assert bwd(desc(bidir=True), st0=state()) == 7
     assert bwd(desc(bidir=True), dst0=state(20)) == 7
     for name in ("q", "k", "v", "lam", "beta", "dO", "dq", "dk", "dv", "dlam", "dbeta"):

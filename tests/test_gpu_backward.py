@@ -81,39 +81,46 @@ def _compare(got, ref, tol, name, slices=None, state=False):
     assert max(errs.values()) < tol, errs
 
 
+# Shapes with F == Dv in {32, 64, 128} run the chunked MFMA backward on the automatic path (these
+# sequences are short); path="sequential" asks for the token-sequential kernels, which the other
+# shapes always run.
+@pytest.mark.parametrize("path", ["auto", "sequential"])
 @pytest.mark.parametrize("shape", [
     (2, 2, 70, 32, 32, 16), (1, 2, 100, 64, 48, 16), (1, 1, 97, 128, 128, 64),
     (1, 2, 65, 16, 16, 32), (2, 1, 33, 32, 32, 16), (2, 1, 64, 256, 64, 16),
-    (1, 1, 40, 192, 256, 32)])
-def test_backward_fp32_matches_oracle(shape):
+    (1, 1, 40, 192, 256, 32), (2, 2, 48, 64, 64, 48), (1, 3, 16, 32, 32, 32)])
+def test_backward_fp32_matches_oracle(shape, path):
     B, H, N, F, D, M = shape
     inp = W.make_inputs(B, H, N, F, D, M, dtype="f32", seed=500 + N + F + D + M)
     dO = np.random.default_rng(501 + N).standard_normal((B, N, H, D)).astype(np.float32)
-    tag(f"backward fp32 B={B} H={H} N={N} F={F} D={D} M={M}")
-    got = _run(inp, dO)
+    tag(f"backward fp32 B={B} H={H} N={N} F={F} D={D} M={M} path={path}")
+    got = _run(inp, dO, path=path)
     ref = oracle.prefill_bwd(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"], dO,
                              threads=4)
-    _compare(got, ref, TOL_F32, f"bwd {shape}")
+    _compare(got, ref, TOL_F32, f"bwd {shape} path={path}")
 
 
-@pytest.mark.parametrize("N", [1, 2, 31, 32, 33, 200])
-def test_backward_with_initial_state(N):
+@pytest.mark.parametrize("FD", [(64, 32), (64, 64)])
+@pytest.mark.parametrize("N", [1, 2, 15, 16, 17, 31, 32, 33, 200])
+def test_backward_with_initial_state(N, FD):
     """Non-zero initial state; the gradient of the initial state too; N around the
-    checkpoint interval.  (The first few tokens from a zero state are tested here, from a
+    checkpoint interval and the chunk length (F = Dv = 64 runs the chunked kernels, 64/32 the
+    token-sequential ones).  (The first few tokens from a zero state are tested here, from a
     state, and in absolute terms below: from zero, o_t for t < 3 or so hardly depends on q
     and k, so their gradients are small differences of the numerator's and denominator's
     terms, and fp32 rounding of those terms is not small relative to them.)"""
-    B, H, F, D, M = 1, 2, 64, 32, 32
+    B, H, M = 1, 2, 32
+    F, D = FD
     inp = W.make_inputs(B, H, N, F, D, M, dtype="f32", seed=510 + N)
     pre = W.make_inputs(B, H, 12, F, D, M, dtype="f32", seed=511, std=0.5)
     st = oracle.prefill(pre["q"], pre["k"], pre["v"], inp["lam"], inp["beta"])[3]
     st = tuple(np.asarray(s, np.complex64).astype(np.complex128) for s in st)
     dO = np.random.default_rng(512).standard_normal((B, N, H, D)).astype(np.float32)
-    tag(f"backward with state N={N}")
+    tag(f"backward with state N={N} F={F} D={D}")
     got = _run(inp, dO, state=st, want_state=True)
     ref = oracle.prefill_bwd(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"], dO,
                              state=st)
-    _compare(got, ref, TOL_F32, f"bwd state N={N}", state=True)
+    _compare(got, ref, TOL_F32, f"bwd state N={N} F={F} D={D}", state=True)
 
 
 def test_backward_single_token_from_zero_state():
@@ -231,15 +238,19 @@ def test_backward_bidirectional(dtype):
              f"bwd bidir {dtype}")
 
 
+@pytest.mark.parametrize("path", ["sequential", "chunked"])
 @pytest.mark.parametrize("case", ["state_fp32", "bf16", "bidir_fp32", "noden_fp32"])
-def test_backward_sequence_segments(case):
-    """Few slices and long enough sequences that the sweeps are cut into segments of 256+
-    tokens (1000 or 2000 tokens: 4 to 8 segments, the last one ragged), joined by the state
-    and adjoint carries."""
+def test_backward_sequence_segments(case, path):
+    """Few slices and long enough sequences that the token-sequential sweeps are cut into
+    segments of 256+ tokens (1000 or 2000 tokens: 4 to 8 segments, the last one ragged), joined
+    by the state and adjoint carries; with path="chunked" the same long sequences on the
+    chunked kernels (one walk per slice and mode group, F = Dv)."""
     import torch
     ia = _ia()
     dtype = "bf16" if case == "bf16" else "f32"
     B, H, N, F, D, M = (1, 2, 2000, 64, 32, 32) if case == "bf16" else (1, 2, 1000, 32, 32, 16)
+    if path == "chunked" and case == "bf16":
+        D = 64
     inp = W.make_inputs(B, H, N, F, D, M, dtype=dtype, seed=570 + N)
     dO = np.random.default_rng(571).standard_normal((B, N, H, D)).astype(np.float32)
     td = torch.bfloat16 if dtype == "bf16" else torch.float32
@@ -248,12 +259,12 @@ def test_backward_sequence_segments(case):
         pre = W.make_inputs(B, H, 12, F, D, M, dtype="f32", seed=572, std=0.5)
         st = oracle.prefill(pre["q"], pre["k"], pre["v"], inp["lam"], inp["beta"])[3]
         st = tuple(np.asarray(x, np.complex64).astype(np.complex128) for x in st)
-    tag(f"backward segments {case} N={N}")
+    tag(f"backward segments {case} N={N} path={path}")
     q, k, v = (dev(inp[n], td) for n in "qkv")
     r = ia.prefill_bwd(q, k, v, dev(inp["lam"]), dev(inp["beta"]), dev(dO),
                        state0=None if st is None else tuple(dev(x) for x in st),
                        want_state_grad=st is not None, bidir=case == "bidir_fp32",
-                       no_den=case == "noden_fp32")
+                       no_den=case == "noden_fp32", path=path)
     torch.cuda.synchronize()
     got = tuple(host(x) for x in r[:5]) + (None if r[5] is None else tuple(host(x) for x in r[5]),)
     if case == "bidir_fp32":
@@ -262,8 +273,8 @@ def test_backward_sequence_segments(case):
     else:
         ref = oracle.prefill_bwd(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"], dO,
                                  state=st, no_den=case == "noden_fp32", threads=2)
-    _compare(got, ref, TOL_BF16 if dtype == "bf16" else TOL_F32, f"bwd segments {case}",
-             state=st is not None)
+    _compare(got, ref, TOL_BF16 if dtype == "bf16" else TOL_F32,
+             f"bwd segments {case} path={path}", state=st is not None)
 
 
 @pytest.mark.parametrize("shape,dtype", [((1, 1, 40, 256, 256, 128), "f32"),
