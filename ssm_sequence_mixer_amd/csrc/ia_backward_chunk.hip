@@ -81,6 +81,8 @@ template <int K, bool AK, bool BK>
 __device__ __forceinline__ void tile_mma(f4& acc, const float* A, int lda, const float* B,
                                          int ldb, int lane) {
   const int rc = lane & 15, kq = 4 * (lane >> 4);
+  // blocks of 16 alternate between two accumulators, so two dependent chains are in flight
+  f4 acc2 = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k0 = 0; k0 < K; k0 += 16) {
     const int kk = k0 + kq;
@@ -99,9 +101,11 @@ __device__ __forceinline__ void tile_mma(f4& acc, const float* A, int lda, const
 #pragma unroll
       for (int s = 0; s < 4; ++s) b[s] = B[(kk + s) * ldb + rc];
     }
+    f4& t = (k0 / 16) % 2 ? acc2 : acc;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc = mfma4(a[s], b[s], acc);
+    for (int s = 0; s < 4; ++s) t = mfma4(a[s], b[s], t);
   }
+  if constexpr (K > 16) acc += acc2;
 }
 
 __device__ __forceinline__ f4 zero4() { return f4{0.f, 0.f, 0.f, 0.f}; }
@@ -209,36 +213,80 @@ struct FwdLds {
   static constexpr size_t bytes = (size_t)floats * 4;
 };
 
-// One chunk's rows into LDS: phi(q), phi(k), v, and (scale 1) dL/do; rows past N are zero.
-template <int F, int D>
-__device__ __forceinline__ void load_rows(const BwdArgs& a, const Wg& w, int t0, float* XQ,
-                                          float* XK, float* XV, float* XD) {
-  constexpr int LF = F + 4, LD = D + 4;
-  for (int e = threadIdx.x; e < kC * F; e += kThreads) {
-    const int i = e / F, f = e % F, t = t0 + i;
-    float q = 0.f, k = 0.f;
-    if (t < a.N) {
-      const size_t r = row_index(a, w, t, F) + f;
-      q = feat(load_in(a.q, r, a.in_bf16), a.opt);
-      k = feat(load_in(a.k, r, a.in_bf16), a.opt);
-    }
-    XQ[i * LF + f] = q;
-    XK[i * LF + f] = k;
-  }
-  for (int e = threadIdx.x; e < kC * D; e += kThreads) {
-    const int i = e / D, d = e % D, t = t0 + i;
-    float v = 0.f, g = 0.f;
-    if (t < a.N) {
-      const size_t r = row_index(a, w, t, D) + d;
-      v = load_in(a.v, r, a.in_bf16);
-      g = load_in(a.dO, r, a.out_bf16);
-    }
-    XV[i * LD + d] = v;
-    XD[i * LD + d] = g;
-  }
-}
+// A chunk's rows of a [B][N][H][W] array (bf16 if BF, else fp32) as 16-byte vectors, PT per
+// thread, held in registers between the load and the write into LDS; rows past N read as zero.
+template <int W, bool BF>
+struct Rows {
+  static constexpr int E = BF ? 8 : 4;             // elements per vector
+  static constexpr int VPR = W / E;                // vectors per row
+  static constexpr int NV = kC * VPR;
+  static constexpr int PT = (NV + kThreads - 1) / kThreads;
+  uint4 r[PT];
 
-template <int F, int D>
+  __device__ __forceinline__ void fetch(const void* base, const BwdArgs& a, const Wg& w, int t0) {
+#pragma unroll
+    for (int p = 0; p < PT; ++p) {
+      const int n = threadIdx.x + kThreads * p, i = n / VPR, t = t0 + i;
+      r[p] = make_uint4(0u, 0u, 0u, 0u);
+      if (n < NV && t < a.N)
+        r[p] = *reinterpret_cast<const uint4*>(static_cast<const char*>(base) +
+                                               (row_index(a, w, t, W) + (n % VPR) * E) *
+                                                   (BF ? 2 : 4));
+    }
+  }
+  // into X ([kC][ld] floats); fmap: the feature map (rows past N stay zero)
+  __device__ __forceinline__ void put(float* X, int ld, int t0, int N, bool fmap, int opt) const {
+#pragma unroll
+    for (int p = 0; p < PT; ++p) {
+      const int n = threadIdx.x + kThreads * p, i = n / VPR;
+      if (n >= NV) continue;
+      float v[E];
+      const uint32_t u[4] = {r[p].x, r[p].y, r[p].z, r[p].w};
+      if constexpr (BF) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[2 * e] = __uint_as_float(u[e] << 16);
+          v[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(u[e]);
+      }
+      if (fmap) {
+        const bool ok = t0 + i < N;
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = ok ? feat(v[e], opt) : 0.f;
+      }
+      float* dst = X + i * ld + (n % VPR) * E;
+#pragma unroll
+      for (int e = 0; e < E; e += 4)
+        *reinterpret_cast<float4*>(dst + e) = make_float4(v[e], v[e + 1], v[e + 2], v[e + 3]);
+    }
+  }
+};
+
+// The four token-row inputs of a chunk: q, k, v (bf16 if BI) and dL/do (bf16 if BO).
+template <int F, int D, bool BI, bool BO>
+struct ChunkRows {
+  Rows<F, BI> q, k;
+  Rows<D, BI> v;
+  Rows<D, BO> g;
+  __device__ __forceinline__ void fetch(const BwdArgs& a, const Wg& w, int t0) {
+    q.fetch(a.q, a, w, t0);
+    k.fetch(a.k, a, w, t0);
+    v.fetch(a.v, a, w, t0);
+    g.fetch(a.dO, a, w, t0);
+  }
+  __device__ __forceinline__ void put(const BwdArgs& a, int t0, float* XQ, float* XK, float* XV,
+                                      float* XG) const {
+    q.put(XQ, F + 4, t0, a.N, true, a.opt);
+    k.put(XK, F + 4, t0, a.N, true, a.opt);
+    v.put(XV, D + 4, t0, a.N, false, 0);
+    g.put(XG, D + 4, t0, a.N, false, 0);
+  }
+};
+
+template <int F, int D, bool BI, bool BO>
 __global__ void __launch_bounds__(kThreads) bwdc_forward_kernel(const BwdArgs a) {
   using L = FwdLds<F, D>;
   constexpr int LF = L::LF, LD = L::LD;
@@ -297,17 +345,24 @@ __global__ void __launch_bounds__(kThreads) bwdc_forward_kernel(const BwdArgs a)
   float* cks = reinterpret_cast<float*>(cks_base) +
                ((size_t)w.slice * groups + w.group) * nch * cks_floats(F, D);
 
+  // chunk c's rows arrive in registers one chunk ahead and stay in flight across its compute
+  ChunkRows<F, D, BI, BO> rows;
+  rows.fetch(a, w, 0);
   for (int c = 0; c < nch; ++c) {
     const int t0 = c * kC, par = c & 1;
-    load_rows<F, D>(a, w, t0, XQ, XK, XV, XD);
+    rows.put(a, t0, XQ, XK, XV, XD);
+    if (c + 1 < nch) rows.fetch(a, w, t0 + kC);
     __syncthreads();
     // ---- phase B: store the chunk's start state; S, S_d, T2, T2_d, and the chunk's state
     // contributions (kept in registers until the update)
     {
       float* dst = cks + (size_t)c * cks_floats(F, D);
-      for (int e = tid; e < kM2 * F; e += kThreads) dst[e] = UC[(e / F) * LF + e % F];
-      for (int e = tid; e < kM2 * D; e += kThreads)
-        dst[kM2 * F + e] = GC[(e / D) * LD + e % D];
+      for (int e = 4 * tid; e < kM2 * F; e += 4 * kThreads)
+        *reinterpret_cast<float4*>(dst + e) =
+            *reinterpret_cast<const float4*>(UC + (e / F) * LF + e % F);
+      for (int e = 4 * tid; e < kM2 * D; e += 4 * kThreads)
+        *reinterpret_cast<float4*>(dst + kM2 * F + e) =
+            *reinterpret_cast<const float4*>(GC + (e / D) * LD + e % D);
       if (tid < kMG) {
         dst[kM2 * (F + D) + tid] = EC[par * kMG + tid].x;
         dst[kM2 * (F + D) + kMG + tid] = EC[par * kMG + tid].y;
@@ -456,7 +511,7 @@ struct RevLds {
   static constexpr size_t bytes = (size_t)floats * 4;
 };
 
-template <int F, int D>
+template <int F, int D, bool BI, bool BO>
 __global__ void __launch_bounds__(kThreads) bwdc_reverse_kernel(const BwdArgs a) {
   using L = RevLds<F, D>;
   constexpr int LF = L::LF, LD = L::LD;
@@ -515,61 +570,92 @@ __global__ void __launch_bounds__(kThreads) bwdc_reverse_kernel(const BwdArgs a)
   constexpr int NYP = F / 16 + D / 16;
   constexpr int YPW = (NYP + kWaves - 1) / kWaves;
 
-  for (int c = nch - 1; c >= 0; --c) {
-    const int t0 = c * kC, par = c & 1;
-    // ---- phase A: inputs, the chunk's start state, 1/c_t and dd_t
-    {
-      const float* src = cks + (size_t)c * cks_floats(F, D);
-      for (int e = tid; e < kM2 * F; e += kThreads) UC[(e / F) * LF + e % F] = src[e];
-      for (int e = tid; e < kM2 * D; e += kThreads) GC[(e / D) * LD + e % D] = src[kM2 * F + e];
-      if (tid < kMG)
-        EC[tid] = make_float2(src[kM2 * (F + D) + tid], src[kM2 * (F + D) + kMG + tid]);
-      if (tid < kC) {
-        const int t = t0 + tid;
-        float inv = 0.f, dd = 0.f;
-        if (t < a.N) {
-          if (no_den) {
-            inv = 1.f;
-          } else {
-            float den = 0.f, gn = 0.f;
-            for (int g = 0; g < groups; ++g) {
-              const float2 p = a.dpart[((size_t)w.slice * a.N + t) * groups + g];
-              den += p.x;
-              gn += p.y;
-            }
-            const float cc = clamp_den(den, a.clamp);
-            inv = 1.f / cc;
-            dd = den >= a.clamp ? -gn * inv * inv : 0.f;
-          }
+  // Chunk c's rows, start state and den partials arrive in registers one chunk ahead.
+  constexpr int NS4 = kM2 * (F + D) / 4;                 // float4s of U and G per stored state
+  constexpr int PTS = (NS4 + kThreads - 1) / kThreads;
+  constexpr int kMaxGroups = kMaxModes / kMG;
+  ChunkRows<F, D, BI, BO> rows;
+  float4 sv[PTS];
+  float2 ev = make_float2(0.f, 0.f), dp[kMaxGroups];
+  auto fetch = [&](int c) {
+    const int t0 = c * kC;
+    rows.fetch(a, w, t0);
+    const float* src = cks + (size_t)c * cks_floats(F, D);
+#pragma unroll
+    for (int p = 0; p < PTS; ++p) {
+      const int n = tid + kThreads * p;
+      sv[p] = n < NS4 ? reinterpret_cast<const float4*>(src)[n] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    if (tid < kMG) ev = make_float2(src[kM2 * (F + D) + tid], src[kM2 * (F + D) + kMG + tid]);
+    if (tid < kC) {
+      const int t = t0 + tid;
+#pragma unroll
+      for (int g = 0; g < kMaxGroups; ++g)
+        dp[g] = g < groups && t < a.N ? a.dpart[((size_t)w.slice * a.N + t) * groups + g]
+                                      : make_float2(0.f, 0.f);
+    }
+  };
+  f4 yre[YPW], yim[YPW];
+  // S^U <- conj(lam^C) S^U + conj(Y_U), S^G likewise, from the Y tiles of the chunk just done
+  auto update_adjoints = [&]() {
+#pragma unroll
+    for (int p = 0; p < YPW; ++p) {
+      const int pr = wv + kWaves * p;
+      if (pr < NYP) {
+        const bool isu = pr < F / 16;
+        float* X = isu ? SU : SG;
+        const int ld = isu ? LF : LD;
+        const int col = 16 * (isu ? pr : pr - F / 16) + acc_col(lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = acc_row(lane, r);
+          const float2 x = make_float2(X[m * ld + col], X[(kMG + m) * ld + col]);
+          const float2 nx = cadd2(cmulc2(x, PW[(kC + kPwLo) * kMG + m]),
+                                  make_float2(yre[p][r], -yim[p][r]));
+          X[m * ld + col] = nx.x;
+          X[(kMG + m) * ld + col] = nx.y;
         }
-        CT[tid] = inv;
-        DD[tid] = dd;
-      }
-      for (int e = tid; e < kC * F; e += kThreads) {
-        const int i = e / F, f = e % F, t = t0 + i;
-        float q = 0.f, k = 0.f;
-        if (t < a.N) {
-          const size_t r = row_index(a, w, t, F) + f;
-          q = feat(load_in(a.q, r, a.in_bf16), a.opt);
-          k = feat(load_in(a.k, r, a.in_bf16), a.opt);
-        }
-        XQ[i * LF + f] = q;
-        XK[i * LF + f] = k;
-      }
-      for (int e = tid; e < kC * D; e += kThreads) {
-        const int i = e / D, d = e % D, t = t0 + i;
-        float v = 0.f, g = 0.f;
-        if (t < a.N) {
-          const size_t r = row_index(a, w, t, D) + d;
-          v = load_in(a.v, r, a.in_bf16);
-          g = load_in(a.dO, r, a.out_bf16);
-        }
-        XV[i * LD + d] = v;
-        XG[i * LD + d] = g;   // scaled by 1/c_t below
       }
     }
-    __syncthreads();
-    for (int e = tid; e < kC * D; e += kThreads) XG[(e / D) * LD + e % D] *= CT[e / D];
+  };
+
+  fetch(nch - 1);
+  for (int c = nch - 1; c >= 0; --c) {
+    const int t0 = c * kC, par = c & 1;
+    // ---- phase A: the adjoint update of chunk c+1; chunk c's inputs, start state, 1/c_t and
+    // dd_t into LDS; chunk c-1's loads issued
+    if (c + 1 < nch) update_adjoints();
+    rows.put(a, t0, XQ, XK, XV, XG);   // XG: dL/do, scaled by 1/c_t in phase C
+#pragma unroll
+    for (int p = 0; p < PTS; ++p) {
+      const int e = 4 * (tid + kThreads * p);
+      if (e < kM2 * F)
+        *reinterpret_cast<float4*>(UC + (e / F) * LF + e % F) = sv[p];
+      else if (e < kM2 * (F + D))
+        *reinterpret_cast<float4*>(GC + ((e - kM2 * F) / D) * LD + (e - kM2 * F) % D) = sv[p];
+    }
+    if (tid < kMG) EC[tid] = ev;
+    if (tid < kC) {
+      float inv = 0.f, dd = 0.f;
+      if (t0 + tid < a.N) {
+        if (no_den) {
+          inv = 1.f;
+        } else {
+          float den = 0.f, gn = 0.f;
+#pragma unroll
+          for (int g = 0; g < kMaxGroups; ++g) {
+            den += dp[g].x;
+            gn += dp[g].y;
+          }
+          const float cc = clamp_den(den, a.clamp);
+          inv = 1.f / cc;
+          dd = den >= a.clamp ? -gn * inv * inv : 0.f;
+        }
+      }
+      CT[tid] = inv;
+      DD[tid] = dd;
+    }
+    if (c > 0) fetch(c - 1);
     __syncthreads();
     // ---- phase B: S, S', T2, T2', Z, Z' (K = F or D)
     for (int tk = wv; tk < 10; tk += kWaves) {
@@ -585,15 +671,21 @@ __global__ void __launch_bounds__(kThreads) bwdc_reverse_kernel(const BwdArgs a)
       for (int r = 0; r < 4; ++r) {
         const int row = acc_row(lane, r);
         if (tk == 0) S1[row * LC + col] = col <= row ? acc[r] : 0.f;
-        else if (tk == 1) SG1[row * LC + col] = col <= row ? acc[r] + DD[row] : 0.f;
+        else if (tk == 1) SG1[row * LC + col] = col <= row ? CT[row] * acc[r] + DD[row] : 0.f;
         else if (tk < 4) T2[row * L2M + 16 * (tk - 2) + col] = acc[r];
-        else if (tk < 6) T2G[row * L2M + 16 * (tk - 4) + col] = acc[r];
+        else if (tk < 6) T2G[row * L2M + 16 * (tk - 4) + col] = CT[row] * acc[r];
         else if (tk < 8) Z[(16 * (tk - 6) + row) * LC + col] = acc[r];
         else ZG[(16 * (tk - 8) + row) * LC + col] = acc[r];
       }
     }
     __syncthreads();
-    // ---- phase C: T01 = S W01, T01' = S' W01 (K = C)
+    // ---- phase C: T01 = S W01, T01' = S' W01 (K = C); the rows of G scaled to dL/do / c_t
+    for (int e = 4 * tid; e < kC * D; e += 4 * kThreads) {
+      float4* x = reinterpret_cast<float4*>(XG + (e / D) * LD + e % D);
+      const float sc = CT[e / D];
+      const float4 y = *x;
+      *x = make_float4(sc * y.x, sc * y.y, sc * y.z, sc * y.w);
+    }
     {
       const float* Sx = wv < 4 ? S1 : SG1;
       float* Tx = wv < 4 ? T01 : T01G;
@@ -719,7 +811,6 @@ __global__ void __launch_bounds__(kThreads) bwdc_reverse_kernel(const BwdArgs a)
         if (t < a.N) gp[(size_t)t * W + (kind == 0 ? 0 : kind == 1 ? F : 2 * F) + col] = x;
       }
     }
-    f4 yre[YPW], yim[YPW];
 #pragma unroll
     for (int p = 0; p < YPW; ++p) {
       const int pr = wv + kWaves * p;
@@ -735,28 +826,9 @@ __global__ void __launch_bounds__(kThreads) bwdc_reverse_kernel(const BwdArgs a)
       }
     }
     __syncthreads();
-    // ---- phase G: S^U <- conj(lam^C) S^U + conj(Y_U), S^G likewise
-#pragma unroll
-    for (int p = 0; p < YPW; ++p) {
-      const int pr = wv + kWaves * p;
-      if (pr < NYP) {
-        const bool isu = pr < F / 16;
-        float* X = isu ? SU : SG;
-        const int ld = isu ? LF : LD;
-        const int col = 16 * (isu ? pr : pr - F / 16) + acc_col(lane);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = acc_row(lane, r);
-          const float2 x = make_float2(X[m * ld + col], X[(kMG + m) * ld + col]);
-          const float2 nx = cadd2(cmulc2(x, PW[(kC + kPwLo) * kMG + m]),
-                                  make_float2(yre[p][r], -yim[p][r]));
-          X[m * ld + col] = nx.x;
-          X[(kMG + m) * ld + col] = nx.y;
-        }
-      }
-    }
-    __syncthreads();
   }
+  update_adjoints();   // chunk 0's
+  __syncthreads();
 
   // gradient of the initial state: the adjoints left after chunk 0
   if (a.dU0) {
@@ -793,23 +865,32 @@ hipError_t allow_lds_c(const void* kernel, size_t bytes, size_t& allowed) {
   return e;
 }
 
-template <int F, int D>
+template <int F, int D, bool BI, bool BO>
 hipError_t launch_bwdc(const BwdArgs& a, hipStream_t st) {
   static size_t allowed_f = 65536, allowed_r = 65536;
   const size_t lf = FwdLds<F, D>::bytes, lr = RevLds<F, D>::bytes;
-  hipError_t e = allow_lds_c(reinterpret_cast<const void*>(&bwdc_forward_kernel<F, D>), lf,
-                             allowed_f);
+  hipError_t e = allow_lds_c(reinterpret_cast<const void*>(&bwdc_forward_kernel<F, D, BI, BO>),
+                             lf, allowed_f);
   if (e == hipSuccess)
-    e = allow_lds_c(reinterpret_cast<const void*>(&bwdc_reverse_kernel<F, D>), lr, allowed_r);
+    e = allow_lds_c(reinterpret_cast<const void*>(&bwdc_reverse_kernel<F, D, BI, BO>), lr,
+                    allowed_r);
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((size_t)a.B * a.H * (a.M / kMG));
   prof_begin(st);
-  hipLaunchKernelGGL((bwdc_forward_kernel<F, D>), dim3(grid), dim3(kThreads), lf, st, a);
+  hipLaunchKernelGGL((bwdc_forward_kernel<F, D, BI, BO>), dim3(grid), dim3(kThreads), lf, st, a);
   prof_end(st, kKindBwdForward);
   prof_begin(st);
-  hipLaunchKernelGGL((bwdc_reverse_kernel<F, D>), dim3(grid), dim3(kThreads), lr, st, a);
+  hipLaunchKernelGGL((bwdc_reverse_kernel<F, D, BI, BO>), dim3(grid), dim3(kThreads), lr, st, a);
   prof_end(st, kKindBwdReverse);
   return hipGetLastError();
+}
+
+template <int F>
+hipError_t launch_bwdc_f(const BwdArgs& a, hipStream_t st) {
+  if (a.in_bf16) return a.out_bf16 ? launch_bwdc<F, F, true, true>(a, st)
+                                   : launch_bwdc<F, F, true, false>(a, st);
+  return a.out_bf16 ? launch_bwdc<F, F, false, true>(a, st)
+                    : launch_bwdc<F, F, false, false>(a, st);
 }
 
 }  // namespace
@@ -836,9 +917,9 @@ BwdLayout bwd_chunked_layout(int B, int H, int N, int F, int D, int M) {
 hipError_t launch_prefill_bwd_chunked(const BwdArgs& a, hipStream_t st) {
   (void)hipGetLastError();
   hipError_t e = hipErrorInvalidValue;
-  if (a.F == 32 && a.D == 32) e = launch_bwdc<32, 32>(a, st);
-  else if (a.F == 64 && a.D == 64) e = launch_bwdc<64, 64>(a, st);
-  else if (a.F == 128 && a.D == 128) e = launch_bwdc<128, 128>(a, st);
+  if (a.F == 32 && a.D == 32) e = launch_bwdc_f<32>(a, st);
+  else if (a.F == 64 && a.D == 64) e = launch_bwdc_f<64>(a, st);
+  else if (a.F == 128 && a.D == 128) e = launch_bwdc_f<128>(a, st);
   if (e != hipSuccess) return e;
   return launch_bwd_reduce(a, st);
 }
