@@ -612,16 +612,23 @@ __global__ void __launch_bounds__(kThreads) bwd_reverse_kernel(const BwdArgs a) 
 }
 
 // dq, dk, dv: the mode groups' partials summed in group order, stored in the input dtype;
-// lambda and beta gradients summed over the batch in b order.
+// lambda and beta gradients summed over the batch in b order.  Four consecutive columns per
+// thread (F and Dv are multiples of 16, so the four lie in one of dq, dk, dv).
 __global__ void __launch_bounds__(256) bwd_reduce_kernel(const BwdArgs a) {
   const int W = 2 * a.F + a.D;
   const int groups = a.M / kModesPerWg;
   const size_t S = (size_t)a.B * a.H;
   const size_t n = S * a.N * W;
-  for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < n;
-       e += (size_t)gridDim.x * blockDim.x) {
-    float sum = 0.f;
-    for (int g = 0; g < groups; ++g) sum += a.gpart[(size_t)g * n + e];
+  for (size_t e = 4 * (blockIdx.x * (size_t)blockDim.x + threadIdx.x); e < n;
+       e += 4 * (size_t)gridDim.x * blockDim.x) {
+    float4 sum = *reinterpret_cast<const float4*>(a.gpart + e);
+    for (int g = 1; g < groups; ++g) {
+      const float4 x = *reinterpret_cast<const float4*>(a.gpart + (size_t)g * n + e);
+      sum.x += x.x;
+      sum.y += x.y;
+      sum.z += x.z;
+      sum.w += x.w;
+    }
     const size_t sl = e / ((size_t)a.N * W);
     const size_t rem = e - sl * a.N * W;
     const size_t t = rem / W;
@@ -640,8 +647,29 @@ __global__ void __launch_bounds__(256) bwd_reduce_kernel(const BwdArgs a) {
       dst = a.dv;
       i = row * a.D + col - 2 * a.F;
     }
-    if (a.accumulate) sum += load_in(dst, i, a.in_bf16);
-    store_out(dst, i, sum, a.in_bf16);
+    float v[4] = {sum.x, sum.y, sum.z, sum.w};
+    if (a.in_bf16) {
+      uint2* p = reinterpret_cast<uint2*>(static_cast<uint16_t*>(dst) + i);
+      if (a.accumulate) {
+        const uint2 o = *p;
+        v[0] += __uint_as_float(o.x << 16);
+        v[1] += __uint_as_float(o.x & 0xffff0000u);
+        v[2] += __uint_as_float(o.y << 16);
+        v[3] += __uint_as_float(o.y & 0xffff0000u);
+      }
+      *p = make_uint2((uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                      (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+    } else {
+      float4* p = reinterpret_cast<float4*>(static_cast<float*>(dst) + i);
+      if (a.accumulate) {
+        const float4 o = *p;
+        v[0] += o.x;
+        v[1] += o.y;
+        v[2] += o.z;
+        v[3] += o.w;
+      }
+      *p = make_float4(v[0], v[1], v[2], v[3]);
+    }
   }
   const size_t hm = (size_t)a.H * a.M;
   for (size_t e = blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < hm;
@@ -840,7 +868,7 @@ hipError_t launch_prefill_bwd(const BwdArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_bwd_reduce(const BwdArgs& a, hipStream_t st) {
-  const size_t n = (size_t)a.B * a.H * a.N * (2 * a.F + a.D);
+  const size_t n = (size_t)a.B * a.H * a.N * (2 * a.F + a.D) / 4;
   size_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks < 1) blocks = 1;

@@ -77,33 +77,56 @@ __device__ __forceinline__ f4 mfma4(float a, float b, f4 c) {
 // acc += A B over K (a multiple of 16) for one 16 x 16 tile.  A points at the tile's first row
 // (AK: A(r,k) = A[r*lda + k], else A(r,k) = A[k*lda + r]); B at its first column (BK:
 // B(k,n) = B[n*ldb + k], else B(k,n) = B[k*ldb + n]).
-template <int K, bool AK, bool BK>
+// Operands of one K block of 16 (four MFMA steps) into registers.
+template <bool AK, bool BK>
+__device__ __forceinline__ void tile_operands(float (&a)[4], float (&b)[4], const float* A,
+                                              int lda, const float* B, int ldb, int rc, int kk) {
+  if constexpr (AK) {
+    const float4 x = *reinterpret_cast<const float4*>(A + rc * lda + kk);
+    a[0] = x.x; a[1] = x.y; a[2] = x.z; a[3] = x.w;
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[s] = A[(kk + s) * lda + rc];
+  }
+  if constexpr (BK) {
+    const float4 x = *reinterpret_cast<const float4*>(B + rc * ldb + kk);
+    b[0] = x.x; b[1] = x.y; b[2] = x.z; b[3] = x.w;
+  } else {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) b[s] = B[(kk + s) * ldb + rc];
+  }
+}
+
+// PIPE: the next block's operands are read from LDS before the current block's MFMAs issue
+// (eight more registers; for kernels with registers to spare).
+template <int K, bool AK, bool BK, bool PIPE = false>
 __device__ __forceinline__ void tile_mma(f4& acc, const float* A, int lda, const float* B,
                                          int ldb, int lane) {
+  static_assert(K % 16 == 0, "K in blocks of 16");
   const int rc = lane & 15, kq = 4 * (lane >> 4);
-  // blocks of 16 alternate between two accumulators, so two dependent chains are in flight
+  // blocks of 16 alternate between two accumulators (two dependent chains in flight)
   f4 acc2 = f4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (PIPE) {
+    float a[2][4], b[2][4];
+    tile_operands<AK, BK>(a[0], b[0], A, lda, B, ldb, rc, kq);
 #pragma unroll
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    const int kk = k0 + kq;
-    float a[4], b[4];
-    if constexpr (AK) {
-      const float4 x = *reinterpret_cast<const float4*>(A + rc * lda + kk);
-      a[0] = x.x; a[1] = x.y; a[2] = x.z; a[3] = x.w;
-    } else {
+    for (int blk = 0; blk < K / 16; ++blk) {
+      if (blk + 1 < K / 16)
+        tile_operands<AK, BK>(a[(blk + 1) & 1], b[(blk + 1) & 1], A, lda, B, ldb, rc,
+                              16 * (blk + 1) + kq);
+      f4& t = blk & 1 ? acc2 : acc;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) a[s] = A[(kk + s) * lda + rc];
+      for (int s = 0; s < 4; ++s) t = mfma4(a[blk & 1][s], b[blk & 1][s], t);
     }
-    if constexpr (BK) {
-      const float4 x = *reinterpret_cast<const float4*>(B + rc * ldb + kk);
-      b[0] = x.x; b[1] = x.y; b[2] = x.z; b[3] = x.w;
-    } else {
+  } else {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) b[s] = B[(kk + s) * ldb + rc];
+    for (int blk = 0; blk < K / 16; ++blk) {
+      float a[4], b[4];
+      tile_operands<AK, BK>(a, b, A, lda, B, ldb, rc, 16 * blk + kq);
+      f4& t = blk & 1 ? acc2 : acc;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) t = mfma4(a[s], b[s], t);
     }
-    f4& t = (k0 / 16) % 2 ? acc2 : acc;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) t = mfma4(a[s], b[s], t);
   }
   if constexpr (K > 16) acc += acc2;
 }
@@ -372,13 +395,13 @@ __global__ void __launch_bounds__(kThreads) bwdc_forward_kernel(const BwdArgs a)
     if (wv < 6) {
       f4 acc = zero4();
       if (wv == 0) {
-        tile_mma<F, true, true>(acc, XQ, LF, XK, LF, lane);
+        tile_mma<F, true, true, true>(acc, XQ, LF, XK, LF, lane);
       } else if (wv == 1) {
-        tile_mma<D, true, true>(acc, XD, LD, XV, LD, lane);
+        tile_mma<D, true, true, true>(acc, XD, LD, XV, LD, lane);
       } else if (wv < 4) {
-        tile_mma<F, true, true>(acc, XQ, LF, UC + 16 * (wv - 2) * LF, LF, lane);
+        tile_mma<F, true, true, true>(acc, XQ, LF, UC + 16 * (wv - 2) * LF, LF, lane);
       } else {
-        tile_mma<D, true, true>(acc, XD, LD, GC + 16 * (wv - 4) * LD, LD, lane);
+        tile_mma<D, true, true, true>(acc, XD, LD, GC + 16 * (wv - 4) * LD, LD, lane);
       }
       const int col = acc_col(lane);
 #pragma unroll
@@ -404,12 +427,12 @@ __global__ void __launch_bounds__(kThreads) bwdc_forward_kernel(const BwdArgs a)
       kre[p] = zero4();
       kim[p] = zero4();
       if (pr < F / 16) {
-        tile_mma<kC, true, false>(kre[p], AW0E, LC, XK + 16 * pr, LF, lane);
-        tile_mma<kC, true, false>(kim[p], AW0E + kMG * LC, LC, XK + 16 * pr, LF, lane);
+        tile_mma<kC, true, false, true>(kre[p], AW0E, LC, XK + 16 * pr, LF, lane);
+        tile_mma<kC, true, false, true>(kim[p], AW0E + kMG * LC, LC, XK + 16 * pr, LF, lane);
       } else if (pr < NPAIR) {
         const int dc = pr - F / 16;
-        tile_mma<kC, true, false>(kre[p], AW0E, LC, XV + 16 * dc, LD, lane);
-        tile_mma<kC, true, false>(kim[p], AW0E + kMG * LC, LC, XV + 16 * dc, LD, lane);
+        tile_mma<kC, true, false, true>(kre[p], AW0E, LC, XV + 16 * dc, LD, lane);
+        tile_mma<kC, true, false, true>(kim[p], AW0E + kMG * LC, LC, XV + 16 * dc, LD, lane);
       }
     }
     __syncthreads();
@@ -418,7 +441,7 @@ __global__ void __launch_bounds__(kThreads) bwdc_forward_kernel(const BwdArgs a)
       f4 acc = zero4();
       const float* Sx = wv < 2 ? S1 : SD1;
       const int nb = 16 * (wv & 1);
-      tile_mma<kC, true, false>(acc, Sx, LC, W0 + nb, L2M, lane);
+      tile_mma<kC, true, false, true>(acc, Sx, LC, W0 + nb, L2M, lane);
       float* Tx = wv < 2 ? T0 : T0D;
       const int col = acc_col(lane);
 #pragma unroll
@@ -507,7 +530,8 @@ struct RevLds {
   static constexpr int SE = EC + 2 * kMG;        // [2][kMG] float2 (parity)
   static constexpr int CT = SE + 4 * kMG;        // [kC]: 1 / c_t
   static constexpr int DD = CT + kC;             // [kC]: dd_t
-  static constexpr int floats = DD + kC;
+  static constexpr int LSUM = DD + kC;           // [kMG] float2 x 2: dlam, dbeta of waves 4-7
+  static constexpr int floats = LSUM + 4 * kMG;
   static constexpr size_t bytes = (size_t)floats * 4;
 };
 
@@ -528,6 +552,7 @@ __global__ void __launch_bounds__(kThreads) bwdc_reverse_kernel(const BwdArgs a)
   float2* EC = reinterpret_cast<float2*>(sm + L::EC);
   float2* SE = reinterpret_cast<float2*>(sm + L::SE);
   float *CT = sm + L::CT, *DD = sm + L::DD;
+  float2* LSUM = reinterpret_cast<float2*>(sm + L::LSUM);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const Wg w = wg_of(a);
   const int groups = a.M / kMG;
@@ -574,9 +599,10 @@ __global__ void __launch_bounds__(kThreads) bwdc_reverse_kernel(const BwdArgs a)
   constexpr int NS4 = kM2 * (F + D) / 4;                 // float4s of U and G per stored state
   constexpr int PTS = (NS4 + kThreads - 1) / kThreads;
   constexpr int kMaxGroups = kMaxModes / kMG;
+  static_assert(kMaxGroups <= 8, "den partials staged 8 groups per token");
   ChunkRows<F, D, BI, BO> rows;
   float4 sv[PTS];
-  float2 ev = make_float2(0.f, 0.f), dp[kMaxGroups];
+  float2 ev = make_float2(0.f, 0.f), dp = make_float2(0.f, 0.f);
   auto fetch = [&](int c) {
     const int t0 = c * kC;
     rows.fetch(a, w, t0);
@@ -587,12 +613,10 @@ __global__ void __launch_bounds__(kThreads) bwdc_reverse_kernel(const BwdArgs a)
       sv[p] = n < NS4 ? reinterpret_cast<const float4*>(src)[n] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     if (tid < kMG) ev = make_float2(src[kM2 * (F + D) + tid], src[kM2 * (F + D) + kMG + tid]);
-    if (tid < kC) {
-      const int t = t0 + tid;
-#pragma unroll
-      for (int g = 0; g < kMaxGroups; ++g)
-        dp[g] = g < groups && t < a.N ? a.dpart[((size_t)w.slice * a.N + t) * groups + g]
-                                      : make_float2(0.f, 0.f);
+    if (tid < kC * 8) {   // token tid / 8, group tid % 8 (groups <= 8)
+      const int t = t0 + (tid >> 3), g = tid & 7;
+      dp = g < groups && t < a.N ? a.dpart[((size_t)w.slice * a.N + t) * groups + g]
+                                 : make_float2(0.f, 0.f);
     }
   };
   f4 yre[YPW], yim[YPW];
@@ -635,37 +659,40 @@ __global__ void __launch_bounds__(kThreads) bwdc_reverse_kernel(const BwdArgs a)
         *reinterpret_cast<float4*>(GC + ((e - kM2 * F) / D) * LD + (e - kM2 * F) % D) = sv[p];
     }
     if (tid < kMG) EC[tid] = ev;
-    if (tid < kC) {
-      float inv = 0.f, dd = 0.f;
-      if (t0 + tid < a.N) {
-        if (no_den) {
-          inv = 1.f;
-        } else {
-          float den = 0.f, gn = 0.f;
+    if (tid < kC * 8) {   // 1/c_t and dd_t: the groups' partials of token tid / 8 summed
+      float den = dp.x, gn = dp.y;
 #pragma unroll
-          for (int g = 0; g < kMaxGroups; ++g) {
-            den += dp[g].x;
-            gn += dp[g].y;
-          }
-          const float cc = clamp_den(den, a.clamp);
-          inv = 1.f / cc;
-          dd = den >= a.clamp ? -gn * inv * inv : 0.f;
-        }
+      for (int off = 4; off > 0; off >>= 1) {
+        den += __shfl_xor(den, off, 64);
+        gn += __shfl_xor(gn, off, 64);
       }
-      CT[tid] = inv;
-      DD[tid] = dd;
+      const int i = tid >> 3;
+      if ((tid & 7) == 0) {
+        float inv = 0.f, dd = 0.f;
+        if (t0 + i < a.N) {
+          if (no_den) {
+            inv = 1.f;
+          } else {
+            const float cc = clamp_den(den, a.clamp);
+            inv = 1.f / cc;
+            dd = den >= a.clamp ? -gn * inv * inv : 0.f;
+          }
+        }
+        CT[i] = inv;
+        DD[i] = dd;
+      }
     }
     if (c > 0) fetch(c - 1);
     __syncthreads();
     // ---- phase B: S, S', T2, T2', Z, Z' (K = F or D)
     for (int tk = wv; tk < 10; tk += kWaves) {
       f4 acc = zero4();
-      if (tk == 0) tile_mma<F, true, true>(acc, XQ, LF, XK, LF, lane);
-      else if (tk == 1) tile_mma<D, true, true>(acc, XG, LD, XV, LD, lane);
-      else if (tk < 4) tile_mma<F, true, true>(acc, XQ, LF, UC + 16 * (tk - 2) * LF, LF, lane);
-      else if (tk < 6) tile_mma<D, true, true>(acc, XG, LD, GC + 16 * (tk - 4) * LD, LD, lane);
-      else if (tk < 8) tile_mma<F, true, true>(acc, SU + 16 * (tk - 6) * LF, LF, XK, LF, lane);
-      else tile_mma<D, true, true>(acc, SG + 16 * (tk - 8) * LD, LD, XV, LD, lane);
+      if (tk == 0) tile_mma<F, true, true, true>(acc, XQ, LF, XK, LF, lane);
+      else if (tk == 1) tile_mma<D, true, true, true>(acc, XG, LD, XV, LD, lane);
+      else if (tk < 4) tile_mma<F, true, true, true>(acc, XQ, LF, UC + 16 * (tk - 2) * LF, LF, lane);
+      else if (tk < 6) tile_mma<D, true, true, true>(acc, XG, LD, GC + 16 * (tk - 4) * LD, LD, lane);
+      else if (tk < 8) tile_mma<F, true, true, true>(acc, SU + 16 * (tk - 6) * LF, LF, XK, LF, lane);
+      else tile_mma<D, true, true, true>(acc, SG + 16 * (tk - 8) * LD, LD, XV, LD, lane);
       const int col = acc_col(lane);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -697,7 +724,8 @@ __global__ void __launch_bounds__(kThreads) bwdc_reverse_kernel(const BwdArgs a)
       for (int r = 0; r < 4; ++r) Tx[acc_row(lane, r) * L4M + nb + col] = acc[r];
     }
     __syncthreads();
-    // ---- phase D: per (token i, mode m)
+    // ---- phase D: per (token i, mode m); waves 0-3 the readout terms, waves 4-7 the terms of
+    // the carried adjoints
     if (tid < kC * kMG) {
       const int i = ei, m = em;
       const float2 li = PW[(i - kO + kPwLo) * kMG + m], l1 = PW[(i + 1 + kPwLo) * kMG + m];
@@ -734,34 +762,40 @@ __global__ void __launch_bounds__(kThreads) bwdc_reverse_kernel(const BwdArgs a)
       const float fi = (float)i;
       const float2 D1 = cmul(lq1, make_float2(fi * t0v.x - t1v.x, fi * t0v.y - t1v.y));
       const float2 D1g = cmul(lq1, make_float2(fi * t0g.x - t1g.x, fi * t0g.y - t1g.y));
-      float2 s = cmul(b, cadd2(cmul(Ag, D1), cmul(av, D1g)));
-      s = cadd2(s, csc(fi + 1.f, cmul(li0, cadd2(cmul(Ag, t2), cmul(av, t2g)))));
+      float2 sx = cmul(b, cadd2(cmul(Ag, D1), cmul(av, D1g)));
+      sx = cadd2(sx, csc(fi + 1.f, cmul(li0, cadd2(cmul(Ag, t2), cmul(av, t2g)))));
+      dlam = cadd2(dlam, cconj(sx));
+      // the eta adjoint: S^e <- conj(lam^C) S^e + conj(sum_i lam^(i+1) a_i dd_i)
+      const float2 sev = SE[par * kMG + m];
+      float sr = row16_sum(ddi * l1a.x), si = row16_sum(ddi * l1a.y);
+      if (i == 0)
+        SE[(par ^ 1) * kMG + m] =
+            cadd2(cmulc2(sev, PW[(kC + kPwLo) * kMG + m]), make_float2(sr, -si));
+    } else {
+      const int i = ei, m = em - kMG;
+      const float2 b = BETA[m];
       // carried adjoints, token j = i: Z[m,j] = S^U . phi(k_j), Z'[m,j] = S^G . v_j + S^e
       const float2 sev = SE[par * kMG + m];
       const float2 zz = cadd2(make_float2(Z[m * LC + i], Z[(kMG + m) * LC + i]),
                               cadd2(make_float2(ZG[m * LC + i], ZG[(kMG + m) * LC + i]), sev));
       dbet = cadd2(dbet, cmulc2(zz, PW[(kC - 1 - i + kPwLo) * kMG + m]));
-      // (C-1-j) conj(beta lam^(C-2-j)) Z_total[m,j], accumulated conjugated like the terms above
+      // dlam: (C-1-j) conj(beta lam^(C-2-j)) Z_total[m,j] and C conj(lam^(C-1)) (S^U . conj(U_c)
+      // + S^G . conj(G_c) + S^e conj(e_c)), the dot products spread over the mode's 16 threads
+      float2 sx = make_float2(0.f, 0.f);
       if (i < kC - 1)
-        s = cadd2(s, csc((float)(kC - 1 - i),
-                         cmul(cconj(zz), cmul(b, PW[(kC - 2 - i + kPwLo) * kMG + m]))));
-      // C conj(lam^(C-1)) (S^U . conj(U_c) + S^G . conj(G_c) + S^e conj(e_c)), the dot products
-      // spread over the 16 token threads of the mode
+        sx = csc((float)(kC - 1 - i),
+                 cconj(cmul(cconj(zz), cmul(b, PW[(kC - 2 - i + kPwLo) * kMG + m]))));
       float2 dotv = make_float2(0.f, 0.f);
+#pragma unroll 2
       for (int f = i; f < F; f += 16)
         dotv = cadd2(dotv, cmulc2(make_float2(SU[m * LF + f], SU[(kMG + m) * LF + f]),
                                   make_float2(UC[m * LF + f], UC[(kMG + m) * LF + f])));
+#pragma unroll 2
       for (int d = i; d < D; d += 16)
         dotv = cadd2(dotv, cmulc2(make_float2(SG[m * LD + d], SG[(kMG + m) * LD + d]),
                                   make_float2(GC[m * LD + d], GC[(kMG + m) * LD + d])));
-      if (i == 0) dotv = cadd2(dotv, cmulc2(sev, ecm));
-      s = cadd2(cconj(s), csc((float)kC, cmulc2(dotv, PW[(kC - 1 + kPwLo) * kMG + m])));
-      dlam = cadd2(dlam, s);
-      // the eta adjoint: S^e <- conj(lam^C) S^e + conj(sum_i lam^(i+1) a_i dd_i)
-      float sr = row16_sum(ddi * l1a.x), si = row16_sum(ddi * l1a.y);
-      if (i == 0)
-        SE[(par ^ 1) * kMG + m] =
-            cadd2(cmulc2(sev, PW[(kC + kPwLo) * kMG + m]), make_float2(sr, -si));
+      if (i == 0) dotv = cadd2(dotv, cmulc2(sev, EC[m]));
+      dlam = cadd2(dlam, cadd2(sx, csc((float)kC, cmulc2(dotv, PW[(kC - 1 + kPwLo) * kMG + m]))));
     }
     __syncthreads();
     // ---- phase E: P and Pg (K = 2 MG), causal, into the operands of phase F
@@ -845,14 +879,19 @@ __global__ void __launch_bounds__(kThreads) bwdc_reverse_kernel(const BwdArgs a)
     // chunk 0 (parity 0) wrote the eta adjoint into parity slot 1
     if (tid < kMG) a.dE0[(size_t)w.slice * a.M + w.m0 + tid] = SE[kMG + tid];
   }
-  // dlam, dbeta: sum over the 16 token threads of each mode
-  if (tid < kC * kMG) {
+  // dlam, dbeta: sum over the 16 token threads of each mode, then over the two wave halves
+  {
     const float lr = row16_sum(dlam.x), lim = row16_sum(dlam.y);
     const float br = row16_sum(dbet.x), bim = row16_sum(dbet.y);
-    if (ei == 0) {
+    if (ei == 0 && tid >= kC * kMG) {
+      LSUM[em - kMG] = make_float2(lr, lim);
+      LSUM[em] = make_float2(br, bim);
+    }
+    __syncthreads();
+    if (ei == 0 && tid < kC * kMG) {
       const size_t i = (size_t)w.slice * a.M + w.m0 + em;
-      a.lpart[2 * i] = make_float2(lr, lim);
-      a.lpart[2 * i + 1] = make_float2(br, bim);
+      a.lpart[2 * i] = cadd2(make_float2(lr, lim), LSUM[em]);
+      a.lpart[2 * i + 1] = cadd2(make_float2(br, bim), LSUM[kMG + em]);
     }
   }
 }
