@@ -368,6 +368,23 @@ __global__ void __launch_bounds__(kThreads) bwdc_forward_kernel(const BwdArgs a)
   float* cks = reinterpret_cast<float*>(cks_base) +
                ((size_t)w.slice * groups + w.group) * nch * cks_floats(F, D);
 
+  // start state of chunk cc (U, G planar in LDS, e in EC[par]) into its workspace block, by half
+  // the workgroup (t: the thread's index among them; threads with t outside [0, nt) return)
+  auto store_state = [&](int cc, int par, int t) {
+    constexpr int nt = kThreads / 2;
+    if (t < 0 || t >= nt) return;
+    float* dst = cks + (size_t)cc * cks_floats(F, D);
+    for (int e = 4 * t; e < kM2 * F; e += 4 * nt)
+      *reinterpret_cast<float4*>(dst + e) =
+          *reinterpret_cast<const float4*>(UC + (e / F) * LF + e % F);
+    for (int e = 4 * t; e < kM2 * D; e += 4 * nt)
+      *reinterpret_cast<float4*>(dst + kM2 * F + e) =
+          *reinterpret_cast<const float4*>(GC + (e / D) * LD + e % D);
+    if (t < kMG) {
+      dst[kM2 * (F + D) + t] = EC[par * kMG + t].x;
+      dst[kM2 * (F + D) + kMG + t] = EC[par * kMG + t].y;
+    }
+  };
   // chunk c's rows arrive in registers one chunk ahead and stay in flight across its compute
   ChunkRows<F, D, BI, BO> rows;
   rows.fetch(a, w, 0);
@@ -376,21 +393,10 @@ __global__ void __launch_bounds__(kThreads) bwdc_forward_kernel(const BwdArgs a)
     rows.put(a, t0, XQ, XK, XV, XD);
     if (c + 1 < nch) rows.fetch(a, w, t0 + kC);
     __syncthreads();
-    // ---- phase B: store the chunk's start state; S, S_d, T2, T2_d, and the chunk's state
-    // contributions (kept in registers until the update)
-    {
-      float* dst = cks + (size_t)c * cks_floats(F, D);
-      for (int e = 4 * tid; e < kM2 * F; e += 4 * kThreads)
-        *reinterpret_cast<float4*>(dst + e) =
-            *reinterpret_cast<const float4*>(UC + (e / F) * LF + e % F);
-      for (int e = 4 * tid; e < kM2 * D; e += 4 * kThreads)
-        *reinterpret_cast<float4*>(dst + kM2 * F + e) =
-            *reinterpret_cast<const float4*>(GC + (e / D) * LD + e % D);
-      if (tid < kMG) {
-        dst[kM2 * (F + D) + tid] = EC[par * kMG + tid].x;
-        dst[kM2 * (F + D) + kMG + tid] = EC[par * kMG + tid].y;
-      }
-    }
+    // ---- phase B: S, S_d, T2, T2_d, and the chunk's state contributions (kept in registers
+    // until the update); chunk 0's start state is stored here, every later one in the previous
+    // chunk's phase D
+    if (c == 0) store_state(0, 0, tid);
     // big tiles: 0 S, 1 S_d, 2-3 T2, 4-5 T2_d
     if (wv < 6) {
       f4 acc = zero4();
@@ -471,6 +477,8 @@ __global__ void __launch_bounds__(kThreads) bwdc_forward_kernel(const BwdArgs a)
                                        cmul(BETA[tid], E0T[(kC - 1) * kMG + tid]));
     __syncthreads();
     // ---- phase D: per (token i, mode m) the readout terms, summed over the group's modes
+    // (waves 0-3); waves 4-7 store the updated state, the next chunk's start state
+    if (c + 1 < nch) store_state(c + 1, par ^ 1, tid - kThreads / 2);
     if (tid < kC * kMG) {
       const int i = tid >> 4, m = tid & 15;
       const float2 li = PW[(i - kO + kPwLo) * kMG + m], l1 = PW[(i + 1 + kPwLo) * kMG + m];
@@ -825,15 +833,15 @@ __global__ void __launch_bounds__(kThreads) bwdc_reverse_kernel(const BwdArgs a)
       if (tk < F / 16) {
         kind = 0;
         col0 = 16 * tk;
-        tile_mma<kC + kM2, true, false>(acc, AQ, LA, XK + col0, LF, lane);
+        tile_mma<kC + kM2, true, false, true>(acc, AQ, LA, XK + col0, LF, lane);
       } else if (tk < 2 * (F / 16)) {
         kind = 1;
         col0 = 16 * (tk - F / 16);
-        tile_mma<kC + kM2, true, false>(acc, AK, LA, XQ + col0, LF, lane);
+        tile_mma<kC + kM2, true, false, true>(acc, AK, LA, XQ + col0, LF, lane);
       } else {
         kind = 2;
         col0 = 16 * (tk - 2 * (F / 16));
-        tile_mma<kC + kM2, true, false>(acc, AV, LA, XG + col0, LD, lane);
+        tile_mma<kC + kM2, true, false, true>(acc, AV, LA, XG + col0, LD, lane);
       }
       const int col = col0 + acc_col(lane);
 #pragma unroll
