@@ -462,9 +462,18 @@ def bwd_alg_flops(B, N, H, F, D, M):
     return float(14 * (F + D) + 44 * F + 41 * D) * M * B * N * H
 
 
+def bwd_chunked_mfma_flops(B, N, H, F, D, M):
+    """FLOPs the chunked backward issues on fp32 MFMA (16x16x4, 2048 FLOP each): per 16-token
+    chunk and 16-mode group, the forward sweep's 1.25 (F + D) + 16 instructions and the reverse
+    sweep's 1.75 (F + D) + 0.75 (2F + D) + 48 (its products, read off the kernels)."""
+    per = 1.25 * (F + D) + 16 + 1.75 * (F + D) + 0.75 * (2 * F + D) + 48
+    return per * 2048.0 * ((N + 15) // 16) * (M // 16) * B * H
+
+
 def bench_backward(torch, ia, inp, bidir=False, steps=5, warmup=2):
     """ia_prefill_bwd over the prefill workload (bf16 q, k, v; fp32 dO), from a zero state
-    (both directions for the bidirectional workload)."""
+    (both directions for the bidirectional workload): the library's choice of kernels (the
+    chunked fp32 MFMA ones on these shapes) and, beside it, the token-sequential kernels."""
     sh = inp["shape"]
     B, H, N, F, D, M = sh["B"], sh["H"], sh["N"], sh["F"], sh["D"], sh["M"]
     q, k, v = (torch.from_numpy(inp[n]).to(torch.bfloat16).cuda() for n in "qkv")
@@ -472,33 +481,52 @@ def bench_backward(torch, ia, inp, bidir=False, steps=5, warmup=2):
     beta = torch.from_numpy(inp["beta"]).cuda()
     g = torch.Generator(device="cpu").manual_seed(550)
     dO = torch.randn((B, N, H, D), generator=g, dtype=torch.float32).cuda()
-    desc = ia.make_desc(B, H, N, F, D, M, ia.IA_BF16, ia.IA_F32, bidir=bidir)
-    ws = torch.empty(ia.ia_prefill_bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
     if N > 16384:   # the long genomic sequence: one timed step (a step takes seconds' share)
         steps, warmup = 1, 1
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dl = torch.empty((H, M), dtype=torch.complex64, device="cuda")
     db = torch.empty_like(dl)
 
-    def step():
-        ia.ia_prefill_bwd(desc, q, k, v, lam, beta, None, dO, dq, dk, dv, dl, db, None, ws)
+    def timed(path):
+        desc = ia.make_desc(B, H, N, F, D, M, ia.IA_BF16, ia.IA_F32, bidir=bidir, bwd_path=path)
+        ws = torch.empty(ia.ia_prefill_bwd_workspace_bytes(desc), dtype=torch.uint8,
+                         device="cuda")
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) / steps * 1e3
-    fl = bwd_alg_flops(B, N, H, F, D, M) * (2 if bidir else 1)
-    return {"us_per_step": us, "tokens_per_s": B * N / (us * 1e-6), "steps": steps,
-            "dtype": "bf16 in, fp32 state and arithmetic", "workspace_bytes": ws.numel(),
-            "alu": {"bound": "alu", "achieved": fl / (us * 1e-6) / 1e12,
-                    "peak": FP32_PEAK / 1e12, "unit": "TFLOP/s",
-                    "frac": fl / (us * 1e-6) / FP32_PEAK, "alg_flops": fl}}
+        def step():
+            ia.ia_prefill_bwd(desc, q, k, v, lam, beta, None, dO, dq, dk, dv, dl, db, None, ws)
+
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        n = ws.numel()
+        del ws
+        return e0.elapsed_time(e1) / steps * 1e3, n
+
+    chunked = F == D and F in (32, 64, 128) and M % 16 == 0
+    us, wsb = timed("auto")
+    seq_us, _ = timed("sequential") if chunked else (us, wsb)
+    dirs = 2 if bidir else 1
+    r = {"us_per_step": us, "tokens_per_s": B * N / (us * 1e-6), "steps": steps,
+         "kernels": "chunked fp32 MFMA" if chunked else "token-sequential fp32",
+         "dtype": "bf16 in, fp32 state and arithmetic", "workspace_bytes": wsb,
+         "sequential_us_per_step": seq_us}
+    if chunked:
+        fl = bwd_chunked_mfma_flops(B, N, H, F, D, M) * dirs
+        r["mfma"] = {"bound": "mfma", "achieved": fl / (us * 1e-6) / 1e12,
+                     "peak": FP32_PEAK / 1e12, "unit": "TFLOP/s",
+                     "frac": fl / (us * 1e-6) / FP32_PEAK, "mfma_flops": fl,
+                     "dtype": "f32 (v_mfma_f32_16x16x4_f32)"}
+    fl = bwd_alg_flops(B, N, H, F, D, M) * dirs
+    r["sequential_alu"] = {"bound": "alu", "achieved": fl / (seq_us * 1e-6) / 1e12,
+                           "peak": FP32_PEAK / 1e12, "unit": "TFLOP/s",
+                           "frac": fl / (seq_us * 1e-6) / FP32_PEAK, "alg_flops": fl}
+    return r
 
 
 def cpu_baseline(inp, bidir, budget_s=12.0):

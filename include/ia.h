@@ -88,7 +88,7 @@ typedef enum { IA_F32 = 0, IA_BF16 = 1 } ia_dtype;
 /* ia_prefill_bwd only (ignored elsewhere): which of its two implementations runs.  Without
  * either flag the chunked kernels run where they exist (F == Dv in {32, 64, 128}) unless the
  * (b,h) slices and mode groups are so few that the token-sequential sweeps would cut each
- * sequence into more than two segments; IA_FLAG_SEQUENTIAL_BWD forces the token-sequential
+ * sequence into more than eight segments; IA_FLAG_SEQUENTIAL_BWD forces the token-sequential
  * kernels, IA_FLAG_CHUNKED_BWD the chunked ones (IA_ERR_UNSUPPORTED on other shapes, and with
  * both flags).  Both give the same gradients up to fp32 rounding. */
 #define IA_FLAG_SEQUENTIAL_BWD 8u
@@ -270,19 +270,26 @@ ia_status ia_decode_step(const ia_desc* desc,
                          const void* lambda, const void* beta,
                          ia_state* st, void* o_t, void* stream);
 
-/* Workspace bytes ia_prefill_bwd needs for this descriptor: state checkpoints every 32 tokens
- * (B*H*ceil(N/32)*M*(F+Dv+1) complex64), per-token partial denominators (B*H*N*M/2 complex64),
- * per-mode-group gradient rows (M/16 * B*H*N*(2F+Dv) float), per-slice lambda/beta gradients,
- * the recompute's a = phi(q) U^T per token (B*H*N*M complex64) and, when a long sequence is
- * cut into segments, their start states and entering adjoints, each region 256-byte aligned.
- * 0 on an invalid descriptor. */
+/* Workspace bytes ia_prefill_bwd needs for this descriptor, each region 256-byte aligned; 0 on
+ * an invalid descriptor (or a backward flag combination it refuses).
+ * Chunked kernels: every 16-token chunk's start state per group of 16 modes
+ * (B*H*ceil(N/16)*M*(F+Dv+1) complex64), per-token den and dL/do.num partials per group
+ * (B*H*N*M/16 float pairs), per-mode-group gradient rows (M/16 * B*H*N*(2F+Dv) float) and
+ * per-slice lambda/beta gradients.
+ * Token-sequential kernels: state checkpoints every 32 tokens (B*H*ceil(N/32)*M*(F+Dv+1)
+ * complex64), per-token partial denominators (B*H*N*M/2 complex64), the gradient rows as above,
+ * per-slice lambda/beta gradients, the recompute's a = phi(q) U^T per token (B*H*N*M complex64)
+ * and, when a long sequence is cut into segments, their start states and entering adjoints. */
 size_t ia_prefill_bwd_workspace_bytes(const ia_desc* desc);
 
 /* Gradients of the causal layer (ia_prefill_fwd's outputs o) for a real loss L, given
  * dO = dL/do: reverse-mode differentiation of the recurrence and readout above, as the
- * training step of [summary §G] needs.  The states are recomputed from st0 (not read from a
- * forward call), checkpointed every 32 tokens, and rebuilt backward inside each interval by
- * U_{t-1} = (U_t - beta phi(k_t)) / lambda, in fp32.
+ * training step of [summary §G] needs, in fp32 throughout.  The states are recomputed from st0
+ * (not read from a forward call).  Chunked kernels (the flags above pick them): 16-token
+ * chunks per (b, h, group of 16 modes), every contraction on fp32 MFMA, each chunk's start
+ * state stored by a forward sweep and the state adjoints carried chunk by chunk backward
+ * [summary §A.2].  Token-sequential kernels: checkpoints every 32 tokens, the states rebuilt
+ * backward inside each interval by U_{t-1} = (U_t - beta phi(k_t)) / lambda.
  *   q, k, v, lambda, beta   as in ia_prefill_fwd (dense layout, in_dtype).
  *   st0      initial state the forward started from, or NULL for zeros; read only.
  *   dO       [B][N][H][Dv] out_dtype.
@@ -295,9 +302,11 @@ size_t ia_prefill_bwd_workspace_bytes(const ia_desc* desc);
  * phi' = 1.  IA_FLAG_BIDIR: gradients of o = IA(x) + flip_t(IA(flip_t x)) (both directions from
  * zero), the reversed walk's added onto the forward's; st0 and dst0 must then be NULL
  * (IA_ERR_UNSUPPORTED otherwise).
- * Accuracy: the rebuild grows fp32 rounding by at most |lambda|^-31 inside an interval; for
- * |lambda| >= 0.9 that is below 30x (an S4D-Lin lambda = exp(dt(-1/2 + i pi m)) with
- * dt <= 0.1 has |lambda| >= 0.95).
+ * Accuracy: the chunked kernels keep fp32's relative accuracy for |lambda| above about 1e-4
+ * (the chunk-local powers lambda^e, |e| <= 9, stay inside fp32's range).  In the
+ * token-sequential kernels the rebuild grows fp32 rounding by at most |lambda|^-31 inside an
+ * interval; for |lambda| >= 0.9 that is below 30x (an S4D-Lin lambda = exp(dt(-1/2 + i pi m))
+ * with dt <= 0.1 has |lambda| >= 0.95).
  * lambda = 0 gives non-finite gradients.
  * Errors: as ia_prefill_fwd (IA_ERR_NULL for a missing required pointer, IA_ERR_ALIGN for
  * pointers not 16-byte aligned, IA_ERR_ALIAS when an output overlaps an input, another

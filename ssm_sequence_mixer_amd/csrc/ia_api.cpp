@@ -516,7 +516,7 @@ static bool bwd_chunked(const ia_desc* d) {
   if (d->flags & IA_FLAG_CHUNKED_BWD) return true;
   int seg_len;
   return ia::bwd_chunked_supported(d->F, d->Dv, d->M) &&
-         ia::bwd_segments(d->B, d->H, d->N, d->M, &seg_len) <= 2;
+         ia::bwd_segments(d->B, d->H, d->N, d->M, &seg_len) <= 8;
 }
 
 static ia_status check_bwd_path(const ia_desc* d) {

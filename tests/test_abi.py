@@ -324,13 +324,17 @@ def test_bwd_workspace_bytes_layout():
     assert ia.lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(desc(N=0))) == 0
     assert ia.lib.ia_prefill_bwd_workspace_bytes(None) == 0
     # automatic choice: few slices and a long sequence take the token-sequential sweeps (cut
-    # into segments); the chunked flag forces the chunked kernels' layout
-    d = desc(B=1, H=2, N=1000, F=32, Dv=32, M=16)
+    # into more than eight segments), more slices the chunked kernels; the chunked flag forces
+    # the chunked kernels' layout
+    d = desc(B=1, H=2, N=4000, F=32, Dv=32, M=16)
     assert ia.lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(d)) != _bwd_chunked_bytes(
-        1, 2, 1000, 32, 32, 16)
+        1, 2, 4000, 32, 32, 16)
     d.flags = ia.IA_FLAG_CHUNKED_BWD
     assert ia.lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(d)) == _bwd_chunked_bytes(
-        1, 2, 1000, 32, 32, 16)
+        1, 2, 4000, 32, 32, 16)
+    d = desc(B=2, H=8, N=131072, F=32, Dv=32, M=32)
+    assert ia.lib.ia_prefill_bwd_workspace_bytes(ctypes.byref(d)) == _bwd_chunked_bytes(
+        2, 8, 131072, 32, 32, 32)
     # the chunked kernels exist for F == Dv in {32, 64, 128} only; both flags: unsupported
     d = desc(B=1, H=1, N=10, F=64, Dv=32, M=16)
     d.flags = ia.IA_FLAG_CHUNKED_BWD
