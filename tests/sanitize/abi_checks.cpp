@@ -48,7 +48,7 @@ int main() {
     expect("dtype", ia_state_init(&d, &st, nullptr), IA_ERR_DTYPE);
     d = desc(); d.den_clamp = -1.f;
     expect("clamp", ia_prefill_workspace_bytes(&d) == 0 ? IA_ERR_DOMAIN : IA_OK, IA_ERR_DOMAIN);
-    d = desc(); d.flags = 8;
+    d = desc(); d.flags = 32;
     expect("flags", ia_prefill_fwd(&d, addr(0), addr(1), addr(2), addr(3), addr(4), &st,
                                    addr(5), addr(6), big, nullptr), IA_ERR_UNSUPPORTED);
     expect("null desc", ia_prefill_fwd(nullptr, addr(0), addr(1), addr(2), addr(3), addr(4), &st,
@@ -100,6 +100,20 @@ int main() {
            ia_prefill_bwd(&d, addr(0), addr(1), addr(2), addr(3), addr(4), nullptr, addr(5),
                           addr(6), addr(7), addr(8), addr(9), addr(13), nullptr, addr(14),
                           need - 1, nullptr), IA_ERR_WORKSPACE);
+    // both backward kernel choices, and the chunked kernels on a shape they do not serve
+    ia_desc db = d;
+    db.flags = IA_FLAG_SEQUENTIAL_BWD | IA_FLAG_CHUNKED_BWD;
+    expect("bwd both kernel flags",
+           ia_prefill_bwd(&db, addr(0), addr(1), addr(2), addr(3), addr(4), nullptr, addr(5),
+                          addr(6), addr(7), addr(8), addr(9), addr(13), nullptr, addr(14), big,
+                          nullptr), IA_ERR_UNSUPPORTED);
+    db.flags = IA_FLAG_CHUNKED_BWD;
+    db.Dv = 48;
+    expect("bwd chunked on Dv 48",
+           ia_prefill_bwd(&db, addr(0), addr(1), addr(2), addr(3), addr(4), nullptr, addr(5),
+                          addr(6), addr(7), addr(8), addr(9), addr(13), nullptr, addr(14), big,
+                          nullptr), IA_ERR_UNSUPPORTED);
+    expect("bwd chunked workspace bytes", ia_prefill_bwd_workspace_bytes(&db) == 0 ? 0 : 1, 0);
     expect("readout null", ia_prefill_fwd_readout(&d, addr(0), addr(1), addr(2), addr(3),
                                                   addr(4), nullptr, &st, addr(5), addr(6), big,
                                                   nullptr), IA_ERR_NULL);
