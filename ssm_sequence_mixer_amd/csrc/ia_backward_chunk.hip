@@ -245,7 +245,18 @@ struct Rows {
   static constexpr int NV = kC * VPR;
   static constexpr int PT = (NV + kThreads - 1) / kThreads;
   uint4 r[PT];
+  long long off0[PT];   // element offset of this thread's vector at walk position 0
+  long long step;       // elements from one walk position to the next (negative backwards)
 
+  // Offsets once per kernel; a chunk's fetch then adds its walk position times the step.
+  __device__ __forceinline__ void init(const BwdArgs& a, const Wg& w) {
+    step = (long long)(a.dir ? -1 : 1) * a.H * W;
+#pragma unroll
+    for (int p = 0; p < PT; ++p) {
+      const int n = threadIdx.x + kThreads * p;
+      off0[p] = (long long)row_index(a, w, 0, W) + (n % VPR) * E;
+    }
+  }
   __device__ __forceinline__ void fetch(const void* base, const BwdArgs& a, const Wg& w, int t0) {
 #pragma unroll
     for (int p = 0; p < PT; ++p) {
@@ -253,8 +264,7 @@ struct Rows {
       r[p] = make_uint4(0u, 0u, 0u, 0u);
       if (n < NV && t < a.N)
         r[p] = *reinterpret_cast<const uint4*>(static_cast<const char*>(base) +
-                                               (row_index(a, w, t, W) + (n % VPR) * E) *
-                                                   (BF ? 2 : 4));
+                                               (off0[p] + t * step) * (BF ? 2 : 4));
     }
   }
   // into X ([kC][ld] floats); fmap: the feature map (rows past N stay zero)
@@ -294,6 +304,12 @@ struct ChunkRows {
   Rows<F, BI> q, k;
   Rows<D, BI> v;
   Rows<D, BO> g;
+  __device__ __forceinline__ void init(const BwdArgs& a, const Wg& w) {
+    q.init(a, w);
+    k.init(a, w);
+    v.init(a, w);
+    g.init(a, w);
+  }
   __device__ __forceinline__ void fetch(const BwdArgs& a, const Wg& w, int t0) {
     q.fetch(a.q, a, w, t0);
     k.fetch(a.k, a, w, t0);
@@ -387,6 +403,7 @@ __global__ void __launch_bounds__(kThreads) bwdc_forward_kernel(const BwdArgs a)
   };
   // chunk c's rows arrive in registers one chunk ahead and stay in flight across its compute
   ChunkRows<F, D, BI, BO> rows;
+  rows.init(a, w);
   rows.fetch(a, w, 0);
   for (int c = 0; c < nch; ++c) {
     const int t0 = c * kC, par = c & 1;
@@ -627,6 +644,7 @@ __global__ void __launch_bounds__(kThreads) bwdc_reverse_kernel(const BwdArgs a)
                                  : make_float2(0.f, 0.f);
     }
   };
+  rows.init(a, w);
   f4 yre[YPW], yim[YPW];
   // S^U <- conj(lam^C) S^U + conj(Y_U), S^G likewise, from the Y tiles of the chunk just done
   auto update_adjoints = [&]() {
