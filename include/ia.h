@@ -302,8 +302,11 @@ size_t ia_prefill_bwd_workspace_bytes(const ia_desc* desc);
  * phi' = 1.  IA_FLAG_BIDIR: gradients of o = IA(x) + flip_t(IA(flip_t x)) (both directions from
  * zero), the reversed walk's added onto the forward's; st0 and dst0 must then be NULL
  * (IA_ERR_UNSUPPORTED otherwise).
- * Accuracy: the chunked kernels keep fp32's relative accuracy for |lambda| above about 1e-4
- * (the chunk-local powers lambda^e, |e| <= 9, stay inside fp32's range).  In the
+ * Accuracy: the chunked kernels' chunk-local powers lambda^e (|e| <= 9) stay inside fp32's
+ * range for |lambda| above about 1e-4.  The gradients then carry fp32 rounding amplified by the
+ * layer's own conditioning: with the denominator and |lambda| well below 1, o_t tends to v_t
+ * and dq, dk are differences of nearly equal terms; dlambda's distance-weighted sums lose
+ * about log10(1/|lambda|) + 2 digits (tested to |lambda| = 0.01).  In the
  * token-sequential kernels the rebuild grows fp32 rounding by at most |lambda|^-31 inside an
  * interval; for |lambda| >= 0.9 that is below 30x (an S4D-Lin lambda = exp(dt(-1/2 + i pi m))
  * with dt <= 0.1 has |lambda| >= 0.95).

@@ -297,3 +297,49 @@ def test_backward_largest_sizes(shape, dtype):
     ref = oracle.prefill_bwd(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"], dO,
                              threads=2)
     _compare(got, ref, TOL_BF16 if dtype == "bf16" else TOL_F32, f"bwd largest {shape}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_chunked_128_modes(dtype):
+    """M = 128 with F = Dv = 128 on the chunked kernels: eight groups of 16 modes, the most the
+    per-token den partials of a chunk are summed over, and a ragged last chunk."""
+    import torch
+    ia = _ia()
+    B, H, N, F, D, M = 1, 2, 45, 128, 128, 128
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    inp = W.make_inputs(B, H, N, F, D, M, dtype=dtype, seed=590)
+    dO = np.random.default_rng(591).standard_normal((B, N, H, D)).astype(np.float32)
+    tag(f"backward chunked M=128 {dtype}")
+    q, k, v = (dev(inp[n], td) for n in "qkv")
+    r = ia.prefill_bwd(q, k, v, dev(inp["lam"]), dev(inp["beta"]), dev(dO), path="chunked")
+    torch.cuda.synchronize()
+    got = tuple(host(x) for x in r[:5]) + (None,)
+    ref = oracle.prefill_bwd(inp["q"], inp["k"], inp["v"], inp["lam"], inp["beta"], dO,
+                             threads=2)
+    _compare(got, ref, TOL_BF16 if dtype == "bf16" else TOL_F32, f"bwd chunked M=128 {dtype}")
+
+
+@pytest.mark.parametrize("mag,no_den", [(1.0, False), (0.5, False), (0.5, True), (0.1, True),
+                                         (0.01, True)])
+def test_backward_chunked_lambda_magnitudes(mag, no_den):
+    """Modes of one magnitude on the chunked kernels, fp32: undamped (|lambda| = 1, the S4D-Lin
+    angles of dt = 0.01) and fast-decaying ones down to |lambda| = 0.01, where the chunk-local
+    powers lambda^e (|e| <= 9) span 1e-16 to 1e18.  Below |lambda| ~ 0.5 the normalised
+    readout is the plain-definition limit o_t -> v_t: dq and dk become differences of the
+    numerator's and the denominator's terms that cancel to 1e-7 of their size (the fp64 oracle
+    itself holds them to about 1e-11), so those magnitudes run the readout without the
+    denominator, whose gradients do not cancel."""
+    B, H, N, F, D, M = 2, 2, 70, 32, 32, 16
+    inp = W.make_inputs(B, H, N, F, D, M, dtype="f32", seed=600)
+    if mag == 1.0:
+        ang = np.pi * 0.01 * np.arange(M)[None, :].repeat(H, 0)
+    else:
+        ang = np.random.default_rng(601).uniform(-np.pi, np.pi, (H, M))
+    lam = (mag * np.exp(1j * ang)).astype(np.complex64)
+    inp = {**inp, "lam": lam}
+    dO = np.random.default_rng(602).standard_normal((B, N, H, D)).astype(np.float32)
+    tag(f"backward chunked |lambda|={mag} no_den={no_den}")
+    got = _run(inp, dO, path="chunked", no_den=no_den)
+    ref = oracle.prefill_bwd(inp["q"], inp["k"], inp["v"], lam, inp["beta"], dO, no_den=no_den,
+                             threads=2)
+    _compare(got, ref, TOL_F32, f"bwd chunked |lambda|={mag} no_den={no_den}")
