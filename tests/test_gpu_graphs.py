@@ -108,16 +108,19 @@ def test_graph_chunked_prefill_with_segments():
     _replays(torch, run, reset, [o] + list(st), eager)
 
 
+@pytest.mark.parametrize("path", ["chunked", "sequential"])
 @pytest.mark.parametrize("bidir", [False, True])
-def test_graph_backward(bidir):
+def test_graph_backward(bidir, path):
+    """The backward in a graph, replayed: the chunked kernels, and the token-sequential ones
+    (few slices: several sequence segments and their carries)."""
     import torch
     ia = _ia()
-    B, H, N, F, D, M = 1, 2, 600, 64, 64, 32   # few slices: several sequence segments
+    B, H, N, F, D, M = 1, 2, 600, 64, 64, 32
     inp = W.make_inputs(B, H, N, F, D, M, dtype="bf16", seed=720)
     q, k, v = (dev(inp[n], torch.bfloat16) for n in "qkv")
     lam, beta = dev(inp["lam"]), dev(inp["beta"])
     dO = dev(np.random.default_rng(721).standard_normal((B, N, H, D)).astype(np.float32))
-    desc = ia.make_desc(B, H, N, F, D, M, ia.IA_BF16, ia.IA_F32, bidir=bidir)
+    desc = ia.make_desc(B, H, N, F, D, M, ia.IA_BF16, ia.IA_F32, bidir=bidir, bwd_path=path)
     ws = torch.empty(ia.ia_prefill_bwd_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dl = torch.empty((H, M), dtype=torch.complex64, device="cuda")
@@ -131,7 +134,7 @@ def test_graph_backward(bidir):
         for x in outs:
             x.zero_()
 
-    tag(f"graph backward bidir={bidir}")
+    tag(f"graph backward bidir={bidir} path={path}")
     run()
     torch.cuda.synchronize()
     eager = [x.clone() for x in outs]
