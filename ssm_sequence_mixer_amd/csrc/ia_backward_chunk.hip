@@ -145,11 +145,14 @@ __device__ __forceinline__ float2 cmulc2(float2 a, float2 b) {
   return make_float2(a.x * b.x + a.y * b.y, a.y * b.x - a.x * b.y);
 }
 
-// Sum over the 16 lanes of a row (lanes 16r .. 16r+15), left in every lane of the row.
-__device__ __forceinline__ float row16_sum(float v) {
-#pragma unroll
-  for (int off = 8; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+// Sum over the 16 lanes of a row (lanes 16r .. 16r+15), left in every lane of the row: two
+// sums at once through DPP moves (row_totals: quad swaps, then half-row and row mirrors), no
+// LDS round trip.
+__device__ __forceinline__ void row16_sum2(float& x, float& y) {
+  float v[2] = {x, y};
+  row_totals<16, 2>(v);
+  x = v[0];
+  y = v[1];
 }
 
 // lam^e for integer e (negative allowed), in fp64 by binary exponentiation, rounded once.
@@ -509,8 +512,7 @@ __global__ void __launch_bounds__(kThreads) bwdc_forward_kernel(const BwdArgs a)
       const float2 ev = cadd2(cmul(l1, EC[par * kMG + m]), cmul(b, E0T[i * kMG + m]));   // e_i
       float den = av.x * ev.x - av.y * ev.y;
       float gn = av.x * xv.x - av.y * xv.y;
-      den = row16_sum(den);
-      gn = row16_sum(gn);
+      row16_sum2(den, gn);
       const int t = t0 + i;
       if (m == 0 && t < a.N)
         a.dpart[((size_t)w.slice * a.N + t) * groups + w.group] = make_float2(den, gn);
@@ -793,7 +795,8 @@ __global__ void __launch_bounds__(kThreads) bwdc_reverse_kernel(const BwdArgs a)
       dlam = cadd2(dlam, cconj(sx));
       // the eta adjoint: S^e <- conj(lam^C) S^e + conj(sum_i lam^(i+1) a_i dd_i)
       const float2 sev = SE[par * kMG + m];
-      float sr = row16_sum(ddi * l1a.x), si = row16_sum(ddi * l1a.y);
+      float sr = ddi * l1a.x, si = ddi * l1a.y;
+      row16_sum2(sr, si);
       if (i == 0)
         SE[(par ^ 1) * kMG + m] =
             cadd2(cmulc2(sev, PW[(kC + kPwLo) * kMG + m]), make_float2(sr, -si));
@@ -907,8 +910,9 @@ __global__ void __launch_bounds__(kThreads) bwdc_reverse_kernel(const BwdArgs a)
   }
   // dlam, dbeta: sum over the 16 token threads of each mode, then over the two wave halves
   {
-    const float lr = row16_sum(dlam.x), lim = row16_sum(dlam.y);
-    const float br = row16_sum(dbet.x), bim = row16_sum(dbet.y);
+    float lr = dlam.x, lim = dlam.y, br = dbet.x, bim = dbet.y;
+    row16_sum2(lr, lim);
+    row16_sum2(br, bim);
     if (ei == 0 && tid >= kC * kMG) {
       LSUM[em - kMG] = make_float2(lr, lim);
       LSUM[em] = make_float2(br, bim);
