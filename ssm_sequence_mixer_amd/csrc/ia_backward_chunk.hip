@@ -178,15 +178,20 @@ __device__ float2 cpow_i(float2 z, int e) {
   return make_float2((float)ar, (float)ai);
 }
 
-// The workgroup's (slice, group) and its per-mode constants.
+// The workgroup's (slice, group) and its per-mode constants.  Workgroups are dispatched to the
+// eight XCDs in turn (block b to XCD b % 8); with the grid a multiple of 8, block b takes
+// position (b % 8) (grid / 8) + b / 8, so every XCD holds whole slices, and the mode groups of
+// a slice, which read the same token rows chunk by chunk, share that XCD's L2.
 struct Wg {
   int slice, b, h, group, m0;
 };
 __device__ __forceinline__ Wg wg_of(const BwdArgs& a) {
   const int groups = a.M / kMG;
+  const int nb = gridDim.x;
+  const int p = nb % 8 ? (int)blockIdx.x : (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8;
   Wg w;
-  w.slice = blockIdx.x / groups;
-  w.group = blockIdx.x % groups;
+  w.slice = p / groups;
+  w.group = p % groups;
   w.b = w.slice / a.H;
   w.h = w.slice % a.H;
   w.m0 = w.group * kMG;
