@@ -92,14 +92,19 @@ struct Slice {
   int lo, hi;   // the segment's tokens [lo, hi)
 };
 
+// Workgroups are dispatched to the eight XCDs in turn (block b to XCD b % 8); with the grid a
+// multiple of 8, block b takes position (b % 8) (grid / 8) + b / 8, so the mode groups of a
+// slice, which read the same token rows, run on one XCD and share its L2.
 __device__ __forceinline__ Slice slice_of(const BwdArgs& a) {
   Slice s;
   s.lane = threadIdx.x & 63;
   s.wave = threadIdx.x >> 6;
   s.groups = a.M / kModesPerWg;
-  s.seg = blockIdx.x % a.nseg;
-  s.slice = blockIdx.x / a.nseg / s.groups;
-  s.grp = blockIdx.x / a.nseg % s.groups;
+  const int nb = gridDim.x;
+  const int p = nb % 8 ? (int)blockIdx.x : (blockIdx.x % 8) * (nb / 8) + blockIdx.x / 8;
+  s.seg = p % a.nseg;
+  s.slice = p / a.nseg / s.groups;
+  s.grp = p / a.nseg % s.groups;
   s.lo = s.seg * a.seg_len;
   s.hi = min(a.N, s.lo + a.seg_len);
   s.b = s.slice / a.H;
