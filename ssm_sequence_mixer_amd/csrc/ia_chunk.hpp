@@ -462,8 +462,21 @@ __device__ __forceinline__ uint32_t row_off(const ChunkArgs& a, int sn, int r, i
 __host__ __device__ inline int pair_wg_count(int seqs, int n_seg, bool pairs) {
   return pairs ? 16 * ((seqs / 2 * n_seg + 7) / 8) : seqs * n_seg;
 }
-__device__ inline bool pair_wg(int w, int seqs, int n_seg, bool pairs, int& seq, int& seg) {
+// heads > 0 (the output pass, plain order): block w takes position
+// p = (w % 8) (grid / 8) + w / 8 of a head-major order p = (h B + b) n_seg + seg, so each XCD
+// runs whole heads: the workgroups that copy one head's tables and fold the same sequences'
+// segment slots find them in that XCD's L2 after the first.
+__device__ inline bool pair_wg(int w, int seqs, int n_seg, bool pairs, int& seq, int& seg,
+                               int heads = 0) {
   if (!pairs) {
+    const int nb = seqs * n_seg;
+    if (heads > 0 && nb % 8 == 0) {
+      const int p = (w % 8) * (nb / 8) + w / 8;
+      const int rows = seqs / heads, hb = p / n_seg;
+      seq = (hb % rows) * heads + hb / rows;
+      seg = p % n_seg;
+      return true;
+    }
     seq = w / n_seg;
     seg = w % n_seg;
     return true;
@@ -1579,7 +1592,7 @@ chunk_prefill_kernel(const ChunkArgs a) {
   x.g = x.lane >> 4;
   {
     int seq, seg;
-    if (!pair_wg(blockIdx.x, a.H * a.B, a.n_seg, a.pair_heads, seq, seg)) return;
+    if (!pair_wg(blockIdx.x, a.H * a.B, a.n_seg, a.pair_heads, seq, seg, a.H)) return;
     x.seq = seq;
     x.seg = a.seg_first + seg;
   }
